@@ -1,0 +1,247 @@
+"""CPU oracle for group-wise asymmetric INT4 quantization and y = x * What^T.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product package.  It wraps the
+plain C implementation in ``wq_oracle.c`` (built with gcc, no fast-math, no
+contraction) through ctypes and numpy arrays.  It shares no code with the HIP
+path.
+
+Every function names the passage it follows; the readings taken where the pages
+are silent are listed at the top of ``wq_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wq_oracle.c")
+_LIB = os.path.join(_HERE, "_liborc.so")
+
+F32, BF16, F16 = 0, 1, 2
+EINVAL, ERANGE = -1, -6
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (plain IEEE binary32/64, no FMA contraction)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+        "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
+        "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    sig = {
+        "orc_set_threads": (None, [I]),
+        "orc_get_threads": (I, []),
+        "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_f32_to_f16_array": (None, [P, I64, P]),
+        "orc_f32_to_bf16_array": (None, [P, I64, P]),
+        "orc_quantize_groups": (I, [P, I, I64, I64, I, P, P, P]),
+        "orc_dequant": (I, [P, P, P, I64, I64, I, I, P]),
+        "orc_pack_canonical": (I, [P, I64, I64, P]),
+        "orc_device_bytes": (I64, [I64, I64]),
+        "orc_pack_device": (I, [P, I64, I64, P]),
+        "orc_unpack_device": (I, [P, I64, I64, P]),
+        "orc_pack_zeros": (I, [P, I64, I64, P]),
+        "orc_gemm_f64": (I, [I64, I64, I64, P, P, P]),
+        "orc_gemm_rows_f64": (I, [I64, I64, I64, I, P, P, P, P, I64, I64, P]),
+        "orc_symmetric": (I, [P, I64, I, P, P, P]),
+        "orc_bits_per_weight": (ctypes.c_double, [I, I, I, I]),
+        "orc_storage_bytes": (ctypes.c_double, [I64, I, I, I, I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise OracleError(f"{what} failed with status {status}")
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())
+
+
+# --- number formats ---------------------------------------------------------
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 bit patterns, round to nearest even, subnormals kept."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_f32_to_f16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns, round to nearest even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_f32_to_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    lib = _load()
+    h = np.ascontiguousarray(h, np.uint16).ravel()
+    return np.array([lib.orc_f16_to_f32(int(v)) for v in h], np.float32)
+
+
+# --- quantizer ---------------------------------------------------------------
+
+def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None):
+    """Group-wise asymmetric INT4 quantization of W[N][K] (the pages' "minimum
+    maths": s = (max - min)/15, z = round(-min/s), q = clip(round(w/s + z), 0, 15)).
+
+    ``W`` is float32, or uint16 bit patterns with ``dtype`` BF16 or F16.
+    Returns (q[N][K] uint8, s[N][K/g] uint16 fp16 bits, z[N][K/g] uint8).
+    """
+    W = np.ascontiguousarray(W)
+    if dtype is None:
+        if W.dtype == np.float32:
+            dtype = F32
+        else:
+            raise ValueError("give dtype for non-float32 input")
+    N, K = W.shape
+    G = K // group
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N, G), np.uint16)
+    z = np.empty((N, G), np.uint8)
+    _check(_load().orc_quantize_groups(_ptr(W), dtype, N, K, group, _ptr(q), _ptr(s), _ptr(z)),
+           "orc_quantize_groups")
+    return q, s, z
+
+
+def dequant(q: np.ndarray, s: np.ndarray, z: np.ndarray, group: int, out_dtype: int = F32) -> np.ndarray:
+    """w_hat = s * (q - z) (the pages' decoding), as fp32 values or fp16/bf16 bits."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint16)
+    z = np.ascontiguousarray(z, np.uint8)
+    N, K = q.shape
+    out = np.empty((N, K), np.float32 if out_dtype == F32 else np.uint16)
+    _check(_load().orc_dequant(_ptr(q), _ptr(s), _ptr(z), N, K, group, out_dtype, _ptr(out)), "orc_dequant")
+    return out
+
+
+# --- packing -----------------------------------------------------------------
+
+def pack_canonical(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    N, K = q.shape
+    out = np.empty((N, K // 2), np.uint8)
+    _check(_load().orc_pack_canonical(_ptr(q), N, K, _ptr(out)), "orc_pack_canonical")
+    return out
+
+
+def device_bytes(N: int, K: int) -> int:
+    return int(_load().orc_device_bytes(N, K))
+
+
+def pack_device(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    N, K = q.shape
+    out = np.empty(device_bytes(N, K), np.uint8)
+    _check(_load().orc_pack_device(_ptr(q), N, K, _ptr(out)), "orc_pack_device")
+    return out
+
+
+def unpack_device(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, np.uint8)
+    q = np.empty((N, K), np.uint8)
+    _check(_load().orc_unpack_device(_ptr(packed), N, K, _ptr(q)), "orc_unpack_device")
+    return q
+
+
+def pack_zeros(z: np.ndarray) -> np.ndarray:
+    z = np.ascontiguousarray(z, np.uint8)
+    N, G = z.shape
+    out = np.empty((N, (G + 1) // 2), np.uint8)
+    _check(_load().orc_pack_zeros(_ptr(z), N, G, _ptr(out)), "orc_pack_zeros")
+    return out
+
+
+# --- product -------------------------------------------------------------------
+
+def gemm_f64(x_f16_bits: np.ndarray, w_hat: np.ndarray) -> np.ndarray:
+    """y[m][n] = sum_k x[m][k] * w_hat[n][k], in fp64, summed in k order."""
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    w = np.ascontiguousarray(w_hat, np.float32)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2
+    y = np.empty((M, N), np.float64)
+    _check(_load().orc_gemm_f64(M, N, K, _ptr(x), _ptr(w), _ptr(y)), "orc_gemm_f64")
+    return y
+
+
+def gemm_rows_f64(x_f16_bits, q, s, z, group: int, n0: int, nrows: int) -> np.ndarray:
+    """Columns n0..n0+nrows-1 of y (all M rows), from codes/scales/zeros."""
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint16)
+    z = np.ascontiguousarray(z, np.uint8)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, nrows), np.float64)
+    _check(_load().orc_gemm_rows_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), _ptr(z), n0, nrows, _ptr(y)),
+           "orc_gemm_rows_f64")
+    return y
+
+
+# --- symmetric quantizers and storage ----------------------------------------
+
+def symmetric(w, bits: int):
+    """Symmetric absmax quantizer: s = max|w| / (2^(bits-1) - 1), q = round(w/s)."""
+    w = np.ascontiguousarray(w, np.float64).ravel()
+    q = np.empty(w.shape, np.int32)
+    s = ctypes.c_double()
+    w_hat = np.empty(w.shape, np.float64)
+    _check(_load().orc_symmetric(_ptr(w), w.size, bits, _ptr(q), ctypes.byref(s), _ptr(w_hat)), "orc_symmetric")
+    return q, s.value, w_hat
+
+
+def bits_per_weight(bits: int, group: int, scale_bits: int = 16, zero_bits: int = 0) -> float:
+    return float(_load().orc_bits_per_weight(bits, group, scale_bits, zero_bits))
+
+
+def storage_bytes(n: int, bits: int, group: int, scale_bits: int = 16, zero_bits: int = 0) -> float:
+    return float(_load().orc_storage_bytes(n, bits, group, scale_bits, zero_bits))

@@ -1,0 +1,410 @@
+/*
+ * wq_oracle.c -- plain, slow CPU oracle for group-wise asymmetric INT4 weight
+ * quantization and the dequantize-and-multiply product y = x * What^T.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load it.  It shares no code, header, table or constant with the
+ * HIP path.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [Q]  "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ) and GGUF - the
+ *        model's accounting zoom", sections "The minimum maths: scale and
+ *        zero-point" (equations for s, z, the encoding and the decoding) and
+ *        "Numerical example" (the 8-weight INT4 table and the storage count).
+ *   [C]  "Quantization Methods Compared: INT8, GPTQ, AWQ, FP8, FP4 and KV-Cache
+ *        Quantization", section "What quantisation does: scale, round, and the
+ *        outlier that ruins a group" (symmetric absmax int8 rule, per-group
+ *        scales, bits per weight).
+ *   [T]  "Test-time quantization", section "The maths that matter" (symmetric
+ *        b-bit scale M/(2^(b-1)-1) and the half-step error bound).
+ *
+ * Where the pages leave a step open, the readings below are used (each is also
+ * listed in the design notes):
+ *   - rounding to an integer is round-half-to-even ("rne");
+ *   - the scale is stored as IEEE fp16 (round to nearest even, subnormals kept)
+ *     and the STORED scale is the one used to encode and to decode;
+ *   - s, z and the codes are computed with single IEEE binary32 operations, in
+ *     the order written, with no fused multiply-add;
+ *   - the group range is widened to include zero (lo' = min(lo,0),
+ *     hi' = max(hi,0)) so that the zero-point is a code in [0, 15];
+ *   - a group whose stored scale is 0 stores s = 0, z = 0 and all codes 0;
+ *   - a group whose range would give a non-finite fp16 scale is an error.
+ *
+ * Packed layouts:
+ *   canonical: [N][K/2] bytes, byte b of a row holds k = 2b in its low nibble
+ *              and k = 2b+1 in its high nibble (the page only fixes that eight
+ *              4-bit codes take four bytes);
+ *   device:    16-row x 128-column tiles, tile (nb, kt) at byte offset
+ *              (nb * ceil(K/128) + kt) * 1024; inside a tile, lane
+ *              l = r + 16*c (r = row in tile 0..15, c = 0..3) owns 16 bytes
+ *              at offset 16*l, made of four little-endian 32-bit words j = 0..3;
+ *              word j holds the eight columns kk = 32*j + 8*c + e (e = 0..7)
+ *              of the tile, column e in nibble p(e) = 4*(e%2) + e/2.  Rows are
+ *              padded to a multiple of 16 and columns to a multiple of 128 with
+ *              code 0.  (Parity unpinned by the pages: the layout is a
+ *              definition; the tests check it is a bijection.)
+ *   zeros:     [N][ceil(G/2)] bytes, G = K/g groups per row, group j in the
+ *              low nibble of byte j/2 when j is even, high nibble when odd.
+ */
+#include "wq_oracle.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 1;
+
+void orc_set_threads(int n) { g_threads = n > 0 ? n : 1; }
+int orc_get_threads(void) { return g_threads; }
+
+/* ------------------------------------------------------------------------- */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------- */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* IEEE fp16 -> fp32, exact.  Value = (-1)^s * 2^(e-15) * (1 + m/1024) for
+ * normal numbers and 2^-24 * m for subnormals. */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 31) {
+        if (m) return bits_to_f32(0x7fc00000u | ((uint32_t)sign << 31));
+        v = INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)m, -24);
+    } else {
+        v = ldexp(1024.0 + m, e - 25);
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* fp32 -> IEEE fp16 with round-to-nearest-even, subnormals kept.  The value is
+ * taken exactly in double, divided by the fp16 spacing of its binade (a power
+ * of two, so exact), rounded half-to-even, and re-encoded. */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint16_t sign = (f32_to_bits(f) >> 16) & 0x8000u;
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs((double)f);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u); /* rounds past 65504 */
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: spacing 2^-24; n = 1024 encodes 2^-14 correctly */
+        double n = nearbyint(a / ldexp(1.0, -24));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    double ulp = ldexp(1.0, e - 1 - 10);
+    double n = nearbyint(a / ulp); /* in [1024, 2048] */
+    uint32_t bits = ((uint32_t)(e - 1 + 15) << 10) + (uint32_t)(n - 1024.0);
+    return (uint16_t)(sign | bits);
+}
+
+float orc_bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+/* fp32 -> bfloat16 with round-to-nearest-even (8 significant bits, fp32's
+ * exponent range, subnormal spacing 2^-133). */
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t u = f32_to_bits(f);
+    uint16_t sign = (u >> 16) & 0x8000u;
+    if (isnan(f)) return (uint16_t)(sign | 0x7fc0u);
+    double a = fabs((double)f);
+    if (isinf(f)) return (uint16_t)(sign | 0x7f80u);
+    double n;
+    uint32_t mag;
+    if (a < ldexp(1.0, -126)) {
+        n = nearbyint(a / ldexp(1.0, -133)); /* 0..128; 128 encodes 2^-126 */
+        mag = (uint32_t)n;
+    } else {
+        int e;
+        frexp(a, &e);
+        double ulp = ldexp(1.0, e - 1 - 7);
+        n = nearbyint(a / ulp); /* in [128, 256] */
+        mag = ((uint32_t)(e - 1 + 127) << 7) + (uint32_t)(n - 128.0);
+        if (mag >= 0x7f80u) mag = 0x7f80u; /* overflow to infinity */
+    }
+    return (uint16_t)(sign | mag);
+}
+
+void orc_f32_to_f16_array(const float* a, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(a[i]);
+}
+
+void orc_f32_to_bf16_array(const float* a, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(a[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Group-wise asymmetric INT4 quantizer  ([Q] "The minimum maths")           */
+/* ------------------------------------------------------------------------- */
+
+static float load_w(const void* W, int dtype, int64_t idx)
+{
+    if (dtype == ORC_F32) return ((const float*)W)[idx];
+    if (dtype == ORC_BF16) return orc_bf16_to_f32(((const uint16_t*)W)[idx]);
+    return orc_f16_to_f32(((const uint16_t*)W)[idx]);
+}
+
+/* One group of g weights -> one fp16 scale, one zero-point, g codes.
+ *   s = (max - min) / (2^4 - 1)          range over the group, widened to 0
+ *   z = round(-min / s)                  integer zero-point in [0, 15]
+ *   q = clip(round(w / s + z), 0, 15)    the encoding
+ * Returns 0, or ORC_ERANGE if the scale is not a finite fp16 number. */
+static int quantize_one_group(const float* w, int g, uint8_t* q, uint16_t* s_out, uint8_t* z_out)
+{
+    float lo = w[0], hi = w[0];
+    for (int i = 1; i < g; ++i) {
+        if (w[i] < lo) lo = w[i];
+        if (w[i] > hi) hi = w[i];
+    }
+    if (!isfinite(lo) || !isfinite(hi)) return ORC_ERANGE;
+    if (lo > 0.0f) lo = 0.0f;
+    if (hi < 0.0f) hi = 0.0f;
+
+    float range = hi - lo;          /* one fp32 subtraction */
+    float s32 = range / 15.0f;      /* one fp32 division    */
+    uint16_t sh_bits = orc_f32_to_f16(s32);
+    float sh = orc_f16_to_f32(sh_bits);
+    if (!isfinite(sh)) return ORC_ERANGE;
+
+    if (sh == 0.0f) { /* degenerate group: everything decodes to 0 */
+        *s_out = 0;
+        *z_out = 0;
+        for (int i = 0; i < g; ++i) q[i] = 0;
+        return 0;
+    }
+    *s_out = sh_bits;
+
+    float zf = nearbyintf(-lo / sh);
+    if (zf < 0.0f) zf = 0.0f;
+    if (zf > 15.0f) zf = 15.0f;
+    *z_out = (uint8_t)zf;
+
+    for (int i = 0; i < g; ++i) {
+        float t = w[i] / sh;        /* fp32 division */
+        t = t + zf;                 /* fp32 addition, not fused */
+        float r = nearbyintf(t);
+        if (r < 0.0f) r = 0.0f;
+        if (r > 15.0f) r = 15.0f;
+        q[i] = (uint8_t)r;
+    }
+    return 0;
+}
+
+int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
+                        uint8_t* q, uint16_t* s, uint8_t* z)
+{
+    if (!W || !q || !s || !z || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
+    int64_t G = K / g;
+    int status = 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        float* buf = (float*)malloc(sizeof(float) * (size_t)g);
+        for (int64_t j = 0; j < G; ++j) {
+            for (int i = 0; i < g; ++i) buf[i] = load_w(W, dtype, n * K + j * g + i);
+            int st = quantize_one_group(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* Decoding  w_hat = s * (q - z).  With an fp16 scale and |q - z| <= 15 the
+ * product has at most 15 significant bits, so it is exact in fp32. */
+int orc_dequant(const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                int64_t N, int64_t K, int g, int out_dtype, void* out)
+{
+    if (!q || !s || !z || !out || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    int64_t G = K / g;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t j = k / g;
+            float sc = orc_f16_to_f32(s[n * G + j]);
+            float d = (float)((int)q[n * K + k] - (int)z[n * G + j]);
+            float v = sc * d;
+            if (out_dtype == ORC_F32) ((float*)out)[n * K + k] = v;
+            else if (out_dtype == ORC_F16) ((uint16_t*)out)[n * K + k] = orc_f32_to_f16(v);
+            else if (out_dtype == ORC_BF16) ((uint16_t*)out)[n * K + k] = orc_f32_to_bf16(v);
+            else return ORC_EINVAL;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Packing  ([Q] "Numerical example": eight 4-bit codes take four bytes)      */
+/* ------------------------------------------------------------------------- */
+
+int orc_pack_canonical(const uint8_t* q, int64_t N, int64_t K, uint8_t* out)
+{
+    if (!q || !out || N <= 0 || K <= 0 || K % 2) return ORC_EINVAL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < K / 2; ++b)
+            out[n * (K / 2) + b] = (uint8_t)((q[n * K + 2 * b] & 15) | ((q[n * K + 2 * b + 1] & 15) << 4));
+    return 0;
+}
+
+int64_t orc_device_bytes(int64_t N, int64_t K)
+{
+    int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128;
+    return Np * Kp / 2;
+}
+
+/* Byte offset and nibble of element (n, k) in the device layout. */
+static void device_pos(int64_t n, int64_t k, int64_t K, int64_t* byte, int* high)
+{
+    int64_t KT = (K + 127) / 128;
+    int64_t nb = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
+    int64_t j = kk / 32, c = (kk % 32) / 8, e = kk % 8;
+    int64_t lane = r + 16 * c;
+    int p = (int)(4 * (e % 2) + e / 2);
+    *byte = (nb * KT + kt) * 1024 + lane * 16 + j * 4 + p / 2;
+    *high = p % 2;
+}
+
+int orc_pack_device(const uint8_t* q, int64_t N, int64_t K, uint8_t* out)
+{
+    if (!q || !out || N <= 0 || K <= 0) return ORC_EINVAL;
+    memset(out, 0, (size_t)orc_device_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t byte;
+            int high;
+            device_pos(n, k, K, &byte, &high);
+            uint8_t v = q[n * K + k] & 15;
+            out[byte] = (uint8_t)(high ? (out[byte] & 0x0f) | (v << 4) : (out[byte] & 0xf0) | v);
+        }
+    return 0;
+}
+
+int orc_unpack_device(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q)
+{
+    if (!packed || !q || N <= 0 || K <= 0) return ORC_EINVAL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t byte;
+            int high;
+            device_pos(n, k, K, &byte, &high);
+            q[n * K + k] = high ? (packed[byte] >> 4) : (packed[byte] & 15);
+        }
+    return 0;
+}
+
+int orc_pack_zeros(const uint8_t* z, int64_t N, int64_t G, uint8_t* out)
+{
+    if (!z || !out || N <= 0 || G <= 0) return ORC_EINVAL;
+    int64_t GB = (G + 1) / 2;
+    memset(out, 0, (size_t)(N * GB));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < G; ++j) {
+            uint8_t v = z[n * G + j] & 15;
+            uint8_t* b = out + n * GB + j / 2;
+            *b = (uint8_t)((j % 2) ? (*b & 0x0f) | (v << 4) : (*b & 0xf0) | v);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* The product y = x * What^T in fp64, summed in k order                     */
+/* ------------------------------------------------------------------------- */
+
+int orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const float* w_hat, double* y)
+{
+    if (!x_f16 || !w_hat || !y || M <= 0 || N <= 0 || K <= 0) return ORC_EINVAL;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)orc_f16_to_f32(x_f16[i]);
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * (double)w_hat[n * K + k];
+            y[m * N + n] = acc;
+        }
+    free(xd);
+    return 0;
+}
+
+/* Rows [n0, n0 + nrows) of the same product, quantized weights given as codes,
+ * scales and zero-points: the oracle's dequantization followed by the fp64
+ * product, one row at a time (used to check sampled outputs of large shapes). */
+int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
+                      const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                      int64_t n0, int64_t nrows, double* y_rows /* [M][nrows] */)
+{
+    if (!x_f16 || !q || !s || !z || !y_rows || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
+    int64_t G = K / g;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = n0 + i;
+        float* wr = (float*)malloc(sizeof(float) * (size_t)K);
+        orc_dequant(q + n * K, s + n * G, z + n * G, 1, K, g, ORC_F32, wr);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            y_rows[m * nrows + i] = acc;
+        }
+        free(wr);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Symmetric quantizers ([C] absmax int8; [T] symmetric b-bit), in fp64      */
+/* ------------------------------------------------------------------------- */
+
+/* Symmetric absmax: s = max|w| / (2^(b-1) - 1), q = round(w / s) clipped to
+ * +-(2^(b-1) - 1), w_hat = q * s.  b = 8 gives the int8 rule s = max|w|/127;
+ * b = 4 gives the +-7 INT4 variant. */
+int orc_symmetric(const double* w, int64_t n, int bits, int32_t* q, double* s_out, double* w_hat)
+{
+    if (!w || !q || !s_out || n <= 0 || bits < 2 || bits > 16) return ORC_EINVAL;
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) if (fabs(w[i]) > amax) amax = fabs(w[i]);
+    int32_t qmax = (1 << (bits - 1)) - 1;
+    double s = amax / (double)qmax;
+    *s_out = s;
+    for (int64_t i = 0; i < n; ++i) {
+        double r = s > 0.0 ? nearbyint(w[i] / s) : 0.0;
+        if (r > qmax) r = qmax;
+        if (r < -qmax) r = -qmax;
+        q[i] = (int32_t)r;
+        if (w_hat) w_hat[i] = r * s;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Storage accounting ([Q] "Numerical example"; [C] per-group scales)        */
+/* ------------------------------------------------------------------------- */
+
+/* Bits per weight of b-bit codes with one scale of scale_bits and one zero-point
+ * of zero_bits per group of g weights. */
+double orc_bits_per_weight(int bits, int g, int scale_bits, int zero_bits)
+{
+    return (double)bits + (double)(scale_bits + zero_bits) / (double)g;
+}
+
+/* Bytes needed to store n weights that way (groups rounded up). */
+double orc_storage_bytes(int64_t n, int bits, int g, int scale_bits, int zero_bits)
+{
+    int64_t groups = (n + g - 1) / g;
+    return ((double)n * bits + (double)groups * (scale_bits + zero_bits)) / 8.0;
+}

@@ -1,0 +1,53 @@
+/*
+ * wq_oracle.h -- declarations of the CPU oracle (test infrastructure only).
+ * The product library never includes this header.  See wq_oracle.c for the
+ * definitions, the pages each function follows and the readings it takes.
+ */
+#ifndef WQ_ORACLE_H
+#define WQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
+enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ERANGE = -6 };
+
+void orc_set_threads(int n);
+int orc_get_threads(void);
+
+float orc_f16_to_f32(uint16_t h);
+uint16_t orc_f32_to_f16(float f);
+float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float f);
+void orc_f32_to_f16_array(const float* a, int64_t n, uint16_t* out);
+void orc_f32_to_bf16_array(const float* a, int64_t n, uint16_t* out);
+
+int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
+                        uint8_t* q, uint16_t* s, uint8_t* z);
+int orc_dequant(const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                int64_t N, int64_t K, int g, int out_dtype, void* out);
+
+int orc_pack_canonical(const uint8_t* q, int64_t N, int64_t K, uint8_t* out);
+int64_t orc_device_bytes(int64_t N, int64_t K);
+int orc_pack_device(const uint8_t* q, int64_t N, int64_t K, uint8_t* out);
+int orc_unpack_device(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q);
+int orc_pack_zeros(const uint8_t* z, int64_t N, int64_t G, uint8_t* out);
+
+int orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const float* w_hat, double* y);
+int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
+                      const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                      int64_t n0, int64_t nrows, double* y_rows);
+
+int orc_symmetric(const double* w, int64_t n, int bits, int32_t* q, double* s_out, double* w_hat);
+
+double orc_bits_per_weight(int bits, int g, int scale_bits, int zero_bits);
+double orc_storage_bytes(int64_t n, int bits, int g, int scale_bits, int zero_bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,467 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+These tests never touch the HIP library.  Each one checks the oracle against
+something other than itself: numbers printed on the pages (fixtures under
+tests/golden/, each with its citation), exact rational arithmetic, an
+independent library conversion, or an invariant that a dropped term, a wrong
+sign, a wrong index or a transposed operand would break.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+import workloads
+
+
+# --------------------------------------------------------------------------
+# The 8-weight INT4 worked example (quantization post, "Numerical example")
+# --------------------------------------------------------------------------
+
+def _example(orc, pad_to=None):
+    w = np.array(workloads.WORKED_EXAMPLE_W, np.float32)
+    if pad_to:
+        w = np.concatenate([w, np.zeros(pad_to - w.size, np.float32)])
+    q, s, z = orc.quantize_groups(w[None, :], w.size)
+    return w, q[0], s[0, 0], z[0, 0]
+
+
+def test_worked_example_codes_scale_zero(orc):
+    g = golden("int4_worked_example.json")["printed"]
+    w, q, s_bits, z = _example(orc)
+    assert list(q) == g["q"] == g["round"]
+    assert z == g["z"]
+    s = float(np.uint16(s_bits).view(np.float16))
+    assert round(s, g["s_decimals"]) == g["s"]
+    # the real-valued zero-point printed before rounding: -min/s
+    assert abs(-g["min"] / s - g["z_real"]) < 0.005
+    assert abs((g["max"] - g["min"]) - g["range"]) < 1e-12
+
+
+def test_worked_example_dequant_error_mse(orc):
+    g = golden("int4_worked_example.json")["printed"]
+    w, q, s_bits, z = _example(orc)
+    w_hat = orc.dequant(q[None], np.array([[s_bits]], np.uint16), np.array([[z]], np.uint8), 8)[0]
+    tol = 10.0 ** -g["decimals"]  # printed to 3 decimals (the page rounds s to 0.1553)
+    assert np.all(np.abs(w_hat - np.array(g["w_hat"])) <= tol)
+    err = w_hat.astype(np.float64) - w.astype(np.float64)
+    assert np.all(np.abs(err - np.array(g["error"])) <= tol)
+    mse = float(np.mean(err ** 2))
+    assert round(mse, 4) == g["mse_approx"]
+
+
+def test_worked_example_encode_column(orc):
+    """The printed w/s+z column agrees with the oracle's stored scale to the
+    printed precision, except the one misprinted entry, which still encodes to 0."""
+    g = golden("int4_worked_example.json")["printed"]
+    w, q, s_bits, z = _example(orc)
+    s = np.float32(np.uint16(s_bits).view(np.float16))
+    t = (w / s + np.float32(z)).astype(np.float64)
+    printed = np.array(g["w_over_s_plus_z"])
+    ok = np.abs(t - printed) <= 0.01
+    assert list(np.nonzero(~ok)[0]) == [5]
+    assert q[5] == 0 and t[5] > 0
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_worked_example_padded_to_real_group(orc, group):
+    """Zero padding to a real group size keeps min, max, s and z; pads get code z."""
+    _, q8, s8, z8 = _example(orc)
+    _, q, s, z = _example(orc, pad_to=group)
+    assert s == s8 and z == z8
+    assert list(q[:8]) == list(q8)
+    assert np.all(q[8:] == z8)
+
+
+def test_worked_example_storage(orc):
+    g = golden("int4_worked_example.json")["printed"]
+    parts = g["storage_parts_bytes"]
+    n = len(g["q"])
+    b = orc.storage_bytes(n, 4, n, scale_bits=16, zero_bits=4)
+    assert b == parts["codes"] + parts["scale_bf16"] + parts["zero_int4"] == g["storage_bytes_quantized_approx"]
+    assert round(g["storage_bytes_bf16_weights"] / b, 1) == g["reduction_factor_approx"]
+
+
+# --------------------------------------------------------------------------
+# Bits per weight (Cruxly lesson, granularity and memory arithmetic)
+# --------------------------------------------------------------------------
+
+def test_bits_per_weight(orc):
+    g = golden("bits_per_weight.json")["printed"]
+    b128 = orc.bits_per_weight(4, 128, 16, 0)
+    b32 = orc.bits_per_weight(4, 32, 16, 0)
+    assert b128 == g["g128_bits"] and b32 == g["g32_bits"]
+    assert round(g["params_70b"] * b128 / 8 / 1e9, g["gb_decimals"]) == g["g128_gb"]
+    assert round(g["params_70b"] * b32 / 8 / 1e9, g["gb_decimals"]) == g["g32_gb"]
+    # storage of the 70B model computed by groups agrees with bits/weight
+    assert orc.storage_bytes(int(g["params_70b"]), 4, 128, 16, 0) == pytest.approx(g["params_70b"] * b128 / 8)
+    # counting the 4-bit zero-point as well (what this library stores)
+    assert orc.bits_per_weight(4, 128, 16, 4) == 4.15625
+    assert orc.bits_per_weight(4, 32, 16, 4) == 4.625
+
+
+# --------------------------------------------------------------------------
+# Symmetric quantizers (absmax int8 and +-7 INT4)
+# --------------------------------------------------------------------------
+
+def test_absmax_int8_example(orc):
+    g = golden("int8_absmax_example.json")
+    w = np.array(g["w"])
+    q, s, w_hat = orc.symmetric(w, 8)
+    assert s == pytest.approx(np.max(np.abs(w)) / g["printed"]["qmax"], rel=0, abs=0)
+    assert list(q) == [17, -71, 47, 127]
+    rel = np.abs(w_hat - w) / np.abs(w)
+    assert rel.max() < 0.01  # the page: error below one percent
+    w2 = np.concatenate([w, [g["outlier"]]])
+    q2, s2, w_hat2 = orc.symmetric(w2, 8)
+    assert round(s2, 4) == g["printed"]["s_with_outlier"]
+    assert s2 == 20.0 / 127.0
+    assert q2[-1] == 127
+    rel2 = abs(w_hat2[0] - w2[0]) / abs(w2[0])
+    assert round(100 * rel2) == g["printed"]["relative_error_with_outlier_percent"]
+
+
+def test_symmetric_int4_outlier(orc):
+    g = golden("symmetric_int4_outlier.json")
+    rng = np.random.default_rng(7)
+    for case in g["cases"]:
+        M = case["M"]
+        w = np.concatenate([rng.uniform(-M, M, 63), [M]])
+        q, s, w_hat = orc.symmetric(w, g["bits"])
+        assert s == M / g["levels"]
+        assert round(s, 2 if M > 2 else 3) == case["s_approx"]
+        assert round(s / 2, 2 if M > 2 else 3) == case["half_step_approx"]
+        assert round(100 * s / 2) == case["relative_error_of_unit_value_percent"]
+        assert np.all(np.abs(q) <= g["levels"])
+        assert np.all(np.abs(w - w_hat) <= s / 2 * (1 + 1e-12))
+
+
+# --------------------------------------------------------------------------
+# Number formats against independent implementations
+# --------------------------------------------------------------------------
+
+def test_f32_to_f16_against_numpy_structured(orc):
+    """Every sign/exponent/top-mantissa combination with the low 13 bits set to
+    the values that decide rounding, plus the whole fp16-subnormal input range."""
+    hi = np.arange(1 << 19, dtype=np.uint32) << np.uint32(13)
+    lows = np.array([0, 1, 0x7FF, 0xFFF, 0x1000, 0x1001, 0x17FF, 0x1FFF], np.uint32)
+    bits = (hi[:, None] | lows[None, :]).ravel()
+    sub = np.arange(0x33000000 - 64, 0x38800000 + 64, 3, dtype=np.uint32)
+    bits = np.concatenate([bits, sub, sub | np.uint32(0x80000000)])
+    f = bits.view(np.float32)
+    ours = orc.f32_to_f16_bits(f)
+    ref = f.astype(np.float16).view(np.uint16)
+    nan = np.isnan(f)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.all((ours[nan] & 0x7C00) == 0x7C00) and np.all((ours[nan] & 0x3FF) != 0)
+
+
+def test_f32_to_f16_random_exhaustive_sample(orc):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    nan = np.isnan(f)
+    assert np.array_equal(orc.f32_to_f16_bits(f)[~nan], f.astype(np.float16).view(np.uint16)[~nan])
+
+
+def test_f16_to_f32_exhaustive(orc):
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = orc.f16_bits_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.all(np.isnan(ours[nan]))
+
+
+def test_f32_to_bf16_against_torch(orc):
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x18000 & 0xFFFF], np.uint32)
+    bits = (hi[:, None] | lows[None, :]).ravel()
+    f = bits.view(np.float32)
+    keep = ~np.isnan(f)
+    f = f[keep]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16_bits(f), ref)
+
+
+# --------------------------------------------------------------------------
+# Quantizer: constructed cases and invariants
+# --------------------------------------------------------------------------
+
+def test_ties_round_half_to_even(orc):
+    """s = 0.25 and z = 4 exactly (min -1, max 2.75); these weights put w/s + z
+    exactly on k + 1/2, where round-half-to-even and round-half-up differ."""
+    base = [-1.0, 2.75]
+    ties = [0.125, 0.375, -0.875, 2.625, 0.625, -0.125]
+    expect = [4, 6, 0, 14, 6, 4]  # 4.5->4, 5.5->6, 0.5->0, 14.5->14, 6.5->6, 3.5->4
+    w = np.array([base + ties], np.float32)
+    q, s, z = orc.quantize_groups(w, w.shape[1])
+    assert s[0, 0] == np.float16(0.25).view(np.uint16) and z[0, 0] == 4
+    assert list(q[0, 2:]) == expect
+    assert list(q[0, :2]) == [0, 15]
+
+
+def test_zero_point_tie_rounds_to_even(orc):
+    """min -1.125, max 2.625: s = 0.25 exactly and -min/s = 4.5 exactly, so the
+    zero-point is 4 under round-half-to-even (5 under round-half-up)."""
+    w = np.array([[-1.125, 2.625, 0.0, 1.0]], np.float32)
+    q, s, z = orc.quantize_groups(w, 4)
+    assert s[0, 0] == np.float16(0.25).view(np.uint16)
+    assert z[0, 0] == 4
+    # -4.5 + 4 = -0.5 -> 0 and 10.5 + 4 = 14.5 -> 14 (ties again), 1/0.25 + 4 = 8
+    assert list(q[0]) == [0, 14, 4, 8]
+
+
+def test_encode_uses_the_stored_fp16_scale(orc):
+    """Range 3.8 gives s32 = 0.25333.. which fp16 rounds up to s_h = 0.25341797.
+    A weight between 6.5*s32 and 6.5*s_h encodes to z+6 with the stored scale
+    and to z+7 with the unrounded one."""
+    s32 = np.float32(3.8) / np.float32(15.0)
+    s_h = np.float32(np.float16(s32))
+    assert s_h > s32
+    w_mid = np.float32(6.5 * (float(s32) + float(s_h)) / 2)
+    w = np.array([[-1.0, 2.8, w_mid, 0.0]], np.float32)
+    q, s, z = orc.quantize_groups(w, 4)
+    assert s[0, 0] == np.float16(s32).view(np.uint16) and z[0, 0] == 4
+    assert q[0, 2] == 10
+
+
+def test_degenerate_and_one_signed_groups(orc):
+    g = 32
+    zeros = np.zeros(g, np.float32)
+    const_pos = np.full(g, 0.3, np.float32)
+    const_neg = np.full(g, -0.3, np.float32)
+    all_pos = np.linspace(0.1, 0.5, g).astype(np.float32)
+    all_neg = -all_pos
+    tiny = np.full(g, 1e-9, np.float32)  # range/15 rounds to fp16 zero
+    W = np.stack([zeros, const_pos, const_neg, all_pos, all_neg, tiny])
+    q, s, z = orc.quantize_groups(W, g)
+    assert s[0, 0] == 0 and z[0, 0] == 0 and np.all(q[0] == 0)
+    assert s[5, 0] == 0 and z[5, 0] == 0 and np.all(q[5] == 0)
+    # constant positive: range [0, 0.3] -> z = 0, every code 15
+    assert z[1, 0] == 0 and np.all(q[1] == 15)
+    # constant negative: range [-0.3, 0] -> z = 15, every code 0
+    assert z[2, 0] == 15 and np.all(q[2] == 0)
+    assert z[3, 0] == 0 and q[3, -1] == 15
+    assert z[4, 0] == 15 and q[4, -1] == 0
+    w_hat = orc.dequant(q, s, z, g)
+    assert np.all(w_hat[0] == 0)
+    np.testing.assert_allclose(w_hat[1], 0.3, rtol=2e-3)
+    np.testing.assert_allclose(w_hat[2], -0.3, rtol=2e-3)
+
+
+def test_subnormal_scale(orc):
+    """A group whose scale is an fp16 subnormal keeps it (no flush to zero)."""
+    w = np.array([[-3e-6, 0.0, 2e-6, 5e-6]], np.float32)
+    q, s, z = orc.quantize_groups(w, 4)
+    assert 0 < s[0, 0] < 0x0400
+    sh = float(np.uint16(s[0, 0]).view(np.float16))
+    assert abs(sh - np.float16(np.float32(8e-6) / np.float32(15.0))) == 0
+
+
+def test_nonfinite_scale_is_an_error(orc):
+    w = np.array([[-5e5, 5e5, 0.0, 1.0]], np.float32)
+    with pytest.raises(orc.OracleError):
+        orc.quantize_groups(w, 4)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantizer_invariants(orc, group):
+    N, K = 24, 1024
+    W = workloads.bf16_bits_to_f32(workloads.gen_weights(11, N, K, outlier_frac=0.01))
+    q, s, z = orc.quantize_groups(W, group)
+    assert q.max() <= 15 and z.max() <= 15
+    sh = s.view(np.float16).astype(np.float64)
+    w_hat = orc.dequant(q, s, z, group).astype(np.float64)
+    # error bound: half a step plus what rounding the scale to fp16 can move
+    # the clipped top code (15 steps of |s32 - s_h|), plus fp32 rounding slack
+    Wg = W.reshape(N, K // group, group).astype(np.float64)
+    lo = np.minimum(Wg.min(-1), 0)
+    hi = np.maximum(Wg.max(-1), 0)
+    s32 = (hi - lo) / 15
+    bound = sh / 2 + 15 * np.abs(s32 - sh) + 1e-6 * sh
+    err = np.abs(Wg - w_hat.reshape(Wg.shape)).max(-1)
+    assert np.all(err <= bound)
+    # the reconstruction reaches both ends of every group's (widened) range
+    assert np.all(np.abs(w_hat.reshape(Wg.shape).max(-1) - hi) <= sh)
+    assert np.all(np.abs(w_hat.reshape(Wg.shape).min(-1) - lo) <= sh)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_requantize_is_identity(orc, group):
+    """Quantizing w_hat again returns the same codes, scales and zero-points in
+    every group whose codes reach both 0 and 15 (15*s_h is exact in fp32)."""
+    W = workloads.bf16_bits_to_f32(workloads.gen_weights(12, 16, 512, outlier_frac=0.01))
+    q, s, z = orc.quantize_groups(W, group)
+    w_hat = orc.dequant(q, s, z, group)
+    q2, s2, z2 = orc.quantize_groups(w_hat, group)
+    G = 512 // group
+    full = (q.reshape(16, G, group).min(-1) == 0) & (q.reshape(16, G, group).max(-1) == 15)
+    assert full.mean() > 0.5
+    assert np.array_equal(s2[full], s[full]) and np.array_equal(z2[full], z[full])
+    assert np.array_equal(q2.reshape(16, G, group)[full], q.reshape(16, G, group)[full])
+
+
+def test_permutation_within_group(orc):
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((4, 128)).astype(np.float32)
+    perm = rng.permutation(128)
+    q, s, z = orc.quantize_groups(W, 128)
+    qp, sp, zp = orc.quantize_groups(np.ascontiguousarray(W[:, perm]), 128)
+    assert np.array_equal(qp, q[:, perm]) and np.array_equal(sp, s) and np.array_equal(zp, z)
+
+
+def test_rows_and_groups_are_independent(orc):
+    """Changing one group changes only that group's outputs (catches a wrong
+    row or group index)."""
+    W = workloads.bf16_bits_to_f32(workloads.gen_weights(13, 8, 256, outlier_frac=0.0))
+    q, s, z = orc.quantize_groups(W, 32)
+    W2 = W.copy()
+    W2[5, 64:96] *= 3.0
+    q2, s2, z2 = orc.quantize_groups(W2, 32)
+    diff_s = s2 != s
+    assert diff_s[5, 2] and diff_s.sum() == 1
+    mask = np.ones_like(q, bool)
+    mask[5, 64:96] = False
+    assert np.array_equal(q2[mask], q[mask])
+
+
+def test_bf16_and_f32_inputs_agree(orc):
+    b = workloads.gen_weights(14, 8, 256, outlier_frac=0.01)
+    f = workloads.bf16_bits_to_f32(b)
+    r1 = orc.quantize_groups(b, 128, dtype=orc.BF16)
+    r2 = orc.quantize_groups(f, 128)
+    for a, c in zip(r1, r2):
+        assert np.array_equal(a, c)
+
+
+# --------------------------------------------------------------------------
+# Dequantization: exact in fp32, one rounding to fp16 / bf16
+# --------------------------------------------------------------------------
+
+def test_dequant_exact_all_code_pairs(orc):
+    rng = np.random.default_rng(5)
+    scales = np.concatenate([
+        np.array([0x0001, 0x0155, 0x03FF, 0x0400, 0x30F8, 0x3C00, 0x7BFF], np.uint16),
+        rng.integers(0x0001, 0x7C00, 57).astype(np.uint16),
+    ])
+    qq, zz = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
+    q = np.tile(qq.ravel().astype(np.uint8), (scales.size, 1))
+    z = np.tile(zz.ravel().astype(np.uint8), (scales.size, 1))
+    s = np.repeat(scales[:, None], 256, axis=1)
+    # one group per element: g = 1
+    f32 = orc.dequant(q, s, z, 1, orc.F32)
+    f16 = orc.dequant(q, s, z, 1, orc.F16)
+    b16 = orc.dequant(q, s, z, 1, orc.BF16)
+    exact = [[Fraction(float(np.uint16(sv).view(np.float16))) * (int(a) - int(b))
+              for a, b in zip(qr, zr)] for sv, qr, zr in zip(scales, q, z)]
+    exact_f = np.array([[float(v) for v in row] for row in exact])
+    assert np.array_equal(f32.astype(np.float64), exact_f)  # exact in fp32
+    assert np.array_equal(f16, exact_f.astype(np.float16).view(np.uint16))
+    ref_b = torch.from_numpy(exact_f.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16, ref_b)
+
+
+# --------------------------------------------------------------------------
+# Packing
+# --------------------------------------------------------------------------
+
+def test_pack_device_is_a_bijection(orc):
+    """Each element lands in its own nibble; pad nibbles stay zero; unpack
+    inverts pack; shapes with ragged rows and columns included."""
+    for N, K in [(16, 128), (37, 96), (5, 416)]:
+        nbytes = orc.device_bytes(N, K)
+        assert nbytes == ((N + 15) // 16 * 16) * ((K + 127) // 128 * 128) // 2
+        seen = np.zeros(2 * nbytes, np.int64)
+        # mark one element at a time in batches: code 1 at positions (n, k)
+        for n in range(N):
+            q = np.zeros((N, K), np.uint8)
+            q[n, :] = 1
+            p = orc.pack_device(q)
+            nib = np.stack([p & 15, p >> 4], axis=1).ravel()
+            assert nib.sum() == K
+            seen += nib
+        assert seen.max() == 1 and seen.sum() == N * K
+        rng = np.random.default_rng(N * K)
+        q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+        assert np.array_equal(orc.unpack_device(orc.pack_device(q), N, K), q)
+
+
+def test_pack_device_word_order(orc):
+    """Within one 32-bit word the eight columns 8c..8c+7 sit in nibbles
+    0,4,1,5,2,6,3,7 (pairs of neighbouring columns 16 bits apart)."""
+    q = np.zeros((16, 128), np.uint8)
+    q[0, :8] = np.arange(1, 9)
+    p = orc.pack_device(q)
+    word = int(p[:4].view(np.uint32)[0])
+    nibbles = [(word >> (4 * i)) & 15 for i in range(8)]
+    assert nibbles == [1, 3, 5, 7, 2, 4, 6, 8]
+    # row 3, columns 40..47 (word j=1 of lane 3 + 16*1)
+    q = np.zeros((16, 128), np.uint8)
+    q[3, 40:48] = 9
+    p = orc.pack_device(q)
+    lane = 3 + 16 * 1
+    assert np.all(p[lane * 16 + 4: lane * 16 + 8] == 0x99)
+    assert p.sum() == 4 * 0x99
+
+
+def test_pack_canonical_and_zeros(orc):
+    q = np.array([[1, 2, 3, 4]], np.uint8)
+    assert list(orc.pack_canonical(q)[0]) == [0x21, 0x43]
+    z = np.array([[5, 6, 7]], np.uint8)
+    assert list(orc.pack_zeros(z)[0]) == [0x65, 0x07]
+
+
+# --------------------------------------------------------------------------
+# The product: brute force against exact rational arithmetic
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 3, 8), (3, 5, 16), (2, 7, 64)])
+def test_gemm_f64_brute_force_exact(orc, M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = orc.gemm_f64(x, w)
+    xf = x.view(np.float16)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(w[n, k])) for k in range(K))
+            mag = sum(abs(float(xf[m, k]) * float(w[n, k])) for k in range(K))
+            assert abs(float(exact) - y[m, n]) <= K * 2.0 ** -52 * mag
+
+
+def test_gemm_rows_matches_full(orc):
+    rng = np.random.default_rng(9)
+    M, N, K, g = 3, 40, 256, 32
+    W = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    q, s, z = orc.quantize_groups(W, g)
+    y = orc.gemm_f64(x, orc.dequant(q, s, z, g))
+    assert np.array_equal(orc.gemm_rows_f64(x, q, s, z, g, 10, 17), y[:, 10:27])
+
+
+def test_one_hot_activation_selects_a_weight(orc):
+    rng = np.random.default_rng(10)
+    W = rng.standard_normal((6, 128)).astype(np.float32)
+    q, s, z = orc.quantize_groups(W, 32)
+    w_hat = orc.dequant(q, s, z, 32)
+    x = np.zeros((1, 128), np.float32)
+    x[0, 77] = 1.0
+    y = orc.gemm_f64(workloads.f32_to_f16_bits(x), w_hat)
+    assert np.array_equal(y[0], w_hat[:, 77].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# Roofline arithmetic (Cruxly lesson, roofline paragraph)
+# --------------------------------------------------------------------------
+
+def test_roofline_numbers():
+    g = golden("roofline.json")
+    ridge = g["assumed"]["tflops"] / g["assumed"]["tbps"]
+    assert round(ridge) == g["printed"]["ridge_flop_per_byte"]
+    # fp16: 2 FLOP per weight per batch row over 2 bytes -> batch FLOP/byte
+    assert round(ridge / 100) * 100 == g["printed"]["fp16_crossover_batch_about"]
+    # 4-bit: 2 FLOP per batch row over half a byte -> 4 * batch FLOP/byte
+    assert round(ridge / 4) == g["printed"]["int4_crossover_batch"]
