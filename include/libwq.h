@@ -1,0 +1,158 @@
+/*
+ * libwq -- group-wise asymmetric INT4 weight quantization and the fused
+ * dequantize-and-multiply y = x * What^T for AMD Instinct MI355X (gfx950).
+ *
+ * The method (from "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ) and
+ * GGUF - the model's accounting zoom", section "The minimum maths: scale and
+ * zero-point"): a weight row is cut into groups of g consecutive weights along
+ * K; each group gets a scale s = (max - min) / 15 and an integer zero-point
+ * z = round(-min / s), each weight the 4-bit code q = clip(round(w/s + z), 0, 15),
+ * and decoding is What = s * (q - z).  The matrix product with fp16 activations
+ * is the weight-only ("W4A16") matmul that decode runs as a memory-bound GEMV
+ * and large batches run as a dense GEMM ("Quantization Methods Compared: INT8,
+ * GPTQ, AWQ, FP8, FP4 and KV-Cache Quantization", section "Hardware, formats and
+ * the roofline: why INT4 gave no speedup at batch 128": kernels dequantize to
+ * fp16 inside the matmul).
+ *
+ * Numerics fixed by this library where the pages leave them open:
+ *   - the scale is stored as IEEE fp16, converted from the fp32 value
+ *     fl32(fl32(hi - lo) / 15) with round-to-nearest-even, subnormals kept,
+ *     where lo = min(0, min of group) and hi = max(0, max of group);
+ *   - z = clamp(rne(fl32(-lo / s)), 0, 15) and
+ *     q = clamp(rne(fl32(fl32(w / s) + z)), 0, 15), with s the stored fp16 scale,
+ *     every operation a single correctly rounded binary32 operation;
+ *   - a group whose fp16 scale is 0 stores s = 0, z = 0 and codes 0;
+ *   - What = s * (q - z) is exact in fp32; fp16 and bf16 outputs are one
+ *     round-to-nearest-even of that value;
+ *   - y is fp16 (round-to-nearest-even) of an fp32 accumulation.
+ *
+ * Layouts (all row-major, the weight matrix is W[N][K]: row = output channel):
+ *   x        [M][K] fp16                        activations
+ *   y        [M][N] fp16                        outputs
+ *   s_f16    [N][G] fp16 bit patterns, G = K / group
+ *   z_codes  [N][G] uint8, values 0..15          (unpacked zero-points)
+ *   q_codes  [N][K] uint8, values 0..15          (unpacked codes)
+ *   zpacked  [N][ceil(G/2)] bytes, group j in the low nibble of byte j/2 when j
+ *            is even, in the high nibble when j is odd
+ *   qpacked  device tile layout: rows padded to Np = ceil(N/16)*16, columns to
+ *            Kp = ceil(K/128)*128 (pad codes are 0); tile (nb, kt) of 16 rows x
+ *            128 columns occupies 1024 bytes at byte offset
+ *            (nb * Kp/128 + kt) * 1024; inside it, "lane" l = r + 16*c
+ *            (r = 0..15 row in tile, c = 0..3) owns the 16 bytes at 16*l, read
+ *            as four little-endian 32-bit words j = 0..3; word j holds columns
+ *            32*j + 8*c + e (e = 0..7) of the tile, column e in nibble
+ *            4*(e%2) + e/2 (so a word splits into four fp16 pairs of
+ *            neighbouring columns with one shift and mask each).
+ *
+ * Conventions:
+ *   - Every pointer argument is device memory (hipMalloc or equivalent) unless
+ *     stated otherwise.  The caller owns every buffer; libwq allocates nothing.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued asynchronously on it; no call synchronizes.
+ *   - Return values: WQ_OK, or a negative wq_status.  Argument errors are
+ *     detected on the host before anything is enqueued.  WQ_EHIP reports a
+ *     failed launch (including an asynchronous error left by earlier work).
+ *   - Preconditions not checked on the fast path: weights are finite and every
+ *     group's range is below 15 * 65520 (so the fp16 scale is finite); codes
+ *     and zero-points passed to wq_pack_int4 are 0..15 (higher bits ignored);
+ *     buffers do not overlap.
+ *   - libwq keeps no state; calls on different streams may run concurrently
+ *     as long as they do not share output or workspace buffers.
+ */
+#ifndef LIBWQ_H
+#define LIBWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ_OK = 0,
+    WQ_EINVAL = -1,       /* null pointer, non-positive size, bad dtype or path */
+    WQ_EUNSUPPORTED = -2, /* group not 32 or 128, or K not a multiple of group */
+    WQ_EALIGN = -3,       /* pointer not aligned as documented */
+    WQ_EWORKSPACE = -4,   /* workspace missing or smaller than required */
+    WQ_EHIP = -5          /* a HIP runtime call or kernel launch failed */
+} wq_status;
+
+typedef enum { WQ_F32 = 0, WQ_BF16 = 1, WQ_F16 = 2 } wq_dtype;
+
+typedef enum {
+    WQ_PATH_AUTO = 0, /* M < 64: GEMV kernel; M >= 64: MFMA GEMM kernel */
+    WQ_PATH_GEMV = 1, /* force the split-K VALU GEMV kernel (any M) */
+    WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
+} wq_path;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int wq_version(void);
+
+/* Static string describing a status code. */
+const char* wq_strerror(int status);
+
+/* Byte sizes of the device layouts for an [N][K] weight matrix with the given
+ * group: qpacked (tile layout, padded), s_f16 ([N][G] fp16) and zpacked
+ * ([N][ceil(G/2)]).  Host-only.  Any output pointer may be NULL. */
+int wq_layout_bytes(int64_t N, int64_t K, int group,
+                    size_t* qpacked_bytes, size_t* s_bytes, size_t* zpacked_bytes);
+
+/* Group quantization (steps: per-group min/max, scale and zero-point, encoding,
+ * packing) -- "The minimum maths: scale and zero-point", equations for s, z and
+ * the encoding, with the readings listed above.
+ *   W        [N][K] weights, w_dtype WQ_F32, WQ_BF16 or WQ_F16; 16-byte aligned,
+ *            K * element size a multiple of 16 bytes when K > group
+ *   s_f16    [N][G] output scales (required, 2-byte aligned)
+ *   q_codes  [N][K] output codes, or NULL
+ *   z_codes  [N][G] output zero-points, or NULL
+ *   qpacked  tile-layout output codes (wq_layout_bytes), 16-byte aligned, or NULL
+ *   zpacked  [N][ceil(G/2)] output packed zero-points, or NULL
+ * Deterministic: the same input gives the same bytes on every run. */
+int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group,
+                       uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
+                       uint32_t* qpacked, uint8_t* zpacked, void* stream);
+
+/* Packing of codes and zero-points into the device layouts -- "Numerical
+ * example" (eight 4-bit codes occupy four bytes; a 4-bit zero-point takes half
+ * a byte).  q_codes [N][K] and z_codes [N][G] in, qpacked (16-byte aligned,
+ * padding written as 0) and zpacked out. */
+int wq_pack_int4(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group,
+                 uint32_t* qpacked, uint8_t* zpacked, void* stream);
+
+/* Dequantization What = s * (q - z) -- "The minimum maths", decoding equation.
+ * Writes W_hat [N][K] as out_dtype (WQ_F32 exact; WQ_F16 / WQ_BF16 one
+ * round-to-nearest-even of the exact value).  W_hat 16-byte aligned. */
+int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zpacked,
+               int64_t N, int64_t K, int group, int out_dtype, void* W_hat, void* stream);
+
+/* Workspace bytes wq_gemm_w4a16 needs for this shape (may be 0).  Host-only. */
+size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+
+/* y = x * What^T with What = s * (q - z) dequantized inside the kernel -- the
+ * fused weight-only matmul of "Hardware, formats and the roofline".  M < 64
+ * runs the split-K GEMV kernel, M >= 64 the MFMA tile GEMM kernel.
+ *   x_f16     [M][K] fp16, 16-byte aligned, finite
+ *   qpacked   tile-layout codes, 16-byte aligned; s_f16 [N][G]; zpacked [N][ceil(G/2)]
+ *   y_f16     [M][N] fp16 output, 2-byte aligned
+ *   workspace at least wq_gemm_workspace_bytes(M, N, K, group) bytes of device
+ *             memory, 256-byte aligned, zero-filled before its first use (libwq
+ *             leaves it zero-filled again at the end of every call); may be NULL
+ *             when that size is 0.  Concurrent calls need separate workspaces.
+ * Results are deterministic (fixed summation order). */
+int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group,
+                  const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,
+                  const uint8_t* zpacked, uint16_t* y_f16,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* As wq_gemm_w4a16, with the kernel family chosen by `path` (wq_path). */
+int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group,
+                     const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,
+                     const uint8_t* zpacked, uint16_t* y_f16,
+                     void* workspace, size_t workspace_bytes, int path, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBWQ_H */

@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: move seeded host inputs to the GPU,
+run the HIP path through the C ABI, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import w4a16_bit_matmul_amd as wq
+
+TOL = 1e-2  # max relative error of y, from the workload specification
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_weights(W: np.ndarray, w_dtype: str) -> torch.Tensor:
+    if w_dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(W, np.uint16).view(np.int16)).cuda()
+    return t.view(torch.bfloat16 if w_dtype == "bf16" else torch.float16)
+
+
+def to_dev_f16(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_bits, np.uint16).view(np.int16)).cuda().view(torch.float16)
+
+
+def f16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_dtype(w_dtype: str) -> int:
+    return {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[w_dtype]
+
+
+def gpu_quantize(W_host: np.ndarray, w_dtype: str, group: int):
+    Wd = to_dev_weights(W_host, w_dtype)
+    out = wq.wq_quantize_groups(Wd, group, codes=True, packed=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def assert_quantize_matches(W_host: np.ndarray, w_dtype: str, group: int, out=None):
+    """Codes, scales, zero-points and both packed layouts bit-exact vs the oracle."""
+    if out is None:
+        out = gpu_quantize(W_host, w_dtype, group)
+    q, s, z = oracle.quantize_groups(W_host, group, dtype=oracle_dtype(w_dtype))
+    s_gpu = f16_bits(out["s"])
+    assert np.array_equal(s_gpu, s), f"scales differ at {np.argwhere(s_gpu != s)[:5]}"
+    z_gpu = out["z_codes"].cpu().numpy()
+    assert np.array_equal(z_gpu, z), f"zero-points differ at {np.argwhere(z_gpu != z)[:5]}"
+    q_gpu = out["q_codes"].cpu().numpy()
+    assert np.array_equal(q_gpu, q), f"codes differ at {np.argwhere(q_gpu != q)[:5]}"
+    assert np.array_equal(out["qw"].qpacked.cpu().numpy(), oracle.pack_device(q))
+    assert np.array_equal(out["qw"].zpacked.cpu().numpy(), oracle.pack_zeros(z))
+    return q, s, z, out
+
+
+# Elementwise floors: the VALU GEMV multiplies exact codes in fp32, so its
+# elementwise error is checked down to 1e-3 of max|y|; the MFMA path rounds
+# What to fp16 for the matrix cores (relative 2^-11 per weight), so its
+# elementwise check floors at 5e-2 of max|y| (its absolute error, ~1e-4 of
+# max|y| on these inputs, is the fp16 rounding of What).
+FLOOR_GEMV = 1e-3
+FLOOR_MFMA = 5e-2
+
+
+def floor_for(path, M):
+    mfma = path == wq.WQ_PATH_MFMA or (path == wq.WQ_PATH_AUTO and M >= 64)
+    return FLOOR_MFMA if mfma else FLOOR_GEMV
+
+
+def compare_y(y_gpu: torch.Tensor, y_ref: np.ndarray, tol: float = TOL, floor_frac: float = FLOOR_MFMA):
+    """Max relative error (normwise: max|y - y_ref| / max|y_ref|, the gate) and
+    the elementwise relative error with its denominator floored at
+    floor_frac * max|y_ref|; both must be within tol."""
+    y = y_gpu.detach().float().cpu().numpy().astype(np.float64)
+    assert y.shape == y_ref.shape
+    assert np.all(np.isfinite(y))
+    err = np.abs(y - y_ref)
+    scale = np.abs(y_ref).max()
+    normwise = err.max() / scale if scale > 0 else err.max()
+    floor = max(floor_frac * scale, 1e-30)
+    elementwise = (err / np.maximum(np.abs(y_ref), floor)).max()
+    assert normwise <= tol, f"normwise relative error {normwise:.3e}"
+    assert elementwise <= tol, f"elementwise relative error {elementwise:.3e}"
+    return normwise, elementwise

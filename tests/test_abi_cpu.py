@@ -1,0 +1,111 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, and rejects bad arguments before touching the GPU (these calls never
+reach a HIP launch, so they run without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import w4a16_bit_matmul_amd as wq
+
+HEADER = os.path.join(ROOT, "include", "libwq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("wq_quantize_groups", "wq_pack_int4", "wq_dequant", "wq_gemm_w4a16"):
+        assert required in names
+    assert set(names) == set(wq.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = wq.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror():
+    assert wq.wq_version() >= 100
+    for st in (0, -1, -2, -3, -4, -5):
+        assert len(wq.strerror(st)) > 5
+    assert wq.strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K,g", [(8192, 8192, 128), (37, 96, 32), (1, 32, 32), (28672, 8192, 32)])
+def test_layout_bytes(N, K, g):
+    q, s, z = wq.wq_layout_bytes(N, K, g)
+    Np, Kp, G = (N + 15) // 16 * 16, (K + 127) // 128 * 128, K // g
+    assert q == Np * Kp // 2 and s == 2 * N * G and z == N * ((G + 1) // 2)
+
+
+def test_layout_bytes_rejects():
+    for args, st in [((0, 128, 128), wq.WQ_EINVAL), ((16, -128, 128), wq.WQ_EINVAL),
+                     ((16, 128, 64), wq.WQ_EUNSUPPORTED), ((16, 96, 128), wq.WQ_EUNSUPPORTED)]:
+        with pytest.raises(wq.WQError) as e:
+            wq.wq_layout_bytes(*args)
+        assert e.value.status == st
+
+
+P = ctypes.c_void_p
+A = P(0x10000)      # aligned fake device address (never dereferenced)
+B = P(0x10001)      # misaligned
+
+
+def call(name, *args):
+    return getattr(wq.lib(), name)(*args)
+
+
+def test_quantize_validation():
+    f = "wq_quantize_groups"
+    assert call(f, None, 1, 16, 128, 128, None, A, None, None, None, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 128, 128, None, None, None, None, None, None) == wq.WQ_EINVAL
+    assert call(f, A, 7, 16, 128, 128, None, A, None, None, None, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 0, 128, 128, None, A, None, None, None, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 128, 64, None, A, None, None, None, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, A, 1, 16, 160, 128, None, A, None, None, None, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, B, 1, 16, 128, 128, None, A, None, None, None, None) == wq.WQ_EALIGN
+    assert call(f, A, 1, 16, 128, 128, None, A, None, B, None, None) == wq.WQ_EALIGN
+
+
+def test_pack_and_dequant_validation():
+    assert call("wq_pack_int4", None, A, 16, 128, 128, A, A, None) == wq.WQ_EINVAL
+    assert call("wq_pack_int4", A, A, 16, 100, 32, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_pack_int4", A, A, 16, 128, 128, B, A, None) == wq.WQ_EALIGN
+    assert call("wq_dequant", A, A, A, 16, 128, 128, 5, A, None) == wq.WQ_EINVAL
+    assert call("wq_dequant", A, A, A, 16, 128, 128, 0, None, None) == wq.WQ_EINVAL
+    assert call("wq_dequant", A, A, A, 16, 128, 48, 0, A, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_dequant", A, A, A, 16, 128, 128, 0, B, None) == wq.WQ_EALIGN
+
+
+def test_gemm_validation():
+    f = "wq_gemm_w4a16_ex"
+    ok = (A, A, A, A, A, None, 0)
+    assert call(f, 0, 16, 128, 128, *ok, 0, None) == wq.WQ_EINVAL
+    assert call(f, 1, 16, 128, 128, None, A, A, A, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(f, 1, 16, 128, 128, *ok, 9, None) == wq.WQ_EINVAL
+    assert call(f, 1, 16, 128, 32 * 3, *ok, 0, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, 1, 16, 100, 32, *ok, 0, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, 1, 16, 128, 128, B, A, A, A, A, None, 0, 0, None) == wq.WQ_EALIGN
+    assert call("wq_gemm_w4a16", 1, 16, 128, 128, A, A, A, A, B, None, 0, None) == wq.WQ_EALIGN
+
+
+def test_workspace_query_and_check():
+    # the query is host-only; the MFMA path asks for workspace only on shapes that split K
+    for M, N, K, g in [(128, 28672, 8192, 128), (1, 8192, 8192, 128), (128, 8192, 28672, 32)]:
+        need = wq.wq_gemm_workspace_bytes(M, N, K, g)
+        assert need >= 0
+        if need:
+            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, None, 0, wq.WQ_PATH_MFMA, None)
+            assert st == wq.WQ_EWORKSPACE
+            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, wq.WQ_PATH_MFMA, None)
+            assert st == wq.WQ_EALIGN
+    assert wq.wq_gemm_workspace_bytes(0, 16, 128, 128) == 0

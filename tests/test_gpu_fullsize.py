@@ -1,0 +1,62 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the default kernel choice): codes, scales, zero-points and
+both packed layouts bit-exact against the oracle over the whole matrix; the
+product on sampled output columns (all batch rows), each computed by the
+oracle one row of weights at a time."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_bit_matmul_amd as wq
+import workloads
+from parity import FLOOR_GEMV, FLOOR_MFMA, assert_quantize_matches, compare_y, say, to_dev_f16, to_dev_weights
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _quantized(wl):
+    """GPU quantization of a workload's weights, checked bit-exact once per
+    weight matrix (the sweep's four batch sizes share one)."""
+    key = (wl.w_seed, wl.N, wl.K, wl.group, wl.w_dtype)
+    if key not in _cache:
+        _cache.clear()
+        say(f"  generating and quantizing {wl.N}x{wl.K} g={wl.group} ({wl.w_dtype})")
+        W = wl.weights()
+        oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
+        out = wq.wq_quantize_groups(to_dev_weights(W, wl.w_dtype), wl.group, codes=True, packed=True)
+        torch.cuda.synchronize()
+        q, s, z, _ = assert_quantize_matches(W, wl.w_dtype, wl.group, out=out)
+        out.pop("q_codes")
+        _cache[key] = (q, s, z, out)
+    return _cache[key]
+
+
+def _sample_ranges(N, rng):
+    starts = sorted(set([0, N - 8] + list(rng.integers(0, N - 8, 6))))
+    return [(int(a), 8) for a in starts]
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name):
+    wl = workloads.WORKLOADS[name]
+    say(f"full-size {name}: M={wl.M} N={wl.N} K={wl.K} g={wl.group}")
+    q, s, z, out = _quantized(wl)
+    x = wl.activations()
+    ws_bytes = wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws)
+    torch.cuda.synchronize()
+    y_host = y.float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(wl.x_seed)
+    floor = FLOOR_MFMA if wl.M >= 64 else FLOOR_GEMV
+    for n0, cnt in _sample_ranges(wl.N, rng):
+        ref = oracle.gemm_rows_f64(x, q, s, z, wl.group, n0, cnt)
+        nw, ew = compare_y(torch.from_numpy(y_host[:, n0:n0 + cnt]), ref, floor_frac=floor)
+    say(f"  last sample: normwise {nw:.2e} elementwise {ew:.2e}")
+    if ws is not None:  # the workspace is left zero-filled for the next call
+        assert int(ws.count_nonzero()) == 0

@@ -1,0 +1,249 @@
+"""HIP path against the oracle, element by element, on seeded inputs small
+enough for the oracle to finish in seconds but spanning several tiles, ragged
+rows/columns/batch, both groups, all input dtypes and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_bit_matmul_amd as wq
+import workloads
+from parity import (assert_quantize_matches, compare_y, f16_bits, floor_for, gpu_quantize, say, to_dev_f16,
+                    to_dev_weights)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [  # N, K, group: ragged N (not a multiple of 16 or of any tile), K not a multiple of 128
+    (256, 1024, 128),
+    (37, 96, 32),
+    (1000, 1152, 128),
+    (130, 544, 32),
+    (16, 128, 128),
+    (1, 32, 32),
+]
+
+
+def _weights(N, K, seed, w_dtype="bf16", outliers=0.01):
+    return workloads.gen_weights(seed, N, K, outlier_frac=outliers, dtype="f32" if w_dtype == "f32" else "bf16")
+
+
+# ---------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("N,K,group", SHAPES)
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_quantize_bit_exact(N, K, group, w_dtype):
+    say(f"quantize N={N} K={K} g={group} {w_dtype}")
+    W = _weights(N, K, 100 + N + K, w_dtype)
+    assert_quantize_matches(W, w_dtype, group)
+
+
+def test_quantize_fp16_input():
+    say("quantize fp16 input")
+    W = workloads.f32_to_f16_bits(workloads.gen_weights(5, 48, 512, dtype="f32"))
+    assert_quantize_matches(W, "f16", 32)
+
+
+def test_quantize_tiny_workload():
+    w = workloads.WORKLOADS["tiny"]
+    say(f"quantize {w}")
+    assert_quantize_matches(w.weights(), "f32", w.group)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantize_worked_example_padded(group):
+    """The page's 8 weights padded with zeros to a real group, plus rows built
+    to hit the spec's special cases: rounding ties, degenerate groups, groups
+    that do not straddle zero, subnormal scales and the stored-scale encode."""
+    say(f"quantize special rows g={group}")
+    rows = []
+    ex = np.zeros(group, np.float32)
+    ex[:8] = workloads.WORKED_EXAMPLE_W
+    rows.append(ex)
+    ties = np.zeros(group, np.float32)
+    ties[:8] = [-1.0, 2.75, 0.125, 0.375, -0.875, 2.625, 0.625, -0.125]
+    rows.append(ties)
+    ztie = np.zeros(group, np.float32)
+    ztie[:4] = [-1.125, 2.625, 0.0, 1.0]
+    rows.append(ztie)
+    rows.append(np.zeros(group, np.float32))
+    rows.append(np.full(group, 0.3, np.float32))
+    rows.append(np.full(group, -0.3, np.float32))
+    rows.append(np.linspace(0.1, 0.5, group).astype(np.float32))
+    rows.append(-np.linspace(0.1, 0.5, group).astype(np.float32))
+    rows.append(np.full(group, 1e-9, np.float32))
+    sub = np.zeros(group, np.float32)
+    sub[:4] = [-3e-6, 0.0, 2e-6, 5e-6]
+    rows.append(sub)
+    s32 = np.float32(3.8) / np.float32(15.0)
+    s_h = np.float32(np.float16(s32))
+    enc = np.zeros(group, np.float32)
+    enc[:3] = [-1.0, 2.8, np.float32(6.5 * (float(s32) + float(s_h)) / 2)]
+    rows.append(enc)
+    big = np.zeros(group, np.float32)
+    big[:2] = [-4.5e5, 4.5e5]  # s = 60000 (near the fp16 limit), -min/s = 7.5 (a tie)
+    rows.append(big)
+    W = np.stack(rows)
+    q, s, z, _ = assert_quantize_matches(W, "f32", group)
+    assert list(q[0, :8]) == [8, 5, 11, 6, 15, 0, 7, 10] and z[0, 0] == 6
+
+
+# ---------------------------------------------------------------- pack / dequant
+
+@pytest.mark.parametrize("N,K,group", SHAPES)
+def test_pack_bit_exact(N, K, group):
+    say(f"pack N={N} K={K} g={group}")
+    rng = np.random.default_rng(N * 7 + K)
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    z = rng.integers(0, 16, (N, K // group)).astype(np.uint8)
+    qw = wq.wq_pack_int4(torch.from_numpy(q).cuda(), torch.from_numpy(z).cuda(), group)
+    torch.cuda.synchronize()
+    assert np.array_equal(qw.qpacked.cpu().numpy(), oracle.pack_device(q))
+    assert np.array_equal(qw.zpacked.cpu().numpy(), oracle.pack_zeros(z))
+
+
+@pytest.mark.parametrize("N,K,group", SHAPES)
+@pytest.mark.parametrize("out_dtype", ["f32", "f16", "bf16"])
+def test_dequant_bit_exact(N, K, group, out_dtype):
+    say(f"dequant N={N} K={K} g={group} -> {out_dtype}")
+    W = _weights(N, K, 200 + N + K, "f32")
+    q, s, z = oracle.quantize_groups(W, group)
+    qd = torch.from_numpy(q).cuda()
+    zd = torch.from_numpy(z).cuda()
+    qw = wq.wq_pack_int4(qd, zd, group)
+    qw.s.copy_(torch.from_numpy(s.view(np.int16)).cuda().view(torch.float16))
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
+    odt = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[out_dtype]
+    got = wq.wq_dequant(qw, tdt)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(q, s, z, group, odt)
+    got_np = got.cpu().numpy() if out_dtype == "f32" else got.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_np.view(np.uint32) if out_dtype == "f32" else got_np,
+                          ref.view(np.uint32) if out_dtype == "f32" else ref)
+
+
+def test_dequant_all_scale_and_code_pairs():
+    """Every (q, z) pair under normal, subnormal, tiny and large fp16 scales:
+    row i uses scale i; its 16 groups of 32 have zero-points 0..15 and each
+    holds the codes 0..15 twice."""
+    say("dequant code/zero/scale grid")
+    rng = np.random.default_rng(3)
+    scales = np.concatenate([np.array([0x0001, 0x03FF, 0x0400, 0x30F8, 0x3C00, 0x7BFF], np.uint16),
+                             rng.integers(1, 0x7C00, 26).astype(np.uint16)])
+    N, K, group = scales.size, 512, 32
+    q = np.tile(np.arange(16, dtype=np.uint8), (N, K // 16))
+    z = np.tile(np.arange(16, dtype=np.uint8), (N, 1))
+    s = np.repeat(scales[:, None], K // group, axis=1)
+    qw = wq.wq_pack_int4(torch.from_numpy(q).cuda(), torch.from_numpy(z).cuda(), group)
+    qw.s.copy_(torch.from_numpy(s.view(np.int16)).cuda().view(torch.float16))
+    for tdt, odt in [(torch.float32, oracle.F32), (torch.float16, oracle.F16), (torch.bfloat16, oracle.BF16)]:
+        got = wq.wq_dequant(qw, tdt)
+        torch.cuda.synchronize()
+        ref = oracle.dequant(q, s, z, group, odt)
+        if tdt == torch.float32:
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        else:
+            assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), ref)
+
+
+# ---------------------------------------------------------------- matmul
+
+MATMUL_CASES = [  # M, N, K, group
+    (1, 256, 1024, 128),
+    (1, 1000, 1152, 128),
+    (2, 130, 544, 32),
+    (3, 37, 96, 32),
+    (5, 300, 512, 32),
+    (8, 272, 640, 128),
+    (16, 512, 1024, 128),
+    (17, 100, 256, 32),
+    (33, 160, 384, 128),
+    (63, 48, 256, 32),
+    (64, 272, 640, 128),
+    (77, 130, 1024, 32),
+    (128, 512, 2048, 128),
+    (130, 100, 256, 128),
+    (200, 64, 128, 32),
+]
+
+
+def _matmul_inputs(M, N, K, group, seed):
+    W = workloads.gen_weights(seed, N, K, outlier_frac=0.01, dtype="bf16")
+    x = workloads.gen_activations(seed + 2, M, K, outlier_frac=0.01)
+    return W, x
+
+
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA, wq.WQ_PATH_AUTO])
+@pytest.mark.parametrize("M,N,K,group", MATMUL_CASES)
+def test_matmul_within_tolerance(M, N, K, group, path):
+    say(f"matmul M={M} N={N} K={K} g={group} path={path}")
+    W, x = _matmul_inputs(M, N, K, group, 300 + M + N + K)
+    out = gpu_quantize(W, "bf16", group)
+    q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16)
+    y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
+    torch.cuda.synchronize()
+    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+
+
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
+@pytest.mark.parametrize("M,N,K,group", [(1, 200, 512, 128), (16, 64, 384, 32), (128, 80, 256, 128),
+                                         (70, 48, 160, 32)])
+def test_one_hot_activations_select_weights_exactly(M, N, K, group, path):
+    """x[m] = e_{k_m}: y[m][n] must be fp16(What[n][k_m]) bit for bit; k_m runs
+    over every offset inside a 128-column tile, catching any nibble or lane
+    unpacking slip that a norm test could average away."""
+    say(f"one-hot M={M} N={N} K={K} g={group} path={path}")
+    W = workloads.gen_weights(400 + M, N, K, outlier_frac=0.01, dtype="bf16")
+    out = gpu_quantize(W, "bf16", group)
+    q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16)
+    w_hat16 = oracle.dequant(q, s, z, group, oracle.F16)
+    reps = (min(K, 256) + M - 1) // M
+    for rep in range(reps):
+        ks = (np.arange(M) + rep * M) % K
+        x = np.zeros((M, K), np.float32)
+        x[np.arange(M), ks] = 1.0
+        y = wq.wq_gemm_w4a16(to_dev_f16(workloads.f32_to_f16_bits(x)), out["qw"], path=path)
+        torch.cuda.synchronize()
+        got = f16_bits(y)
+        assert np.array_equal(got, w_hat16[:, ks].T), f"rep {rep} columns {ks[:4]}"
+
+
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
+def test_grid_exact_weights_reduce_to_fp16_gemm(path):
+    """Weights of the form 2^-6 * (c - 7) with every group holding codes 0 and 15
+    quantize losslessly, so y is an ordinary fp16 product: compare with the
+    fp64 product of the original weights and with torch.matmul."""
+    say(f"grid-exact path={path}")
+    M, N, K, group = 24, 96, 512, 32
+    rng = np.random.default_rng(17)
+    c = rng.integers(0, 16, (N, K))
+    c[:, ::group] = 0
+    c[:, 1::group] = 15
+    W = (np.ldexp(1.0, -6) * (c - 7)).astype(np.float32)
+    x = workloads.gen_activations(18, M, K)
+    out = gpu_quantize(W, "f32", group)
+    wh = wq.wq_dequant(out["qw"], torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(wh.cpu(), torch.from_numpy(W))
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
+    torch.cuda.synchronize()
+    y_ref = oracle.gemm_f64(x, W)
+    compare_y(y, y_ref, floor_frac=floor_for(path, M))
+    y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
+    compare_y(y, y_torch, floor_frac=floor_for(path, M))
+
+
+def test_repeated_calls_are_deterministic():
+    say("determinism")
+    M, N, K, group = 128, 448, 2048, 128
+    W, x = _matmul_inputs(M, N, K, group, 500)
+    out = gpu_quantize(W, "bf16", group)
+    xd = to_dev_f16(x)
+    for path in (wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA):
+        y1 = wq.wq_gemm_w4a16(xd, out["qw"], path=path)
+        y2 = wq.wq_gemm_w4a16(xd, out["qw"], path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+    out2 = gpu_quantize(W, "bf16", group)
+    assert torch.equal(out2["qw"].qpacked, out["qw"].qpacked)

@@ -1,0 +1,175 @@
+"""libwq: group-wise asymmetric INT4 weight quantization and the fused W4A16
+matmul for AMD MI355X (gfx950).
+
+This module is the thin Python binding of the C ABI declared in
+``include/libwq.h``: it marshals torch device tensors (PyTorch supplies device
+memory and streams only) into the C calls of the same names.  Every step of the
+computation runs in the HIP kernels of ``libwq.so``; there is no other path.
+If the library has not been built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2, -3, -4, -5
+WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
+WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
+
+EXPORTED = (
+    "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_pack_int4", "wq_dequant",
+    "wq_gemm_workspace_bytes", "wq_gemm_w4a16", "wq_gemm_w4a16_ex",
+)
+
+_lib = None
+
+
+class WQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libwq.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python __graft_entry__.py or "
+                          f"python w4a16_bit_matmul_amd/_build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "wq_version": (I, []),
+        "wq_strerror": (ctypes.c_char_p, [I]),
+        "wq_layout_bytes": (I, [I64, I64, I, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "wq_quantize_groups": (I, [P, I, I64, I64, I, P, P, P, P, P, P]),
+        "wq_pack_int4": (I, [P, P, I64, I64, I, P, P, P]),
+        "wq_dequant": (I, [P, P, P, I64, I64, I, I, P, P]),
+        "wq_gemm_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
+        "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().wq_strerror(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != WQ_OK:
+        raise WQError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DT = {torch.float32: WQ_F32, torch.bfloat16: WQ_BF16, torch.float16: WQ_F16}
+
+
+@dataclass
+class QuantizedWeight:
+    """Device buffers of one quantized [N][K] weight matrix."""
+    qpacked: torch.Tensor  # uint8, tile layout (wq_layout_bytes)
+    s: torch.Tensor        # float16 [N][K/group]
+    zpacked: torch.Tensor  # uint8 [N][ceil(G/2)]
+    N: int
+    K: int
+    group: int
+
+
+def wq_version() -> int:
+    return int(lib().wq_version())
+
+
+def wq_layout_bytes(N: int, K: int, group: int):
+    q, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wq_layout_bytes(N, K, group, ctypes.byref(q), ctypes.byref(s), ctypes.byref(z)), "wq_layout_bytes")
+    return q.value, s.value, z.value
+
+
+def wq_gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
+    return int(lib().wq_gemm_workspace_bytes(M, N, K, group))
+
+
+def alloc_quantized(N: int, K: int, group: int, device="cuda") -> QuantizedWeight:
+    qb, _, zb = wq_layout_bytes(N, K, group)
+    return QuantizedWeight(torch.empty(qb, dtype=torch.uint8, device=device),
+                           torch.empty((N, K // group), dtype=torch.float16, device=device),
+                           torch.empty((N, zb // N), dtype=torch.uint8, device=device), N, K, group)
+
+
+def wq_quantize_groups(W: torch.Tensor, group: int, *, codes: bool = False, packed: bool = True,
+                       out: QuantizedWeight | None = None, stream=None):
+    """Quantize W[N][K] (float32, bfloat16 or float16, on the GPU).
+
+    Returns a dict with ``s`` (fp16 [N][G]) and, as requested, ``q_codes``
+    (uint8 [N][K]), ``z_codes`` (uint8 [N][G]) and ``qw`` (QuantizedWeight with
+    the packed device layouts)."""
+    N, K = W.shape
+    G = K // group if group else 0
+    dev = W.device
+    qw = out
+    if packed and qw is None:
+        qw = alloc_quantized(N, K, group, dev)
+    s = qw.s if packed else torch.empty((N, G), dtype=torch.float16, device=dev)
+    q_codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes else None
+    z_codes = torch.empty((N, G), dtype=torch.uint8, device=dev) if codes else None
+    _check(lib().wq_quantize_groups(_ptr(W), _DT.get(W.dtype, -1), N, K, group, _ptr(q_codes), _ptr(s),
+                                    _ptr(z_codes), _ptr(qw.qpacked) if packed else None,
+                                    _ptr(qw.zpacked) if packed else None, _stream(stream)),
+           "wq_quantize_groups")
+    return {"s": s, "q_codes": q_codes, "z_codes": z_codes, "qw": qw if packed else None}
+
+
+def wq_pack_int4(q_codes: torch.Tensor, z_codes: torch.Tensor, group: int, stream=None) -> QuantizedWeight:
+    """Pack codes [N][K] and zero-points [N][G] into the device layouts (the
+    returned QuantizedWeight's ``s`` is left uninitialised)."""
+    N, K = q_codes.shape
+    qw = alloc_quantized(N, K, group, q_codes.device)
+    _check(lib().wq_pack_int4(_ptr(q_codes), _ptr(z_codes), N, K, group, _ptr(qw.qpacked), _ptr(qw.zpacked),
+                              _stream(stream)), "wq_pack_int4")
+    return qw
+
+
+def wq_dequant(qw: QuantizedWeight, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty((qw.N, qw.K), dtype=out_dtype, device=qw.qpacked.device)
+    _check(lib().wq_dequant(_ptr(qw.qpacked), _ptr(qw.s), _ptr(qw.zpacked), qw.N, qw.K, qw.group,
+                            _DT.get(out_dtype, -1), _ptr(out), _stream(stream)), "wq_dequant")
+    return out
+
+
+def wq_gemm_w4a16(x: torch.Tensor, qw: QuantizedWeight, *, y: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y[M][N] = x[M][K] * What^T, What = s * (q - z), fp16 in and out."""
+    M, K = x.shape
+    assert K == qw.K, "x and the weight disagree on K"
+    if y is None:
+        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
+    need = wq_gemm_workspace_bytes(M, qw.N, qw.K, qw.group)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    _check(lib().wq_gemm_w4a16_ex(M, qw.N, qw.K, qw.group, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s),
+                                  _ptr(qw.zpacked), _ptr(y), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  path, _stream(stream)), "wq_gemm_w4a16")
+    return y

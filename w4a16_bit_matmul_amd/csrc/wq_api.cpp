@@ -1,0 +1,120 @@
+// libwq C ABI: argument validation (host only, before anything is enqueued),
+// kernel selection and launch.  Declarations and the contract of every entry
+// point are in include/libwq.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libwq.h"
+#include "wq_kernels.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(int64_t N, int64_t K, int group) {
+  if (N <= 0 || K <= 0) return WQ_EINVAL;
+  if (group != 32 && group != 128) return WQ_EUNSUPPORTED;
+  if (K % group != 0) return WQ_EUNSUPPORTED;
+  // int32 grid dimensions and tile counts stay far below these limits
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return WQ_EINVAL;
+  return WQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int wq_version(void) { return kVersion; }
+
+const char* wq_strerror(int status) {
+  switch (status) {
+    case WQ_OK: return "success";
+    case WQ_EINVAL: return "invalid argument (null pointer, non-positive size, bad dtype or path)";
+    case WQ_EUNSUPPORTED: return "unsupported shape (group must be 32 or 128 and divide K)";
+    case WQ_EALIGN: return "pointer not aligned as required";
+    case WQ_EWORKSPACE: return "workspace missing or too small";
+    case WQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int wq_layout_bytes(int64_t N, int64_t K, int group, size_t* qpacked_bytes, size_t* s_bytes, size_t* zpacked_bytes) {
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  const int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128, G = K / group;
+  if (qpacked_bytes) *qpacked_bytes = (size_t)(Np * Kp / 2);
+  if (s_bytes) *s_bytes = (size_t)(N * G * 2);
+  if (zpacked_bytes) *zpacked_bytes = (size_t)(N * ((G + 1) / 2));
+  return WQ_OK;
+}
+
+int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+                       uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, void* stream) {
+  if (!W || !s_f16) return WQ_EINVAL;
+  if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(W, 16) || !aligned(s_f16, 2) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8)))
+    return WQ_EALIGN;
+  return hip_status(wq::launch_quantize(W, w_dtype, N, K, group, q_codes, s_f16, z_codes, qpacked, zpacked,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int wq_pack_int4(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group, uint32_t* qpacked,
+                 uint8_t* zpacked, void* stream) {
+  if (!q_codes || !z_codes || !qpacked || !zpacked) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(q_codes, 8) || !aligned(qpacked, 16)) return WQ_EALIGN;
+  return hip_status(
+      wq::launch_pack(q_codes, z_codes, N, K, group, qpacked, zpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zpacked, int64_t N, int64_t K,
+               int group, int out_dtype, void* W_hat, void* stream) {
+  if (!qpacked || !s_f16 || !zpacked || !W_hat) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16 && out_dtype != WQ_F16) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(W_hat, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_dequant(qpacked, s_f16, zpacked, N, K, group, out_dtype, W_hat,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
+  if (M <= 0 || check_shape(N, K, group)) return 0;
+  return wq::gemm_workspace_bytes(M, N, K, group);
+}
+
+int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
+                     size_t workspace_bytes, int path, void* stream) {
+  if (!x_f16 || !qpacked || !s_f16 || !zpacked || !y_f16) return WQ_EINVAL;
+  if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
+  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!mfma) return hip_status(wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, s));
+  const size_t need = wq::gemm_workspace_bytes(M, N, K, group);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
+    if (!aligned(workspace, 256)) return WQ_EALIGN;
+  }
+  return hip_status(wq::launch_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s));
+}
+
+int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
+                  const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return wq_gemm_w4a16_ex(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, workspace_bytes,
+                          WQ_PATH_AUTO, stream);
+}
+
+}  // extern "C"

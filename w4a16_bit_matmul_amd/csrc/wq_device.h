@@ -1,0 +1,75 @@
+// Device-side helpers shared by the libwq kernels (gfx950 only).
+//
+// Packed-code tile layout (one 1024-byte tile = 16 rows x 128 columns):
+//   lane l = r + 16*c owns bytes [16*l, 16*l + 16) of the tile: four 32-bit
+//   words j = 0..3; word j holds columns 32*j + 8*c + e (e = 0..7), column e in
+//   nibble 4*(e%2) + e/2.  Shifting a word right by 4*p (p = 0..3) and masking
+//   with 0x000F000F leaves the codes of columns 2p and 2p+1 in the two 16-bit
+//   halves, which is one fp16 pair after OR-ing in the exponent of 1024.0.
+//   That lane/column assignment is also the A/B operand assignment of
+//   v_mfma_f32_16x16x32_f16 (lane l: row l%16, eight k values 8*(l/16)..+7),
+//   so a word is directly one MFMA B-fragment for the k-slots of step j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 128;
+constexpr int kTileBytes = 1024;
+
+// fp16 bit pattern of 1024.0: OR-ing a 4-bit code q into the low mantissa bits
+// gives exactly 1024 + q.
+constexpr uint32_t kMagicPair = 0x64006400u;
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// (1024 + q_{2p}, 1024 + q_{2p+1}) of one packed word, p = 0..3.
+__device__ __forceinline__ h2 biased_pair(uint32_t word, int p) {
+  return as_h2(((word >> (4 * p)) & 0x000F000Fu) | kMagicPair);
+}
+
+// (1024 + 64*q_{2p}, 1024 + 64*q_{2p+1}) of one packed word, p = 0..3: the code
+// lands in mantissa bits 6..9, so the bias 1024 is small next to the code term
+// (1024 + 64*15 = 1984 < 2048 keeps every value an exact fp16 integer).
+__device__ __forceinline__ h2 biased_pair64(uint32_t word, int p) {
+  const uint32_t sh = p == 0 ? (word << 6) : p == 1 ? (word << 2) : p == 2 ? (word >> 2) : (word >> 6);
+  return as_h2((sh & 0x03C003C0u) | kMagicPair);
+}
+
+// Round-to-nearest-even fp32 -> fp16 bits.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int64_t tile_offset_bytes(int64_t nb, int64_t kt, int64_t KT) {
+  return (nb * KT + kt) * kTileBytes;
+}
+
+// Zero-point of (row n, group gi) from the packed [N][ceil(G/2)] array.
+__device__ __forceinline__ uint32_t load_zero(const uint8_t* zpacked, int64_t GB, int64_t n, int64_t gi) {
+  uint32_t b = zpacked[n * GB + (gi >> 1)];
+  return (gi & 1) ? (b >> 4) : (b & 15u);
+}
+
+}  // namespace wq

@@ -1,0 +1,27 @@
+// Launch entry points of the libwq kernels (host side of each .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+                           uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream);
+
+hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group,
+                       uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream);
+
+hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint8_t* zpacked, int64_t N, int64_t K,
+                          int group, int out_dtype, void* out, hipStream_t stream);
+
+// VALU split-K GEMV for small M.
+hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, hipStream_t stream);
+
+// MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
+
+}  // namespace wq

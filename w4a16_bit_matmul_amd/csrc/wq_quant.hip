@@ -1,0 +1,360 @@
+// Group quantization, packing and dequantization kernels (gfx950).
+//
+// Method: "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ) and GGUF -
+// the model's accounting zoom", section "The minimum maths: scale and
+// zero-point" (s = (max - min) / 15, z = round(-min / s),
+// q = clip(round(w / s + z), 0, 15), decoding s * (q - z)) and section
+// "Numerical example" (8 codes in 4 bytes, a 4-bit zero-point in half a byte).
+//
+// This translation unit is compiled with -ffp-contract=off: every fp32
+// operation below is one correctly rounded IEEE operation (division is the
+// correctly rounded HIP default), so codes, scales and zero-points are
+// bit-identical to any other implementation of the same steps.
+//
+// Work decomposition: one wavefront per (16-row block, pair of 128-column
+// tiles).  Lane l = r + 16*c reads the 32 weights of row r that its 16 bytes of
+// the packed tile hold (columns 32*j + 8*c + e), so each wave writes whole
+// 1024-byte tiles with one 16-byte store per lane, and a group's min/max is a
+// reduction over the four lanes r, r+16, r+32, r+48 (two xor-shuffles).
+#include "wq_device.h"
+#include "wq_kernels.h"
+
+namespace wq {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* W, int64_t idx, float* out) {
+  if constexpr (DT == 0) {  // fp32
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + idx);
+    float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + idx);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == 1) {  // bf16: exact widening
+        out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+      } else {  // fp16: exact widening
+        out[2 * i] = f16_bits_to_f32((uint16_t)(w[i] & 0xffffu));
+        out[2 * i + 1] = f16_bits_to_f32((uint16_t)(w[i] >> 16));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_min4(float v) {
+  v = fminf(v, __shfl_xor(v, 16));
+  v = fminf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Scale (fp16 bits), its fp32 value and the zero-point of a group whose
+// min and max are lo and hi.
+struct GroupParams {
+  uint16_t s_bits;
+  float s;
+  float z;
+};
+
+__device__ __forceinline__ GroupParams group_params(float lo, float hi) {
+  lo = fminf(lo, 0.0f);  // range widened to contain 0: z is then a code
+  hi = fmaxf(hi, 0.0f);
+  float range = hi - lo;
+  float s32 = range / 15.0f;
+  GroupParams p;
+  p.s_bits = f32_to_f16_bits(s32);
+  p.s = f16_bits_to_f32(p.s_bits);
+  if (p.s == 0.0f) {  // degenerate group: s = 0, z = 0, codes 0
+    p.s_bits = 0;
+    p.z = 0.0f;
+    return p;
+  }
+  float z = rintf(-lo / p.s);
+  p.z = fminf(fmaxf(z, 0.0f), 15.0f);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t encode(float w, const GroupParams& p) {
+  if (p.s == 0.0f) return 0u;
+  float t = w / p.s;
+  t = t + p.z;
+  float r = rintf(t);
+  r = fminf(fmaxf(r, 0.0f), 15.0f);
+  return (uint32_t)r;
+}
+
+// Nibble position of column e (0..7) inside a packed word.
+__device__ __forceinline__ int nibble_pos(int e) { return 4 * (e & 1) + (e >> 1); }
+
+template <int DT, int G>
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const void* __restrict__ W, int64_t N, int64_t K, int64_t NBLK, int64_t KT,
+    uint8_t* __restrict__ q_codes, uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_codes,
+    uint32_t* __restrict__ qpacked, uint8_t* __restrict__ zpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ST = (KT + 1) / 2;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * ST) return;  // whole wave exits together
+  const int64_t nb = item / ST, st = item % ST;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  const bool row_ok = n < N;
+  const int64_t Gtot = K / G;
+  const int64_t GB = (Gtot + 1) / 2;
+
+  uint32_t zkeep[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+
+  for (int t = 0; t < 2; ++t) {
+    const int64_t kt = 2 * st + t;
+    if (kt >= KT) break;
+    float w[4][8];
+    bool jok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+      jok[j] = row_ok && (kt * 128 + 32 * j < K);
+      if (jok[j]) {
+        load8<DT>(W, n * K + k0, w[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[j][e] = 0.0f;
+      }
+    }
+
+    GroupParams gp[4];
+    if constexpr (G == 128) {
+      float lo = w[0][0], hi = w[0][0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
+      lo = wave_min4(lo);
+      hi = wave_max4(hi);
+      GroupParams p = group_params(lo, hi);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gp[j] = p;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo = w[j][0], hi = w[j][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
+        lo = wave_min4(lo);
+        hi = wave_max4(hi);
+        gp[j] = group_params(lo, hi);
+      }
+    }
+
+    uint32_t words[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+      uint32_t codes[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        codes[e] = jok[j] ? encode(w[j][e], gp[j]) : 0u;
+        word |= codes[e] << (4 * nibble_pos(e));
+      }
+      words[j] = word;
+      if (q_codes && jok[j]) {
+        const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+        uint2 lohi;
+        lohi.x = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
+        lohi.y = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
+        *reinterpret_cast<uint2*>(q_codes + n * K + k0) = lohi;
+      }
+      zkeep[t][j] = (uint32_t)gp[j].z;
+    }
+    if (qpacked) {
+      u4 v = {words[0], words[1], words[2], words[3]};
+      *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(qpacked) + tile_offset_bytes(nb, kt, KT) + 16 * lane) = v;
+    }
+    if (row_ok) {
+      if constexpr (G == 128) {
+        if (c == 0) {
+          s_out[n * Gtot + kt] = gp[0].s_bits;
+          if (z_codes) z_codes[n * Gtot + kt] = (uint8_t)gp[0].z;
+        }
+      } else {
+        // lane c writes group j = c of this tile
+        const int64_t gi = kt * 4 + c;
+        if (gi < Gtot) {
+          uint16_t sb = c == 0 ? gp[0].s_bits : c == 1 ? gp[1].s_bits : c == 2 ? gp[2].s_bits : gp[3].s_bits;
+          float zz = c == 0 ? gp[0].z : c == 1 ? gp[1].z : c == 2 ? gp[2].z : gp[3].z;
+          s_out[n * Gtot + gi] = sb;
+          if (z_codes) z_codes[n * Gtot + gi] = (uint8_t)zz;
+        }
+      }
+    }
+  }
+
+  if (zpacked && row_ok) {
+    if constexpr (G == 128) {
+      // groups 2*st and 2*st + 1 share byte st
+      if (c == 0 && st < GB) zpacked[n * GB + st] = (uint8_t)(zkeep[0][0] | (zkeep[1][0] << 4));
+    } else {
+      // groups 8*st .. 8*st+7 -> bytes 4*st .. 4*st+3; lane c writes byte 4*st + c
+      const int64_t b = st * 4 + c;
+      if (b < GB) {
+        const int t = c >> 1;            // tile of group 8*st + 2c
+        const int j0 = (2 * c) & 3;      // its column group inside the tile
+        uint32_t lo = zkeep[t][j0];
+        uint32_t hi = (2 * b + 1 < Gtot) ? zkeep[t][j0 + 1] : 0u;
+        zpacked[n * GB + b] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+// Codes [N][K] and zero-points [N][G] -> tile-layout codes and packed zeros.
+template <int G>
+__global__ __launch_bounds__(256) void pack_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ z_codes, int64_t N, int64_t K,
+    int64_t NBLK, int64_t KT, uint32_t* __restrict__ qpacked, uint8_t* __restrict__ zpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ST = (KT + 1) / 2;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * ST) return;
+  const int64_t nb = item / ST, st = item % ST;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  const bool row_ok = n < N;
+  const int64_t Gtot = K / G;
+  const int64_t GB = (Gtot + 1) / 2;
+
+  for (int t = 0; t < 2; ++t) {
+    const int64_t kt = 2 * st + t;
+    if (kt >= KT) break;
+    uint32_t words[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+      uint32_t word = 0;
+      if (row_ok && kt * 128 + 32 * j < K) {
+        uint2 v = *reinterpret_cast<const uint2*>(q_codes + n * K + k0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t code = ((e < 4 ? v.x >> (8 * e) : v.y >> (8 * (e - 4)))) & 15u;
+          word |= code << (4 * nibble_pos(e));
+        }
+      }
+      words[j] = word;
+    }
+    u4 out = {words[0], words[1], words[2], words[3]};
+    *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(qpacked) + tile_offset_bytes(nb, kt, KT) + 16 * lane) = out;
+  }
+  if (row_ok) {
+    // this item's 256 columns hold 256/G groups -> 128/G bytes of zpacked
+    constexpr int kBytes = 128 / G;
+    if (c < kBytes) {
+      const int64_t b = st * kBytes + c;
+      if (b < GB) {
+        uint32_t lo = z_codes[n * Gtot + 2 * b] & 15u;
+        uint32_t hi = (2 * b + 1 < Gtot) ? (z_codes[n * Gtot + 2 * b + 1] & 15u) : 0u;
+        zpacked[n * GB + b] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+// Tile-layout codes + scales + zeros -> What[N][K] = s * (q - z).
+template <int OUT, int G>
+__global__ __launch_bounds__(256) void dequant_kernel(
+    const uint32_t* __restrict__ qpacked, const uint16_t* __restrict__ s_in, const uint8_t* __restrict__ zpacked,
+    int64_t N, int64_t K, int64_t NBLK, int64_t KT, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  if (n >= N) return;
+  const int64_t Gtot = K / G;
+  const int64_t GB = (Gtot + 1) / 2;
+  const u4 v = *reinterpret_cast<const u4*>(reinterpret_cast<const uint8_t*>(qpacked) +
+                                            tile_offset_bytes(nb, kt, KT) + 16 * lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+    if (k0 >= K) continue;
+    const int64_t gi = k0 / G;
+    const float s = f16_bits_to_f32(s_in[n * Gtot + gi]);
+    const int z = (int)load_zero(zpacked, GB, n, gi);
+    const uint32_t word = v[j];
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int q = (int)((word >> (4 * nibble_pos(e))) & 15u);
+      d[e] = s * (float)(q - z);  // exact: 11-bit significand times |q - z| <= 15
+    }
+    if constexpr (OUT == 0) {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + n * K + k0);
+      o[0] = make_float4(d[0], d[1], d[2], d[3]);
+      o[1] = make_float4(d[4], d[5], d[6], d[7]);
+    } else {
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t a = OUT == 2 ? f32_to_f16_bits(d[2 * i]) : f32_to_bf16_bits(d[2 * i]);
+        uint32_t b = OUT == 2 ? f32_to_f16_bits(d[2 * i + 1]) : f32_to_bf16_bits(d[2 * i + 1]);
+        p[i] = a | (b << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + n * K + k0) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  }
+}
+
+inline int64_t blocks_for(int64_t waves) { return (waves + kWavesPerBlock - 1) / kWavesPerBlock; }
+
+}  // namespace
+
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+                           uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128, ST = (KT + 1) / 2;
+  dim3 grid((unsigned)blocks_for(NBLK * ST)), block(256);
+#define WQ_Q(DT, G) quantize_kernel<DT, G><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, s, z_codes, qpacked, zpacked)
+  if (group == 128) {
+    if (dtype == 0) WQ_Q(0, 128); else if (dtype == 1) WQ_Q(1, 128); else WQ_Q(2, 128);
+  } else {
+    if (dtype == 0) WQ_Q(0, 32); else if (dtype == 1) WQ_Q(1, 32); else WQ_Q(2, 32);
+  }
+#undef WQ_Q
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group,
+                       uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128, ST = (KT + 1) / 2;
+  dim3 grid((unsigned)blocks_for(NBLK * ST)), block(256);
+  if (group == 128)
+    pack_kernel<128><<<grid, block, 0, stream>>>(q_codes, z_codes, N, K, NBLK, KT, qpacked, zpacked);
+  else
+    pack_kernel<32><<<grid, block, 0, stream>>>(q_codes, z_codes, N, K, NBLK, KT, qpacked, zpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint8_t* zpacked, int64_t N, int64_t K,
+                          int group, int out_dtype, void* out, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+#define WQ_D(O, G) dequant_kernel<O, G><<<grid, block, 0, stream>>>(qpacked, s, zpacked, N, K, NBLK, KT, out)
+  if (group == 128) {
+    if (out_dtype == 0) WQ_D(0, 128); else if (out_dtype == 1) WQ_D(1, 128); else WQ_D(2, 128);
+  } else {
+    if (out_dtype == 0) WQ_D(0, 32); else if (out_dtype == 1) WQ_D(1, 32); else WQ_D(2, 32);
+  }
+#undef WQ_D
+  return hipGetLastError();
+}
+
+}  // namespace wq
