@@ -67,7 +67,8 @@ def _quantize_workload(wl):
 
 
 def _time_calls(fn, n_calls, warmup):
-    """Average GPU time per call from events on the launch stream."""
+    """Average time per call of n_calls back-to-back calls, from events on the
+    launch stream (torch's current stream, the one libwq is handed)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -81,40 +82,47 @@ def _time_calls(fn, n_calls, warmup):
     return e0.elapsed_time(e1) / 1e3 / n_calls  # seconds per call
 
 
-def bench_gemv(steps, warmup):
+def _time_each(fn, n_calls):
+    """Average kernel duration: an event pair on the launch stream around each
+    call, so launch gaps between calls are not counted."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def _workspace(wl):
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    n = wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+
+
+def bench_gemv(steps, warmup, name="decode_gemv"):
     import torch
     import w4a16_bit_matmul_amd as wq
     import workloads
-    wl = workloads.WORKLOADS["decode_gemv"]
+    wl = workloads.WORKLOADS[name]
     Wd, xd, qw = _quantize_workload(wl)
     del Wd
     nbytes = wl.algorithmic_bytes()
     copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
     qws = _device_copies(qw, copies)
     y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+    ws = _workspace(wl)
 
     def step(i):
-        wq.wq_gemm_w4a16(xd, qws[i % copies], y=y)
+        wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws)
 
-    # eager: one launch per step, back to back on the current stream
-    torch.cuda.synchronize()
-    t_eager = _time_calls(step, steps, warmup)
-    # the same launches replayed from a HIP graph (removes host launch gaps)
-    per_graph = copies
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(per_graph):
-            step(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        for i in range(per_graph):
-            step(i)
-    reps = max(1, math.ceil(steps / per_graph))
-    t_graph = _time_calls(lambda i: g.replay(), reps, max(1, warmup // per_graph)) / per_graph
-    return wl, nbytes, copies, t_eager, t_graph, (xd, qw, y)
+    t_step = _time_calls(step, steps, warmup)
+    t_kernel, t_kernel_med = _time_each(step, steps)
+    return wl, nbytes, copies, t_step, t_kernel, t_kernel_med
 
 
 def bench_gemm(steps, warmup):
@@ -129,12 +137,11 @@ def bench_gemm(steps, warmup):
     del Wd
     qws = _device_copies(qw, copies)
     y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
-    ws_bytes = wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    t = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws if ws_bytes else None),
-                    steps, warmup)
+    ws = _workspace(wl)
+    t = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws), steps, warmup)
+    t_kernel, _ = _time_each(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws), steps)
     t_dense = _time_calls(lambda i: torch.matmul(xd, Wf.t()), max(10, steps // 4), 3)
-    return wl, t, t_dense
+    return wl, t, t_kernel, t_dense
 
 
 def bench_quantize(wl_name="decode_gemv", reps=20):
@@ -149,39 +156,31 @@ def bench_quantize(wl_name="decode_gemv", reps=20):
     return t, moved
 
 
-def cpu_baseline(target_s=15.0):
-    """The C oracle's fused product (dequantize + fp64 dot) on a bounded sample
-    of the decode workload's rows, with all host threads."""
-    import numpy as np
+def cpu_baseline(target_s=12.0):
+    """The C oracle's fused product (dequantize each weight row, fp64 dot with
+    x) over the whole decode workload, repeated for about target_s seconds on
+    all host threads; reported in the metric's unit (algorithmic GB/s)."""
     import oracle
     import workloads
     wl = workloads.WORKLOADS["decode_gemv"]
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
-    rows = 256
-    W = workloads.gen_weights(wl.w_seed, wl.N, wl.K, outlier_frac=wl.w_outlier_frac)[:4096]
+    W = wl.weights()
     x = wl.activations()
     q, s, z = oracle.quantize_groups(W, wl.group, dtype=oracle.BF16)
-    # grow the sample until the timed call takes a meaningful time
+    reps, t0 = 0, time.perf_counter()
     while True:
-        t0 = time.perf_counter()
-        oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, rows)
+        oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
+        reps += 1
         dt = time.perf_counter() - t0
-        if dt > target_s / 4 or rows >= q.shape[0]:
+        if dt >= target_s:
             break
-        rows = min(q.shape[0], rows * 4)
-    reps = max(1, int(target_s / max(dt, 1e-3)))
-    reps = min(reps, 8)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, rows)
-    dt = (time.perf_counter() - t0) / reps
-    frac = rows / wl.N
-    bytes_sample = (wl.N * wl.K // 2 + 2 * wl.N * wl.K // wl.group + wl.N * wl.K // (2 * wl.group)) * frac \
-        + 2 * wl.K + 2 * rows
-    return {"value": round(bytes_sample / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"decode_gemv rows 0..{rows - 1} of {wl.N} (M=1, K={wl.K}, g={wl.group}), "
-                      f"C oracle dequant + fp64 dot, {reps} reps, {dt:.2f}s each"}
+    per = dt / reps
+    return {"value": round(wl.algorithmic_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole decode_gemv product (M=1, N=K={wl.K}, g={wl.group}): C oracle dequantizes each "
+                      f"row and takes fp64 dot products, {reps} repetitions in {dt:.1f}s ({per * 1e3:.1f} ms each), "
+                      f"{threads} OpenMP threads"}
 
 
 def main():
@@ -211,12 +210,11 @@ def main():
         del a, b
         log("[bench] copy probe: 3 x elementwise neg over 256 MiB (268435456 B read, 268435456 B written)")
 
-    wl, nbytes, copies, t_eager, t_graph, _ = bench_gemv(args.steps, args.warmup)
-    log(f"[bench] decode GEMV: eager {t_eager * 1e6:.2f} us/call, graph {t_graph * 1e6:.2f} us/call, "
-        f"{copies} weight copies")
-    t_step = t_eager
+    wl, nbytes, copies, t_step, t_kernel, t_kernel_med = bench_gemv(args.steps, args.warmup)
+    log(f"[bench] decode GEMV: {t_step * 1e6:.2f} us/step back to back, kernel {t_kernel * 1e6:.2f} us "
+        f"(median {t_kernel_med * 1e6:.2f}), {copies} weight copies")
     value = nbytes / t_step / 1e9
-    achieved = nbytes / t_graph / 1e9
+    achieved = nbytes / t_kernel / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -237,18 +235,21 @@ def main():
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel<MT=1>", "timing": "hip events over graph-replayed back-to-back launches",
-                     "us_per_launch": round(t_graph * 1e6, 3)},
+                     "kernel": "gemv_kernel<MT=1, RB=2, W=16, KB=4, G=128>",
+                     "timing": "mean of hip event pairs around each launch on the launch stream",
+                     "us_per_launch": round(t_kernel * 1e6, 3)},
     }
     if not args.no_extras:
-        gwl, t_gemm, t_dense = bench_gemm(max(20, args.steps // 4), max(5, args.warmup // 4))
-        tflops = gwl.flops() / t_gemm / 1e12
+        gwl, t_gemm, t_gemm_k, t_dense = bench_gemm(max(20, args.steps // 4), max(5, args.warmup // 4))
+        tflops = gwl.flops() / t_gemm_k / 1e12
         line["gemm_m128"] = {"workload": gwl.name, "M": gwl.M, "N": gwl.N, "K": gwl.K, "group": gwl.group,
-                             "us": round(t_gemm * 1e6, 2), "tflops": round(tflops, 2),
+                             "us_per_step": round(t_gemm * 1e6, 2), "us_kernel": round(t_gemm_k * 1e6, 2),
+                             "tflops": round(tflops, 2), "peak_tflops": FP16_PEAK_TFLOPS,
                              "frac_fp16_peak": round(tflops / FP16_PEAK_TFLOPS, 4),
                              "dense_fp16_torch_matmul_us": round(t_dense * 1e6, 2),
                              "dense_fp16_tflops": round(gwl.flops() / t_dense / 1e12, 2)}
-        log(f"[bench] M=128 GEMM: {t_gemm * 1e6:.1f} us, {tflops:.1f} TFLOP/s; dense fp16 {t_dense * 1e6:.1f} us")
+        log(f"[bench] M=128 GEMM: kernel {t_gemm_k * 1e6:.1f} us, {tflops:.1f} TFLOP/s; "
+            f"dense fp16 {t_dense * 1e6:.1f} us")
         tq, moved = bench_quantize()
         line["quantize"] = {"workload": "decode_gemv weights (bf16 8192x8192, g=128)", "us": round(tq * 1e6, 2),
                             "gbs": round(moved / tq / 1e9, 2)}

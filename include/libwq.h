@@ -126,7 +126,10 @@ int wq_pack_int4(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int6
 int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zpacked,
                int64_t N, int64_t K, int group, int out_dtype, void* W_hat, void* stream);
 
-/* Workspace bytes wq_gemm_w4a16 needs for this shape (may be 0).  Host-only. */
+/* Workspace bytes wq_gemm_w4a16 / wq_gemm_w4a16_ex need for this shape, enough
+ * for either kernel family (may be 0).  The GEMV needs one only when it splits
+ * K across workgroups (fp32 partial sums plus one counter per row range).
+ * Host-only. */
 size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 
 /* y = x * What^T with What = s * (q - z) dequantized inside the kernel -- the
@@ -136,9 +139,11 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
  *   qpacked   tile-layout codes, 16-byte aligned; s_f16 [N][G]; zpacked [N][ceil(G/2)]
  *   y_f16     [M][N] fp16 output, 2-byte aligned
  *   workspace at least wq_gemm_workspace_bytes(M, N, K, group) bytes of device
- *             memory, 256-byte aligned, zero-filled before its first use (libwq
- *             leaves it zero-filled again at the end of every call); may be NULL
- *             when that size is 0.  Concurrent calls need separate workspaces.
+ *             memory, 256-byte aligned and zero-filled before its first use;
+ *             may be NULL when that size is 0.  Every call leaves the bytes it
+ *             used zero-filled again, so one workspace can serve later calls of
+ *             any shape without clearing; calls that may run concurrently need
+ *             separate workspaces.
  * Results are deterministic (fixed summation order). */
 int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group,
                   const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,

@@ -99,13 +99,17 @@ def test_gemm_validation():
 
 
 def test_workspace_query_and_check():
-    # the query is host-only; the MFMA path asks for workspace only on shapes that split K
-    for M, N, K, g in [(128, 28672, 8192, 128), (1, 8192, 8192, 128), (128, 8192, 28672, 32)]:
+    # host-only: the GEMV asks for a workspace when it splits K across
+    # workgroups (few row blocks, or an x slab too large for LDS); the decode
+    # workload (M=1, N=K=8192) runs without one
+    assert wq.wq_gemm_workspace_bytes(1, 8192, 8192, 128) == 0
+    for M, N, K, g in [(1, 1024, 8192, 32), (8, 1024, 8192, 128), (1, 48, 8192, 128), (16, 64, 8192, 32)]:
         need = wq.wq_gemm_workspace_bytes(M, N, K, g)
-        assert need >= 0
-        if need:
-            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, None, 0, wq.WQ_PATH_MFMA, None)
-            assert st == wq.WQ_EWORKSPACE
-            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, wq.WQ_PATH_MFMA, None)
-            assert st == wq.WQ_EALIGN
+        assert need > 0, (M, N, K, g)
+        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, None, 0, wq.WQ_PATH_GEMV, None)
+        assert st == wq.WQ_EWORKSPACE
+        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, A, need - 1, wq.WQ_PATH_GEMV, None)
+        assert st == wq.WQ_EWORKSPACE
+        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, wq.WQ_PATH_GEMV, None)
+        assert st == wq.WQ_EALIGN
     assert wq.wq_gemm_workspace_bytes(0, 16, 128, 128) == 0

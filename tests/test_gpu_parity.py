@@ -163,6 +163,11 @@ MATMUL_CASES = [  # M, N, K, group
     (128, 512, 2048, 128),
     (130, 100, 256, 128),
     (200, 64, 128, 32),
+    # few row blocks and a long K: the GEMV splits K across workgroups
+    (1, 48, 8192, 128),
+    (2, 1000, 8192, 128),
+    (5, 100, 8192, 32),
+    (12, 40, 8192, 32),
 ]
 
 
@@ -232,6 +237,27 @@ def test_grid_exact_weights_reduce_to_fp16_gemm(path):
     compare_y(y, y_ref, floor_frac=floor_for(path, M))
     y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
     compare_y(y, y_torch, floor_frac=floor_for(path, M))
+
+
+def test_split_k_workspace_is_reusable():
+    """Split-K GEMV calls of different shapes share one workspace without
+    clearing it in between (each call leaves it zero-filled), and give the same
+    bytes as calls with a fresh zero-filled workspace."""
+    say("split-K workspace reuse")
+    cases = [(1, 48, 8192, 128), (5, 100, 8192, 32), (2, 1000, 8192, 128), (1, 48, 8192, 128)]
+    need = max(wq.wq_gemm_workspace_bytes(M, N, K, g) for M, N, K, g in cases)
+    assert need > 0
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K, g) in enumerate(cases):
+        W, x = _matmul_inputs(M, N, K, g, 600 + i)
+        out = gpu_quantize(W, "bf16", g)
+        xd = to_dev_f16(x)
+        y_shared = wq.wq_gemm_w4a16(xd, out["qw"], workspace=shared, path=wq.WQ_PATH_GEMV)
+        fresh = torch.zeros(wq.wq_gemm_workspace_bytes(M, N, K, g), dtype=torch.uint8, device="cuda")
+        y_fresh = wq.wq_gemm_w4a16(xd, out["qw"], workspace=fresh, path=wq.WQ_PATH_GEMV)
+        torch.cuda.synchronize()
+        assert torch.equal(y_shared, y_fresh), (M, N, K, g)
+        assert int(shared.count_nonzero()) == 0 and int(fresh.count_nonzero()) == 0
 
 
 def test_repeated_calls_are_deterministic():

@@ -86,8 +86,9 @@ int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zp
 }
 
 size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
-  if (M <= 0 || check_shape(N, K, group)) return 0;
-  return wq::gemm_workspace_bytes(M, N, K, group);
+  if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
+  const size_t a = wq::gemv_workspace_bytes(M, N, K, group), b = wq::gemm_workspace_bytes(M, N, K, group);
+  return a > b ? a : b;
 }
 
 int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
@@ -101,12 +102,12 @@ int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t*
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
   const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!mfma) return hip_status(wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, s));
-  const size_t need = wq::gemm_workspace_bytes(M, N, K, group);
+  const size_t need = mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
     if (!aligned(workspace, 256)) return WQ_EALIGN;
   }
+  if (!mfma) return hip_status(wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s));
   return hip_status(wq::launch_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s));
 }
 

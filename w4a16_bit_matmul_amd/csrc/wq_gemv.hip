@@ -7,192 +7,354 @@
 // with the decoding of "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ)
 // and GGUF", section "The minimum maths".
 //
-// Arithmetic: a packed word becomes four fp16 pairs (1024 + 64q) with one shift
-// and one AND-OR each; v_dot2_f32_f16 multiplies them with fp16 activation
-// pairs into fp32.  Per group,
-//   sum_k x * s * (q - z) = (s/64) * (sum_k x * (1024 + 64q) - (1024 + 64z) * sum_k x),
-// so the scale and zero-point are applied once per lane and group, not per
-// weight.  All products are exact in fp32; the sums round in fp32.  Putting
-// the code in the upper mantissa bits (64q rather than q) keeps the bias term
-// within a few times the code term, so the subtraction cancels few bits.
+// Arithmetic.  A packed word (eight 4-bit codes of one row; column e in nibble
+// 4*(e%2) + e/2) splits into four fp16 pairs with one shift and four AND-ORs:
+//   word & 0x000F000F | 0x6400 6400        = (1024 + q0,    1024 + q1)
+//   word & 0x00F000F0 | 0x6400 6400        = (1024 + 16q2,  1024 + 16q3)
+//   (word>>8) & 0x000F000F | 0x6400 6400   = (1024 + q4,    1024 + q5)
+//   (word>>8) & 0x00F000F0 | 0x6400 6400   = (1024 + 16q6,  1024 + 16q7)
+// (all exact fp16 integers).  One packed fp16 subtraction of the group's
+// (1024 + z) or (1024 + 16z) pair leaves q - z or 16(q - z), still exact, and
+// v_dot2_f32_f16 multiplies those with the matching fp16 activation pairs into
+// two fp32 sums, a1 (the q - z pairs) and a16 (the 16(q - z) pairs):
+//   sum_k x (q - z) = a1 + a16 / 16,
+// after which one fp32 multiply-add applies the group's scale.  Every product
+// is exact and no sum carries a bias that would later cancel.
 //
-// Decomposition: a workgroup owns NB consecutive 16-row blocks and MT rows of
-// x, over all of K; its waves split the 128-column tiles round-robin (split-K
-// inside the workgroup), every lane streaming 16 bytes of codes per tile.
-// Partial sums meet in LDS in a fixed order, so results are deterministic.
+// Decomposition.  A workgroup owns one 16-row block, MT rows of x and a range
+// of 128-column K tiles (all of K unless the grid splits K).  Wave w walks
+// segments of KQ consecutive K tiles (w, w + W, w + 2W, ... in segment units).
+// For each segment it first loads the segment's slice of x (one 16-byte load
+// per lane and x row), then the segment's scales and zero-points (one or two
+// vector loads per lane when the layout allows), then the KQ code tiles, and
+// copies the x slice into its own LDS region: no workgroup barrier stands
+// between the loads and the arithmetic, so each wave starts as soon as its own
+// data arrives, and with few registers two workgroups share a CU.  The waves'
+// partial sums meet in LDS in a fixed order.  When the grid splits K, each
+// workgroup writes fp32 partial sums to the workspace and the last workgroup of
+// a row range (found with a device-scope atomic counter) adds them in split
+// order and writes y, so results stay deterministic; it then zeroes the partial
+// sums and the counter, leaving the whole workspace zero for the next call.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
 namespace wq {
 namespace {
 
-__device__ __forceinline__ float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+struct GemvArgs {
+  const uint16_t* x;
+  const uint8_t* qp;
+  const uint16_t* s;
+  const uint8_t* zp;
+  uint16_t* y;
+  float* partial;      // [KS][M][N] fp32 (KS > 1 only)
+  unsigned* counters;  // [gridDim.y][gridDim.x] (KS > 1 only)
+  int M, N, K, KT, Gtot, GB, NBLK, kt_per_split, KS, sz_vec;
+};
 
-template <int MT, int NB, int G, int KU, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
-    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ x, const uint32_t* __restrict__ qpacked,
-    const uint16_t* __restrict__ s_in, const uint8_t* __restrict__ zpacked, uint16_t* __restrict__ y,
-    int64_t KT) {
-  constexpr int JG = (G == 128) ? 1 : 4;  // groups per 16-byte lane chunk
-  __shared__ float red[WAVES][NB][MT][16];
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
 
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, c = lane >> 4;
-  const int64_t nb0 = (int64_t)blockIdx.x * NB;
-  const int64_t m0 = (int64_t)blockIdx.y * MT;
-  const int64_t Gtot = K / G, GB = (Gtot + 1) / 2;
-  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+// Forces a value into a VGPR and hides it from constant folding, so that
+// v_and_or_b32 can take the mask from an SGPR and the fp16 exponent bits from
+// this register (a VOP3 instruction takes no literal and one SGPR at most).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
-  const int64_t NBLK = (N + 15) / 16;
-  int64_t nrow[NB];
-  bool blk_ok[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    blk_ok[b] = nb0 + b < NBLK;  // the last workgroup may own fewer row blocks
-    int64_t n = (nb0 + b) * 16 + r;
-    nrow[b] = n < N ? n : N - 1;  // pad rows read a valid scale; their output is dropped
+// Scales and zero-points of the NS = KQ * 128 / G groups one segment covers in
+// one row, kept as loaded until use (so that issuing the loads never waits):
+// group t's scale is half t of sv, its zero-point nibble t of zv.
+template <int NS>
+struct SZ {
+  uint32_t sv[NS / 2];
+  uint32_t zv[(NS + 7) / 8];
+  __device__ __forceinline__ float scale(int t) const {
+    return f16_bits_to_f32((uint16_t)(sv[t >> 1] >> (16 * (t & 1))));
   }
+  __device__ __forceinline__ uint32_t zero(int t) const { return (zv[t >> 3] >> (4 * (t & 7))) & 15u; }
+};
 
-  float acc[NB][MT];
+// srow / zrow: element offsets of the row's scales and zero-point bytes (rows
+// past N are clamped to row N - 1 by the caller: their outputs are never
+// stored); g0: first group of the segment (wave-uniform).  With a.sz_vec the
+// segment's groups lie inside the row and are aligned for vector loads;
+// otherwise each group is loaded alone, clamped into the row (groups past the
+// row meet zero activations and zero codes).
+template <int NS>
+__device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, uint32_t srow, uint32_t zrow, int g0) {
+  SZ<NS> v;
+  if (a.sz_vec) {
+    const uint16_t* sp = a.s + srow + g0;
+    const uint8_t* zp = a.zp + zrow + g0 / 2;
+    if constexpr (NS == 4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(sp);
+      v.sv[0] = t.x;
+      v.sv[1] = t.y;
+      v.zv[0] = *reinterpret_cast<const uint16_t*>(zp);
+    } else if constexpr (NS == 8) {
+      const uint4 t = *reinterpret_cast<const uint4*>(sp);
+      v.sv[0] = t.x; v.sv[1] = t.y; v.sv[2] = t.z; v.sv[3] = t.w;
+      v.zv[0] = *reinterpret_cast<const uint32_t*>(zp);
+    } else {
+      static_assert(NS == 16, "segment of 4 or 8 groups at g = 128, 16 at g = 32");
+      const uint4 t0 = *reinterpret_cast<const uint4*>(sp), t1 = *reinterpret_cast<const uint4*>(sp + 8);
+      v.sv[0] = t0.x; v.sv[1] = t0.y; v.sv[2] = t0.z; v.sv[3] = t0.w;
+      v.sv[4] = t1.x; v.sv[5] = t1.y; v.sv[6] = t1.z; v.sv[7] = t1.w;
+      const uint2 zz = *reinterpret_cast<const uint2*>(zp);
+      v.zv[0] = zz.x;
+      v.zv[1] = zz.y;
+    }
+  } else {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int i = 0; i < NS / 2; ++i) v.sv[i] = 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[b][m] = 0.0f;
+    for (int i = 0; i < (NS + 7) / 8; ++i) v.zv[i] = 0;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int gi = min(g0 + t, a.Gtot - 1);
+      v.sv[t >> 1] |= (uint32_t)a.s[srow + gi] << (16 * (t & 1));
+      const uint32_t zb = a.zp[zrow + (gi >> 1)];
+      v.zv[t >> 3] |= ((gi & 1) ? (zb >> 4) : (zb & 15u)) << (4 * (t & 7));
+    }
+  }
+  return v;
+}
 
-  const uint8_t* qbase = reinterpret_cast<const uint8_t*>(qpacked) + 16 * lane;
+template <int MT, int W, int KQ, int G>
+__global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
+  constexpr int GPT = 128 / G;     // groups per 128-column tile
+  constexpr int NS = KQ * GPT;     // groups per segment
+  constexpr int NT = W * 64;
+  constexpr int XCH = MT * KQ / 4; // 16-byte x chunks per lane and segment (64 lanes x 16 B = 4 tiles of one row)
+  static_assert(KQ % 4 == 0, "a segment is a multiple of four tiles");
+  extern __shared__ __align__(16) uint8_t smem[];
 
-  for (int64_t kt0 = wv; kt0 < KT; kt0 += (int64_t)WAVES * KU) {
-    u4 wword[KU][NB];
-    uint4 xraw[KU][MT][4];
-    float sc[KU][NB][JG];
-    float zb[KU][NB][JG];
-    // ---- issue every load of this step first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int nb = blockIdx.x, m0 = blockIdx.y * MT, ks = blockIdx.z;
+  const int kt_lo = ks * a.kt_per_split;
+  const int nkt = min(a.KT, kt_lo + a.kt_per_split) - kt_lo;
+  // this wave's x slice: [MT][KQ * 128] halves
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
+  float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][16]
+
+  const uint8_t* tbase = a.qp + (size_t)nb * a.KT * kTileBytes;
+  const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
+  const uint32_t srow = n * (uint32_t)a.Gtot, zrow = n * (uint32_t)a.GB;
+  const uint32_t lane16 = 16u * lane;
+  const uint32_t magic = in_vgpr(kMagicPair);
+
+  float acc[MT];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int64_t kt = kt0 + (int64_t)u * WAVES;
-      const bool kt_ok = kt < KT;
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+
+  for (int sg = wv; sg * KQ < nkt; sg += W) {
+    const int q0 = sg * KQ;                 // first local tile of the segment
+    const int nq = min(KQ, nkt - q0);       // tiles of the segment inside the split
+    const int kt0 = kt_lo + q0;
+
+    // ---- x slice (zeros past M and K), then scales / zero-points, then codes
+    uint4 xc[XCH];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (kt_ok && blk_ok[b]) {
-          wword[u][b] = *reinterpret_cast<const u4*>(qbase + tile_offset_bytes(nb0 + b, kt, KT));
-        } else {
-          wword[u][b] = u4{0, 0, 0, 0};
-        }
+    for (int i = 0; i < XCH; ++i) {
+      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
+      const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
+      xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
+    }
+    const SZ<NS> sz = load_sz<NS>(a, srow, zrow, kt0 * GPT);
+    u4 buf[KQ];
 #pragma unroll
-        for (int jg = 0; jg < JG; ++jg) {
-          int64_t gi = (G == 128) ? kt : kt * 4 + jg;
-          gi = gi < Gtot ? gi : Gtot - 1;
-          // s/64 and 1024 + 64z: both exact in fp32
-          sc[u][b][jg] = kt_ok ? f16_bits_to_f32(s_in[nrow[b] * Gtot + gi]) * 0.015625f : 0.0f;
-          zb[u][b][jg] = kt_ok ? 1024.0f + 64.0f * (float)load_zero(zpacked, GB, nrow[b], gi) : 0.0f;
-        }
-      }
+    for (int t = 0; t < KQ; ++t)
+      buf[t] = *reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, a.KT - 1) * kTileBytes + lane16);
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
+      const bool ok = m0 + m < a.M && kt0 * 128 + cc * 8 < a.K;
+      *reinterpret_cast<uint4*>(xw + m * (KQ * 128) + cc * 8) = ok ? xc[i] : make_uint4(0, 0, 0, 0);
+    }
+    // the slice is read back by other lanes of this wave only
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+    for (int t = 0; t < KQ; ++t) {
+      if (t >= nq) break;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
+        const uint16_t* xr = xw + m * (KQ * 128) + t * 128 + 8 * c;
+        uint4 xv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t k0 = kt * 128 + 32 * j + 8 * c;
-          if (kt_ok && m0 + m < M && kt * 128 + 32 * j < K) {
-            xraw[u][m][j] = *reinterpret_cast<const uint4*>(x + (m0 + m) * K + k0);
-          } else {
-            xraw[u][m][j] = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 32 * j);
+#pragma unroll
+        for (int gi = 0; gi < GPT; ++gi) {
+          const uint32_t z = sz.zero(t * GPT + gi);
+          const h2 zq = as_h2(z * 0x00010001u + magic);   // (1024 + z) twice
+          const h2 z16 = as_h2(z * 0x00100010u + magic);  // (1024 + 16z) twice
+          float a1 = 0.0f, a16 = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < 4 / GPT; ++jj) {
+            const int j = gi * (4 / GPT) + jj;
+            const uint32_t w = buf[t][j], w8 = w >> 8;
+            a1 = dot2(as_u32(as_h2((w & 0x000F000Fu) | magic) - zq), xv[j].x, a1);
+            a16 = dot2(as_u32(as_h2((w & 0x00F000F0u) | magic) - z16), xv[j].y, a16);
+            a1 = dot2(as_u32(as_h2((w8 & 0x000F000Fu) | magic) - zq), xv[j].z, a1);
+            a16 = dot2(as_u32(as_h2((w8 & 0x00F000F0u) | magic) - z16), xv[j].w, a16);
           }
+          acc[m] = fmaf(sz.scale(t * GPT + gi), fmaf(a16, 0.0625f, a1), acc[m]);
         }
       }
     }
-    // ---- compute
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      // per-group activation sums of this lane's columns
-      float xs[MT][JG];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int jg = 0; jg < JG; ++jg) xs[m][jg] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 v = xraw[u][m][j];
-          const int jg = (G == 128) ? 0 : j;
-          xs[m][jg] = dot2(as_h2(v.x), ones, xs[m][jg]);
-          xs[m][jg] = dot2(as_h2(v.y), ones, xs[m][jg]);
-          xs[m][jg] = dot2(as_h2(v.z), ones, xs[m][jg]);
-          xs[m][jg] = dot2(as_h2(v.w), ones, xs[m][jg]);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float t[MT][JG];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int jg = 0; jg < JG; ++jg) t[m][jg] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t word = wword[u][b][j];
-          const h2 p0 = biased_pair64(word, 0), p1 = biased_pair64(word, 1);
-          const h2 p2 = biased_pair64(word, 2), p3 = biased_pair64(word, 3);
-          const int jg = (G == 128) ? 0 : j;
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const uint4 v = xraw[u][m][j];
-            float a = t[m][jg];
-            a = dot2(p0, as_h2(v.x), a);
-            a = dot2(p1, as_h2(v.y), a);
-            a = dot2(p2, as_h2(v.z), a);
-            a = dot2(p3, as_h2(v.w), a);
-            t[m][jg] = a;
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int jg = 0; jg < JG; ++jg)
-            acc[b][m] = fmaf(sc[u][b][jg], fmaf(-zb[u][b][jg], xs[m][jg], t[m][jg]), acc[b][m]);
-      }
-    }
+    // the next segment overwrites this wave's slice: finish reading it first
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   }
 
   // ---- reduce: the four lanes of a row, then the waves, in a fixed order
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = acc[b][m];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (c == 0) red[wv][b][m][r] = v;
-    }
-  __syncthreads();
-  for (int i = threadIdx.x; i < NB * MT * 16; i += WAVES * 64) {
-    const int rr = i & 15, m = (i >> 4) % MT, b = (i >> 4) / MT;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][b][m][rr];
-    const int64_t n = (nb0 + b) * 16 + rr;
-    if (n < N && m0 + m < M) y[(m0 + m) * N + n] = f32_to_f16_bits(v);
+  for (int m = 0; m < MT; ++m) {
+    float v = acc[m];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (c == 0) red[(wv * MT + m) * 16 + r] = v;
   }
+  __syncthreads();
+  constexpr int NOUT = MT * 16;
+  for (int i = tid; i < NOUT; i += NT) {
+    float v = 0.0f;
+#pragma unroll 4
+    for (int w = 0; w < W; ++w) v += red[w * NOUT + i];
+    const int rr = i & 15, m = i >> 4;
+    const int nn = nb * 16 + rr, mm = m0 + m;
+    if (nn < a.N && mm < a.M) {
+      if (a.KS == 1)
+        a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+      else
+        a.partial[((size_t)ks * a.M + mm) * a.N + nn] = v;
+    }
+  }
+  if (a.KS == 1) return;
+
+  // ---- split-K: the last workgroup of this row range adds the partial sums
+  __shared__ unsigned last;
+  __threadfence();
+  __syncthreads();
+  unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
+  if (tid == 0) last = (atomicAdd(ctr, 1u) == (unsigned)(a.KS - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int i = tid; i < NOUT; i += NT) {
+    const int rr = i & 15, m = i >> 4;
+    const int nn = nb * 16 + rr, mm = m0 + m;
+    if (nn < a.N && mm < a.M) {
+      float v = 0.0f;
+      for (int k2 = 0; k2 < a.KS; ++k2) {
+        float* pp = a.partial + ((size_t)k2 * a.M + mm) * a.N + nn;
+        v += *pp;
+        *pp = 0.0f;  // the workspace is left zero-filled for the next call, whatever its shape
+      }
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+    }
+  }
+  if (tid == 0) *ctr = 0u;
 }
 
-template <int MT, int NB, int KU128, int KU32, int WAVES>
-hipError_t launch_t(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
-                    const uint16_t* s, const uint8_t* zpacked, uint16_t* y, hipStream_t stream) {
+// Launch shape of the GEMV for one problem; shared by the launcher and the
+// workspace query so both agree.
+constexpr int kKQ = 4;  // K tiles per wave segment
+
+struct GemvPlan {
+  int MT, W, KS, kt_per_split;
+  unsigned gx, gy;
+  size_t lds;
+};
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
+  GemvPlan p;
+  p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  p.W = p.MT <= 4 ? 16 : 8;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
-  dim3 grid((unsigned)((NBLK + NB - 1) / NB), (unsigned)((M + MT - 1) / MT)), block(WAVES * 64);
-  if (group == 128)
-    gemv_kernel<MT, NB, 128, KU128, WAVES><<<grid, block, 0, stream>>>(M, N, K, x, qpacked, s, zpacked, y, KT);
-  else
-    gemv_kernel<MT, NB, 32, KU32, WAVES><<<grid, block, 0, stream>>>(M, N, K, x, qpacked, s, zpacked, y, KT);
+  p.gx = (unsigned)NBLK;
+  p.gy = (unsigned)((M + p.MT - 1) / p.MT);
+  // split K across workgroups only to fill the GPU (two workgroups per CU),
+  // keeping at least one full pass of the waves per split
+  int64_t ks = 1;
+  const int64_t wgs = (int64_t)p.gx * p.gy, pass = (int64_t)p.W * kKQ;
+  while (wgs * ks < 512 && KT / (ks * 2) >= pass / 2) ks *= 2;
+  // split boundaries on whole segments
+  p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
+  p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
+  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * 16 * 4;
+  return p;
+}
+
+template <int MT, int W>
+hipError_t launch_t(const GemvPlan& p, int group, GemvArgs a, hipStream_t stream) {
+  dim3 grid(p.gx, p.gy, p.KS), block(W * 64);
+  if (group == 128) {
+    auto k = gemv_kernel<MT, W, kKQ, 128>;
+    if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    k<<<grid, block, p.lds, stream>>>(a);
+  } else {
+    auto k = gemv_kernel<MT, W, kKQ, 32>;
+    if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    k<<<grid, block, p.lds, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
+  const GemvPlan p = plan_gemv(M, N, K);
+  if (p.KS == 1) return 0;
+  const size_t part = (size_t)p.KS * M * N * sizeof(float);
+  const size_t part_al = (part + 255) / 256 * 256;
+  return part_al + (size_t)p.gx * p.gy * sizeof(unsigned);
+}
+
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, hipStream_t stream) {
-  if (M == 1) return launch_t<1, 2, 2, 1, 16>(M, N, K, group, x, qpacked, s, zpacked, y, stream);
-  if (M == 2) return launch_t<2, 2, 2, 1, 16>(M, N, K, group, x, qpacked, s, zpacked, y, stream);
-  if (M <= 4) return launch_t<4, 2, 1, 1, 16>(M, N, K, group, x, qpacked, s, zpacked, y, stream);
-  return launch_t<8, 2, 1, 1, 8>(M, N, K, group, x, qpacked, s, zpacked, y, stream);
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
+                       hipStream_t stream) {
+  const GemvPlan p = plan_gemv(M, N, K);
+  GemvArgs a;
+  a.x = x;
+  a.qp = reinterpret_cast<const uint8_t*>(qpacked);
+  a.s = s;
+  a.zp = zpacked;
+  a.y = y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.KT = (int)((K + 127) / 128);
+  a.Gtot = (int)(K / group);
+  a.GB = (a.Gtot + 1) / 2;
+  a.NBLK = (int)((N + 15) / 16);
+  a.kt_per_split = p.kt_per_split;
+  a.KS = p.KS;
+  // a segment's scales / zero-points load as vectors when every segment lies
+  // inside its row and starts suitably aligned
+  const int ns = kKQ * (128 / group);  // groups per segment
+  a.sz_vec = (a.Gtot % ns == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
+              (reinterpret_cast<uintptr_t>(s) & (uintptr_t)(2 * ns > 16 ? 15 : 2 * ns - 1)) == 0 &&
+              (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0)
+                 ? 1
+                 : 0;
+  a.partial = nullptr;
+  a.counters = nullptr;
+  if (p.KS > 1) {
+    const size_t part = (size_t)p.KS * M * N * sizeof(float);
+    a.partial = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
+  }
+  if (p.MT == 1) return launch_t<1, 16>(p, group, a, stream);
+  if (p.MT == 2) return launch_t<2, 16>(p, group, a, stream);
+  if (p.MT == 4) return launch_t<4, 16>(p, group, a, stream);
+  return launch_t<8, 8>(p, group, a, stream);
 }
 
 }  // namespace wq

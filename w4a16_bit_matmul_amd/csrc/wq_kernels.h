@@ -15,9 +15,13 @@ hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N
 hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint8_t* zpacked, int64_t N, int64_t K,
                           int group, int out_dtype, void* out, hipStream_t stream);
 
-// VALU split-K GEMV for small M.
+// VALU split-K GEMV for small M.  It needs a workspace (fp32 partial sums and
+// counters, zero on entry and left zero) only when it splits K across
+// workgroups; gemv_workspace_bytes gives the size (0 otherwise).
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, hipStream_t stream);
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
+                       hipStream_t stream);
 
 // MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
