@@ -19,21 +19,24 @@
 // scale (one round-to-nearest-even: fp16(What)).  Accumulation is fp32 in the
 // matrix cores.
 //
-// Decomposition: a workgroup (4 waves, one per SIMD) owns a (16*MB) x (64*NPW)
-// output tile.  The activation tile of each 128-column K step (16*MB rows) is
-// loaded once per workgroup into LDS (double-buffered, rows padded against
-// bank conflicts) and read by all four waves; wave w owns NPW 16-column blocks,
-// dequantizes its own B operands in registers (no weight is dequantized
-// twice) and accumulates its columns over all of K, so no partial sums cross
+// Decomposition: a workgroup of eight waves (two per SIMD) owns a (16*MB) x
+// (64*NPW) output tile.  Waves 0-3 take the first half of the 128-column K
+// steps and waves 4-7 the second; within a half, wave w owns NPW 16-column
+// blocks, dequantizes its own B operands in registers (no weight is
+// dequantized twice) and accumulates its columns over its half of K.  Each
+// half loads the activation tile of its current K step once into LDS
+// (double-buffered, rows padded against bank conflicts), read by its four
 // waves.  Code tiles, scales and zero-points are loaded three K steps ahead of
-// use, activations one K step ahead.
+// use, activations one step ahead.  At the end the second half's sums are
+// added to the first half's through LDS, in a fixed order.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
 namespace wq {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;      // per workgroup: two K halves of four waves
+constexpr int kHalfThreads = 256;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -43,6 +46,15 @@ struct GemmArgs {
   uint16_t* y;
   int M, N, K, KT, Gtot, GB, NBLK, sz_vec;
 };
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, which on gfx9 means waiting for every outstanding global load
+// (vmcnt(0)) -- including the prefetches meant to stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -127,17 +139,23 @@ constexpr int kBdepth = 3;           // K steps of codes in flight ahead of use
 template <int MB, int NPW, int G>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MB;
-  constexpr int ACH = ROWS * 16 / (kWaves * 64);  // 16-byte activation chunks per thread and K step
-  static_assert(ACH >= 1 && ROWS * 16 % (kWaves * 64) == 0, "whole chunks per thread");
-  extern __shared__ __align__(16) uint8_t smem[];  // [2][ROWS][kArow]
+  constexpr int ACH = ROWS * 16 / kHalfThreads;  // 16-byte activation chunks per thread and K step
+  static_assert(ACH >= 1 && ROWS * 16 % kHalfThreads == 0, "whole chunks per thread");
+  constexpr int TILE = ROWS * kArow;              // LDS bytes of one activation tile
+  extern __shared__ __align__(16) uint8_t smem[];  // [2 halves][2 buffers][ROWS][kArow]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wv >> 2, wn = wv & 3;            // K half, column group
+  const int th = tid & (kHalfThreads - 1);        // thread index within the half
   const int r = lane & 15, c = lane >> 4;
-  const int nbw0 = blockIdx.x * (kWaves * NPW) + wv * NPW;  // this wave's first column block
+  const int nbw0 = blockIdx.x * (4 * NPW) + wn * NPW;  // this wave's first column block
   const int mrow0 = blockIdx.y * ROWS;
   const uint32_t magic = in_vgpr(kMagicPair);
   const int KT = a.KT;
+  const int S = (KT + 1) / 2;                     // K steps per half (the second may have one less)
+  const int kt0 = kh * S, kt_end = min(KT, kt0 + S);
+  uint8_t* lds = smem + kh * 2 * TILE;
 
   // wave-uniform B tile bases of this wave's column blocks (blocks past the end
   // re-read the last one), per-lane offsets of the row's scales / zeros
@@ -150,19 +168,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     srow[b] = n * (uint32_t)a.Gtot;
     zrow[b] = n * (uint32_t)a.GB;
   }
-  // activation chunks this thread stages: chunk q = tid + 256*i is row q / 16,
+  // activation chunks this thread stages: chunk q = th + 256*i is row q / 16,
   // columns 8*(q % 16) .. +8 of the K step (rows past M re-read row M - 1,
   // columns past K are stored as zeros)
   uint32_t xoff[ACH], loff[ACH];
   int xcol[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int q = tid + kWaves * 64 * i, row = q >> 4, cc = q & 15;
+    const int q = th + kHalfThreads * i, row = q >> 4, cc = q & 15;
     xoff[i] = (uint32_t)min(mrow0 + row, a.M - 1) * (uint32_t)a.K;
     xcol[i] = 8 * cc;
     loff[i] = (uint32_t)(row * kArow + 16 * cc);
   }
   auto load_x = [&](int kt, uint4 (&v)[ACH]) {
+    kt = min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int col = min(kt * 128 + xcol[i], a.K - 8);
@@ -173,13 +192,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const bool ok = kt * 128 + xcol[i] < a.K;
-      *reinterpret_cast<uint4*>(smem + buf * (ROWS * kArow) + loff[i]) = ok ? v[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(lds + buf * TILE + loff[i]) = ok ? v[i] : make_uint4(0, 0, 0, 0);
     }
   };
   struct BStep {
     u4 codes[NPW];
     TileSZ<G> sz[NPW];
   };
+  f4 acc[MB][NPW];
   auto load_b = [&](int kt, BStep& d) {
     kt = min(kt, KT - 1);  // steps past the end re-load the last (unused)
 #pragma unroll
@@ -188,77 +208,106 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     for (int b = 0; b < NPW; ++b) d.codes[b] = *reinterpret_cast<const u4*>(tb[b] + (size_t)kt * kTileBytes);
   };
 
-  f4 acc[MB][NPW];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int b = 0; b < NPW; ++b) acc[i][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: codes of steps 0..kBdepth-1, activations of step 0 in LDS
-  BStep bq[kBdepth + 1];
+  // ---- prologue: codes of this half's steps 0..2, activations of step 0 in LDS
+  static_assert(kBdepth == 3, "the K loop below is unrolled over a ring of four code buffers");
+  BStep b0, b1, b2, b3;
   {
     uint4 xv[ACH];
-    load_x(0, xv);
-#pragma unroll
-    for (int d = 0; d < kBdepth; ++d) load_b(d, bq[d]);
-    store_x(0, 0, xv);
+    load_x(kt0, xv);
+    load_b(kt0, b0);
+    load_b(kt0 + 1, b1);
+    load_b(kt0 + 2, b2);
+    store_x(kt0, 0, xv);
   }
-  __syncthreads();
+  lds_barrier();
 
   // lane (r, c) reads A rows 16i + r, columns 32j + 8c .. +8 of the step
   const uint32_t aread = (uint32_t)(r * kArow + 16 * c);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
+  // One K step of this half (both halves run the same number of steps and
+  // barriers; a half past its last step only keeps the barriers): prefetch the
+  // activations of the next step and the codes three steps ahead (into the
+  // ring slot the previous step used), multiply with this step's activations
+  // from LDS, then store the prefetched activations.  Buffers have fixed ring
+  // slots, so nothing still in flight is ever copied.
+  auto step = [&](int s, const BStep& cur, BStep& nxt) {
+    const int kt = kt0 + s;
+    const int buf = s & 1;
+    const bool live = kt < kt_end, more = kt + 1 < kt_end;
     uint4 xv[ACH];
     if (more) load_x(kt + 1, xv);
-    load_b(kt + kBdepth, bq[kBdepth]);
-    const BStep& cur = bq[0];
-    const uint8_t* abase = smem + buf * (ROWS * kArow) + aread;
+    load_b(kt + kBdepth, nxt);
+    if (live) {
+      const uint8_t* abase = lds + buf * TILE + aread;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kt * 128 + 32 * j >= a.K) break;  // ragged last step: no columns left
-      h8 af[MB];
+      for (int j = 0; j < 4; ++j) {
+        if (kt * 128 + 32 * j >= a.K) break;  // ragged last step: no columns left
+        h8 af[MB];
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[i] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(abase + i * 16 * kArow + 64 * j));
+        for (int i = 0; i < MB; ++i)
+          af[i] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(abase + i * 16 * kArow + 64 * j));
 #pragma unroll
-      for (int b = 0; b < NPW; ++b) {
-        h2 sc, nbias;
-        tile_consts<G>(cur.sz[b], kt, j, magic, sc, nbias);
-        const h8 bf = dequant_word(cur.codes[b][j], magic, nbias, sc);
+        for (int b = 0; b < NPW; ++b) {
+          h2 sc, nbias;
+          tile_consts<G>(cur.sz[b], kt, j, magic, sc, nbias);
+          const h8 bf = dequant_word(cur.codes[b][j], magic, nbias, sc);
 #pragma unroll
-        for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
+          for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
+        }
       }
     }
     if (more) store_x(kt + 1, buf ^ 1, xv);
-    __syncthreads();
-#pragma unroll
-    for (int d = 0; d < kBdepth; ++d) bq[d] = bq[d + 1];
+    lds_barrier();
+  };
+
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    step(s0, b0, b3);
+    if (s0 + 1 < S) step(s0 + 1, b1, b0);
+    if (s0 + 2 < S) step(s0 + 2, b2, b1);
+    if (s0 + 3 < S) step(s0 + 3, b3, b2);
   }
 
-  // ---- epilogue: lane (r, c) holds rows 4c..4c+3 of column r of each block
+  // ---- add the second half's sums to the first half's (LDS reused), then
+  // lane (r, c) of the first half holds rows 4c..4c+3 of column r of each block
+  float* red = reinterpret_cast<float*>(smem);  // [4 column groups][MB*NPW*4][64]
+  constexpr int NACC = MB * NPW * 4;
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int b = 0; b < NPW; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(wn * NACC + (i * NPW + b) * 4 + e) * 64 + lane] = acc[i][b][e];
+  }
+  lds_barrier();
+  if (kh == 1) return;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int b = 0; b < NPW; ++b) {
       const int n = (nbw0 + b) * 16 + r;
-      if (n >= a.N) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const float v = acc[i][b][e] + red[(wn * NACC + (i * NPW + b) * 4 + e) * 64 + lane];
         const int m = mrow0 + 16 * i + 4 * c + e;
-        if (m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(acc[i][b][e]);
+        if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v);
       }
     }
 }
 
 template <int MB, int NPW>
 hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
-  const int cols = kWaves * NPW;  // column blocks per workgroup
+  const int cols = 4 * NPW;  // column blocks per workgroup
   dim3 grid((unsigned)((a.NBLK + cols - 1) / cols), (unsigned)((a.M + 16 * MB - 1) / (16 * MB))),
       block(kWaves * 64);
-  const size_t lds = (size_t)2 * 16 * MB * kArow;
+  // two halves x two buffers of activation tiles; the final reduction reuses it
+  const size_t lds_tiles = (size_t)4 * 16 * MB * kArow, lds_red = (size_t)4 * MB * NPW * 4 * 64 * sizeof(float);
+  const size_t lds = lds_tiles > lds_red ? lds_tiles : lds_red;
   if (group == 128) {
     auto k = gemm_kernel<MB, NPW, 128>;
     if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
