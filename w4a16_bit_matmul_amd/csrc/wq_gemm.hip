@@ -29,6 +29,8 @@
 // waves.  Code tiles, scales and zero-points are loaded three K steps ahead of
 // use, activations one step ahead.  At the end the second half's sums are
 // added to the first half's through LDS, in a fixed order.
+#include <type_traits>
+
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -168,32 +170,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     srow[b] = n * (uint32_t)a.Gtot;
     zrow[b] = n * (uint32_t)a.GB;
   }
-  // activation chunks this thread stages: chunk q = th + 256*i is row q / 16,
-  // columns 8*(q % 16) .. +8 of the K step (rows past M re-read row M - 1,
-  // columns past K are stored as zeros)
-  uint32_t xoff[ACH], loff[ACH];
-  int xcol[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int q = th + kHalfThreads * i, row = q >> 4, cc = q & 15;
-    xoff[i] = (uint32_t)min(mrow0 + row, a.M - 1) * (uint32_t)a.K;
-    xcol[i] = 8 * cc;
-    loff[i] = (uint32_t)(row * kArow + 16 * cc);
-  }
-  auto load_x = [&](int kt, uint4 (&v)[ACH]) {
+  // activation chunks this thread stages: chunk q = th + 256*i is row
+  // q / 16 = th / 16 + 16i, columns 8*(th % 16) .. +8 of the K step (rows past
+  // M re-read row M - 1; columns past K re-read the last columns and are never
+  // used: K is a multiple of 32, so an MFMA step is wholly inside K or skipped)
+  const int xr0 = mrow0 + (th >> 4), xcol = 8 * (th & 15);
+  const uint32_t lds_x = (uint32_t)((th >> 4) * kArow + 16 * (th & 15));
+  auto load_x = [&](int kt, u4 (&v)[ACH]) {
     kt = min(kt, KT - 1);
+    const int col = min(kt * 128 + xcol, a.K - 8);
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-      const int col = min(kt * 128 + xcol[i], a.K - 8);
-      v[i] = *reinterpret_cast<const uint4*>(a.x + xoff[i] + col);
+      const uint32_t row = (uint32_t)min(xr0 + 16 * i, a.M - 1);
+      v[i] = *reinterpret_cast<const u4*>(a.x + row * (uint32_t)a.K + col);
     }
   };
-  auto store_x = [&](int kt, int buf, const uint4 (&v)[ACH]) {
+  auto store_x = [&](int buf, const u4 (&v)[ACH]) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const bool ok = kt * 128 + xcol[i] < a.K;
-      *reinterpret_cast<uint4*>(lds + buf * TILE + loff[i]) = ok ? v[i] : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u4*>(lds + buf * TILE + lds_x + i * 16 * kArow) = v[i];
   };
   struct BStep {
     u4 codes[NPW];
@@ -217,12 +211,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   static_assert(kBdepth == 3, "the K loop below is unrolled over a ring of four code buffers");
   BStep b0, b1, b2, b3;
   {
-    uint4 xv[ACH];
+    u4 xv[ACH];
     load_x(kt0, xv);
     load_b(kt0, b0);
     load_b(kt0 + 1, b1);
     load_b(kt0 + 2, b2);
-    store_x(kt0, 0, xv);
+    store_x(0, xv);
   }
   lds_barrier();
 
@@ -234,23 +228,29 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // activations of the next step and the codes three steps ahead (into the
   // ring slot the previous step used), multiply with this step's activations
   // from LDS, then store the prefetched activations.  Buffers have fixed ring
-  // slots, so nothing still in flight is ever copied.
-  auto step = [&](int s, const BStep& cur, BStep& nxt) {
+  // slots, so nothing still in flight is ever copied.  FULL steps (both
+  // halves' tiles whole, next tiles exist) have no branch at all: every load is
+  // issued unconditionally (addresses clamped into the arrays), so the
+  // compiler's wait counting stays exact and the prefetches stay in flight.
+  auto step = [&](auto full_tag, int s, const BStep& cur, BStep& nxt) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int kt = kt0 + s;
     const int buf = s & 1;
-    const bool live = kt < kt_end, more = kt + 1 < kt_end;
-    uint4 xv[ACH];
+    const bool live = FULL || kt < kt_end, more = FULL || kt + 1 < kt_end;
+    // activations first: loads complete in issue order, so storing them at the
+    // end of the step does not wait for the code prefetch issued after them
+    u4 xv[ACH];
     if (more) load_x(kt + 1, xv);
+    __builtin_amdgcn_sched_barrier(0);
     load_b(kt + kBdepth, nxt);
     if (live) {
       const uint8_t* abase = lds + buf * TILE + aread;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (kt * 128 + 32 * j >= a.K) break;  // ragged last step: no columns left
+        if (!FULL && kt * 128 + 32 * j >= a.K) break;  // ragged last step: no columns left
         h8 af[MB];
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
-          af[i] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(abase + i * 16 * kArow + 64 * j));
+        for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abase + i * 16 * kArow + 64 * j);
 #pragma unroll
         for (int b = 0; b < NPW; ++b) {
           h2 sc, nbias;
@@ -261,15 +261,27 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         }
       }
     }
-    if (more) store_x(kt + 1, buf ^ 1, xv);
+    if (more) store_x(buf ^ 1, xv);
     lds_barrier();
   };
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
 
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    step(s0, b0, b3);
-    if (s0 + 1 < S) step(s0 + 1, b1, b0);
-    if (s0 + 2 < S) step(s0 + 2, b2, b1);
-    if (s0 + 3 < S) step(s0 + 3, b3, b2);
+  // steps where both halves have whole tiles with a successor, in groups of
+  // four (the ring size)
+  const int s_full = min(a.K / 128 - S, S - 1) & ~3;
+  int s0 = 0;
+  for (; s0 < s_full; s0 += 4) {
+    step(Full{}, s0, b0, b3);
+    step(Full{}, s0 + 1, b1, b0);
+    step(Full{}, s0 + 2, b2, b1);
+    step(Full{}, s0 + 3, b3, b2);
+  }
+  for (; s0 < S; s0 += 4) {
+    step(Part{}, s0, b0, b3);
+    if (s0 + 1 < S) step(Part{}, s0 + 1, b1, b0);
+    if (s0 + 2 < S) step(Part{}, s0 + 2, b2, b1);
+    if (s0 + 3 < S) step(Part{}, s0 + 3, b3, b2);
   }
 
   // ---- add the second half's sums to the first half's (LDS reused), then
