@@ -150,6 +150,14 @@ int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group,
                   const uint8_t* zpacked, uint16_t* y_f16,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Describes, as one NUL-terminated line written into buf (host memory,
+ * buf_len bytes, truncated to fit), the kernel and launch shape that
+ * wq_gemm_w4a16_ex would use for this problem and path: kernel template
+ * parameters, grid, block, LDS bytes and (GEMV) the number of K splits.
+ * Host-only; launches nothing.  WQ_EINVAL for a NULL or empty buffer or a bad
+ * size or path, WQ_EUNSUPPORTED as for wq_gemm_w4a16. */
+int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len);
+
 /* As wq_gemm_w4a16, with the kernel family chosen by `path` (wq_path). */
 int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group,
                      const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,

@@ -113,3 +113,23 @@ def test_workspace_query_and_check():
         st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, wq.WQ_PATH_GEMV, None)
         assert st == wq.WQ_EALIGN
     assert wq.wq_gemm_workspace_bytes(0, 16, 128, 128) == 0
+
+
+def test_gemm_plan_names_the_dispatched_kernel():
+    # host-only description of the kernel each problem runs: the decode GEMV
+    # (one row block of 16 outputs per workgroup, no K split) and the M=128 MFMA
+    # GEMM (eight 16-row blocks per workgroup)
+    d = wq.wq_gemm_plan(1, 8192, 8192, 128)
+    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=128>") and "grid=(512,1,1)" in d and "split_k=1" in d, d
+    d = wq.wq_gemm_plan(128, 28672, 8192, 128)
+    assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128>") and "grid=(224,1,1)" in d, d
+    assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
+    assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=1, G=32>")
+    assert "split_k=1" not in wq.wq_gemm_plan(1, 48, 8192, 128)
+    buf = ctypes.create_string_buffer(8)
+    assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, buf, 8) == wq.WQ_OK and len(buf.value) == 7
+    assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, None, 8) == wq.WQ_EINVAL
+    assert wq.lib().wq_gemm_plan(0, 8192, 8192, 128, 0, buf, 8) == wq.WQ_EINVAL
+    assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 7, buf, 8) == wq.WQ_EINVAL
+    assert wq.lib().wq_gemm_plan(1, 8192, 8192, 48, 0, buf, 8) == wq.WQ_EUNSUPPORTED
+

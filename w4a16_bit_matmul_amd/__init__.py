@@ -24,7 +24,7 @@ WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 
 EXPORTED = (
     "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_pack_int4", "wq_dequant",
-    "wq_gemm_workspace_bytes", "wq_gemm_w4a16", "wq_gemm_w4a16_ex",
+    "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex",
 )
 
 _lib = None
@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         "wq_pack_int4": (I, [P, P, I64, I64, I, P, P, P]),
         "wq_dequant": (I, [P, P, P, I64, I64, I, I, P, P]),
         "wq_gemm_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "wq_gemm_plan": (I, [I64, I64, I64, I, I, ctypes.c_char_p, SZ]),
         "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
         "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
     }
@@ -109,6 +110,13 @@ def wq_layout_bytes(N: int, K: int, group: int):
 
 def wq_gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
     return int(lib().wq_gemm_workspace_bytes(M, N, K, group))
+
+
+def wq_gemm_plan(M: int, N: int, K: int, group: int, path: int = WQ_PATH_AUTO) -> str:
+    """One-line description of the kernel and launch shape wq_gemm_w4a16 uses."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().wq_gemm_plan(M, N, K, group, path, buf, len(buf)), "wq_gemm_plan")
+    return buf.value.decode()
 
 
 def alloc_quantized(N: int, K: int, group: int, device="cuda") -> QuantizedWeight:

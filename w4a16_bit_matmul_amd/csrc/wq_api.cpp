@@ -91,6 +91,21 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
   return a > b ? a : b;
 }
 
+int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len) {
+  if (!buf || buf_len == 0) return WQ_EINVAL;
+  buf[0] = 0;
+  if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  if (mfma)
+    wq::describe_gemm(M, N, K, group, buf, buf_len);
+  else
+    wq::describe_gemv(M, N, K, group, buf, buf_len);
+  return WQ_OK;
+}
+
 int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
                      const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
                      size_t workspace_bytes, int path, void* stream) {

@@ -29,6 +29,8 @@
 // waves.  Code tiles, scales and zero-points are loaded three K steps ahead of
 // use, activations one step ahead.  At the end the second half's sums are
 // added to the first half's through LDS, in a fixed order.
+#include <stdio.h>
+
 #include <type_traits>
 
 #include "wq_device.h"
@@ -312,14 +314,32 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int MB, int NPW>
-hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
-  const int cols = 4 * NPW;  // column blocks per workgroup
-  dim3 grid((unsigned)((a.NBLK + cols - 1) / cols), (unsigned)((a.M + 16 * MB - 1) / (16 * MB))),
-      block(kWaves * 64);
+// Row blocks (MB) and column blocks per wave (NPW) for a problem of M rows.
+struct GemmTiles {
+  int MB, NPW;
+};
+GemmTiles gemm_tiles(int64_t M) {
+  if (M <= 16) return {1, 1};
+  if (M <= 32) return {2, 1};
+  if (M <= 64) return {4, 2};
+  return {8, 2};
+}
+
+dim3 gemm_grid(int MB, int NPW, int64_t M, int64_t N) {
+  const int64_t cols = 4 * NPW;  // column blocks per workgroup
+  return dim3((unsigned)(((N + 15) / 16 + cols - 1) / cols), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+}
+
+size_t gemm_lds(int MB, int NPW) {
   // two halves x two buffers of activation tiles; the final reduction reuses it
   const size_t lds_tiles = (size_t)4 * 16 * MB * kArow, lds_red = (size_t)4 * MB * NPW * 4 * 64 * sizeof(float);
-  const size_t lds = lds_tiles > lds_red ? lds_tiles : lds_red;
+  return lds_tiles > lds_red ? lds_tiles : lds_red;
+}
+
+template <int MB, int NPW>
+hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid = gemm_grid(MB, NPW, a.M, a.N), block(kWaves * 64);
+  const size_t lds = gemm_lds(MB, NPW);
   if (group == 128) {
     auto k = gemm_kernel<MB, NPW, 128>;
     if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -335,6 +355,13 @@ hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+
+int describe_gemm(int64_t M, int64_t N, int64_t, int group, char* buf, size_t len) {
+  const GemmTiles t = gemm_tiles(M);
+  const dim3 g = gemm_grid(t.MB, t.NPW, M, N);
+  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d> grid=(%u,%u,1) block=%d lds=%zu", t.MB, t.NPW, group,
+                  g.x, g.y, kWaves * 64, gemm_lds(t.MB, t.NPW));
+}
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* /*workspace*/,
@@ -358,9 +385,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_
               (reinterpret_cast<uintptr_t>(zpacked) & 1) == 0)
                  ? 1
                  : 0;
-  if (M <= 16) return launch_t<1, 1>(group, a, stream);
-  if (M <= 32) return launch_t<2, 1>(group, a, stream);
-  if (M <= 64) return launch_t<4, 2>(group, a, stream);
+  const GemmTiles t = gemm_tiles(M);
+  if (t.MB == 1) return launch_t<1, 1>(group, a, stream);
+  if (t.MB == 2) return launch_t<2, 1>(group, a, stream);
+  if (t.MB == 4) return launch_t<4, 2>(group, a, stream);
   return launch_t<8, 2>(group, a, stream);
 }
 

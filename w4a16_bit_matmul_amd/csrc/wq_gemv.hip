@@ -35,6 +35,8 @@
 // a row range (found with a device-scope atomic counter) adds them in split
 // order and writes y, so results stay deterministic; it then zeroes the partial
 // sums and the counter, leaving the whole workspace zero for the next call.
+#include <stdio.h>
+
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -308,6 +310,12 @@ hipError_t launch_t(const GemvPlan& p, int group, GemvArgs a, hipStream_t stream
 }
 
 }  // namespace
+
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len) {
+  const GemvPlan p = plan_gemv(M, N, K);
+  return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+                  p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
+}
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
   const GemvPlan p = plan_gemv(M, N, K);

@@ -19,12 +19,16 @@ hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint
 // counters, zero on entry and left zero) only when it splits K across
 // workgroups; gemv_workspace_bytes gives the size (0 otherwise).
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+// Writes a one-line description of the kernel and launch shape chosen for this
+// problem (snprintf semantics).
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len);
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream);
 
 // MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+int describe_gemm(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
 
