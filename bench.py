@@ -10,7 +10,7 @@ value = effective GB/s = algorithmic bytes (4-bit codes + fp16 scales + 4-bit
 zero-points + fp16 x + fp16 y) / time per step.  The M=128 GEMM (TFLOP/s), the
 quantization kernel and the CPU oracle are reported alongside in the same line.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 500]
 """
 from __future__ import annotations
 
@@ -198,7 +198,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the decode GEMV")
     ap.add_argument("--copy-probe", action="store_true",
@@ -258,7 +258,9 @@ def main():
                      "us_per_launch": round(t_step * 1e6, 3)},
     }
     if not args.no_extras:
-        gwl, t_gemm, t_dense = bench_gemm(max(20, args.steps // 4), max(5, args.warmup // 4))
+        # the GEMM draws enough power that the clock settles only after tens of
+        # milliseconds of sustained work: warm it for at least 300 launches
+        gwl, t_gemm, t_dense = bench_gemm(max(50, args.steps // 2), max(300, args.warmup // 2))
         tflops = gwl.flops() / t_gemm / 1e12
         line["gemm_m128"] = {"workload": gwl.name, "M": gwl.M, "N": gwl.N, "K": gwl.K, "group": gwl.group,
                              "kernel": wq.wq_gemm_plan(gwl.M, gwl.N, gwl.K, gwl.group), "bound": "mfma",

@@ -124,7 +124,7 @@ def test_gemm_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128>") and "grid=(224,1,1)" in d, d
     assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
-    assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=1, G=32>")
+    assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     assert "split_k=1" not in wq.wq_gemm_plan(1, 48, 8192, 128)
     buf = ctypes.create_string_buffer(8)
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, buf, 8) == wq.WQ_OK and len(buf.value) == 7

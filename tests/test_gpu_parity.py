@@ -163,6 +163,13 @@ MATMUL_CASES = [  # M, N, K, group
     (128, 512, 2048, 128),
     (130, 100, 256, 128),
     (200, 64, 128, 32),
+    # MFMA shapes with a ragged last K tile and partial row tiles: K = 96
+    # (one tile, three MFMA steps), 160 (second tile one step), 4224 (33
+    # tiles: whole groups of four plus one), 1056 (eight tiles plus one step)
+    (40, 100, 96, 32),
+    (100, 72, 160, 32),
+    (96, 50, 4224, 128),
+    (129, 300, 1056, 32),
     # few row blocks and a long K: the GEMV splits K across workgroups
     (1, 48, 8192, 128),
     (2, 1000, 8192, 128),

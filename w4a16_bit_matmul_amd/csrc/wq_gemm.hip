@@ -11,24 +11,34 @@
 // column r, each with the eight k-slots 8c..8c+7 of the 32-deep step, and
 // receives D rows 4c..4c+3 of column r.  The packed tile layout gives lane l
 // exactly those slots for column r: word j of its 16 bytes holds columns
-// 32j + 8c + e, so step j of a 128-column tile uses word j as the B operand and
-// x[m][32j + 8c .. 32j + 8c + 7] (one 16-byte load) as the A operand.
+// 32j + 8c + e, so MFMA step j of a 128-column K tile uses word j as the B
+// operand and x[m][32j + 8c .. 32j + 8c + 7] as the A operand.
 //
 // B dequantization per pair of columns: shift + AND-OR (1024 + q, exact fp16),
 // packed fp16 add of -(1024 + z) (exact q - z), packed fp16 multiply by the
 // scale (one round-to-nearest-even: fp16(What)).  Accumulation is fp32 in the
 // matrix cores.
 //
-// Decomposition: a workgroup of eight waves (two per SIMD) owns a (16*MB) x
-// (64*NPW) output tile.  Waves 0-3 take the first half of the 128-column K
-// steps and waves 4-7 the second; within a half, wave w owns NPW 16-column
-// blocks, dequantizes its own B operands in registers (no weight is
-// dequantized twice) and accumulates its columns over its half of K.  Each
-// half loads the activation tile of its current K step once into LDS
-// (double-buffered, rows padded against bank conflicts), read by its four
-// waves.  Code tiles, scales and zero-points are loaded three K steps ahead of
-// use, activations one step ahead.  At the end the second half's sums are
-// added to the first half's through LDS, in a fixed order.
+// Decomposition.  A workgroup of eight waves (two per SIMD) owns a (16*MB) x
+// 128 output tile and walks K one 128-column tile per step, all waves on the
+// same tile.  Wave w = 4p + cg takes MFMA steps 2p and 2p + 1 of every tile
+// for the two 16-column blocks of column group cg: it dequantizes its own B
+// operands in registers (no weight is dequantized twice), using two of the
+// four code words in each lane's 16 bytes, loaded three tiles ahead into a
+// four-slot register ring.  The activations of a tile are staged in LDS once
+// for the workgroup: every thread loads whole 256-byte row segments with
+// 16-byte loads (sixteen threads per row) two tiles ahead of use into
+// registers and stores them, one step before their use, into one of two LDS
+// buffers; chunk cc of row R sits in slot cc ^ (R % 16) of its row, so the
+// A-operand reads (lane l = r + 16c takes chunk 4j + c of row 16i + r) spread
+// over all banks.  Scales and zero-points of eight tiles at a time are staged
+// into LDS with wide loads (a row's scales for eight tiles in one load instead
+// of one load per tile), half a chunk ahead.  The steady state runs in groups
+// of eight tiles without a branch, so the compiler's wait counts stay exact
+// and every load stays in flight until its first use; barriers order LDS only
+// (__syncthreads() on gfx9 would also wait for every outstanding global load).
+// At the end the second step pair's sums are added to the first pair's
+// through LDS, in a fixed order.
 #include <stdio.h>
 
 #include <type_traits>
@@ -39,8 +49,9 @@
 namespace wq {
 namespace {
 
-constexpr int kWaves = 8;      // per workgroup: two K halves of four waves
-constexpr int kHalfThreads = 256;
+constexpr int kWaves = 8;     // per workgroup: four column groups x two MFMA-step pairs
+constexpr int kSzChunk = 8;   // K tiles per staged chunk of scales / zero-points
+constexpr int kNPW = 2;       // 16-column blocks per wave (eight per workgroup)
 
 struct GemmArgs {
   const uint16_t* x;
@@ -48,12 +59,10 @@ struct GemmArgs {
   const uint16_t* s;
   const uint8_t* zp;
   uint16_t* y;
-  int M, N, K, KT, Gtot, GB, NBLK, sz_vec;
+  int M, N, K, KT, Gtot, GB, NBLK;
 };
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also releases
-// global memory, which on gfx9 means waiting for every outstanding global load
-// (vmcnt(0)) -- including the prefetches meant to stay in flight across it.
+// Workgroup barrier that orders LDS only.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -71,60 +80,6 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   return v;
 }
 
-// Scales and zero-points of one row for one 128-column K tile, as loaded:
-// g = 128: one group (scale bits in s, zero-point byte in z, nibble zsh);
-// g = 32: four groups (scales in the four halves of s / s2, nibbles of z).
-template <int G>
-struct TileSZ {
-  uint32_t s, s2, z;
-};
-
-template <int G>
-__device__ __forceinline__ TileSZ<G> load_tile_sz(const GemmArgs& a, uint32_t srow, uint32_t zrow, int kt) {
-  TileSZ<G> v;
-  if constexpr (G == 128) {
-    v.s = a.s[srow + kt];
-    v.z = a.zp[zrow + (kt >> 1)];
-    v.s2 = 0;
-  } else {
-    const int g0 = kt * 4;
-    if (a.sz_vec) {
-      const uint2 t = *reinterpret_cast<const uint2*>(a.s + srow + g0);
-      v.s = t.x;
-      v.s2 = t.y;
-      v.z = *reinterpret_cast<const uint16_t*>(a.zp + zrow + g0 / 2);
-    } else {
-      uint32_t sh[4], zz = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gi = min(g0 + j, a.Gtot - 1);
-        sh[j] = a.s[srow + gi];
-        const uint32_t zb = a.zp[zrow + (gi >> 1)];
-        zz |= ((gi & 1) ? (zb >> 4) : (zb & 15u)) << (4 * j);
-      }
-      v.s = sh[0] | (sh[1] << 16);
-      v.s2 = sh[2] | (sh[3] << 16);
-      v.z = zz;
-    }
-  }
-  return v;
-}
-
-// (scale, scale) and (-(1024 + z), -(1024 + z)) fp16 pairs of group j (word j).
-template <int G>
-__device__ __forceinline__ void tile_consts(const TileSZ<G>& v, int kt, int j, uint32_t magic, h2& sc, h2& nb) {
-  uint32_t sb, z;
-  if constexpr (G == 128) {
-    sb = v.s & 0xffffu;
-    z = (v.z >> (4 * (kt & 1))) & 15u;
-  } else {
-    sb = ((j < 2 ? v.s : v.s2) >> (16 * (j & 1))) & 0xffffu;
-    z = (v.z >> (4 * j)) & 15u;
-  }
-  sc = as_h2(sb * 0x00010001u);
-  nb = -as_h2(z * 0x00010001u + magic);
-}
-
 // fp16(s * (q - z)) for the eight columns held by one packed word.
 __device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t magic, h2 nb, h2 sc) {
   const h2 p0 = (as_h2((w & 0x000F000Fu) | magic) + nb) * sc;
@@ -137,169 +92,250 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t magic, h2 nb, h2
   return out;
 }
 
-constexpr int kArow = 128 * 2 + 16;  // LDS bytes per activation row of a K step (padded)
-constexpr int kBdepth = 3;           // K steps of codes in flight ahead of use
+// LDS bytes of one staged chunk for the workgroup's 128 weight rows:
+// g = 128: [tile][row] u32 (scale bits, zero-point in bits 16..19);
+// g = 32: [tile][pair][row] u32 (scales of groups 4t + 2q, 4t + 2q + 1), then
+// [tile][row] u16 (the tile's four zero-points, group 4t in bits 0..3).
+template <int G>
+constexpr int sz_chunk_bytes() {
+  return G == 128 ? kSzChunk * 128 * 4 : kSzChunk * 2 * 128 * 4 + kSzChunk * 128 * 2;
+}
 
-template <int MB, int NPW, int G>
+// SZV: every row of s (and zpacked) is aligned for the wide staging loads.
+template <int MB, int G, bool SZV>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
+  constexpr int NPW = kNPW;
+  constexpr int NTH = kWaves * 64;
   constexpr int ROWS = 16 * MB;
-  constexpr int ACH = ROWS * 16 / kHalfThreads;  // 16-byte activation chunks per thread and K step
-  static_assert(ACH >= 1 && ROWS * 16 % kHalfThreads == 0, "whole chunks per thread");
-  constexpr int TILE = ROWS * kArow;              // LDS bytes of one activation tile
-  extern __shared__ __align__(16) uint8_t smem[];  // [2 halves][2 buffers][ROWS][kArow]
+  constexpr int XTILE = ROWS * 256;                            // one K tile of activations in LDS
+  constexpr int XCH = ROWS * 16 >= NTH ? ROWS * 16 / NTH : 1;  // 16-byte chunks per thread per tile
+  constexpr int SZB = sz_chunk_bytes<G>();
+  static_assert(ROWS * 16 % NTH == 0 || NTH % (ROWS * 16) == 0, "whole chunks per thread");
+  extern __shared__ __align__(16) uint8_t smem[];  // [2][XTILE] activations, [2][SZB] scales
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wv >> 2, wn = wv & 3;            // K half, column group
-  const int th = tid & (kHalfThreads - 1);        // thread index within the half
+  const int jp = wv >> 2, cgp = wv & 3;
   const int r = lane & 15, c = lane >> 4;
-  const int nbw0 = blockIdx.x * (4 * NPW) + wn * NPW;  // this wave's first column block
+  const int nwg0 = blockIdx.x * 8 * 16;  // first weight row of the workgroup
+  const int nbw0 = blockIdx.x * 8 + cgp * NPW;
   const int mrow0 = blockIdx.y * ROWS;
   const uint32_t magic = in_vgpr(kMagicPair);
   const int KT = a.KT;
-  const int S = (KT + 1) / 2;                     // K steps per half (the second may have one less)
-  const int kt0 = kh * S, kt_end = min(KT, kt0 + S);
-  uint8_t* lds = smem + kh * 2 * TILE;
 
-  // wave-uniform B tile bases of this wave's column blocks (blocks past the end
-  // re-read the last one), per-lane offsets of the row's scales / zeros
+  // code words 2jp, 2jp + 1 of the lane's 16 bytes in each of the wave's
+  // blocks (blocks past the end re-read the last one)
   const uint8_t* tb[NPW];
-  uint32_t srow[NPW], zrow[NPW];
 #pragma unroll
-  for (int b = 0; b < NPW; ++b) {
-    tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * kTileBytes + 16u * lane;
-    const uint32_t n = (uint32_t)min((nbw0 + b) * 16 + r, a.N - 1);
-    srow[b] = n * (uint32_t)a.Gtot;
-    zrow[b] = n * (uint32_t)a.GB;
+  for (int b = 0; b < NPW; ++b)
+    tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * kTileBytes + 16u * lane + 8u * jp;
+  auto load_b = [&](int kt, uint2 (&d)[NPW]) {
+    kt = min(kt, KT - 1);  // tiles past the end re-load the last (unused)
+#pragma unroll
+    for (int b = 0; b < NPW; ++b) d[b] = *reinterpret_cast<const uint2*>(tb[b] + (size_t)kt * kTileBytes);
+  };
+
+  // activation chunk q = tid + NTH * i: row q / 16 of the tile, global chunk
+  // q % 16 (with fewer chunks than threads, threads share chunks and store
+  // the same bytes).  Rows past M re-read row M - 1; in a ragged last tile,
+  // chunks past K re-read the last chunk inside K (K is a multiple of 32, so
+  // an MFMA step lies wholly inside K or is skipped).
+  const uint16_t* xrow[XCH];
+  uint32_t xlds[XCH];
+  const int xcc = tid & 15;
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int row = ((tid >> 4) + (NTH / 16) * i) % ROWS;
+    xrow[i] = a.x + (size_t)min(mrow0 + row, a.M - 1) * a.K;
+    xlds[i] = (uint32_t)(row * 256 + 16 * (xcc ^ (row & 15)));
   }
-  // activation chunks this thread stages: chunk q = th + 256*i is row
-  // q / 16 = th / 16 + 16i, columns 8*(th % 16) .. +8 of the K step (rows past
-  // M re-read row M - 1; columns past K re-read the last columns and are never
-  // used: K is a multiple of 32, so an MFMA step is wholly inside K or skipped)
-  const int xr0 = mrow0 + (th >> 4), xcol = 8 * (th & 15);
-  const uint32_t lds_x = (uint32_t)((th >> 4) * kArow + 16 * (th & 15));
-  auto load_x = [&](int kt, u4 (&v)[ACH]) {
-    kt = min(kt, KT - 1);
-    const int col = min(kt * 128 + xcol, a.K - 8);
+  auto load_x = [&](int kt, u4 (&v)[XCH]) {
+    const int col = min(min(kt, KT - 1) * 128 + 8 * xcc, a.K - 8);
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const uint32_t row = (uint32_t)min(xr0 + 16 * i, a.M - 1);
-      v[i] = *reinterpret_cast<const u4*>(a.x + row * (uint32_t)a.K + col);
+    for (int i = 0; i < XCH; ++i) v[i] = *reinterpret_cast<const u4*>(xrow[i] + col);
+  };
+  auto store_x = [&](int kt, const u4 (&v)[XCH]) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) *reinterpret_cast<u4*>(smem + (kt & 1) * XTILE + xlds[i]) = v[i];
+  };
+
+  // ---- scale / zero-point staging: thread (row n = tid / 4, part p = tid % 4)
+  // covers tiles 2p, 2p + 1 of a chunk (groups past the end re-read the last)
+  const int sn = tid >> 2, sp = tid & 3;
+  const size_t srow = (size_t)min(nwg0 + sn, a.N - 1) * a.Gtot;
+  const size_t zrow = (size_t)min(nwg0 + sn, a.N - 1) * a.GB;
+  struct SzStage {
+    uint32_t s[4], z;
+  };
+  auto sz_load = [&](int chunk, SzStage& v) {
+    const int t0 = chunk * kSzChunk + 2 * sp;  // first of this thread's two tiles
+    if constexpr (G == 128) {
+      if constexpr (SZV) {  // Gtot even: one u32 holds both scales
+        v.s[0] = *reinterpret_cast<const uint32_t*>(a.s + srow + min(t0, a.Gtot - 2));
+      } else {
+        v.s[0] = a.s[srow + min(t0, a.Gtot - 1)];
+        v.s[1] = a.s[srow + min(t0 + 1, a.Gtot - 1)];
+      }
+      v.z = a.zp[zrow + (min(t0, a.Gtot - 1) >> 1)];
+    } else {
+      if constexpr (SZV) {  // Gtot % 8 == 0: 16 bytes of scales, 4 bytes of zero-points
+        const int g = min(4 * t0, a.Gtot - 8);
+        const u4 t = *reinterpret_cast<const u4*>(a.s + srow + g);
+        v.s[0] = t.x; v.s[1] = t.y; v.s[2] = t.z; v.s[3] = t.w;
+        v.z = *reinterpret_cast<const uint32_t*>(a.zp + zrow + g / 2);
+      } else {
+        uint32_t zz = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g0 = min(4 * t0 + 2 * q, a.Gtot - 1), g1 = min(4 * t0 + 2 * q + 1, a.Gtot - 1);
+          v.s[q] = (uint32_t)a.s[srow + g0] | ((uint32_t)a.s[srow + g1] << 16);
+          const uint32_t zb0 = a.zp[zrow + (g0 >> 1)], zb1 = a.zp[zrow + (g1 >> 1)];
+          zz |= (((g0 & 1) ? zb0 >> 4 : zb0 & 15u) | (((g1 & 1) ? zb1 >> 4 : zb1 & 15u) << 4)) << (8 * q);
+        }
+        v.z = zz;
+      }
     }
   };
-  auto store_x = [&](int buf, const u4 (&v)[ACH]) {
+  uint8_t* const szbase = smem + 2 * XTILE;
+  auto sz_store = [&](int chunk, const SzStage& v) {
+    uint8_t* buf = szbase + (chunk & 1) * SZB;
+    if constexpr (G == 128) {
+      const uint32_t s0 = SZV ? v.s[0] & 0xffffu : v.s[0];
+      const uint32_t s1 = SZV ? v.s[0] >> 16 : v.s[1];
+      // tiles 2p (low nibble) and 2p + 1 (high nibble) share a zero-point byte
+      *reinterpret_cast<uint32_t*>(buf + (2 * sp) * 512 + 4 * sn) = s0 | ((v.z & 15u) << 16);
+      *reinterpret_cast<uint32_t*>(buf + (2 * sp + 1) * 512 + 4 * sn) = s1 | ((v.z >> 4) << 16);
+    } else {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u4*>(lds + buf * TILE + lds_x + i * 16 * kArow) = v[i];
-  };
-  struct BStep {
-    u4 codes[NPW];
-    TileSZ<G> sz[NPW];
-  };
-  f4 acc[MB][NPW];
-  auto load_b = [&](int kt, BStep& d) {
-    kt = min(kt, KT - 1);  // steps past the end re-load the last (unused)
+      for (int e = 0; e < 2; ++e) {
 #pragma unroll
-    for (int b = 0; b < NPW; ++b) d.sz[b] = load_tile_sz<G>(a, srow[b], zrow[b], kt);
-#pragma unroll
-    for (int b = 0; b < NPW; ++b) d.codes[b] = *reinterpret_cast<const u4*>(tb[b] + (size_t)kt * kTileBytes);
+        for (int q = 0; q < 2; ++q)
+          *reinterpret_cast<uint32_t*>(buf + ((2 * sp + e) * 2 + q) * 512 + 4 * sn) = v.s[2 * e + q];
+        *reinterpret_cast<uint16_t*>(buf + kSzChunk * 1024 + (2 * sp + e) * 256 + 2 * sn) =
+            (uint16_t)(v.z >> (16 * e));
+      }
+    }
   };
 
+  f4 acc[MB][NPW];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int b = 0; b < NPW; ++b) acc[i][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: codes of this half's steps 0..2, activations of step 0 in LDS
-  static_assert(kBdepth == 3, "the K loop below is unrolled over a ring of four code buffers");
-  BStep b0, b1, b2, b3;
-  {
-    u4 xv[ACH];
-    load_x(kt0, xv);
-    load_b(kt0, b0);
-    load_b(kt0 + 1, b1);
-    load_b(kt0 + 2, b2);
-    store_x(0, xv);
-  }
+  // ---- prologue: activations of tile 0 (in LDS) and tile 1 (in registers),
+  // codes of tiles 0..2, scales / zero-points of the first chunk
+  uint2 b0[NPW], b1[NPW], b2[NPW], b3[NPW];
+  u4 xs0[XCH], xs1[XCH];
+  SzStage szs;
+  load_x(0, xs0);
+  load_x(1, xs1);
+  load_b(0, b0);
+  load_b(1, b1);
+  load_b(2, b2);
+  sz_load(0, szs);
+  store_x(0, xs0);
+  sz_store(0, szs);
   lds_barrier();
 
-  // lane (r, c) reads A rows 16i + r, columns 32j + 8c .. +8 of the step
-  const uint32_t aread = (uint32_t)(r * kArow + 16 * c);
+  // this lane's A reads: row r of block i, chunk 4j + c at slot (4j + c) ^ r;
+  // its scale / zero entries: rows (cg*NPW + b)*16 + r of the workgroup
+  const uint8_t* const arow = smem + r * 256;
+  const int szrow = cgp * NPW * 16 + r;
 
-  // One K step of this half (both halves run the same number of steps and
-  // barriers; a half past its last step only keeps the barriers): prefetch the
-  // activations of the next step and the codes three steps ahead (into the
-  // ring slot the previous step used), multiply with this step's activations
-  // from LDS, then store the prefetched activations.  Buffers have fixed ring
-  // slots, so nothing still in flight is ever copied.  FULL steps (both
-  // halves' tiles whole, next tiles exist) have no branch at all: every load is
-  // issued unconditionally (addresses clamped into the arrays), so the
-  // compiler's wait counting stays exact and the prefetches stay in flight.
-  auto step = [&](auto full_tag, int s, const BStep& cur, BStep& nxt) {
+  // One step (K tile kt): load the activations of tile kt + 2 and the codes
+  // of tile kt + 3, multiply tile kt, and store the activations of tile
+  // kt + 1 (loaded one step earlier) into the other LDS buffer.
+  auto step = [&](auto full_tag, int kt, u4 (&xld)[XCH], const u4 (&xst)[XCH], const uint2 (&cur)[NPW],
+                  uint2 (&nxt)[NPW]) {
     constexpr bool FULL = decltype(full_tag)::value;
-    const int kt = kt0 + s;
-    const int buf = s & 1;
-    const bool live = FULL || kt < kt_end, more = FULL || kt + 1 < kt_end;
-    // activations first: loads complete in issue order, so storing them at the
-    // end of the step does not wait for the code prefetch issued after them
-    u4 xv[ACH];
-    if (more) load_x(kt + 1, xv);
+    load_x(kt + 2, xld);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(kt + kBdepth, nxt);
-    if (live) {
-      const uint8_t* abase = lds + buf * TILE + aread;
+    load_b(kt + 3, nxt);
+    // scale / zero-point of this tile for the wave's blocks
+    const uint8_t* szt = szbase + ((kt / kSzChunk) & 1) * SZB;
+    const int tt = kt % kSzChunk;
+    uint32_t sv[NPW], zv[NPW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!FULL && kt * 128 + 32 * j >= a.K) break;  // ragged last step: no columns left
-        h8 af[MB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abase + i * 16 * kArow + 64 * j);
-#pragma unroll
-        for (int b = 0; b < NPW; ++b) {
-          h2 sc, nbias;
-          tile_consts<G>(cur.sz[b], kt, j, magic, sc, nbias);
-          const h8 bf = dequant_word(cur.codes[b][j], magic, nbias, sc);
-#pragma unroll
-          for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
-        }
+    for (int b = 0; b < NPW; ++b) {
+      if constexpr (G == 128) {
+        sv[b] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * (szrow + 16 * b));
+        zv[b] = sv[b] >> 16;
+      } else {
+        sv[b] = *reinterpret_cast<const uint32_t*>(szt + (tt * 2 + jp) * 512 + 4 * (szrow + 16 * b));
+        zv[b] = (uint32_t)*reinterpret_cast<const uint16_t*>(szt + kSzChunk * 1024 + tt * 256 + 2 * (szrow + 16 * b)) >>
+                (8 * jp);
       }
     }
-    if (more) store_x(buf ^ 1, xv);
+    const uint8_t* abuf = arow + (kt & 1) * XTILE;
+    auto mstep = [&](int jj) {
+      const int j = 2 * jp + jj;
+      if (!FULL && kt * 128 + 32 * j >= a.K) return;  // ragged last tile
+      const int slot = ((4 * j + c) ^ r) * 16;
+      h8 af[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abuf + i * 16 * 256 + slot);
+#pragma unroll
+      for (int b = 0; b < NPW; ++b) {
+        const uint32_t sb = G == 128 ? sv[b] & 0xffffu : (jj ? sv[b] >> 16 : sv[b] & 0xffffu);
+        const uint32_t z = G == 128 ? zv[b] & 15u : (zv[b] >> (4 * jj)) & 15u;
+        const h2 sc = as_h2(sb * 0x00010001u);
+        const h2 nbias = -as_h2(z * 0x00010001u + magic);
+        const h8 bf = dequant_word(jj ? cur[b].y : cur[b].x, magic, nbias, sc);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
+      }
+    };
+    mstep(0);
+    // the other buffer was last read before the previous barrier
+    store_x(kt + 1, xst);
+    mstep(1);
     lds_barrier();
   };
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
 
-  // steps where both halves have whole tiles with a successor, in groups of
-  // four (the ring size)
-  const int s_full = min(a.K / 128 - S, S - 1) & ~3;
-  int s0 = 0;
-  for (; s0 < s_full; s0 += 4) {
-    step(Full{}, s0, b0, b3);
-    step(Full{}, s0 + 1, b1, b0);
-    step(Full{}, s0 + 2, b2, b1);
-    step(Full{}, s0 + 3, b3, b2);
+  // whole tiles in groups of eight (two turns of the code ring, four of the
+  // activation registers); the next chunk's scales / zero-points are loaded
+  // at step 1 and stored at step 5
+  const int kt_full = (a.K / 128) & ~(kSzChunk - 1);
+  int kt = 0;
+  for (; kt < kt_full; kt += kSzChunk) {
+    const int ch = kt / kSzChunk;
+    step(Full{}, kt, xs0, xs1, b0, b3);
+    sz_load(ch + 1, szs);
+    step(Full{}, kt + 1, xs1, xs0, b1, b0);
+    step(Full{}, kt + 2, xs0, xs1, b2, b1);
+    step(Full{}, kt + 3, xs1, xs0, b3, b2);
+    step(Full{}, kt + 4, xs0, xs1, b0, b3);
+    sz_store(ch + 1, szs);
+    step(Full{}, kt + 5, xs1, xs0, b1, b0);
+    step(Full{}, kt + 6, xs0, xs1, b2, b1);
+    step(Full{}, kt + 7, xs1, xs0, b3, b2);
   }
-  for (; s0 < S; s0 += 4) {
-    step(Part{}, s0, b0, b3);
-    if (s0 + 1 < S) step(Part{}, s0 + 1, b1, b0);
-    if (s0 + 2 < S) step(Part{}, s0 + 2, b2, b1);
-    if (s0 + 3 < S) step(Part{}, s0 + 3, b3, b2);
+  // the rest (fewer than eight tiles, the last one possibly ragged); their
+  // chunk was staged during the previous chunk or before the loop
+  for (; kt < KT; kt += 4) {
+    step(Part{}, kt, xs0, xs1, b0, b3);
+    if (kt + 1 < KT) step(Part{}, kt + 1, xs1, xs0, b1, b0);
+    if (kt + 2 < KT) step(Part{}, kt + 2, xs0, xs1, b2, b1);
+    if (kt + 3 < KT) step(Part{}, kt + 3, xs1, xs0, b3, b2);
   }
 
-  // ---- add the second half's sums to the first half's (LDS reused), then
-  // lane (r, c) of the first half holds rows 4c..4c+3 of column r of each block
-  float* red = reinterpret_cast<float*>(smem);  // [4 column groups][MB*NPW*4][64]
+  // ---- add the second step pair's sums to the first's (LDS reused), then
+  // lane (r, c) of the first pair holds rows 4c..4c+3 of column r of each block
+  float* red = reinterpret_cast<float*>(smem);  // [column group][MB*NPW*4][64]
   constexpr int NACC = MB * NPW * 4;
-  if (kh == 1) {
+  if (jp == 1) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int b = 0; b < NPW; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(wn * NACC + (i * NPW + b) * 4 + e) * 64 + lane] = acc[i][b][e];
+        for (int e = 0; e < 4; ++e) red[(cgp * NACC + (i * NPW + b) * 4 + e) * 64 + lane] = acc[i][b][e];
   }
   lds_barrier();
-  if (kh == 1) return;
+  if (jp == 1) return;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -307,49 +343,51 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
       const int n = (nbw0 + b) * 16 + r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = acc[i][b][e] + red[(wn * NACC + (i * NPW + b) * 4 + e) * 64 + lane];
+        const float v = acc[i][b][e] + red[(cgp * NACC + (i * NPW + b) * 4 + e) * 64 + lane];
         const int m = mrow0 + 16 * i + 4 * c + e;
         if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v);
       }
     }
 }
 
-// Row blocks (MB) and column blocks per wave (NPW) for a problem of M rows.
-struct GemmTiles {
-  int MB, NPW;
-};
-GemmTiles gemm_tiles(int64_t M) {
-  if (M <= 16) return {1, 1};
-  if (M <= 32) return {2, 1};
-  if (M <= 64) return {4, 2};
-  return {8, 2};
+// Row blocks per workgroup for a problem of M rows.
+int gemm_mb(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+
+dim3 gemm_grid(int MB, int64_t M, int64_t N) {
+  return dim3((unsigned)(((N + 15) / 16 + 7) / 8), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
 }
 
-dim3 gemm_grid(int MB, int NPW, int64_t M, int64_t N) {
-  const int64_t cols = 4 * NPW;  // column blocks per workgroup
-  return dim3((unsigned)(((N + 15) / 16 + cols - 1) / cols), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+size_t gemm_lds(int MB, int group) {
+  // two activation buffers and two staged chunks of scales / zero-points; the
+  // final reduction ([4][MB*NPW*4][64] fp32) reuses the front of it
+  const size_t tiles =
+      (size_t)2 * MB * 16 * 256 + 2 * (size_t)(group == 128 ? sz_chunk_bytes<128>() : sz_chunk_bytes<32>());
+  const size_t red = (size_t)4 * MB * kNPW * 4 * 64 * sizeof(float);
+  return tiles > red ? tiles : red;
 }
 
-size_t gemm_lds(int MB, int NPW) {
-  // two halves x two buffers of activation tiles; the final reduction reuses it
-  const size_t lds_tiles = (size_t)4 * 16 * MB * kArow, lds_red = (size_t)4 * MB * NPW * 4 * 64 * sizeof(float);
-  return lds_tiles > lds_red ? lds_tiles : lds_red;
-}
-
-template <int MB, int NPW>
-hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid = gemm_grid(MB, NPW, a.M, a.N), block(kWaves * 64);
-  const size_t lds = gemm_lds(MB, NPW);
-  if (group == 128) {
-    auto k = gemm_kernel<MB, NPW, 128>;
-    if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<grid, block, lds, stream>>>(a);
-  } else {
-    auto k = gemm_kernel<MB, NPW, 32>;
-    if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<grid, block, lds, stream>>>(a);
-  }
+template <int MB, int G, bool SZV>
+hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid = gemm_grid(MB, a.M, a.N), block(kWaves * 64);
+  const size_t lds = gemm_lds(MB, G);
+  auto k = gemm_kernel<MB, G, SZV>;
+  if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  k<<<grid, block, lds, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int MB>
+hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
+  // wide staging loads of scales / zero-points when every row is aligned for
+  // them: g = 128 two scales (4 bytes); g = 32 eight scales (16 bytes) and
+  // eight zero-points (4 bytes)
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(a.s), zp = reinterpret_cast<uintptr_t>(a.zp);
+  if (group == 128) {
+    if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true>(a, stream);
+    return launch_kg<MB, 128, false>(a, stream);
+  }
+  if (a.Gtot % 8 == 0 && sp % 16 == 0 && zp % 4 == 0) return launch_kg<MB, 32, true>(a, stream);
+  return launch_kg<MB, 32, false>(a, stream);
 }
 
 }  // namespace
@@ -357,10 +395,10 @@ hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
 int describe_gemm(int64_t M, int64_t N, int64_t, int group, char* buf, size_t len) {
-  const GemmTiles t = gemm_tiles(M);
-  const dim3 g = gemm_grid(t.MB, t.NPW, M, N);
-  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d> grid=(%u,%u,1) block=%d lds=%zu", t.MB, t.NPW, group,
-                  g.x, g.y, kWaves * 64, gemm_lds(t.MB, t.NPW));
+  const int MB = gemm_mb(M);
+  const dim3 g = gemm_grid(MB, M, N);
+  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d> grid=(%u,%u,1) block=%d lds=%zu", MB, kNPW, group, g.x,
+                  g.y, kWaves * 64, gemm_lds(MB, group));
 }
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
@@ -379,17 +417,12 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_
   a.Gtot = (int)(K / group);
   a.GB = (a.Gtot + 1) / 2;
   a.NBLK = (int)((N + 15) / 16);
-  // g = 32: a tile's four scales (8 bytes) and zero-points (2 bytes) load as
-  // one vector each when every row starts suitably aligned
-  a.sz_vec = (group == 32 && a.Gtot % 4 == 0 && (reinterpret_cast<uintptr_t>(s) & 7) == 0 &&
-              (reinterpret_cast<uintptr_t>(zpacked) & 1) == 0)
-                 ? 1
-                 : 0;
-  const GemmTiles t = gemm_tiles(M);
-  if (t.MB == 1) return launch_t<1, 1>(group, a, stream);
-  if (t.MB == 2) return launch_t<2, 1>(group, a, stream);
-  if (t.MB == 4) return launch_t<4, 2>(group, a, stream);
-  return launch_t<8, 2>(group, a, stream);
+  switch (gemm_mb(M)) {
+    case 1: return launch_t<1>(group, a, stream);
+    case 2: return launch_t<2>(group, a, stream);
+    case 4: return launch_t<4>(group, a, stream);
+    default: return launch_t<8>(group, a, stream);
+  }
 }
 
 }  // namespace wq
