@@ -150,6 +150,18 @@ int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group,
                   const uint8_t* zpacked, uint16_t* y_f16,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* count products of one shape issued back to back on `stream`, in order:
+ * y_f16[i] = x_f16[i] * What_i^T with What_i from (qpacked[i], s_f16[i],
+ * zpacked[i]), as wq_gemm_w4a16 would compute each.  The five arrays are host
+ * arrays of count device pointers.  Every product is checked before the first
+ * is enqueued, so an argument error enqueues nothing; the products run in
+ * stream order, so one workspace (sized for the shape) serves all of them.
+ * For decode loops whose per-call host cost would exceed a kernel's time. */
+int wq_gemm_w4a16_seq(int count, int64_t M, int64_t N, int64_t K, int group,
+                      const uint16_t* const* x_f16, const uint32_t* const* qpacked,
+                      const uint16_t* const* s_f16, const uint8_t* const* zpacked,
+                      uint16_t* const* y_f16, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Describes, as one NUL-terminated line written into buf (host memory,
  * buf_len bytes, truncated to fit), the kernel and launch shape that
  * wq_gemm_w4a16_ex would use for this problem and path: kernel template

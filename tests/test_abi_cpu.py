@@ -133,3 +133,18 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 7, buf, 8) == wq.WQ_EINVAL
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 48, 0, buf, 8) == wq.WQ_EUNSUPPORTED
 
+
+
+def test_sequence_call_checks_every_product_first():
+    # host-only: an error in any product of the sequence returns before
+    # anything is enqueued (no GPU here, so nothing could run anyway)
+    P = ctypes.c_void_p
+    ok = (P * 2)(A, A)
+    bad = (P * 2)(A, None)
+    f = wq.lib().wq_gemm_w4a16_seq
+    assert f(2, 1, 16, 128, 128, ok, ok, ok, ok, bad, None, 0, None) == wq.WQ_EINVAL
+    assert f(2, 1, 16, 128, 128, ok, ok, ok, ok, (P * 2)(A, B), None, 0, None) == wq.WQ_EALIGN
+    assert f(-1, 1, 16, 128, 128, ok, ok, ok, ok, ok, None, 0, None) == wq.WQ_EINVAL
+    assert f(2, 1, 16, 128, 128, None, ok, ok, ok, ok, None, 0, None) == wq.WQ_EINVAL
+    assert f(0, 1, 16, 128, 128, None, None, None, None, None, None, 0, None) == wq.WQ_OK
+    assert f(1, 1, 16, 100, 32, ok, ok, ok, ok, ok, None, 0, None) == wq.WQ_EUNSUPPORTED

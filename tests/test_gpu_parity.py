@@ -280,3 +280,24 @@ def test_repeated_calls_are_deterministic():
         assert torch.equal(y1, y2)
     out2 = gpu_quantize(W, "bf16", group)
     assert torch.equal(out2["qw"].qpacked, out["qw"].qpacked)
+
+
+@pytest.mark.gpu
+def test_sequence_call_matches_single_calls():
+    # one host call issuing several products equals the single calls, for the
+    # GEMV (with a split-K workspace shared by the sequence) and the MFMA path
+    for (M, N, K, group) in [(3, 272, 640, 32), (1, 48, 8192, 128), (80, 100, 512, 128)]:
+        say(f"sequence M={M} N={N} K={K} g={group}")
+        qws, xs, refs = [], [], []
+        for t in range(3):
+            W, x = _matmul_inputs(M, N, K, group, 77 + t)
+            qw = gpu_quantize(W, "bf16", group)["qw"]
+            xd = to_dev_f16(x)
+            qws.append(qw)
+            xs.append(xd)
+            refs.append(wq.wq_gemm_w4a16(xd, qw))
+        ys = [torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda") for _ in range(3)]
+        wq.wq_gemm_w4a16_seq(xs, qws, ys)
+        torch.cuda.synchronize()
+        for y, ref in zip(ys, refs):
+            assert torch.equal(y, ref)

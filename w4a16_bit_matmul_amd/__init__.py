@@ -24,7 +24,7 @@ WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 
 EXPORTED = (
     "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_pack_int4", "wq_dequant",
-    "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex",
+    "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
 )
 
 _lib = None
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, ctypes.c_char_p, SZ]),
         "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
         "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
+        "wq_gemm_w4a16_seq": (I, [I, I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -181,3 +182,39 @@ def wq_gemm_w4a16(x: torch.Tensor, qw: QuantizedWeight, *, y: torch.Tensor | Non
                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
                                   path, _stream(stream)), "wq_gemm_w4a16")
     return y
+
+
+def wq_gemm_w4a16_seq_prepared(xs, qws, ys, *, workspace: torch.Tensor | None = None, stream=None):
+    """Marshals the arguments of wq_gemm_w4a16_seq once and returns a function
+    of no arguments that issues the whole sequence (one C call) on the stream
+    current at preparation time.  The buffers stay referenced by the function."""
+    count = len(xs)
+    assert len(qws) == count and len(ys) == count and count > 0
+    M, K = xs[0].shape
+    q0 = qws[0]
+    for x, qw, y in zip(xs, qws, ys):
+        assert x.shape == (M, K) and (qw.N, qw.K, qw.group) == (q0.N, q0.K, q0.group)
+        assert y.shape == (M, q0.N) and y.dtype == torch.float16
+    need = wq_gemm_workspace_bytes(M, q0.N, q0.K, q0.group)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=xs[0].device)
+    arr = lambda ts: (ctypes.c_void_p * count)(*[t.data_ptr() for t in ts])
+    args = (count, M, q0.N, q0.K, q0.group, arr(xs), arr([q.qpacked for q in qws]), arr([q.s for q in qws]),
+            arr([q.zpacked for q in qws]), arr(ys), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    fn = lib().wq_gemm_w4a16_seq
+    keep = (list(xs), list(qws), list(ys), workspace)
+
+    def call():
+        _check(fn(*args), "wq_gemm_w4a16_seq")
+        return keep[2]
+    return call
+
+
+def wq_gemm_w4a16_seq(xs, qws, ys, *, workspace: torch.Tensor | None = None, stream=None):
+    """ys[i] = xs[i] * What_i^T for every i, issued back to back by one C call
+    (wq_gemm_w4a16_seq).  All products have one shape; ys are preallocated
+    fp16 [M][N] tensors."""
+    if len(xs) == 0:
+        return ys
+    return wq_gemm_w4a16_seq_prepared(xs, qws, ys, workspace=workspace, stream=stream)()

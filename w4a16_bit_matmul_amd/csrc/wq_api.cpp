@@ -106,24 +106,64 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   return WQ_OK;
 }
 
-int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
-                     const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
-                     size_t workspace_bytes, int path, void* stream) {
+namespace {
+
+// Argument checks of one product (host only); 0 or a wq_status.
+int check_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
+               const uint16_t* s_f16, const uint8_t* zpacked, const uint16_t* y_f16, const void* workspace,
+               size_t workspace_bytes, int path, bool* mfma) {
   if (!x_f16 || !qpacked || !s_f16 || !zpacked || !y_f16) return WQ_EINVAL;
   if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
-  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t need = mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
+  *mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
     if (!aligned(workspace, 256)) return WQ_EALIGN;
   }
-  if (!mfma) return hip_status(wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s));
-  return hip_status(wq::launch_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s));
+  return WQ_OK;
+}
+
+hipError_t launch_one(bool mfma, int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16,
+                      const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16,
+                      void* workspace, hipStream_t s) {
+  if (!mfma) return wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
+  return wq::launch_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
+}
+
+}  // namespace
+
+int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
+                     size_t workspace_bytes, int path, void* stream) {
+  bool mfma = false;
+  const int st = check_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, workspace_bytes,
+                            path, &mfma);
+  if (st) return st;
+  return hip_status(launch_one(mfma, M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace,
+                               static_cast<hipStream_t>(stream)));
+}
+
+int wq_gemm_w4a16_seq(int count, int64_t M, int64_t N, int64_t K, int group, const uint16_t* const* x_f16,
+                      const uint32_t* const* qpacked, const uint16_t* const* s_f16, const uint8_t* const* zpacked,
+                      uint16_t* const* y_f16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 0 || (count > 0 && (!x_f16 || !qpacked || !s_f16 || !zpacked || !y_f16))) return WQ_EINVAL;
+  bool mfma = false;
+  for (int i = 0; i < count; ++i) {
+    const int st = check_gemm(M, N, K, group, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i], workspace,
+                              workspace_bytes, WQ_PATH_AUTO, &mfma);
+    if (st) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < count; ++i) {
+    const hipError_t e = launch_one(mfma, M, N, K, group, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i],
+                                    workspace, s);
+    if (e != hipSuccess) return WQ_EHIP;
+  }
+  return WQ_OK;
 }
 
 int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
