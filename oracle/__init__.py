@@ -60,6 +60,7 @@ def _load():
         "orc_f32_to_f16_array": (None, [P, I64, P]),
         "orc_f32_to_bf16_array": (None, [P, I64, P]),
         "orc_quantize_groups": (I, [P, I, I64, I64, I, P, P, P]),
+        "orc_quantize_groups_ex": (I, [P, I, I64, I64, I, I, P, P, P]),
         "orc_dequant": (I, [P, P, P, I64, I64, I, I, P]),
         "orc_pack_canonical": (I, [P, I64, I64, P]),
         "orc_device_bytes": (I64, [I64, I64]),
@@ -128,9 +129,14 @@ def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 
 # --- quantizer ---------------------------------------------------------------
 
-def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None):
-    """Group-wise asymmetric INT4 quantization of W[N][K] (the pages' "minimum
-    maths": s = (max - min)/15, z = round(-min/s), q = clip(round(w/s + z), 0, 15)).
+ASYM, SYM = 0, 1
+
+
+def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None, scheme: int = ASYM):
+    """Group-wise INT4 quantization of W[N][K].  ASYM: the pages' "minimum
+    maths" (s = (max - min)/15, z = round(-min/s), q = clip(round(w/s + z), 0,
+    15)).  SYM: symmetric 4-bit (s = max|w|/7, q = clip(round(w/s), -7, 7),
+    stored as q + 8 with zero-point 8).
 
     ``W`` is float32, or uint16 bit patterns with ``dtype`` BF16 or F16.
     Returns (q[N][K] uint8, s[N][K/g] uint16 fp16 bits, z[N][K/g] uint8).
@@ -146,7 +152,7 @@ def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None):
     q = np.empty((N, K), np.uint8)
     s = np.empty((N, G), np.uint16)
     z = np.empty((N, G), np.uint8)
-    _check(_load().orc_quantize_groups(_ptr(W), dtype, N, K, group, _ptr(q), _ptr(s), _ptr(z)),
+    _check(_load().orc_quantize_groups_ex(_ptr(W), dtype, N, K, group, scheme, _ptr(q), _ptr(s), _ptr(z)),
            "orc_quantize_groups")
     return q, s, z
 

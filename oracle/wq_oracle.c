@@ -31,6 +31,13 @@
  *   - a group whose stored scale is 0 stores s = 0, z = 0 and all codes 0;
  *   - a group whose range would give a non-finite fp16 scale is an error.
  *
+ * The symmetric variant ([T] "The maths that matter": b-bit symmetric range,
+ * s = M / (2^(b-1) - 1); [C] "What quantisation does": q = round(w / s)) at
+ * b = 4 uses the same storage: s = fp16(fl32(max|w| / 7)), q = clip(rne(fl32(w
+ * / s)), -7, 7), stored as the code q + 8 with zero-point 8, so that
+ * s * (code - 8) decodes it; a group whose stored scale is 0 stores s = 0,
+ * zero-point 8 and codes 8.
+ *
  * Packed layouts:
  *   canonical: [N][K/2] bytes, byte b of a row holds k = 2b in its low nibble
  *              and k = 2b+1 in its high nibble (the page only fixes that eight
@@ -204,10 +211,49 @@ static int quantize_one_group(const float* w, int g, uint8_t* q, uint16_t* s_out
     return 0;
 }
 
+/* One group, symmetric 4-bit ([T] "The maths that matter", b = 4):
+ *   s = M / (2^3 - 1),  M = max |w| over the group
+ *   q = clip(round(w / s), -7, 7), kept as the code q + 8 (zero-point 8)
+ * Returns 0, or ORC_ERANGE if the scale is not a finite fp16 number. */
+static int quantize_one_group_sym(const float* w, int g, uint8_t* q, uint16_t* s_out, uint8_t* z_out)
+{
+    float m = 0.0f;
+    for (int i = 0; i < g; ++i) {
+        if (!isfinite(w[i])) return ORC_ERANGE;
+        float a = fabsf(w[i]);
+        if (a > m) m = a;
+    }
+    float s32 = m / 7.0f;           /* one fp32 division */
+    uint16_t sh_bits = orc_f32_to_f16(s32);
+    float sh = orc_f16_to_f32(sh_bits);
+    if (!isfinite(sh)) return ORC_ERANGE;
+    *z_out = 8;
+    if (sh == 0.0f) { /* degenerate group: everything decodes to 0 */
+        *s_out = 0;
+        for (int i = 0; i < g; ++i) q[i] = 8;
+        return 0;
+    }
+    *s_out = sh_bits;
+    for (int i = 0; i < g; ++i) {
+        float r = nearbyintf(w[i] / sh);  /* fp32 division, then rne */
+        if (r < -7.0f) r = -7.0f;
+        if (r > 7.0f) r = 7.0f;
+        q[i] = (uint8_t)(r + 8.0f);
+    }
+    return 0;
+}
+
 int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
                         uint8_t* q, uint16_t* s, uint8_t* z)
 {
+    return orc_quantize_groups_ex(W, dtype, N, K, g, ORC_ASYM, q, s, z);
+}
+
+int orc_quantize_groups_ex(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
+                           uint8_t* q, uint16_t* s, uint8_t* z)
+{
     if (!W || !q || !s || !z || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (scheme != ORC_ASYM && scheme != ORC_SYM) return ORC_EINVAL;
     if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
     int64_t G = K / g;
     int status = 0;
@@ -216,7 +262,9 @@ int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
         float* buf = (float*)malloc(sizeof(float) * (size_t)g);
         for (int64_t j = 0; j < G; ++j) {
             for (int i = 0; i < g; ++i) buf[i] = load_w(W, dtype, n * K + j * g + i);
-            int st = quantize_one_group(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j);
+            int st = scheme == ORC_SYM
+                         ? quantize_one_group_sym(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j)
+                         : quantize_one_group(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j);
             if (st) {
 #pragma omp critical
                 status = st;

@@ -14,6 +14,7 @@ extern "C" {
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ERANGE = -6 };
+enum { ORC_ASYM = 0, ORC_SYM = 1 };  /* quantization scheme */
 
 void orc_set_threads(int n);
 int orc_get_threads(void);
@@ -27,6 +28,10 @@ void orc_f32_to_bf16_array(const float* a, int64_t n, uint16_t* out);
 
 int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
                         uint8_t* q, uint16_t* s, uint8_t* z);
+/* As orc_quantize_groups, with the scheme ORC_ASYM or ORC_SYM (symmetric 4-bit,
+ * codes q + 8 with zero-point 8). */
+int orc_quantize_groups_ex(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
+                           uint8_t* q, uint16_t* s, uint8_t* z);
 int orc_dequant(const uint8_t* q, const uint16_t* s, const uint8_t* z,
                 int64_t N, int64_t K, int g, int out_dtype, void* out);
 

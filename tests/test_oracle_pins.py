@@ -138,6 +138,90 @@ def test_symmetric_int4_outlier(orc):
         assert np.all(np.abs(w - w_hat) <= s / 2 * (1 + 1e-12))
 
 
+def _sym(orc, w, group, dtype=None):
+    w = np.ascontiguousarray(w, np.float32)
+    if w.ndim == 1:
+        w = w[None, :]
+    q, s, z = orc.quantize_groups(w, group, dtype=dtype, scheme=orc.SYM)
+    return q, s, z
+
+
+def test_symmetric_groups_printed_outlier_numbers(orc):
+    # The same page's INT4 calculation through the group quantizer with an fp16
+    # scale: a group holding the outlier 30.0 and values of magnitude about 1,
+    # and the same values with the outlier removed (M = 1).
+    g = golden("symmetric_int4_outlier.json")
+    rng = np.random.default_rng(11)
+    for case, group in [(c, grp) for c in g["cases"] for grp in (32, 128)]:
+        M = case["M"]
+        w = np.concatenate([[M], rng.uniform(-1.0, 1.0, group - 1)]).astype(np.float32)
+        if M < 2:
+            w = np.clip(w, -1.0, 1.0)
+            w[0] = 1.0
+        q, s, z = _sym(orc, w, group)
+        sh = float(orc.f16_bits_to_f32(s)[0])
+        assert z[0, 0] == 8
+        assert round(sh, 2 if M > 2 else 3) == case["s_approx"]
+        assert round(sh / 2, 2 if M > 2 else 3) == case["half_step_approx"]
+        w_hat = sh * (q[0].astype(np.float64) - 8)
+        # the half-step bound, widened by the fp16 rounding of the scale
+        s32 = np.float32(np.float32(M) / np.float32(7.0))
+        bound = sh / 2 + 7 * abs(float(s32) - sh)
+        assert np.all(np.abs(w - w_hat) <= bound * (1 + 1e-7))
+        # the outlier itself is the top code
+        assert q[0, 0] == 15
+
+
+def test_symmetric_groups_equal_textbook_when_scale_is_exact(orc):
+    # When max|w| = 7 * 2^e the scale 2^e is exact in fp32 and fp16, so the
+    # fp32 steps reduce to the fp64 textbook rule q = round(w / s) (its own
+    # implementation in orc.symmetric), codes offset by the zero-point 8.
+    rng = np.random.default_rng(12)
+    for e in (-9, -4, 0, 3):
+        for group in (32, 128):
+            w = rng.uniform(-7.0, 7.0, (6, group)) * 2.0 ** e
+            w[:, 0] = 7.0 * 2.0 ** e * np.where(np.arange(6) % 2, 1, -1)
+            w = w.astype(np.float32)
+            q, s, z = _sym(orc, w, group)
+            for r in range(6):
+                qt, st, wt = orc.symmetric(w[r].astype(np.float64), 4)
+                assert st == 2.0 ** e
+                assert orc.f16_bits_to_f32(s[r])[0] == 2.0 ** e
+                assert np.array_equal(q[r].astype(np.int64) - 8, qt)
+                assert np.array_equal(st * (q[r].astype(np.float64) - 8), wt)
+
+
+def test_symmetric_groups_invariants_ties_and_degenerate(orc):
+    rng = np.random.default_rng(13)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    W[:, 5] *= 20  # an outlier channel
+    for group in (32, 128):
+        q, s, z = _sym(orc, W, group)
+        assert np.all(z == 8) and q.min() >= 1 and q.max() <= 15
+        sh = orc.f16_bits_to_f32(s.ravel()).reshape(s.shape).astype(np.float64)
+        w_hat = np.repeat(sh, group, axis=1) * (q.astype(np.float64) - 8)
+        amax = np.abs(W.reshape(8, -1, group)).max(axis=2)
+        s32 = (amax.astype(np.float32) / np.float32(7.0)).astype(np.float64)
+        bound = np.repeat(sh / 2 + 7 * np.abs(s32 - sh), group, axis=1)
+        assert np.all(np.abs(W - w_hat) <= bound * (1 + 1e-7))
+        # negating the weights negates the symmetric codes
+        qn, sn, _ = _sym(orc, -W, group)
+        assert np.array_equal(sn, s) and np.array_equal(qn.astype(int) - 8, -(q.astype(int) - 8))
+    # exact halves round to even: s = 1 (max |w| = 7), w = k + 0.5
+    w = np.array([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5] + [0.0] * 24, np.float32)
+    q, s, z = _sym(orc, w, 32)
+    assert list(q[0, :8].astype(int) - 8) == [7, 0, 2, 2, 0, -2, -2, 4]
+    # an all-zero group: scale 0, zero-point 8, every code 8 (decodes to 0)
+    q, s, z = _sym(orc, np.zeros(32, np.float32), 32)
+    assert s[0, 0] == 0 and z[0, 0] == 8 and np.all(q == 8)
+    # bf16 input is widened exactly: same result as its fp32 value
+    Wb = orc.f32_to_bf16_bits(W)
+    qb, sb, zb = orc.quantize_groups(Wb, 32, dtype=orc.BF16, scheme=orc.SYM)
+    W32 = (Wb.astype(np.uint32) << 16).view(np.float32)
+    q2, s2, z2 = _sym(orc, W32, 32)
+    assert np.array_equal(qb, q2) and np.array_equal(sb, s2)
+
+
 # --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
