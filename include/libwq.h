@@ -71,7 +71,7 @@ extern "C" {
 
 typedef enum {
     WQ_OK = 0,
-    WQ_EINVAL = -1,       /* null pointer, non-positive size, bad dtype or path */
+    WQ_EINVAL = -1,       /* null pointer, non-positive size, bad dtype, path or scheme */
     WQ_EUNSUPPORTED = -2, /* group not 32 or 128, or K not a multiple of group */
     WQ_EALIGN = -3,       /* pointer not aligned as documented */
     WQ_EWORKSPACE = -4,   /* workspace missing or smaller than required */
@@ -79,6 +79,11 @@ typedef enum {
 } wq_status;
 
 typedef enum { WQ_F32 = 0, WQ_BF16 = 1, WQ_F16 = 2 } wq_dtype;
+
+typedef enum {
+    WQ_ASYM = 0, /* asymmetric: s = (max - min) / 15, z = round(-min / s) */
+    WQ_SYM = 1   /* symmetric: s = max|w| / 7, codes q + 8 (q in -7..7), z = 8 */
+} wq_scheme;
 
 typedef enum {
     WQ_PATH_AUTO = 0, /* M < 64: GEMV kernel; M >= 64: MFMA GEMM kernel */
@@ -112,6 +117,23 @@ int wq_layout_bytes(int64_t N, int64_t K, int group,
 int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group,
                        uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
                        uint32_t* qpacked, uint8_t* zpacked, void* stream);
+
+/* As wq_quantize_groups, with the quantization scheme (wq_scheme).  WQ_SYM is
+ * the symmetric 4-bit quantizer of "Test-time quantization", section "The
+ * maths that matter" (s = M / (2^(b-1) - 1) at b = 4, M = max|w| over the
+ * group) with the code q = round(w / s) of "Quantization Methods Compared",
+ * section "What quantisation does", read as:
+ *   s = fp16(fl32(M / 7)) (round-to-nearest-even, subnormals kept);
+ *   q = clamp(rne(fl32(w / s)), -7, 7), stored as the code q + 8;
+ *   zero-point 8 for every group (z_codes / zpacked hold 8), so
+ *   s * (code - zero-point) = s * q and every other entry point (dequant,
+ *   product) applies unchanged;
+ *   a group whose fp16 scale is 0 stores s = 0 and codes 8.
+ * Same arguments, layouts and error behaviour as wq_quantize_groups; WQ_EINVAL
+ * for an unknown scheme. */
+int wq_quantize_groups_ex(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
+                          uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
+                          uint32_t* qpacked, uint8_t* zpacked, void* stream);
 
 /* Packing of codes and zero-points into the device layouts -- "Numerical
  * example" (eight 4-bit codes occupy four bytes; a 4-bit zero-point takes half

@@ -37,18 +37,19 @@ def oracle_dtype(w_dtype: str) -> int:
     return {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[w_dtype]
 
 
-def gpu_quantize(W_host: np.ndarray, w_dtype: str, group: int):
+def gpu_quantize(W_host: np.ndarray, w_dtype: str, group: int, scheme: int = wq.WQ_ASYM):
     Wd = to_dev_weights(W_host, w_dtype)
-    out = wq.wq_quantize_groups(Wd, group, codes=True, packed=True)
+    out = wq.wq_quantize_groups(Wd, group, codes=True, packed=True, scheme=scheme)
     torch.cuda.synchronize()
     return out
 
 
-def assert_quantize_matches(W_host: np.ndarray, w_dtype: str, group: int, out=None):
+def assert_quantize_matches(W_host: np.ndarray, w_dtype: str, group: int, out=None, scheme: int = wq.WQ_ASYM):
     """Codes, scales, zero-points and both packed layouts bit-exact vs the oracle."""
     if out is None:
-        out = gpu_quantize(W_host, w_dtype, group)
-    q, s, z = oracle.quantize_groups(W_host, group, dtype=oracle_dtype(w_dtype))
+        out = gpu_quantize(W_host, w_dtype, group, scheme)
+    q, s, z = oracle.quantize_groups(W_host, group, dtype=oracle_dtype(w_dtype),
+                                     scheme=oracle.SYM if scheme == wq.WQ_SYM else oracle.ASYM)
     s_gpu = f16_bits(out["s"])
     assert np.array_equal(s_gpu, s), f"scales differ at {np.argwhere(s_gpu != s)[:5]}"
     z_gpu = out["z_codes"].cpu().numpy()

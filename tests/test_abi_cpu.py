@@ -148,3 +148,13 @@ def test_sequence_call_checks_every_product_first():
     assert f(2, 1, 16, 128, 128, None, ok, ok, ok, ok, None, 0, None) == wq.WQ_EINVAL
     assert f(0, 1, 16, 128, 128, None, None, None, None, None, None, 0, None) == wq.WQ_OK
     assert f(1, 1, 16, 100, 32, ok, ok, ok, ok, ok, None, 0, None) == wq.WQ_EUNSUPPORTED
+
+
+def test_quantize_scheme_checked_on_host():
+    # an unknown scheme, like any other argument error, returns before
+    # anything is enqueued
+    f = "wq_quantize_groups_ex"
+    assert call(f, A, wq.WQ_BF16, 16, 128, 128, 2, None, A, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, wq.WQ_BF16, 16, 128, 128, -1, None, A, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, wq.WQ_BF16, 16, 100, 32, wq.WQ_SYM, None, A, None, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, B, wq.WQ_BF16, 16, 128, 128, wq.WQ_SYM, None, A, None, A, A, None) == wq.WQ_EALIGN

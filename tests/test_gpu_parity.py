@@ -301,3 +301,58 @@ def test_sequence_call_matches_single_calls():
         torch.cuda.synchronize()
         for y, ref in zip(ys, refs):
             assert torch.equal(y, ref)
+
+
+# ---------------------------------------------------------------- symmetric scheme
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,K,group", SHAPES)
+def test_quantize_symmetric_bit_exact(N, K, group, w_dtype):
+    say(f"quantize sym N={N} K={K} g={group} {w_dtype}")
+    W = _weights(N, K, 900 + N + K, w_dtype)
+    q, s, z, _ = assert_quantize_matches(W, w_dtype, group, scheme=wq.WQ_SYM)
+    assert np.all(z == 8) and q.min() >= 0 and q.max() <= 15
+
+
+def test_quantize_symmetric_edge_groups():
+    # all-zero groups, exact halves (max |w| = 7: scale 1), one-signed groups,
+    # a single outlier, subnormal-scale groups
+    say("quantize sym edge groups")
+    K, group = 256, 32
+    W = np.zeros((16, K), np.float32)
+    W[1, :32] = np.array([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5] * 4, np.float32)
+    W[2, :] = np.abs(np.linspace(0.1, 3.0, K, dtype=np.float32))
+    W[3, :] = -np.abs(np.linspace(0.1, 3.0, K, dtype=np.float32))
+    W[4, 40] = 30.0
+    W[4, 41:64] = np.linspace(-1, 1, 23, dtype=np.float32)
+    W[5, :] = np.float32(3e-6) * np.sin(np.arange(K, dtype=np.float32))
+    q, s, z, _ = assert_quantize_matches(W, "f32", group, scheme=wq.WQ_SYM)
+    assert np.all(q[0] == 8) and np.all(s[0] == 0)
+    assert list(q[1, :8].astype(int) - 8) == [7, 0, 2, 2, 0, -2, -2, 4]
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_dequant_symmetric_bit_exact(group):
+    say(f"dequant sym g={group}")
+    N, K = 130, 1152 if group == 128 else 544
+    W = workloads.gen_weights(931 + group, N, K, outlier_frac=0.01, dtype="bf16")
+    q, s, z, out = assert_quantize_matches(W, "bf16", group, scheme=wq.WQ_SYM)
+    got = wq.wq_dequant(out["qw"], torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.dequant(q, s, z, group))
+
+
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
+@pytest.mark.parametrize("M,N,K,group", [(1, 1000, 1152, 128), (5, 300, 512, 32), (77, 130, 1024, 32),
+                                         (128, 512, 2048, 128), (1, 48, 8192, 128)])
+def test_matmul_symmetric_within_tolerance(M, N, K, group, path):
+    say(f"matmul sym M={M} N={N} K={K} g={group} path={path}")
+    W, x = _matmul_inputs(M, N, K, group, 950 + M + N + K)
+    out = gpu_quantize(W, "bf16", group, scheme=wq.WQ_SYM)
+    q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16, scheme=oracle.SYM)
+    y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
+    torch.cuda.synchronize()
+    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+

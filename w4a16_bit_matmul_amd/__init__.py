@@ -21,9 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2, -3, -4, -5
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
+WQ_ASYM, WQ_SYM = 0, 1
 
 EXPORTED = (
-    "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_pack_int4", "wq_dequant",
+    "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_quantize_groups_ex", "wq_pack_int4",
+    "wq_dequant",
     "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
 )
 
@@ -51,6 +53,7 @@ def lib() -> ctypes.CDLL:
         "wq_strerror": (ctypes.c_char_p, [I]),
         "wq_layout_bytes": (I, [I64, I64, I, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "wq_quantize_groups": (I, [P, I, I64, I64, I, P, P, P, P, P, P]),
+        "wq_quantize_groups_ex": (I, [P, I, I64, I64, I, I, P, P, P, P, P, P]),
         "wq_pack_int4": (I, [P, P, I64, I64, I, P, P, P]),
         "wq_dequant": (I, [P, P, P, I64, I64, I, I, P, P]),
         "wq_gemm_workspace_bytes": (SZ, [I64, I64, I64, I]),
@@ -128,8 +131,10 @@ def alloc_quantized(N: int, K: int, group: int, device="cuda") -> QuantizedWeigh
 
 
 def wq_quantize_groups(W: torch.Tensor, group: int, *, codes: bool = False, packed: bool = True,
-                       out: QuantizedWeight | None = None, stream=None):
-    """Quantize W[N][K] (float32, bfloat16 or float16, on the GPU).
+                       out: QuantizedWeight | None = None, scheme: int = WQ_ASYM, stream=None):
+    """Quantize W[N][K] (float32, bfloat16 or float16, on the GPU) with the
+    asymmetric (WQ_ASYM) or symmetric (WQ_SYM: codes q + 8, zero-point 8)
+    4-bit scheme.
 
     Returns a dict with ``s`` (fp16 [N][G]) and, as requested, ``q_codes``
     (uint8 [N][K]), ``z_codes`` (uint8 [N][G]) and ``qw`` (QuantizedWeight with
@@ -143,9 +148,9 @@ def wq_quantize_groups(W: torch.Tensor, group: int, *, codes: bool = False, pack
     s = qw.s if packed else torch.empty((N, G), dtype=torch.float16, device=dev)
     q_codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes else None
     z_codes = torch.empty((N, G), dtype=torch.uint8, device=dev) if codes else None
-    _check(lib().wq_quantize_groups(_ptr(W), _DT.get(W.dtype, -1), N, K, group, _ptr(q_codes), _ptr(s),
-                                    _ptr(z_codes), _ptr(qw.qpacked) if packed else None,
-                                    _ptr(qw.zpacked) if packed else None, _stream(stream)),
+    _check(lib().wq_quantize_groups_ex(_ptr(W), _DT.get(W.dtype, -1), N, K, group, scheme, _ptr(q_codes), _ptr(s),
+                                       _ptr(z_codes), _ptr(qw.qpacked) if packed else None,
+                                       _ptr(qw.zpacked) if packed else None, _stream(stream)),
            "wq_quantize_groups")
     return {"s": s, "q_codes": q_codes, "z_codes": z_codes, "qw": qw if packed else None}
 

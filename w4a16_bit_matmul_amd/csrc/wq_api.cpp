@@ -33,7 +33,7 @@ int wq_version(void) { return kVersion; }
 const char* wq_strerror(int status) {
   switch (status) {
     case WQ_OK: return "success";
-    case WQ_EINVAL: return "invalid argument (null pointer, non-positive size, bad dtype or path)";
+    case WQ_EINVAL: return "invalid argument (null pointer, non-positive size, bad dtype, path or scheme)";
     case WQ_EUNSUPPORTED: return "unsupported shape (group must be 32 or 128 and divide K)";
     case WQ_EALIGN: return "pointer not aligned as required";
     case WQ_EWORKSPACE: return "workspace missing or too small";
@@ -52,16 +52,23 @@ int wq_layout_bytes(int64_t N, int64_t K, int group, size_t* qpacked_bytes, size
   return WQ_OK;
 }
 
-int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
-                       uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, void* stream) {
+int wq_quantize_groups_ex(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
+                          uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked,
+                          void* stream) {
   if (!W || !s_f16) return WQ_EINVAL;
   if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
+  if (scheme != WQ_ASYM && scheme != WQ_SYM) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
   if (!aligned(W, 16) || !aligned(s_f16, 2) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8)))
     return WQ_EALIGN;
-  return hip_status(wq::launch_quantize(W, w_dtype, N, K, group, q_codes, s_f16, z_codes, qpacked, zpacked,
-                                        static_cast<hipStream_t>(stream)));
+  return hip_status(wq::launch_quantize(W, w_dtype, N, K, group, scheme == WQ_SYM, q_codes, s_f16, z_codes, qpacked,
+                                        zpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+                       uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, void* stream) {
+  return wq_quantize_groups_ex(W, w_dtype, N, K, group, WQ_ASYM, q_codes, s_f16, z_codes, qpacked, zpacked, stream);
 }
 
 int wq_pack_int4(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group, uint32_t* qpacked,

@@ -6,7 +6,9 @@
 
 namespace wq {
 
-hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+// sym: the symmetric 4-bit scheme (codes q + 8, zero-point 8) instead of the
+// asymmetric one.
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, uint8_t* q_codes,
                            uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream);
 
 hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group,

@@ -5,6 +5,11 @@
 // zero-point" (s = (max - min) / 15, z = round(-min / s),
 // q = clip(round(w / s + z), 0, 15), decoding s * (q - z)) and section
 // "Numerical example" (8 codes in 4 bytes, a 4-bit zero-point in half a byte).
+// Symmetric variant: "Test-time quantization", section "The maths that
+// matter" (b-bit symmetric range, s = M / (2^(b-1) - 1)) with the code of
+// "Quantization Methods Compared", section "What quantisation does"
+// (q = round(w / s)); at b = 4 the code q in [-7, 7] is stored as q + 8 with
+// zero-point 8, so every kernel that decodes s * (q - z) decodes it.
 //
 // This translation unit is compiled with -ffp-contract=off: every fp32
 // operation below is one correctly rounded IEEE operation (division is the
@@ -84,6 +89,26 @@ __device__ __forceinline__ GroupParams group_params(float lo, float hi) {
   return p;
 }
 
+// Symmetric 4-bit: s = max|w| / 7 (max|w| = max(hi, -lo)), zero-point 8; a
+// group whose fp16 scale is 0 stores s = 0 and codes 8.
+__device__ __forceinline__ GroupParams group_params_sym(float lo, float hi) {
+  const float m = fmaxf(hi, -lo);
+  const float s32 = m / 7.0f;
+  GroupParams p;
+  p.s_bits = f32_to_f16_bits(s32);
+  p.s = f16_bits_to_f32(p.s_bits);
+  p.z = 8.0f;
+  if (p.s == 0.0f) p.s_bits = 0;
+  return p;
+}
+
+__device__ __forceinline__ uint32_t encode_sym(float w, const GroupParams& p) {
+  if (p.s == 0.0f) return 8u;
+  float r = rintf(w / p.s);
+  r = fminf(fmaxf(r, -7.0f), 7.0f);
+  return (uint32_t)(r + 8.0f);
+}
+
 __device__ __forceinline__ uint32_t encode(float w, const GroupParams& p) {
   if (p.s == 0.0f) return 0u;
   float t = w / p.s;
@@ -96,7 +121,7 @@ __device__ __forceinline__ uint32_t encode(float w, const GroupParams& p) {
 // Nibble position of column e (0..7) inside a packed word.
 __device__ __forceinline__ int nibble_pos(int e) { return 4 * (e & 1) + (e >> 1); }
 
-template <int DT, int G>
+template <int DT, int G, bool SYM>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, int64_t NBLK, int64_t KT,
     uint8_t* __restrict__ q_codes, uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_codes,
@@ -140,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
         for (int e = 0; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
       lo = wave_min4(lo);
       hi = wave_max4(hi);
-      GroupParams p = group_params(lo, hi);
+      GroupParams p = SYM ? group_params_sym(lo, hi) : group_params(lo, hi);
 #pragma unroll
       for (int j = 0; j < 4; ++j) gp[j] = p;
     } else {
@@ -151,7 +176,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
         for (int e = 1; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
         lo = wave_min4(lo);
         hi = wave_max4(hi);
-        gp[j] = group_params(lo, hi);
+        gp[j] = SYM ? group_params_sym(lo, hi) : group_params(lo, hi);
       }
     }
 
@@ -162,7 +187,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       uint32_t codes[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        codes[e] = jok[j] ? encode(w[j][e], gp[j]) : 0u;
+        codes[e] = jok[j] ? (SYM ? encode_sym(w[j][e], gp[j]) : encode(w[j][e], gp[j])) : 0u;
         word |= codes[e] << (4 * nibble_pos(e));
       }
       words[j] = word;
@@ -318,16 +343,25 @@ inline int64_t blocks_for(int64_t waves) { return (waves + kWavesPerBlock - 1) /
 
 }  // namespace
 
-hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, uint8_t* q_codes,
                            uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream) {
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128, ST = (KT + 1) / 2;
   dim3 grid((unsigned)blocks_for(NBLK * ST)), block(256);
-#define WQ_Q(DT, G) quantize_kernel<DT, G><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, s, z_codes, qpacked, zpacked)
+#define WQ_Q(DT, G, S) \
+  quantize_kernel<DT, G, S><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, s, z_codes, qpacked, zpacked)
+#define WQ_QS(DT, G) \
+  do {                  \
+    if (sym)            \
+      WQ_Q(DT, G, true);  \
+    else                \
+      WQ_Q(DT, G, false); \
+  } while (0)
   if (group == 128) {
-    if (dtype == 0) WQ_Q(0, 128); else if (dtype == 1) WQ_Q(1, 128); else WQ_Q(2, 128);
+    if (dtype == 0) WQ_QS(0, 128); else if (dtype == 1) WQ_QS(1, 128); else WQ_QS(2, 128);
   } else {
-    if (dtype == 0) WQ_Q(0, 32); else if (dtype == 1) WQ_Q(1, 32); else WQ_Q(2, 32);
+    if (dtype == 0) WQ_QS(0, 32); else if (dtype == 1) WQ_QS(1, 32); else WQ_QS(2, 32);
   }
+#undef WQ_QS
 #undef WQ_Q
   return hipGetLastError();
 }
