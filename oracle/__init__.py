@@ -70,6 +70,12 @@ def _load():
         "orc_gemm_f64": (I, [I64, I64, I64, P, P, P]),
         "orc_gemm_rows_f64": (I, [I64, I64, I64, I, P, P, P, P, I64, I64, P]),
         "orc_symmetric": (I, [P, I64, I, P, P, P]),
+        "orc_quantize_w8": (I, [P, I, I64, I64, I, P, P]),
+        "orc_dequant_w8": (I, [P, P, I64, I64, I, I, P]),
+        "orc_device_bytes_w8": (I64, [I64, I64]),
+        "orc_pack_device_w8": (I, [P, I64, I64, P]),
+        "orc_unpack_device_w8": (I, [P, I64, I64, P]),
+        "orc_gemm_rows_w8_f64": (I, [I64, I64, I64, I, P, P, P, I64, I64, P]),
         "orc_bits_per_weight": (ctypes.c_double, [I, I, I, I]),
         "orc_storage_bytes": (ctypes.c_double, [I64, I, I, I, I]),
     }
@@ -230,6 +236,69 @@ def gemm_rows_f64(x_f16_bits, q, s, z, group: int, n0: int, nrows: int) -> np.nd
     y = np.empty((M, nrows), np.float64)
     _check(_load().orc_gemm_rows_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), _ptr(z), n0, nrows, _ptr(y)),
            "orc_gemm_rows_f64")
+    return y
+
+
+# --- group absmax int8 (W8A16) ---------------------------------------------
+
+def quantize_w8(W: np.ndarray, group: int, dtype: int | None = None):
+    """Group absmax int8 ("Quantization Methods Compared", section "What
+    quantisation does": s = max|w| / 127, q = round(w / s)) with an fp16 scale
+    per group of ``group`` weights along K: s = fp16(fl32(max|w| / 127)),
+    q = clip(rne(fl32(w / s)), -127, 127); a zero scale gives codes 0.
+    Returns (q[N][K] int8, s[N][K/g] uint16 fp16 bits)."""
+    W = np.ascontiguousarray(W)
+    if dtype is None:
+        if W.dtype == np.float32:
+            dtype = F32
+        else:
+            raise ValueError("give dtype for non-float32 input")
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // group), np.uint16)
+    _check(_load().orc_quantize_w8(_ptr(W), dtype, N, K, group, _ptr(q), _ptr(s)), "orc_quantize_w8")
+    return q, s
+
+
+def dequant_w8(q: np.ndarray, s: np.ndarray, group: int, out_dtype: int = F32) -> np.ndarray:
+    """w_hat = s * q (exact in fp32), as fp32 values or fp16/bf16 bits."""
+    q = np.ascontiguousarray(q, np.int8)
+    s = np.ascontiguousarray(s, np.uint16)
+    N, K = q.shape
+    out = np.empty((N, K), np.float32 if out_dtype == F32 else np.uint16)
+    _check(_load().orc_dequant_w8(_ptr(q), _ptr(s), N, K, group, out_dtype, _ptr(out)), "orc_dequant_w8")
+    return out
+
+
+def device_bytes_w8(N: int, K: int) -> int:
+    return int(_load().orc_device_bytes_w8(N, K))
+
+
+def pack_device_w8(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.int8)
+    N, K = q.shape
+    out = np.empty(device_bytes_w8(N, K), np.uint8)
+    _check(_load().orc_pack_device_w8(_ptr(q), N, K, _ptr(out)), "orc_pack_device_w8")
+    return out
+
+
+def unpack_device_w8(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, np.uint8)
+    q = np.empty((N, K), np.int8)
+    _check(_load().orc_unpack_device_w8(_ptr(packed), N, K, _ptr(q)), "orc_unpack_device_w8")
+    return q
+
+
+def gemm_rows_w8_f64(x_f16_bits, q, s, group: int, n0: int, nrows: int) -> np.ndarray:
+    """Columns n0..n0+nrows-1 of y = x * (s * q)^T (all M rows), in fp64."""
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    q = np.ascontiguousarray(q, np.int8)
+    s = np.ascontiguousarray(s, np.uint16)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, nrows), np.float64)
+    _check(_load().orc_gemm_rows_w8_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), n0, nrows, _ptr(y)),
+           "orc_gemm_rows_w8_f64")
     return y
 
 

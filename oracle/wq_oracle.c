@@ -53,6 +53,20 @@
  *              definition; the tests check it is a bijection.)
  *   zeros:     [N][ceil(G/2)] bytes, G = K/g groups per row, group j in the
  *              low nibble of byte j/2 when j is even, high nibble when odd.
+ *
+ * Group absmax int8 ([C] "What quantisation does": s = max|w| / 127,
+ * q = round(w / s), w_hat = q * s, one scale per group of g weights), read the
+ * same way: s = fp16(fl32(max|w| / 127)), q = clip(rne(fl32(w / s)), -127, 127)
+ * with the stored scale s, no zero-point, and a group whose stored scale is 0
+ * stores s = 0 and codes 0.  w_hat = s * q is exact in fp32 (an 11-bit
+ * significand times a 7-bit integer).  Its device layout (a definition, parity
+ * unpinned by the pages; the tests check it is a bijection):
+ *   device8:   16-row x 128-column tiles of 2048 bytes, tile (nb, kt) at byte
+ *              offset (nb * ceil(K/128) + kt) * 2048; inside a tile, half
+ *              h = 0, 1 at 1024 * h; in it lane l = r + 16*c owns the 16 bytes
+ *              at 16*l, whose byte 8*i + e (i = 0, 1; e = 0..7) holds column
+ *              32*(2h + i) + 8*c + e of row r, as a two's-complement byte.
+ *              Padding rows and columns hold code 0.
  */
 #include "wq_oracle.h"
 
@@ -404,6 +418,134 @@ int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_
         int64_t n = n0 + i;
         float* wr = (float*)malloc(sizeof(float) * (size_t)K);
         orc_dequant(q + n * K, s + n * G, z + n * G, 1, K, g, ORC_F32, wr);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            y_rows[m * nrows + i] = acc;
+        }
+        free(wr);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Group absmax int8  ([C] "What quantisation does")                         */
+/* ------------------------------------------------------------------------- */
+
+/* One group of g weights -> one fp16 scale and g int8 codes:
+ *   s = max|w| / 127,  q = clip(round(w / s), -127, 127)
+ * Returns 0, or ORC_ERANGE for a non-finite weight or fp16 scale. */
+static int quantize_one_group_w8(const float* w, int g, int8_t* q, uint16_t* s_out)
+{
+    float m = 0.0f;
+    for (int i = 0; i < g; ++i) {
+        if (!isfinite(w[i])) return ORC_ERANGE;
+        float a = fabsf(w[i]);
+        if (a > m) m = a;
+    }
+    float s32 = m / 127.0f;         /* one fp32 division */
+    uint16_t sh_bits = orc_f32_to_f16(s32);
+    float sh = orc_f16_to_f32(sh_bits);
+    if (!isfinite(sh)) return ORC_ERANGE;
+    if (sh == 0.0f) { /* degenerate group: everything decodes to 0 */
+        *s_out = 0;
+        for (int i = 0; i < g; ++i) q[i] = 0;
+        return 0;
+    }
+    *s_out = sh_bits;
+    for (int i = 0; i < g; ++i) {
+        float r = nearbyintf(w[i] / sh);  /* fp32 division, then rne */
+        if (r < -127.0f) r = -127.0f;
+        if (r > 127.0f) r = 127.0f;
+        q[i] = (int8_t)r;
+    }
+    return 0;
+}
+
+int orc_quantize_w8(const void* W, int dtype, int64_t N, int64_t K, int g, int8_t* q, uint16_t* s)
+{
+    if (!W || !q || !s || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
+    int64_t G = K / g;
+    int status = 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        float* buf = (float*)malloc(sizeof(float) * (size_t)g);
+        for (int64_t j = 0; j < G; ++j) {
+            for (int i = 0; i < g; ++i) buf[i] = load_w(W, dtype, n * K + j * g + i);
+            int st = quantize_one_group_w8(buf, g, q + n * K + j * g, s + n * G + j);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* Decoding  w_hat = s * q, exact in fp32; fp16 / bf16 are one rounding of it. */
+int orc_dequant_w8(const int8_t* q, const uint16_t* s, int64_t N, int64_t K, int g, int out_dtype, void* out)
+{
+    if (!q || !s || !out || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EINVAL;
+    int64_t G = K / g;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float v = orc_f16_to_f32(s[n * G + k / g]) * (float)q[n * K + k];
+            if (out_dtype == ORC_F32) ((float*)out)[n * K + k] = v;
+            else if (out_dtype == ORC_F16) ((uint16_t*)out)[n * K + k] = orc_f32_to_f16(v);
+            else ((uint16_t*)out)[n * K + k] = orc_f32_to_bf16(v);
+        }
+    return 0;
+}
+
+int64_t orc_device_bytes_w8(int64_t N, int64_t K)
+{
+    int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128;
+    return Np * Kp;
+}
+
+/* Byte offset of element (n, k) in the device8 layout. */
+static int64_t device8_pos(int64_t n, int64_t k, int64_t K)
+{
+    int64_t KT = (K + 127) / 128;
+    int64_t nb = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
+    int64_t j = kk / 32, c = (kk % 32) / 8, e = kk % 8;
+    int64_t h = j / 2, i = j % 2, lane = r + 16 * c;
+    return (nb * KT + kt) * 2048 + h * 1024 + lane * 16 + i * 8 + e;
+}
+
+int orc_pack_device_w8(const int8_t* q, int64_t N, int64_t K, uint8_t* out)
+{
+    if (!q || !out || N <= 0 || K <= 0) return ORC_EINVAL;
+    memset(out, 0, (size_t)orc_device_bytes_w8(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) out[device8_pos(n, k, K)] = (uint8_t)q[n * K + k];
+    return 0;
+}
+
+int orc_unpack_device_w8(const uint8_t* packed, int64_t N, int64_t K, int8_t* q)
+{
+    if (!packed || !q || N <= 0 || K <= 0) return ORC_EINVAL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) q[n * K + k] = (int8_t)packed[device8_pos(n, k, K)];
+    return 0;
+}
+
+/* Rows [n0, n0 + nrows) of y = x * What^T with What = s * q (int8 codes),
+ * dequantized by orc_dequant_w8 and multiplied in fp64 in k order. */
+int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
+                         const int8_t* q, const uint16_t* s, int64_t n0, int64_t nrows, double* y_rows)
+{
+    if (!x_f16 || !q || !s || !y_rows || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
+    if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
+    int64_t G = K / g;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = n0 + i;
+        float* wr = (float*)malloc(sizeof(float) * (size_t)K);
+        orc_dequant_w8(q + n * K, s + n * G, 1, K, g, ORC_F32, wr);
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];

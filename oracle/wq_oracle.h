@@ -46,6 +46,15 @@ int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_
                       const uint8_t* q, const uint16_t* s, const uint8_t* z,
                       int64_t n0, int64_t nrows, double* y_rows);
 
+/* Group absmax int8: s = fp16(max|w| / 127), q = clip(rne(w / s), -127, 127). */
+int orc_quantize_w8(const void* W, int dtype, int64_t N, int64_t K, int g, int8_t* q, uint16_t* s);
+int orc_dequant_w8(const int8_t* q, const uint16_t* s, int64_t N, int64_t K, int g, int out_dtype, void* out);
+int64_t orc_device_bytes_w8(int64_t N, int64_t K);
+int orc_pack_device_w8(const int8_t* q, int64_t N, int64_t K, uint8_t* out);
+int orc_unpack_device_w8(const uint8_t* packed, int64_t N, int64_t K, int8_t* q);
+int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
+                         const int8_t* q, const uint16_t* s, int64_t n0, int64_t nrows, double* y_rows);
+
 int orc_symmetric(const double* w, int64_t n, int bits, int32_t* q, double* s_out, double* w_hat);
 
 double orc_bits_per_weight(int bits, int g, int scale_bits, int zero_bits);

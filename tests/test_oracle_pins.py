@@ -223,6 +223,184 @@ def test_symmetric_groups_invariants_ties_and_degenerate(orc):
 
 
 # --------------------------------------------------------------------------
+# Group absmax int8 (W8A16): the same page's int8 rule with an fp16 scale per
+# group of 32 or 128 weights
+# --------------------------------------------------------------------------
+
+def _w8(orc, w, group, dtype=None):
+    w = np.ascontiguousarray(w, np.float32)
+    if w.ndim == 1:
+        w = w[None, :]
+    return orc.quantize_w8(w, group, dtype=dtype)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_w8_groups_printed_example(orc, group):
+    # The four printed weights, and the same with the outlier 20.0 appended,
+    # padded with zeros to a whole group (zeros change neither max|w| nor the
+    # other codes).
+    g = golden("int8_absmax_example.json")
+    w = np.zeros(group, np.float32)
+    w[:4] = g["w"]
+    q, s = _w8(orc, w, group)
+    sh = float(orc.f16_bits_to_f32(s)[0])
+    assert list(q[0, :4]) == [17, -71, 47, 127] and np.all(q[0, 4:] == 0)
+    w_hat = sh * q[0, :4].astype(np.float64)
+    assert np.max(np.abs(w_hat - w[:4]) / np.abs(w[:4])) < 0.01  # below one percent
+    w[4] = g["outlier"]
+    q, s = _w8(orc, w, group)
+    sh = float(orc.f16_bits_to_f32(s)[0])
+    assert round(sh, 4) == g["printed"]["s_with_outlier"]
+    assert list(q[0, :5]) == [1, -3, 2, 6, 127]
+    assert round(100 * abs(sh * 1 - w[0]) / w[0]) == g["printed"]["relative_error_with_outlier_percent"]
+
+
+def test_w8_groups_equal_textbook_when_scale_is_exact(orc):
+    # max|w| = 127 * 2^e makes s = 2^e exact in fp32 and fp16: the fp32 steps
+    # reduce to the fp64 textbook rule (orc.symmetric at 8 bits).
+    rng = np.random.default_rng(21)
+    for e in (-12, -7, 0, 2):
+        for group in (32, 128):
+            w = rng.uniform(-127.0, 127.0, (6, group)) * 2.0 ** e
+            w[:, 3] = 127.0 * 2.0 ** e * np.where(np.arange(6) % 2, 1, -1)
+            w = w.astype(np.float32)
+            q, s = _w8(orc, w, group)
+            for r in range(6):
+                qt, st, wt = orc.symmetric(w[r].astype(np.float64), 8)
+                assert st == 2.0 ** e
+                assert orc.f16_bits_to_f32(s[r])[0] == 2.0 ** e
+                assert np.array_equal(q[r].astype(np.int64), qt)
+                assert np.array_equal(st * q[r].astype(np.float64), wt)
+
+
+def test_w8_groups_invariants(orc):
+    rng = np.random.default_rng(22)
+    W = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
+    W[:, 17] *= 20  # an outlier channel
+    for group in (32, 128):
+        q, s = _w8(orc, W, group)
+        sh = orc.f16_bits_to_f32(s.ravel()).reshape(s.shape).astype(np.float64)
+        assert q.min() >= -127 and q.max() <= 127
+        # half-step bound, widened by the fp16 rounding of the scale
+        amax = np.abs(W.reshape(8, -1, group)).max(axis=2)
+        s32 = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float64)
+        bound = np.repeat(sh / 2 + 127 * np.abs(s32 - sh), group, axis=1)
+        w_hat = np.repeat(sh, group, axis=1) * q.astype(np.float64)
+        assert np.all(np.abs(W - w_hat) <= bound * (1 + 1e-7))
+        # every group's largest magnitude gets the top code
+        Wg, qg = W.reshape(8, -1, group), q.reshape(8, -1, group).astype(int)
+        top = np.take_along_axis(qg, np.abs(Wg).argmax(axis=2)[..., None], axis=2)[..., 0]
+        assert np.all(np.abs(top) == 127)
+        # codes keep the order of the weights inside a group, and the sign
+        order = np.argsort(Wg, axis=2, kind="stable")
+        assert np.all(np.diff(np.take_along_axis(qg, order, axis=2), axis=2) >= 0)
+        assert np.all(np.sign(qg) * np.sign(Wg) >= 0)
+        # negating the weights negates the codes; scales unchanged
+        qn, sn = _w8(orc, -W, group)
+        assert np.array_equal(sn, s) and np.array_equal(qn.astype(int), -q.astype(int))
+        # re-quantizing the decoded weights returns the same codes and scales
+        q2, s2 = _w8(orc, orc.dequant_w8(q, s, group), group)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+def test_w8_ties_degenerate_and_input_dtypes(orc):
+    # exact halves round to even: s = 1 (max |w| = 127), w = k + 0.5
+    w = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5] + [0.0] * 24, np.float32)
+    q, s = _w8(orc, w, 32)
+    assert orc.f16_bits_to_f32(s)[0] == 1.0
+    assert list(q[0, :8]) == [127, 0, 2, 2, 0, -2, -2, 126]
+    # all-zero group: scale 0, codes 0; a tiny group whose scale underflows fp16
+    q, s = _w8(orc, np.zeros(32, np.float32), 32)
+    assert s[0, 0] == 0 and np.all(q == 0)
+    tiny = np.full(32, 2.0 ** -40, np.float32)
+    q, s = _w8(orc, tiny, 32)
+    assert s[0, 0] == 0 and np.all(q == 0)
+    # a non-finite weight, or a scale past fp16's range, is an error
+    with pytest.raises(orc.OracleError):
+        _w8(orc, np.array([np.inf] + [0.0] * 31, np.float32), 32)
+    with pytest.raises(orc.OracleError):
+        _w8(orc, np.array([127.0 * 70000.0] + [0.0] * 31, np.float32), 32)
+    # bf16 and fp16 inputs are widened exactly
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    Wb = orc.f32_to_bf16_bits(W)
+    qb, sb = orc.quantize_w8(Wb, 128, dtype=orc.BF16)
+    q2, s2 = _w8(orc, (Wb.astype(np.uint32) << 16).view(np.float32), 128)
+    assert np.array_equal(qb, q2) and np.array_equal(sb, s2)
+    Wh = W.astype(np.float16)
+    qh, sh = orc.quantize_w8(Wh.view(np.uint16), 128, dtype=orc.F16)
+    q3, s3 = _w8(orc, Wh.astype(np.float32), 128)
+    assert np.array_equal(qh, q3) and np.array_equal(sh, s3)
+
+
+def test_w8_dequant_exact_all_codes(orc):
+    rng = np.random.default_rng(24)
+    scales = np.concatenate([
+        np.array([0x0001, 0x0155, 0x03FF, 0x0400, 0x1F42, 0x3C00, 0x7BFF], np.uint16),
+        rng.integers(0x0001, 0x7C00, 25).astype(np.uint16),
+    ])
+    codes = np.arange(-127, 128, dtype=np.int8)
+    q = np.tile(codes, (scales.size, 1))
+    s = scales[:, None].copy()
+    f32 = orc.dequant_w8(q, s, codes.size, orc.F32)
+    f16 = orc.dequant_w8(q, s, codes.size, orc.F16)
+    b16 = orc.dequant_w8(q, s, codes.size, orc.BF16)
+    exact = np.array([[float(Fraction(float(np.uint16(sv).view(np.float16))) * int(c)) for c in codes]
+                      for sv in scales])
+    assert np.array_equal(f32.astype(np.float64), exact)  # exact in fp32
+    with np.errstate(over="ignore"):  # 65504 * 127 rounds to fp16 infinity
+        assert np.array_equal(f16, exact.astype(np.float16).view(np.uint16))
+    ref_b = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16, ref_b)
+
+
+def test_w8_pack_device_is_a_bijection_and_byte_order(orc):
+    for N, K in [(16, 128), (37, 96), (5, 416)]:
+        nbytes = orc.device_bytes_w8(N, K)
+        assert nbytes == ((N + 15) // 16 * 16) * ((K + 127) // 128 * 128)
+        seen = np.zeros(nbytes, np.int64)
+        for n in range(N):
+            q = np.zeros((N, K), np.int8)
+            q[n, :] = 1
+            p = orc.pack_device_w8(q)
+            assert p.sum() == K
+            seen += p
+        assert seen.max() == 1 and seen.sum() == N * K
+        rng = np.random.default_rng(N + K)
+        q = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        assert np.array_equal(orc.unpack_device_w8(orc.pack_device_w8(q), N, K), q)
+    # hand-placed elements: row 3, columns 40..47 (MFMA step 1 -> half 0, second
+    # eight bytes; column block c = 1 -> lane 19); row 0, column 100 (step 3 ->
+    # half 1, second eight bytes, c = 0, e = 4); row 17, column 130 (second row
+    # block, second K tile: tile 1 * 2 + 1 = 3, step 0, lane 1, e = 2)
+    q = np.zeros((32, 256), np.int8)
+    q[3, 40:48] = -5
+    q[0, 100] = 77
+    q[17, 130] = -128 + 1
+    p = orc.pack_device_w8(q)
+    assert np.all(p[16 * 19 + 8: 16 * 19 + 16] == np.uint8(251))
+    assert p[1024 + 8 + 4] == 77
+    assert p[3 * 2048 + 16 * 1 + 2] == np.uint8(129)
+    assert np.count_nonzero(p) == 10
+
+
+def test_w8_gemm_rows(orc):
+    rng = np.random.default_rng(25)
+    M, N, K, g = 3, 40, 256, 32
+    W = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    q, s = orc.quantize_w8(W, g)
+    w_hat = orc.dequant_w8(q, s, g)
+    y = orc.gemm_f64(x, w_hat)
+    assert np.array_equal(orc.gemm_rows_w8_f64(x, q, s, g, 10, 17), y[:, 10:27])
+    # a one-hot activation row selects one decoded weight per output
+    xo = np.zeros((1, K), np.float32)
+    xo[0, 77] = 1.0
+    yo = orc.gemm_rows_w8_f64(workloads.f32_to_f16_bits(xo), q, s, g, 0, N)
+    assert np.array_equal(yo[0], w_hat[:, 77].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
 
