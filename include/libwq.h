@@ -198,6 +198,70 @@ int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group,
                      const uint8_t* zpacked, uint16_t* y_f16,
                      void* workspace, size_t workspace_bytes, int path, void* stream);
 
+/* ---- Group absmax int8 weights (W8A16) --------------------------------------
+ * The int8 rule of "Quantization Methods Compared: INT8, GPTQ, AWQ, FP8, FP4
+ * and KV-Cache Quantization", section "What quantisation does: scale, round,
+ * and the outlier that ruins a group" (s = max|w| / 127, q = round(w / s),
+ * decoding q * s), with one scale per group of `group` (32 or 128) weights
+ * along K, read as:
+ *   s = fp16(fl32(M / 127)), M = max|w| over the group (round-to-nearest-even,
+ *   subnormals kept);
+ *   q = clamp(rne(fl32(w / s)), -127, 127) with the stored scale s;
+ *   a group whose fp16 scale is 0 stores s = 0 and codes 0;
+ *   What = s * q, exact in fp32.
+ * No zero-points.  Layouts:
+ *   q_codes  [N][K] int8 (two's complement)
+ *   s_f16    [N][G] fp16 bit patterns, G = K / group
+ *   qpacked  2048-byte tiles of 16 rows x 128 columns (rows padded to
+ *            ceil(N/16)*16, columns to ceil(K/128)*128 with code 0), tile
+ *            (nb, kt) at byte offset (nb * Kp/128 + kt) * 2048; inside it half
+ *            h = 0, 1 at byte 1024*h, lane l = r + 16*c at byte 16*l of the
+ *            half, and byte 8*i + e (i = 0, 1; e = 0..7) of that holds the code
+ *            of column 32*(2h + i) + 8*c + e of row r.
+ * Same conventions as the 4-bit entry points (device pointers, caller-owned
+ * buffers, asynchronous on `stream`, status codes). */
+
+/* Byte sizes of qpacked (2048-byte tiles) and s_f16 for [N][K] at `group`.
+ * Host-only; either output may be NULL. */
+int wq_layout_bytes_w8(int64_t N, int64_t K, int group, size_t* qpacked_bytes, size_t* s_bytes);
+
+/* Group absmax int8 quantization of W [N][K] (w_dtype WQ_F32, WQ_BF16 or
+ * WQ_F16; 16-byte aligned).  s_f16 [N][G] required; q_codes [N][K] (8-byte
+ * aligned) and qpacked (16-byte aligned) may each be NULL.  Deterministic. */
+int wq_quantize_w8(const void* W, int w_dtype, int64_t N, int64_t K, int group,
+                   int8_t* q_codes, uint16_t* s_f16, uint8_t* qpacked, void* stream);
+
+/* int8 codes [N][K] -> qpacked tiles (padding written as 0).  K must be a
+ * multiple of 32 (WQ_EUNSUPPORTED otherwise); q_codes 8-byte aligned,
+ * qpacked 16-byte aligned. */
+int wq_pack_int8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, void* stream);
+
+/* What = s * q into W_hat [N][K] as out_dtype (WQ_F32 exact; WQ_F16 / WQ_BF16
+ * one round-to-nearest-even of it); W_hat 16-byte aligned. */
+int wq_dequant_w8(const uint8_t* qpacked, const uint16_t* s_f16, int64_t N, int64_t K, int group,
+                  int out_dtype, void* W_hat, void* stream);
+
+/* Workspace bytes for wq_gemm_w8a16 / wq_gemm_w8a16_ex (same rules as
+ * wq_gemm_workspace_bytes).  Host-only. */
+size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+
+/* y = x * What^T with What = s * q dequantized inside the kernel (the
+ * weight-only product of "Hardware, formats and the roofline" with 8-bit
+ * weights): M < 64 the split-K GEMV, M >= 64 the MFMA tile GEMM.  Arguments,
+ * workspace contract, alignment, determinism and errors as wq_gemm_w4a16,
+ * without zero-points. */
+int wq_gemm_w8a16(int64_t M, int64_t N, int64_t K, int group,
+                  const uint16_t* x_f16, const uint8_t* qpacked, const uint16_t* s_f16,
+                  uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As wq_gemm_w8a16, with the kernel family chosen by `path` (wq_path). */
+int wq_gemm_w8a16_ex(int64_t M, int64_t N, int64_t K, int group,
+                     const uint16_t* x_f16, const uint8_t* qpacked, const uint16_t* s_f16,
+                     uint16_t* y_f16, void* workspace, size_t workspace_bytes, int path, void* stream);
+
+/* As wq_gemm_plan, for wq_gemm_w8a16_ex. */
+int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len);
+
 #ifdef __cplusplus
 }
 #endif

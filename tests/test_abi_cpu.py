@@ -158,3 +158,49 @@ def test_quantize_scheme_checked_on_host():
     assert call(f, A, wq.WQ_BF16, 16, 128, 128, -1, None, A, None, A, A, None) == wq.WQ_EINVAL
     assert call(f, A, wq.WQ_BF16, 16, 100, 32, wq.WQ_SYM, None, A, None, A, A, None) == wq.WQ_EUNSUPPORTED
     assert call(f, B, wq.WQ_BF16, 16, 128, 128, wq.WQ_SYM, None, A, None, A, A, None) == wq.WQ_EALIGN
+
+
+@pytest.mark.parametrize("N,K,g", [(8192, 8192, 128), (37, 96, 32), (28672, 8192, 32)])
+def test_layout_bytes_w8(N, K, g):
+    q, s = wq.wq_layout_bytes_w8(N, K, g)
+    Np, Kp = (N + 15) // 16 * 16, (K + 127) // 128 * 128
+    assert q == Np * Kp and s == 2 * N * (K // g)
+    with pytest.raises(wq.WQError):
+        wq.wq_layout_bytes_w8(N, K, 64)
+
+
+def test_w8_entry_points_checked_on_host():
+    f = "wq_quantize_w8"
+    assert call(f, None, 1, 16, 128, 128, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 128, 128, None, None, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 9, 16, 128, 128, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 160, 128, None, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, A, 1, 16, 128, 128, B, A, A, None) == wq.WQ_EALIGN
+    assert call(f, A, 1, 16, 128, 128, None, A, B, None) == wq.WQ_EALIGN
+    assert call("wq_pack_int8", None, 16, 128, A, None) == wq.WQ_EINVAL
+    assert call("wq_pack_int8", A, 0, 128, A, None) == wq.WQ_EINVAL
+    assert call("wq_pack_int8", A, 16, 100, A, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_pack_int8", A, 16, 128, B, None) == wq.WQ_EALIGN
+    assert call("wq_dequant_w8", A, A, 16, 128, 128, 5, A, None) == wq.WQ_EINVAL
+    assert call("wq_dequant_w8", A, A, 16, 128, 48, 0, A, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_dequant_w8", B, A, 16, 128, 128, 0, A, None) == wq.WQ_EALIGN
+    g = "wq_gemm_w8a16_ex"
+    # no zero-point argument: x, qpacked, s, y, workspace, bytes, path, stream
+    assert call(g, 0, 16, 128, 128, A, A, A, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(g, 1, 16, 128, 128, A, None, A, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(g, 1, 16, 128, 128, A, A, A, A, None, 0, 9, None) == wq.WQ_EINVAL
+    assert call(g, 1, 16, 100, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
+    assert call(g, 1, 16, 128, 128, A, B, A, A, None, 0, 0, None) == wq.WQ_EALIGN
+    assert call("wq_gemm_w8a16", 1, 16, 128, 128, B, A, A, A, None, 0, None) == wq.WQ_EALIGN
+    need = wq.wq_gemm_w8a16_workspace_bytes(1, 1024, 8192, 32)
+    assert need == wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32) > 0
+    assert call(g, 1, 1024, 8192, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
+    assert call(g, 1, 1024, 8192, 32, A, A, A, A, A, need - 1, 0, None) == wq.WQ_EWORKSPACE
+
+
+def test_w8_plan_names_the_dispatched_kernel():
+    d = wq.wq_gemm_w8a16_plan(1, 8192, 8192, 128)
+    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=128, BITS=8>") and "grid=(512,1,1)" in d, d
+    d = wq.wq_gemm_w8a16_plan(128, 28672, 8192, 128)
+    assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128, BITS=8>") and "grid=(224,1,1)" in d, d
+    assert wq.wq_gemm_w8a16_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32, BITS=8>")

@@ -27,6 +27,8 @@ EXPORTED = (
     "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_quantize_groups_ex", "wq_pack_int4",
     "wq_dequant",
     "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
+    "wq_layout_bytes_w8", "wq_quantize_w8", "wq_pack_int8", "wq_dequant_w8", "wq_gemm_w8a16_workspace_bytes",
+    "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
 )
 
 _lib = None
@@ -61,6 +63,14 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
         "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_w4a16_seq": (I, [I, I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
+        "wq_layout_bytes_w8": (I, [I64, I64, I, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "wq_quantize_w8": (I, [P, I, I64, I64, I, P, P, P, P]),
+        "wq_pack_int8": (I, [P, I64, I64, P, P]),
+        "wq_dequant_w8": (I, [P, P, I64, I64, I, I, P, P]),
+        "wq_gemm_w8a16_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "wq_gemm_w8a16": (I, [I64, I64, I64, I, P, P, P, P, P, SZ, P]),
+        "wq_gemm_w8a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, SZ, I, P]),
+        "wq_gemm_w8a16_plan": (I, [I64, I64, I64, I, I, ctypes.c_char_p, SZ]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -223,3 +233,87 @@ def wq_gemm_w4a16_seq(xs, qws, ys, *, workspace: torch.Tensor | None = None, str
     if len(xs) == 0:
         return ys
     return wq_gemm_w4a16_seq_prepared(xs, qws, ys, workspace=workspace, stream=stream)()
+
+
+# ---- group absmax int8 weights (W8A16) --------------------------------------
+
+@dataclass
+class QuantizedWeight8:
+    """Device buffers of one int8-quantized [N][K] weight matrix."""
+    qpacked: torch.Tensor  # uint8, 2048-byte tiles (wq_layout_bytes_w8)
+    s: torch.Tensor        # float16 [N][K/group]
+    N: int
+    K: int
+    group: int
+
+
+def wq_layout_bytes_w8(N: int, K: int, group: int):
+    q, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wq_layout_bytes_w8(N, K, group, ctypes.byref(q), ctypes.byref(s)), "wq_layout_bytes_w8")
+    return q.value, s.value
+
+
+def alloc_quantized_w8(N: int, K: int, group: int, device="cuda") -> QuantizedWeight8:
+    qb, _ = wq_layout_bytes_w8(N, K, group)
+    return QuantizedWeight8(torch.empty(qb, dtype=torch.uint8, device=device),
+                            torch.empty((N, K // group), dtype=torch.float16, device=device), N, K, group)
+
+
+def wq_quantize_w8(W: torch.Tensor, group: int, *, codes: bool = False, packed: bool = True,
+                   out: QuantizedWeight8 | None = None, stream=None):
+    """Group absmax int8 quantization of W[N][K] (float32, bfloat16 or float16,
+    on the GPU).  Returns a dict with ``s`` (fp16 [N][G]) and, as requested,
+    ``q_codes`` (int8 [N][K]) and ``qw`` (QuantizedWeight8)."""
+    N, K = W.shape
+    G = K // group if group else 0
+    dev = W.device
+    qw = out
+    if packed and qw is None:
+        qw = alloc_quantized_w8(N, K, group, dev)
+    s = qw.s if packed else torch.empty((N, G), dtype=torch.float16, device=dev)
+    q_codes = torch.empty((N, K), dtype=torch.int8, device=dev) if codes else None
+    _check(lib().wq_quantize_w8(_ptr(W), _DT.get(W.dtype, -1), N, K, group, _ptr(q_codes), _ptr(s),
+                                _ptr(qw.qpacked) if packed else None, _stream(stream)), "wq_quantize_w8")
+    return {"s": s, "q_codes": q_codes, "qw": qw if packed else None}
+
+
+def wq_pack_int8(q_codes: torch.Tensor, group: int, stream=None) -> QuantizedWeight8:
+    """Pack int8 codes [N][K] into the tile layout (the returned weight's ``s``
+    is left uninitialised)."""
+    N, K = q_codes.shape
+    qw = alloc_quantized_w8(N, K, group, q_codes.device)
+    _check(lib().wq_pack_int8(_ptr(q_codes), N, K, _ptr(qw.qpacked), _stream(stream)), "wq_pack_int8")
+    return qw
+
+
+def wq_dequant_w8(qw: QuantizedWeight8, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty((qw.N, qw.K), dtype=out_dtype, device=qw.qpacked.device)
+    _check(lib().wq_dequant_w8(_ptr(qw.qpacked), _ptr(qw.s), qw.N, qw.K, qw.group, _DT.get(out_dtype, -1),
+                               _ptr(out), _stream(stream)), "wq_dequant_w8")
+    return out
+
+
+def wq_gemm_w8a16_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
+    return int(lib().wq_gemm_w8a16_workspace_bytes(M, N, K, group))
+
+
+def wq_gemm_w8a16_plan(M: int, N: int, K: int, group: int, path: int = WQ_PATH_AUTO) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().wq_gemm_w8a16_plan(M, N, K, group, path, buf, len(buf)), "wq_gemm_w8a16_plan")
+    return buf.value.decode()
+
+
+def wq_gemm_w8a16(x: torch.Tensor, qw: QuantizedWeight8, *, y: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y[M][N] = x[M][K] * What^T, What = s * q (int8 codes), fp16 in and out."""
+    M, K = x.shape
+    assert K == qw.K, "x and the weight disagree on K"
+    if y is None:
+        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
+    need = wq_gemm_w8a16_workspace_bytes(M, qw.N, qw.K, qw.group)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    _check(lib().wq_gemm_w8a16_ex(M, qw.N, qw.K, qw.group, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s), _ptr(y),
+                                  _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  path, _stream(stream)), "wq_gemm_w8a16")
+    return y

@@ -107,19 +107,20 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   if (st) return st;
   const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
   if (mfma)
-    wq::describe_gemm(M, N, K, group, buf, buf_len);
+    wq::describe_gemm(M, N, K, group, 4, buf, buf_len);
   else
-    wq::describe_gemv(M, N, K, group, buf, buf_len);
+    wq::describe_gemv(M, N, K, group, 4, buf, buf_len);
   return WQ_OK;
 }
 
 namespace {
 
-// Argument checks of one product (host only); 0 or a wq_status.
-int check_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint32_t* qpacked,
+// Argument checks of one product (host only); 0 or a wq_status.  bits 8 takes
+// no zero-points.
+int check_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x_f16, const void* qpacked,
                const uint16_t* s_f16, const uint8_t* zpacked, const uint16_t* y_f16, const void* workspace,
                size_t workspace_bytes, int path, bool* mfma) {
-  if (!x_f16 || !qpacked || !s_f16 || !zpacked || !y_f16) return WQ_EINVAL;
+  if (!x_f16 || !qpacked || !s_f16 || (bits == 4 && !zpacked) || !y_f16) return WQ_EINVAL;
   if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
@@ -134,11 +135,11 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16
   return WQ_OK;
 }
 
-hipError_t launch_one(bool mfma, int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16,
-                      const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16,
+hipError_t launch_one(bool mfma, int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x_f16,
+                      const void* qpacked, const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16,
                       void* workspace, hipStream_t s) {
-  if (!mfma) return wq::launch_gemv(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
-  return wq::launch_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
+  if (!mfma) return wq::launch_gemv(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
+  return wq::launch_gemm(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
 }
 
 }  // namespace
@@ -147,10 +148,10 @@ int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t*
                      const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16, void* workspace,
                      size_t workspace_bytes, int path, void* stream) {
   bool mfma = false;
-  const int st = check_gemm(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, workspace_bytes,
+  const int st = check_gemm(M, N, K, group, 4, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, workspace_bytes,
                             path, &mfma);
   if (st) return st;
-  return hip_status(launch_one(mfma, M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace,
+  return hip_status(launch_one(mfma, M, N, K, group, 4, x_f16, qpacked, s_f16, zpacked, y_f16, workspace,
                                static_cast<hipStream_t>(stream)));
 }
 
@@ -160,13 +161,13 @@ int wq_gemm_w4a16_seq(int count, int64_t M, int64_t N, int64_t K, int group, con
   if (count < 0 || (count > 0 && (!x_f16 || !qpacked || !s_f16 || !zpacked || !y_f16))) return WQ_EINVAL;
   bool mfma = false;
   for (int i = 0; i < count; ++i) {
-    const int st = check_gemm(M, N, K, group, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i], workspace,
+    const int st = check_gemm(M, N, K, group, 4, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i], workspace,
                               workspace_bytes, WQ_PATH_AUTO, &mfma);
     if (st) return st;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int i = 0; i < count; ++i) {
-    const hipError_t e = launch_one(mfma, M, N, K, group, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i],
+    const hipError_t e = launch_one(mfma, M, N, K, group, 4, x_f16[i], qpacked[i], s_f16[i], zpacked[i], y_f16[i],
                                     workspace, s);
     if (e != hipSuccess) return WQ_EHIP;
   }
@@ -178,6 +179,84 @@ int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_
                   size_t workspace_bytes, void* stream) {
   return wq_gemm_w4a16_ex(M, N, K, group, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, workspace_bytes,
                           WQ_PATH_AUTO, stream);
+}
+
+// ---- group absmax int8 (W8A16) ---------------------------------------------
+
+int wq_layout_bytes_w8(int64_t N, int64_t K, int group, size_t* qpacked_bytes, size_t* s_bytes) {
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  const int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128;
+  if (qpacked_bytes) *qpacked_bytes = (size_t)(Np * Kp);
+  if (s_bytes) *s_bytes = (size_t)(N * (K / group) * 2);
+  return WQ_OK;
+}
+
+int wq_quantize_w8(const void* W, int w_dtype, int64_t N, int64_t K, int group, int8_t* q_codes, uint16_t* s_f16,
+                   uint8_t* qpacked, void* stream) {
+  if (!W || !s_f16) return WQ_EINVAL;
+  if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(W, 16) || !aligned(s_f16, 2) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8)))
+    return WQ_EALIGN;
+  return hip_status(
+      wq::launch_quantize_w8(W, w_dtype, N, K, group, q_codes, s_f16, qpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_pack_int8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, void* stream) {
+  if (!q_codes || !qpacked) return WQ_EINVAL;
+  if (N <= 0 || K <= 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (K % 32 != 0) return WQ_EUNSUPPORTED;
+  if (!aligned(q_codes, 8) || !aligned(qpacked, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_pack_w8(q_codes, N, K, qpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_dequant_w8(const uint8_t* qpacked, const uint16_t* s_f16, int64_t N, int64_t K, int group, int out_dtype,
+                  void* W_hat, void* stream) {
+  if (!qpacked || !s_f16 || !W_hat) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16 && out_dtype != WQ_F16) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  if (!aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(W_hat, 16)) return WQ_EALIGN;
+  return hip_status(
+      wq::launch_dequant_w8(qpacked, s_f16, N, K, group, out_dtype, W_hat, static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
+  return wq_gemm_workspace_bytes(M, N, K, group);
+}
+
+int wq_gemm_w8a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint8_t* qpacked,
+                     const uint16_t* s_f16, uint16_t* y_f16, void* workspace, size_t workspace_bytes, int path,
+                     void* stream) {
+  bool mfma = false;
+  const int st = check_gemm(M, N, K, group, 8, x_f16, qpacked, s_f16, nullptr, y_f16, workspace, workspace_bytes,
+                            path, &mfma);
+  if (st) return st;
+  return hip_status(launch_one(mfma, M, N, K, group, 8, x_f16, qpacked, s_f16, nullptr, y_f16, workspace,
+                               static_cast<hipStream_t>(stream)));
+}
+
+int wq_gemm_w8a16(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint8_t* qpacked,
+                  const uint16_t* s_f16, uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream) {
+  return wq_gemm_w8a16_ex(M, N, K, group, x_f16, qpacked, s_f16, y_f16, workspace, workspace_bytes, WQ_PATH_AUTO,
+                          stream);
+}
+
+int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len) {
+  if (!buf || buf_len == 0) return WQ_EINVAL;
+  buf[0] = 0;
+  if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
+  int st = check_shape(N, K, group);
+  if (st) return st;
+  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  if (mfma)
+    wq::describe_gemm(M, N, K, group, 8, buf, buf_len);
+  else
+    wq::describe_gemv(M, N, K, group, 8, buf, buf_len);
+  return WQ_OK;
 }
 
 }  // extern "C"

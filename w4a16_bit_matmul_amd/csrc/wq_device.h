@@ -9,6 +9,13 @@
 //   That lane/column assignment is also the A/B operand assignment of
 //   v_mfma_f32_16x16x32_f16 (lane l: row l%16, eight k values 8*(l/16)..+7),
 //   so a word is directly one MFMA B-fragment for the k-slots of step j.
+//
+// 8-bit codes (group absmax int8) use 2048-byte tiles of the same 16 x 128
+// shape: half h = 0, 1 at byte 1024*h holds MFMA steps 2h and 2h + 1; in it
+// lane l = r + 16*c owns the 16 bytes at 16*l, whose byte 8*i + e (i = 0, 1)
+// is the two's-complement code of column 32*(2h + i) + 8*c + e.  So one
+// 16-byte load gives a lane its B operands for two MFMA steps, and a wave's
+// load covers 1024 contiguous bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +31,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 128;
 constexpr int kTileBytes = 1024;
+constexpr int kTileBytes8 = 2048;
 
 // fp16 bit pattern of 1024.0: OR-ing a 4-bit code q into the low mantissa bits
 // gives exactly 1024 + q.
@@ -45,6 +53,16 @@ __device__ __forceinline__ h2 biased_pair64(uint32_t word, int p) {
   return as_h2((sh & 0x03C003C0u) | kMagicPair);
 }
 
+// fp16 pair (1152 + q_a, 1152 + q_b) of two int8 codes of a 32-bit word (four
+// codes, little-endian): flipping the sign bits turns each code q into the
+// unsigned byte q + 128, which v_perm_b32 places under the fp16 exponent of
+// 1024.0 (bytes 0x64); sel picks the two bytes (0x04010400: bytes 0 and 1,
+// 0x04030402: bytes 2 and 3).  Subtracting 1152 leaves q exactly.
+constexpr uint32_t kMagicBytes = 0x64646464u;
+__device__ __forceinline__ uint32_t byte_pair(uint32_t word_flipped, uint32_t sel) {
+  return __builtin_amdgcn_perm(kMagicBytes, word_flipped, sel);
+}
+
 // Round-to-nearest-even fp32 -> fp16 bits.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
@@ -64,6 +82,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 
 __device__ __forceinline__ int64_t tile_offset_bytes(int64_t nb, int64_t kt, int64_t KT) {
   return (nb * KT + kt) * kTileBytes;
+}
+__device__ __forceinline__ int64_t tile8_offset_bytes(int64_t nb, int64_t kt, int64_t KT) {
+  return (nb * KT + kt) * kTileBytes8;
 }
 
 // Zero-point of (row n, group gi) from the packed [N][ceil(G/2)] array.

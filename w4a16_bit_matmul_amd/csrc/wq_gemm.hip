@@ -17,7 +17,10 @@
 // B dequantization per pair of columns: shift + AND-OR (1024 + q, exact fp16),
 // packed fp16 add of -(1024 + z) (exact q - z), packed fp16 multiply by the
 // scale (one round-to-nearest-even: fp16(What)).  Accumulation is fp32 in the
-// matrix cores.
+// matrix cores.  8-bit codes (group absmax int8, What = s * q): sign-bit flip
+// and byte permute (1152 + q, exact fp16), packed subtraction of 1152, packed
+// multiply by the scale; each wave's 16-byte load then holds its two MFMA
+// steps of a 2048-byte tile.
 //
 // Decomposition.  A workgroup of eight waves (two per SIMD) owns a (16*MB) x
 // 128 output tile and walks K one 128-column tile per step, all waves on the
@@ -92,6 +95,21 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t magic, h2 nb, h2
   return out;
 }
 
+// fp16(s * q) for the eight columns held by two words of 8-bit codes.
+__device__ __forceinline__ h8 dequant_words8(uint32_t lo, uint32_t hi, h2 sc) {
+  const h2 bias = as_h2(0x64806480u);  // (1152, 1152)
+  lo ^= 0x80808080u;
+  hi ^= 0x80808080u;
+  const h2 p0 = (as_h2(byte_pair(lo, 0x04010400u)) - bias) * sc;
+  const h2 p1 = (as_h2(byte_pair(lo, 0x04030402u)) - bias) * sc;
+  const h2 p2 = (as_h2(byte_pair(hi, 0x04010400u)) - bias) * sc;
+  const h2 p3 = (as_h2(byte_pair(hi, 0x04030402u)) - bias) * sc;
+  h8 out;
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+  return out;
+}
+
 // LDS bytes of one staged chunk for the workgroup's 128 weight rows:
 // g = 128: [tile][row] u32 (scale bits, zero-point in bits 16..19);
 // g = 32: [tile][pair][row] u32 (scales of groups 4t + 2q, 4t + 2q + 1), then
@@ -102,8 +120,12 @@ constexpr int sz_chunk_bytes() {
 }
 
 // SZV: every row of s (and zpacked) is aligned for the wide staging loads.
-template <int MB, int G, bool SZV>
+// BITS: 4 (codes and zero-points) or 8 (int8 codes, no zero-points).
+template <int MB, int G, bool SZV, int BITS>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  using CodeT = std::conditional_t<BITS == 4, uint2, u4>;  // one wave's two MFMA steps of a tile
+  constexpr int TB = BITS == 4 ? kTileBytes : kTileBytes8;
   constexpr int NPW = kNPW;
   constexpr int NTH = kWaves * 64;
   constexpr int ROWS = 16 * MB;
@@ -123,16 +145,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   const uint32_t magic = in_vgpr(kMagicPair);
   const int KT = a.KT;
 
-  // code words 2jp, 2jp + 1 of the lane's 16 bytes in each of the wave's
-  // blocks (blocks past the end re-read the last one)
+  // the codes of MFMA steps 2jp, 2jp + 1 in each of the wave's blocks: 4-bit,
+  // words 2jp and 2jp + 1 of the lane's 16 bytes; 8-bit, the lane's 16 bytes
+  // of half jp (blocks past the end re-read the last one)
   const uint8_t* tb[NPW];
 #pragma unroll
   for (int b = 0; b < NPW; ++b)
-    tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * kTileBytes + 16u * lane + 8u * jp;
-  auto load_b = [&](int kt, uint2 (&d)[NPW]) {
+    tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * TB + 16u * lane + (BITS == 4 ? 8u : 1024u) * jp;
+  auto load_b = [&](int kt, CodeT (&d)[NPW]) {
     kt = min(kt, KT - 1);  // tiles past the end re-load the last (unused)
 #pragma unroll
-    for (int b = 0; b < NPW; ++b) d[b] = *reinterpret_cast<const uint2*>(tb[b] + (size_t)kt * kTileBytes);
+    for (int b = 0; b < NPW; ++b) d[b] = *reinterpret_cast<const CodeT*>(tb[b] + (size_t)kt * TB);
   };
 
   // activation chunk q = tid + NTH * i: row q / 16 of the tile, global chunk
@@ -176,21 +199,23 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         v.s[0] = a.s[srow + min(t0, a.Gtot - 1)];
         v.s[1] = a.s[srow + min(t0 + 1, a.Gtot - 1)];
       }
-      v.z = a.zp[zrow + (min(t0, a.Gtot - 1) >> 1)];
+      v.z = BITS == 4 ? a.zp[zrow + (min(t0, a.Gtot - 1) >> 1)] : 0u;
     } else {
       if constexpr (SZV) {  // Gtot % 8 == 0: 16 bytes of scales, 4 bytes of zero-points
         const int g = min(4 * t0, a.Gtot - 8);
         const u4 t = *reinterpret_cast<const u4*>(a.s + srow + g);
         v.s[0] = t.x; v.s[1] = t.y; v.s[2] = t.z; v.s[3] = t.w;
-        v.z = *reinterpret_cast<const uint32_t*>(a.zp + zrow + g / 2);
+        v.z = BITS == 4 ? *reinterpret_cast<const uint32_t*>(a.zp + zrow + g / 2) : 0u;
       } else {
         uint32_t zz = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int g0 = min(4 * t0 + 2 * q, a.Gtot - 1), g1 = min(4 * t0 + 2 * q + 1, a.Gtot - 1);
           v.s[q] = (uint32_t)a.s[srow + g0] | ((uint32_t)a.s[srow + g1] << 16);
-          const uint32_t zb0 = a.zp[zrow + (g0 >> 1)], zb1 = a.zp[zrow + (g1 >> 1)];
-          zz |= (((g0 & 1) ? zb0 >> 4 : zb0 & 15u) | (((g1 & 1) ? zb1 >> 4 : zb1 & 15u) << 4)) << (8 * q);
+          if constexpr (BITS == 4) {
+            const uint32_t zb0 = a.zp[zrow + (g0 >> 1)], zb1 = a.zp[zrow + (g1 >> 1)];
+            zz |= (((g0 & 1) ? zb0 >> 4 : zb0 & 15u) | (((g1 & 1) ? zb1 >> 4 : zb1 & 15u) << 4)) << (8 * q);
+          }
         }
         v.z = zz;
       }
@@ -225,7 +250,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 
   // ---- prologue: activations of tile 0 (in LDS) and tile 1 (in registers),
   // codes of tiles 0..2, scales / zero-points of the first chunk
-  uint2 b0[NPW], b1[NPW], b2[NPW], b3[NPW];
+  CodeT b0[NPW], b1[NPW], b2[NPW], b3[NPW];
   u4 xs0[XCH], xs1[XCH];
   SzStage szs;
   load_x(0, xs0);
@@ -246,8 +271,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // One step (K tile kt): load the activations of tile kt + 2 and the codes
   // of tile kt + 3, multiply tile kt, and store the activations of tile
   // kt + 1 (loaded one step earlier) into the other LDS buffer.
-  auto step = [&](auto full_tag, int kt, u4 (&xld)[XCH], const u4 (&xst)[XCH], const uint2 (&cur)[NPW],
-                  uint2 (&nxt)[NPW]) {
+  auto step = [&](auto full_tag, int kt, u4 (&xld)[XCH], const u4 (&xst)[XCH], const CodeT (&cur)[NPW],
+                  CodeT (&nxt)[NPW]) {
     constexpr bool FULL = decltype(full_tag)::value;
     load_x(kt + 2, xld);
     __builtin_amdgcn_sched_barrier(0);
@@ -278,10 +303,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int b = 0; b < NPW; ++b) {
         const uint32_t sb = G == 128 ? sv[b] & 0xffffu : (jj ? sv[b] >> 16 : sv[b] & 0xffffu);
-        const uint32_t z = G == 128 ? zv[b] & 15u : (zv[b] >> (4 * jj)) & 15u;
         const h2 sc = as_h2(sb * 0x00010001u);
-        const h2 nbias = -as_h2(z * 0x00010001u + magic);
-        const h8 bf = dequant_word(jj ? cur[b].y : cur[b].x, magic, nbias, sc);
+        h8 bf;
+        if constexpr (BITS == 4) {
+          const uint32_t z = G == 128 ? zv[b] & 15u : (zv[b] >> (4 * jj)) & 15u;
+          const h2 nbias = -as_h2(z * 0x00010001u + magic);
+          bf = dequant_word(jj ? cur[b].y : cur[b].x, magic, nbias, sc);
+        } else {
+          bf = dequant_words8(jj ? cur[b][2] : cur[b][0], jj ? cur[b][3] : cur[b][1], sc);
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
       }
@@ -366,47 +396,47 @@ size_t gemm_lds(int MB, int group) {
   return tiles > red ? tiles : red;
 }
 
-template <int MB, int G, bool SZV>
+template <int MB, int G, bool SZV, int BITS>
 hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid = gemm_grid(MB, a.M, a.N), block(kWaves * 64);
   const size_t lds = gemm_lds(MB, G);
-  auto k = gemm_kernel<MB, G, SZV>;
+  auto k = gemm_kernel<MB, G, SZV, BITS>;
   if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   k<<<grid, block, lds, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int MB>
+template <int MB, int BITS>
 hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
   // wide staging loads of scales / zero-points when every row is aligned for
   // them: g = 128 two scales (4 bytes); g = 32 eight scales (16 bytes) and
   // eight zero-points (4 bytes)
   const uintptr_t sp = reinterpret_cast<uintptr_t>(a.s), zp = reinterpret_cast<uintptr_t>(a.zp);
   if (group == 128) {
-    if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true>(a, stream);
-    return launch_kg<MB, 128, false>(a, stream);
+    if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, BITS>(a, stream);
+    return launch_kg<MB, 128, false, BITS>(a, stream);
   }
-  if (a.Gtot % 8 == 0 && sp % 16 == 0 && zp % 4 == 0) return launch_kg<MB, 32, true>(a, stream);
-  return launch_kg<MB, 32, false>(a, stream);
+  if (a.Gtot % 8 == 0 && sp % 16 == 0 && (BITS == 8 || zp % 4 == 0)) return launch_kg<MB, 32, true, BITS>(a, stream);
+  return launch_kg<MB, 32, false, BITS>(a, stream);
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
-int describe_gemm(int64_t M, int64_t N, int64_t, int group, char* buf, size_t len) {
+int describe_gemm(int64_t M, int64_t N, int64_t, int group, int bits, char* buf, size_t len) {
   const int MB = gemm_mb(M);
   const dim3 g = gemm_grid(MB, M, N);
-  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d> grid=(%u,%u,1) block=%d lds=%zu", MB, kNPW, group, g.x,
-                  g.y, kWaves * 64, gemm_lds(MB, group));
+  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d%s> grid=(%u,%u,1) block=%d lds=%zu", MB, kNPW, group,
+                  bits == 8 ? ", BITS=8" : "", g.x, g.y, kWaves * 64, gemm_lds(MB, group));
 }
 
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* /*workspace*/,
                        hipStream_t stream) {
   GemmArgs a;
   a.x = x;
-  a.qp = reinterpret_cast<const uint8_t*>(qpacked);
+  a.qp = static_cast<const uint8_t*>(qpacked);
   a.s = s;
   a.zp = zpacked;
   a.y = y;
@@ -417,11 +447,19 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_
   a.Gtot = (int)(K / group);
   a.GB = (a.Gtot + 1) / 2;
   a.NBLK = (int)((N + 15) / 16);
+  if (bits == 8) {
+    switch (gemm_mb(M)) {
+      case 1: return launch_t<1, 8>(group, a, stream);
+      case 2: return launch_t<2, 8>(group, a, stream);
+      case 4: return launch_t<4, 8>(group, a, stream);
+      default: return launch_t<8, 8>(group, a, stream);
+    }
+  }
   switch (gemm_mb(M)) {
-    case 1: return launch_t<1>(group, a, stream);
-    case 2: return launch_t<2>(group, a, stream);
-    case 4: return launch_t<4>(group, a, stream);
-    default: return launch_t<8>(group, a, stream);
+    case 1: return launch_t<1, 4>(group, a, stream);
+    case 2: return launch_t<2, 4>(group, a, stream);
+    case 4: return launch_t<4, 4>(group, a, stream);
+    default: return launch_t<8, 4>(group, a, stream);
   }
 }
 

@@ -21,6 +21,12 @@
 // after which one fp32 multiply-add applies the group's scale.  Every product
 // is exact and no sum carries a bias that would later cancel.
 //
+// 8-bit codes (group absmax int8, decoding s * q, no zero-point): a word holds
+// four two's-complement codes; XOR-ing the sign bits and placing two bytes
+// under the fp16 exponent of 1024 (v_perm_b32) gives (1152 + q) pairs, and one
+// packed fp16 subtraction of 1152 leaves q exactly, which v_dot2_f32_f16
+// multiplies with the activation pairs into one fp32 sum per group.
+//
 // Decomposition.  A workgroup owns one 16-row block, MT rows of x and a range
 // of 128-column K tiles (all of K unless the grid splits K).  Wave w walks
 // segments of KQ consecutive K tiles (w, w + W, w + 2W, ... in segment units).
@@ -79,54 +85,100 @@ struct SZ {
   __device__ __forceinline__ uint32_t zero(int t) const { return (zv[t >> 3] >> (4 * (t & 7))) & 15u; }
 };
 
+// (srow / zrow as below; ZP = false: no zero-points, zv stays zero.)
 // srow / zrow: element offsets of the row's scales and zero-point bytes (rows
 // past N are clamped to row N - 1 by the caller: their outputs are never
 // stored); g0: first group of the segment (wave-uniform).  With a.sz_vec the
 // segment's groups lie inside the row and are aligned for vector loads;
 // otherwise each group is loaded alone, clamped into the row (groups past the
 // row meet zero activations and zero codes).
-template <int NS>
+template <int NS, bool ZP>
 __device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, uint32_t srow, uint32_t zrow, int g0) {
   SZ<NS> v;
+#pragma unroll
+  for (int i = 0; i < (NS + 7) / 8; ++i) v.zv[i] = 0;
   if (a.sz_vec) {
     const uint16_t* sp = a.s + srow + g0;
-    const uint8_t* zp = a.zp + zrow + g0 / 2;
+    const uint8_t* zp = ZP ? a.zp + zrow + g0 / 2 : nullptr;
     if constexpr (NS == 4) {
       const uint2 t = *reinterpret_cast<const uint2*>(sp);
       v.sv[0] = t.x;
       v.sv[1] = t.y;
-      v.zv[0] = *reinterpret_cast<const uint16_t*>(zp);
+      if constexpr (ZP) v.zv[0] = *reinterpret_cast<const uint16_t*>(zp);
     } else if constexpr (NS == 8) {
       const uint4 t = *reinterpret_cast<const uint4*>(sp);
       v.sv[0] = t.x; v.sv[1] = t.y; v.sv[2] = t.z; v.sv[3] = t.w;
-      v.zv[0] = *reinterpret_cast<const uint32_t*>(zp);
+      if constexpr (ZP) v.zv[0] = *reinterpret_cast<const uint32_t*>(zp);
     } else {
       static_assert(NS == 16, "segment of 4 or 8 groups at g = 128, 16 at g = 32");
       const uint4 t0 = *reinterpret_cast<const uint4*>(sp), t1 = *reinterpret_cast<const uint4*>(sp + 8);
       v.sv[0] = t0.x; v.sv[1] = t0.y; v.sv[2] = t0.z; v.sv[3] = t0.w;
       v.sv[4] = t1.x; v.sv[5] = t1.y; v.sv[6] = t1.z; v.sv[7] = t1.w;
-      const uint2 zz = *reinterpret_cast<const uint2*>(zp);
-      v.zv[0] = zz.x;
-      v.zv[1] = zz.y;
+      if constexpr (ZP) {
+        const uint2 zz = *reinterpret_cast<const uint2*>(zp);
+        v.zv[0] = zz.x;
+        v.zv[1] = zz.y;
+      }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < NS / 2; ++i) v.sv[i] = 0;
 #pragma unroll
-    for (int i = 0; i < (NS + 7) / 8; ++i) v.zv[i] = 0;
-#pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int gi = min(g0 + t, a.Gtot - 1);
       v.sv[t >> 1] |= (uint32_t)a.s[srow + gi] << (16 * (t & 1));
-      const uint32_t zb = a.zp[zrow + (gi >> 1)];
-      v.zv[t >> 3] |= ((gi & 1) ? (zb >> 4) : (zb & 15u)) << (4 * (t & 7));
+      if constexpr (ZP) {
+        const uint32_t zb = a.zp[zrow + (gi >> 1)];
+        v.zv[t >> 3] |= ((gi & 1) ? (zb >> 4) : (zb & 15u)) << (4 * (t & 7));
+      }
     }
   }
   return v;
 }
 
-template <int MT, int W, int KQ, int G>
+// sum over one group of x * (q - z) for 4-bit codes: steps j0 .. j0 + NJ - 1
+// of a tile (word j of the lane's 16 bytes), as a1 + a16 / 16.
+template <int NJ>
+__device__ __forceinline__ float dot_group4(const u4& w4, uint32_t z, uint32_t magic, int j0, const uint4 (&xv)[4]) {
+  const h2 zq = as_h2(z * 0x00010001u + magic);   // (1024 + z) twice
+  const h2 z16 = as_h2(z * 0x00100010u + magic);  // (1024 + 16z) twice
+  float a1 = 0.0f, a16 = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int j = j0 + jj;
+    const uint32_t w = w4[j], w8 = w >> 8;
+    a1 = dot2(as_u32(as_h2((w & 0x000F000Fu) | magic) - zq), xv[j].x, a1);
+    a16 = dot2(as_u32(as_h2((w & 0x00F000F0u) | magic) - z16), xv[j].y, a16);
+    a1 = dot2(as_u32(as_h2((w8 & 0x000F000Fu) | magic) - zq), xv[j].z, a1);
+    a16 = dot2(as_u32(as_h2((w8 & 0x00F000F0u) | magic) - z16), xv[j].w, a16);
+  }
+  return fmaf(a16, 0.0625f, a1);
+}
+
+// sum over one group of x * q for 8-bit codes: steps j0 .. j0 + NJ - 1 of a
+// tile, codes in the two halves h0 (steps 0, 1) and h1 (steps 2, 3).
+template <int NJ>
+__device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, const uint4 (&xv)[4]) {
+  const h2 bias = as_h2(0x64806480u);  // (1152, 1152)
+  float a = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int j = j0 + jj;
+    const u4& h = j < 2 ? h0 : h1;
+    const uint32_t lo = h[2 * (j & 1)] ^ 0x80808080u, hi = h[2 * (j & 1) + 1] ^ 0x80808080u;
+    a = dot2(as_u32(as_h2(byte_pair(lo, 0x04010400u)) - bias), xv[j].x, a);
+    a = dot2(as_u32(as_h2(byte_pair(lo, 0x04030402u)) - bias), xv[j].y, a);
+    a = dot2(as_u32(as_h2(byte_pair(hi, 0x04010400u)) - bias), xv[j].z, a);
+    a = dot2(as_u32(as_h2(byte_pair(hi, 0x04030402u)) - bias), xv[j].w, a);
+  }
+  return a;
+}
+
+template <int MT, int W, int KQ, int G, int BITS>
 __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  constexpr int TB = BITS == 4 ? kTileBytes : kTileBytes8;
+  constexpr int HALVES = BITS / 4;  // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;     // groups per 128-column tile
   constexpr int NS = KQ * GPT;     // groups per segment
   constexpr int NT = W * 64;
@@ -144,7 +196,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
   uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
   float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][16]
 
-  const uint8_t* tbase = a.qp + (size_t)nb * a.KT * kTileBytes;
+  const uint8_t* tbase = a.qp + (size_t)nb * a.KT * TB;
   const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
   const uint32_t srow = n * (uint32_t)a.Gtot, zrow = n * (uint32_t)a.GB;
   const uint32_t lane16 = 16u * lane;
@@ -167,11 +219,13 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    const SZ<NS> sz = load_sz<NS>(a, srow, zrow, kt0 * GPT);
-    u4 buf[KQ];
+    const SZ<NS> sz = load_sz<NS, BITS == 4>(a, srow, zrow, kt0 * GPT);
+    u4 buf[KQ][HALVES];
 #pragma unroll
     for (int t = 0; t < KQ; ++t)
-      buf[t] = *reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, a.KT - 1) * kTileBytes + lane16);
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h)
+        buf[t][h] = *reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, a.KT - 1) * TB + 1024u * h + lane16);
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
@@ -193,20 +247,13 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
         for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 32 * j);
 #pragma unroll
         for (int gi = 0; gi < GPT; ++gi) {
-          const uint32_t z = sz.zero(t * GPT + gi);
-          const h2 zq = as_h2(z * 0x00010001u + magic);   // (1024 + z) twice
-          const h2 z16 = as_h2(z * 0x00100010u + magic);  // (1024 + 16z) twice
-          float a1 = 0.0f, a16 = 0.0f;
-#pragma unroll
-          for (int jj = 0; jj < 4 / GPT; ++jj) {
-            const int j = gi * (4 / GPT) + jj;
-            const uint32_t w = buf[t][j], w8 = w >> 8;
-            a1 = dot2(as_u32(as_h2((w & 0x000F000Fu) | magic) - zq), xv[j].x, a1);
-            a16 = dot2(as_u32(as_h2((w & 0x00F000F0u) | magic) - z16), xv[j].y, a16);
-            a1 = dot2(as_u32(as_h2((w8 & 0x000F000Fu) | magic) - zq), xv[j].z, a1);
-            a16 = dot2(as_u32(as_h2((w8 & 0x00F000F0u) | magic) - z16), xv[j].w, a16);
-          }
-          acc[m] = fmaf(sz.scale(t * GPT + gi), fmaf(a16, 0.0625f, a1), acc[m]);
+          const int j0 = gi * (4 / GPT);
+          float d;
+          if constexpr (BITS == 8)
+            d = dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], j0, xv);
+          else
+            d = dot_group4<4 / GPT>(buf[t][0], sz.zero(t * GPT + gi), magic, j0, xv);
+          acc[m] = fmaf(sz.scale(t * GPT + gi), d, acc[m]);
         }
       }
     }
@@ -294,25 +341,33 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+template <int MT, int W, int G, int BITS>
+void launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  auto k = gemv_kernel<MT, W, kKQ, G, BITS>;
+  if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+  k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
+}
+
 template <int MT, int W>
-hipError_t launch_t(const GemvPlan& p, int group, GemvArgs a, hipStream_t stream) {
-  dim3 grid(p.gx, p.gy, p.KS), block(W * 64);
-  if (group == 128) {
-    auto k = gemv_kernel<MT, W, kKQ, 128>;
-    if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    k<<<grid, block, p.lds, stream>>>(a);
+hipError_t launch_t(const GemvPlan& p, int group, int bits, GemvArgs a, hipStream_t stream) {
+  if (bits == 8) {
+    if (group == 128) launch_k<MT, W, 128, 8>(p, a, stream);
+    else launch_k<MT, W, 32, 8>(p, a, stream);
   } else {
-    auto k = gemv_kernel<MT, W, kKQ, 32>;
-    if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    k<<<grid, block, p.lds, stream>>>(a);
+    if (group == 128) launch_k<MT, W, 128, 4>(p, a, stream);
+    else launch_k<MT, W, 32, 4>(p, a, stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int describe_gemv(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len) {
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len) {
   const GemvPlan p = plan_gemv(M, N, K);
+  if (bits == 8)
+    return snprintf(buf, len,
+                    "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, BITS=8> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d", p.MT,
+                    p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
   return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                   p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
 }
@@ -325,13 +380,13 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
   return part_al + (size_t)p.gx * p.gy * sizeof(unsigned);
 }
 
-hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
+hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x,
+                       const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream) {
   const GemvPlan p = plan_gemv(M, N, K);
   GemvArgs a;
   a.x = x;
-  a.qp = reinterpret_cast<const uint8_t*>(qpacked);
+  a.qp = static_cast<const uint8_t*>(qpacked);
   a.s = s;
   a.zp = zpacked;
   a.y = y;
@@ -349,7 +404,7 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_
   const int ns = kKQ * (128 / group);  // groups per segment
   a.sz_vec = (a.Gtot % ns == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
               (reinterpret_cast<uintptr_t>(s) & (uintptr_t)(2 * ns > 16 ? 15 : 2 * ns - 1)) == 0 &&
-              (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0)
+              (bits == 8 || (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0))
                  ? 1
                  : 0;
   a.partial = nullptr;
@@ -359,10 +414,10 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_
     a.partial = static_cast<float*>(workspace);
     a.counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
   }
-  if (p.MT == 1) return launch_t<1, 16>(p, group, a, stream);
-  if (p.MT == 2) return launch_t<2, 16>(p, group, a, stream);
-  if (p.MT == 4) return launch_t<4, 16>(p, group, a, stream);
-  return launch_t<8, 8>(p, group, a, stream);
+  if (p.MT == 1) return launch_t<1, 16>(p, group, bits, a, stream);
+  if (p.MT == 2) return launch_t<2, 16>(p, group, bits, a, stream);
+  if (p.MT == 4) return launch_t<4, 16>(p, group, bits, a, stream);
+  return launch_t<8, 8>(p, group, bits, a, stream);
 }
 
 }  // namespace wq

@@ -17,21 +17,30 @@ hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N
 hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint8_t* zpacked, int64_t N, int64_t K,
                           int group, int out_dtype, void* out, hipStream_t stream);
 
+// Group absmax int8: codes [N][K] int8 (or NULL), scales [N][G], 2048-byte
+// tiles (or NULL).
+hipError_t launch_quantize_w8(const void* W, int dtype, int64_t N, int64_t K, int group, int8_t* q_codes,
+                              uint16_t* s, uint8_t* qpacked, hipStream_t stream);
+hipError_t launch_pack_w8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, hipStream_t stream);
+hipError_t launch_dequant_w8(const uint8_t* qpacked, const uint16_t* s, int64_t N, int64_t K, int group,
+                             int out_dtype, void* out, hipStream_t stream);
+
 // VALU split-K GEMV for small M.  It needs a workspace (fp32 partial sums and
 // counters, zero on entry and left zero) only when it splits K across
 // workgroups; gemv_workspace_bytes gives the size (0 otherwise).
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 // Writes a one-line description of the kernel and launch shape chosen for this
-// problem (snprintf semantics).
-int describe_gemv(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len);
-hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
+// problem (snprintf semantics).  bits: 4 (tile codes + zero-points) or 8
+// (2048-byte int8 tiles; zpacked unused).
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len);
+hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x,
+                       const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream);
 
 // MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
-int describe_gemm(int64_t M, int64_t N, int64_t K, int group, char* buf, size_t len);
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x, const uint32_t* qpacked,
+int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len);
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
 
 }  // namespace wq

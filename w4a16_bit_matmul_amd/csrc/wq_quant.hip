@@ -10,6 +10,9 @@
 // "Quantization Methods Compared", section "What quantisation does"
 // (q = round(w / s)); at b = 4 the code q in [-7, 7] is stored as q + 8 with
 // zero-point 8, so every kernel that decodes s * (q - z) decodes it.
+// Group absmax int8 (same page and section: s = max|w| / 127, q = round(w / s),
+// decoding q * s) keeps one fp16 scale per group, no zero-point, and 8-bit
+// codes in 2048-byte tiles (16 rows x 128 columns).
 //
 // This translation unit is compiled with -ffp-contract=off: every fp32
 // operation below is one correctly rounded IEEE operation (division is the
@@ -116,6 +119,26 @@ __device__ __forceinline__ uint32_t encode(float w, const GroupParams& p) {
   float r = rintf(t);
   r = fminf(fmaxf(r, 0.0f), 15.0f);
   return (uint32_t)r;
+}
+
+// Group absmax int8: s = max|w| / 127; a group whose fp16 scale is 0 stores
+// s = 0 and codes 0.
+__device__ __forceinline__ GroupParams group_params_w8(float lo, float hi) {
+  const float m = fmaxf(hi, -lo);
+  const float s32 = m / 127.0f;
+  GroupParams p;
+  p.s_bits = f32_to_f16_bits(s32);
+  p.s = f16_bits_to_f32(p.s_bits);
+  p.z = 0.0f;
+  if (p.s == 0.0f) p.s_bits = 0;
+  return p;
+}
+
+__device__ __forceinline__ uint32_t encode_w8(float w, const GroupParams& p) {
+  if (p.s == 0.0f) return 0u;
+  float r = rintf(w / p.s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (uint32_t)(int)r & 0xffu;  // two's-complement byte
 }
 
 // Nibble position of column e (0..7) inside a packed word.
@@ -339,6 +362,154 @@ __global__ __launch_bounds__(256) void dequant_kernel(
   }
 }
 
+// ---- group absmax int8 -------------------------------------------------------
+// One wavefront per (16-row block, 128-column tile).  Lane l = r + 16*c reads
+// the 32 weights of row r that its bytes of the tile hold (columns
+// 32*j + 8*c + e) and writes them with two 16-byte stores, one per half tile.
+
+// Loads the 32 weights of lane (r, c) of tile kt, zeros past K or N.
+template <int DT>
+__device__ __forceinline__ void load_lane_tile(const void* W, int64_t n, bool row_ok, int64_t K, int64_t kt, int c,
+                                               float (&w)[4][8], bool (&jok)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    jok[j] = row_ok && (kt * 128 + 32 * j < K);
+    if (jok[j]) {
+      load8<DT>(W, n * K + kt * 128 + 32 * j + 8 * c, w[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[j][e] = 0.0f;
+    }
+  }
+}
+
+template <int DT, int G>
+__global__ __launch_bounds__(256) void quantize_w8_kernel(const void* __restrict__ W, int64_t N, int64_t K,
+                                                          int64_t NBLK, int64_t KT, int8_t* __restrict__ q_codes,
+                                                          uint16_t* __restrict__ s_out, uint8_t* __restrict__ qpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;  // whole wave exits together
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  const bool row_ok = n < N;
+  const int64_t Gtot = K / G;
+
+  float w[4][8];
+  bool jok[4];
+  load_lane_tile<DT>(W, n, row_ok, K, kt, c, w, jok);
+
+  GroupParams gp[4];
+  if constexpr (G == 128) {
+    float lo = w[0][0], hi = w[0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
+    const GroupParams p = group_params_w8(wave_min4(lo), wave_max4(hi));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gp[j] = p;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float lo = w[j][0], hi = w[j][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) { lo = fminf(lo, w[j][e]); hi = fmaxf(hi, w[j][e]); }
+      gp[j] = group_params_w8(wave_min4(lo), wave_max4(hi));
+    }
+  }
+
+  uint32_t words[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = jok[j] ? encode_w8(w[j][e], gp[j]) : 0u;
+    words[j][0] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    words[j][1] = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    if (q_codes && jok[j])
+      *reinterpret_cast<uint2*>(q_codes + n * K + kt * 128 + 32 * j + 8 * c) = make_uint2(words[j][0], words[j][1]);
+  }
+  if (qpacked) {
+    uint8_t* t = qpacked + tile8_offset_bytes(nb, kt, KT) + 16 * lane;
+    *reinterpret_cast<u4*>(t) = u4{words[0][0], words[0][1], words[1][0], words[1][1]};
+    *reinterpret_cast<u4*>(t + 1024) = u4{words[2][0], words[2][1], words[3][0], words[3][1]};
+  }
+  if (row_ok) {
+    if constexpr (G == 128) {
+      if (c == 0) s_out[n * Gtot + kt] = gp[0].s_bits;
+    } else {
+      const int64_t gi = kt * 4 + c;  // lane c writes group c of this tile
+      if (gi < Gtot) s_out[n * Gtot + gi] = c == 0 ? gp[0].s_bits : c == 1 ? gp[1].s_bits : c == 2 ? gp[2].s_bits : gp[3].s_bits;
+    }
+  }
+}
+
+// int8 codes [N][K] -> 2048-byte tiles.
+__global__ __launch_bounds__(256) void pack_w8_kernel(const int8_t* __restrict__ q_codes, int64_t N, int64_t K,
+                                                      int64_t NBLK, int64_t KT, uint8_t* __restrict__ qpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  uint2 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+    v[j] = (n < N && kt * 128 + 32 * j < K) ? *reinterpret_cast<const uint2*>(q_codes + n * K + k0) : make_uint2(0, 0);
+  }
+  uint8_t* t = qpacked + tile8_offset_bytes(nb, kt, KT) + 16 * lane;
+  *reinterpret_cast<u4*>(t) = u4{v[0].x, v[0].y, v[1].x, v[1].y};
+  *reinterpret_cast<u4*>(t + 1024) = u4{v[2].x, v[2].y, v[3].x, v[3].y};
+}
+
+// 2048-byte tiles + scales -> What[N][K] = s * q (exact in fp32).
+template <int OUT, int G>
+__global__ __launch_bounds__(256) void dequant_w8_kernel(const uint8_t* __restrict__ qpacked,
+                                                         const uint16_t* __restrict__ s_in, int64_t N, int64_t K,
+                                                         int64_t NBLK, int64_t KT, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  if (n >= N) return;
+  const int64_t Gtot = K / G;
+  const uint8_t* t = qpacked + tile8_offset_bytes(nb, kt, KT) + 16 * lane;
+  const u4 h0 = *reinterpret_cast<const u4*>(t), h1 = *reinterpret_cast<const u4*>(t + 1024);
+  const uint32_t wd[4][2] = {{h0[0], h0[1]}, {h0[2], h0[3]}, {h1[0], h1[1]}, {h1[2], h1[3]}};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+    if (k0 >= K) continue;
+    const float s = f16_bits_to_f32(s_in[n * Gtot + k0 / G]);
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = (int)(int8_t)(uint8_t)(wd[j][e >> 2] >> (8 * (e & 3)));
+      d[e] = s * (float)q;  // exact: 11-bit significand times |q| <= 127
+    }
+    if constexpr (OUT == 0) {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + n * K + k0);
+      o[0] = make_float4(d[0], d[1], d[2], d[3]);
+      o[1] = make_float4(d[4], d[5], d[6], d[7]);
+    } else {
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t a = OUT == 2 ? f32_to_f16_bits(d[2 * i]) : f32_to_bf16_bits(d[2 * i]);
+        uint32_t b = OUT == 2 ? f32_to_f16_bits(d[2 * i + 1]) : f32_to_bf16_bits(d[2 * i + 1]);
+        p[i] = a | (b << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + n * K + k0) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  }
+}
+
 inline int64_t blocks_for(int64_t waves) { return (waves + kWavesPerBlock - 1) / kWavesPerBlock; }
 
 }  // namespace
@@ -388,6 +559,40 @@ hipError_t launch_dequant(const uint32_t* qpacked, const uint16_t* s, const uint
     if (out_dtype == 0) WQ_D(0, 32); else if (out_dtype == 1) WQ_D(1, 32); else WQ_D(2, 32);
   }
 #undef WQ_D
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_w8(const void* W, int dtype, int64_t N, int64_t K, int group, int8_t* q_codes,
+                              uint16_t* s, uint8_t* qpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+#define WQ_Q8(DT, G) quantize_w8_kernel<DT, G><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, s, qpacked)
+  if (group == 128) {
+    if (dtype == 0) WQ_Q8(0, 128); else if (dtype == 1) WQ_Q8(1, 128); else WQ_Q8(2, 128);
+  } else {
+    if (dtype == 0) WQ_Q8(0, 32); else if (dtype == 1) WQ_Q8(1, 32); else WQ_Q8(2, 32);
+  }
+#undef WQ_Q8
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_w8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  pack_w8_kernel<<<dim3((unsigned)blocks_for(NBLK * KT)), dim3(256), 0, stream>>>(q_codes, N, K, NBLK, KT, qpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_w8(const uint8_t* qpacked, const uint16_t* s, int64_t N, int64_t K, int group,
+                             int out_dtype, void* out, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+#define WQ_D8(O, G) dequant_w8_kernel<O, G><<<grid, block, 0, stream>>>(qpacked, s, N, K, NBLK, KT, out)
+  if (group == 128) {
+    if (out_dtype == 0) WQ_D8(0, 128); else if (out_dtype == 1) WQ_D8(1, 128); else WQ_D8(2, 128);
+  } else {
+    if (out_dtype == 0) WQ_D8(0, 32); else if (out_dtype == 1) WQ_D8(1, 32); else WQ_D8(2, 32);
+  }
+#undef WQ_D8
   return hipGetLastError();
 }
 
