@@ -132,6 +132,44 @@ def bench_gemm(steps, warmup):
     return wl, t, t_dense
 
 
+def bench_w8(steps, warmup):
+    """Group absmax int8 weights (W8A16) on the decode and M=128 workloads:
+    the same seeded weights quantized to int8 on the GPU, the GEMV and the MFMA
+    GEMM timed like the 4-bit ones (one Python call per launch; the int8 GEMV
+    takes longer than that call)."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    out = {}
+    for name, n_steps, n_warm in (("decode_gemv", steps, warmup // 2), ("batched_gemm", max(50, steps // 2),
+                                                                        max(300, warmup // 30))):
+        wl = workloads.WORKLOADS[name]
+        W = wl.weights()
+        Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        qw = wq.wq_quantize_w8(Wd, wl.group)["qw"]
+        del Wd
+        nbytes = wl.algorithmic_bytes_w8()
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        qws = [qw] + [wq.QuantizedWeight8(qw.qpacked.clone(), qw.s.clone(), qw.N, qw.K, qw.group)
+                      for _ in range(copies - 1)]
+        y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+        n = wq.wq_gemm_w8a16_workspace_bytes(wl.M, wl.N, wl.K, wl.group)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+        t = _time_calls(lambda i: wq.wq_gemm_w8a16(xd, qws[i % copies], y=y, workspace=ws), n_steps, n_warm)
+        rec = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
+               "kernel": wq.wq_gemm_w8a16_plan(wl.M, wl.N, wl.K, wl.group), "us_per_launch": round(t * 1e6, 3),
+               "algorithmic_bytes": nbytes, "gbs": round(nbytes / t / 1e9, 2),
+               "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "weight_copies_rotated": copies}
+        if wl.M >= 64:
+            tf = wl.flops() / t / 1e12
+            rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
+        out[name] = rec
+        log(f"[bench] W8A16 {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.1f} GB/s")
+    return out
+
+
 def bench_quantize(wl_name="decode_gemv", reps=20):
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -284,6 +322,7 @@ def main():
         tq, moved = bench_quantize()
         line["quantize"] = {"workload": "decode_gemv weights (bf16 8192x8192, g=128)", "us": round(tq * 1e6, 2),
                             "gbs": round(moved / tq / 1e9, 2)}
+        line["w8a16"] = bench_w8(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -106,6 +106,11 @@ class Workload:
         nk = self.N * self.K
         return nk // 2 + 2 * nk // self.group + nk // (2 * self.group) + 2 * self.M * self.K + 2 * self.M * self.N
 
+    def algorithmic_bytes_w8(self) -> int:
+        """The same for int8 weights: 8-bit codes and fp16 scales, no zero-points."""
+        nk = self.N * self.K
+        return nk + 2 * nk // self.group + 2 * self.M * self.K + 2 * self.M * self.N
+
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
 
