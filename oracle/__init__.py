@@ -76,6 +76,8 @@ def _load():
         "orc_pack_device_w8": (I, [P, I64, I64, P]),
         "orc_unpack_device_w8": (I, [P, I64, I64, P]),
         "orc_gemm_rows_w8_f64": (I, [I64, I64, I64, I, P, P, P, I64, I64, P]),
+        "orc_kv_quantize": (I, [P, I, I64, I64, P, I64, P, P, P]),
+        "orc_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P]),
         "orc_bits_per_weight": (ctypes.c_double, [I, I, I, I]),
         "orc_storage_bytes": (ctypes.c_double, [I64, I, I, I, I]),
     }
@@ -300,6 +302,41 @@ def gemm_rows_w8_f64(x_f16_bits, q, s, group: int, n0: int, nrows: int) -> np.nd
     _check(_load().orc_gemm_rows_w8_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), n0, nrows, _ptr(y)),
            "orc_gemm_rows_w8_f64")
     return y
+
+
+# --- INT4 KV cache in blocks of 128 ------------------------------------------
+
+def kv_alloc(S: int, hd: int):
+    """Empty (zero-filled) cache arrays for S rows of hd values."""
+    nb = hd // 128
+    return (np.zeros((S, hd // 2), np.uint8), np.zeros((S, nb), np.uint16), np.zeros((S, (nb + 1) // 2), np.uint8))
+
+
+def kv_quantize(X: np.ndarray, cache, slot=None, dtype: int | None = None):
+    """Quantizes each token's vector X[t] (hd values, blocks of 128: the
+    "KV cache quantization" section's int4 cache) into cache row slot[t]
+    (default t), in place; slots outside the cache are skipped."""
+    X = np.ascontiguousarray(X)
+    if dtype is None:
+        if X.dtype == np.float32:
+            dtype = F32
+        else:
+            raise ValueError("give dtype for non-float32 input")
+    T, hd = X.shape
+    codes, s, z = cache
+    sl = None if slot is None else np.ascontiguousarray(slot, np.int32)
+    _check(_load().orc_kv_quantize(_ptr(X), dtype, T, hd, None if sl is None else _ptr(sl), codes.shape[0],
+                                   _ptr(codes), _ptr(s), _ptr(z)), "orc_kv_quantize")
+    return cache
+
+
+def kv_dequant(cache, T: int, hd: int, slot=None, out_dtype: int = F32) -> np.ndarray:
+    codes, s, z = cache
+    sl = None if slot is None else np.ascontiguousarray(slot, np.int32)
+    out = np.empty((T, hd), np.float32 if out_dtype == F32 else np.uint16)
+    _check(_load().orc_kv_dequant(_ptr(codes), _ptr(s), _ptr(z), T, hd, None if sl is None else _ptr(sl),
+                                  codes.shape[0], out_dtype, _ptr(out)), "orc_kv_dequant")
+    return out
 
 
 # --- symmetric quantizers and storage ----------------------------------------

@@ -18,6 +18,8 @@
  *        scales, bits per weight).
  *   [T]  "Test-time quantization", section "The maths that matter" (symmetric
  *        b-bit scale M/(2^(b-1)-1) and the half-step error bound).
+ *   [Q]  also section "KV cache quantization" (the cache stored as int4 in
+ *        blocks of 128 values, half a byte per value plus the scale overhead).
  *
  * Where the pages leave a step open, the readings below are used (each is also
  * listed in the design notes):
@@ -552,6 +554,91 @@ int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t*
             y_rows[m * nrows + i] = acc;
         }
         free(wr);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* INT4 KV cache in blocks of 128  ([Q] "KV cache quantization")             */
+/* ------------------------------------------------------------------------- */
+
+/* Each token's K (or V) vector of hd values (all heads, hd a multiple of 128)
+ * is cut into hd/128 blocks of 128 consecutive values, and each block goes
+ * through the same group quantizer as the weights (scale, zero-point, 4-bit
+ * codes).  Token t of a call is written to cache row slot[t] (slot == NULL:
+ * row t); tokens whose slot lies outside [0, S) are skipped.  Cache layout of
+ * one row:
+ *   codes  hd/2 bytes: block b at byte 64*b; its 16 little-endian 32-bit words
+ *          j = 0..15 hold values 8j + e (e = 0..7), value e in nibble
+ *          4*(e%2) + e/2 (the word format of the weight tiles);
+ *   s      hd/128 fp16 scales;
+ *   z      ceil(hd/256) bytes, block b's zero-point in the low nibble of byte
+ *          b/2 when b is even, in the high nibble when b is odd. */
+static int64_t kv_nibble_byte(int64_t v, int* high)
+{
+    int64_t b = v / 128, i = v % 128, j = i / 8, e = i % 8;
+    int p = (int)(4 * (e % 2) + e / 2);
+    *high = p % 2;
+    return b * 64 + j * 4 + p / 2;
+}
+
+int orc_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                    uint8_t* codes, uint16_t* s, uint8_t* z)
+{
+    if (!X || !codes || !s || !z || T <= 0 || hd <= 0 || hd % 128 || S <= 0) return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
+    int64_t nb = hd / 128, zb = (nb + 1) / 2;
+    float w[128];
+    uint8_t q[128];
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t row = slot ? (int64_t)slot[t] : t;
+        if (row < 0 || row >= S) continue;
+        uint8_t* crow = codes + row * (hd / 2);
+        uint8_t* zrow = z + row * zb;
+        if (nb % 2) zrow[zb - 1] &= 0x0f;  /* an odd block count leaves the last high nibble 0 */
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int i = 0; i < 128; ++i) w[i] = load_w(X, dtype, t * hd + b * 128 + i);
+            uint8_t zz;
+            int st = quantize_one_group(w, 128, q, s + row * nb + b, &zz);
+            if (st) return st;
+            zrow[b / 2] = (uint8_t)((b % 2) ? (zrow[b / 2] & 0x0f) | (zz << 4) : (zrow[b / 2] & 0xf0) | zz);
+            for (int i = 0; i < 128; ++i) {
+                int high;
+                int64_t byte = kv_nibble_byte(b * 128 + i, &high);
+                crow[byte] = (uint8_t)(high ? (crow[byte] & 0x0f) | (q[i] << 4) : (crow[byte] & 0xf0) | q[i]);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Rows slot[t] (slot == NULL: row t) of the cache decoded to x_hat[t][hd] =
+ * s * (q - z) (fp32 exact; fp16 / bf16 one rounding); rows outside [0, S)
+ * decode to zeros. */
+int orc_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* z, int64_t T, int64_t hd,
+                   const int32_t* slot, int64_t S, int out_dtype, void* out)
+{
+    if (!codes || !s || !z || !out || T <= 0 || hd <= 0 || hd % 128 || S <= 0) return ORC_EINVAL;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EINVAL;
+    int64_t nb = hd / 128, zb = (nb + 1) / 2;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t row = slot ? (int64_t)slot[t] : t;
+        int ok = row >= 0 && row < S;
+        for (int64_t v = 0; v < hd; ++v) {
+            float val = 0.0f;
+            if (ok) {
+                int high;
+                int64_t byte = kv_nibble_byte(v, &high);
+                int q = high ? codes[row * (hd / 2) + byte] >> 4 : codes[row * (hd / 2) + byte] & 15;
+                int64_t b = v / 128;
+                uint8_t zbyte = z[row * zb + b / 2];
+                int zz = (b % 2) ? zbyte >> 4 : zbyte & 15;
+                val = orc_f16_to_f32(s[row * nb + b]) * (float)(q - zz);
+            }
+            if (out_dtype == ORC_F32) ((float*)out)[t * hd + v] = val;
+            else if (out_dtype == ORC_F16) ((uint16_t*)out)[t * hd + v] = orc_f32_to_f16(val);
+            else ((uint16_t*)out)[t * hd + v] = orc_f32_to_bf16(val);
+        }
     }
     return 0;
 }

@@ -55,6 +55,13 @@ int orc_unpack_device_w8(const uint8_t* packed, int64_t N, int64_t K, int8_t* q)
 int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
                          const int8_t* q, const uint16_t* s, int64_t n0, int64_t nrows, double* y_rows);
 
+/* INT4 KV cache: blocks of 128 values of each token's vector, the group
+ * quantizer per block, scattered to cache rows slot[t] (NULL: row t). */
+int orc_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                    uint8_t* codes, uint16_t* s, uint8_t* z);
+int orc_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* z, int64_t T, int64_t hd,
+                   const int32_t* slot, int64_t S, int out_dtype, void* out);
+
 int orc_symmetric(const double* w, int64_t n, int bits, int32_t* q, double* s_out, double* w_hat);
 
 double orc_bits_per_weight(int bits, int g, int scale_bits, int zero_bits);

@@ -401,6 +401,115 @@ def test_w8_gemm_rows(orc):
 
 
 # --------------------------------------------------------------------------
+# INT4 KV cache in blocks of 128 (quantization post, "KV cache quantization")
+# --------------------------------------------------------------------------
+
+def test_kv_block_holds_the_printed_example():
+    # the page's 8 weights padded to one block of 128, placed as block 3 of a
+    # token vector of 8 heads x 128: codes, scale and zero-point as printed
+    import oracle as orc
+    g = golden("int4_worked_example.json")
+    X = (np.random.default_rng(40).standard_normal((3, 1024)) * 0.5).astype(np.float32)
+    X[1, 384:512] = 0.0
+    X[1, 384:392] = workloads.WORKED_EXAMPLE_W
+    cache = orc.kv_alloc(3, 1024)
+    orc.kv_quantize(X, cache)
+    codes, s, z = cache
+    assert round(float(orc.f16_bits_to_f32(s[1, 3:4])[0]), g["printed"]["s_decimals"]) == g["printed"]["s"]
+    assert (z[1, 1] & 15) == g["printed"]["z"]
+    x_hat = orc.kv_dequant(cache, 3, 1024)
+    w_hat = x_hat[1, 384:392]
+    assert np.allclose(w_hat, g["printed"]["w_hat"], atol=1e-3, rtol=0)
+    # the block's codes, read back through the documented nibble positions
+    word = int(codes[1, 3 * 64: 3 * 64 + 4].view(np.uint32)[0])
+    got = [(word >> (4 * (4 * (e % 2) + e // 2))) & 15 for e in range(8)]
+    assert got == g["printed"]["q"]
+
+
+def test_kv_storage_per_value():
+    # half a byte per value plus the per-block scale and zero-point
+    import oracle as orc
+    hd = 1024
+    codes, s, z = orc.kv_alloc(1, hd)
+    per_value = (codes.nbytes + s.nbytes + z.nbytes) / hd
+    assert per_value == 0.5 + 2.5 / 128
+    assert round(2 / per_value, 2) == 3.85  # against a 2-byte fp16/bf16 cache
+
+
+def test_kv_blocks_invariants_and_bound():
+    import oracle as orc
+    rng = np.random.default_rng(41)
+    T, hd = 16, 1024
+    X = (rng.standard_normal((T, hd)) * 2.0).astype(np.float32)
+    X[:, 77] *= 30  # an outlier channel in every token
+    cache = orc.kv_alloc(T, hd)
+    orc.kv_quantize(X, cache)
+    codes, s, z = cache
+    sh = orc.f16_bits_to_f32(s.ravel()).reshape(s.shape).astype(np.float64)
+    x_hat = orc.kv_dequant(cache, T, hd).astype(np.float64)
+    Xb = X.reshape(T, hd // 128, 128).astype(np.float64)
+    lo = np.minimum(Xb.min(axis=2), 0)
+    hi = np.maximum(Xb.max(axis=2), 0)
+    s32 = ((hi - lo).astype(np.float32) / np.float32(15)).astype(np.float64)
+    bound = sh / 2 + 15 * np.abs(s32 - sh)
+    err = np.abs(x_hat.reshape(T, hd // 128, 128) - Xb).max(axis=2)
+    assert np.all(err <= bound * (1 + 1e-6))
+    # each block's zero-point decodes to exactly zero and lies in [0, 15]
+    zz = np.stack([z & 15, z >> 4], axis=2).reshape(T, -1)[:, :hd // 128]
+    assert zz.max() <= 15
+    # blocks are independent: changing one block leaves every other one alone
+    X2 = X.copy()
+    X2[5, 300] = 100.0
+    c2 = orc.kv_alloc(T, hd)
+    orc.kv_quantize(X2, c2)
+    diff_s = np.argwhere(c2[1] != s)
+    assert all(tuple(d) == (5, 2) for d in diff_s) and len(diff_s) == 1
+
+
+def test_kv_slots_scatter_skip_and_keep():
+    import oracle as orc
+    rng = np.random.default_rng(42)
+    T, hd, S = 6, 256, 10
+    X = rng.standard_normal((T, hd)).astype(np.float32)
+    ref = orc.kv_alloc(T, hd)
+    orc.kv_quantize(X, ref)
+    cache = orc.kv_alloc(S, hd)
+    for a in cache:
+        a[...] = 0xAB if a.dtype == np.uint8 else 0x1234  # previous contents
+    slots = np.array([7, 2, -1, 9, 10, 0], np.int32)  # -1 and 10 are outside the cache
+    orc.kv_quantize(X, cache, slot=slots)
+    for t, row in enumerate(slots):
+        if 0 <= row < S:
+            for a, b in zip(cache, ref):
+                assert np.array_equal(a[row], b[t])
+    for row in (1, 3, 4, 5, 6, 8):  # untouched rows keep their contents
+        assert np.all(cache[0][row] == 0xAB) and np.all(cache[1][row] == 0x1234)
+    got = orc.kv_dequant(cache, T, hd, slot=slots)
+    assert np.all(got[2] == 0) and np.all(got[4] == 0)
+    assert np.array_equal(got[0], orc.kv_dequant(ref, T, hd)[0])
+
+
+def test_kv_odd_block_count_and_grid_exact_values():
+    # hd = 384 (three blocks: the third zero-point alone in its byte); values
+    # of the form 2^-4 * (c - z0) with codes 0 and 15 in every block decode
+    # exactly
+    import oracle as orc
+    rng = np.random.default_rng(43)
+    T, hd = 5, 384
+    c = rng.integers(0, 16, (T, hd))
+    c[:, ::128] = 0
+    c[:, 1::128] = 15
+    z0 = rng.integers(1, 15, (T, hd // 128))
+    X = (np.ldexp(1.0, -4) * (c - np.repeat(z0, 128, axis=1))).astype(np.float32)
+    cache = orc.kv_alloc(T, hd)
+    orc.kv_quantize(X, cache)
+    assert np.array_equal(orc.kv_dequant(cache, T, hd), X)
+    assert np.all((cache[2][:, 1] >> 4) == 0)
+    zz = np.stack([cache[2][:, 0] & 15, cache[2][:, 0] >> 4, cache[2][:, 1] & 15], axis=1)
+    assert np.array_equal(zz, z0)
+
+
+# --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
 
