@@ -72,7 +72,7 @@ extern "C" {
 typedef enum {
     WQ_OK = 0,
     WQ_EINVAL = -1,       /* null pointer, non-positive size, bad dtype, path or scheme */
-    WQ_EUNSUPPORTED = -2, /* group not 32 or 128, or K not a multiple of group */
+    WQ_EUNSUPPORTED = -2, /* group not 32 or 128, K not a multiple of group (or of 32 / 128 where stated) */
     WQ_EALIGN = -3,       /* pointer not aligned as documented */
     WQ_EWORKSPACE = -4,   /* workspace missing or smaller than required */
     WQ_EHIP = -5          /* a HIP runtime call or kernel launch failed */
@@ -261,6 +261,45 @@ int wq_gemm_w8a16_ex(int64_t M, int64_t N, int64_t K, int group,
 
 /* As wq_gemm_plan, for wq_gemm_w8a16_ex. */
 int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len);
+
+/* ---- INT4 KV cache in blocks of 128 -----------------------------------------
+ * "Quantization for LLM inference", section "KV cache quantization": the K/V
+ * cache stored as int4 in blocks of 128 values (half a byte per value plus
+ * the scale overhead).  Read as: each token's K (or V) vector of hd values
+ * (all KV heads of one layer, hd a multiple of 128) is cut into hd/128 blocks
+ * of 128 consecutive values, and each block is quantized exactly like one
+ * weight group of 128 (wq_quantize_groups' numerics: fp16 scale, 4-bit
+ * zero-point, 4-bit codes).  A cache of S rows (token slots) holds per row:
+ *   codes   hd/2 bytes; block b at byte 64*b, as 16 little-endian 32-bit words,
+ *           word j holding values 8j + e (e = 0..7) of the block, value e in
+ *           nibble 4*(e%2) + e/2 (the word format of the weight tiles)
+ *   s_f16   hd/128 fp16 scales
+ *   zpacked ceil(hd/256) bytes, block b's zero-point in the low nibble of
+ *           byte b/2 when b is even, in the high nibble when b is odd (an odd
+ *           block count leaves the last high nibble 0)
+ * so 0.5 + 2.5/128 bytes per value (3.85x smaller than an fp16 cache).  Arrays
+ * are row-major [S][...]; device memory, caller-owned. */
+
+/* Byte sizes of the three cache arrays for S rows of hd values.  Host-only.
+ * WQ_EUNSUPPORTED when hd is not a multiple of 128. */
+int wq_kv_layout_bytes(int64_t S, int64_t hd, size_t* codes_bytes, size_t* s_bytes, size_t* z_bytes);
+
+/* Quantizes X [T][hd] (x_dtype WQ_F32, WQ_BF16 or WQ_F16; 16-byte aligned)
+ * token by token into cache row slot[t] (slot: device int32 [T], 4-byte
+ * aligned, or NULL for rows 0..T-1).  Tokens whose slot lies outside [0, S)
+ * are skipped; rows not named keep their contents; two tokens naming the same
+ * row in one call leave either token's values there.  codes 8-byte aligned.
+ * Preconditions as wq_quantize_groups (finite values, block range below
+ * 15 * 65520).  Deterministic. */
+int wq_kv_quantize(const void* X, int x_dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                   uint8_t* codes, uint16_t* s_f16, uint8_t* zpacked, void* stream);
+
+/* Decodes cache rows slot[t] (NULL: rows 0..T-1) into out [T][hd] as out_dtype
+ * (WQ_F32 exact s * (q - z); WQ_F16 / WQ_BF16 one round-to-nearest-even of it);
+ * tokens whose slot lies outside [0, S) decode to zeros.  out 16-byte
+ * aligned. */
+int wq_kv_dequant(const uint8_t* codes, const uint16_t* s_f16, const uint8_t* zpacked, int64_t T, int64_t hd,
+                  const int32_t* slot, int64_t S, int out_dtype, void* out, void* stream);
 
 #ifdef __cplusplus
 }

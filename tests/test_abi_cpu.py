@@ -204,3 +204,26 @@ def test_w8_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_w8a16_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128, BITS=8>") and "grid=(224,1,1)" in d, d
     assert wq.wq_gemm_w8a16_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32, BITS=8>")
+
+
+def test_kv_entry_points_checked_on_host():
+    c, s, z = wq.wq_kv_layout_bytes(4096, 1024)
+    assert (c, s, z) == (4096 * 512, 4096 * 8 * 2, 4096 * 4)
+    assert wq.wq_kv_layout_bytes(10, 384)[2] == 10 * 2
+    with pytest.raises(wq.WQError) as e:
+        wq.wq_kv_layout_bytes(10, 200)
+    assert e.value.status == wq.WQ_EUNSUPPORTED
+    f = "wq_kv_quantize"
+    assert call(f, None, 1, 4, 1024, None, 8, A, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 4, 1024, None, 8, A, A, None, None) == wq.WQ_EINVAL
+    assert call(f, A, 5, 4, 1024, None, 8, A, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 0, 1024, None, 8, A, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 4, 1024, None, 0, A, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 4, 1000, None, 8, A, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, B, 1, 4, 1024, None, 8, A, A, A, None) == wq.WQ_EALIGN
+    assert call(f, A, 1, 4, 1024, B, 8, A, A, A, None) == wq.WQ_EALIGN
+    g = "wq_kv_dequant"
+    assert call(g, A, A, A, 4, 1024, None, 8, 7, A, None) == wq.WQ_EINVAL
+    assert call(g, A, A, None, 4, 1024, None, 8, 0, A, None) == wq.WQ_EINVAL
+    assert call(g, A, A, A, 4, 96, None, 8, 0, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(g, A, A, A, 4, 1024, None, 8, 0, B, None) == wq.WQ_EALIGN

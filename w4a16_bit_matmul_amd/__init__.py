@@ -29,6 +29,7 @@ EXPORTED = (
     "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
     "wq_layout_bytes_w8", "wq_quantize_w8", "wq_pack_int8", "wq_dequant_w8", "wq_gemm_w8a16_workspace_bytes",
     "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
+    "wq_kv_layout_bytes", "wq_kv_quantize", "wq_kv_dequant",
 )
 
 _lib = None
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_w8a16": (I, [I64, I64, I64, I, P, P, P, P, P, SZ, P]),
         "wq_gemm_w8a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_w8a16_plan": (I, [I64, I64, I64, I, I, ctypes.c_char_p, SZ]),
+        "wq_kv_layout_bytes": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "wq_kv_quantize": (I, [P, I, I64, I64, P, I64, P, P, P, P]),
+        "wq_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -317,3 +321,49 @@ def wq_gemm_w8a16(x: torch.Tensor, qw: QuantizedWeight8, *, y: torch.Tensor | No
                                   _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                   path, _stream(stream)), "wq_gemm_w8a16")
     return y
+
+
+# ---- INT4 KV cache in blocks of 128 -------------------------------------------
+
+@dataclass
+class KVCache:
+    """Device arrays of an INT4 KV cache of S rows (token slots) of hd values."""
+    codes: torch.Tensor  # uint8 [S][hd/2]
+    s: torch.Tensor      # float16 [S][hd/128]
+    zpacked: torch.Tensor  # uint8 [S][ceil(hd/256)]
+    S: int
+    hd: int
+
+
+def wq_kv_layout_bytes(S: int, hd: int):
+    c, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wq_kv_layout_bytes(S, hd, ctypes.byref(c), ctypes.byref(s), ctypes.byref(z)), "wq_kv_layout_bytes")
+    return c.value, s.value, z.value
+
+
+def kv_cache_alloc(S: int, hd: int, device="cuda") -> KVCache:
+    wq_kv_layout_bytes(S, hd)  # validates hd
+    nb = hd // 128
+    return KVCache(torch.zeros((S, hd // 2), dtype=torch.uint8, device=device),
+                   torch.zeros((S, nb), dtype=torch.float16, device=device),
+                   torch.zeros((S, (nb + 1) // 2), dtype=torch.uint8, device=device), S, hd)
+
+
+def wq_kv_quantize(X: torch.Tensor, cache: KVCache, slot: torch.Tensor | None = None, stream=None) -> KVCache:
+    """Quantizes X [T][hd] (fp32, bf16 or fp16, on the GPU) into cache rows
+    slot[t] (int32 device tensor, or None for rows 0..T-1)."""
+    T, hd = X.shape
+    assert hd == cache.hd
+    assert slot is None or (slot.dtype == torch.int32 and slot.numel() == T and slot.is_contiguous())
+    _check(lib().wq_kv_quantize(_ptr(X), _DT.get(X.dtype, -1), T, hd, _ptr(slot), cache.S, _ptr(cache.codes),
+                                _ptr(cache.s), _ptr(cache.zpacked), _stream(stream)), "wq_kv_quantize")
+    return cache
+
+
+def wq_kv_dequant(cache: KVCache, T: int, slot: torch.Tensor | None = None, out_dtype=torch.float16,
+                  stream=None) -> torch.Tensor:
+    assert slot is None or (slot.dtype == torch.int32 and slot.numel() == T and slot.is_contiguous())
+    out = torch.empty((T, cache.hd), dtype=out_dtype, device=cache.codes.device)
+    _check(lib().wq_kv_dequant(_ptr(cache.codes), _ptr(cache.s), _ptr(cache.zpacked), T, cache.hd, _ptr(slot),
+                               cache.S, _DT.get(out_dtype, -1), _ptr(out), _stream(stream)), "wq_kv_dequant")
+    return out

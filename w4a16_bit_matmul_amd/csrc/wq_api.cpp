@@ -259,4 +259,47 @@ int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, cha
   return WQ_OK;
 }
 
+// ---- INT4 KV cache in blocks of 128 ------------------------------------------
+
+namespace {
+int check_kv(int64_t T, int64_t hd, int64_t S) {
+  if (T <= 0 || hd <= 0 || S <= 0) return WQ_EINVAL;
+  if (hd % 128 != 0) return WQ_EUNSUPPORTED;
+  if (T > (int64_t(1) << 31) || S > (int64_t(1) << 31) || hd > (int64_t(1) << 24)) return WQ_EINVAL;
+  return WQ_OK;
+}
+}  // namespace
+
+int wq_kv_layout_bytes(int64_t S, int64_t hd, size_t* codes_bytes, size_t* s_bytes, size_t* z_bytes) {
+  const int st = check_kv(1, hd, S);
+  if (st) return st;
+  const int64_t nb = hd / 128;
+  if (codes_bytes) *codes_bytes = (size_t)(S * (hd / 2));
+  if (s_bytes) *s_bytes = (size_t)(S * nb * 2);
+  if (z_bytes) *z_bytes = (size_t)(S * ((nb + 1) / 2));
+  return WQ_OK;
+}
+
+int wq_kv_quantize(const void* X, int x_dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                   uint8_t* codes, uint16_t* s_f16, uint8_t* zpacked, void* stream) {
+  if (!X || !codes || !s_f16 || !zpacked) return WQ_EINVAL;
+  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16 && x_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_kv(T, hd, S);
+  if (st) return st;
+  if (!aligned(X, 16) || !aligned(codes, 8) || !aligned(s_f16, 2) || (slot && !aligned(slot, 4))) return WQ_EALIGN;
+  return hip_status(
+      wq::launch_kv_quantize(X, x_dtype, T, hd, slot, S, codes, s_f16, zpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_kv_dequant(const uint8_t* codes, const uint16_t* s_f16, const uint8_t* zpacked, int64_t T, int64_t hd,
+                  const int32_t* slot, int64_t S, int out_dtype, void* out, void* stream) {
+  if (!codes || !s_f16 || !zpacked || !out) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16 && out_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_kv(T, hd, S);
+  if (st) return st;
+  if (!aligned(codes, 8) || !aligned(s_f16, 2) || !aligned(out, 16) || (slot && !aligned(slot, 4))) return WQ_EALIGN;
+  return hip_status(wq::launch_kv_dequant(codes, s_f16, zpacked, T, hd, slot, S, out_dtype, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -25,6 +25,13 @@ hipError_t launch_pack_w8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* 
 hipError_t launch_dequant_w8(const uint8_t* qpacked, const uint16_t* s, int64_t N, int64_t K, int group,
                              int out_dtype, void* out, hipStream_t stream);
 
+// INT4 KV cache in blocks of 128: token t's hd values (X [T][hd]) into cache
+// row slot[t] (slot NULL: row t; rows outside [0, S) skipped), and back.
+hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                              uint8_t* codes, uint16_t* s, uint8_t* zp, hipStream_t stream);
+hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* zp, int64_t T, int64_t hd,
+                             const int32_t* slot, int64_t S, int out_dtype, void* out, hipStream_t stream);
+
 // VALU split-K GEMV for small M.  It needs a workspace (fp32 partial sums and
 // counters, zero on entry and left zero) only when it splits K across
 // workgroups; gemv_workspace_bytes gives the size (0 otherwise).

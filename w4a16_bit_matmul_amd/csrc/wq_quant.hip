@@ -13,6 +13,10 @@
 // Group absmax int8 (same page and section: s = max|w| / 127, q = round(w / s),
 // decoding q * s) keeps one fp16 scale per group, no zero-point, and 8-bit
 // codes in 2048-byte tiles (16 rows x 128 columns).
+// INT4 KV cache ("Quantization for LLM inference", section "KV cache
+// quantization": int4 in blocks of 128): each token's K or V vector is cut into
+// blocks of 128 values, each block quantized like a weight group, the rows
+// scattered to caller-chosen cache slots.
 //
 // This translation unit is compiled with -ffp-contract=off: every fp32
 // operation below is one correctly rounded IEEE operation (division is the
@@ -510,6 +514,107 @@ __global__ __launch_bounds__(256) void dequant_w8_kernel(const uint8_t* __restri
   }
 }
 
+// ---- INT4 KV cache in blocks of 128 ------------------------------------------
+// A 16-lane group owns a pair of blocks (2p, 2p + 1) of one token: lanes 0..7
+// block 2p, lanes 8..15 block 2p + 1, each lane 16 consecutive values (two
+// code words).  A block's min / max is a reduction over its 8 lanes; the
+// pair's zero-points share one byte, composed with one shuffle inside the
+// group.  Cache row of hd values: codes hd/2 bytes (block b at byte 64*b, word
+// j = values 8j..8j+7 in the weight-tile nibble order), hd/128 fp16 scales,
+// ceil(hd/256) zero-point bytes.
+
+template <int DT>
+__device__ __forceinline__ void load16(const void* X, int64_t idx, float (&v)[16]) {
+  load8<DT>(X, idx, v);
+  load8<DT>(X, idx + 8, v + 8);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const void* __restrict__ X, int64_t T, int64_t hd,
+                                                          const int32_t* __restrict__ slot, int64_t S,
+                                                          uint8_t* __restrict__ codes, uint16_t* __restrict__ s_out,
+                                                          uint8_t* __restrict__ zp) {
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nb = hd / 128, ppt = (nb + 1) / 2, zb = ppt;
+  const int64_t pid = gl >> 4;
+  const int half = (int)(gl >> 3) & 1, part = (int)gl & 7;
+  const int64_t t = min(pid / ppt, T - 1);      // clamped: lanes past the end compute on real data, store nothing
+  const int64_t b = min(2 * (pid % ppt) + half, nb - 1);
+  const bool active = pid < T * ppt && 2 * (pid % ppt) + half < nb;
+  float v[16];
+  load16<DT>(X, t * hd + b * 128 + part * 16, v);
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, m));
+    hi = fmaxf(hi, __shfl_xor(hi, m));
+  }
+  const GroupParams p = group_params(lo, hi);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= encode(v[i], p) << (4 * nibble_pos(i & 7));
+  const uint32_t z = (uint32_t)p.z;
+  const uint32_t z_next = (uint32_t)__shfl_down((int)z, 8, 16);  // zero-point of block 2p + 1 (lanes 0..7)
+  const int64_t row = slot ? (int64_t)slot[t] : t;
+  if (!active || row < 0 || row >= S) return;
+  *reinterpret_cast<uint2*>(codes + row * (hd / 2) + b * 64 + part * 8) = make_uint2(w[0], w[1]);
+  if (part == 0) {
+    s_out[row * nb + b] = p.s_bits;
+    if (half == 0) zp[row * zb + b / 2] = (uint8_t)(z | ((b + 1 < nb ? z_next : 0u) << 4));
+  }
+}
+
+// Cache rows slot[t] -> out[t][hd] = s * (q - z); rows outside [0, S) give 0.
+template <int OUT>
+__global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ s_in,
+                                                         const uint8_t* __restrict__ zp, int64_t T, int64_t hd,
+                                                         const int32_t* __restrict__ slot, int64_t S,
+                                                         void* __restrict__ out) {
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nb = hd / 128, zb = (nb + 1) / 2;
+  const int64_t bid = gl >> 3;
+  if (bid >= T * nb) return;
+  const int part = (int)gl & 7;
+  const int64_t t = bid / nb, b = bid % nb;
+  const int64_t row = slot ? (int64_t)slot[t] : t;
+  const bool ok = row >= 0 && row < S;
+  float d[16];
+  if (ok) {
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + row * (hd / 2) + b * 64 + part * 8);
+    const float sc = f16_bits_to_f32(s_in[row * nb + b]);
+    const uint32_t zbyte = zp[row * zb + b / 2];
+    const int z = (int)((b & 1) ? zbyte >> 4 : zbyte & 15u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = (int)((((i < 8) ? w.x : w.y) >> (4 * nibble_pos(i & 7))) & 15u);
+      d[i] = sc * (float)(q - z);  // exact
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = 0.0f;
+  }
+  const int64_t o = t * hd + b * 128 + part * 16;
+  if constexpr (OUT == 0) {
+    float4* po = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) po[i] = make_float4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
+  } else {
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = OUT == 2 ? f32_to_f16_bits(d[2 * i]) : f32_to_bf16_bits(d[2 * i]);
+      const uint32_t c = OUT == 2 ? f32_to_f16_bits(d[2 * i + 1]) : f32_to_bf16_bits(d[2 * i + 1]);
+      pk[i] = a | (c << 16);
+    }
+    uint4* po = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
+    po[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    po[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+  }
+}
+
 inline int64_t blocks_for(int64_t waves) { return (waves + kWavesPerBlock - 1) / kWavesPerBlock; }
 
 }  // namespace
@@ -593,6 +698,26 @@ hipError_t launch_dequant_w8(const uint8_t* qpacked, const uint16_t* s, int64_t 
     if (out_dtype == 0) WQ_D8(0, 32); else if (out_dtype == 1) WQ_D8(1, 32); else WQ_D8(2, 32);
   }
 #undef WQ_D8
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
+                              uint8_t* codes, uint16_t* s, uint8_t* zp, hipStream_t stream) {
+  const int64_t lanes = T * ((hd / 128 + 1) / 2) * 16;
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if (dtype == 0) kv_quantize_kernel<0><<<grid, block, 0, stream>>>(X, T, hd, slot, S, codes, s, zp);
+  else if (dtype == 1) kv_quantize_kernel<1><<<grid, block, 0, stream>>>(X, T, hd, slot, S, codes, s, zp);
+  else kv_quantize_kernel<2><<<grid, block, 0, stream>>>(X, T, hd, slot, S, codes, s, zp);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* zp, int64_t T, int64_t hd,
+                             const int32_t* slot, int64_t S, int out_dtype, void* out, hipStream_t stream) {
+  const int64_t lanes = T * (hd / 128) * 8;
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if (out_dtype == 0) kv_dequant_kernel<0><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
+  else if (out_dtype == 1) kv_dequant_kernel<1><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
+  else kv_dequant_kernel<2><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
   return hipGetLastError();
 }
 
