@@ -15,6 +15,7 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10000]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -167,6 +168,42 @@ def bench_w8(steps, warmup):
             rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
         out[name] = rec
         log(f"[bench] W8A16 {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.1f} GB/s")
+    return out
+
+
+def bench_kv(steps, warmup):
+    """INT4 KV cache in blocks of 128, the 70B layer's K and V (8 KV heads x
+    128 = 1024 values per token): the decode append (64 sequences, K and V
+    rows of one layer stacked: 128 rows scattered into a 131072-row cache) and
+    a 32768-token prefill of one K tensor (bf16 in)."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    hd = 1024
+    out = {}
+    rng = np.random.default_rng(77)
+    for name, T, S in (("decode_append", 128, 131072), ("prefill", 32768, 32768)):
+        X = workloads.f32_to_bf16_bits(rng.standard_normal((T, hd)).astype(np.float32))
+        Xd = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
+        cache = wq.kv_cache_alloc(S, hd)
+        slot = None
+        if name == "decode_append":
+            slot = torch.from_numpy(rng.choice(S, T, replace=False).astype(np.int32)).cuda()
+        n = steps if name == "decode_append" else max(20, steps // 10)
+        # arguments marshalled once: each timed call is one C call (the append
+        # is shorter than a Python call of the binding)
+        fn = wq.lib().wq_kv_quantize
+        args = (ctypes.c_void_p(Xd.data_ptr()), wq.WQ_BF16, T, hd,
+                None if slot is None else ctypes.c_void_p(slot.data_ptr()), S, ctypes.c_void_p(cache.codes.data_ptr()),
+                ctypes.c_void_p(cache.s.data_ptr()), ctypes.c_void_p(cache.zpacked.data_ptr()),
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert fn(*args) == wq.WQ_OK
+        t = _time_calls(lambda i: fn(*args), n, min(warmup, 2000) if T < 1000 else 20)
+        moved = T * hd * 2 + T * hd // 2 + T * (hd // 128) * 2 + T * ((hd // 128 + 1) // 2) + (T * 4 if slot is not None else 0)
+        out[name] = {"tokens": T, "values_per_token": hd, "cache_rows": S, "us_per_call": round(t * 1e6, 3),
+                     "bytes": moved, "gbs": round(moved / t / 1e9, 2), "frac_hbm_peak": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] KV int4 {name}: {t * 1e6:.2f} us per call, {moved / t / 1e9:.1f} GB/s")
     return out
 
 
@@ -323,6 +360,7 @@ def main():
         line["quantize"] = {"workload": "decode_gemv weights (bf16 8192x8192, g=128)", "us": round(tq * 1e6, 2),
                             "gbs": round(moved / tq / 1e9, 2)}
         line["w8a16"] = bench_w8(args.steps, args.warmup)
+        line["kv_int4"] = bench_kv(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -356,3 +356,46 @@ def test_matmul_symmetric_within_tolerance(M, N, K, group, path):
     nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
     say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
 
+
+
+# ---------------------------------------------------------------- near-tie encodings
+
+def _near_tie_rows(group, rng, lo_mult, hi_mult):
+    """Rows whose weights sit on, and a few ulps either side of, the points where
+    w / s + z is a half-integer: the first two weights pin the group's range to
+    (hi_mult - lo_mult) * s_target with s_target exact in fp16, so the stored
+    scale is s_target; the rest are s_target * (k + 1/2), nudged by 0-3 ulps.
+    The quantizers' rounding shortcut must agree there with the exact division."""
+    rows = []
+    for s_target in (1.0, 0.0999755859375, 0.005859375, 7.75, 2.0 ** -20):
+        for _ in range(4):
+            k = rng.integers(lo_mult, hi_mult, group).astype(np.float32) + np.float32(0.5)
+            w = (np.float32(s_target) * k).astype(np.float32)
+            for i, d in enumerate(rng.integers(-3, 4, group)):
+                for _ in range(abs(int(d))):
+                    w[i] = np.nextafter(w[i], np.float32(np.inf if d > 0 else -np.inf))
+            w[0], w[1] = np.float32(s_target * hi_mult), np.float32(s_target * lo_mult)
+            rows.append(w)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantize_near_ties_bit_exact(group):
+    say(f"near-tie encodings g={group}")
+    rng = np.random.default_rng(90 + group)
+    assert_quantize_matches(_near_tie_rows(group, rng, -7, 8), "f32", group)
+    assert_quantize_matches(_near_tie_rows(group, rng, -7, 7), "f32", group, scheme=wq.WQ_SYM)
+    W8 = _near_tie_rows(group, rng, -127, 127)
+    out = wq.wq_quantize_w8(to_dev_weights(W8, "f32"), group, codes=True, packed=True)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize_w8(W8, group)
+    assert np.array_equal(out["q_codes"].cpu().numpy(), q) and np.array_equal(f16_bits(out["s"]), s)
+    # the same rows as KV-cache blocks of 128
+    Wk = _near_tie_rows(128, rng, -7, 8).reshape(-1, 256)
+    ref = oracle.kv_alloc(Wk.shape[0], 256)
+    oracle.kv_quantize(Wk, ref)
+    cache = wq.kv_cache_alloc(Wk.shape[0], 256)
+    wq.wq_kv_quantize(torch.from_numpy(Wk).cuda(), cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.codes.cpu().numpy(), ref[0])
+    assert np.array_equal(f16_bits(cache.s), ref[1]) and np.array_equal(cache.zpacked.cpu().numpy(), ref[2])

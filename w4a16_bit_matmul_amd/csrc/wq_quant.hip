@@ -70,11 +70,12 @@ __device__ __forceinline__ float wave_max4(float v) {
   return v;
 }
 
-// Scale (fp16 bits), its fp32 value and the zero-point of a group whose
-// min and max are lo and hi.
+// Scale (fp16 bits), its fp32 value, an approximate reciprocal of it and the
+// zero-point of a group whose min and max are lo and hi.
 struct GroupParams {
   uint16_t s_bits;
   float s;
+  float r;  // v_rcp_f32(s): only steers the rounding shortcut below
   float z;
 };
 
@@ -86,6 +87,7 @@ __device__ __forceinline__ GroupParams group_params(float lo, float hi) {
   GroupParams p;
   p.s_bits = f32_to_f16_bits(s32);
   p.s = f16_bits_to_f32(p.s_bits);
+  p.r = __builtin_amdgcn_rcpf(p.s);
   if (p.s == 0.0f) {  // degenerate group: s = 0, z = 0, codes 0
     p.s_bits = 0;
     p.z = 0.0f;
@@ -104,23 +106,39 @@ __device__ __forceinline__ GroupParams group_params_sym(float lo, float hi) {
   GroupParams p;
   p.s_bits = f32_to_f16_bits(s32);
   p.s = f16_bits_to_f32(p.s_bits);
+  p.r = __builtin_amdgcn_rcpf(p.s);
   p.z = 8.0f;
   if (p.s == 0.0f) p.s_bits = 0;
   return p;
 }
 
+// rne(fl32(fl32(w / s) + z)) -- the encoding's two correctly rounded fp32
+// operations and the rounding to an integer -- without the division wherever
+// it cannot matter.  t = fma(w, r, z) with r = v_rcp_f32(s) (1 ulp) lies within
+// |w/s| * 2^-22 + ulp(t) of the real w/s + z, and the exact steps lie within
+// 2^-24 * (|w/s| + |t|) of it; with |w/s| <= 2^(B-1) + 1 for B-bit codes both
+// are below 2^(B-1) * 2^-21.  So when t is farther than `margin` (2^-14 for
+// 4-bit codes, 2^-10 for 8-bit: room for an rcp error of 16 ulp) from every
+// half-integer, t, the real value and the exact result all round to the same
+// integer; otherwise the exact steps run.
+__device__ __forceinline__ float round_quotient(float w, const GroupParams& p, float z, float margin) {
+  const float t = fmaf(w, p.r, z);
+  const float f = t - floorf(t);  // exact for |t| < 2^23
+  if (fabsf(f - 0.5f) > margin) return rintf(t);
+  const float u = w / p.s;  // correctly rounded
+  return rintf(u + z);
+}
+
 __device__ __forceinline__ uint32_t encode_sym(float w, const GroupParams& p) {
   if (p.s == 0.0f) return 8u;
-  float r = rintf(w / p.s);
+  float r = round_quotient(w, p, 0.0f, 0x1p-14f);
   r = fminf(fmaxf(r, -7.0f), 7.0f);
   return (uint32_t)(r + 8.0f);
 }
 
 __device__ __forceinline__ uint32_t encode(float w, const GroupParams& p) {
   if (p.s == 0.0f) return 0u;
-  float t = w / p.s;
-  t = t + p.z;
-  float r = rintf(t);
+  float r = round_quotient(w, p, p.z, 0x1p-14f);
   r = fminf(fmaxf(r, 0.0f), 15.0f);
   return (uint32_t)r;
 }
@@ -133,6 +151,7 @@ __device__ __forceinline__ GroupParams group_params_w8(float lo, float hi) {
   GroupParams p;
   p.s_bits = f32_to_f16_bits(s32);
   p.s = f16_bits_to_f32(p.s_bits);
+  p.r = __builtin_amdgcn_rcpf(p.s);
   p.z = 0.0f;
   if (p.s == 0.0f) p.s_bits = 0;
   return p;
@@ -140,7 +159,7 @@ __device__ __forceinline__ GroupParams group_params_w8(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t encode_w8(float w, const GroupParams& p) {
   if (p.s == 0.0f) return 0u;
-  float r = rintf(w / p.s);
+  float r = round_quotient(w, p, 0.0f, 0x1p-10f);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return (uint32_t)(int)r & 0xffu;  // two's-complement byte
 }
