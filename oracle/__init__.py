@@ -77,6 +77,9 @@ def _load():
         "orc_unpack_device_w8": (I, [P, I64, I64, P]),
         "orc_gemm_rows_w8_f64": (I, [I64, I64, I64, I, P, P, P, I64, I64, P]),
         "orc_kv_quantize": (I, [P, I, I64, I64, P, I64, P, P, P]),
+        "orc_quantize_groups_scaled": (I, [P, I, I64, I64, I, I, P, P, P, P]),
+        "orc_scale_activations": (I, [P, I64, I64, P, P]),
+        "orc_channel_absmean": (I, [P, I64, I64, P]),
         "orc_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P]),
         "orc_bits_per_weight": (ctypes.c_double, [I, I, I, I]),
         "orc_storage_bytes": (ctypes.c_double, [I64, I, I, I, I]),
@@ -140,13 +143,15 @@ def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 ASYM, SYM = 0, 1
 
 
-def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None, scheme: int = ASYM):
+def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None, scheme: int = ASYM, alpha=None):
     """Group-wise INT4 quantization of W[N][K].  ASYM: the pages' "minimum
     maths" (s = (max - min)/15, z = round(-min/s), q = clip(round(w/s + z), 0,
     15)).  SYM: symmetric 4-bit (s = max|w|/7, q = clip(round(w/s), -7, 7),
     stored as q + 8 with zero-point 8).
 
     ``W`` is float32, or uint16 bit patterns with ``dtype`` BF16 or F16.
+    ``alpha`` (float32 [K], optional): the AWQ fold, each weight multiplied
+    by its input channel's factor (one fp32 multiplication) before quantizing.
     Returns (q[N][K] uint8, s[N][K/g] uint16 fp16 bits, z[N][K/g] uint8).
     """
     W = np.ascontiguousarray(W)
@@ -160,8 +165,10 @@ def quantize_groups(W: np.ndarray, group: int, dtype: int | None = None, scheme:
     q = np.empty((N, K), np.uint8)
     s = np.empty((N, G), np.uint16)
     z = np.empty((N, G), np.uint8)
-    _check(_load().orc_quantize_groups_ex(_ptr(W), dtype, N, K, group, scheme, _ptr(q), _ptr(s), _ptr(z)),
-           "orc_quantize_groups")
+    a = None if alpha is None else np.ascontiguousarray(alpha, np.float32)
+    assert a is None or a.shape == (K,)
+    _check(_load().orc_quantize_groups_scaled(_ptr(W), dtype, N, K, group, scheme, None if a is None else _ptr(a),
+                                              _ptr(q), _ptr(s), _ptr(z)), "orc_quantize_groups")
     return q, s, z
 
 
@@ -302,6 +309,27 @@ def gemm_rows_w8_f64(x_f16_bits, q, s, group: int, n0: int, nrows: int) -> np.nd
     _check(_load().orc_gemm_rows_w8_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), n0, nrows, _ptr(y)),
            "orc_gemm_rows_w8_f64")
     return y
+
+
+# --- AWQ-style per-input-channel scaling --------------------------------------
+
+def scale_activations(x_f16_bits: np.ndarray, alpha) -> np.ndarray:
+    """x' = fp16(fl32(x / alpha[k])) (the activation side of the AWQ fold)."""
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    a = np.ascontiguousarray(alpha, np.float32)
+    M, K = x.shape
+    out = np.empty((M, K), np.uint16)
+    _check(_load().orc_scale_activations(_ptr(x), M, K, _ptr(a), _ptr(out)), "orc_scale_activations")
+    return out
+
+
+def channel_absmean(x_f16_bits: np.ndarray) -> np.ndarray:
+    """Mean |x| of each input channel (fp32 sum in row order, then / M)."""
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    M, K = x.shape
+    out = np.empty(K, np.float32)
+    _check(_load().orc_channel_absmean(_ptr(x), M, K, _ptr(out)), "orc_channel_absmean")
+    return out
 
 
 # --- INT4 KV cache in blocks of 128 ------------------------------------------

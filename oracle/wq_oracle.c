@@ -19,7 +19,11 @@
  *   [T]  "Test-time quantization", section "The maths that matter" (symmetric
  *        b-bit scale M/(2^(b-1)-1) and the half-step error bound).
  *   [Q]  also section "KV cache quantization" (the cache stored as int4 in
- *        blocks of 128 values, half a byte per value plus the scale overhead).
+ *        blocks of 128 values, half a byte per value plus the scale overhead)
+ *        and section "AWQ" (a salient input channel's weights multiplied by a
+ *        factor before quantizing, its activations divided by it).
+ *   [C]  also section "The methods compared" (the activation-aware scaling of
+ *        salient channels and its toy example in symmetric int4).
  *
  * Where the pages leave a step open, the readings below are used (each is also
  * listed in the design notes):
@@ -268,6 +272,15 @@ int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
 int orc_quantize_groups_ex(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
                            uint8_t* q, uint16_t* s, uint8_t* z)
 {
+    return orc_quantize_groups_scaled(W, dtype, N, K, g, scheme, NULL, q, s, z);
+}
+
+/* As orc_quantize_groups_ex, each weight first multiplied by its input
+ * channel's factor alpha[k] (one fp32 multiplication; alpha == NULL: no
+ * scaling) -- the AWQ fold W' = W diag(alpha) ([Q] "AWQ"). */
+int orc_quantize_groups_scaled(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
+                               const float* alpha, uint8_t* q, uint16_t* s, uint8_t* z)
+{
     if (!W || !q || !s || !z || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
     if (scheme != ORC_ASYM && scheme != ORC_SYM) return ORC_EINVAL;
     if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
@@ -277,7 +290,10 @@ int orc_quantize_groups_ex(const void* W, int dtype, int64_t N, int64_t K, int g
     for (int64_t n = 0; n < N; ++n) {
         float* buf = (float*)malloc(sizeof(float) * (size_t)g);
         for (int64_t j = 0; j < G; ++j) {
-            for (int i = 0; i < g; ++i) buf[i] = load_w(W, dtype, n * K + j * g + i);
+            for (int i = 0; i < g; ++i) {
+                buf[i] = load_w(W, dtype, n * K + j * g + i);
+                if (alpha) buf[i] = buf[i] * alpha[j * g + i];
+            }
             int st = scheme == ORC_SYM
                          ? quantize_one_group_sym(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j)
                          : quantize_one_group(buf, g, q + n * K + j * g, s + n * G + j, z + n * G + j);
@@ -554,6 +570,36 @@ int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t*
             y_rows[m * nrows + i] = acc;
         }
         free(wr);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* AWQ-style per-input-channel scaling  ([Q] "AWQ", [C] "The methods compared") */
+/* ------------------------------------------------------------------------- */
+
+/* The activation side of the fold: x'[m][k] = fp16(fl32(x[m][k] / alpha[k])),
+ * so that x' W'^T = x W^T up to rounding. */
+int orc_scale_activations(const uint16_t* x_f16, int64_t M, int64_t K, const float* alpha, uint16_t* out)
+{
+    if (!x_f16 || !alpha || !out || M <= 0 || K <= 0) return ORC_EINVAL;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float v = orc_f16_to_f32(x_f16[m * K + k]) / alpha[k];
+            out[m * K + k] = orc_f32_to_f16(v);
+        }
+    return 0;
+}
+
+/* The statistic that finds salient channels: mean |x| of each input channel
+ * over the M rows, summed in row order in fp32, then divided by M in fp32. */
+int orc_channel_absmean(const uint16_t* x_f16, int64_t M, int64_t K, float* out)
+{
+    if (!x_f16 || !out || M <= 0 || K <= 0) return ORC_EINVAL;
+    for (int64_t k = 0; k < K; ++k) {
+        float acc = 0.0f;
+        for (int64_t m = 0; m < M; ++m) acc = acc + fabsf(orc_f16_to_f32(x_f16[m * K + k]));
+        out[k] = acc / (float)M;
     }
     return 0;
 }

@@ -32,8 +32,14 @@ int orc_quantize_groups(const void* W, int dtype, int64_t N, int64_t K, int g,
  * codes q + 8 with zero-point 8). */
 int orc_quantize_groups_ex(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
                            uint8_t* q, uint16_t* s, uint8_t* z);
+/* AWQ fold: each weight multiplied by alpha[k] (fp32) before quantizing. */
+int orc_quantize_groups_scaled(const void* W, int dtype, int64_t N, int64_t K, int g, int scheme,
+                               const float* alpha, uint8_t* q, uint16_t* s, uint8_t* z);
 int orc_dequant(const uint8_t* q, const uint16_t* s, const uint8_t* z,
                 int64_t N, int64_t K, int g, int out_dtype, void* out);
+/* x' = fp16(x / alpha[k]); mean |x| per channel (fp32, row order). */
+int orc_scale_activations(const uint16_t* x_f16, int64_t M, int64_t K, const float* alpha, uint16_t* out);
+int orc_channel_absmean(const uint16_t* x_f16, int64_t M, int64_t K, float* out);
 
 int orc_pack_canonical(const uint8_t* q, int64_t N, int64_t K, uint8_t* out);
 int64_t orc_device_bytes(int64_t N, int64_t K);

@@ -510,6 +510,86 @@ def test_kv_odd_block_count_and_grid_exact_values():
 
 
 # --------------------------------------------------------------------------
+# AWQ-style per-input-channel scaling (quantization post "AWQ"; methods page,
+# the symmetric int4 example by hand)
+# --------------------------------------------------------------------------
+
+def test_awq_toy_example(orc):
+    g = golden("awq_toy_example.json")
+    w = np.array([g["w"]], np.float32)
+    x = np.array(g["x"], np.float64)
+    c = g["salient_channel"]
+    assert x[c] / np.delete(x, c).max() == g["printed"]["salient_activation_ratio"]
+
+    def run(f):
+        a = np.ones(4, np.float32)
+        a[c] = f
+        q, s, z = orc.quantize_groups(w, 4, scheme=orc.SYM, alpha=a)
+        sh = float(orc.f16_bits_to_f32(s)[0])
+        w_eff = sh * (q[0].astype(np.float64) - 8) / a  # the layer's effective weights (x / alpha times W' hat)
+        return q[0].astype(int) - 8, sh, w_eff
+
+    q1, s1, w1 = run(1.0)
+    assert np.all(np.abs(q1) <= g["levels"])
+    y_err_plain = abs(x @ w1 - x @ w[0].astype(np.float64))
+    for f in (1.5, 2.0, 3.0, 4.0):  # factors that keep f * |w_c| below the group's max |w|
+        qf, sf, wf = run(f)
+        assert sf == s1  # same scale ...
+        assert np.array_equal(np.delete(qf, c), np.delete(q1, c))  # ... so the other channels' rounding is unchanged
+        assert np.array_equal(np.delete(wf, c), np.delete(w1, c))
+        assert abs(wf[c] - w[0, c]) < abs(w1[c] - w[0, c])  # the salient channel is kept more finely
+        assert abs(wf[c] - w[0, c]) <= sf / (2 * f) * (1 + 1e-6)
+        assert abs(x @ wf - x @ w[0].astype(np.float64)) < y_err_plain
+    # past max|w| / |w_c| the scaled weight raises the group maximum: a larger scale
+    # for every channel, so the other channels' rounding changes
+    q5, s5, w5 = run(5.0)
+    assert s5 > s1 and not np.array_equal(np.delete(w5, c), np.delete(w1, c))
+
+
+def test_awq_fold_identities(orc):
+    rng = np.random.default_rng(50)
+    W = (rng.standard_normal((12, 256)) * 0.02).astype(np.float32)
+    for group in (32, 128):
+        plain = orc.quantize_groups(W, group)
+        # alpha = 1 is no fold at all
+        assert all(np.array_equal(a, b) for a, b in zip(orc.quantize_groups(W, group, alpha=np.ones(256)), plain))
+        # a power of two on every channel commutes with the quantizer: same
+        # codes and zero-points, scales times that power (exact in fp16)
+        for e in (-3, 2):
+            q, s, z = orc.quantize_groups(W, group, alpha=np.full(256, 2.0 ** e, np.float32))
+            assert np.array_equal(q, plain[0]) and np.array_equal(z, plain[2])
+            assert np.array_equal(orc.f16_bits_to_f32(s.ravel()), orc.f16_bits_to_f32(plain[1].ravel()) * 2.0 ** e)
+    # the fold multiplies before quantizing: W diag(alpha) through the plain quantizer
+    alpha = rng.uniform(0.5, 3.0, 256).astype(np.float32)
+    Wa = (W * alpha[None, :]).astype(np.float32)
+    assert all(np.array_equal(a, b) for a, b in zip(orc.quantize_groups(W, 32, alpha=alpha),
+                                                     orc.quantize_groups(Wa, 32)))
+
+
+def test_awq_activation_side_and_statistic(orc):
+    rng = np.random.default_rng(51)
+    M, K = 9, 384
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    alpha = rng.uniform(0.3, 5.0, K).astype(np.float32)
+    xf = x.view(np.float16).astype(np.float32)
+    want = (xf / alpha[None, :]).astype(np.float32).astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.scale_activations(x, alpha), want)
+    p2 = (2.0 ** rng.integers(-2, 3, K)).astype(np.float32)  # powers of two: exact
+    assert np.array_equal(orc.scale_activations(x, p2).view(np.float16).astype(np.float64),
+                          xf.astype(np.float64) / p2[None, :])
+    # the statistic: fp32 sum of |x| in row order, then / M
+    acc = np.zeros(K, np.float32)
+    for m in range(M):
+        acc = (acc + np.abs(xf[m])).astype(np.float32)
+    assert np.array_equal(orc.channel_absmean(x), (acc / np.float32(M)).astype(np.float32))
+    # the maths cancels: with power-of-two factors, x' (W diag(alpha))^T = x W^T exactly
+    W = rng.standard_normal((5, K)).astype(np.float32)
+    xs = orc.scale_activations(x, p2)
+    y1 = orc.gemm_f64(xs, (W * p2[None, :]).astype(np.float32))
+    assert np.array_equal(y1, orc.gemm_f64(x, W))
+
+
+# --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
 
