@@ -207,6 +207,45 @@ def bench_kv(steps, warmup):
     return out
 
 
+def bench_awq():
+    """AWQ-style fold on the decode layer (8192 x 8192, g=128): salient channels
+    = the 1 % with the largest mean |x| over 64 calibration rows (the library's
+    statistic), alpha = factor there; the error ||y - x W^T|| of the INT4
+    product over 64 evaluation rows (same outlier channels, other values),
+    against the fp32 product of the unquantized bf16 weights, for each factor;
+    and the time of the activation-side kernel at M = 1."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    wl = workloads.WORKLOADS["decode_gemv"]
+    Wd = torch.from_numpy(wl.weights().view(np.int16)).cuda().view(torch.bfloat16)
+    f16 = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+    x = f16(workloads.gen_activations(wl.x_seed, 64, wl.K, outlier_frac=wl.x_outlier_frac))
+    x_cal = f16(workloads.gen_activations(wl.x_seed + 50, 64, wl.K, outlier_frac=wl.x_outlier_frac,
+                                          channel_seed=wl.x_seed + 1))
+    y_true = (x.float() @ Wd.float().t()).double()
+    stat = wq.wq_channel_absmean(x_cal)
+    top = torch.argsort(stat, descending=True, stable=True)[:round(0.01 * wl.K)]
+    err = {}
+    for factor in (1.0, 1.5, 2.0, 3.0, 4.0):
+        alpha = torch.ones(wl.K, dtype=torch.float32, device="cuda")
+        alpha[top] = factor
+        qw = wq.wq_quantize_groups(Wd, wl.group, alpha=alpha)["qw"]
+        y = wq.wq_gemm_w4a16(wq.wq_scale_activations(x, alpha), qw)
+        err[factor] = float((y.double() - y_true).norm())
+    alpha = torch.ones(wl.K, dtype=torch.float32, device="cuda")
+    x1 = x[:1].contiguous()
+    out = torch.empty_like(x1)
+    t = _time_calls(lambda i: wq.wq_scale_activations(x1, alpha, out=out), 200, 200)
+    best = min((f for f in err if f != 1.0), key=lambda f: err[f])
+    log(f"[bench] AWQ fold: error ratio {err[best] / err[1.0]:.3f} at factor {best}; activation scaling {t * 1e6:.2f} us")
+    return {"workload": "decode_gemv layer, 64 calibration + 64 evaluation rows", "salient_channels": int(top.numel()),
+            "error_norm_by_factor": {str(k): round(v, 5) for k, v in err.items()},
+            "best_factor": best, "error_ratio_best": round(err[best] / err[1.0], 4),
+            "scale_activations_us_m1_python_call": round(t * 1e6, 3)}
+
+
 def bench_quantize(wl_name="decode_gemv", reps=20):
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -361,6 +400,7 @@ def main():
                             "gbs": round(moved / tq / 1e9, 2)}
         line["w8a16"] = bench_w8(args.steps, args.warmup)
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
+        line["awq_fold"] = bench_awq()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

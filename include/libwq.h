@@ -135,6 +135,39 @@ int wq_quantize_groups_ex(const void* W, int w_dtype, int64_t N, int64_t K, int 
                           uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
                           uint32_t* qpacked, uint8_t* zpacked, void* stream);
 
+/* ---- AWQ-style per-input-channel scaling -------------------------------------
+ * "Quantization for LLM inference", section "AWQ": the weights of a salient
+ * input channel (one with large mean activation magnitude) are multiplied by a
+ * factor before quantizing and that channel's activations are divided by it,
+ * so the product is unchanged while the salient weights get a finer effective
+ * step ("Quantization Methods Compared", section "The methods compared").
+ * Read as: W' = W diag(alpha) with alpha[k] > 0 per input channel, quantized
+ * with the usual group quantizer; x' = x / alpha at run time; y = x' W'hat^T.
+ * In a model x / alpha folds into the preceding operation's weights; the
+ * standalone kernel below serves callers without one. */
+
+/* As wq_quantize_groups_ex, each weight first multiplied by alpha[k] (device
+ * fp32 [K], 16-byte aligned, positive and finite; one fp32 multiplication)
+ * before the group min/max, scale, zero-point and encoding.  alpha == NULL is
+ * wq_quantize_groups_ex.  The scaled weights must meet the same range
+ * precondition. */
+int wq_quantize_groups_scaled(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
+                              const float* alpha, uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
+                              uint32_t* qpacked, uint8_t* zpacked, void* stream);
+
+/* x_out[m][k] = fp16(fl32(x[m][k] / alpha[k])) (correctly rounded division,
+ * then round-to-nearest-even to fp16).  x_f16, x_out_f16 [M][K] and alpha [K]
+ * 16-byte aligned; K a multiple of 8 (WQ_EUNSUPPORTED otherwise); x_out may
+ * equal x (in place). */
+int wq_scale_activations(const uint16_t* x_f16, int64_t M, int64_t K, const float* alpha,
+                         uint16_t* x_out_f16, void* stream);
+
+/* out[k] = (|x[0][k]| + |x[1][k]| + ... + |x[M-1][k]|) / M, the sum taken in row
+ * order in fp32 and divided in fp32: the mean activation magnitude per input
+ * channel over calibration rows x [M][K], from which salient channels are
+ * chosen.  Deterministic. */
+int wq_channel_absmean(const uint16_t* x_f16, int64_t M, int64_t K, float* out, void* stream);
+
 /* Packing of codes and zero-points into the device layouts -- "Numerical
  * example" (eight 4-bit codes occupy four bytes; a 4-bit zero-point takes half
  * a byte).  q_codes [N][K] and z_codes [N][G] in, qpacked (16-byte aligned,

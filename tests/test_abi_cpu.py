@@ -227,3 +227,21 @@ def test_kv_entry_points_checked_on_host():
     assert call(g, A, A, None, 4, 1024, None, 8, 0, A, None) == wq.WQ_EINVAL
     assert call(g, A, A, A, 4, 96, None, 8, 0, A, None) == wq.WQ_EUNSUPPORTED
     assert call(g, A, A, A, 4, 1024, None, 8, 0, B, None) == wq.WQ_EALIGN
+
+
+def test_awq_entry_points_checked_on_host():
+    f = "wq_quantize_groups_scaled"
+    assert call(f, None, 1, 16, 128, 128, 0, A, None, A, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 128, 128, 3, A, None, A, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 100, 32, 0, A, None, A, None, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, A, 1, 16, 128, 128, 0, B, None, A, None, A, A, None) == wq.WQ_EALIGN
+    g = "wq_scale_activations"
+    assert call(g, None, 4, 128, A, A, None) == wq.WQ_EINVAL
+    assert call(g, A, 4, 128, None, A, None) == wq.WQ_EINVAL
+    assert call(g, A, 0, 128, A, A, None) == wq.WQ_EINVAL
+    assert call(g, A, 4, 100, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(g, A, 4, 128, B, A, None) == wq.WQ_EALIGN
+    h = "wq_channel_absmean"
+    assert call(h, None, 4, 128, A, None) == wq.WQ_EINVAL
+    assert call(h, A, 4, -1, A, None) == wq.WQ_EINVAL
+    assert call(h, A, 4, 128, B, None) == wq.WQ_EALIGN

@@ -30,6 +30,7 @@ EXPORTED = (
     "wq_layout_bytes_w8", "wq_quantize_w8", "wq_pack_int8", "wq_dequant_w8", "wq_gemm_w8a16_workspace_bytes",
     "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
     "wq_kv_layout_bytes", "wq_kv_quantize", "wq_kv_dequant",
+    "wq_quantize_groups_scaled", "wq_scale_activations", "wq_channel_absmean",
 )
 
 _lib = None
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
         "wq_kv_layout_bytes": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "wq_kv_quantize": (I, [P, I, I64, I64, P, I64, P, P, P, P]),
         "wq_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P, P]),
+        "wq_quantize_groups_scaled": (I, [P, I, I64, I64, I, I, P, P, P, P, P, P, P]),
+        "wq_scale_activations": (I, [P, I64, I64, P, P, P]),
+        "wq_channel_absmean": (I, [P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -145,10 +149,12 @@ def alloc_quantized(N: int, K: int, group: int, device="cuda") -> QuantizedWeigh
 
 
 def wq_quantize_groups(W: torch.Tensor, group: int, *, codes: bool = False, packed: bool = True,
-                       out: QuantizedWeight | None = None, scheme: int = WQ_ASYM, stream=None):
+                       out: QuantizedWeight | None = None, scheme: int = WQ_ASYM, alpha: torch.Tensor | None = None,
+                       stream=None):
     """Quantize W[N][K] (float32, bfloat16 or float16, on the GPU) with the
     asymmetric (WQ_ASYM) or symmetric (WQ_SYM: codes q + 8, zero-point 8)
-    4-bit scheme.
+    4-bit scheme; with ``alpha`` (float32 [K] on the GPU) the weights are first
+    multiplied by the per-input-channel factors (wq_quantize_groups_scaled).
 
     Returns a dict with ``s`` (fp16 [N][G]) and, as requested, ``q_codes``
     (uint8 [N][K]), ``z_codes`` (uint8 [N][G]) and ``qw`` (QuantizedWeight with
@@ -162,9 +168,10 @@ def wq_quantize_groups(W: torch.Tensor, group: int, *, codes: bool = False, pack
     s = qw.s if packed else torch.empty((N, G), dtype=torch.float16, device=dev)
     q_codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes else None
     z_codes = torch.empty((N, G), dtype=torch.uint8, device=dev) if codes else None
-    _check(lib().wq_quantize_groups_ex(_ptr(W), _DT.get(W.dtype, -1), N, K, group, scheme, _ptr(q_codes), _ptr(s),
-                                       _ptr(z_codes), _ptr(qw.qpacked) if packed else None,
-                                       _ptr(qw.zpacked) if packed else None, _stream(stream)),
+    assert alpha is None or (alpha.dtype == torch.float32 and alpha.numel() == K and alpha.is_contiguous())
+    _check(lib().wq_quantize_groups_scaled(_ptr(W), _DT.get(W.dtype, -1), N, K, group, scheme, _ptr(alpha),
+                                           _ptr(q_codes), _ptr(s), _ptr(z_codes), _ptr(qw.qpacked) if packed else None,
+                                           _ptr(qw.zpacked) if packed else None, _stream(stream)),
            "wq_quantize_groups")
     return {"s": s, "q_codes": q_codes, "z_codes": z_codes, "qw": qw if packed else None}
 
@@ -366,4 +373,26 @@ def wq_kv_dequant(cache: KVCache, T: int, slot: torch.Tensor | None = None, out_
     out = torch.empty((T, cache.hd), dtype=out_dtype, device=cache.codes.device)
     _check(lib().wq_kv_dequant(_ptr(cache.codes), _ptr(cache.s), _ptr(cache.zpacked), T, cache.hd, _ptr(slot),
                                cache.S, _DT.get(out_dtype, -1), _ptr(out), _stream(stream)), "wq_kv_dequant")
+    return out
+
+
+# ---- AWQ-style per-input-channel scaling ---------------------------------------
+
+def wq_scale_activations(x: torch.Tensor, alpha: torch.Tensor, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """x' = fp16(x / alpha[k]) for x [M][K] fp16 and alpha float32 [K]."""
+    M, K = x.shape
+    assert x.dtype == torch.float16 and alpha.dtype == torch.float32 and alpha.numel() == K
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().wq_scale_activations(_ptr(x), M, K, _ptr(alpha), _ptr(out), _stream(stream)), "wq_scale_activations")
+    return out
+
+
+def wq_channel_absmean(x: torch.Tensor, stream=None) -> torch.Tensor:
+    """Mean |x| per input channel of x [M][K] fp16 (fp32 sum in row order)."""
+    M, K = x.shape
+    assert x.dtype == torch.float16
+    out = torch.empty(K, dtype=torch.float32, device=x.device)
+    _check(lib().wq_channel_absmean(_ptr(x), M, K, _ptr(out), _stream(stream)), "wq_channel_absmean")
     return out

@@ -52,18 +52,42 @@ int wq_layout_bytes(int64_t N, int64_t K, int group, size_t* qpacked_bytes, size
   return WQ_OK;
 }
 
-int wq_quantize_groups_ex(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
-                          uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked,
-                          void* stream) {
+int wq_quantize_groups_scaled(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
+                              const float* alpha, uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes,
+                              uint32_t* qpacked, uint8_t* zpacked, void* stream) {
   if (!W || !s_f16) return WQ_EINVAL;
   if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
   if (scheme != WQ_ASYM && scheme != WQ_SYM) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  if (!aligned(W, 16) || !aligned(s_f16, 2) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8)))
+  if (!aligned(W, 16) || !aligned(s_f16, 2) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8)) ||
+      (alpha && !aligned(alpha, 16)))
     return WQ_EALIGN;
-  return hip_status(wq::launch_quantize(W, w_dtype, N, K, group, scheme == WQ_SYM, q_codes, s_f16, z_codes, qpacked,
-                                        zpacked, static_cast<hipStream_t>(stream)));
+  return hip_status(wq::launch_quantize(W, w_dtype, N, K, group, scheme == WQ_SYM, alpha, q_codes, s_f16, z_codes,
+                                        qpacked, zpacked, static_cast<hipStream_t>(stream)));
+}
+
+int wq_quantize_groups_ex(const void* W, int w_dtype, int64_t N, int64_t K, int group, int scheme,
+                          uint8_t* q_codes, uint16_t* s_f16, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked,
+                          void* stream) {
+  return wq_quantize_groups_scaled(W, w_dtype, N, K, group, scheme, nullptr, q_codes, s_f16, z_codes, qpacked,
+                                   zpacked, stream);
+}
+
+int wq_scale_activations(const uint16_t* x_f16, int64_t M, int64_t K, const float* alpha, uint16_t* x_out_f16,
+                         void* stream) {
+  if (!x_f16 || !alpha || !x_out_f16) return WQ_EINVAL;
+  if (M <= 0 || K <= 0 || M > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (K % 8 != 0) return WQ_EUNSUPPORTED;
+  if (!aligned(x_f16, 16) || !aligned(alpha, 16) || !aligned(x_out_f16, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_scale_activations(x_f16, M, K, alpha, x_out_f16, static_cast<hipStream_t>(stream)));
+}
+
+int wq_channel_absmean(const uint16_t* x_f16, int64_t M, int64_t K, float* out, void* stream) {
+  if (!x_f16 || !out) return WQ_EINVAL;
+  if (M <= 0 || K <= 0 || M > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (!aligned(x_f16, 2) || !aligned(out, 4)) return WQ_EALIGN;
+  return hip_status(wq::launch_channel_absmean(x_f16, M, K, out, static_cast<hipStream_t>(stream)));
 }
 
 int wq_quantize_groups(const void* W, int w_dtype, int64_t N, int64_t K, int group, uint8_t* q_codes,

@@ -7,9 +7,18 @@
 namespace wq {
 
 // sym: the symmetric 4-bit scheme (codes q + 8, zero-point 8) instead of the
-// asymmetric one.
-hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, uint8_t* q_codes,
-                           uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream);
+// asymmetric one.  alpha (fp32 [K] or NULL): per-input-channel factors applied
+// to the weights before quantizing (the AWQ fold).
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, const float* alpha,
+                           uint8_t* q_codes, uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked,
+                           hipStream_t stream);
+
+// The activation side of the AWQ fold, x' = fp16(x / alpha[k]) (K a multiple
+// of 8), and the per-channel mean |x| (fp32, row order) that finds salient
+// channels.
+hipError_t launch_scale_activations(const uint16_t* x, int64_t M, int64_t K, const float* alpha, uint16_t* out,
+                                    hipStream_t stream);
+hipError_t launch_channel_absmean(const uint16_t* x, int64_t M, int64_t K, float* out, hipStream_t stream);
 
 hipError_t launch_pack(const uint8_t* q_codes, const uint8_t* z_codes, int64_t N, int64_t K, int group,
                        uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream);

@@ -167,9 +167,11 @@ __device__ __forceinline__ uint32_t encode_w8(float w, const GroupParams& p) {
 // Nibble position of column e (0..7) inside a packed word.
 __device__ __forceinline__ int nibble_pos(int e) { return 4 * (e & 1) + (e >> 1); }
 
-template <int DT, int G, bool SYM>
+// SCALED: each weight is first multiplied by its input channel's factor
+// alpha[k] (the AWQ fold, one fp32 multiplication).
+template <int DT, int G, bool SYM, bool SCALED>
 __global__ __launch_bounds__(256) void quantize_kernel(
-    const void* __restrict__ W, int64_t N, int64_t K, int64_t NBLK, int64_t KT,
+    const void* __restrict__ W, int64_t N, int64_t K, int64_t NBLK, int64_t KT, const float* __restrict__ alpha,
     uint8_t* __restrict__ q_codes, uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_codes,
     uint32_t* __restrict__ qpacked, uint8_t* __restrict__ zpacked) {
   const int lane = threadIdx.x & 63;
@@ -196,6 +198,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       jok[j] = row_ok && (kt * 128 + 32 * j < K);
       if (jok[j]) {
         load8<DT>(W, n * K + k0, w[j]);
+        if constexpr (SCALED) {
+          const float4 a0 = *reinterpret_cast<const float4*>(alpha + k0);
+          const float4 a1 = *reinterpret_cast<const float4*>(alpha + k0 + 4);
+          const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[j][e] = w[j][e] * a[e];
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[j][e] = 0.0f;
@@ -634,22 +643,61 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restri
   }
 }
 
+// ---- the activation side of the AWQ fold, and its channel statistic --------
+
+// x'[m][k] = fp16(fl32(x[m][k] / alpha[k])); eight values per thread.
+__global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                                const float* __restrict__ alpha,
+                                                                uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= M * K) return;
+  const int64_t k = i % K;  // K is a multiple of 8: the eight values share a row
+  const uint4 v = *reinterpret_cast<const uint4*>(x + i);
+  const float4 a0 = *reinterpret_cast<const float4*>(alpha + k), a1 = *reinterpret_cast<const float4*>(alpha + k + 4);
+  const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float lo = f16_bits_to_f32((uint16_t)(in[p] & 0xffffu)) / a[2 * p];
+    const float hi = f16_bits_to_f32((uint16_t)(in[p] >> 16)) / a[2 * p + 1];
+    o[p] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + i) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// out[k] = (sum over m in row order of |x[m][k]|, in fp32) / M; one thread per
+// channel, consecutive threads on consecutive channels.
+__global__ __launch_bounds__(256) void channel_absmean_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                              float* __restrict__ out) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  float acc = 0.0f;
+  for (int64_t m = 0; m < M; ++m) acc = acc + fabsf(f16_bits_to_f32(x[m * K + k]));
+  out[k] = acc / (float)M;
+}
+
 inline int64_t blocks_for(int64_t waves) { return (waves + kWavesPerBlock - 1) / kWavesPerBlock; }
 
 }  // namespace
 
-hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, uint8_t* q_codes,
-                           uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked, hipStream_t stream) {
+hipError_t launch_quantize(const void* W, int dtype, int64_t N, int64_t K, int group, int sym, const float* alpha,
+                           uint8_t* q_codes, uint16_t* s, uint8_t* z_codes, uint32_t* qpacked, uint8_t* zpacked,
+                           hipStream_t stream) {
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128, ST = (KT + 1) / 2;
   dim3 grid((unsigned)blocks_for(NBLK * ST)), block(256);
-#define WQ_Q(DT, G, S) \
-  quantize_kernel<DT, G, S><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, s, z_codes, qpacked, zpacked)
-#define WQ_QS(DT, G) \
-  do {                  \
-    if (sym)            \
-      WQ_Q(DT, G, true);  \
-    else                \
-      WQ_Q(DT, G, false); \
+#define WQ_Q(DT, G, S, A)                                                                                \
+  quantize_kernel<DT, G, S, A><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, alpha, q_codes, s, z_codes, qpacked, \
+                                                           zpacked)
+#define WQ_QS(DT, G)                              \
+  do {                                            \
+    if (sym) {                                    \
+      if (alpha) WQ_Q(DT, G, true, true);         \
+      else WQ_Q(DT, G, true, false);              \
+    } else {                                      \
+      if (alpha) WQ_Q(DT, G, false, true);        \
+      else WQ_Q(DT, G, false, false);             \
+    }                                             \
   } while (0)
   if (group == 128) {
     if (dtype == 0) WQ_QS(0, 128); else if (dtype == 1) WQ_QS(1, 128); else WQ_QS(2, 128);
@@ -737,6 +785,18 @@ hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint
   if (out_dtype == 0) kv_dequant_kernel<0><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
   else if (out_dtype == 1) kv_dequant_kernel<1><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
   else kv_dequant_kernel<2><<<grid, block, 0, stream>>>(codes, s, zp, T, hd, slot, S, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_activations(const uint16_t* x, int64_t M, int64_t K, const float* alpha, uint16_t* out,
+                                    hipStream_t stream) {
+  const int64_t threads = M * K / 8;
+  scale_activations_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(x, M, K, alpha, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_channel_absmean(const uint16_t* x, int64_t M, int64_t K, float* out, hipStream_t stream) {
+  channel_absmean_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream>>>(x, M, K, out);
   return hipGetLastError();
 }
 
