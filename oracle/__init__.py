@@ -78,6 +78,10 @@ def _load():
         "orc_gemm_rows_w8_f64": (I, [I64, I64, I64, I, P, P, P, I64, I64, P]),
         "orc_kv_quantize": (I, [P, I, I64, I64, P, I64, P, P, P]),
         "orc_quantize_groups_scaled": (I, [P, I, I64, I64, I, I, P, P, P, P]),
+        "orc_quantize_mxfp4": (I, [P, I, I64, I64, P, P]),
+        "orc_dequant_mxfp4": (I, [P, P, I64, I64, I, P]),
+        "orc_pack_device_mxfp4": (I, [P, I64, I64, P]),
+        "orc_gemm_rows_mxfp4_f64": (I, [I64, I64, I64, P, P, P, I64, I64, P]),
         "orc_scale_activations": (I, [P, I64, I64, P, P]),
         "orc_channel_absmean": (I, [P, I64, I64, P]),
         "orc_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P]),
@@ -308,6 +312,55 @@ def gemm_rows_w8_f64(x_f16_bits, q, s, group: int, n0: int, nrows: int) -> np.nd
     y = np.empty((M, nrows), np.float64)
     _check(_load().orc_gemm_rows_w8_f64(M, N, K, group, _ptr(x), _ptr(q), _ptr(s), n0, nrows, _ptr(y)),
            "orc_gemm_rows_w8_f64")
+    return y
+
+
+# --- MXFP4 (E2M1 elements, blocks of 32, E8M0 scale) ---------------------------
+
+def quantize_mxfp4(W: np.ndarray, dtype: int | None = None):
+    """MXFP4 quantization of W[N][K] (K a multiple of 32): per block of 32
+    along K an E8M0 scale 2^(floor(log2 max|w|) - 2) and E2M1 codes (nearest,
+    ties to even, saturating at 6; sign in bit 3).  Returns (q uint8 [N][K],
+    e8 uint8 [N][K/32])."""
+    W = np.ascontiguousarray(W)
+    if dtype is None:
+        if W.dtype == np.float32:
+            dtype = F32
+        else:
+            raise ValueError("give dtype for non-float32 input")
+    N, K = W.shape
+    q = np.empty((N, K), np.uint8)
+    e8 = np.empty((N, K // 32), np.uint8)
+    _check(_load().orc_quantize_mxfp4(_ptr(W), dtype, N, K, _ptr(q), _ptr(e8)), "orc_quantize_mxfp4")
+    return q, e8
+
+
+def dequant_mxfp4(q: np.ndarray, e8: np.ndarray, out_dtype: int = F32) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    e8 = np.ascontiguousarray(e8, np.uint8)
+    N, K = q.shape
+    out = np.empty((N, K), np.float32 if out_dtype == F32 else np.uint16)
+    _check(_load().orc_dequant_mxfp4(_ptr(q), _ptr(e8), N, K, out_dtype, _ptr(out)), "orc_dequant_mxfp4")
+    return out
+
+
+def pack_device_mxfp4(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    N, K = q.shape
+    out = np.empty(device_bytes(N, K), np.uint8)
+    _check(_load().orc_pack_device_mxfp4(_ptr(q), N, K, _ptr(out)), "orc_pack_device_mxfp4")
+    return out
+
+
+def gemm_rows_mxfp4_f64(x_f16_bits, q, e8, n0: int, nrows: int) -> np.ndarray:
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    q = np.ascontiguousarray(q, np.uint8)
+    e8 = np.ascontiguousarray(e8, np.uint8)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, nrows), np.float64)
+    _check(_load().orc_gemm_rows_mxfp4_f64(M, N, K, _ptr(x), _ptr(q), _ptr(e8), n0, nrows, _ptr(y)),
+           "orc_gemm_rows_mxfp4_f64")
     return y
 
 

@@ -24,6 +24,11 @@
  *        factor before quantizing, its activations divided by it).
  *   [C]  also section "The methods compared" (the activation-aware scaling of
  *        salient channels and its toy example in symmetric int4).
+ *   [Q]  also section "Microscaling: NVFP4 and MXFP4" (4-bit floating-point
+ *        elements with one 8-bit scale per small block of 16 or 32), with the
+ *        format of the microscaling paper that section cites: E2M1 elements
+ *        (sign, 2 exponent bits with bias 1, 1 mantissa bit), blocks of 32,
+ *        an E8M0 power-of-two scale.
  *
  * Where the pages leave a step open, the readings below are used (each is also
  * listed in the design notes):
@@ -600,6 +605,148 @@ int orc_channel_absmean(const uint16_t* x_f16, int64_t M, int64_t K, float* out)
         float acc = 0.0f;
         for (int64_t m = 0; m < M; ++m) acc = acc + fabsf(orc_f16_to_f32(x_f16[m * K + k]));
         out[k] = acc / (float)M;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* MXFP4  ([Q] "Microscaling: NVFP4 and MXFP4")                              */
+/* ------------------------------------------------------------------------- */
+
+/* The eight E2M1 magnitudes, code m = 0..7 (exponent field m >> 1, mantissa
+ * bit m & 1): exponent field 0 is subnormal, 0.5 * mantissa; otherwise
+ * 2^(e - 1) * (1 + mantissa / 2). */
+static double e2m1_magnitude(int m)
+{
+    int e = m >> 1, f = m & 1;
+    return e == 0 ? 0.5 * f : ldexp(1.0 + 0.5 * f, e - 1);
+}
+
+/* Nearest E2M1 magnitude code to v >= 0 (ties to the code with an even
+ * mantissa bit; anything past 6 gives 6, the largest: the saturating
+ * conversion). */
+static int e2m1_encode_magnitude(double v)
+{
+    int best = 0;
+    double best_d = fabs(v - e2m1_magnitude(0));
+    for (int m = 1; m < 8; ++m) {
+        double d = fabs(v - e2m1_magnitude(m));
+        if (d < best_d || (d == best_d && (m & 1) == 0 && (best & 1) == 1)) {
+            best = m;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+/* One block of 32 values -> E8M0 scale byte and 32 E2M1 codes (sign in bit 3).
+ * The shared exponent is floor(log2(max|v|)) - 2 (2 = the largest E2M1
+ * exponent, so the block maximum lands in [4, 8) before rounding), clamped to
+ * the E8M0 range [-127, 127]; an all-zero block stores exponent -127 and codes
+ * 0.  A value below zero keeps its sign bit even when it rounds to zero. */
+static int quantize_block_mxfp4(const float* v, uint8_t* q, uint8_t* e8)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        if (!isfinite(v[i])) return ORC_ERANGE;
+        if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+    }
+    int shared = -127;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);       /* amax = f * 2^ex, f in [0.5, 1) */
+        shared = ex - 1 - 2;
+        if (shared < -127) shared = -127;
+        if (shared > 127) shared = 127;
+    }
+    *e8 = (uint8_t)(shared + 127);
+    for (int i = 0; i < 32; ++i) {
+        double x = ldexp((double)v[i], -shared);  /* exact */
+        int m = e2m1_encode_magnitude(fabs(x));
+        q[i] = (uint8_t)(((v[i] < 0.0f) ? 8 : 0) | m);
+    }
+    return 0;
+}
+
+int orc_quantize_mxfp4(const void* W, int dtype, int64_t N, int64_t K, uint8_t* q, uint8_t* e8)
+{
+    if (!W || !q || !e8 || N <= 0 || K <= 0 || K % 32) return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
+    int64_t G = K / 32;
+    int status = 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        float buf[32];
+        for (int64_t j = 0; j < G; ++j) {
+            for (int i = 0; i < 32; ++i) buf[i] = load_w(W, dtype, n * K + j * 32 + i);
+            int st = quantize_block_mxfp4(buf, q + n * K + j * 32, e8 + n * G + j);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+    }
+    return status;
+}
+
+/* w_hat = E2M1(q) * 2^(e8 - 127), exact in fp32 (fp32 subnormals cover the
+ * smallest block exponent); fp16 / bf16 outputs are one rounding of it. */
+int orc_dequant_mxfp4(const uint8_t* q, const uint8_t* e8, int64_t N, int64_t K, int out_dtype, void* out)
+{
+    if (!q || !e8 || !out || N <= 0 || K <= 0 || K % 32) return ORC_EINVAL;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EINVAL;
+    int64_t G = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int c = q[n * K + k] & 15;
+            double mag = e2m1_magnitude(c & 7);
+            double v = ldexp((c & 8) ? -mag : mag, (int)e8[n * G + k / 32] - 127);
+            float f = (float)v;
+            if (out_dtype == ORC_F32) ((float*)out)[n * K + k] = f;
+            else if (out_dtype == ORC_F16) ((uint16_t*)out)[n * K + k] = orc_f32_to_f16(f);
+            else ((uint16_t*)out)[n * K + k] = orc_f32_to_bf16(f);
+        }
+    return 0;
+}
+
+/* Device layout of MXFP4 codes: the 1024-byte tiles of the INT4 layout
+ * (16 rows x 128 columns, lane l = r + 16c owns 16 bytes, word j = columns
+ * 32j + 8c + e), with column e in nibble e of its word (two neighbouring
+ * columns per byte, the even one in the low nibble). */
+int orc_pack_device_mxfp4(const uint8_t* q, int64_t N, int64_t K, uint8_t* out)
+{
+    if (!q || !out || N <= 0 || K <= 0) return ORC_EINVAL;
+    int64_t KT = (K + 127) / 128;
+    memset(out, 0, (size_t)orc_device_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, r = n % 16, kt = k / 128, kk = k % 128;
+            int64_t j = kk / 32, c = (kk % 32) / 8, e = kk % 8;
+            int64_t byte = (nb * KT + kt) * 1024 + (r + 16 * c) * 16 + j * 4 + e / 2;
+            uint8_t v = q[n * K + k] & 15;
+            out[byte] = (uint8_t)((e % 2) ? (out[byte] & 0x0f) | (v << 4) : (out[byte] & 0xf0) | v);
+        }
+    return 0;
+}
+
+/* Rows [n0, n0 + nrows) of y = x * What^T for MXFP4 weights, in fp64. */
+int orc_gemm_rows_mxfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint8_t* q,
+                            const uint8_t* e8, int64_t n0, int64_t nrows, double* y_rows)
+{
+    if (!x_f16 || !q || !e8 || !y_rows || M <= 0 || N <= 0 || K <= 0 || K % 32) return ORC_EINVAL;
+    if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
+    int64_t G = K / 32;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = n0 + i;
+        float* wr = (float*)malloc(sizeof(float) * (size_t)K);
+        orc_dequant_mxfp4(q + n * K, e8 + n * G, 1, K, ORC_F32, wr);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            y_rows[m * nrows + i] = acc;
+        }
+        free(wr);
     }
     return 0;
 }

@@ -590,6 +590,115 @@ def test_awq_activation_side_and_statistic(orc):
 
 
 # --------------------------------------------------------------------------
+# MXFP4 (quantization post, "Microscaling: NVFP4 and MXFP4"; element and scale
+# formats from the microscaling paper it cites)
+# --------------------------------------------------------------------------
+
+def test_mxfp4_storage_matches_printed_bits():
+    import oracle as orc
+    # the methods page prints NVFP4 as 4.5 bits (one 8-bit scale per 16 values)
+    # and 70B x 4.5 / 8 = 39.4 GB; MXFP4 (one 8-bit scale per 32) is 4.25 bits
+    assert orc.bits_per_weight(4, 16, 8, 0) == 4.5
+    assert round(orc.storage_bytes(70_000_000_000, 4, 16, 8, 0) / 1e9, 1) == 39.4
+    assert orc.bits_per_weight(4, 32, 8, 0) == 4.25
+
+
+def test_mxfp4_grid_and_decoding():
+    # 16 codes: sign bit 3, then a 4-point exponent range with one mantissa bit
+    # and a subnormal step; the largest magnitude is 6, the smallest nonzero 0.5
+    import oracle as orc
+    q = np.tile(np.arange(16, dtype=np.uint8), 2).reshape(1, 32)
+    v = orc.dequant_mxfp4(q, np.array([[127]], np.uint8))[0, :16].astype(np.float64)
+    mags = v[:8]
+    assert mags[0] == 0 and np.all(np.diff(mags) > 0)
+    assert mags.max() == 6.0 and mags[1] == 0.5
+    assert np.array_equal(v[8:], -mags)
+    # one mantissa bit: neighbouring magnitudes within a binade differ by half the binade's base
+    assert np.array_equal(mags[2:] / np.repeat([1.0, 2.0, 4.0], 2), np.tile([1.0, 1.5], 3))
+    # the scale byte is a power of two 2^(e8 - 127), applied exactly, down to
+    # e8 = 0 (fp32 subnormals) and up to 252, the largest a finite fp32 block gives
+    for e8 in (0, 1, 100, 127, 140, 252):
+        w = orc.dequant_mxfp4(q, np.array([[e8]], np.uint8))[0, :16].astype(np.float64)
+        assert np.array_equal(w, v * 2.0 ** (e8 - 127))
+
+
+def test_mxfp4_encoding_is_nearest_with_ties_to_even():
+    import oracle as orc
+    grid = orc.dequant_mxfp4(np.tile(np.arange(8, dtype=np.uint8), 4).reshape(1, 32),
+                             np.array([[127]], np.uint8))[0, :8].astype(np.float64)
+    rng = np.random.default_rng(60)
+    vals = np.concatenate([rng.uniform(0, 8, 4000), (grid[:-1] + grid[1:]) / 2, grid, [7.0, 7.5, 6.5]])
+    vals = vals.astype(np.float32)
+    # blocks of 31 test values behind a leading 4.0, which pins each block's
+    # scale to 1 (its maximum lies in [4, 8))
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.float32)]).reshape(-1, 31)
+    row = np.concatenate([np.full((vals.shape[0], 1), 4.0, np.float32), vals], axis=1).reshape(1, -1)
+    q, e8 = orc.quantize_mxfp4(row)
+    blocks_max = np.abs(row.reshape(-1, 32)).max(axis=1)
+    assert np.all(e8 == 127 + np.floor(np.log2(blocks_max)).astype(int) - 2)
+    got = grid[q[0] & 7]
+    for v, g in zip(row[0].astype(np.float64), got):
+        d = np.abs(grid - v)
+        best = np.flatnonzero(d == d.min())
+        want = grid[best[0]] if best.size == 1 else grid[[b for b in best if b % 2 == 0][0]]
+        assert g == want, (v, g, want)
+    # negative values mirror, keeping the sign bit (also when they round to zero)
+    qn, e8n = orc.quantize_mxfp4(-row)
+    assert np.array_equal(e8n, e8) and np.array_equal(qn & 7, q & 7) and np.all(qn[row != 0] & 8)
+
+
+def test_mxfp4_scale_commutes_with_powers_of_two_and_grid_is_lossless():
+    import oracle as orc
+    rng = np.random.default_rng(61)
+    W = (rng.standard_normal((6, 256)) * 0.05).astype(np.float32)
+    q, e8 = orc.quantize_mxfp4(W)
+    for k in (-5, 3):
+        qk, e8k = orc.quantize_mxfp4((W * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(qk, q) and np.array_equal(e8k.astype(int), e8.astype(int) + k)
+    # every block's largest code is 4 or 6 times the scale (the maximum lands in [4, 8))
+    mags = orc.dequant_mxfp4(q, np.full_like(e8, 127))
+    top = np.abs(mags.reshape(6, -1, 32)).max(axis=2)
+    assert np.all((top == 4) | (top == 6))
+    # values on the grid times a block's power of two, with a 4 or 6 in each block, decode exactly
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    c = rng.integers(0, 8, (6, 256))
+    c[:, ::32] = rng.choice([6, 7], (6, 8))
+    sign = np.where(rng.integers(0, 2, (6, 256)) == 1, -1.0, 1.0)
+    e = rng.integers(-20, 5, (6, 8))
+    Wg = (sign * grid[c] * np.repeat(2.0 ** e, 32, axis=1)).astype(np.float32)
+    qg, e8g = orc.quantize_mxfp4(Wg)
+    assert np.array_equal(orc.dequant_mxfp4(qg, e8g), Wg)
+    assert np.array_equal(e8g.astype(int), e + 127)
+    # all-zero block: scale byte 0, codes 0
+    qz, ez = orc.quantize_mxfp4(np.zeros((1, 32), np.float32))
+    assert ez[0, 0] == 0 and np.all(qz == 0)
+
+
+def test_mxfp4_error_bound_and_device_layout():
+    import oracle as orc
+    rng = np.random.default_rng(62)
+    W = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    W[:, 9] *= 20
+    q, e8 = orc.quantize_mxfp4(W)
+    X = np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=1)
+    err = np.abs(orc.dequant_mxfp4(q, e8).astype(np.float64) - W)
+    v = np.abs(W) / X
+    half_step = np.where(v < 2, 0.25, np.where(v < 4, 0.5, np.where(v <= 6, 1.0, np.inf)))
+    assert np.all(err <= half_step * X)
+    assert np.all(err[v > 6] <= (v[v > 6] - 6) * X[v > 6])  # saturation
+    # device layout: column e of a word in nibble e; the tile geometry of the INT4 layout
+    qq = np.zeros((16, 128), np.uint8)
+    qq[0, :8] = np.arange(1, 9)
+    p = orc.pack_device_mxfp4(qq)
+    word = int(p[:4].view(np.uint32)[0])
+    assert [(word >> (4 * i)) & 15 for i in range(8)] == list(range(1, 9))
+    qq = np.zeros((16, 128), np.uint8)
+    qq[3, 40:48] = 9
+    p = orc.pack_device_mxfp4(qq)
+    assert np.all(p[19 * 16 + 4: 19 * 16 + 8] == 0x99) and p.sum() == 4 * 0x99
+
+
+# --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
 
