@@ -207,6 +207,48 @@ def bench_kv(steps, warmup):
     return out
 
 
+def bench_mxfp4(steps, warmup):
+    """MXFP4 weights (E2M1, blocks of 32, E8M0 scales) on the decode and M=128
+    workloads, timed like the int8 leg; plus each format's weight error on the
+    decode layer (relative Frobenius norm of W_hat - W)."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    out = {}
+    for name, n_steps, n_warm in (("decode_gemv", steps, warmup // 2), ("batched_gemm", max(50, steps // 2),
+                                                                        max(300, warmup // 30))):
+        wl = workloads.WORKLOADS[name]
+        Wd = torch.from_numpy(wl.weights().view(np.int16)).cuda().view(torch.bfloat16)
+        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        qw = wq.wq_quantize_mxfp4(Wd)["qw"]
+        if name == "decode_gemv":
+            ref = Wd.float()
+            nrm = float(ref.norm())
+            err = {"mxfp4_g32": float((wq.wq_dequant_mxfp4(qw) - ref).norm()) / nrm}
+            for g in (32, 128):
+                err[f"int4_asym_g{g}"] = float((wq.wq_dequant(wq.wq_quantize_groups(Wd, g)["qw"]) - ref).norm()) / nrm
+            out["weight_relative_error"] = {k: round(v, 5) for k, v in err.items()}
+        del Wd
+        nbytes = wl.N * wl.K // 2 + wl.N * wl.K // 32 + 2 * wl.M * wl.K + 2 * wl.M * wl.N
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        qws = [qw] + [wq.QuantizedWeightMX(qw.qpacked.clone(), qw.e8.clone(), qw.N, qw.K) for _ in range(copies - 1)]
+        y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+        n = wq.wq_gemm_mxfp4_workspace_bytes(wl.M, wl.N, wl.K)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+        t = _time_calls(lambda i: wq.wq_gemm_mxfp4(xd, qws[i % copies], y=y, workspace=ws), n_steps, n_warm)
+        rec = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "kernel": wq.wq_gemm_mxfp4_plan(wl.M, wl.N, wl.K),
+               "us_per_launch_one_python_call_each": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
+               "gbs": round(nbytes / t / 1e9, 2), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+               "weight_copies_rotated": copies}
+        if wl.M >= 64:
+            tf = wl.flops() / t / 1e12
+            rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
+        out[name] = rec
+        log(f"[bench] MXFP4 {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.1f} GB/s")
+    return out
+
+
 def bench_awq():
     """AWQ-style fold on the decode layer (8192 x 8192, g=128): salient channels
     = the 1 % with the largest mean |x| over 64 calibration rows (the library's
@@ -401,6 +443,7 @@ def main():
         line["w8a16"] = bench_w8(args.steps, args.warmup)
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
         line["awq_fold"] = bench_awq()
+        line["mxfp4"] = bench_mxfp4(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -295,6 +295,62 @@ int wq_gemm_w8a16_ex(int64_t M, int64_t N, int64_t K, int group,
 /* As wq_gemm_plan, for wq_gemm_w8a16_ex. */
 int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len);
 
+/* ---- MXFP4 weights ----------------------------------------------------------
+ * "Quantization for LLM inference", section "Microscaling: NVFP4 and MXFP4":
+ * 4-bit floating-point weights with one 8-bit scale per small block, in the
+ * format of the microscaling paper that section cites: E2M1 elements (sign,
+ * two exponent bits with bias 1, one mantissa bit: magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6), blocks of 32 consecutive weights along K, an E8M0 scale byte e8
+ * meaning 2^(e8 - 127).  Read as:
+ *   e8 = clamp(floor(log2 max|w|) - 2 + 127, 0, 254), 0 for an all-zero block
+ *   (so the block maximum lands in [4, 8) before rounding);
+ *   code = nearest E2M1 value of w / 2^(e8 - 127), ties to the even mantissa
+ *   bit, saturating at 6; sign in bit 3 (kept when a negative value rounds to 0);
+ *   What = E2M1(code) * 2^(e8 - 127).
+ * 4.25 bits per weight.  Layouts: q_codes [N][K] uint8 (0..15); e8 [N][K/32];
+ * qpacked the INT4 tile geometry (wq_layout_bytes) with column e of a word in
+ * nibble e (two neighbouring columns per byte, the even one low).  K a
+ * multiple of 32 (WQ_EUNSUPPORTED otherwise).  Same conventions as above. */
+
+/* Byte sizes of qpacked and e8 for [N][K].  Host-only. */
+int wq_layout_bytes_mxfp4(int64_t N, int64_t K, size_t* qpacked_bytes, size_t* e8_bytes);
+
+/* MXFP4 quantization of W [N][K] (WQ_F32, WQ_BF16 or WQ_F16, 16-byte aligned;
+ * finite).  e8 [N][K/32] required; q_codes (8-byte aligned) and qpacked
+ * (16-byte aligned) may each be NULL.  Deterministic. */
+int wq_quantize_mxfp4(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* e8,
+                      uint32_t* qpacked, void* stream);
+
+/* Codes [N][K] (low 4 bits used) -> qpacked (padding written as 0). */
+int wq_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint32_t* qpacked, void* stream);
+
+/* What = E2M1(code) * 2^(e8 - 127) into W_hat [N][K] (WQ_F32 exact; WQ_F16 /
+ * WQ_BF16 one round-to-nearest-even of it); W_hat 16-byte aligned. */
+int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype,
+                     void* W_hat, void* stream);
+
+/* Workspace bytes for wq_gemm_mxfp4 / _ex (same rules as
+ * wq_gemm_workspace_bytes at group 32).  Host-only. */
+size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV (M < 64)
+ * sums exact E2M1 values times x per block in fp32 and applies the block's
+ * power of two in fp32 (exact for every e8); the MFMA GEMM (M >= 64) takes fp16
+ * operands fp16(E2M1 * 2^(e8 - 127)), exact while the block exponent lies in
+ * [-23, 13] (outside, the operand rounds to fp16's range).  Arguments,
+ * workspace contract and errors as wq_gemm_w4a16 with e8 for the scales and no
+ * zero-points. */
+int wq_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
+                  const uint8_t* e8, uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As wq_gemm_mxfp4, with the kernel family chosen by `path` (wq_path). */
+int wq_gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint8_t* e8, uint16_t* y_f16, void* workspace, size_t workspace_bytes, int path,
+                     void* stream);
+
+/* As wq_gemm_plan, for wq_gemm_mxfp4_ex. */
+int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, size_t buf_len);
+
 /* ---- INT4 KV cache in blocks of 128 -----------------------------------------
  * "Quantization for LLM inference", section "KV cache quantization": the K/V
  * cache stored as int4 in blocks of 128 values (half a byte per value plus

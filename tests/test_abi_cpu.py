@@ -245,3 +245,33 @@ def test_awq_entry_points_checked_on_host():
     assert call(h, None, 4, 128, A, None) == wq.WQ_EINVAL
     assert call(h, A, 4, -1, A, None) == wq.WQ_EINVAL
     assert call(h, A, 4, 128, B, None) == wq.WQ_EALIGN
+
+
+def test_mxfp4_entry_points_checked_on_host():
+    q, e = wq.wq_layout_bytes_mxfp4(8192, 8192)
+    assert q == 8192 * 8192 // 2 and e == 8192 * 256
+    with pytest.raises(wq.WQError) as err:
+        wq.wq_layout_bytes_mxfp4(16, 100)
+    assert err.value.status == wq.WQ_EUNSUPPORTED
+    f = "wq_quantize_mxfp4"
+    assert call(f, None, 1, 16, 128, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 128, None, None, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 4, 16, 128, None, A, A, None) == wq.WQ_EINVAL
+    assert call(f, A, 1, 16, 100, None, A, A, None) == wq.WQ_EUNSUPPORTED
+    assert call(f, B, 1, 16, 128, None, A, A, None) == wq.WQ_EALIGN
+    assert call("wq_pack_mxfp4", A, 16, 96 + 4, A, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_pack_mxfp4", A, 16, 128, B, None) == wq.WQ_EALIGN
+    assert call("wq_dequant_mxfp4", A, A, 16, 128, 3, A, None) == wq.WQ_EINVAL
+    assert call("wq_dequant_mxfp4", A, A, 16, 128, 0, B, None) == wq.WQ_EALIGN
+    g = "wq_gemm_mxfp4_ex"
+    assert call(g, 1, 16, 128, A, A, None, A, None, 0, 0, None) == wq.WQ_EINVAL  # e8 missing
+    assert call(g, 0, 16, 128, A, A, A, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(g, 1, 16, 100, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
+    assert call(g, 1, 16, 128, B, A, A, A, None, 0, 0, None) == wq.WQ_EALIGN
+    assert call(g, 1, 16, 128, A, A, A, A, None, 0, 5, None) == wq.WQ_EINVAL
+    need = wq.wq_gemm_mxfp4_workspace_bytes(1, 1024, 8192)
+    assert need > 0 and call(g, 1, 1024, 8192, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
+    d = wq.wq_gemm_mxfp4_plan(1, 8192, 8192)
+    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=32, MXFP4>") and "grid=(512,1,1)" in d, d
+    d = wq.wq_gemm_mxfp4_plan(128, 28672, 8192)
+    assert d.startswith("gemm_kernel<MB=8, NPW=2, G=32, MXFP4>") and "grid=(224,1,1)" in d, d

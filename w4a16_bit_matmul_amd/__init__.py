@@ -31,6 +31,8 @@ EXPORTED = (
     "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
     "wq_kv_layout_bytes", "wq_kv_quantize", "wq_kv_dequant",
     "wq_quantize_groups_scaled", "wq_scale_activations", "wq_channel_absmean",
+    "wq_layout_bytes_mxfp4", "wq_quantize_mxfp4", "wq_pack_mxfp4", "wq_dequant_mxfp4",
+    "wq_gemm_mxfp4_workspace_bytes", "wq_gemm_mxfp4", "wq_gemm_mxfp4_ex", "wq_gemm_mxfp4_plan",
 )
 
 _lib = None
@@ -79,6 +81,14 @@ def lib() -> ctypes.CDLL:
         "wq_quantize_groups_scaled": (I, [P, I, I64, I64, I, I, P, P, P, P, P, P, P]),
         "wq_scale_activations": (I, [P, I64, I64, P, P, P]),
         "wq_channel_absmean": (I, [P, I64, I64, P, P]),
+        "wq_layout_bytes_mxfp4": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "wq_quantize_mxfp4": (I, [P, I, I64, I64, P, P, P, P]),
+        "wq_pack_mxfp4": (I, [P, I64, I64, P, P]),
+        "wq_dequant_mxfp4": (I, [P, P, I64, I64, I, P, P]),
+        "wq_gemm_mxfp4_workspace_bytes": (SZ, [I64, I64, I64]),
+        "wq_gemm_mxfp4": (I, [I64, I64, I64, P, P, P, P, P, SZ, P]),
+        "wq_gemm_mxfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, SZ, I, P]),
+        "wq_gemm_mxfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -396,3 +406,80 @@ def wq_channel_absmean(x: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty(K, dtype=torch.float32, device=x.device)
     _check(lib().wq_channel_absmean(_ptr(x), M, K, _ptr(out), _stream(stream)), "wq_channel_absmean")
     return out
+
+
+# ---- MXFP4 weights (E2M1 codes, blocks of 32, E8M0 scales) ---------------------
+
+@dataclass
+class QuantizedWeightMX:
+    """Device buffers of one MXFP4-quantized [N][K] weight matrix."""
+    qpacked: torch.Tensor  # uint8, 1 KB tiles (natural nibble order)
+    e8: torch.Tensor       # uint8 [N][K/32]
+    N: int
+    K: int
+
+
+def wq_layout_bytes_mxfp4(N: int, K: int):
+    q, e = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wq_layout_bytes_mxfp4(N, K, ctypes.byref(q), ctypes.byref(e)), "wq_layout_bytes_mxfp4")
+    return q.value, e.value
+
+
+def alloc_quantized_mxfp4(N: int, K: int, device="cuda") -> QuantizedWeightMX:
+    qb, _ = wq_layout_bytes_mxfp4(N, K)
+    return QuantizedWeightMX(torch.empty(qb, dtype=torch.uint8, device=device),
+                             torch.empty((N, K // 32), dtype=torch.uint8, device=device), N, K)
+
+
+def wq_quantize_mxfp4(W: torch.Tensor, *, codes: bool = False, stream=None):
+    """MXFP4 quantization of W[N][K] (float32, bfloat16 or float16, on the GPU).
+    Returns a dict with ``qw`` (QuantizedWeightMX) and, if asked, ``q_codes``
+    (uint8 [N][K])."""
+    N, K = W.shape
+    qw = alloc_quantized_mxfp4(N, K, W.device)
+    q_codes = torch.empty((N, K), dtype=torch.uint8, device=W.device) if codes else None
+    _check(lib().wq_quantize_mxfp4(_ptr(W), _DT.get(W.dtype, -1), N, K, _ptr(q_codes), _ptr(qw.e8), _ptr(qw.qpacked),
+                                   _stream(stream)), "wq_quantize_mxfp4")
+    return {"qw": qw, "q_codes": q_codes}
+
+
+def wq_pack_mxfp4(q_codes: torch.Tensor, stream=None) -> QuantizedWeightMX:
+    """Pack codes [N][K] into the tile layout (the returned weight's ``e8`` is
+    left uninitialised)."""
+    N, K = q_codes.shape
+    qw = alloc_quantized_mxfp4(N, K, q_codes.device)
+    _check(lib().wq_pack_mxfp4(_ptr(q_codes), N, K, _ptr(qw.qpacked), _stream(stream)), "wq_pack_mxfp4")
+    return qw
+
+
+def wq_dequant_mxfp4(qw: QuantizedWeightMX, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty((qw.N, qw.K), dtype=out_dtype, device=qw.qpacked.device)
+    _check(lib().wq_dequant_mxfp4(_ptr(qw.qpacked), _ptr(qw.e8), qw.N, qw.K, _DT.get(out_dtype, -1), _ptr(out),
+                                  _stream(stream)), "wq_dequant_mxfp4")
+    return out
+
+
+def wq_gemm_mxfp4_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().wq_gemm_mxfp4_workspace_bytes(M, N, K))
+
+
+def wq_gemm_mxfp4_plan(M: int, N: int, K: int, path: int = WQ_PATH_AUTO) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().wq_gemm_mxfp4_plan(M, N, K, path, buf, len(buf)), "wq_gemm_mxfp4_plan")
+    return buf.value.decode()
+
+
+def wq_gemm_mxfp4(x: torch.Tensor, qw: QuantizedWeightMX, *, y: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y[M][N] = x[M][K] * What^T with MXFP4 weights, fp16 in and out."""
+    M, K = x.shape
+    assert K == qw.K, "x and the weight disagree on K"
+    if y is None:
+        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
+    need = wq_gemm_mxfp4_workspace_bytes(M, qw.N, qw.K)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    _check(lib().wq_gemm_mxfp4_ex(M, qw.N, qw.K, _ptr(x), _ptr(qw.qpacked), _ptr(qw.e8), _ptr(y), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(), path,
+                                  _stream(stream)), "wq_gemm_mxfp4")
+    return y

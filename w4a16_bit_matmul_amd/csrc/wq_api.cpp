@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/libwq.h"
+#include "wq_device.h"
 #include "wq_kernels.h"
 
 namespace {
@@ -139,12 +140,14 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
 
 namespace {
 
-// Argument checks of one product (host only); 0 or a wq_status.  bits 8 takes
-// no zero-points.
-int check_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x_f16, const void* qpacked,
+// Argument checks of one product (host only); 0 or a wq_status.  fmt: the code
+// format (wq_device.h); int8 takes no zero-points, MXFP4 takes its scale
+// bytes in zpacked and no fp16 scales.
+int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x_f16, const void* qpacked,
                const uint16_t* s_f16, const uint8_t* zpacked, const uint16_t* y_f16, const void* workspace,
                size_t workspace_bytes, int path, bool* mfma) {
-  if (!x_f16 || !qpacked || !s_f16 || (bits == 4 && !zpacked) || !y_f16) return WQ_EINVAL;
+  if (!x_f16 || !qpacked || (fmt != wq::kFmtMxfp4 && !s_f16) || (fmt != wq::kFmtInt8 && !zpacked) || !y_f16)
+    return WQ_EINVAL;
   if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
@@ -324,6 +327,85 @@ int wq_kv_dequant(const uint8_t* codes, const uint16_t* s_f16, const uint8_t* zp
   if (!aligned(codes, 8) || !aligned(s_f16, 2) || !aligned(out, 16) || (slot && !aligned(slot, 4))) return WQ_EALIGN;
   return hip_status(wq::launch_kv_dequant(codes, s_f16, zpacked, T, hd, slot, S, out_dtype, out,
                                           static_cast<hipStream_t>(stream)));
+}
+
+// ---- MXFP4 (E2M1 codes, blocks of 32, E8M0 scales) ---------------------------
+
+namespace {
+int check_mx_shape(int64_t N, int64_t K) { return check_shape(N, K, 32); }
+}  // namespace
+
+int wq_layout_bytes_mxfp4(int64_t N, int64_t K, size_t* qpacked_bytes, size_t* e8_bytes) {
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  const int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128;
+  if (qpacked_bytes) *qpacked_bytes = (size_t)(Np * Kp / 2);
+  if (e8_bytes) *e8_bytes = (size_t)(N * (K / 32));
+  return WQ_OK;
+}
+
+int wq_quantize_mxfp4(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* e8,
+                      uint32_t* qpacked, void* stream) {
+  if (!W || !e8) return WQ_EINVAL;
+  if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (!aligned(W, 16) || (qpacked && !aligned(qpacked, 16)) || (q_codes && !aligned(q_codes, 8))) return WQ_EALIGN;
+  return hip_status(wq::launch_quantize_mxfp4(W, w_dtype, N, K, q_codes, e8, reinterpret_cast<uint8_t*>(qpacked),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int wq_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint32_t* qpacked, void* stream) {
+  if (!q_codes || !qpacked) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (!aligned(q_codes, 8) || !aligned(qpacked, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_pack_mxfp4(q_codes, N, K, reinterpret_cast<uint8_t*>(qpacked),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype, void* W_hat,
+                     void* stream) {
+  if (!qpacked || !e8 || !W_hat) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16 && out_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (!aligned(qpacked, 16) || !aligned(W_hat, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_dequant_mxfp4(reinterpret_cast<const uint8_t*>(qpacked), e8, N, K, out_dtype, W_hat,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) { return wq_gemm_workspace_bytes(M, N, K, 32); }
+
+int wq_gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint8_t* e8, uint16_t* y_f16, void* workspace, size_t workspace_bytes, int path,
+                     void* stream) {
+  bool mfma = false;
+  const int st = check_gemm(M, N, K, 32, wq::kFmtMxfp4, x_f16, qpacked, nullptr, e8, y_f16, workspace,
+                            workspace_bytes, path, &mfma);
+  if (st) return st;
+  return hip_status(launch_one(mfma, M, N, K, 32, wq::kFmtMxfp4, x_f16, qpacked, nullptr, e8, y_f16, workspace,
+                               static_cast<hipStream_t>(stream)));
+}
+
+int wq_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked, const uint8_t* e8,
+                  uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream) {
+  return wq_gemm_mxfp4_ex(M, N, K, x_f16, qpacked, e8, y_f16, workspace, workspace_bytes, WQ_PATH_AUTO, stream);
+}
+
+int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, size_t buf_len) {
+  if (!buf || buf_len == 0) return WQ_EINVAL;
+  buf[0] = 0;
+  if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  if (mfma)
+    wq::describe_gemm(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
+  else
+    wq::describe_gemv(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
+  return WQ_OK;
 }
 
 }  // extern "C"

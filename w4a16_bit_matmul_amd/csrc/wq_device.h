@@ -28,6 +28,12 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+// Code formats of the product kernels: 4-bit asymmetric / symmetric INT4 (with
+// fp16 scales and 4-bit zero-points), group absmax int8 (fp16 scales), MXFP4
+// (E2M1 codes in the INT4 tile geometry, natural nibble order, one E8M0 scale
+// byte per block of 32).
+enum : int { kFmtInt4 = 4, kFmtInt8 = 8, kFmtMxfp4 = 2 };
+
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 128;
 constexpr int kTileBytes = 1024;
@@ -61,6 +67,19 @@ __device__ __forceinline__ h2 biased_pair64(uint32_t word, int p) {
 constexpr uint32_t kMagicBytes = 0x64646464u;
 __device__ __forceinline__ uint32_t byte_pair(uint32_t word_flipped, uint32_t sel) {
   return __builtin_amdgcn_perm(kMagicBytes, word_flipped, sel);
+}
+
+// The fp16 pair (E2M1 code of byte b's low nibble, high nibble) * 2^e, where the
+// scale argument's exponent field gives e (v_cvt_scalef32_pk_f16_fp4: fp16
+// rounding of the exact product).
+template <int B>
+__device__ __forceinline__ h2 fp4_pair(uint32_t word, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, scale, B);
+}
+
+// 2^(e8 - 127) as fp32 (e8 = 0: the fp32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e8) {
+  return __builtin_bit_cast(float, e8 == 0 ? 0x00400000u : e8 << 23);
 }
 
 // Round-to-nearest-even fp32 -> fp16 bits.

@@ -20,7 +20,10 @@
 // matrix cores.  8-bit codes (group absmax int8, What = s * q): sign-bit flip
 // and byte permute (1152 + q, exact fp16), packed subtraction of 1152, packed
 // multiply by the scale; each wave's 16-byte load then holds its two MFMA
-// steps of a 2048-byte tile.
+// steps of a 2048-byte tile.  MXFP4 codes (E2M1, one E8M0 scale per block of
+// 32 = one MFMA step): v_cvt_scalef32_pk_f16_fp4 turns each byte of a code
+// word into the fp16 pair of E2M1 value times the block's power of two, four
+// instructions per operand.
 //
 // Decomposition.  A workgroup of eight waves (two per SIMD) owns a (16*MB) x
 // 128 output tile and walks K one 128-column tile per step, all waves on the
@@ -95,6 +98,17 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t magic, h2 nb, h2
   return out;
 }
 
+// fp16(E2M1(q) * 2^e) for the eight columns of an MXFP4 code word (column e in
+// nibble e); the scale's exponent field gives e.
+__device__ __forceinline__ h8 dequant_word_mx(uint32_t w, float scale) {
+  const h2 p0 = fp4_pair<0>(w, scale), p1 = fp4_pair<1>(w, scale), p2 = fp4_pair<2>(w, scale),
+           p3 = fp4_pair<3>(w, scale);
+  h8 out;
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+  return out;
+}
+
 // fp16(s * q) for the eight columns held by two words of 8-bit codes.
 __device__ __forceinline__ h8 dequant_words8(uint32_t lo, uint32_t hi, h2 sc) {
   const h2 bias = as_h2(0x64806480u);  // (1152, 1152)
@@ -113,17 +127,20 @@ __device__ __forceinline__ h8 dequant_words8(uint32_t lo, uint32_t hi, h2 sc) {
 // LDS bytes of one staged chunk for the workgroup's 128 weight rows:
 // g = 128: [tile][row] u32 (scale bits, zero-point in bits 16..19);
 // g = 32: [tile][pair][row] u32 (scales of groups 4t + 2q, 4t + 2q + 1), then
-// [tile][row] u16 (the tile's four zero-points, group 4t in bits 0..3).
-template <int G>
+// [tile][row] u16 (the tile's four zero-points, group 4t in bits 0..3);
+// MXFP4: [tile][row] u32 (the tile's four E8M0 scale bytes, block 4t first).
+template <int G, int FMT = kFmtInt4>
 constexpr int sz_chunk_bytes() {
-  return G == 128 ? kSzChunk * 128 * 4 : kSzChunk * 2 * 128 * 4 + kSzChunk * 128 * 2;
+  return (G == 128 || FMT == kFmtMxfp4) ? kSzChunk * 128 * 4 : kSzChunk * 2 * 128 * 4 + kSzChunk * 128 * 2;
 }
 
 // SZV: every row of s (and zpacked) is aligned for the wide staging loads.
-// BITS: 4 (codes and zero-points) or 8 (int8 codes, no zero-points).
-template <int MB, int G, bool SZV, int BITS>
+// FMT: kFmtInt4 (codes and zero-points), kFmtInt8 (int8 codes, no
+// zero-points) or kFmtMxfp4 (E2M1 codes, E8M0 scale bytes in a.zp, G = 32).
+template <int MB, int G, bool SZV, int FMT>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
-  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
+  constexpr int BITS = FMT == kFmtInt8 ? 8 : 4;
   using CodeT = std::conditional_t<BITS == 4, uint2, u4>;  // one wave's two MFMA steps of a tile
   constexpr int TB = BITS == 4 ? kTileBytes : kTileBytes8;
   constexpr int NPW = kNPW;
@@ -131,7 +148,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   constexpr int ROWS = 16 * MB;
   constexpr int XTILE = ROWS * 256;                            // one K tile of activations in LDS
   constexpr int XCH = ROWS * 16 >= NTH ? ROWS * 16 / NTH : 1;  // 16-byte chunks per thread per tile
-  constexpr int SZB = sz_chunk_bytes<G>();
+  constexpr int SZB = sz_chunk_bytes<G, FMT>();
   static_assert(ROWS * 16 % NTH == 0 || NTH % (ROWS * 16) == 0, "whole chunks per thread");
   extern __shared__ __align__(16) uint8_t smem[];  // [2][XTILE] activations, [2][SZB] scales
 
@@ -192,27 +209,40 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   };
   auto sz_load = [&](int chunk, SzStage& v) {
     const int t0 = chunk * kSzChunk + 2 * sp;  // first of this thread's two tiles
-    if constexpr (G == 128) {
+    if constexpr (FMT == kFmtMxfp4) {  // eight scale bytes: blocks 4 t0 .. 4 t0 + 7
+      if constexpr (SZV) {  // Gtot % 8 == 0
+        const uint2 t = *reinterpret_cast<const uint2*>(a.zp + srow + min(4 * t0, a.Gtot - 8));
+        v.s[0] = t.x;
+        v.s[1] = t.y;
+      } else {
+        uint32_t b[2] = {0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) b[q >> 2] |= (uint32_t)a.zp[srow + min(4 * t0 + q, a.Gtot - 1)] << (8 * (q & 3));
+        v.s[0] = b[0];
+        v.s[1] = b[1];
+      }
+      v.z = 0u;
+    } else if constexpr (G == 128) {
       if constexpr (SZV) {  // Gtot even: one u32 holds both scales
         v.s[0] = *reinterpret_cast<const uint32_t*>(a.s + srow + min(t0, a.Gtot - 2));
       } else {
         v.s[0] = a.s[srow + min(t0, a.Gtot - 1)];
         v.s[1] = a.s[srow + min(t0 + 1, a.Gtot - 1)];
       }
-      v.z = BITS == 4 ? a.zp[zrow + (min(t0, a.Gtot - 1) >> 1)] : 0u;
+      v.z = FMT == kFmtInt4 ? a.zp[zrow + (min(t0, a.Gtot - 1) >> 1)] : 0u;
     } else {
       if constexpr (SZV) {  // Gtot % 8 == 0: 16 bytes of scales, 4 bytes of zero-points
         const int g = min(4 * t0, a.Gtot - 8);
         const u4 t = *reinterpret_cast<const u4*>(a.s + srow + g);
         v.s[0] = t.x; v.s[1] = t.y; v.s[2] = t.z; v.s[3] = t.w;
-        v.z = BITS == 4 ? *reinterpret_cast<const uint32_t*>(a.zp + zrow + g / 2) : 0u;
+        v.z = FMT == kFmtInt4 ? *reinterpret_cast<const uint32_t*>(a.zp + zrow + g / 2) : 0u;
       } else {
         uint32_t zz = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int g0 = min(4 * t0 + 2 * q, a.Gtot - 1), g1 = min(4 * t0 + 2 * q + 1, a.Gtot - 1);
           v.s[q] = (uint32_t)a.s[srow + g0] | ((uint32_t)a.s[srow + g1] << 16);
-          if constexpr (BITS == 4) {
+          if constexpr (FMT == kFmtInt4) {
             const uint32_t zb0 = a.zp[zrow + (g0 >> 1)], zb1 = a.zp[zrow + (g1 >> 1)];
             zz |= (((g0 & 1) ? zb0 >> 4 : zb0 & 15u) | (((g1 & 1) ? zb1 >> 4 : zb1 & 15u) << 4)) << (8 * q);
           }
@@ -224,7 +254,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   uint8_t* const szbase = smem + 2 * XTILE;
   auto sz_store = [&](int chunk, const SzStage& v) {
     uint8_t* buf = szbase + (chunk & 1) * SZB;
-    if constexpr (G == 128) {
+    if constexpr (FMT == kFmtMxfp4) {
+      *reinterpret_cast<uint32_t*>(buf + (2 * sp) * 512 + 4 * sn) = v.s[0];
+      *reinterpret_cast<uint32_t*>(buf + (2 * sp + 1) * 512 + 4 * sn) = v.s[1];
+    } else if constexpr (G == 128) {
       const uint32_t s0 = SZV ? v.s[0] & 0xffffu : v.s[0];
       const uint32_t s1 = SZV ? v.s[0] >> 16 : v.s[1];
       // tiles 2p (low nibble) and 2p + 1 (high nibble) share a zero-point byte
@@ -283,7 +316,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     uint32_t sv[NPW], zv[NPW];
 #pragma unroll
     for (int b = 0; b < NPW; ++b) {
-      if constexpr (G == 128) {
+      if constexpr (FMT == kFmtMxfp4) {
+        sv[b] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * (szrow + 16 * b));
+        zv[b] = 0u;
+      } else if constexpr (G == 128) {
         sv[b] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * (szrow + 16 * b));
         zv[b] = sv[b] >> 16;
       } else {
@@ -302,10 +338,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abuf + i * 16 * 256 + slot);
 #pragma unroll
       for (int b = 0; b < NPW; ++b) {
+        h8 bf;
         const uint32_t sb = G == 128 ? sv[b] & 0xffffu : (jj ? sv[b] >> 16 : sv[b] & 0xffffu);
         const h2 sc = as_h2(sb * 0x00010001u);
-        h8 bf;
-        if constexpr (BITS == 4) {
+        if constexpr (FMT == kFmtMxfp4) {
+          // block 4 kt + j: byte j of the tile's scale word (exponent field only)
+          const float scale = __builtin_bit_cast(float, ((sv[b] >> (8 * j)) & 0xffu) << 23);
+          bf = dequant_word_mx(jj ? cur[b].y : cur[b].x, scale);
+        } else if constexpr (FMT == kFmtInt4) {
           const uint32_t z = G == 128 ? zv[b] & 15u : (zv[b] >> (4 * jj)) & 15u;
           const h2 nbias = -as_h2(z * 0x00010001u + magic);
           bf = dequant_word(jj ? cur[b].y : cur[b].x, magic, nbias, sc);
@@ -387,51 +427,60 @@ dim3 gemm_grid(int MB, int64_t M, int64_t N) {
   return dim3((unsigned)(((N + 15) / 16 + 7) / 8), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
 }
 
-size_t gemm_lds(int MB, int group) {
+size_t gemm_lds(int MB, int group, int fmt) {
   // two activation buffers and two staged chunks of scales / zero-points; the
   // final reduction ([4][MB*NPW*4][64] fp32) reuses the front of it
   const size_t tiles =
-      (size_t)2 * MB * 16 * 256 + 2 * (size_t)(group == 128 ? sz_chunk_bytes<128>() : sz_chunk_bytes<32>());
+      (size_t)2 * MB * 16 * 256 +
+      2 * (size_t)(fmt == kFmtMxfp4 ? sz_chunk_bytes<32, kFmtMxfp4>()
+                                    : group == 128 ? sz_chunk_bytes<128>() : sz_chunk_bytes<32>());
   const size_t red = (size_t)4 * MB * kNPW * 4 * 64 * sizeof(float);
   return tiles > red ? tiles : red;
 }
 
-template <int MB, int G, bool SZV, int BITS>
+template <int MB, int G, bool SZV, int FMT>
 hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid = gemm_grid(MB, a.M, a.N), block(kWaves * 64);
-  const size_t lds = gemm_lds(MB, G);
-  auto k = gemm_kernel<MB, G, SZV, BITS>;
+  const size_t lds = gemm_lds(MB, G, FMT);
+  auto k = gemm_kernel<MB, G, SZV, FMT>;
   if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   k<<<grid, block, lds, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int MB, int BITS>
+template <int MB, int FMT>
 hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
   // wide staging loads of scales / zero-points when every row is aligned for
   // them: g = 128 two scales (4 bytes); g = 32 eight scales (16 bytes) and
-  // eight zero-points (4 bytes)
+  // eight zero-points (4 bytes); MXFP4 eight scale bytes
   const uintptr_t sp = reinterpret_cast<uintptr_t>(a.s), zp = reinterpret_cast<uintptr_t>(a.zp);
-  if (group == 128) {
-    if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, BITS>(a, stream);
-    return launch_kg<MB, 128, false, BITS>(a, stream);
+  if constexpr (FMT == kFmtMxfp4) {
+    if (a.Gtot % 8 == 0 && zp % 8 == 0) return launch_kg<MB, 32, true, FMT>(a, stream);
+    return launch_kg<MB, 32, false, FMT>(a, stream);
+  } else {
+    if (group == 128) {
+      if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, FMT>(a, stream);
+      return launch_kg<MB, 128, false, FMT>(a, stream);
+    }
+    if (a.Gtot % 8 == 0 && sp % 16 == 0 && (FMT == kFmtInt8 || zp % 4 == 0))
+      return launch_kg<MB, 32, true, FMT>(a, stream);
+    return launch_kg<MB, 32, false, FMT>(a, stream);
   }
-  if (a.Gtot % 8 == 0 && sp % 16 == 0 && (BITS == 8 || zp % 4 == 0)) return launch_kg<MB, 32, true, BITS>(a, stream);
-  return launch_kg<MB, 32, false, BITS>(a, stream);
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
-int describe_gemm(int64_t M, int64_t N, int64_t, int group, int bits, char* buf, size_t len) {
+int describe_gemm(int64_t M, int64_t N, int64_t, int group, int fmt, char* buf, size_t len) {
   const int MB = gemm_mb(M);
   const dim3 g = gemm_grid(MB, M, N);
   return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d%s> grid=(%u,%u,1) block=%d lds=%zu", MB, kNPW, group,
-                  bits == 8 ? ", BITS=8" : "", g.x, g.y, kWaves * 64, gemm_lds(MB, group));
+                  fmt == kFmtInt8 ? ", BITS=8" : fmt == kFmtMxfp4 ? ", MXFP4" : "", g.x, g.y, kWaves * 64,
+                  gemm_lds(MB, group, fmt));
 }
 
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x, const void* qpacked,
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* /*workspace*/,
                        hipStream_t stream) {
   GemmArgs a;
@@ -447,19 +496,27 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, con
   a.Gtot = (int)(K / group);
   a.GB = (a.Gtot + 1) / 2;
   a.NBLK = (int)((N + 15) / 16);
-  if (bits == 8) {
+  if (fmt == kFmtInt8) {
     switch (gemm_mb(M)) {
-      case 1: return launch_t<1, 8>(group, a, stream);
-      case 2: return launch_t<2, 8>(group, a, stream);
-      case 4: return launch_t<4, 8>(group, a, stream);
-      default: return launch_t<8, 8>(group, a, stream);
+      case 1: return launch_t<1, kFmtInt8>(group, a, stream);
+      case 2: return launch_t<2, kFmtInt8>(group, a, stream);
+      case 4: return launch_t<4, kFmtInt8>(group, a, stream);
+      default: return launch_t<8, kFmtInt8>(group, a, stream);
+    }
+  }
+  if (fmt == kFmtMxfp4) {
+    switch (gemm_mb(M)) {
+      case 1: return launch_t<1, kFmtMxfp4>(group, a, stream);
+      case 2: return launch_t<2, kFmtMxfp4>(group, a, stream);
+      case 4: return launch_t<4, kFmtMxfp4>(group, a, stream);
+      default: return launch_t<8, kFmtMxfp4>(group, a, stream);
     }
   }
   switch (gemm_mb(M)) {
-    case 1: return launch_t<1, 4>(group, a, stream);
-    case 2: return launch_t<2, 4>(group, a, stream);
-    case 4: return launch_t<4, 4>(group, a, stream);
-    default: return launch_t<8, 4>(group, a, stream);
+    case 1: return launch_t<1, kFmtInt4>(group, a, stream);
+    case 2: return launch_t<2, kFmtInt4>(group, a, stream);
+    case 4: return launch_t<4, kFmtInt4>(group, a, stream);
+    default: return launch_t<8, kFmtInt4>(group, a, stream);
   }
 }
 

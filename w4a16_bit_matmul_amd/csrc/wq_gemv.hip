@@ -27,6 +27,12 @@
 // packed fp16 subtraction of 1152 leaves q exactly, which v_dot2_f32_f16
 // multiplies with the activation pairs into one fp32 sum per group.
 //
+// MXFP4 codes (E2M1, natural nibble order, one E8M0 scale per block of 32 =
+// one code word per lane): v_cvt_scalef32_pk_f16_fp4 turns each byte into the
+// exact fp16 pair of E2M1 values, v_dot2_f32_f16 takes the block's fp32 sum,
+// and the power-of-two scale is applied in fp32 (exact over the whole E8M0
+// range).
+//
 // Decomposition.  A workgroup owns one 16-row block, MT rows of x and a range
 // of 128-column K tiles (all of K unless the grid splits K).  Wave w walks
 // segments of KQ consecutive K tiles (w, w + W, w + 2W, ... in segment units).
@@ -155,6 +161,40 @@ __device__ __forceinline__ float dot_group4(const u4& w4, uint32_t z, uint32_t m
   return fmaf(a16, 0.0625f, a1);
 }
 
+// E8M0 scale bytes of the NS blocks one segment covers in one row.
+template <int NS>
+struct E8 {
+  uint32_t v[NS / 4];
+  __device__ __forceinline__ float scale(int t) const { return e8m0_to_f32((v[t >> 2] >> (8 * (t & 3))) & 0xffu); }
+};
+
+template <int NS>
+__device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, uint32_t erow, int g0) {
+  static_assert(NS == 16, "segment of four tiles of four blocks");
+  E8<NS> v;
+  if (a.sz_vec) {
+    const u4 t = *reinterpret_cast<const u4*>(a.zp + erow + g0);
+    v.v[0] = t[0]; v.v[1] = t[1]; v.v[2] = t[2]; v.v[3] = t[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS / 4; ++i) v.v[i] = 0;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) v.v[t >> 2] |= (uint32_t)a.zp[erow + min(g0 + t, a.Gtot - 1)] << (8 * (t & 3));
+  }
+  return v;
+}
+
+// sum over one block of 32 of x * E2M1(q): code word w (columns 8c .. 8c+7 of
+// the block for this lane), exact fp16 values, fp32 sum.
+__device__ __forceinline__ float dot_block_mx(uint32_t w, const uint4& xv) {
+  float a = 0.0f;
+  a = __builtin_amdgcn_fdot2(fp4_pair<0>(w, 1.0f), as_h2(xv.x), a, false);
+  a = __builtin_amdgcn_fdot2(fp4_pair<1>(w, 1.0f), as_h2(xv.y), a, false);
+  a = __builtin_amdgcn_fdot2(fp4_pair<2>(w, 1.0f), as_h2(xv.z), a, false);
+  a = __builtin_amdgcn_fdot2(fp4_pair<3>(w, 1.0f), as_h2(xv.w), a, false);
+  return a;
+}
+
 // sum over one group of x * q for 8-bit codes: steps j0 .. j0 + NJ - 1 of a
 // tile, codes in the two halves h0 (steps 0, 1) and h1 (steps 2, 3).
 template <int NJ>
@@ -174,11 +214,13 @@ __device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, 
   return a;
 }
 
-template <int MT, int W, int KQ, int G, int BITS>
+// FMT: kFmtInt4 (codes, fp16 scales, zero-points), kFmtInt8 (2048-byte tiles,
+// fp16 scales), kFmtMxfp4 (E2M1 tiles, E8M0 scale bytes in a.zp, G = 32).
+template <int MT, int W, int KQ, int G, int FMT>
 __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
-  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
-  constexpr int TB = BITS == 4 ? kTileBytes : kTileBytes8;
-  constexpr int HALVES = BITS / 4;  // 16-byte loads per lane and tile
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
+  constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
+  constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;     // groups per 128-column tile
   constexpr int NS = KQ * GPT;     // groups per segment
   constexpr int NT = W * 64;
@@ -219,7 +261,12 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    const SZ<NS> sz = load_sz<NS, BITS == 4>(a, srow, zrow, kt0 * GPT);
+    SZ<NS> sz;
+    E8<16> e8s;
+    if constexpr (FMT == kFmtMxfp4)
+      e8s = load_e8<16>(a, srow, kt0 * GPT);
+    else
+      sz = load_sz<NS, FMT == kFmtInt4>(a, srow, zrow, kt0 * GPT);
     u4 buf[KQ][HALVES];
 #pragma unroll
     for (int t = 0; t < KQ; ++t)
@@ -248,12 +295,16 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int gi = 0; gi < GPT; ++gi) {
           const int j0 = gi * (4 / GPT);
-          float d;
-          if constexpr (BITS == 8)
-            d = dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], j0, xv);
-          else
-            d = dot_group4<4 / GPT>(buf[t][0], sz.zero(t * GPT + gi), magic, j0, xv);
-          acc[m] = fmaf(sz.scale(t * GPT + gi), d, acc[m]);
+          if constexpr (FMT == kFmtMxfp4) {
+            acc[m] = fmaf(e8s.scale(t * GPT + gi), dot_block_mx(buf[t][0][gi], xv[gi]), acc[m]);
+          } else {
+            float d;
+            if constexpr (FMT == kFmtInt8)
+              d = dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], j0, xv);
+            else
+              d = dot_group4<4 / GPT>(buf[t][0], sz.zero(t * GPT + gi), magic, j0, xv);
+            acc[m] = fmaf(sz.scale(t * GPT + gi), d, acc[m]);
+          }
         }
       }
     }
@@ -341,33 +392,35 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-template <int MT, int W, int G, int BITS>
+template <int MT, int W, int G, int FMT>
 void launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto k = gemv_kernel<MT, W, kKQ, G, BITS>;
+  auto k = gemv_kernel<MT, W, kKQ, G, FMT>;
   if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
   k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
 }
 
 template <int MT, int W>
-hipError_t launch_t(const GemvPlan& p, int group, int bits, GemvArgs a, hipStream_t stream) {
-  if (bits == 8) {
-    if (group == 128) launch_k<MT, W, 128, 8>(p, a, stream);
-    else launch_k<MT, W, 32, 8>(p, a, stream);
+hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
+  if (fmt == kFmtMxfp4) {
+    launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
+  } else if (fmt == kFmtInt8) {
+    if (group == 128) launch_k<MT, W, 128, kFmtInt8>(p, a, stream);
+    else launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
   } else {
-    if (group == 128) launch_k<MT, W, 128, 4>(p, a, stream);
-    else launch_k<MT, W, 32, 4>(p, a, stream);
+    if (group == 128) launch_k<MT, W, 128, kFmtInt4>(p, a, stream);
+    else launch_k<MT, W, 32, kFmtInt4>(p, a, stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len) {
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
   const GemvPlan p = plan_gemv(M, N, K);
-  if (bits == 8)
-    return snprintf(buf, len,
-                    "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, BITS=8> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d", p.MT,
-                    p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
+  if (fmt == kFmtInt8 || fmt == kFmtMxfp4)
+    return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "MXFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
+                    p.KS);
   return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                   p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
 }
@@ -380,7 +433,7 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
   return part_al + (size_t)p.gx * p.gy * sizeof(unsigned);
 }
 
-hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x,
+hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
                        const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream) {
   const GemvPlan p = plan_gemv(M, N, K);
@@ -404,9 +457,14 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, con
   const int ns = kKQ * (128 / group);  // groups per segment
   a.sz_vec = (a.Gtot % ns == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
               (reinterpret_cast<uintptr_t>(s) & (uintptr_t)(2 * ns > 16 ? 15 : 2 * ns - 1)) == 0 &&
-              (bits == 8 || (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0))
+              (fmt == kFmtInt8 || (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0))
                  ? 1
                  : 0;
+  if (fmt == kFmtMxfp4)  // 16 scale bytes per segment, one 16-byte load
+    a.sz_vec = (a.Gtot % 16 == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
+                (reinterpret_cast<uintptr_t>(zpacked) & 15) == 0)
+                   ? 1
+                   : 0;
   a.partial = nullptr;
   a.counters = nullptr;
   if (p.KS > 1) {
@@ -414,10 +472,10 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, con
     a.partial = static_cast<float*>(workspace);
     a.counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
   }
-  if (p.MT == 1) return launch_t<1, 16>(p, group, bits, a, stream);
-  if (p.MT == 2) return launch_t<2, 16>(p, group, bits, a, stream);
-  if (p.MT == 4) return launch_t<4, 16>(p, group, bits, a, stream);
-  return launch_t<8, 8>(p, group, bits, a, stream);
+  if (p.MT == 1) return launch_t<1, 16>(p, group, fmt, a, stream);
+  if (p.MT == 2) return launch_t<2, 16>(p, group, fmt, a, stream);
+  if (p.MT == 4) return launch_t<4, 16>(p, group, fmt, a, stream);
+  return launch_t<8, 8>(p, group, fmt, a, stream);
 }
 
 }  // namespace wq

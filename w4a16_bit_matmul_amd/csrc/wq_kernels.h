@@ -34,6 +34,14 @@ hipError_t launch_pack_w8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* 
 hipError_t launch_dequant_w8(const uint8_t* qpacked, const uint16_t* s, int64_t N, int64_t K, int group,
                              int out_dtype, void* out, hipStream_t stream);
 
+// MXFP4: E2M1 codes [N][K] (or NULL), E8M0 scale bytes [N][K/32], 1 KB tiles
+// with natural nibble order (or NULL).
+hipError_t launch_quantize_mxfp4(const void* W, int dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* e8,
+                                 uint8_t* qpacked, hipStream_t stream);
+hipError_t launch_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, hipStream_t stream);
+hipError_t launch_dequant_mxfp4(const uint8_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype,
+                                void* out, hipStream_t stream);
+
 // INT4 KV cache in blocks of 128: token t's hd values (X [T][hd]) into cache
 // row slot[t] (slot NULL: row t; rows outside [0, S) skipped), and back.
 hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
@@ -46,17 +54,18 @@ hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint
 // workgroups; gemv_workspace_bytes gives the size (0 otherwise).
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 // Writes a one-line description of the kernel and launch shape chosen for this
-// problem (snprintf semantics).  bits: 4 (tile codes + zero-points) or 8
-// (2048-byte int8 tiles; zpacked unused).
-int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len);
-hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x,
+// problem (snprintf semantics).  fmt (wq_device.h): kFmtInt4 (tile codes +
+// zero-points), kFmtInt8 (2048-byte int8 tiles; zpacked unused) or kFmtMxfp4
+// (E2M1 tiles; zpacked holds the E8M0 scale bytes, s unused, group 32).
+int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len);
+hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
                        const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream);
 
 // MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
-int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, char* buf, size_t len);
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x, const void* qpacked,
+int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len);
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
 
 }  // namespace wq

@@ -13,6 +13,11 @@
 // Group absmax int8 (same page and section: s = max|w| / 127, q = round(w / s),
 // decoding q * s) keeps one fp16 scale per group, no zero-point, and 8-bit
 // codes in 2048-byte tiles (16 rows x 128 columns).
+// MXFP4 ("Quantization for LLM inference", section "Microscaling: NVFP4 and
+// MXFP4", in the format of the microscaling paper it cites): E2M1 codes, one
+// E8M0 power-of-two scale per block of 32 along K, in the 1 KB tiles with
+// natural nibble order (two neighbouring columns per byte, as the hardware's
+// FP4 conversion takes them).
 // INT4 KV cache ("Quantization for LLM inference", section "KV cache
 // quantization": int4 in blocks of 128): each token's K or V vector is cut into
 // blocks of 128 values, each block quantized like a weight group, the rows
@@ -542,6 +547,155 @@ __global__ __launch_bounds__(256) void dequant_w8_kernel(const uint8_t* __restri
   }
 }
 
+// ---- MXFP4 --------------------------------------------------------------------
+
+// E8M0 scale byte of a block whose max |v| is amax: the shared exponent
+// floor(log2 amax) - 2 (the exponent field of amax minus 129 for normal amax),
+// clamped at -127; 0 for an all-zero or fp32-subnormal maximum.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const int E = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu);
+  return (uint32_t)max(E - 2, 0);
+}
+
+// E2M1 code of v / 2^(e8 - 127): nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to
+// the even mantissa bit, saturating at 6, sign in bit 3 (kept for negative
+// values that round to zero).  The scaled magnitude m is below 8; on the
+// grids 0.5 (m < 2), 1 (m < 4) and 2 (m >= 4) an integer's parity is the
+// mantissa bit, so rint on each grid rounds ties to even.
+__device__ __forceinline__ uint32_t mx_encode(float v, uint32_t e8) {
+  const float inv = __builtin_bit_cast(float, (254u - e8) << 23);  // 2^(127 - e8), exact
+  const float m = fabsf(v) * inv;
+  uint32_t code;
+  if (m < 2.0f) code = (uint32_t)rintf(2.0f * m);           // 0 .. 4
+  else if (m < 4.0f) code = (uint32_t)rintf(m) + 2u;        // 4 .. 6
+  else code = min((uint32_t)rintf(0.5f * m) + 4u, 7u);      // 6, 7 (saturating)
+  return code | (v < 0.0f ? 8u : 0u);
+}
+
+// E2M1 magnitude of code bits 0..2 (exact in fp32).
+__device__ __forceinline__ float mx_magnitude(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, f = c & 1u;
+  return e == 0 ? 0.5f * (float)f : __builtin_bit_cast(float, (e + 126u) << 23) * (1.0f + 0.5f * (float)f);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const void* __restrict__ W, int64_t N, int64_t K,
+                                                             int64_t NBLK, int64_t KT, uint8_t* __restrict__ q_codes,
+                                                             uint8_t* __restrict__ e8_out, uint8_t* __restrict__ qpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;  // whole wave exits together
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  const bool row_ok = n < N;
+  const int64_t Gtot = K / 32;
+
+  float w[4][8];
+  bool jok[4];
+  load_lane_tile<DT>(W, n, row_ok, K, kt, c, w, jok);
+  uint32_t words[4], e8[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(w[j][e]));
+    amax = wave_max4(amax);
+    e8[j] = amax > 0.0f ? mx_scale_byte(amax) : 0u;
+    uint32_t word = 0;
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = jok[j] ? mx_encode(w[j][e], e8[j]) : 0u;
+      word |= b[e] << (4 * e);
+    }
+    words[j] = word;
+    if (q_codes && jok[j])
+      *reinterpret_cast<uint2*>(q_codes + n * K + kt * 128 + 32 * j + 8 * c) =
+          make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  }
+  if (qpacked)
+    *reinterpret_cast<u4*>(qpacked + tile_offset_bytes(nb, kt, KT) + 16 * lane) = u4{words[0], words[1], words[2], words[3]};
+  if (row_ok) {
+    const int64_t gi = kt * 4 + c;  // lane c writes block c of this tile
+    if (gi < Gtot) e8_out[n * Gtot + gi] = (uint8_t)(c == 0 ? e8[0] : c == 1 ? e8[1] : c == 2 ? e8[2] : e8[3]);
+  }
+}
+
+// MXFP4 codes [N][K] (low 4 bits) -> tiles with natural nibble order.
+__global__ __launch_bounds__(256) void pack_mxfp4_kernel(const uint8_t* __restrict__ q_codes, int64_t N, int64_t K,
+                                                         int64_t NBLK, int64_t KT, uint8_t* __restrict__ qpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  uint32_t words[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;
+    if (n < N && kt * 128 + 32 * j < K) {
+      const uint2 v = *reinterpret_cast<const uint2*>(q_codes + n * K + kt * 128 + 32 * j + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= (((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 15u) << (4 * e);
+    }
+    words[j] = word;
+  }
+  *reinterpret_cast<u4*>(qpacked + tile_offset_bytes(nb, kt, KT) + 16 * lane) = u4{words[0], words[1], words[2], words[3]};
+}
+
+// Tiles + E8M0 scales -> What[N][K] = E2M1(q) * 2^(e8 - 127) (exact in fp32).
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint8_t* __restrict__ qpacked,
+                                                            const uint8_t* __restrict__ e8_in, int64_t N, int64_t K,
+                                                            int64_t NBLK, int64_t KT, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  if (n >= N) return;
+  const int64_t Gtot = K / 32;
+  const u4 v = *reinterpret_cast<const u4*>(qpacked + tile_offset_bytes(nb, kt, KT) + 16 * lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+    if (k0 >= K) continue;
+    const uint32_t e8 = e8_in[n * Gtot + k0 / 32];
+    const float sc = __builtin_bit_cast(float, e8 == 0 ? 0x00400000u : e8 << 23);  // 2^(e8 - 127)
+    // magnitudes (exact, >= 0) converted first, the sign then set as a bit: a
+    // code of -0 must give -0 in every output format (the compiler may fuse
+    // the product and the fp16 conversion into one fma with a +0 addend)
+    float d[8];
+    uint32_t neg[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t c = (v[j] >> (4 * e)) & 15u;
+      d[e] = mx_magnitude(c) * sc;
+      neg[e] = c >> 3;
+    }
+    if constexpr (OUT == 0) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(uint32_t, d[e]) | (neg[e] << 31);
+      uint4* o = reinterpret_cast<uint4*>(static_cast<float*>(out) + n * K + k0);
+      o[0] = make_uint4(b[0], b[1], b[2], b[3]);
+      o[1] = make_uint4(b[4], b[5], b[6], b[7]);
+    } else {
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t a = OUT == 2 ? f32_to_f16_bits(d[2 * i]) : f32_to_bf16_bits(d[2 * i]);
+        uint32_t b = OUT == 2 ? f32_to_f16_bits(d[2 * i + 1]) : f32_to_bf16_bits(d[2 * i + 1]);
+        p[i] = (a | (neg[2 * i] << 15)) | ((b | (neg[2 * i + 1] << 15)) << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + n * K + k0) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  }
+}
+
 // ---- INT4 KV cache in blocks of 128 ------------------------------------------
 // A 16-lane group owns a pair of blocks (2p, 2p + 1) of one token: lanes 0..7
 // block 2p, lanes 8..15 block 2p + 1, each lane 16 consecutive values (two
@@ -797,6 +951,32 @@ hipError_t launch_scale_activations(const uint16_t* x, int64_t M, int64_t K, con
 
 hipError_t launch_channel_absmean(const uint16_t* x, int64_t M, int64_t K, float* out, hipStream_t stream) {
   channel_absmean_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream>>>(x, M, K, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4(const void* W, int dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* e8,
+                                 uint8_t* qpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+  if (dtype == 0) quantize_mxfp4_kernel<0><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, e8, qpacked);
+  else if (dtype == 1) quantize_mxfp4_kernel<1><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, e8, qpacked);
+  else quantize_mxfp4_kernel<2><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, q_codes, e8, qpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  pack_mxfp4_kernel<<<dim3((unsigned)blocks_for(NBLK * KT)), dim3(256), 0, stream>>>(q_codes, N, K, NBLK, KT, qpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp4(const uint8_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype,
+                                void* out, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+  if (out_dtype == 0) dequant_mxfp4_kernel<0><<<grid, block, 0, stream>>>(qpacked, e8, N, K, NBLK, KT, out);
+  else if (out_dtype == 1) dequant_mxfp4_kernel<1><<<grid, block, 0, stream>>>(qpacked, e8, N, K, NBLK, KT, out);
+  else dequant_mxfp4_kernel<2><<<grid, block, 0, stream>>>(qpacked, e8, N, K, NBLK, KT, out);
   return hipGetLastError();
 }
 
