@@ -288,6 +288,43 @@ def bench_awq():
             "scale_activations_us_m1_python_call": round(t * 1e6, 3)}
 
 
+def bench_sweep(steps):
+    """Every workload (the tiny case, decode, the M=16 up-projection, the M=128
+    GEMM and the g=32 sweep of 70B layer shapes) through both kernel families:
+    time per launch, effective GB/s and TFLOP/s; one JSON line each."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    qcache = {}
+    for name, wl in workloads.WORKLOADS.items():
+        key = (wl.w_seed, wl.N, wl.K, wl.group, wl.w_dtype)
+        if key not in qcache:
+            qcache.clear()
+            W = wl.weights()
+            Wd = torch.from_numpy(W.view(np.int16 if W.dtype == np.uint16 else np.float32)).cuda()
+            if W.dtype == np.uint16:
+                Wd = Wd.view(torch.bfloat16)
+            qw = wq.wq_quantize_groups(Wd, wl.group)["qw"]
+            del Wd
+            copies = max(2, math.ceil(ROTATE_BYTES / wl.algorithmic_bytes()))
+            qcache[key] = _device_copies(qw, copies)
+        qws = qcache[key]
+        copies = len(qws)
+        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+        ws = _workspace(wl)
+        rec = {"workload": name, "M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
+               "auto": "mfma" if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else "gemv"}
+        for path, tag in ((wq.WQ_PATH_GEMV, "gemv"), (wq.WQ_PATH_MFMA, "mfma")):
+            n_steps = max(20, steps // 4)
+            t = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws, path=path), n_steps,
+                            max(50, 2000 // max(1, wl.M)))
+            rec[tag] = {"us": round(t * 1e6, 3), "gbs": round(wl.algorithmic_bytes() / t / 1e9, 1),
+                        "tflops": round(wl.flops() / t / 1e12, 2)}
+        print(json.dumps(rec), flush=True)
+
+
 def bench_quantize(wl_name="decode_gemv", reps=20):
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -364,6 +401,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the decode GEMV")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line, time every workload through both kernel families "
+                         "(one JSON line each)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run an elementwise kernel over 256 MiB (reads and writes a known byte count), "
                          "to calibrate hardware byte counters")
@@ -385,6 +425,9 @@ def main():
         log("[bench] copy probe: 3 x elementwise neg over 256 MiB (268435456 B read, 268435456 B written)")
 
     import w4a16_bit_matmul_amd as wq
+    if args.sweep:
+        bench_sweep(args.steps)
+        return
     wl, nbytes, copies, t_step, t_single = bench_gemv(args.steps, args.warmup)
     plan = wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group)
     log(f"[bench] decode GEMV: {t_step * 1e6:.2f} us per launch back to back "

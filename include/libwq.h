@@ -86,10 +86,20 @@ typedef enum {
 } wq_scheme;
 
 typedef enum {
-    WQ_PATH_AUTO = 0, /* M < 64: GEMV kernel; M >= 64: MFMA GEMM kernel */
+    WQ_PATH_AUTO = 0, /* M < WQ_AUTO_MFMA_MIN_M: GEMV kernel; otherwise MFMA GEMM kernel */
     WQ_PATH_GEMV = 1, /* force the split-K VALU GEMV kernel (any M) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
+
+/* Smallest M for which WQ_PATH_AUTO runs the MFMA GEMM kernel. */
+#define WQ_AUTO_MFMA_MIN_M 5
+
+/* A product that splits K across workgroups uses a caller-provided workspace:
+ * WQ_WORKSPACE_COUNTER_BYTES bytes of 32-bit counters (one per output tile),
+ * then the fp32 partial sums.  The counter bytes must be zero before a
+ * workspace's first use and every call puts back to zero those it used; the
+ * partial sums are overwritten by each call and need no clearing. */
+#define WQ_WORKSPACE_COUNTER_BYTES 2048
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int wq_version(void);
@@ -182,23 +192,30 @@ int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zp
                int64_t N, int64_t K, int group, int out_dtype, void* W_hat, void* stream);
 
 /* Workspace bytes wq_gemm_w4a16 / wq_gemm_w4a16_ex need for this shape, enough
- * for either kernel family (may be 0).  The GEMV needs one only when it splits
- * K across workgroups (fp32 partial sums plus one counter per row range).
- * Host-only. */
+ * for either kernel family (may be 0).  Either kernel needs one only when it
+ * splits K across workgroups to fill the GPU (fp32 partial sums plus one
+ * counter per output tile): the GEMV for few row blocks, the MFMA GEMM for few
+ * 128-column blocks.  Host-only. */
 size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 
+/* Workspace bytes of the one kernel family `path` (wq_path) selects for this
+ * shape: what wq_gemm_w4a16_ex with that path requires (0 for bad arguments).
+ * Host-only. */
+size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path);
+
 /* y = x * What^T with What = s * (q - z) dequantized inside the kernel -- the
- * fused weight-only matmul of "Hardware, formats and the roofline".  M < 64
- * runs the split-K GEMV kernel, M >= 64 the MFMA tile GEMM kernel.
+ * fused weight-only matmul of "Hardware, formats and the roofline".  M below
+ * WQ_AUTO_MFMA_MIN_M runs the split-K GEMV kernel, larger M the MFMA tile
+ * GEMM kernel (which also splits K when its grid is small).
  *   x_f16     [M][K] fp16, 16-byte aligned, finite
  *   qpacked   tile-layout codes, 16-byte aligned; s_f16 [N][G]; zpacked [N][ceil(G/2)]
  *   y_f16     [M][N] fp16 output, 2-byte aligned
  *   workspace at least wq_gemm_workspace_bytes(M, N, K, group) bytes of device
- *             memory, 256-byte aligned and zero-filled before its first use;
- *             may be NULL when that size is 0.  Every call leaves the bytes it
- *             used zero-filled again, so one workspace can serve later calls of
- *             any shape without clearing; calls that may run concurrently need
- *             separate workspaces.
+ *             memory, 256-byte aligned, its first WQ_WORKSPACE_COUNTER_BYTES
+ *             bytes zero before its first use; may be NULL when that size is
+ *             0.  Every call leaves those counter bytes zero again, so one
+ *             workspace serves later calls of any shape without clearing;
+ *             calls that may run concurrently need separate workspaces.
  * Results are deterministic (fixed summation order). */
 int wq_gemm_w4a16(int64_t M, int64_t N, int64_t K, int group,
                   const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,
@@ -280,8 +297,9 @@ size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
 
 /* y = x * What^T with What = s * q dequantized inside the kernel (the
  * weight-only product of "Hardware, formats and the roofline" with 8-bit
- * weights): M < 64 the split-K GEMV, M >= 64 the MFMA tile GEMM.  Arguments,
- * workspace contract, alignment, determinism and errors as wq_gemm_w4a16,
+ * weights): M < WQ_AUTO_MFMA_MIN_M the split-K GEMV, else the MFMA tile
+ * GEMM.  Arguments, workspace contract, alignment, determinism and errors as
+ * wq_gemm_w4a16,
  * without zero-points. */
 int wq_gemm_w8a16(int64_t M, int64_t N, int64_t K, int group,
                   const uint16_t* x_f16, const uint8_t* qpacked, const uint16_t* s_f16,
@@ -333,9 +351,9 @@ int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int6
  * wq_gemm_workspace_bytes at group 32).  Host-only. */
 size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV (M < 64)
- * sums exact E2M1 values times x per block in fp32 and applies the block's
- * power of two in fp32 (exact for every e8); the MFMA GEMM (M >= 64) takes fp16
+/* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV
+ * (M < WQ_AUTO_MFMA_MIN_M) sums exact E2M1 values times x per block in fp32 and applies the block's
+ * power of two in fp32 (exact for every e8); the MFMA GEMM (larger M) takes fp16
  * operands fp16(E2M1 * 2^(e8 - 127)), exact while the block exponent lies in
  * [-23, 13] (outside, the operand rounds to fp16's range).  Arguments,
  * workspace contract and errors as wq_gemm_w4a16 with e8 for the scales and no

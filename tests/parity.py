@@ -71,7 +71,7 @@ FLOOR_MFMA = 5e-2
 
 
 def floor_for(path, M):
-    mfma = path == wq.WQ_PATH_MFMA or (path == wq.WQ_PATH_AUTO and M >= 64)
+    mfma = path == wq.WQ_PATH_MFMA or (path == wq.WQ_PATH_AUTO and M >= wq.WQ_AUTO_MFMA_MIN_M)
     return FLOOR_MFMA if mfma else FLOOR_GEMV
 
 

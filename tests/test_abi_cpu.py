@@ -99,20 +99,32 @@ def test_gemm_validation():
 
 
 def test_workspace_query_and_check():
-    # host-only: the GEMV asks for a workspace when it splits K across
-    # workgroups (few row blocks, or an x slab too large for LDS); the decode
-    # workload (M=1, N=K=8192) runs without one
-    assert wq.wq_gemm_workspace_bytes(1, 8192, 8192, 128) == 0
+    # host-only: either kernel family asks for a workspace when it splits K
+    # across workgroups to fill the GPU (few row or column blocks); the
+    # query covers both families (the M=128, N=28672 GEMM splits nothing)
+    assert wq.wq_gemm_workspace_bytes(128, 28672, 8192, 128) == 0
     for M, N, K, g in [(1, 1024, 8192, 32), (8, 1024, 8192, 128), (1, 48, 8192, 128), (16, 64, 8192, 32)]:
-        need = wq.wq_gemm_workspace_bytes(M, N, K, g)
-        assert need > 0, (M, N, K, g)
-        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, None, 0, wq.WQ_PATH_GEMV, None)
-        assert st == wq.WQ_EWORKSPACE
-        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, A, need - 1, wq.WQ_PATH_GEMV, None)
-        assert st == wq.WQ_EWORKSPACE
-        st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, wq.WQ_PATH_GEMV, None)
-        assert st == wq.WQ_EALIGN
+        for path in (wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA):
+            need = wq.wq_gemm_workspace_bytes(M, N, K, g, path)
+            assert 0 < need <= wq.wq_gemm_workspace_bytes(M, N, K, g), (M, N, K, g, path)
+            # counter region, then KS fp32 partial-sum planes padded to whole
+            # tiles: GEMV MT x 16 per workgroup, MFMA 16*MB x 128
+            plan = wq.wq_gemm_plan(M, N, K, g, path)
+            gx, gy, ks = (int(v) for v in plan.split("grid=(", 1)[1].split(")", 1)[0].split(","))
+            if path == wq.WQ_PATH_GEMV:
+                rows, cols = int(plan.split("MT=", 1)[1].split(",")[0]), 16
+            else:
+                rows, cols = 16 * int(plan.split("MB=", 1)[1].split(",")[0]), 128
+            assert gy * rows >= M and gx * cols >= N
+            assert need == wq.WQ_WORKSPACE_COUNTER_BYTES + ks * gy * rows * gx * cols * 4, (M, N, K, g, path, plan)
+            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, None, 0, path, None)
+            assert st == wq.WQ_EWORKSPACE
+            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, A, need - 1, path, None)
+            assert st == wq.WQ_EWORKSPACE
+            st = call("wq_gemm_w4a16_ex", M, N, K, g, A, A, A, A, A, B, need, path, None)
+            assert st == wq.WQ_EALIGN
     assert wq.wq_gemm_workspace_bytes(0, 16, 128, 128) == 0
+    assert wq.wq_gemm_workspace_bytes(1, 16, 128, 128, 9) == 0
 
 
 def test_gemm_plan_names_the_dispatched_kernel():
@@ -125,7 +137,26 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128>") and "grid=(224,1,1)" in d, d
     assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
+    # a small grid splits K across workgroups in whole eight-tile chunks
+    d = wq.wq_gemm_plan(128, 8192, 8192, 128)
+    assert "grid=(64,1,4)" in d and "split_k=4" in d, d
+    d = wq.wq_gemm_plan(32, 1024, 8192, 32, wq.WQ_PATH_MFMA)
+    assert "grid=(8,1,8)" in d and "split_k=8" in d, d
+    assert "split_k=1" in wq.wq_gemm_plan(128, 28672, 8192, 128)
     assert "split_k=1" not in wq.wq_gemm_plan(1, 48, 8192, 128)
+    # AUTO switches from the GEMV to the MFMA GEMM at WQ_AUTO_MFMA_MIN_M rows,
+    # the same value in the header and the binding
+    m = re.search(r"#define WQ_AUTO_MFMA_MIN_M (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == wq.WQ_AUTO_MFMA_MIN_M
+    m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
+    lo = wq.WQ_AUTO_MFMA_MIN_M
+    assert wq.wq_gemm_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel"), lo
+    assert wq.wq_gemm_plan(lo, 8192, 8192, 128).startswith("gemm_kernel"), lo
+    assert wq.wq_gemm_w8a16_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel")
+    assert wq.wq_gemm_w8a16_plan(lo, 8192, 8192, 128).startswith("gemm_kernel")
+    assert wq.wq_gemm_mxfp4_plan(lo - 1, 8192, 8192).startswith("gemv_kernel")
+    assert wq.wq_gemm_mxfp4_plan(lo, 8192, 8192).startswith("gemm_kernel")
     buf = ctypes.create_string_buffer(8)
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, buf, 8) == wq.WQ_OK and len(buf.value) == 7
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, None, 8) == wq.WQ_EINVAL
@@ -192,8 +223,8 @@ def test_w8_entry_points_checked_on_host():
     assert call(g, 1, 16, 100, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
     assert call(g, 1, 16, 128, 128, A, B, A, A, None, 0, 0, None) == wq.WQ_EALIGN
     assert call("wq_gemm_w8a16", 1, 16, 128, 128, B, A, A, A, None, 0, None) == wq.WQ_EALIGN
-    need = wq.wq_gemm_w8a16_workspace_bytes(1, 1024, 8192, 32)
-    assert need == wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32) > 0
+    assert wq.wq_gemm_w8a16_workspace_bytes(1, 1024, 8192, 32) == wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32) > 0
+    need = wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32, wq.WQ_PATH_GEMV)  # the same launch plan as the INT4 GEMV
     assert call(g, 1, 1024, 8192, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
     assert call(g, 1, 1024, 8192, 32, A, A, A, A, A, need - 1, 0, None) == wq.WQ_EWORKSPACE
 

@@ -53,13 +53,13 @@ def test_workload_full_size(name):
     torch.cuda.synchronize()
     y_host = y.float().cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(wl.x_seed)
-    floor = FLOOR_MFMA if wl.M >= 64 else FLOOR_GEMV
+    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
     for n0, cnt in _sample_ranges(wl.N, rng):
         ref = oracle.gemm_rows_f64(x, q, s, z, wl.group, n0, cnt)
         nw, ew = compare_y(torch.from_numpy(y_host[:, n0:n0 + cnt]), ref, floor_frac=floor)
     say(f"  last sample: normwise {nw:.2e} elementwise {ew:.2e}")
-    if ws is not None:  # the workspace is left zero-filled and reusable: same result again
-        assert int(ws.count_nonzero()) == 0
+    if ws is not None:  # the counters are left zero and the workspace reusable: same result again
+        assert int(ws[:wq.WQ_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
         y2 = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y, y2)

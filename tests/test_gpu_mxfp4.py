@@ -155,7 +155,7 @@ def test_mxfp4_workload_full_size(name):
     torch.cuda.synchronize()
     y_host = y.float().cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(wl.x_seed + 7)
-    floor = FLOOR_MFMA if wl.M >= 64 else FLOOR_GEMV
+    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
     for n0 in sorted(set([0, wl.N - 8] + list(rng.integers(0, wl.N - 8, 6)))):
         ref = oracle.gemm_rows_mxfp4_f64(x, q, e8, int(n0), 8)
         nw, ew = compare_y(torch.from_numpy(y_host[:, n0:n0 + 8]), ref, floor_frac=floor)

@@ -248,13 +248,15 @@ def test_grid_exact_weights_reduce_to_fp16_gemm(path):
 
 def test_split_k_workspace_is_reusable():
     """Split-K GEMV calls of different shapes share one workspace without
-    clearing it in between (each call leaves it zero-filled), and give the same
-    bytes as calls with a fresh zero-filled workspace."""
+    clearing it in between (each call puts its counters back to zero; the
+    partial sums, here pre-filled with NaN bytes, need no clearing), and give
+    the same bytes as calls with a fresh zero-filled workspace."""
     say("split-K workspace reuse")
     cases = [(1, 48, 8192, 128), (5, 100, 8192, 32), (2, 1000, 8192, 128), (1, 48, 8192, 128)]
     need = max(wq.wq_gemm_workspace_bytes(M, N, K, g) for M, N, K, g in cases)
     assert need > 0
     shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    shared[wq.WQ_WORKSPACE_COUNTER_BYTES:] = 0xFF  # partial sums: NaN bytes, never read before written
     for i, (M, N, K, g) in enumerate(cases):
         W, x = _matmul_inputs(M, N, K, g, 600 + i)
         out = gpu_quantize(W, "bf16", g)
@@ -264,7 +266,35 @@ def test_split_k_workspace_is_reusable():
         y_fresh = wq.wq_gemm_w4a16(xd, out["qw"], workspace=fresh, path=wq.WQ_PATH_GEMV)
         torch.cuda.synchronize()
         assert torch.equal(y_shared, y_fresh), (M, N, K, g)
-        assert int(shared.count_nonzero()) == 0 and int(fresh.count_nonzero()) == 0
+        ctr = wq.WQ_WORKSPACE_COUNTER_BYTES
+        assert int(shared[:ctr].count_nonzero()) == 0 and int(fresh[:ctr].count_nonzero()) == 0
+
+
+def test_mfma_split_k_workspace_is_reusable():
+    """MFMA calls whose grid splits K across workgroups (few 128-column blocks)
+    share one workspace across shapes without clearing it (partial sums
+    pre-filled with NaN bytes), match calls with a fresh zero-filled workspace
+    bit for bit, and leave the counters zero."""
+    say("MFMA split-K workspace reuse")
+    cases = [(8, 256, 8192, 128), (128, 1024, 8192, 32), (70, 300, 4224, 128), (16, 48, 2048, 32), (8, 256, 8192, 128)]
+    for M, N, K, g in cases:
+        assert "split_k=1" not in wq.wq_gemm_plan(M, N, K, g, wq.WQ_PATH_MFMA), (M, N, K, g)
+    need = max(wq.wq_gemm_workspace_bytes(M, N, K, g) for M, N, K, g in cases)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    shared[wq.WQ_WORKSPACE_COUNTER_BYTES:] = 0xFF  # partial sums: NaN bytes, never read before written
+    for i, (M, N, K, g) in enumerate(cases):
+        W, x = _matmul_inputs(M, N, K, g, 640 + i)
+        out = gpu_quantize(W, "bf16", g)
+        xd = to_dev_f16(x)
+        y_shared = wq.wq_gemm_w4a16(xd, out["qw"], workspace=shared, path=wq.WQ_PATH_MFMA)
+        fresh = torch.zeros(wq.wq_gemm_workspace_bytes(M, N, K, g), dtype=torch.uint8, device="cuda")
+        y_fresh = wq.wq_gemm_w4a16(xd, out["qw"], workspace=fresh, path=wq.WQ_PATH_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(y_shared, y_fresh), (M, N, K, g)
+        ctr = wq.WQ_WORKSPACE_COUNTER_BYTES
+        assert int(shared[:ctr].count_nonzero()) == 0 and int(fresh[:ctr].count_nonzero()) == 0
+        q, s, z = oracle.quantize_groups(W, g, dtype=oracle.BF16)
+        compare_y(y_shared, oracle.gemm_f64(x, oracle.dequant(q, s, z, g)), floor_frac=floor_for(wq.WQ_PATH_MFMA, M))
 
 
 def test_repeated_calls_are_deterministic():

@@ -209,7 +209,7 @@ def test_w8_workload_full_size(name):
     torch.cuda.synchronize()
     y_host = y.float().cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(wl.x_seed + 5)
-    floor = FLOOR_MFMA if wl.M >= 64 else FLOOR_GEMV
+    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
     starts = sorted(set([0, wl.N - 8] + list(rng.integers(0, wl.N - 8, 6))))
     for n0 in starts:
         ref = oracle.gemm_rows_w8_f64(x, q, s, wl.group, int(n0), 8)

@@ -22,11 +22,13 @@ WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_ASYM, WQ_SYM = 0, 1
+WQ_AUTO_MFMA_MIN_M = 5  # smallest M that WQ_PATH_AUTO runs on the MFMA GEMM kernel
+WQ_WORKSPACE_COUNTER_BYTES = 2048  # leading counter bytes of a split-K workspace (zero before first use)
 
 EXPORTED = (
     "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_quantize_groups_ex", "wq_pack_int4",
     "wq_dequant",
-    "wq_gemm_workspace_bytes", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
+    "wq_gemm_workspace_bytes", "wq_gemm_workspace_bytes_ex", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
     "wq_layout_bytes_w8", "wq_quantize_w8", "wq_pack_int8", "wq_dequant_w8", "wq_gemm_w8a16_workspace_bytes",
     "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
     "wq_kv_layout_bytes", "wq_kv_quantize", "wq_kv_dequant",
@@ -63,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "wq_pack_int4": (I, [P, P, I64, I64, I, P, P, P]),
         "wq_dequant": (I, [P, P, P, I64, I64, I, I, P, P]),
         "wq_gemm_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "wq_gemm_workspace_bytes_ex": (SZ, [I64, I64, I64, I, I]),
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, ctypes.c_char_p, SZ]),
         "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
         "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
@@ -140,8 +143,12 @@ def wq_layout_bytes(N: int, K: int, group: int):
     return q.value, s.value, z.value
 
 
-def wq_gemm_workspace_bytes(M: int, N: int, K: int, group: int) -> int:
-    return int(lib().wq_gemm_workspace_bytes(M, N, K, group))
+def wq_gemm_workspace_bytes(M: int, N: int, K: int, group: int, path: int | None = None) -> int:
+    """Workspace bytes for either kernel family (path None), or for the one
+    family `path` selects."""
+    if path is None:
+        return int(lib().wq_gemm_workspace_bytes(M, N, K, group))
+    return int(lib().wq_gemm_workspace_bytes_ex(M, N, K, group, path))
 
 
 def wq_gemm_plan(M: int, N: int, K: int, group: int, path: int = WQ_PATH_AUTO) -> str:

@@ -8,6 +8,15 @@
 #include "wq_device.h"
 #include "wq_kernels.h"
 
+static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K counter region size");
+
+// Kernel family for a product: WQ_PATH_AUTO takes the MFMA tile GEMM from
+// WQ_AUTO_MFMA_MIN_M rows on (with split K it beats the GEMV from there on
+// MI355X, whose per-row VALU work grows with M), the GEMV below.
+static bool auto_mfma(int64_t M, int path) {
+  return path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= WQ_AUTO_MFMA_MIN_M);
+}
+
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
@@ -123,6 +132,13 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
   return a > b ? a : b;
 }
 
+size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path) {
+  if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return 0;
+  const bool mfma = auto_mfma(M, path);
+  return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
+}
+
 int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len) {
   if (!buf || buf_len == 0) return WQ_EINVAL;
   buf[0] = 0;
@@ -130,7 +146,7 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  const bool mfma = auto_mfma(M, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 4, buf, buf_len);
   else
@@ -153,7 +169,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
   int st = check_shape(N, K, group);
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
-  *mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  *mfma = auto_mfma(M, path);
   const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
@@ -278,7 +294,7 @@ int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, cha
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  const bool mfma = auto_mfma(M, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 8, buf, buf_len);
   else
@@ -400,7 +416,7 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  const bool mfma = path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= 64);
+  const bool mfma = auto_mfma(M, path);
   if (mfma)
     wq::describe_gemm(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
   else

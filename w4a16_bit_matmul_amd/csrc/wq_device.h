@@ -112,4 +112,43 @@ __device__ __forceinline__ uint32_t load_zero(const uint8_t* zpacked, int64_t GB
   return (gi & 1) ? (b >> 4) : (b & 15u);
 }
 
+// ---- Split-K hand-off between the workgroups that share one output tile.
+// The workspace starts with a fixed counter region (one 32-bit counter per
+// output tile; a split launch never has more than kSplitMaxTiles tiles) and
+// holds the fp32 partial sums after it.  Counters start at zero and the last
+// workgroup of a tile puts its counter back to zero, so one zero-filled
+// workspace serves later launches of any shape; the partial sums are fully
+// overwritten by every launch and need no clearing.
+constexpr int kSplitMaxTiles = 512;
+constexpr size_t kSplitCounterBytes = kSplitMaxTiles * sizeof(unsigned);
+
+// Partial sums travel through device-scope relaxed atomic stores and loads
+// (cache-coherent across the chiplets' separate L2 caches), so no whole-cache
+// write-back or invalidate is needed: a workgroup's stores are complete before
+// its counter increment (waitcnt + barrier below), and the last workgroup
+// issues its loads only after its own increment has returned.
+__device__ __forceinline__ void split_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float split_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of the workgroup after its split_store calls; true in
+// the workgroup that arrives last at counter `ctr` (of KS arrivals).
+__device__ __forceinline__ bool split_arrive(unsigned* ctr, int KS) {
+  __shared__ unsigned last;
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(KS - 1);
+  __syncthreads();
+  return last != 0;
+}
+
+// The last workgroup of a tile resets its counter for the next launch.
+__device__ __forceinline__ void split_reset(unsigned* ctr) {
+  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace wq

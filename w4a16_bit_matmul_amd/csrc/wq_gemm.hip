@@ -44,9 +44,14 @@
 // and every load stays in flight until its first use; barriers order LDS only
 // (__syncthreads() on gfx9 would also wait for every outstanding global load).
 // At the end the second step pair's sums are added to the first pair's
-// through LDS, in a fixed order.
+// through LDS, in a fixed order.  A grid too small to fill the GPU (few
+// 128-column blocks) splits K across workgroups in runs of whole eight-tile
+// chunks: each split writes fp32 partial sums to the workspace, and the last
+// workgroup of an output tile (a device-scope counter) adds them in split order,
+// writes y and puts the counter back to zero.
 #include <stdio.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "wq_device.h"
@@ -65,7 +70,9 @@ struct GemmArgs {
   const uint16_t* s;
   const uint8_t* zp;
   uint16_t* y;
-  int M, N, K, KT, Gtot, GB, NBLK;
+  float* partial;      // [KS][M][N] fp32 (KS > 1 only)
+  unsigned* counters;  // [gridDim.y][gridDim.x] (KS > 1 only)
+  int M, N, K, KT, Gtot, GB, NBLK, kt_per_split, KS;
 };
 
 // Workgroup barrier that orders LDS only.
@@ -281,19 +288,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int b = 0; b < NPW; ++b) acc[i][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: activations of tile 0 (in LDS) and tile 1 (in registers),
-  // codes of tiles 0..2, scales / zero-points of the first chunk
+  // this workgroup's K tiles [kt_lo, kt_hi): all of K, or one split (kt_lo a
+  // multiple of the eight-tile chunk)
+  const int kt_lo = blockIdx.z * a.kt_per_split;
+  const int kt_hi = min(KT, kt_lo + a.kt_per_split);
+
+  // ---- prologue: activations of the first tile (in LDS) and the second (in
+  // registers), codes of the first three tiles, scales / zero-points of the
+  // first chunk
   CodeT b0[NPW], b1[NPW], b2[NPW], b3[NPW];
   u4 xs0[XCH], xs1[XCH];
   SzStage szs;
-  load_x(0, xs0);
-  load_x(1, xs1);
-  load_b(0, b0);
-  load_b(1, b1);
-  load_b(2, b2);
-  sz_load(0, szs);
-  store_x(0, xs0);
-  sz_store(0, szs);
+  load_x(kt_lo, xs0);
+  load_x(kt_lo + 1, xs1);
+  load_b(kt_lo, b0);
+  load_b(kt_lo + 1, b1);
+  load_b(kt_lo + 2, b2);
+  sz_load(kt_lo / kSzChunk, szs);
+  store_x(kt_lo, xs0);
+  sz_store(kt_lo / kSzChunk, szs);
   lds_barrier();
 
   // this lane's A reads: row r of block i, chunk 4j + c at slot (4j + c) ^ r;
@@ -368,8 +381,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // whole tiles in groups of eight (two turns of the code ring, four of the
   // activation registers); the next chunk's scales / zero-points are loaded
   // at step 1 and stored at step 5
-  const int kt_full = (a.K / 128) & ~(kSzChunk - 1);
-  int kt = 0;
+  const int kt_full = kt_lo + ((min(kt_hi, a.K / 128) - kt_lo) & ~(kSzChunk - 1));
+  int kt = kt_lo;
   for (; kt < kt_full; kt += kSzChunk) {
     const int ch = kt / kSzChunk;
     step(Full{}, kt, xs0, xs1, b0, b3);
@@ -385,11 +398,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   }
   // the rest (fewer than eight tiles, the last one possibly ragged); their
   // chunk was staged during the previous chunk or before the loop
-  for (; kt < KT; kt += 4) {
+  for (; kt < kt_hi; kt += 4) {
     step(Part{}, kt, xs0, xs1, b0, b3);
-    if (kt + 1 < KT) step(Part{}, kt + 1, xs1, xs0, b1, b0);
-    if (kt + 2 < KT) step(Part{}, kt + 2, xs0, xs1, b2, b1);
-    if (kt + 3 < KT) step(Part{}, kt + 3, xs1, xs0, b3, b2);
+    if (kt + 1 < kt_hi) step(Part{}, kt + 1, xs1, xs0, b1, b0);
+    if (kt + 2 < kt_hi) step(Part{}, kt + 2, xs0, xs1, b2, b1);
+    if (kt + 3 < kt_hi) step(Part{}, kt + 3, xs1, xs0, b3, b2);
   }
 
   // ---- add the second step pair's sums to the first's (LDS reused), then
@@ -405,23 +418,82 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         for (int e = 0; e < 4; ++e) red[(cgp * NACC + (i * NPW + b) * 4 + e) * 64 + lane] = acc[i][b][e];
   }
   lds_barrier();
-  if (jp == 1) return;
+  if (jp == 0) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int b = 0; b < NPW; ++b) {
-      const int n = (nbw0 + b) * 16 + r;
+      for (int b = 0; b < NPW; ++b) {
+        const int n = (nbw0 + b) * 16 + r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = acc[i][b][e] + red[(cgp * NACC + (i * NPW + b) * 4 + e) * 64 + lane];
-        const int m = mrow0 + 16 * i + 4 * c + e;
-        if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v);
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[i][b][e] + red[(cgp * NACC + (i * NPW + b) * 4 + e) * 64 + lane];
+          const int m = mrow0 + 16 * i + 4 * c + e;
+          if (a.KS > 1)  // padded plane: every element of the tile is inside it
+            split_store(a.partial + ((size_t)blockIdx.z * gridDim.y * ROWS + m) * (gridDim.x * 128) + n, v);
+          else if (n < a.N && m < a.M)
+            a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v);
+        }
       }
+  }
+  if (a.KS == 1) return;
+
+  // ---- split K: the last workgroup of this output tile adds the partial sums
+  unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
+  if (!split_arrive(ctr, a.KS)) return;
+  {
+    // every thread sums, in split order, one column of the tile at rows
+    // row0 + 4j: consecutive threads read consecutive columns (coalesced) and
+    // a thread's loads differ by a uniform stride, all in flight together
+    constexpr int RPP = NTH / 128, PER = ROWS / RPP;  // rows per pass, elements per thread
+    const int col = tid & 127, row0 = tid / 128;
+    const size_t Np = (size_t)gridDim.x * 128, plane = (size_t)gridDim.y * ROWS * Np;
+    const float* base = a.partial + (size_t)(mrow0 + row0) * Np + blockIdx.x * 128 + col;
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = 0.0f;
+    for (int k2 = 0; k2 < a.KS; ++k2) {
+      float t[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) t[j] = split_load(base + k2 * plane + (size_t)(RPP * j) * Np);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[j] += t[j];
     }
+    const int n = blockIdx.x * 128 + col;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int m = mrow0 + row0 + RPP * j;
+      if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v[j]);
+    }
+  }
+  if (tid == 0) split_reset(ctr);
 }
 
 // Row blocks per workgroup for a problem of M rows.
 int gemm_mb(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+
+// Launch shape: (128-column blocks, 16*MB-row blocks, K splits).  A grid of
+// fewer than 192 workgroups splits K so that about 256 run (one per CU), in
+// runs of whole eight-tile chunks.
+struct GemmPlan {
+  int MB, KS, kt_per_split;
+  unsigned gx, gy;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p;
+  p.MB = gemm_mb(M);
+  p.gx = (unsigned)(((N + 15) / 16 + 7) / 8);
+  p.gy = (unsigned)((M + 16 * p.MB - 1) / (16 * p.MB));
+  const int KT = (int)((K + 127) / 128);
+  const int64_t wgs = (int64_t)p.gx * p.gy;
+  int ks = 1;
+  if (wgs < 192 && wgs <= kSplitMaxTiles)
+    ks = (int)std::min<int64_t>((256 + wgs - 1) / wgs, std::max(1, KT / kSzChunk));
+  p.kt_per_split = (KT + ks - 1) / ks;
+  p.kt_per_split = (p.kt_per_split + kSzChunk - 1) / kSzChunk * kSzChunk;
+  p.KS = (KT + p.kt_per_split - 1) / p.kt_per_split;
+  return p;
+}
 
 dim3 gemm_grid(int MB, int64_t M, int64_t N) {
   return dim3((unsigned)(((N + 15) / 16 + 7) / 8), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
@@ -440,7 +512,7 @@ size_t gemm_lds(int MB, int group, int fmt) {
 
 template <int MB, int G, bool SZV, int FMT>
 hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid = gemm_grid(MB, a.M, a.N), block(kWaves * 64);
+  const dim3 g2 = gemm_grid(MB, a.M, a.N), grid(g2.x, g2.y, (unsigned)a.KS), block(kWaves * 64);
   const size_t lds = gemm_lds(MB, G, FMT);
   auto k = gemm_kernel<MB, G, SZV, FMT>;
   if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -470,20 +542,33 @@ hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  if (p.KS == 1) return 0;
+  // partial-sum planes padded to whole tiles: [KS][gy * 16 * MB][gx * 128]
+  return kSplitCounterBytes + (size_t)p.KS * p.gy * 16 * p.MB * p.gx * 128 * sizeof(float);
+}
 
-int describe_gemm(int64_t M, int64_t N, int64_t, int group, int fmt, char* buf, size_t len) {
-  const int MB = gemm_mb(M);
-  const dim3 g = gemm_grid(MB, M, N);
-  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d%s> grid=(%u,%u,1) block=%d lds=%zu", MB, kNPW, group,
-                  fmt == kFmtInt8 ? ", BITS=8" : fmt == kFmtMxfp4 ? ", MXFP4" : "", g.x, g.y, kWaves * 64,
-                  gemm_lds(MB, group, fmt));
+int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d%s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d", p.MB,
+                  kNPW, group, fmt == kFmtInt8 ? ", BITS=8" : fmt == kFmtMxfp4 ? ", MXFP4" : "", p.gx, p.gy, p.KS,
+                  kWaves * 64, gemm_lds(p.MB, group, fmt), p.KS);
 }
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* /*workspace*/,
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream) {
+  const GemmPlan p = plan_gemm(M, N, K);
   GemmArgs a;
+  a.KS = p.KS;
+  a.kt_per_split = p.kt_per_split;
+  a.partial = nullptr;
+  a.counters = nullptr;
+  if (p.KS > 1) {
+    a.counters = static_cast<unsigned*>(workspace);
+    a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
+  }
   a.x = x;
   a.qp = static_cast<const uint8_t*>(qpacked);
   a.s = s;

@@ -45,8 +45,8 @@
 // partial sums meet in LDS in a fixed order.  When the grid splits K, each
 // workgroup writes fp32 partial sums to the workspace and the last workgroup of
 // a row range (found with a device-scope atomic counter) adds them in split
-// order and writes y, so results stay deterministic; it then zeroes the partial
-// sums and the counter, leaving the whole workspace zero for the next call.
+// order and writes y, so results stay deterministic; it then puts the counter
+// back to zero for the next call.
 #include <stdio.h>
 
 #include "wq_device.h"
@@ -329,38 +329,35 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     for (int w = 0; w < W; ++w) v += red[w * NOUT + i];
     const int rr = i & 15, m = i >> 4;
     const int nn = nb * 16 + rr, mm = m0 + m;
-    if (nn < a.N && mm < a.M) {
-      if (a.KS == 1)
-        a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
-      else
-        a.partial[((size_t)ks * a.M + mm) * a.N + nn] = v;
-    }
+    if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
+      split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
+    else if (nn < a.N && mm < a.M)
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
   }
   if (a.KS == 1) return;
 
   // ---- split-K: the last workgroup of this row range adds the partial sums
-  __shared__ unsigned last;
-  __threadfence();
-  __syncthreads();
   unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
-  if (tid == 0) last = (atomicAdd(ctr, 1u) == (unsigned)(a.KS - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (!split_arrive(ctr, a.KS)) return;
   for (int i = tid; i < NOUT; i += NT) {
     const int rr = i & 15, m = i >> 4;
     const int nn = nb * 16 + rr, mm = m0 + m;
     if (nn < a.N && mm < a.M) {
+      const float* pp = a.partial + (size_t)mm * (gridDim.x * 16) + nn;
+      const size_t plane = (size_t)gridDim.y * MT * gridDim.x * 16;
       float v = 0.0f;
-      for (int k2 = 0; k2 < a.KS; ++k2) {
-        float* pp = a.partial + ((size_t)k2 * a.M + mm) * a.N + nn;
-        v += *pp;
-        *pp = 0.0f;  // the workspace is left zero-filled for the next call, whatever its shape
+      for (int k0 = 0; k0 < a.KS; k0 += 4) {  // four loads in flight, added in split order
+        float t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = split_load(pp + (size_t)min(k0 + j, a.KS - 1) * plane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + j < a.KS) v += t[j];
       }
       a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
     }
   }
-  if (tid == 0) *ctr = 0u;
+  if (tid == 0) split_reset(ctr);
 }
 
 // Launch shape of the GEMV for one problem; shared by the launcher and the
@@ -385,6 +382,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   int64_t ks = 1;
   const int64_t wgs = (int64_t)p.gx * p.gy, pass = (int64_t)p.W * kKQ;
   while (wgs * ks < 512 && KT / (ks * 2) >= pass / 2) ks *= 2;
+  if (wgs > kSplitMaxTiles) ks = 1;  // (never taken: a split grid has < 512 row ranges)
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
@@ -428,9 +426,8 @@ int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
   const GemvPlan p = plan_gemv(M, N, K);
   if (p.KS == 1) return 0;
-  const size_t part = (size_t)p.KS * M * N * sizeof(float);
-  const size_t part_al = (part + 255) / 256 * 256;
-  return part_al + (size_t)p.gx * p.gy * sizeof(unsigned);
+  // partial-sum planes padded to whole tiles: [KS][gy * MT][gx * 16]
+  return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * 16 * sizeof(float);
 }
 
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
@@ -468,9 +465,8 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   a.partial = nullptr;
   a.counters = nullptr;
   if (p.KS > 1) {
-    const size_t part = (size_t)p.KS * M * N * sizeof(float);
-    a.partial = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
+    a.counters = static_cast<unsigned*>(workspace);
+    a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
   }
   if (p.MT == 1) return launch_t<1, 16>(p, group, fmt, a, stream);
   if (p.MT == 2) return launch_t<2, 16>(p, group, fmt, a, stream);
