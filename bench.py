@@ -325,6 +325,77 @@ def bench_sweep(steps):
         print(json.dumps(rec), flush=True)
 
 
+def bench_read_ceiling(nbytes, steps, warmup):
+    """The streaming-read probe on the decode GEMV's byte count (rounded up to
+    256), rotating over >= 512 MB so that every launch reads HBM: the best of
+    4, 8 and 16 16-byte loads per thread.  Each timed run is one C call that
+    issues every launch, so the host never gaps the GPU."""
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    window = (nbytes + 255) // 256 * 256
+    nwin = max(2, math.ceil(ROTATE_BYTES / window))
+    buf = torch.ones(window * nwin // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for chunks in (4, 8, 16):
+        wq.wq_read_probe(buf, window, warmup, chunks=chunks, sink=sink)
+        t = _time_calls(lambda i: wq.wq_read_probe(buf, window, steps, chunks=chunks, sink=sink), 1, 0) / steps
+        if best is None or t < best[0]:
+            best = (t, chunks)
+    del buf
+    t, chunks = best
+    return {"bytes_per_launch": window, "us_per_launch": round(t * 1e6, 3), "gbs": round(window / t / 1e9, 2),
+            "frac_hbm_peak": round(window / t / 1e9 / HBM_PEAK_GBS, 4), "loads_per_thread": chunks,
+            "windows_rotated": nwin}
+
+
+def bench_configs(steps):
+    """Every workload (the tiny case, decode, the M=16 up-projection, the M=128
+    GEMM and the g=32 sweep of 70B layer shapes) on the kernel WQ_PATH_AUTO
+    picks: time per launch from one wq_gemm_w4a16_seq call of back-to-back
+    launches (weights rotated over >= 512 MB of copies, at most 128), after one
+    untimed call; effective GB/s and TFLOP/s."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    out = {}
+    qcache = {}
+    for name, wl in workloads.WORKLOADS.items():
+        key = (wl.w_seed, wl.N, wl.K, wl.group, wl.w_dtype)
+        if key not in qcache:
+            qcache.clear()
+            torch.cuda.empty_cache()
+            W = wl.weights()
+            if W.dtype == np.uint16:
+                Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+            else:
+                Wd = torch.from_numpy(W).cuda()
+            qw = wq.wq_quantize_groups(Wd, wl.group)["qw"]
+            del Wd, W
+            copies = min(128, max(2, math.ceil(ROTATE_BYTES / wl.algorithmic_bytes())))
+            qcache[key] = _device_copies(qw, copies)
+        qws = qcache[key]
+        copies = len(qws)
+        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+        ws = _workspace(wl)
+        n = max(steps, copies)
+        run_seq = wq.wq_gemm_w4a16_seq_prepared([xd] * n, [qws[i % copies] for i in range(n)], [y] * n,
+                                                workspace=ws)
+        run_seq()
+        t = _time_calls(lambda i: run_seq(), 1, 0) / n
+        nbytes = wl.algorithmic_bytes()
+        out[name] = {"M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
+                     "kernel": wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group), "us_per_launch": round(t * 1e6, 3),
+                     "algorithmic_bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "tflops": round(wl.flops() / t / 1e12, 2), "weight_copies_rotated": copies}
+        log(f"[bench] {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.0f} GB/s, "
+            f"{wl.flops() / t / 1e12:.1f} TFLOP/s")
+    return out
+
+
 def bench_quantize(wl_name="decode_gemv", reps=20):
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -487,6 +558,9 @@ def main():
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
         line["awq_fold"] = bench_awq()
         line["mxfp4"] = bench_mxfp4(args.steps, args.warmup)
+        line["read_ceiling"] = bench_read_ceiling(nbytes, args.steps, 2000)
+        line["read_ceiling"]["gemv_frac_of_ceiling"] = round(line["read_ceiling"]["us_per_launch"] / (t_step * 1e6), 4)
+        line["configs"] = bench_configs(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

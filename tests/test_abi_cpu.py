@@ -306,3 +306,22 @@ def test_mxfp4_entry_points_checked_on_host():
     assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=32, MXFP4>") and "grid=(512,1,1)" in d, d
     d = wq.wq_gemm_mxfp4_plan(128, 28672, 8192)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=32, MXFP4>") and "grid=(224,1,1)" in d, d
+
+
+def test_read_probe_argument_checks():
+    # host-only: every rejection happens before a launch, and count == 0
+    # enqueues nothing (so fake, aligned pointers are safe here)
+    f = wq.lib().wq_read_probe
+    A, B = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    assert f(A, 1 << 20, 1 << 24, 0, 8, A, None) == wq.WQ_OK
+    assert f(None, 1 << 20, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL
+    assert f(A, 1 << 20, 1 << 24, 1, 8, None, None) == wq.WQ_EINVAL
+    assert f(A, 0, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL
+    assert f(A, 1000, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL            # not a multiple of 256
+    assert f(A, 1 << 20, (1 << 20) - 256, 1, 8, A, None) == wq.WQ_EINVAL  # span smaller than a window
+    assert f(A, 1 << 20, 1 << 24, -1, 8, A, None) == wq.WQ_EINVAL
+    for chunks in (0, 2, 5, 32):
+        assert f(A, 1 << 20, 1 << 24, 1, chunks, A, None) == wq.WQ_EINVAL
+    assert f(B, 1 << 20, 1 << 24, 1, 8, A, None) == wq.WQ_EALIGN
+    assert f(A, 1 << 20, 1 << 24, 1, 8, ctypes.c_void_p((1 << 20) + 2), None) == wq.WQ_EALIGN
+

@@ -35,6 +35,7 @@ EXPORTED = (
     "wq_quantize_groups_scaled", "wq_scale_activations", "wq_channel_absmean",
     "wq_layout_bytes_mxfp4", "wq_quantize_mxfp4", "wq_pack_mxfp4", "wq_dequant_mxfp4",
     "wq_gemm_mxfp4_workspace_bytes", "wq_gemm_mxfp4", "wq_gemm_mxfp4_ex", "wq_gemm_mxfp4_plan",
+    "wq_read_probe",
 )
 
 _lib = None
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_mxfp4": (I, [I64, I64, I64, P, P, P, P, P, SZ, P]),
         "wq_gemm_mxfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_mxfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
+        "wq_read_probe": (I, [P, SZ, SZ, I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -490,3 +492,15 @@ def wq_gemm_mxfp4(x: torch.Tensor, qw: QuantizedWeightMX, *, y: torch.Tensor | N
                                   0 if workspace is None else workspace.numel() * workspace.element_size(), path,
                                   _stream(stream)), "wq_gemm_mxfp4")
     return y
+
+
+def wq_read_probe(src: torch.Tensor, window_bytes: int, count: int, *, chunks: int = 8,
+                  sink: torch.Tensor | None = None, stream=None) -> None:
+    """count streaming reads of window_bytes each, rotating over the bytes of
+    the device tensor src (a measurement aid: the read ceiling for a product
+    whose time is the reading of its weights)."""
+    span = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    _check(lib().wq_read_probe(_ptr(src), window_bytes, span, count, chunks, _ptr(sink), _stream(stream)),
+           "wq_read_probe")

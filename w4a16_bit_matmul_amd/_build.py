@@ -23,6 +23,7 @@ PER_FILE = {
     "wq_quant.hip": ["-ffp-contract=off"],
     "wq_gemv.hip": [],
     "wq_gemm.hip": [],
+    "wq_probe.hip": [],
     "wq_api.cpp": [],
 }
 

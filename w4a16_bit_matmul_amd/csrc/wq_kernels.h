@@ -49,9 +49,9 @@ hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, c
 hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* zp, int64_t T, int64_t hd,
                              const int32_t* slot, int64_t S, int out_dtype, void* out, hipStream_t stream);
 
-// VALU split-K GEMV for small M.  It needs a workspace (fp32 partial sums and
-// counters, zero on entry and left zero) only when it splits K across
-// workgroups; gemv_workspace_bytes gives the size (0 otherwise).
+// VALU split-K GEMV for small M.  It needs a workspace (a counter region that
+// is zero on entry and left zero, then fp32 partial sums) only when it splits K
+// across workgroups; gemv_workspace_bytes gives the size (0 otherwise).
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 // Writes a one-line description of the kernel and launch shape chosen for this
 // problem (snprintf semantics).  fmt (wq_device.h): kFmtInt4 (tile codes +
@@ -67,5 +67,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
+
+// Streaming-read probe: count launches back to back, launch i reading the
+// window_bytes at src + (i mod (span_bytes / window_bytes)) * window_bytes once,
+// with chunks (4, 8 or 16) 16-byte loads per thread.  sink: one device word,
+// written only if a thread's XOR of its words hits a fixed value.
+hipError_t launch_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks,
+                             uint32_t* sink, hipStream_t stream);
 
 }  // namespace wq
