@@ -328,8 +328,8 @@ def bench_sweep(steps):
 def bench_read_ceiling(nbytes, steps, warmup):
     """The streaming-read probe on the decode GEMV's byte count (rounded up to
     256), rotating over >= 512 MB so that every launch reads HBM: the best of
-    4, 8 and 16 16-byte loads per thread.  Each timed run is one C call that
-    issues every launch, so the host never gaps the GPU."""
+    1, 2, 4 and 8 16-byte loads per thread, plain or non-temporal.  Each timed
+    run is one C call that issues every launch, so the host never gaps the GPU."""
     import torch
     import w4a16_bit_matmul_amd as wq
     window = (nbytes + 255) // 256 * 256
@@ -337,16 +337,18 @@ def bench_read_ceiling(nbytes, steps, warmup):
     buf = torch.ones(window * nwin // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     best = None
-    for chunks in (4, 8, 16):
-        wq.wq_read_probe(buf, window, warmup, chunks=chunks, sink=sink)
-        t = _time_calls(lambda i: wq.wq_read_probe(buf, window, steps, chunks=chunks, sink=sink), 1, 0) / steps
-        if best is None or t < best[0]:
-            best = (t, chunks)
+    for nt in (False, True):
+        for chunks in (1, 2, 4, 8):
+            wq.wq_read_probe(buf, window, warmup, chunks=chunks, nontemporal=nt, sink=sink)
+            t = _time_calls(lambda i: wq.wq_read_probe(buf, window, steps, chunks=chunks, nontemporal=nt, sink=sink),
+                            1, 0) / steps
+            if best is None or t < best[0]:
+                best = (t, chunks, nt)
     del buf
-    t, chunks = best
+    t, chunks, nt = best
     return {"bytes_per_launch": window, "us_per_launch": round(t * 1e6, 3), "gbs": round(window / t / 1e9, 2),
             "frac_hbm_peak": round(window / t / 1e9 / HBM_PEAK_GBS, 4), "loads_per_thread": chunks,
-            "windows_rotated": nwin}
+            "nontemporal": nt, "windows_rotated": nwin}
 
 
 def bench_configs(steps):
@@ -423,9 +425,10 @@ def kernel_source_digest():
 
 def measured_traffic():
     """HBM bytes per launch of the decode GEMV from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by the factor a
-    copy kernel of known size gives), or None when that summary is missing or
-    was taken on other kernel sources than the ones built now."""
+    counter summary (L2-to-memory read requests weighted by their size, and
+    WRITE_SIZE, each scaled by the factor a copy kernel of known size gives),
+    or None when that summary is missing or was taken on other kernel sources
+    than the ones built now."""
     try:
         with open(TRAFFIC_PROFILE) as f:
             fields = dict(ln[2:].split(": ", 1) for ln in f.read().splitlines() if ln.startswith("- ") and ": " in ln)
@@ -528,7 +531,8 @@ def main():
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 TCC_EA0_RDREQ_{32B,64B,128B} x size + WRITE_SIZE, "
+                                     "copy-calibrated)",
                      "traffic_over_algorithmic": None if traffic is None else round(traffic / nbytes, 4),
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel": plan,
@@ -558,7 +562,7 @@ def main():
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
         line["awq_fold"] = bench_awq()
         line["mxfp4"] = bench_mxfp4(args.steps, args.warmup)
-        line["read_ceiling"] = bench_read_ceiling(nbytes, args.steps, 2000)
+        line["read_ceiling"] = bench_read_ceiling(nbytes, args.steps, max(1, min(2000, args.warmup)))
         line["read_ceiling"]["gemv_frac_of_ceiling"] = round(line["read_ceiling"]["us_per_launch"] / (t_step * 1e6), 4)
         line["configs"] = bench_configs(args.steps)
     if not args.no_cpu_baseline:

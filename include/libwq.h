@@ -415,17 +415,18 @@ int wq_kv_dequant(const uint8_t* codes, const uint16_t* s_f16, const uint8_t* zp
  * this part, next to the nominal HBM peak.  Issues `count` kernel launches
  * back to back on `stream`; launch i reads the window_bytes bytes at
  * src + (i mod (span_bytes / window_bytes)) * window_bytes, once, with
- * `chunks` (4, 8 or 16) 16-byte loads per thread, and writes nothing to
+ * `chunks` (1, 2, 4, 8 or 16) 16-byte loads per thread, plain (nontemporal
+ * 0) or with the non-temporal streaming hint (1), and writes nothing to
  * memory except, if the XOR of one thread's words equals a fixed 32-bit value,
  * that value to *sink.  Rotating over a span larger than the last-level cache
  * keeps every launch reading from HBM.
  *   src     device memory, 16-byte aligned, span_bytes readable
  *   window_bytes  a positive multiple of 256, at most span_bytes (and 2^40)
  *   sink    one device word, 4-byte aligned
- * WQ_EINVAL for a NULL pointer, a negative count or a bad size or chunk
- * count; WQ_EALIGN for misaligned pointers; count == 0 enqueues nothing. */
+ * WQ_EINVAL for a NULL pointer, a negative count or a bad size, chunk count
+ * or nontemporal flag; WQ_EALIGN for misaligned pointers; count == 0 enqueues nothing. */
 int wq_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks,
-                  uint32_t* sink, void* stream);
+                  int nontemporal, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -313,15 +313,16 @@ def test_read_probe_argument_checks():
     # enqueues nothing (so fake, aligned pointers are safe here)
     f = wq.lib().wq_read_probe
     A, B = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
-    assert f(A, 1 << 20, 1 << 24, 0, 8, A, None) == wq.WQ_OK
-    assert f(None, 1 << 20, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL
-    assert f(A, 1 << 20, 1 << 24, 1, 8, None, None) == wq.WQ_EINVAL
-    assert f(A, 0, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL
-    assert f(A, 1000, 1 << 24, 1, 8, A, None) == wq.WQ_EINVAL            # not a multiple of 256
-    assert f(A, 1 << 20, (1 << 20) - 256, 1, 8, A, None) == wq.WQ_EINVAL  # span smaller than a window
-    assert f(A, 1 << 20, 1 << 24, -1, 8, A, None) == wq.WQ_EINVAL
-    for chunks in (0, 2, 5, 32):
-        assert f(A, 1 << 20, 1 << 24, 1, chunks, A, None) == wq.WQ_EINVAL
-    assert f(B, 1 << 20, 1 << 24, 1, 8, A, None) == wq.WQ_EALIGN
-    assert f(A, 1 << 20, 1 << 24, 1, 8, ctypes.c_void_p((1 << 20) + 2), None) == wq.WQ_EALIGN
-
+    for nt in (0, 1):
+        assert f(A, 1 << 20, 1 << 24, 0, 8, nt, A, None) == wq.WQ_OK
+    assert f(None, 1 << 20, 1 << 24, 1, 8, 0, A, None) == wq.WQ_EINVAL
+    assert f(A, 1 << 20, 1 << 24, 1, 8, 0, None, None) == wq.WQ_EINVAL
+    assert f(A, 0, 1 << 24, 1, 8, 0, A, None) == wq.WQ_EINVAL
+    assert f(A, 1000, 1 << 24, 1, 8, 0, A, None) == wq.WQ_EINVAL            # not a multiple of 256
+    assert f(A, 1 << 20, (1 << 20) - 256, 1, 8, 0, A, None) == wq.WQ_EINVAL  # span smaller than a window
+    assert f(A, 1 << 20, 1 << 24, -1, 8, 0, A, None) == wq.WQ_EINVAL
+    for chunks in (0, 3, 5, 32):
+        assert f(A, 1 << 20, 1 << 24, 1, chunks, 0, A, None) == wq.WQ_EINVAL
+    assert f(A, 1 << 20, 1 << 24, 1, 8, 2, A, None) == wq.WQ_EINVAL
+    assert f(B, 1 << 20, 1 << 24, 1, 8, 0, A, None) == wq.WQ_EALIGN
+    assert f(A, 1 << 20, 1 << 24, 1, 8, 0, ctypes.c_void_p((1 << 20) + 2), None) == wq.WQ_EALIGN

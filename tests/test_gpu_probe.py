@@ -12,9 +12,10 @@ pytestmark = pytest.mark.gpu
 MAGIC = 0x9E3779B9  # the probe's fixed value (a thread's XOR of its words)
 
 
-@pytest.mark.parametrize("chunks", [4, 8, 16])
-def test_read_probe_reads_the_named_windows(chunks):
-    say(f"read probe chunks={chunks}")
+@pytest.mark.parametrize("nontemporal", [False, True])
+@pytest.mark.parametrize("chunks", [1, 2, 4, 8, 16])
+def test_read_probe_reads_the_named_windows(chunks, nontemporal):
+    say(f"read probe chunks={chunks} nontemporal={nontemporal}")
     window = 256 * chunks * 16 * 3  # three workgroups per window
     span_windows = 3
     for target in range(span_windows):
@@ -25,7 +26,7 @@ def test_read_probe_reads_the_named_windows(chunks):
             word = (target * window + 256 * chunks * 16 + 5 * 16) // 4
             buf[word] = MAGIC - (1 << 32)
             sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-            wq.wq_read_probe(buf, window, count, chunks=chunks, sink=sink)
+            wq.wq_read_probe(buf, window, count, chunks=chunks, nontemporal=nontemporal, sink=sink)
             torch.cuda.synchronize()
             read = {i % span_windows for i in range(count)}
             got = int(sink.item()) & 0xFFFFFFFF

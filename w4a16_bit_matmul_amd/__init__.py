@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_mxfp4": (I, [I64, I64, I64, P, P, P, P, P, SZ, P]),
         "wq_gemm_mxfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_mxfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
-        "wq_read_probe": (I, [P, SZ, SZ, I, I, P, P]),
+        "wq_read_probe": (I, [P, SZ, SZ, I, I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -494,7 +494,7 @@ def wq_gemm_mxfp4(x: torch.Tensor, qw: QuantizedWeightMX, *, y: torch.Tensor | N
     return y
 
 
-def wq_read_probe(src: torch.Tensor, window_bytes: int, count: int, *, chunks: int = 8,
+def wq_read_probe(src: torch.Tensor, window_bytes: int, count: int, *, chunks: int = 8, nontemporal: bool = False,
                   sink: torch.Tensor | None = None, stream=None) -> None:
     """count streaming reads of window_bytes each, rotating over the bytes of
     the device tensor src (a measurement aid: the read ceiling for a product
@@ -502,5 +502,6 @@ def wq_read_probe(src: torch.Tensor, window_bytes: int, count: int, *, chunks: i
     span = src.numel() * src.element_size()
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=src.device)
-    _check(lib().wq_read_probe(_ptr(src), window_bytes, span, count, chunks, _ptr(sink), _stream(stream)),
+    _check(lib().wq_read_probe(_ptr(src), window_bytes, span, count, chunks, int(nontemporal), _ptr(sink),
+                               _stream(stream)),
            "wq_read_probe")

@@ -428,13 +428,14 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
 
 // ---- streaming-read probe (measurement aid) ----------------------------------
 
-int wq_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks, uint32_t* sink,
-                  void* stream) {
+int wq_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks, int nontemporal,
+                  uint32_t* sink, void* stream) {
   if (!src || !sink || count < 0 || window_bytes == 0 || window_bytes % 256 != 0 || span_bytes < window_bytes ||
-      window_bytes > (size_t(1) << 40) || (chunks != 4 && chunks != 8 && chunks != 16))
+      window_bytes > (size_t(1) << 40) || (chunks != 1 && chunks != 2 && chunks != 4 && chunks != 8 && chunks != 16) ||
+      (nontemporal != 0 && nontemporal != 1))
     return WQ_EINVAL;
   if (!aligned(src, 16) || !aligned(sink, 4)) return WQ_EALIGN;
   if (count == 0) return WQ_OK;
-  return hip_status(wq::launch_read_probe(src, window_bytes, span_bytes, count, chunks, sink,
+  return hip_status(wq::launch_read_probe(src, window_bytes, span_bytes, count, chunks, nontemporal, sink,
                                           static_cast<hipStream_t>(stream)));
 }

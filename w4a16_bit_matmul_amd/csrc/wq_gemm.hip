@@ -176,10 +176,23 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int b = 0; b < NPW; ++b)
     tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * TB + 16u * lane + (BITS == 4 ? 8u : 1024u) * jp;
+  // With few rows (MB <= 2) the kernel streams codes at HBM speed and
+  // non-temporal loads measure faster; with more rows they do not.
   auto load_b = [&](int kt, CodeT (&d)[NPW]) {
     kt = min(kt, KT - 1);  // tiles past the end re-load the last (unused)
 #pragma unroll
-    for (int b = 0; b < NPW; ++b) d[b] = *reinterpret_cast<const CodeT*>(tb[b] + (size_t)kt * TB);
+    for (int b = 0; b < NPW; ++b) {
+      const uint8_t* p = tb[b] + (size_t)kt * TB;
+      if constexpr (MB > 2) {
+        d[b] = *reinterpret_cast<const CodeT*>(p);
+      } else if constexpr (BITS == 4) {
+        typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+        const v2 t = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p));
+        d[b] = CodeT{t.x, t.y};
+      } else {
+        d[b] = __builtin_nontemporal_load(reinterpret_cast<const CodeT*>(p));
+      }
+    }
   };
 
   // activation chunk q = tid + NTH * i: row q / 16 of the tile, global chunk

@@ -70,9 +70,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
 
 // Streaming-read probe: count launches back to back, launch i reading the
 // window_bytes at src + (i mod (span_bytes / window_bytes)) * window_bytes once,
-// with chunks (4, 8 or 16) 16-byte loads per thread.  sink: one device word,
-// written only if a thread's XOR of its words hits a fixed value.
+// with chunks (1, 2, 4, 8 or 16) 16-byte loads per thread, plain or
+// non-temporal.  sink: one device word, written only if a thread's XOR of its
+// words hits a fixed value.
 hipError_t launch_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks,
-                             uint32_t* sink, hipStream_t stream);
+                             int nontemporal, uint32_t* sink, hipStream_t stream);
 
 }  // namespace wq
