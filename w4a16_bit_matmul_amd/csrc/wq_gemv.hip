@@ -65,8 +65,21 @@ struct GemvArgs {
   uint16_t* y;
   float* partial;      // [KS][M][N] fp32 (KS > 1 only)
   unsigned* counters;  // [gridDim.y][gridDim.x] (KS > 1 only)
-  int M, N, K, KT, Gtot, GB, NBLK, kt_per_split, KS, sz_vec;
+  int M, N, K, kt_per_split, KS, sz_vec;
 };
+
+// Tile and group counts derived in the kernel from K (and the group size G),
+// so that every kernel argument arrives in the first batch of scalar loads
+// (a field first used after a branch is otherwise fetched there, adding a
+// second kernel-argument round trip before the first weight load).
+struct Dims {
+  int KT, Gtot, GB;
+};
+template <int G>
+__device__ __forceinline__ Dims dims_of(int K) {
+  const int gtot = K / G;
+  return Dims{(K + 127) >> 7, gtot, (gtot + 1) >> 1};
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
@@ -101,7 +114,7 @@ struct SZ {
 // otherwise each group is loaded alone, clamped into the row (groups past the
 // row meet zero activations and zero codes).
 template <int NS, bool ZP>
-__device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, uint32_t srow, uint32_t zrow, int g0) {
+__device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, int Gtot, uint32_t srow, uint32_t zrow, int g0) {
   SZ<NS> v;
 #pragma unroll
   for (int i = 0; i < (NS + 7) / 8; ++i) v.zv[i] = 0;
@@ -133,7 +146,7 @@ __device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, uint32_t srow, uint
     for (int i = 0; i < NS / 2; ++i) v.sv[i] = 0;
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      const int gi = min(g0 + t, a.Gtot - 1);
+      const int gi = min(g0 + t, Gtot - 1);
       v.sv[t >> 1] |= (uint32_t)a.s[srow + gi] << (16 * (t & 1));
       if constexpr (ZP) {
         const uint32_t zb = a.zp[zrow + (gi >> 1)];
@@ -171,7 +184,7 @@ struct E8 {
 };
 
 template <int NS>
-__device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, uint32_t erow, int g0) {
+__device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, int Gtot, uint32_t erow, int g0) {
   static_assert(NS == 16, "segment of four tiles of four blocks");
   E8<NS> v;
   if (a.sz_vec) {
@@ -181,7 +194,7 @@ __device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, uint32_t erow, int 
 #pragma unroll
     for (int i = 0; i < NS / 4; ++i) v.v[i] = 0;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) v.v[t >> 2] |= (uint32_t)a.zp[erow + min(g0 + t, a.Gtot - 1)] << (8 * (t & 3));
+    for (int t = 0; t < NS; ++t) v.v[t >> 2] |= (uint32_t)a.zp[erow + min(g0 + t, Gtot - 1)] << (8 * (t & 3));
   }
   return v;
 }
@@ -219,7 +232,7 @@ __device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, 
 // FMT: kFmtInt4 (codes, fp16 scales, zero-points), kFmtInt8 (2048-byte tiles,
 // fp16 scales), kFmtMxfp4 (E2M1 tiles, E8M0 scale bytes in a.zp, G = 32).
 template <int MT, int W, int KQ, int G, int FMT>
-__global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8 : 1) void gemv_kernel(GemvArgs a) {
   static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
   constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
   constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
@@ -234,15 +247,16 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, c = lane >> 4;
   const int nb = blockIdx.x, m0 = blockIdx.y * MT, ks = blockIdx.z;
+  const Dims d = dims_of<G>(a.K);
   const int kt_lo = ks * a.kt_per_split;
-  const int nkt = min(a.KT, kt_lo + a.kt_per_split) - kt_lo;
+  const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
   // this wave's x slice: [MT][KQ * 128] halves
   uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
   float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][16]
 
-  const uint8_t* tbase = a.qp + (size_t)nb * a.KT * TB;
+  const uint8_t* tbase = a.qp + (size_t)nb * d.KT * TB;
   const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
-  const uint32_t srow = n * (uint32_t)a.Gtot, zrow = n * (uint32_t)a.GB;
+  const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
   const uint32_t lane16 = 16u * lane;
   const uint32_t magic = in_vgpr(kMagicPair);
 
@@ -266,16 +280,16 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     SZ<NS> sz;
     E8<16> e8s;
     if constexpr (FMT == kFmtMxfp4)
-      e8s = load_e8<16>(a, srow, kt0 * GPT);
+      e8s = load_e8<16>(a, d.Gtot, srow, kt0 * GPT);
     else
-      sz = load_sz<NS, FMT == kFmtInt4>(a, srow, zrow, kt0 * GPT);
+      sz = load_sz<NS, FMT == kFmtInt4>(a, d.Gtot, srow, zrow, kt0 * GPT);
     u4 buf[KQ][HALVES];
 #pragma unroll
     for (int t = 0; t < KQ; ++t)
 #pragma unroll
       for (int h = 0; h < HALVES; ++h)
         buf[t][h] = __builtin_nontemporal_load(
-            reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, a.KT - 1) * TB + 1024u * h + lane16));
+            reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
@@ -446,22 +460,19 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
-  a.KT = (int)((K + 127) / 128);
-  a.Gtot = (int)(K / group);
-  a.GB = (a.Gtot + 1) / 2;
-  a.NBLK = (int)((N + 15) / 16);
+  const int KT = (int)((K + 127) / 128), Gtot = (int)(K / group);
   a.kt_per_split = p.kt_per_split;
   a.KS = p.KS;
   // a segment's scales / zero-points load as vectors when every segment lies
   // inside its row and starts suitably aligned
   const int ns = kKQ * (128 / group);  // groups per segment
-  a.sz_vec = (a.Gtot % ns == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
+  a.sz_vec = (Gtot % ns == 0 && KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
               (reinterpret_cast<uintptr_t>(s) & (uintptr_t)(2 * ns > 16 ? 15 : 2 * ns - 1)) == 0 &&
               (fmt == kFmtInt8 || (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0))
                  ? 1
                  : 0;
   if (fmt == kFmtMxfp4)  // 16 scale bytes per segment, one 16-byte load
-    a.sz_vec = (a.Gtot % 16 == 0 && a.KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
+    a.sz_vec = (Gtot % 16 == 0 && KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
                 (reinterpret_cast<uintptr_t>(zpacked) & 15) == 0)
                    ? 1
                    : 0;
