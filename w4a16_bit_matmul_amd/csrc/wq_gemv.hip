@@ -271,7 +271,21 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     const int nq = min(KQ, nkt - q0);       // tiles of the segment inside the split
     const int kt0 = kt_lo + q0;
 
-    // ---- x slice (zeros past M and K), then scales / zero-points, then codes
+    // ---- x slice (zeros past M and K), then scales / zero-points, then codes.
+    // With 4-bit codes at g = 32 a segment's scales and zero-points take 40
+    // bytes per lane, and issuing the first code tile ahead of them measured
+    // 5 % faster (loads retire in order, so that tile still arrives before the
+    // x slice is needed); at g = 128 and for the other formats the order below
+    // measured faster.
+    constexpr bool CODE0_FIRST = FMT == kFmtInt4 && G == 32;
+    u4 buf[KQ][HALVES];
+    const auto load_tile = [&](int t) {
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h)
+        buf[t][h] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
+    };
+    if constexpr (CODE0_FIRST) load_tile(0);
     uint4 xc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -285,13 +299,8 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
       e8s = load_e8<16>(a, d.Gtot, srow, kt0 * GPT);
     else
       sz = load_sz<NS, FMT == kFmtInt4>(a, d.Gtot, srow, zrow, kt0 * GPT);
-    u4 buf[KQ][HALVES];
 #pragma unroll
-    for (int t = 0; t < KQ; ++t)
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h)
-        buf[t][h] = __builtin_nontemporal_load(
-            reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
+    for (int t = CODE0_FIRST ? 1 : 0; t < KQ; ++t) load_tile(t);
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
