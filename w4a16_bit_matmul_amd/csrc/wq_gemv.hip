@@ -87,6 +87,13 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
 
+// The value that lane perm(lane) of this lane's quad holds (DPP quad_perm control
+// CTRL; every lane of the quad must be active).
+template <int CTRL>
+__device__ __forceinline__ float quad_xchg(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
 // Forces a value into a VGPR and hides it from constant folding, so that
 // v_and_or_b32 can take the mask from an SGPR and the fp16 exponent bits from
 // this register (a VOP3 instruction takes no literal and one SGPR at most).
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
   const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
   // this wave's x slice: [MT][KQ * 128] halves
   uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
-  float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][16]
+  float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][64]
 
   const uint8_t* tbase = a.qp + (size_t)nb * d.KT * TB;
   const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
@@ -341,21 +348,24 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- reduce: the four lanes of a row, then the waves, in a fixed order
+  // ---- reduce: every lane's sums go to LDS as [W][MT][16 rows][4 lanes];
+  // thread i = 64m + 4r + c adds the W waves' sums of lane (r, c) in wave
+  // order (all reads in flight together), and the four lanes of row r, which
+  // are one quad of threads, meet by two DPP quad exchanges: no cross-row
+  // shuffle through LDS and no dependent LDS reads on the workgroup's tail.
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    float v = acc[m];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (c == 0) red[(wv * MT + m) * 16 + r] = v;
-  }
+  for (int m = 0; m < MT; ++m) red[(wv * MT + m) * 64 + 4 * r + c] = acc[m];
   __syncthreads();
   constexpr int NOUT = MT * 16;
-  for (int i = tid; i < NOUT; i += NT) {
+  constexpr int NQ = MT * 64;  // a multiple of 64: every wave runs the loop with all lanes
+  for (int i = tid; i < NQ; i += NT) {
     float v = 0.0f;
-#pragma unroll 4
-    for (int w = 0; w < W; ++w) v += red[w * NOUT + i];
-    const int rr = i & 15, m = i >> 4;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * NQ + i];
+    v += quad_xchg<0xb1>(v);  // lane c ^ 1
+    v += quad_xchg<0x4e>(v);  // lane c ^ 2
+    if ((i & 3) != 0) continue;
+    const int rr = (i >> 2) & 15, m = i >> 6;
     const int nn = nb * 16 + rr, mm = m0 + m;
     if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
       split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
@@ -414,7 +424,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
-  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * 16 * 4;
+  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * 64 * 4;
   return p;
 }
 
