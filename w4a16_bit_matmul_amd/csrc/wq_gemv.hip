@@ -411,7 +411,10 @@ struct GemvPlan {
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   GemvPlan p;
   p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  p.W = p.MT <= 4 ? 16 : 8;
+  // one row: sixteen waves, two workgroups per CU at 64 VGPRs; two to eight
+  // rows need more registers, where eight-wave workgroups (two or three per
+  // CU) measured 4-20 % faster than sixteen-wave ones (one per CU)
+  p.W = p.MT <= 1 ? 16 : 8;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   p.gx = (unsigned)NBLK;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
@@ -504,8 +507,8 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
     a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
   }
   if (p.MT == 1) return launch_t<1, 16>(p, group, fmt, a, stream);
-  if (p.MT == 2) return launch_t<2, 16>(p, group, fmt, a, stream);
-  if (p.MT == 4) return launch_t<4, 16>(p, group, fmt, a, stream);
+  if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
+  if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
   return launch_t<8, 8>(p, group, fmt, a, stream);
 }
 
