@@ -115,6 +115,41 @@ def bench_gemv(steps, warmup, name="decode_gemv"):
     return wl, nbytes, copies, t_step, t_single
 
 
+def flush_check(calls=200, warmup=2000):
+    """Cross-check of the weight rotation: the decode GEMV on ONE weight copy,
+    with a 512 MiB read-and-write flush of the GPU's caches (256 MB last-level
+    cache) between consecutive calls, each call timed alone by events on the
+    launch stream; next to the same calls back to back without the flush (the
+    weights then stay cache resident) and the rotated figure of bench_gemv."""
+    import statistics
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    wl = workloads.WORKLOADS["decode_gemv"]
+    Wd, xd, qw = _quantize_workload(wl)
+    del Wd
+    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+    ws = _workspace(wl)
+    scratch = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
+    for _ in range(warmup):
+        wq.wq_gemm_w4a16(xd, qw, y=y, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in ev:
+        scratch.add_(1.0)  # reads and writes 512 MiB: evicts the weights from every cache level
+        e0.record()
+        wq.wq_gemm_w4a16(xd, qw, y=y, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    flushed = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    hot = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qw, y=y, workspace=ws), calls, 0) * 1e6
+    return {"workload": "decode_gemv", "calls": calls, "flush_bytes": 512 << 20,
+            "us_per_call_flushed_median": round(statistics.median(flushed), 3),
+            "us_per_call_flushed_mean": round(statistics.mean(flushed), 3),
+            "us_per_call_same_copy_back_to_back": round(hot, 3),
+            "note": "flushed calls are timed one at a time (each includes one event pair's overhead); the "
+                    "rotated back-to-back figure is the benchmark value"}
+
+
 def bench_gemm(steps, warmup):
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -478,6 +513,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line, time every workload through both kernel families "
                          "(one JSON line each)")
+    ap.add_argument("--flush-check", action="store_true",
+                    help="instead of the benchmark line, time the decode GEMV on one weight copy with a 512 MiB "
+                         "cache flush between calls (cross-check of the weight rotation)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run an elementwise kernel over 256 MiB (reads and writes a known byte count), "
                          "to calibrate hardware byte counters")
@@ -501,6 +539,13 @@ def main():
     import w4a16_bit_matmul_amd as wq
     if args.sweep:
         bench_sweep(args.steps)
+        return
+    if args.flush_check:
+        rec = flush_check()
+        _, _, copies, t_step, _ = bench_gemv(args.steps, args.warmup)
+        rec["us_per_call_rotated_back_to_back"] = round(t_step * 1e6, 3)
+        rec["rotated_weight_copies"] = copies
+        print(json.dumps(rec), flush=True)
         return
     wl, nbytes, copies, t_step, t_single = bench_gemv(args.steps, args.warmup)
     plan = wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group)
