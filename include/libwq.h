@@ -291,8 +291,9 @@ int wq_pack_int8(const int8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, 
 int wq_dequant_w8(const uint8_t* qpacked, const uint16_t* s_f16, int64_t N, int64_t K, int group,
                   int out_dtype, void* W_hat, void* stream);
 
-/* Workspace bytes for wq_gemm_w8a16 / wq_gemm_w8a16_ex (same rules as
- * wq_gemm_workspace_bytes).  Host-only. */
+/* Workspace bytes for wq_gemm_w8a16 / wq_gemm_w8a16_ex, enough for either
+ * kernel family with int8 codes (as wq_gemm_workspace_bytes, but the int8 GEMV
+ * may split K across more workgroups than the 4-bit one).  Host-only. */
 size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 
 /* y = x * What^T with What = s * q dequantized inside the kernel (the

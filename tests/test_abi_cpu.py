@@ -223,15 +223,20 @@ def test_w8_entry_points_checked_on_host():
     assert call(g, 1, 16, 100, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
     assert call(g, 1, 16, 128, 128, A, B, A, A, None, 0, 0, None) == wq.WQ_EALIGN
     assert call("wq_gemm_w8a16", 1, 16, 128, 128, B, A, A, A, None, 0, None) == wq.WQ_EALIGN
-    assert wq.wq_gemm_w8a16_workspace_bytes(1, 1024, 8192, 32) == wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32) > 0
-    need = wq.wq_gemm_workspace_bytes(1, 1024, 8192, 32, wq.WQ_PATH_GEMV)  # the same launch plan as the INT4 GEMV
+    # the int8 GEMV runs eight-wave workgroups and may split K further than the
+    # 4-bit one: its workspace follows its own launch plan (counter region, then
+    # KS fp32 partial-sum planes of MT x 16 per workgroup)
+    plan = wq.wq_gemm_w8a16_plan(1, 1024, 8192, 32, wq.WQ_PATH_GEMV)
+    gx, gy, ks = (int(v) for v in plan.split("grid=(", 1)[1].split(")", 1)[0].split(","))
+    need = wq.WQ_WORKSPACE_COUNTER_BYTES + ks * gy * 1 * gx * 16 * 4
+    assert ks > 1 and wq.wq_gemm_w8a16_workspace_bytes(1, 1024, 8192, 32) >= need, plan
     assert call(g, 1, 1024, 8192, 32, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
     assert call(g, 1, 1024, 8192, 32, A, A, A, A, A, need - 1, 0, None) == wq.WQ_EWORKSPACE
 
 
 def test_w8_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_w8a16_plan(1, 8192, 8192, 128)
-    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=128, BITS=8>") and "grid=(512,1,1)" in d, d
+    assert d.startswith("gemv_kernel<MT=1, W=8, KQ=4, G=128, BITS=8>") and "grid=(512,1,1)" in d, d
     d = wq.wq_gemm_w8a16_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128, BITS=8>") and "grid=(224,1,1)" in d, d
     assert wq.wq_gemm_w8a16_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32, BITS=8>")

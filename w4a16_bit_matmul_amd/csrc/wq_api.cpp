@@ -128,7 +128,7 @@ int wq_dequant(const uint32_t* qpacked, const uint16_t* s_f16, const uint8_t* zp
 
 size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
   if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
-  const size_t a = wq::gemv_workspace_bytes(M, N, K, group), b = wq::gemm_workspace_bytes(M, N, K, group);
+  const size_t a = wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt4), b = wq::gemm_workspace_bytes(M, N, K, group);
   return a > b ? a : b;
 }
 
@@ -136,7 +136,7 @@ size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, in
   if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return 0;
   const bool mfma = auto_mfma(M, path);
-  return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
+  return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt4);
 }
 
 int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf, size_t buf_len) {
@@ -170,7 +170,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
   *mfma = auto_mfma(M, path);
-  const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group);
+  const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, fmt);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
     if (!aligned(workspace, 256)) return WQ_EALIGN;
@@ -267,7 +267,10 @@ int wq_dequant_w8(const uint8_t* qpacked, const uint16_t* s_f16, int64_t N, int6
 }
 
 size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
-  return wq_gemm_workspace_bytes(M, N, K, group);
+  if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
+  // the int8 GEMV may split K differently from the 4-bit one
+  const size_t a = wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt8), b = wq::gemm_workspace_bytes(M, N, K, group);
+  return a > b ? a : b;
 }
 
 int wq_gemm_w8a16_ex(int64_t M, int64_t N, int64_t K, int group, const uint16_t* x_f16, const uint8_t* qpacked,

@@ -408,13 +408,15 @@ struct GemvPlan {
   size_t lds;
 };
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   GemvPlan p;
   p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  // one row: sixteen waves, two workgroups per CU at 64 VGPRs; two to eight
-  // rows need more registers, where eight-wave workgroups (two or three per
-  // CU) measured 4-20 % faster than sixteen-wave ones (one per CU)
-  p.W = p.MT <= 1 ? 16 : 8;
+  // one row of 4-bit or MXFP4 codes: sixteen waves, two workgroups per CU at
+  // 64 VGPRs.  Kernels that need more registers (two to eight rows, and int8
+  // codes with twice the bytes in flight per lane) measured 4-20 % faster with
+  // eight-wave workgroups (two or three per CU) than with one sixteen-wave
+  // workgroup per CU.
+  p.W = (p.MT <= 1 && fmt != kFmtInt8) ? 16 : 8;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   p.gx = (unsigned)NBLK;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
@@ -455,7 +457,7 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
 }  // namespace
 
 int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
-  const GemvPlan p = plan_gemv(M, N, K);
+  const GemvPlan p = plan_gemv(M, N, K, fmt);
   if (fmt == kFmtInt8 || fmt == kFmtMxfp4)
     return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                     p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "MXFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
@@ -464,8 +466,8 @@ int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf
                   p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
 }
 
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
-  const GemvPlan p = plan_gemv(M, N, K);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int, int fmt) {
+  const GemvPlan p = plan_gemv(M, N, K, fmt);
   if (p.KS == 1) return 0;
   // partial-sum planes padded to whole tiles: [KS][gy * MT][gx * 16]
   return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * 16 * sizeof(float);
@@ -474,7 +476,7 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
                        const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
                        hipStream_t stream) {
-  const GemvPlan p = plan_gemv(M, N, K);
+  const GemvPlan p = plan_gemv(M, N, K, fmt);
   GemvArgs a;
   a.x = x;
   a.qp = static_cast<const uint8_t*>(qpacked);
@@ -506,7 +508,7 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
     a.counters = static_cast<unsigned*>(workspace);
     a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
   }
-  if (p.MT == 1) return launch_t<1, 16>(p, group, fmt, a, stream);
+  if (p.MT == 1) return p.W == 16 ? launch_t<1, 16>(p, group, fmt, a, stream) : launch_t<1, 8>(p, group, fmt, a, stream);
   if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
   if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
   return launch_t<8, 8>(p, group, fmt, a, stream);

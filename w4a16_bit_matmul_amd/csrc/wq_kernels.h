@@ -52,7 +52,7 @@ hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint
 // VALU split-K GEMV for small M.  It needs a workspace (a counter region that
 // is zero on entry and left zero, then fp32 partial sums) only when it splits K
 // across workgroups; gemv_workspace_bytes gives the size (0 otherwise).
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int fmt);
 // Writes a one-line description of the kernel and launch shape chosen for this
 // problem (snprintf semantics).  fmt (wq_device.h): kFmtInt4 (tile codes +
 // zero-points), kFmtInt8 (2048-byte int8 tiles; zpacked unused) or kFmtMxfp4
