@@ -103,7 +103,7 @@ def test_workspace_query_and_check():
     # across workgroups to fill the GPU (few row or column blocks); the
     # query covers both families (the M=128, N=28672 GEMM splits nothing)
     assert wq.wq_gemm_workspace_bytes(128, 28672, 8192, 128) == 0
-    for M, N, K, g in [(1, 1024, 8192, 32), (8, 1024, 8192, 128), (1, 48, 8192, 128), (16, 64, 8192, 32)]:
+    for M, N, K, g in [(1, 1024, 28672, 32), (8, 1024, 8192, 128), (1, 48, 28672, 128), (16, 64, 8192, 32)]:
         for path in (wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA):
             need = wq.wq_gemm_workspace_bytes(M, N, K, g, path)
             assert 0 < need <= wq.wq_gemm_workspace_bytes(M, N, K, g), (M, N, K, g, path)
@@ -143,7 +143,10 @@ def test_gemm_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_plan(32, 1024, 8192, 32, wq.WQ_PATH_MFMA)
     assert "grid=(8,1,8)" in d and "split_k=8" in d, d
     assert "split_k=1" in wq.wq_gemm_plan(128, 28672, 8192, 128)
-    assert "split_k=1" not in wq.wq_gemm_plan(1, 48, 8192, 128)
+    assert "split_k=1" not in wq.wq_gemm_plan(1, 48, 28672, 128)
+    # one pass of the waves covers K = 8192 at one row: no split, which would
+    # only leave waves idle and add the hand-off
+    assert "split_k=1" in wq.wq_gemm_plan(1, 1024, 8192, 32)
     # AUTO switches from the GEMV to the MFMA GEMM at WQ_AUTO_MFMA_MIN_M rows,
     # the same value in the header and the binding
     m = re.search(r"#define WQ_AUTO_MFMA_MIN_M (\d+)", open(HEADER).read())
@@ -305,8 +308,12 @@ def test_mxfp4_entry_points_checked_on_host():
     assert call(g, 1, 16, 100, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
     assert call(g, 1, 16, 128, B, A, A, A, None, 0, 0, None) == wq.WQ_EALIGN
     assert call(g, 1, 16, 128, A, A, A, A, None, 0, 5, None) == wq.WQ_EINVAL
-    need = wq.wq_gemm_mxfp4_workspace_bytes(1, 1024, 8192)
-    assert need > 0 and call(g, 1, 1024, 8192, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
+    # a one-row GEMV over K = 28672 splits K, so a missing workspace is refused
+    # before anything is launched (the plan is checked first: the call must not
+    # reach a launch with these placeholder pointers)
+    assert "split_k=1" not in wq.wq_gemm_mxfp4_plan(1, 1024, 28672)
+    need = wq.wq_gemm_mxfp4_workspace_bytes(1, 1024, 28672)
+    assert need > 0 and call(g, 1, 1024, 28672, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
     d = wq.wq_gemm_mxfp4_plan(1, 8192, 8192)
     assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=32, MXFP4>") and "grid=(512,1,1)" in d, d
     d = wq.wq_gemm_mxfp4_plan(128, 28672, 8192)

@@ -98,7 +98,7 @@ def test_pack_and_dequant_mxfp4_bit_exact(N, K):
 
 MATMUL_CASES = [(1, 256, 1024), (1, 1000, 1152), (3, 37, 96), (8, 272, 640), (17, 100, 256), (63, 48, 256),
                 (64, 272, 640), (128, 512, 2048), (130, 100, 256), (40, 100, 96), (96, 50, 4224), (129, 300, 1056),
-                (1, 48, 8192), (5, 100, 8192)]
+                (1, 48, 28672), (5, 100, 8192)]
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA, wq.WQ_PATH_AUTO])

@@ -170,8 +170,9 @@ MATMUL_CASES = [  # M, N, K, group
     (100, 72, 160, 32),
     (96, 50, 4224, 128),
     (129, 300, 1056, 32),
-    # few row blocks and a long K: the GEMV splits K across workgroups
-    (1, 48, 8192, 128),
+    # few row blocks and a K longer than one pass of a workgroup's waves: the
+    # GEMV splits K across workgroups
+    (1, 48, 28672, 128),
     (2, 1000, 8192, 128),
     (5, 100, 8192, 32),
     (12, 40, 8192, 32),
@@ -252,7 +253,7 @@ def test_split_k_workspace_is_reusable():
     partial sums, here pre-filled with NaN bytes, need no clearing), and give
     the same bytes as calls with a fresh zero-filled workspace."""
     say("split-K workspace reuse")
-    cases = [(1, 48, 8192, 128), (5, 100, 8192, 32), (2, 1000, 8192, 128), (1, 48, 8192, 128)]
+    cases = [(1, 48, 28672, 128), (5, 100, 8192, 32), (2, 1000, 8192, 128), (1, 48, 28672, 128)]
     need = max(wq.wq_gemm_workspace_bytes(M, N, K, g) for M, N, K, g in cases)
     assert need > 0
     shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
@@ -316,7 +317,7 @@ def test_repeated_calls_are_deterministic():
 def test_sequence_call_matches_single_calls():
     # one host call issuing several products equals the single calls, for the
     # GEMV (with a split-K workspace shared by the sequence) and the MFMA path
-    for (M, N, K, group) in [(3, 272, 640, 32), (1, 48, 8192, 128), (80, 100, 512, 128)]:
+    for (M, N, K, group) in [(3, 272, 640, 32), (1, 48, 28672, 128), (80, 100, 512, 128)]:
         say(f"sequence M={M} N={N} K={K} g={group}")
         qws, xs, refs = [], [], []
         for t in range(3):
@@ -374,7 +375,7 @@ def test_dequant_symmetric_bit_exact(group):
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
 @pytest.mark.parametrize("M,N,K,group", [(1, 1000, 1152, 128), (5, 300, 512, 32), (77, 130, 1024, 32),
-                                         (128, 512, 2048, 128), (1, 48, 8192, 128)])
+                                         (128, 512, 2048, 128), (1, 48, 28672, 128)])
 def test_matmul_symmetric_within_tolerance(M, N, K, group, path):
     say(f"matmul sym M={M} N={N} K={K} g={group} path={path}")
     W, x = _matmul_inputs(M, N, K, group, 950 + M + N + K)
