@@ -139,7 +139,7 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     # a small grid splits K across workgroups in whole eight-tile chunks
     d = wq.wq_gemm_plan(128, 8192, 8192, 128)
-    assert "grid=(64,1,4)" in d and "split_k=4" in d, d
+    assert d.startswith("gemm_kernel<MB=4,") and "grid=(64,2,2)" in d and "split_k=2" in d, d
     d = wq.wq_gemm_plan(32, 1024, 8192, 32, wq.WQ_PATH_MFMA)
     assert "grid=(8,1,8)" in d and "split_k=8" in d, d
     assert "split_k=1" in wq.wq_gemm_plan(128, 28672, 8192, 128)

@@ -170,6 +170,10 @@ MATMUL_CASES = [  # M, N, K, group
     (100, 72, 160, 32),
     (96, 50, 4224, 128),
     (129, 300, 1056, 32),
+    # eight row blocks per workgroup need at least 192 128-column blocks:
+    # N = 24592 gives 193, the last holding a single 16-row block, and M = 130
+    # leaves a partial second row tile
+    (130, 24592, 384, 32),
     # few row blocks and a K longer than one pass of a workgroup's waves: the
     # GEMV splits K across workgroups
     (1, 48, 28672, 128),
