@@ -170,6 +170,9 @@ MATMUL_CASES = [  # M, N, K, group
     (100, 72, 160, 32),
     (96, 50, 4224, 128),
     (129, 300, 1056, 32),
+    # four row blocks per workgroup: 32 to 191 128-column blocks and M > 32
+    (40, 4100, 256, 32),
+    (100, 4100, 2048, 128),  # and K split two ways
     # eight row blocks per workgroup need at least 192 128-column blocks:
     # N = 24592 gives 193, the last holding a single 16-row block, and M = 130
     # leaves a partial second row tile

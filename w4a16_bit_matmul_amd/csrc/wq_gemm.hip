@@ -483,13 +483,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 
 // Row blocks per workgroup for a problem of M rows and N columns.  Eight row
 // blocks (128 rows) per workgroup only when the grid has enough
-// 128-column blocks to fill the GPU: with few of them (N below 24,576) four row
-// blocks give twice the workgroups before K is split, and fewer split planes
-// to write and add (M=128: N=K=8192 31.8 -> 29.2 us, N=1024 24.1 -> 16.8 us;
-// at N=28672 eight measured 8 % faster).
+// 128-column blocks to fill the GPU: with fewer of them (N below 24,576) four
+// row blocks give twice the workgroups before K is split, and fewer split
+// planes to write and add, and with very few (N below 4,096) two do (M=128:
+// N=K=8192 31.8 -> 29.2 us with four; N=1024, K=8192 24.1 -> 16.8 us with
+// four, 13.3 us with two; at N=28672 eight measured 8 % faster than four).
 int gemm_mb(int64_t M, int64_t N) {
   const int64_t gx = ((N + 15) / 16 + 7) / 8;
-  return M <= 16 ? 1 : M <= 32 ? 2 : (M <= 64 || gx < 192) ? 4 : 8;
+  return M <= 16 ? 1 : (M <= 32 || gx < 32) ? 2 : (M <= 64 || gx < 192) ? 4 : 8;
 }
 
 // Launch shape: (128-column blocks, 16*MB-row blocks, K splits).  A grid of
