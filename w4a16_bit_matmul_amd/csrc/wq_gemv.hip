@@ -44,9 +44,10 @@
 // workgroup barrier stands between the loads and the arithmetic, so each wave
 // starts as soon as its own data arrives.  Two 1024-thread workgroups share
 // a CU only if every wave holds at most 64 VGPRs (eight waves per SIMD), so the
-// one-row 4-bit and MXFP4 instances are compiled to that bound (the int8
-// instance would spill and keeps one workgroup per CU).  The waves'
-// partial sums meet in LDS in a fixed order.  When the grid splits K, each
+// one-row 4-bit and MXFP4 instances are compiled to that bound; the kernels
+// that need more registers (int8 codes, two or more rows of x) run eight-wave
+// workgroups instead, two or three per CU.  The waves' partial sums meet in
+// LDS in a fixed order.  When the grid splits K, each
 // workgroup writes fp32 partial sums to the workspace and the last workgroup of
 // a row range (found with a device-scope atomic counter) adds them in split
 // order and writes y, so results stay deterministic; it then puts the counter
