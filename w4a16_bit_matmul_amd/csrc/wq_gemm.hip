@@ -481,16 +481,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   if (tid == 0) split_reset(ctr);
 }
 
-// Row blocks per workgroup for a problem of M rows and N columns.  Eight row
-// blocks (128 rows) per workgroup only when the grid has enough
+// Row blocks per workgroup for a problem of M rows, N columns and depth K.
+// Eight row blocks (128 rows) per workgroup only when the grid has enough
 // 128-column blocks to fill the GPU: with fewer of them (N below 24,576) four
 // row blocks give twice the workgroups before K is split, and fewer split
 // planes to write and add, and with very few (N below 4,096) two do (M=128:
 // N=K=8192 31.8 -> 29.2 us with four; N=1024, K=8192 24.1 -> 16.8 us with
 // four, 13.3 us with two; at N=28672 eight measured 8 % faster than four).
-int gemm_mb(int64_t M, int64_t N) {
+// Fewer row blocks dequantize every weight once per block of rows, which a
+// long K does not repay: at N=8192, K=28672 four measured 91 us against 81
+// with eight, so the smaller blocks are used only up to K = 16384.
+int gemm_mb(int64_t M, int64_t N, int64_t K) {
   const int64_t gx = ((N + 15) / 16 + 7) / 8;
-  return M <= 16 ? 1 : (M <= 32 || gx < 32) ? 2 : (M <= 64 || gx < 192) ? 4 : 8;
+  const bool short_k = K <= 16384;
+  return M <= 16 ? 1 : (M <= 32 || (short_k && gx < 32)) ? 2 : (M <= 64 || (short_k && gx < 192)) ? 4 : 8;
 }
 
 // Launch shape: (128-column blocks, 16*MB-row blocks, K splits).  A grid of
@@ -503,7 +507,7 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
-  p.MB = gemm_mb(M, N);
+  p.MB = gemm_mb(M, N, K);
   p.gx = (unsigned)(((N + 15) / 16 + 7) / 8);
   p.gy = (unsigned)((M + 16 * p.MB - 1) / (16 * p.MB));
   const int KT = (int)((K + 127) / 128);
@@ -604,7 +608,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   a.GB = (a.Gtot + 1) / 2;
   a.NBLK = (int)((N + 15) / 16);
   if (fmt == kFmtInt8) {
-    switch (gemm_mb(M, N)) {
+    switch (gemm_mb(M, N, K)) {
       case 1: return launch_t<1, kFmtInt8>(group, a, stream);
       case 2: return launch_t<2, kFmtInt8>(group, a, stream);
       case 4: return launch_t<4, kFmtInt8>(group, a, stream);
@@ -612,14 +616,14 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
     }
   }
   if (fmt == kFmtMxfp4) {
-    switch (gemm_mb(M, N)) {
+    switch (gemm_mb(M, N, K)) {
       case 1: return launch_t<1, kFmtMxfp4>(group, a, stream);
       case 2: return launch_t<2, kFmtMxfp4>(group, a, stream);
       case 4: return launch_t<4, kFmtMxfp4>(group, a, stream);
       default: return launch_t<8, kFmtMxfp4>(group, a, stream);
     }
   }
-  switch (gemm_mb(M, N)) {
+  switch (gemm_mb(M, N, K)) {
     case 1: return launch_t<1, kFmtInt4>(group, a, stream);
     case 2: return launch_t<2, kFmtInt4>(group, a, stream);
     case 4: return launch_t<4, kFmtInt4>(group, a, stream);
