@@ -173,9 +173,12 @@ __device__ __forceinline__ uint32_t encode_w8(float w, const GroupParams& p) {
 __device__ __forceinline__ int nibble_pos(int e) { return 4 * (e & 1) + (e >> 1); }
 
 // SCALED: each weight is first multiplied by its input channel's factor
-// alpha[k] (the AWQ fold, one fp32 multiplication).
+// alpha[k] (the AWQ fold, one fp32 multiplication).  At g = 128 without the
+// fold the kernel fits 64 VGPRs, which lets eight workgroups share a CU instead
+// of six or seven (bf16 8192 x 8192: 56.3 -> 44.0 us); the other instances
+// would spill at that bound (g = 32 measured 59 -> 78 us) and keep theirs.
 template <int DT, int G, bool SYM, bool SCALED>
-__global__ __launch_bounds__(256) void quantize_kernel(
+__global__ __launch_bounds__(256, (G == 128 && !SCALED) ? 8 : 1) void quantize_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, int64_t NBLK, int64_t KT, const float* __restrict__ alpha,
     uint8_t* __restrict__ q_codes, uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_codes,
     uint32_t* __restrict__ qpacked, uint8_t* __restrict__ zpacked) {
