@@ -1,0 +1,63 @@
+"""Register budgets the launch shapes depend on, checked on the compiled
+gfx950 code (host-only: hipcc cross-compiles without a GPU).
+
+A 1024-thread GEMV workgroup is sixteen waves, four per SIMD; two of them share
+a CU only while every wave holds at most 64 VGPRs (eight waves per SIMD out of
+512 registers).  The one-row 4-bit and MXFP4 GEMV instances and the g = 128
+quantize kernel are compiled to that bound; crossing it halves their
+workgroups per CU without any other symptom, so the bound and the absence of
+register spills are checked here."""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from w4a16_bit_matmul_amd import _build
+
+
+def _kernel_metadata(src_name):
+    src = os.path.join(_build.CSRC, src_name)
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [_build.HIPCC, *_build.COMMON, *_build.PER_FILE[src_name], "-Wno-unused-value",
+               "--cuda-device-only", "-S", src, "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            pytest.fail(res.stdout + res.stderr)
+        text = open(out).read()
+    meta = {}
+    # the metadata block lists, per kernel, .name, .private_segment_fixed_size and .vgpr_count
+    for block in text.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        vgpr = int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1))
+        scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
+        meta[name] = (vgpr, scratch)
+    return meta
+
+
+def _find(meta, fragment):
+    hits = [(n, v) for n, v in meta.items() if fragment in n]
+    assert hits, f"no kernel matching {fragment}"
+    return hits
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
+def test_one_row_gemv_fits_two_workgroups_per_cu():
+    meta = _kernel_metadata("wq_gemv.hip")
+    # gemv_kernel<MT=1, W=16, KQ=4, G, FMT>: 4-bit at g = 128 and 32, MXFP4
+    for frag in ("gemv_kernelILi1ELi16ELi4ELi128ELi4E", "gemv_kernelILi1ELi16ELi4ELi32ELi4E",
+                 "gemv_kernelILi1ELi16ELi4ELi32ELi2E"):
+        for name, (vgpr, scratch) in _find(meta, frag):
+            assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
+def test_g128_quantize_fits_eight_workgroups_per_cu():
+    meta = _kernel_metadata("wq_quant.hip")
+    # quantize_kernel<DT, G=128, SYM, SCALED=false> for every input dtype
+    for dt in range(3):
+        for sym in "01":
+            for name, (vgpr, scratch) in _find(meta, f"quantize_kernelILi{dt}ELi128ELb{sym}ELb0E"):
+                assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)
