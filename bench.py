@@ -3,7 +3,7 @@
 Step = one call of wq_gemm_w4a16 (the fused dequantize-and-multiply) on the
 decode workload M=1, N=K=8192, group 128, with seeded synthetic bf16 weights
 (quantized once on the GPU before timing) and fp16 activations, all resident
-in HBM.  The weights are replicated into enough copies (>= 512 MB) that
+in HBM.  The weights are replicated into enough copies (>= 1 GB) that
 consecutive steps never find them in the 256 MB last-level cache.
 
 value = effective GB/s = algorithmic bytes (4-bit codes + fp16 scales + 4-bit
@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD published
 FP16_PEAK_TFLOPS = 2516.6       # MI355X dense fp16 MFMA, AMD published (256 CU x 4096 FLOP/clk x 2.4 GHz)
 METRIC = "W4A16 GEMV effective HBM GB/s (% of peak) at M=1; GEMM TFLOP/s at M=128"
-ROTATE_BYTES = 512 << 20
+ROTATE_BYTES = 1024 << 20  # four times the 256 MB last-level cache
 
 
 def log(*a):
@@ -362,7 +362,7 @@ def bench_sweep(steps):
 
 def bench_read_ceiling(nbytes, steps, warmup):
     """The streaming-read probe on the decode GEMV's byte count (rounded up to
-    256), rotating over >= 512 MB so that every launch reads HBM: the best of
+    256), rotating over >= 1 GB so that every launch reads HBM: the best of
     1, 2, 4 and 8 16-byte loads per thread, plain or non-temporal.  Each timed
     run is one C call that issues every launch, so the host never gaps the GPU."""
     import torch
@@ -390,7 +390,7 @@ def bench_configs(steps):
     """Every workload (the tiny case, decode, the M=16 up-projection, the M=128
     GEMM and the g=32 sweep of 70B layer shapes) on the kernel WQ_PATH_AUTO
     picks: time per launch from one wq_gemm_w4a16_seq call of back-to-back
-    launches (weights rotated over >= 512 MB of copies, at most 128), after one
+    launches (weights rotated over >= 1 GB of copies, at most 128), after one
     untimed call; effective GB/s and TFLOP/s."""
     import numpy as np
     import torch
@@ -502,6 +502,7 @@ def cpu_baseline(target_s=12.0):
 
 
 def main():
+    global ROTATE_BYTES
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -516,10 +517,14 @@ def main():
     ap.add_argument("--flush-check", action="store_true",
                     help="instead of the benchmark line, time the decode GEMV on one weight copy with a 512 MiB "
                          "cache flush between calls (cross-check of the weight rotation)")
+    ap.add_argument("--rotate-mb", type=int, default=ROTATE_BYTES >> 20,
+                    help="span of the weight copies the timed calls rotate over, in MiB (default 1024, four "
+                         "times the last-level cache)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run an elementwise kernel over 256 MiB (reads and writes a known byte count), "
                          "to calibrate hardware byte counters")
     args = ap.parse_args()
+    ROTATE_BYTES = args.rotate_mb << 20
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the W4A16 path here is a "
               f"single-GPU kernel library with no multi-GPU component", file=sys.stderr)
@@ -545,6 +550,7 @@ def main():
         _, _, copies, t_step, _ = bench_gemv(args.steps, args.warmup)
         rec["us_per_call_rotated_back_to_back"] = round(t_step * 1e6, 3)
         rec["rotated_weight_copies"] = copies
+        rec["rotate_mb"] = args.rotate_mb
         print(json.dumps(rec), flush=True)
         return
     wl, nbytes, copies, t_step, t_single = bench_gemv(args.steps, args.warmup)
