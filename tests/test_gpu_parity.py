@@ -207,6 +207,27 @@ def test_matmul_within_tolerance(M, N, K, group, path):
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
+@pytest.mark.parametrize("M,N,K,group", [(1, 500, 2048, 128), (3, 300, 1024, 32), (9, 300, 1024, 128),
+                                         (64, 200, 1024, 32)])
+def test_matmul_offset_activations(M, N, K, group, path):
+    """Activations with a common offset (mean 3) and outlier channels (x20):
+    each output is then a sum of large terms of both signs (the offset times
+    the row's dequantized weights, the outlier channels), and small outputs
+    come from their cancellation; checked element by element."""
+    say(f"matmul offset activations M={M} N={N} K={K} g={group} path={path}")
+    seed = 700 + M + N + K + group
+    W = workloads.gen_weights(seed, N, K, outlier_frac=0.01, dtype="bf16")
+    x = workloads.gen_activations(seed + 2, M, K, outlier_frac=0.01, outlier_mult=20.0, offset=3.0)
+    out = gpu_quantize(W, "bf16", group)
+    q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16)
+    y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
+    torch.cuda.synchronize()
+    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+
+
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
 @pytest.mark.parametrize("M,N,K,group", [(1, 200, 512, 128), (16, 64, 384, 32), (128, 80, 256, 128),
                                          (70, 48, 160, 32)])
 def test_one_hot_activations_select_weights_exactly(M, N, K, group, path):

@@ -69,12 +69,16 @@ def gen_weights(seed: int, N: int, K: int, std: float = 0.02, outlier_frac: floa
 
 
 def gen_activations(seed: int, M: int, K: int, outlier_frac: float = 0.0,
-                    outlier_mult: float = 10.0, channel_seed: int | None = None) -> np.ndarray:
-    """Activations [M][K] as fp16 bit patterns.  The outlier channels are drawn
-    from channel_seed (default seed + 1), so draws with different values can
-    share them (calibration rows and evaluation rows of one layer)."""
+                    outlier_mult: float = 10.0, channel_seed: int | None = None,
+                    offset: float = 0.0) -> np.ndarray:
+    """Activations [M][K] as fp16 bit patterns: N(offset, 1), then the outlier
+    channels scaled by outlier_mult.  The outlier channels are drawn from
+    channel_seed (default seed + 1), so draws with different values can share
+    them (calibration rows and evaluation rows of one layer)."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K), dtype=np.float32)
+    if offset:
+        x += np.float32(offset)
     n_out = int(round(outlier_frac * K))
     if n_out:
         cols = np.random.default_rng(seed + 1 if channel_seed is None else channel_seed).choice(K, n_out, replace=False)
