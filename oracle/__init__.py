@@ -27,27 +27,36 @@ EINVAL, ERANGE = -1, -6
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the oracle with gcc (plain IEEE binary32/64, no FMA contraction)."""
+def build(verbose: bool = False, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (plain IEEE binary32/64, no FMA contraction).
+    sanitize=True adds AddressSanitizer and UndefinedBehaviorSanitizer (every
+    report fatal) for the sanitized test run; out names the library file."""
+    target = out or _LIB
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
         "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
-        "-o", _LIB + ".tmp", _SRC, "-lm",
     ]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    cmd += ["-o", target + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(target + ".tmp", target)
+    return target
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    alt = os.environ.get("WQ_ORACLE_LIB")  # a separately built copy (the sanitized test run)
+    if alt:
+        lib = ctypes.CDLL(alt)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I = ctypes.c_int

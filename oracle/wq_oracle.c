@@ -410,11 +410,21 @@ int orc_pack_zeros(const uint8_t* z, int64_t N, int64_t G, uint8_t* out)
 /* The product y = x * What^T in fp64, summed in k order                     */
 /* ------------------------------------------------------------------------- */
 
+/* The activations as fp64 (exact: every fp16 value is a double), converted once
+ * per call so the products below need no conversion per multiply. */
+static double* x_to_f64(const uint16_t* x_f16, int64_t n)
+{
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n);
+    if (xd)
+        for (int64_t i = 0; i < n; ++i) xd[i] = (double)orc_f16_to_f32(x_f16[i]);
+    return xd;
+}
+
 int orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const float* w_hat, double* y)
 {
     if (!x_f16 || !w_hat || !y || M <= 0 || N <= 0 || K <= 0) return ORC_EINVAL;
-    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
-    for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)orc_f16_to_f32(x_f16[i]);
+    double* xd = x_to_f64(x_f16, M * K);
+    if (!xd) return ORC_EINVAL;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t m = 0; m < M; ++m) {
@@ -428,7 +438,8 @@ int orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const f
 
 /* Rows [n0, n0 + nrows) of the same product, quantized weights given as codes,
  * scales and zero-points: the oracle's dequantization followed by the fp64
- * product, one row at a time (used to check sampled outputs of large shapes). */
+ * product, one row at a time (any range of rows, up to all of them, for the
+ * full-size checks). */
 int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_f16,
                       const uint8_t* q, const uint16_t* s, const uint8_t* z,
                       int64_t n0, int64_t nrows, double* y_rows /* [M][nrows] */)
@@ -436,6 +447,8 @@ int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_
     if (!x_f16 || !q || !s || !z || !y_rows || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
     if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
     int64_t G = K / g;
+    double* xd = x_to_f64(x_f16, M * K);
+    if (!xd) return ORC_EINVAL;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t n = n0 + i;
@@ -443,11 +456,12 @@ int orc_gemm_rows_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t* x_
         orc_dequant(q + n * K, s + n * G, z + n * G, 1, K, g, ORC_F32, wr);
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * (double)wr[k];
             y_rows[m * nrows + i] = acc;
         }
         free(wr);
     }
+    free(xd);
     return 0;
 }
 
@@ -564,6 +578,8 @@ int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t*
     if (!x_f16 || !q || !s || !y_rows || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g) return ORC_EINVAL;
     if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
     int64_t G = K / g;
+    double* xd = x_to_f64(x_f16, M * K);
+    if (!xd) return ORC_EINVAL;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t n = n0 + i;
@@ -571,11 +587,12 @@ int orc_gemm_rows_w8_f64(int64_t M, int64_t N, int64_t K, int g, const uint16_t*
         orc_dequant_w8(q + n * K, s + n * G, 1, K, g, ORC_F32, wr);
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * (double)wr[k];
             y_rows[m * nrows + i] = acc;
         }
         free(wr);
     }
+    free(xd);
     return 0;
 }
 
@@ -736,6 +753,8 @@ int orc_gemm_rows_mxfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f
     if (!x_f16 || !q || !e8 || !y_rows || M <= 0 || N <= 0 || K <= 0 || K % 32) return ORC_EINVAL;
     if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
     int64_t G = K / 32;
+    double* xd = x_to_f64(x_f16, M * K);
+    if (!xd) return ORC_EINVAL;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t n = n0 + i;
@@ -743,11 +762,12 @@ int orc_gemm_rows_mxfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f
         orc_dequant_mxfp4(q + n * K, e8 + n * G, 1, K, ORC_F32, wr);
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) acc += (double)orc_f16_to_f32(x_f16[m * K + k]) * (double)wr[k];
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * (double)wr[k];
             y_rows[m * nrows + i] = acc;
         }
         free(wr);
     }
+    free(xd);
     return 0;
 }
 

@@ -338,3 +338,33 @@ def test_read_probe_argument_checks():
     assert f(A, 1 << 20, 1 << 24, 1, 8, 2, A, None) == wq.WQ_EINVAL
     assert f(B, 1 << 20, 1 << 24, 1, 8, 0, A, None) == wq.WQ_EALIGN
     assert f(A, 1 << 20, 1 << 24, 1, 8, 0, ctypes.c_void_p((1 << 20) + 2), None) == wq.WQ_EALIGN
+
+
+def test_binding_rejects_bad_activations_and_outputs():
+    """The Python binding checks x (contiguous fp16 [M][K] on the weights'
+    device) and a caller-given y (contiguous fp16 [M][N]) before any C call:
+    a wrong dtype or shape would otherwise be read as fp16 bits or written out
+    of bounds."""
+    import torch
+    N, K, g = 32, 256, 128
+    qb, sb, zb = wq.wq_layout_bytes(N, K, g)
+    qw = wq.QuantizedWeight(torch.zeros(qb, dtype=torch.uint8), torch.zeros((N, K // g), dtype=torch.float16),
+                            torch.zeros((N, zb // N), dtype=torch.uint8), N, K, g)
+    x = torch.zeros((3, K), dtype=torch.float16)
+    with pytest.raises(ValueError, match="float16"):
+        wq.wq_gemm_w4a16(x.float(), qw)
+    with pytest.raises(ValueError, match="contiguous"):
+        wq.wq_gemm_w4a16(torch.zeros((K, 3), dtype=torch.float16).t(), qw)
+    with pytest.raises(ValueError, match="K=128"):
+        wq.wq_gemm_w4a16(torch.zeros((3, 128), dtype=torch.float16), qw)
+    with pytest.raises(ValueError, match=r"\[3\]\[32\]"):
+        wq.wq_gemm_w4a16(x, qw, y=torch.zeros((3, 16), dtype=torch.float16))
+    with pytest.raises(ValueError, match=r"\[3\]\[32\]"):
+        wq.wq_gemm_w4a16(x, qw, y=torch.zeros((3, 32), dtype=torch.float32))
+    q8 = wq.QuantizedWeight8(torch.zeros(N * K * 2, dtype=torch.uint8), torch.zeros((N, K // g), dtype=torch.float16),
+                             N, K, g)
+    with pytest.raises(ValueError):
+        wq.wq_gemm_w8a16(x.to(torch.bfloat16), q8)
+    qm = wq.QuantizedWeightMX(torch.zeros(qb, dtype=torch.uint8), torch.zeros((N, K // 32), dtype=torch.uint8), N, K)
+    with pytest.raises(ValueError):
+        wq.wq_gemm_mxfp4(x, qm, y=torch.zeros((2, 32), dtype=torch.float16))

@@ -8,7 +8,8 @@ import torch
 import oracle
 import w4a16_bit_matmul_amd as wq
 import workloads
-from parity import (assert_quantize_matches, compare_y, f16_bits, floor_for, gpu_quantize, say, to_dev_f16,
+from parity import (assert_quantize_matches, compare_y, compare_y_path, f16_bits, floor_for, gpu_quantize, ref16, say,
+                    to_dev_f16,
                     to_dev_weights)
 
 pytestmark = pytest.mark.gpu
@@ -202,8 +203,8 @@ def test_matmul_within_tolerance(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
-    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
@@ -223,8 +224,8 @@ def test_matmul_offset_activations(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
-    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
@@ -412,8 +413,8 @@ def test_matmul_symmetric_within_tolerance(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew = compare_y(y, y_ref, floor_frac=floor_for(path, M))
-    say(f"  normwise {nw:.2e} elementwise {ew:.2e}")
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
 

@@ -589,6 +589,36 @@ def test_awq_activation_side_and_statistic(orc):
     assert np.array_equal(y1, orc.gemm_f64(x, W))
 
 
+def test_channel_absmean_exact_means():
+    """The per-channel mean |x| on inputs whose fp32 sums are exact (small
+    integers and halves in fp16), against exact rational means: with M a power
+    of two the mean is exact in fp32; with M = 3 and a constant magnitude per
+    channel the correctly rounded division returns that magnitude.  Every
+    channel has its own values, so a transposed or shifted index fails."""
+    import oracle as orc
+    rng = np.random.default_rng(52)
+    for M, K in ((8, 40), (16, 24), (1, 9)):
+        mag = rng.integers(0, 200, (M, K)) / 2.0          # 0, 0.5, ... 99.5: exact in fp16
+        mag[:, 3] = 1000.0 + np.arange(M)                  # a channel of distinct large values
+        sign = np.where(rng.integers(0, 2, (M, K)) == 1, -1.0, 1.0)
+        x = workloads.f32_to_f16_bits((sign * mag).astype(np.float32))
+        got = orc.channel_absmean(x).astype(np.float64)
+        for k in range(K):
+            want = Fraction(sum(Fraction(v) for v in mag[:, k]), M)
+            assert Fraction(float(got[k])) == want, (M, k)
+    M, K = 3, 17
+    per_channel = (np.arange(K) * 3 + 1) / 4.0  # 0.25, 1.0, 1.75, ...: distinct per channel
+    sign = np.where(rng.integers(0, 2, (M, K)) == 1, -1.0, 1.0)
+    x = workloads.f32_to_f16_bits((sign * per_channel[None, :]).astype(np.float32))
+    assert np.array_equal(orc.channel_absmean(x).astype(np.float64), per_channel)
+    # a row permutation does not change exact sums; doubling every value doubles the means
+    x8 = workloads.f32_to_f16_bits((rng.integers(-64, 64, (8, 12)) / 4.0).astype(np.float32))
+    base = orc.channel_absmean(x8)
+    assert np.array_equal(orc.channel_absmean(x8[::-1].copy()), base)
+    x8d = workloads.f32_to_f16_bits((x8.view(np.float16).astype(np.float32) * 2))
+    assert np.array_equal(orc.channel_absmean(x8d), base * 2)
+
+
 # --------------------------------------------------------------------------
 # MXFP4 (quantization post, "Microscaling: NVFP4 and MXFP4"; element and scale
 # formats from the microscaling paper it cites)
@@ -696,6 +726,34 @@ def test_mxfp4_error_bound_and_device_layout():
     qq[3, 40:48] = 9
     p = orc.pack_device_mxfp4(qq)
     assert np.all(p[19 * 16 + 4: 19 * 16 + 8] == 0x99) and p.sum() == 4 * 0x99
+
+
+@pytest.mark.parametrize("M,N,K,n0,nrows", [(3, 40, 256, 10, 17), (2, 33, 96, 0, 33), (1, 21, 160, 20, 1),
+                                            (4, 50, 64, 0, 1)])
+def test_mxfp4_gemm_rows(M, N, K, n0, nrows):
+    """The MXFP4 product rows equal the fp64 product of the oracle's decoded
+    weights (the same sums in the same order) on ragged shapes, for the first,
+    middle and last row ranges; scale bytes differ per row and per block, so a
+    wrong scale-row stride or block index changes the result."""
+    import oracle as orc
+    rng = np.random.default_rng(63 + M * 7 + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W *= (2.0 ** rng.integers(-6, 7, (N, K // 32))).repeat(32, axis=1).astype(np.float32)
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    q, e8 = orc.quantize_mxfp4(W)
+    assert len(np.unique(e8)) > 8
+    w_hat = orc.dequant_mxfp4(q, e8)
+    y = orc.gemm_f64(x, w_hat)
+    assert np.array_equal(orc.gemm_rows_mxfp4_f64(x, q, e8, n0, nrows), y[:, n0:n0 + nrows])
+    assert np.array_equal(orc.gemm_rows_mxfp4_f64(x, q, e8, 0, N), y)
+    # one-hot activations select the decoded weights of one input channel, exactly
+    for k in (0, 37, K - 1):
+        xo = np.zeros((1, K), np.float32)
+        xo[0, k] = 1.0
+        yo = orc.gemm_rows_mxfp4_f64(workloads.f32_to_f16_bits(xo), q, e8, 0, N)
+        grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+        want = np.where(q[:, k] & 8, -1.0, 1.0) * grid[q[:, k] & 7] * 2.0 ** (e8[:, k // 32].astype(np.float64) - 127)
+        assert np.array_equal(yo[0], want)
 
 
 # --------------------------------------------------------------------------

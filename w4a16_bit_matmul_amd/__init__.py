@@ -116,9 +116,55 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream_obj(stream=None):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_obj(stream).cuda_stream)
+
+
+# Workspaces of calls that pass none: one per (device, stream), grown on
+# demand.  It is allocated and zero-filled on the stream the products run on,
+# so the zeros are in place before the first product reads its counters, and
+# products on one stream run in order, so they can share it (each leaves its
+# counters zero again).  Concurrent streams get separate workspaces.
+_workspaces: dict = {}
+
+
+def _default_workspace(need: int, device: torch.device, stream=None):
+    if not need:
+        return None
+    s = _stream_obj(stream)
+    key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check_x(x: torch.Tensor, K: int, weight: torch.Tensor) -> int:
+    """x must be a contiguous fp16 [M][K] tensor on the weights' device."""
+    if x.dtype != torch.float16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous 2-D float16 tensor (got {x.dtype}, shape {tuple(x.shape)})")
+    if x.shape[1] != K:
+        raise ValueError(f"x has K={x.shape[1]}, the weight K={K}")
+    if x.device != weight.device:
+        raise ValueError(f"x is on {x.device}, the weight on {weight.device}")
+    return x.shape[0]
+
+
+def _out_y(y, M: int, N: int, x: torch.Tensor) -> torch.Tensor:
+    """The output tensor: a new fp16 [M][N] tensor, or the caller's, which must
+    be exactly that (shape, dtype, contiguous, on x's device)."""
+    if y is None:
+        return torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if y.shape != (M, N) or y.dtype != torch.float16 or not y.is_contiguous() or y.device != x.device:
+        raise ValueError(f"y must be a contiguous float16 [{M}][{N}] tensor on {x.device} "
+                         f"(got {y.dtype}, shape {tuple(y.shape)}, on {y.device})")
+    return y
 
 
 _DT = {torch.float32: WQ_F32, torch.bfloat16: WQ_BF16, torch.float16: WQ_F16}
@@ -214,14 +260,13 @@ def wq_dequant(qw: QuantizedWeight, out_dtype=torch.float32, stream=None) -> tor
 
 def wq_gemm_w4a16(x: torch.Tensor, qw: QuantizedWeight, *, y: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
-    """y[M][N] = x[M][K] * What^T, What = s * (q - z), fp16 in and out."""
-    M, K = x.shape
-    assert K == qw.K, "x and the weight disagree on K"
-    if y is None:
-        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
-    need = wq_gemm_workspace_bytes(M, qw.N, qw.K, qw.group)
-    if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    """y[M][N] = x[M][K] * What^T, What = s * (q - z), fp16 in and out.
+    Without a workspace, a split-K shape uses the binding's workspace for this
+    stream (allocated once, zero-filled on the stream)."""
+    M = _check_x(x, qw.K, qw.qpacked)
+    y = _out_y(y, M, qw.N, x)
+    if workspace is None:
+        workspace = _default_workspace(wq_gemm_workspace_bytes(M, qw.N, qw.K, qw.group), x.device, stream)
     _check(lib().wq_gemm_w4a16_ex(M, qw.N, qw.K, qw.group, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s),
                                   _ptr(qw.zpacked), _ptr(y), _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
@@ -235,14 +280,13 @@ def wq_gemm_w4a16_seq_prepared(xs, qws, ys, *, workspace: torch.Tensor | None = 
     current at preparation time.  The buffers stay referenced by the function."""
     count = len(xs)
     assert len(qws) == count and len(ys) == count and count > 0
-    M, K = xs[0].shape
     q0 = qws[0]
+    M = _check_x(xs[0], q0.K, q0.qpacked)
     for x, qw, y in zip(xs, qws, ys):
-        assert x.shape == (M, K) and (qw.N, qw.K, qw.group) == (q0.N, q0.K, q0.group)
-        assert y.shape == (M, q0.N) and y.dtype == torch.float16
-    need = wq_gemm_workspace_bytes(M, q0.N, q0.K, q0.group)
-    if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=xs[0].device)
+        assert _check_x(x, q0.K, qw.qpacked) == M and (qw.N, qw.K, qw.group) == (q0.N, q0.K, q0.group)
+        _out_y(y, M, q0.N, x)
+    if workspace is None:
+        workspace = _default_workspace(wq_gemm_workspace_bytes(M, q0.N, q0.K, q0.group), xs[0].device, stream)
     arr = lambda ts: (ctypes.c_void_p * count)(*[t.data_ptr() for t in ts])
     args = (count, M, q0.N, q0.K, q0.group, arr(xs), arr([q.qpacked for q in qws]), arr([q.s for q in qws]),
             arr([q.zpacked for q in qws]), arr(ys), _ptr(workspace),
@@ -335,14 +379,12 @@ def wq_gemm_w8a16_plan(M: int, N: int, K: int, group: int, path: int = WQ_PATH_A
 
 def wq_gemm_w8a16(x: torch.Tensor, qw: QuantizedWeight8, *, y: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
-    """y[M][N] = x[M][K] * What^T, What = s * q (int8 codes), fp16 in and out."""
-    M, K = x.shape
-    assert K == qw.K, "x and the weight disagree on K"
-    if y is None:
-        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
-    need = wq_gemm_w8a16_workspace_bytes(M, qw.N, qw.K, qw.group)
-    if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    """y[M][N] = x[M][K] * What^T, What = s * q (int8 codes), fp16 in and out
+    (workspace as for wq_gemm_w4a16)."""
+    M = _check_x(x, qw.K, qw.qpacked)
+    y = _out_y(y, M, qw.N, x)
+    if workspace is None:
+        workspace = _default_workspace(wq_gemm_w8a16_workspace_bytes(M, qw.N, qw.K, qw.group), x.device, stream)
     _check(lib().wq_gemm_w8a16_ex(M, qw.N, qw.K, qw.group, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s), _ptr(y),
                                   _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                   path, _stream(stream)), "wq_gemm_w8a16")
@@ -480,14 +522,12 @@ def wq_gemm_mxfp4_plan(M: int, N: int, K: int, path: int = WQ_PATH_AUTO) -> str:
 
 def wq_gemm_mxfp4(x: torch.Tensor, qw: QuantizedWeightMX, *, y: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
-    """y[M][N] = x[M][K] * What^T with MXFP4 weights, fp16 in and out."""
-    M, K = x.shape
-    assert K == qw.K, "x and the weight disagree on K"
-    if y is None:
-        y = torch.empty((M, qw.N), dtype=torch.float16, device=x.device)
-    need = wq_gemm_mxfp4_workspace_bytes(M, qw.N, qw.K)
-    if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    """y[M][N] = x[M][K] * What^T with MXFP4 weights, fp16 in and out
+    (workspace as for wq_gemm_w4a16)."""
+    M = _check_x(x, qw.K, qw.qpacked)
+    y = _out_y(y, M, qw.N, x)
+    if workspace is None:
+        workspace = _default_workspace(wq_gemm_mxfp4_workspace_bytes(M, qw.N, qw.K), x.device, stream)
     _check(lib().wq_gemm_mxfp4_ex(M, qw.N, qw.K, _ptr(x), _ptr(qw.qpacked), _ptr(qw.e8), _ptr(y), _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(), path,
                                   _stream(stream)), "wq_gemm_mxfp4")
