@@ -10,7 +10,7 @@ value = effective GB/s = algorithmic bytes (4-bit codes + fp16 scales + 4-bit
 zero-points + fp16 x + fp16 y) / time per step.  The M=128 GEMM (TFLOP/s), the
 quantization kernel and the CPU oracle are reported alongside in the same line.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10000]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200]
 """
 from __future__ import annotations
 
@@ -29,6 +29,12 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, AMD published
 FP16_PEAK_TFLOPS = 2516.6       # MI355X dense fp16 MFMA, AMD published (256 CU x 4096 FLOP/clk x 2.4 GHz)
 METRIC = "W4A16 GEMV effective HBM GB/s (% of peak) at M=1; GEMM TFLOP/s at M=128"
 ROTATE_BYTES = 1024 << 20  # four times the 256 MB last-level cache
+SETTLE_MS = 100.0          # untimed back-to-back launches before the headline's warm-up steps
+
+
+def workloads_mod():
+    import workloads
+    return workloads
 
 
 def log(*a):
@@ -67,13 +73,14 @@ def _quantize_workload(wl):
     return Wd, xd, qw
 
 
-def _time_calls(fn, n_calls, warmup):
+def _time_calls(fn, n_calls, warmup, sync_before=True):
     """Average time per call of n_calls back-to-back calls, from events on the
     launch stream (torch's current stream, the one libwq is handed)."""
     import torch
     for i in range(warmup):
         fn(i)
-    torch.cuda.synchronize()
+    if sync_before:
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n_calls):
@@ -81,6 +88,57 @@ def _time_calls(fn, n_calls, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / n_calls  # seconds per call
+
+
+def read_clock(stream=None):
+    """Core clock in MHz measured by the library's clock probe, launched now on
+    the stream (after the work whose clock it reports) and synchronized: the
+    median over 256 one-wave workgroups of the shader clock counter's advance
+    per tick of the 100 MHz real-time counter, over a 20 us spin."""
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    out = wq.wq_clock_probe(256, 2000, stream=stream)
+    torch.cuda.synchronize()
+    c = out.cpu().double()
+    mhz = (100.0 * c[:, 0] / c[:, 1]).median().item()
+    return round(mhz, 1)
+
+
+# One timing protocol for every figure beside the headline: warm-up launches
+# of the same call until at least WARM_MS of GPU time (and at least
+# WARM_MIN_LAUNCHES launches) have run, then a timed region of at least
+# TIMED_MIN_LAUNCHES launches and TIMED_MIN_MS, between two HIP events on the
+# launch stream, with the core clock read by the clock probe right before and
+# right after the timed region.
+WARM_MS = 40.0
+WARM_MIN_LAUNCHES = 300
+TIMED_MIN_LAUNCHES = 200
+TIMED_MIN_MS = 20.0
+
+
+def timed_protocol(run_batch, batch_launches, est_us=None):
+    """run_batch() issues batch_launches back-to-back launches (one host call).
+    Returns (seconds per launch, record of the protocol: warm-up and timed
+    launch counts and the clock over the timed region)."""
+    import torch
+    if est_us is None:  # one batch to estimate the launch time
+        est_us = _time_calls(lambda i: run_batch(), 1, 0) / batch_launches * 1e6
+    warm_batches = max(1, math.ceil(max(WARM_MIN_LAUNCHES, WARM_MS * 1e3 / est_us) / batch_launches))
+    timed_batches = max(1, math.ceil(max(TIMED_MIN_LAUNCHES, TIMED_MIN_MS * 1e3 / est_us) / batch_launches))
+    for _ in range(warm_batches):
+        run_batch()
+    clk0 = read_clock()
+    run_batch()  # keeps the GPU busy while the host issues the timed region
+    t = _time_calls(lambda i: run_batch(), timed_batches, 0, sync_before=False) / batch_launches
+    clk1 = read_clock()
+    return t, {"warmup_launches": warm_batches * batch_launches, "timed_launches": timed_batches * batch_launches,
+               "timing": "back-to-back launches between two HIP events on the launch stream",
+               "clock_mhz_before": clk0, "clock_mhz_after": clk1}
+
+
+def sha256_of(a) -> str:
+    import hashlib
+    return hashlib.sha256(a.tobytes()).hexdigest()
 
 
 def _workspace(wl):
@@ -108,11 +166,42 @@ def bench_gemv(steps, warmup, name="decode_gemv"):
     # for the host; one Python call per step is timed alongside
     run_seq = wq.wq_gemm_w4a16_seq_prepared([xd] * steps, [qws[i % copies] for i in range(steps)], [y] * steps,
                                             workspace=ws)
-    for i in range(warmup):
-        wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws)
-    t_step = _time_calls(lambda i: run_seq(), 1, 0) / steps
+    # Clock settling: the GPU's clocks settle only after tens of milliseconds
+    # of sustained load, so before the warm-up steps the same product runs
+    # back to back, untimed, for about SETTLE_MS (issued 1000 launches per
+    # host call).  Then the `warmup` warm-up steps and, with no wait in
+    # between, the `steps` timed steps, each group one wq_gemm_w4a16_seq call
+    # (a timed region that began on an idle GPU would count the host's launch
+    # latency).  The core clock is read by the clock probe right after the
+    # timed region.
+    n_settle = 1000
+    settle = wq.wq_gemm_w4a16_seq_prepared([xd] * n_settle, [qws[i % copies] for i in range(n_settle)],
+                                           [y] * n_settle, workspace=ws)
+    t_settle_batch = _time_calls(lambda i: settle(), 1, 1)
+    settle_batches = max(1, math.ceil(SETTLE_MS * 1e-3 / t_settle_batch))
+    # no synchronization from here to the end of the timed steps: the settling
+    # launches still queued keep the GPU busy while the host records the first
+    # event and issues the timed steps, so the timed region never waits for the
+    # host
+    for _ in range(settle_batches):
+        settle()
+    warm = None
+    if warmup > 0:
+        warm = wq.wq_gemm_w4a16_seq_prepared([xd] * warmup, [qws[(steps + i) % copies] for i in range(warmup)],
+                                             [y] * warmup, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if warm is not None:
+        warm()
+    e0.record()
+    run_seq()
+    e1.record()
+    clock_mhz = read_clock()
+    t_step = e0.elapsed_time(e1) / 1e3 / steps
     t_single = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws), steps, 0)
-    return wl, nbytes, copies, t_step, t_single
+    clock = {"clock_mhz_after_timed_steps": clock_mhz,
+             "settle_launches_before_warmup": (settle_batches + 1) * n_settle,
+             "source": "clock probe (s_memtime against the 100 MHz s_memrealtime), launched right after the timed steps"}
+    return wl, nbytes, copies, t_step, t_single, clock
 
 
 def flush_check(calls=200, warmup=2000):
@@ -150,22 +239,19 @@ def flush_check(calls=200, warmup=2000):
                     "rotated back-to-back figure is the benchmark value"}
 
 
-def bench_gemm(steps, warmup):
+def bench_dense_same_shape():
+    """Dense fp16 torch.matmul of the batched workload's shape (fp16 weights
+    of 470 MB, larger than the last-level cache), under the common protocol."""
+    import numpy as np
     import torch
-    import w4a16_bit_matmul_amd as wq
     import workloads
     wl = workloads.WORKLOADS["batched_gemm"]
-    Wd, xd, qw = _quantize_workload(wl)
-    copies = max(2, math.ceil(ROTATE_BYTES / wl.algorithmic_bytes()))
-    # dense fp16 reference point of the same shape (weights as fp16)
-    Wf = Wd.to(torch.float16)
-    del Wd
-    qws = _device_copies(qw, copies)
-    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
-    ws = _workspace(wl)
-    t = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws), steps, warmup)
-    t_dense = _time_calls(lambda i: torch.matmul(xd, Wf.t()), max(10, steps // 4), 3)
-    return wl, t, t_dense
+    Wf = torch.from_numpy(wl.weights().view(np.int16)).cuda().view(torch.bfloat16).to(torch.float16)
+    xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+    Wt = Wf.t()
+    t, proto = timed_protocol(lambda: torch.matmul(xd, Wt), 1)
+    del Wf, Wt
+    return t, proto
 
 
 def bench_w8(steps, warmup):
@@ -178,8 +264,7 @@ def bench_w8(steps, warmup):
     import w4a16_bit_matmul_amd as wq
     import workloads
     out = {}
-    for name, n_steps, n_warm in (("decode_gemv", steps, warmup // 2), ("batched_gemm", max(50, steps // 2),
-                                                                        max(300, warmup // 30))):
+    for name in ("decode_gemv", "batched_gemm"):
         wl = workloads.WORKLOADS[name]
         W = wl.weights()
         Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
@@ -193,11 +278,14 @@ def bench_w8(steps, warmup):
         y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
         n = wq.wq_gemm_w8a16_workspace_bytes(wl.M, wl.N, wl.K, wl.group)
         ws = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
-        t = _time_calls(lambda i: wq.wq_gemm_w8a16(xd, qws[i % copies], y=y, workspace=ws), n_steps, n_warm)
+        nb = max(copies, 20)
+        t, proto = timed_protocol(lambda: [wq.wq_gemm_w8a16(xd, qws[i % copies], y=y, workspace=ws)
+                                           for i in range(nb)], nb)
         rec = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
                "kernel": wq.wq_gemm_w8a16_plan(wl.M, wl.N, wl.K, wl.group), "us_per_launch": round(t * 1e6, 3),
                "algorithmic_bytes": nbytes, "gbs": round(nbytes / t / 1e9, 2),
-               "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "weight_copies_rotated": copies}
+               "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "weight_copies_rotated": copies,
+               "launches": "one Python call each", **proto}
         if wl.M >= 64:
             tf = wl.flops() / t / 1e12
             rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
@@ -225,7 +313,6 @@ def bench_kv(steps, warmup):
         slot = None
         if name == "decode_append":
             slot = torch.from_numpy(rng.choice(S, T, replace=False).astype(np.int32)).cuda()
-        n = steps if name == "decode_append" else max(20, steps // 10)
         # arguments marshalled once: each timed call is one C call (the append
         # is shorter than a Python call of the binding)
         fn = wq.lib().wq_kv_quantize
@@ -234,10 +321,12 @@ def bench_kv(steps, warmup):
                 ctypes.c_void_p(cache.s.data_ptr()), ctypes.c_void_p(cache.zpacked.data_ptr()),
                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         assert fn(*args) == wq.WQ_OK
-        t = _time_calls(lambda i: fn(*args), n, min(warmup, 2000) if T < 1000 else 20)
+        nb = 50
+        t, proto = timed_protocol(lambda: [fn(*args) for _ in range(nb)], nb)
         moved = T * hd * 2 + T * hd // 2 + T * (hd // 128) * 2 + T * ((hd // 128 + 1) // 2) + (T * 4 if slot is not None else 0)
         out[name] = {"tokens": T, "values_per_token": hd, "cache_rows": S, "us_per_call": round(t * 1e6, 3),
-                     "bytes": moved, "gbs": round(moved / t / 1e9, 2), "frac_hbm_peak": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)}
+                     "bytes": moved, "gbs": round(moved / t / 1e9, 2),
+                     "frac_hbm_peak": round(moved / t / 1e9 / HBM_PEAK_GBS, 4), **proto}
         log(f"[bench] KV int4 {name}: {t * 1e6:.2f} us per call, {moved / t / 1e9:.1f} GB/s")
     return out
 
@@ -251,8 +340,7 @@ def bench_mxfp4(steps, warmup):
     import w4a16_bit_matmul_amd as wq
     import workloads
     out = {}
-    for name, n_steps, n_warm in (("decode_gemv", steps, warmup // 2), ("batched_gemm", max(50, steps // 2),
-                                                                        max(300, warmup // 30))):
+    for name in ("decode_gemv", "batched_gemm"):
         wl = workloads.WORKLOADS[name]
         Wd = torch.from_numpy(wl.weights().view(np.int16)).cuda().view(torch.bfloat16)
         xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
@@ -271,11 +359,13 @@ def bench_mxfp4(steps, warmup):
         y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
         n = wq.wq_gemm_mxfp4_workspace_bytes(wl.M, wl.N, wl.K)
         ws = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
-        t = _time_calls(lambda i: wq.wq_gemm_mxfp4(xd, qws[i % copies], y=y, workspace=ws), n_steps, n_warm)
+        nb = max(copies, 20)
+        t, proto = timed_protocol(lambda: [wq.wq_gemm_mxfp4(xd, qws[i % copies], y=y, workspace=ws)
+                                           for i in range(nb)], nb)
         rec = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "kernel": wq.wq_gemm_mxfp4_plan(wl.M, wl.N, wl.K),
                "us_per_launch_one_python_call_each": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
                "gbs": round(nbytes / t / 1e9, 2), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-               "weight_copies_rotated": copies}
+               "weight_copies_rotated": copies, **proto}
         if wl.M >= 64:
             tf = wl.flops() / t / 1e12
             rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
@@ -364,7 +454,11 @@ def bench_read_ceiling(nbytes, steps, warmup):
     """The streaming-read probe on the decode GEMV's byte count (rounded up to
     256), rotating over >= 1 GB so that every launch reads HBM: the best of
     1, 2, 4 and 8 16-byte loads per thread, plain or non-temporal.  Each timed
-    run is one C call that issues every launch, so the host never gaps the GPU."""
+    run is one C call that issues every launch, so the host never gaps the GPU.
+    Then one launch reading 1 GiB at once (four times the last-level cache),
+    under the common protocol: its rate is the steady-state read bandwidth,
+    and the decode-sized read's time minus its bytes at that rate is the
+    per-launch fixed cost (launch, ramp, drain)."""
     import torch
     import w4a16_bit_matmul_amd as wq
     window = (nbytes + 255) // 256 * 256
@@ -381,17 +475,36 @@ def bench_read_ceiling(nbytes, steps, warmup):
                 best = (t, chunks, nt)
     del buf
     t, chunks, nt = best
-    return {"bytes_per_launch": window, "us_per_launch": round(t * 1e6, 3), "gbs": round(window / t / 1e9, 2),
-            "frac_hbm_peak": round(window / t / 1e9 / HBM_PEAK_GBS, 4), "loads_per_thread": chunks,
-            "nontemporal": nt, "windows_rotated": nwin}
+    rec = {"bytes_per_launch": window, "us_per_launch": round(t * 1e6, 3), "gbs": round(window / t / 1e9, 2),
+           "frac_hbm_peak": round(window / t / 1e9 / HBM_PEAK_GBS, 4), "loads_per_thread": chunks,
+           "nontemporal": nt, "windows_rotated": nwin}
+    big = 1 << 30
+    buf = torch.ones(big // 4, dtype=torch.int32, device="cuda")
+    best_big = None
+    for chunks in (2, 4, 8):
+        tb, proto = timed_protocol(lambda: wq.wq_read_probe(buf, big, 1, chunks=chunks, nontemporal=True, sink=sink), 1)
+        if best_big is None or tb < best_big[0]:
+            best_big = (tb, chunks, proto)
+    del buf
+    tb, chunks_b, proto = best_big
+    bw = big / tb
+    rec["one_launch_1gib"] = {"bytes": big, "us_per_launch": round(tb * 1e6, 2), "gbs": round(bw / 1e9, 1),
+                              "frac_hbm_peak": round(bw / 1e9 / HBM_PEAK_GBS, 4), "loads_per_thread": chunks_b,
+                              "nontemporal": True, **proto}
+    rec["fixed_cost_us_at_decode_size"] = round((t - window / bw) * 1e6, 3)
+    log(f"[bench] read ceiling: {window} B in {t * 1e6:.2f} us; 1 GiB in one launch {tb * 1e6:.1f} us "
+        f"({bw / 1e9:.0f} GB/s); fixed cost {rec['fixed_cost_us_at_decode_size']} us")
+    return rec
 
 
-def bench_configs(steps):
+def bench_configs():
     """Every workload (the tiny case, decode, the M=16 up-projection, the M=128
     GEMM and the g=32 sweep of 70B layer shapes) on the kernel WQ_PATH_AUTO
-    picks: time per launch from one wq_gemm_w4a16_seq call of back-to-back
-    launches (weights rotated over >= 1 GB of copies, at most 128), after one
-    untimed call; effective GB/s and TFLOP/s."""
+    picks, under the common timing protocol (timed_protocol): launches issued
+    by wq_gemm_w4a16_seq calls (arguments marshalled beforehand, so the host
+    never gaps the GPU), weights rotated over >= 1 GB of copies (at most 128);
+    effective GB/s and TFLOP/s, the inputs' SHA-256 and the clock.  The M=16
+    up-projection is also timed on the split-K GEMV kernel (forced)."""
     import numpy as np
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -404,6 +517,7 @@ def bench_configs(steps):
             qcache.clear()
             torch.cuda.empty_cache()
             W = wl.weights()
+            w_sha = sha256_of(W)
             if W.dtype == np.uint16:
                 Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
             else:
@@ -411,26 +525,70 @@ def bench_configs(steps):
             qw = wq.wq_quantize_groups(Wd, wl.group)["qw"]
             del Wd, W
             copies = min(128, max(2, math.ceil(ROTATE_BYTES / wl.algorithmic_bytes())))
-            qcache[key] = _device_copies(qw, copies)
-        qws = qcache[key]
+            qcache[key] = (_device_copies(qw, copies), w_sha)
+        qws, w_sha = qcache[key]
         copies = len(qws)
-        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        x = wl.activations()
+        xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
         y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
         ws = _workspace(wl)
-        n = max(steps, copies)
-        run_seq = wq.wq_gemm_w4a16_seq_prepared([xd] * n, [qws[i % copies] for i in range(n)], [y] * n,
-                                                workspace=ws)
-        run_seq()
-        t = _time_calls(lambda i: run_seq(), 1, 0) / n
         nbytes = wl.algorithmic_bytes()
-        out[name] = {"M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
-                     "kernel": wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group), "us_per_launch": round(t * 1e6, 3),
-                     "algorithmic_bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1),
-                     "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "tflops": round(wl.flops() / t / 1e12, 2), "weight_copies_rotated": copies}
-        log(f"[bench] {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.0f} GB/s, "
-            f"{wl.flops() / t / 1e12:.1f} TFLOP/s")
+        n = max(copies, 50)
+        paths = [("auto", wq.WQ_PATH_AUTO)]
+        if name == "mlp_up_decode":
+            paths.append(("forced_gemv", wq.WQ_PATH_GEMV))
+        for tag, path in paths:
+            if path == wq.WQ_PATH_AUTO:
+                run_seq = wq.wq_gemm_w4a16_seq_prepared([xd] * n, [qws[i % copies] for i in range(n)], [y] * n,
+                                                        workspace=ws)
+            else:  # one Python call per launch: the GEMV path has no sequence entry point
+                wsg = torch.zeros(max(1, wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group, path)),
+                                  dtype=torch.uint8, device="cuda")
+                run_seq = lambda: [wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=wsg, path=path)
+                                   for i in range(n)]
+            t, proto = timed_protocol(run_seq, n)
+            rec = {"M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
+                   "kernel": wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group, path), "us_per_launch": round(t * 1e6, 3),
+                   "algorithmic_bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1),
+                   "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                   "tflops": round(wl.flops() / t / 1e12, 2),
+                   "frac_fp16_peak": round(wl.flops() / t / 1e12 / FP16_PEAK_TFLOPS, 4),
+                   "weight_copies_rotated": copies, **proto, "W_sha256": w_sha, "x_sha256": sha256_of(x)}
+            if tag == "auto":
+                out[name] = rec
+            else:
+                out[name][tag] = rec
+            log(f"[bench] {name} ({tag}): {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.0f} GB/s, "
+                f"{wl.flops() / t / 1e12:.1f} TFLOP/s, clock {proto.get('clock_mhz_after')} MHz")
     return out
+
+
+def bench_matrix_ceiling():
+    """The matrix-core counterpart of the read ceiling: the library's MFMA
+    probe (v_mfma_f32_16x16x32_f16 on register operands, nothing else) on 1024
+    workgroups of four waves, and a compute-bound dense fp16 GEMM
+    (torch.matmul, hipBLASLt, 8192 x 8192 x 8192), each under the common
+    protocol with the clock sampled."""
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wgs, iters, per_batch = 1024, 1024, 10
+    flop = wq.wq_mfma_probe(wgs, iters, 1, sink=sink)
+    t, proto = timed_protocol(lambda: wq.wq_mfma_probe(wgs, iters, per_batch, sink=sink), per_batch)
+    probe = {"instruction": "v_mfma_f32_16x16x32_f16", "flop_per_launch": flop, "us_per_launch": round(t * 1e6, 2),
+             "tflops": round(flop / t / 1e12, 1), "frac_fp16_peak": round(flop / t / 1e12 / FP16_PEAK_TFLOPS, 4),
+             "grid": f"{wgs} workgroups x 256 threads, {iters} x 8 MFMAs per wave", **proto}
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.float16, device="cuda")
+    t2, proto2 = timed_protocol(lambda: torch.matmul(a, b, out=c), 1)
+    dense = {"shape": [n, n, n], "us_per_call": round(t2 * 1e6, 1), "tflops": round(2 * n ** 3 / t2 / 1e12, 1),
+             "frac_fp16_peak": round(2 * n ** 3 / t2 / 1e12 / FP16_PEAK_TFLOPS, 4), **proto2}
+    del a, b, c
+    log(f"[bench] matrix ceiling: MFMA probe {probe['tflops']} TFLOP/s at {probe.get('clock_mhz_after')} MHz; "
+        f"dense fp16 GEMM 8192^3 {dense['tflops']} TFLOP/s")
+    return {"mfma_probe": probe, "dense_fp16_gemm_8192": dense}
 
 
 def bench_quantize(wl_name="decode_gemv", reps=20):
@@ -439,7 +597,7 @@ def bench_quantize(wl_name="decode_gemv", reps=20):
     import workloads
     wl = workloads.WORKLOADS[wl_name]
     Wd, _, qw = _quantize_workload(wl)
-    t = _time_calls(lambda i: wq.wq_quantize_groups(Wd, wl.group, out=qw), reps, 3)
+    t, _ = timed_protocol(lambda: wq.wq_quantize_groups(Wd, wl.group, out=qw), 1)
     qbytes, sbytes, zbytes = wq.wq_layout_bytes(wl.N, wl.K, wl.group)
     moved = wl.N * wl.K * 2 + qbytes + sbytes + zbytes
     return t, moved
@@ -474,31 +632,56 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(target_s=12.0):
-    """The C oracle's fused product (dequantize each weight row, fp64 dot with
-    x) over the whole decode workload, repeated for about target_s seconds on
-    all host threads; reported in the metric's unit (algorithmic GB/s)."""
-    import oracle
-    import workloads
-    wl = workloads.WORKLOADS["decode_gemv"]
-    threads = len(os.sched_getaffinity(0))
-    oracle.set_threads(threads)
-    W = wl.weights()
-    x = wl.activations()
-    q, s, z = oracle.quantize_groups(W, wl.group, dtype=oracle.BF16)
+def _oracle_rate(fn, nbytes, target_s):
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
+        fn()
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= target_s:
             break
-    per = dt / reps
-    return {"value": round(wl.algorithmic_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+    return nbytes * reps / dt / 1e9, reps, dt
+
+
+def cpu_baseline(target_s=12.0, leg_s=3.0):
+    """The C oracle timed on the host: its fused product (dequantize each
+    weight row, fp64 dot with x) over the whole decode workload for about
+    target_s seconds on all host threads, reported in the metric's unit
+    (algorithmic GB/s); beside it, legs of about leg_s seconds each: the
+    product on one thread, and the oracle's quantization of the same weights
+    (bf16 read, codes, scales and zero-points written) on all threads and on
+    one."""
+    import oracle
+    import workloads
+    wl = workloads.WORKLOADS["decode_gemv"]
+    threads = len(os.sched_getaffinity(0))
+    W = wl.weights()
+    x = wl.activations()
+    oracle.set_threads(threads)
+    q, s, z = oracle.quantize_groups(W, wl.group, dtype=oracle.BF16)
+    nbytes = wl.algorithmic_bytes()
+    product = lambda: oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
+    rate, reps, dt = _oracle_rate(product, nbytes, target_s)
+    qbytes = wl.N * wl.K * 2 + wl.N * wl.K // 2 + wl.N * (wl.K // wl.group) * 2 + wl.N * (wl.K // wl.group + 1) // 2
+    quant = lambda: oracle.quantize_groups(W, wl.group, dtype=oracle.BF16)
+    legs = {}
+    for tag, n in (("all_threads", threads), ("one_thread", 1)):
+        oracle.set_threads(n)
+        if n == 1:
+            r, k, d = _oracle_rate(product, nbytes, leg_s)
+            legs[f"product_{tag}"] = {"gbs": round(r, 4), "threads": n, "reps": k, "seconds": round(d, 2)}
+        r, k, d = _oracle_rate(quant, qbytes, leg_s)
+        legs[f"quantize_{tag}"] = {"gbs": round(r, 4), "threads": n, "reps": k, "seconds": round(d, 2),
+                                   "bytes": qbytes}
+    oracle.set_threads(threads)
+    legs["product_all_threads"] = {"gbs": round(rate, 4), "threads": threads, "reps": reps, "seconds": round(dt, 2)}
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"whole decode_gemv product (M=1, N=K={wl.K}, g={wl.group}): C oracle dequantizes each "
-                      f"row and takes fp64 dot products, {reps} repetitions in {dt:.1f}s ({per * 1e3:.1f} ms each), "
-                      f"{threads} OpenMP threads"}
+                      f"row and takes fp64 dot products, {reps} repetitions in {dt:.1f}s "
+                      f"({dt / reps * 1e3:.1f} ms each), {threads} OpenMP threads; legs: the same product on one "
+                      f"thread, and the oracle's quantization of the same 8192x8192 bf16 weights on all threads "
+                      f"and on one (GB/s of bf16 in + codes, scales, zero-points out), about {leg_s:.0f} s each",
+            "legs": legs}
 
 
 def main():
@@ -506,9 +689,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU's clocks settle only after tens of milliseconds of sustained
-    # load: the default warm-up runs the decode GEMV for about 85 ms
-    ap.add_argument("--warmup", type=int, default=10000)
+    # warm-up steps after the ~100 ms of untimed clock settling
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the decode GEMV")
     ap.add_argument("--sweep", action="store_true",
@@ -547,13 +729,13 @@ def main():
         return
     if args.flush_check:
         rec = flush_check()
-        _, _, copies, t_step, _ = bench_gemv(args.steps, args.warmup)
+        _, _, copies, t_step, _, _ = bench_gemv(args.steps, args.warmup)
         rec["us_per_call_rotated_back_to_back"] = round(t_step * 1e6, 3)
         rec["rotated_weight_copies"] = copies
         rec["rotate_mb"] = args.rotate_mb
         print(json.dumps(rec), flush=True)
         return
-    wl, nbytes, copies, t_step, t_single = bench_gemv(args.steps, args.warmup)
+    wl, nbytes, copies, t_step, t_single, clock = bench_gemv(args.steps, args.warmup)
     plan = wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group)
     log(f"[bench] decode GEMV: {t_step * 1e6:.2f} us per launch back to back "
         f"(one Python call per launch: {t_single * 1e6:.2f} us), {copies} weight copies; {plan}")
@@ -590,21 +772,32 @@ def main():
                      "timing": f"{args.steps} back-to-back launches (one wq_gemm_w4a16_seq call) between two "
                                f"HIP events on the launch stream",
                      "us_per_launch": round(t_step * 1e6, 3),
-                     "us_per_launch_one_python_call_each": round(t_single * 1e6, 3)},
+                     "us_per_launch_one_python_call_each": round(t_single * 1e6, 3),
+                     "clock": clock},
     }
+    line["config"].update(W_sha256=sha256_of(wl.weights()), x_sha256=sha256_of(wl.activations()))
     if not args.no_extras:
-        # the GEMM draws enough power that the clock settles only after tens of
-        # milliseconds of sustained work: warm it for at least 300 launches
-        gwl, t_gemm, t_dense = bench_gemm(max(50, args.steps // 2), max(300, args.warmup // 30))
-        tflops = gwl.flops() / t_gemm / 1e12
+        # every other figure below follows one timing protocol (timed_protocol):
+        # >= 40 ms and >= 300 launches of warm-up, then >= 200 launches and
+        # >= 20 ms timed, the clock sampled over the timed region
+        line["configs"] = bench_configs()
+        bg = line["configs"]["batched_gemm"]
+        t_dense, proto_dense = bench_dense_same_shape()
+        ceiling = bench_matrix_ceiling()
+        gwl = workloads_mod().WORKLOADS["batched_gemm"]
         line["gemm_m128"] = {"workload": gwl.name, "M": gwl.M, "N": gwl.N, "K": gwl.K, "group": gwl.group,
-                             "kernel": wq.wq_gemm_plan(gwl.M, gwl.N, gwl.K, gwl.group), "bound": "mfma",
-                             "us_per_launch": round(t_gemm * 1e6, 2),
-                             "tflops": round(tflops, 2), "peak_tflops": FP16_PEAK_TFLOPS,
-                             "frac_fp16_peak": round(tflops / FP16_PEAK_TFLOPS, 4),
+                             "kernel": bg["kernel"], "bound": "mfma", "us_per_launch": bg["us_per_launch"],
+                             "tflops": bg["tflops"], "peak_tflops": FP16_PEAK_TFLOPS,
+                             "frac_fp16_peak": bg["frac_fp16_peak"],
+                             "frac_of_mfma_probe": round(bg["tflops"] / ceiling["mfma_probe"]["tflops"], 4),
+                             "source": "the batched_gemm entry of configs (same measurement)",
+                             "warmup_launches": bg["warmup_launches"], "timed_launches": bg["timed_launches"],
+                             "clock_mhz_after": bg.get("clock_mhz_after"),
                              "dense_fp16_torch_matmul_us": round(t_dense * 1e6, 2),
-                             "dense_fp16_tflops": round(gwl.flops() / t_dense / 1e12, 2)}
-        log(f"[bench] M=128 GEMM: {t_gemm * 1e6:.1f} us per launch, {tflops:.1f} TFLOP/s; "
+                             "dense_fp16_tflops": round(gwl.flops() / t_dense / 1e12, 2),
+                             "dense_fp16_protocol": proto_dense}
+        line["matrix_ceiling"] = ceiling
+        log(f"[bench] M=128 GEMM: {bg['us_per_launch']:.1f} us per launch, {bg['tflops']:.1f} TFLOP/s; "
             f"dense fp16 {t_dense * 1e6:.1f} us")
         tq, moved = bench_quantize()
         line["quantize"] = {"workload": "decode_gemv weights (bf16 8192x8192, g=128)", "us": round(tq * 1e6, 2),
@@ -613,9 +806,8 @@ def main():
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
         line["awq_fold"] = bench_awq()
         line["mxfp4"] = bench_mxfp4(args.steps, args.warmup)
-        line["read_ceiling"] = bench_read_ceiling(nbytes, args.steps, max(1, min(2000, args.warmup)))
+        line["read_ceiling"] = bench_read_ceiling(nbytes, max(200, args.steps), 2000)
         line["read_ceiling"]["gemv_frac_of_ceiling"] = round(line["read_ceiling"]["us_per_launch"] / (t_step * 1e6), 4)
-        line["configs"] = bench_configs(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -429,6 +429,35 @@ int wq_kv_dequant(const uint8_t* codes, const uint16_t* s_f16, const uint8_t* zp
 int wq_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks,
                   int nontemporal, uint32_t* sink, void* stream);
 
+/* ---- Matrix-core probe (a measurement aid, not a step of the method) --------
+ * Past the ridge point the batched product is bound by its matrix-core work
+ * ("Hardware, formats and the roofline"), so the rate at which this GPU
+ * sustains the fp16 MFMA instruction the product kernels issue
+ * (v_mfma_f32_16x16x32_f16, 16,384 FLOP each), with no memory traffic and no
+ * other vector work and at the clock the part holds under that load, is that
+ * product's ceiling on this part, next to the nominal dense fp16 peak.
+ * Issues `count` launches back to back on `stream`, each of `workgroups`
+ * workgroups of 256 threads (four waves); every wave issues iters x 8 MFMAs,
+ * so one launch performs workgroups * 4 * iters * 8 * 16384 FLOP.  Writes
+ * nothing to memory except, on one fixed result, a word to *sink.
+ *   sink    one device word, 4-byte aligned
+ * WQ_EINVAL for a NULL sink or a non-positive size (count == 0 enqueues
+ * nothing), WQ_EALIGN for a misaligned sink. */
+int wq_mfma_probe(int workgroups, int iters, int count, uint32_t* sink, void* stream);
+
+/* ---- Clock probe (a measurement aid) ----------------------------------------
+ * The matrix-core and read ceilings above depend on the core clock the part
+ * holds under load, so timed regions are paired with a reading of it: one
+ * launch of `workgroups` workgroups of one wave, each spinning for `ticks`
+ * ticks of the constant 100 MHz real-time counter (s_memrealtime) and writing
+ * how far the shader clock counter (s_memtime) and the real-time counter
+ * advanced: out[2b] and out[2b + 1] for workgroup b (device memory, 8-byte
+ * aligned, 2 * workgroups entries).  Core clock = 100 MHz * out[2b] / out[2b+1].
+ * The spin also ends after a fixed number of counter reads.
+ * WQ_EINVAL for a NULL out, workgroups outside 1..65536 or ticks outside
+ * 1..10^7; WQ_EALIGN for a misaligned out. */
+int wq_clock_probe(int workgroups, uint32_t ticks, unsigned long long* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

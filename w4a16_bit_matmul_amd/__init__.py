@@ -35,7 +35,7 @@ EXPORTED = (
     "wq_quantize_groups_scaled", "wq_scale_activations", "wq_channel_absmean",
     "wq_layout_bytes_mxfp4", "wq_quantize_mxfp4", "wq_pack_mxfp4", "wq_dequant_mxfp4",
     "wq_gemm_mxfp4_workspace_bytes", "wq_gemm_mxfp4", "wq_gemm_mxfp4_ex", "wq_gemm_mxfp4_plan",
-    "wq_read_probe",
+    "wq_read_probe", "wq_mfma_probe", "wq_clock_probe",
 )
 
 _lib = None
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_mxfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_mxfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
         "wq_read_probe": (I, [P, SZ, SZ, I, I, I, P, P]),
+        "wq_mfma_probe": (I, [I, I, I, P, P]),
+        "wq_clock_probe": (I, [I, ctypes.c_uint32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -545,3 +547,26 @@ def wq_read_probe(src: torch.Tensor, window_bytes: int, count: int, *, chunks: i
     _check(lib().wq_read_probe(_ptr(src), window_bytes, span, count, chunks, int(nontemporal), _ptr(sink),
                                _stream(stream)),
            "wq_read_probe")
+
+
+MFMA_PROBE_FLOP_PER_WAVE_ITER = 8 * 16384  # eight v_mfma_f32_16x16x32_f16 per wave and iteration
+
+
+def wq_mfma_probe(workgroups: int, iters: int, count: int, *, sink: torch.Tensor | None = None, stream=None) -> int:
+    """count launches of the matrix-core probe; returns the FLOP of one launch
+    (workgroups x 4 waves x iters x 8 x 16384)."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _check(lib().wq_mfma_probe(workgroups, iters, count, _ptr(sink), _stream(stream)), "wq_mfma_probe")
+    return workgroups * 4 * iters * MFMA_PROBE_FLOP_PER_WAVE_ITER
+
+
+def wq_clock_probe(workgroups: int = 256, ticks: int = 2000, stream=None):
+    """Enqueues the clock probe on the stream and returns the device tensor
+    [workgroups][2] (shader clock counter advance, 100 MHz real-time counter
+    advance); synchronize before reading it.  Core clock in MHz =
+    100 * out[:, 0] / out[:, 1]."""
+    out = torch.zeros((workgroups, 2), dtype=torch.int64, device="cuda")
+    _check(lib().wq_clock_probe(workgroups, ticks, _ptr(out), _stream(stream)), "wq_clock_probe")
+    return out
+

@@ -23,7 +23,9 @@ PER_FILE = {
     "wq_quant.hip": ["-ffp-contract=off"],
     "wq_gemv.hip": [],
     "wq_gemm.hip": [],
-    "wq_probe.hip": [],
+    # the probe's loop-carried MFMA accumulators stay in place only in the
+    # VGPR form (the default AGPR form rotates them through copies every turn)
+    "wq_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "wq_api.cpp": [],
 }
 

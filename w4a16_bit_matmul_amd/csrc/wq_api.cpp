@@ -442,3 +442,16 @@ int wq_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int c
   return hip_status(wq::launch_read_probe(src, window_bytes, span_bytes, count, chunks, nontemporal, sink,
                                           static_cast<hipStream_t>(stream)));
 }
+
+int wq_mfma_probe(int workgroups, int iters, int count, uint32_t* sink, void* stream) {
+  if (!sink || workgroups <= 0 || iters <= 0 || count < 0) return WQ_EINVAL;
+  if (!aligned(sink, 4)) return WQ_EALIGN;
+  if (count == 0) return WQ_OK;
+  return hip_status(wq::launch_mfma_probe(workgroups, iters, count, sink, static_cast<hipStream_t>(stream)));
+}
+
+int wq_clock_probe(int workgroups, uint32_t ticks, unsigned long long* out, void* stream) {
+  if (!out || workgroups <= 0 || workgroups > 65536 || ticks == 0 || ticks > 10000000u) return WQ_EINVAL;
+  if (!aligned(out, 8)) return WQ_EALIGN;
+  return hip_status(wq::launch_clock_probe(workgroups, ticks, out, static_cast<hipStream_t>(stream)));
+}

@@ -541,7 +541,9 @@ hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
   const dim3 g2 = gemm_grid(MB, a.M, a.N), grid(g2.x, g2.y, (unsigned)a.KS), block(kWaves * 64);
   const size_t lds = gemm_lds(MB, G, FMT);
   auto k = gemm_kernel<MB, G, SZV, FMT>;
-  if (lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit((const void*)k, lds, lds_raised);
+  if (e != hipSuccess) return e;
   k<<<grid, block, lds, stream>>>(a);
   return hipGetLastError();
 }

@@ -440,24 +440,21 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
 }
 
 template <int MT, int W, int G, int FMT>
-void launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   auto k = gemv_kernel<MT, W, kKQ, G, FMT>;
-  if (p.lds > 65536) hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
+  if (e != hipSuccess) return e;
   k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
+  return hipGetLastError();
 }
 
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
-  if (fmt == kFmtMxfp4) {
-    launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
-  } else if (fmt == kFmtInt8) {
-    if (group == 128) launch_k<MT, W, 128, kFmtInt8>(p, a, stream);
-    else launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
-  } else {
-    if (group == 128) launch_k<MT, W, 128, kFmtInt4>(p, a, stream);
-    else launch_k<MT, W, 32, kFmtInt4>(p, a, stream);
-  }
-  return hipGetLastError();
+  if (fmt == kFmtMxfp4) return launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
+  if (fmt == kFmtInt8)
+    return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
+  return group == 128 ? launch_k<MT, W, 128, kFmtInt4>(p, a, stream) : launch_k<MT, W, 32, kFmtInt4>(p, a, stream);
 }
 
 }  // namespace

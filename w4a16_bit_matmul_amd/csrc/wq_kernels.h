@@ -4,7 +4,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace wq {
+
+// Raises a kernel's dynamic LDS limit to `lds` bytes (needed above 64 KiB)
+// once per device: the attribute stays with the function on that device, so
+// later launches skip the runtime call.  `done` is the kernel instance's own
+// set of devices already raised (one bit per device; devices past 63 raise it
+// on every launch).
+inline hipError_t raise_lds_limit(const void* kernel, size_t lds, std::atomic<uint64_t>& done) {
+  if (lds <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // sym: the symmetric 4-bit scheme (codes q + 8, zero-point 8) instead of the
 // asymmetric one.  alpha (fp32 [K] or NULL): per-input-channel factors applied
@@ -75,5 +94,15 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
 // words hits a fixed value.
 hipError_t launch_read_probe(const void* src, size_t window_bytes, size_t span_bytes, int count, int chunks,
                              int nontemporal, uint32_t* sink, hipStream_t stream);
+
+// Matrix-core probe: count launches of `workgroups` workgroups of four waves,
+// each wave issuing iters x 8 v_mfma_f32_16x16x32_f16 on register operands
+// (16,384 FLOP each).  sink: one device word, written only on a fixed result.
+hipError_t launch_mfma_probe(int workgroups, int iters, int count, uint32_t* sink, hipStream_t stream);
+
+// Clock probe: `workgroups` workgroups of one wave spin for `ticks` ticks of
+// the 100 MHz real-time counter; workgroup b writes the shader clock counter's
+// and the real-time counter's advance to out[2b], out[2b + 1].
+hipError_t launch_clock_probe(int workgroups, uint32_t ticks, unsigned long long* out, hipStream_t stream);
 
 }  // namespace wq
