@@ -248,6 +248,29 @@ int wq_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, int group,
                      const uint8_t* zpacked, uint16_t* y_f16,
                      void* workspace, size_t workspace_bytes, int path, void* stream);
 
+/* Bytes of the fixed per-GPU scratch of wq_gemm_w4a16_noalloc: the split-K
+ * counter region and 16 MiB of fp32 partial sums (enough for every product
+ * whose kernel splits K at K <= 28672 with N up to 8192 at M = 128, e.g. the
+ * 8192 x 28672 down projection). */
+#define WQ_NOALLOC_SCRATCH_BYTES (WQ_WORKSPACE_COUNTER_BYTES + (16 << 20))
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * wq_gemm_w4a16 with the workspace taken from a fixed device array of
+ * WQ_NOALLOC_SCRATCH_BYTES that the library holds once per GPU for the life of
+ * the process, instead of from the caller.  Same arguments (minus the
+ * workspace), kernels, results and errors as wq_gemm_w4a16; calls no
+ * allocating routine.  WQ_EWORKSPACE when the product's kernel would need more
+ * scratch than WQ_NOALLOC_SCRATCH_BYTES (nothing is enqueued).  The first call
+ * on a device looks up that device's scratch address and clears its counters
+ * with a kernel on `stream`; each product leaves them zero again.  Every call
+ * on one GPU shares that GPU's scratch: calls that may overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * must be serialized by the caller. */
+int wq_gemm_w4a16_noalloc(int64_t M, int64_t N, int64_t K, int group,
+                          const uint16_t* x_f16, const uint32_t* qpacked, const uint16_t* s_f16,
+                          const uint8_t* zpacked, uint16_t* y_f16, void* stream);
+
 /* ---- Group absmax int8 weights (W8A16) --------------------------------------
  * The int8 rule of "Quantization Methods Compared: INT8, GPTQ, AWQ, FP8, FP4
  * and KV-Cache Quantization", section "What quantisation does: scale, round,

@@ -24,11 +24,13 @@ WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_ASYM, WQ_SYM = 0, 1
 WQ_AUTO_MFMA_MIN_M = 5  # smallest M that WQ_PATH_AUTO runs on the MFMA GEMM kernel
 WQ_WORKSPACE_COUNTER_BYTES = 2048  # leading counter bytes of a split-K workspace (zero before first use)
+WQ_NOALLOC_SCRATCH_BYTES = WQ_WORKSPACE_COUNTER_BYTES + (16 << 20)  # per-GPU scratch of wq_gemm_w4a16_noalloc
 
 EXPORTED = (
     "wq_version", "wq_strerror", "wq_layout_bytes", "wq_quantize_groups", "wq_quantize_groups_ex", "wq_pack_int4",
     "wq_dequant",
     "wq_gemm_workspace_bytes", "wq_gemm_workspace_bytes_ex", "wq_gemm_plan", "wq_gemm_w4a16", "wq_gemm_w4a16_ex", "wq_gemm_w4a16_seq",
+    "wq_gemm_w4a16_noalloc",
     "wq_layout_bytes_w8", "wq_quantize_w8", "wq_pack_int8", "wq_dequant_w8", "wq_gemm_w8a16_workspace_bytes",
     "wq_gemm_w8a16", "wq_gemm_w8a16_ex", "wq_gemm_w8a16_plan",
     "wq_kv_layout_bytes", "wq_kv_quantize", "wq_kv_dequant",
@@ -71,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_w4a16": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
         "wq_gemm_w4a16_ex": (I, [I64, I64, I64, I, P, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_w4a16_seq": (I, [I, I64, I64, I64, I, P, P, P, P, P, P, SZ, P]),
+        "wq_gemm_w4a16_noalloc": (I, [I64, I64, I64, I, P, P, P, P, P, P]),
         "wq_layout_bytes_w8": (I, [I64, I64, I, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "wq_quantize_w8": (I, [P, I, I64, I64, I, P, P, P, P]),
         "wq_pack_int8": (I, [P, I64, I64, P, P]),
@@ -273,6 +276,18 @@ def wq_gemm_w4a16(x: torch.Tensor, qw: QuantizedWeight, *, y: torch.Tensor | Non
                                   _ptr(qw.zpacked), _ptr(y), _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
                                   path, _stream(stream)), "wq_gemm_w4a16")
+    return y
+
+
+def wq_gemm_w4a16_noalloc(x: torch.Tensor, qw: QuantizedWeight, *, y: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """wq_gemm_w4a16 through the allocation-free entry point: its split-K
+    scratch is the library's fixed per-GPU array (calls on one GPU must not
+    overlap).  With y given, this wrapper allocates nothing either."""
+    M = _check_x(x, qw.K, qw.qpacked)
+    y = _out_y(y, M, qw.N, x)
+    _check(lib().wq_gemm_w4a16_noalloc(M, qw.N, qw.K, qw.group, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s),
+                                       _ptr(qw.zpacked), _ptr(y), _stream(stream)), "wq_gemm_w4a16_noalloc")
     return y
 
 

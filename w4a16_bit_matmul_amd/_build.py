@@ -26,6 +26,7 @@ PER_FILE = {
     # the probe's loop-carried MFMA accumulators stay in place only in the
     # VGPR form (the default AGPR form rotates them through copies every turn)
     "wq_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "wq_noalloc.hip": [],
     "wq_api.cpp": [],
 }
 
