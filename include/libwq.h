@@ -87,7 +87,8 @@ typedef enum {
 
 typedef enum {
     WQ_PATH_AUTO = 0, /* M < WQ_AUTO_MFMA_MIN_M: GEMV kernel; otherwise MFMA GEMM kernel */
-    WQ_PATH_GEMV = 1, /* force the split-K VALU GEMV kernel (any M) */
+    WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; 4-bit codes take their dot products on
+                         the matrix cores, int8 and MXFP4 codes on the vector units) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
 

@@ -108,10 +108,13 @@ def test_workspace_query_and_check():
             need = wq.wq_gemm_workspace_bytes(M, N, K, g, path)
             assert 0 < need <= wq.wq_gemm_workspace_bytes(M, N, K, g), (M, N, K, g, path)
             # counter region, then KS fp32 partial-sum planes padded to whole
-            # tiles: GEMV MT x 16 per workgroup, MFMA 16*MB x 128
+            # tiles: GEMV MT x 16 per workgroup (1 x 8 for the eight-row
+            # one-row kernel), MFMA 16*MB x 128
             plan = wq.wq_gemm_plan(M, N, K, g, path)
             gx, gy, ks = (int(v) for v in plan.split("grid=(", 1)[1].split(")", 1)[0].split(","))
-            if path == wq.WQ_PATH_GEMV:
+            if path == wq.WQ_PATH_GEMV and "half" in plan:
+                rows, cols = 1, 8
+            elif path == wq.WQ_PATH_GEMV:
                 rows, cols = int(plan.split("MT=", 1)[1].split(",")[0]), 16
             else:
                 rows, cols = 16 * int(plan.split("MB=", 1)[1].split(",")[0]), 128
@@ -132,10 +135,13 @@ def test_gemm_plan_names_the_dispatched_kernel():
     # (one row block of 16 outputs per workgroup, no K split) and the M=128 MFMA
     # GEMM (eight 16-row blocks per workgroup)
     d = wq.wq_gemm_plan(1, 8192, 8192, 128)
-    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=128>") and "grid=(512,1,1)" in d and "split_k=1" in d, d
+    assert d.startswith("gemv_mfma_kernel<MT=1, W=16, KQ=4, G=128>") and "grid=(512,1,1)" in d and "split_k=1" in d, d
+    # one row of x over few row blocks: eight weight rows per workgroup
+    d = wq.wq_gemm_plan(1, 1024, 8192, 32)
+    assert d.startswith("gemv_mfma_half_kernel<W=16, KQ=4, G=32>") and "grid=(128,1,1)" in d, d
     d = wq.wq_gemm_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128>") and "grid=(224,1,1)" in d, d
-    assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
+    assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=8")
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     # a small grid splits K across workgroups in whole eight-tile chunks
     d = wq.wq_gemm_plan(128, 8192, 8192, 128)
@@ -154,7 +160,7 @@ def test_gemm_plan_names_the_dispatched_kernel():
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
     lo = wq.WQ_AUTO_MFMA_MIN_M
-    assert wq.wq_gemm_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel"), lo
+    assert wq.wq_gemm_plan(lo - 1, 8192, 8192, 128).startswith("gemv_mfma_kernel"), lo
     assert wq.wq_gemm_plan(lo, 8192, 8192, 128).startswith("gemm_kernel"), lo
     assert wq.wq_gemm_w8a16_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel")
     assert wq.wq_gemm_w8a16_plan(lo, 8192, 8192, 128).startswith("gemm_kernel")

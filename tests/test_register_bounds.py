@@ -46,8 +46,11 @@ def _find(meta, fragment):
 @pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
 def test_one_row_gemv_fits_two_workgroups_per_cu():
     meta = _kernel_metadata("wq_gemv.hip")
-    # gemv_kernel<MT=1, W=16, KQ=4, G, FMT>: 4-bit at g = 128 and 32, MXFP4
-    for frag in ("gemv_kernelILi1ELi16ELi4ELi128ELi4E", "gemv_kernelILi1ELi16ELi4ELi32ELi4E",
+    # 4-bit codes: gemv_mfma_half_kernel<W=16, KQ=4, G> (the one-row launch) and
+    # gemv_mfma_kernel<MT=1, W=16, KQ=4, G>, at g = 128 and 32; MXFP4:
+    # gemv_kernel<MT=1, W=16, KQ=4, G=32, FMT>
+    for frag in ("gemv_mfma_half_kernelILi16ELi4ELi128E", "gemv_mfma_half_kernelILi16ELi4ELi32E",
+                 "gemv_mfma_kernelILi1ELi16ELi4ELi128E", "gemv_mfma_kernelILi1ELi16ELi4ELi32E",
                  "gemv_kernelILi1ELi16ELi4ELi32ELi2E"):
         for name, (vgpr, scratch) in _find(meta, frag):
             assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)

@@ -399,12 +399,310 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
   if (tid == 0) split_reset(ctr);
 }
 
+// ---- GEMV with the dot products on the matrix cores (4-bit codes, M <= 16).
+//
+// The same decomposition, loads and LDS slices as gemv_kernel, but each code
+// word j of a tile becomes one v_mfma_f32_16x16x32_f16 B operand instead of
+// four v_dot2_f32_f16 operands: lane l = r + 16c supplies B column r (weight
+// row nb*16 + r) with k-slots 8c..8c+7 of step j, which is exactly word j of
+// its 16 bytes, and A row r (activation row m0 + r, clamped to the block's
+// last row; the D rows it produces past MT are never read) with the same
+// k-slots, read from the wave's LDS slice.  The B operand is the exact fp16
+// q - z of each code:
+//   word & 0x000F000F | 0x6400 6400     = (1024 + q0, 1024 + q1)
+//   word & 0x00F000F0 | 0x5400 5400     = (  64 + q2,   64 + q3)
+// and the same two of (word >> 8) for columns 4..7 (an fp16 with exponent
+// 2^6 has unit spacing 2^-4, so code bits 4..7 land on whole numbers), minus
+// the group's (1024 + z) or (64 + z) pair; the matrix core accumulates the
+// exact products x * (q - z) in fp32 over a group, and one fp32 multiply-add
+// per group applies the scale, so the arithmetic is the VALU GEMV's with the
+// sum order of the matrix core: 9 VALU instructions per code word instead of
+// 13.  Lane (r, c) receives D rows 4c..4c+3 (activation rows) of column r.
+template <int MT, int W, int KQ, int G>
+__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfma_kernel(GemvArgs a) {
+  constexpr int GPT = 128 / G;       // groups per 128-column tile
+  constexpr int SPG = 4 / GPT;       // MFMA steps per group
+  constexpr int NS = KQ * GPT;       // groups per segment
+  constexpr int NT = W * 64;
+  constexpr int XCH = MT * KQ / 4;   // 16-byte x chunks per lane and segment
+  constexpr int NA = MT < 4 ? MT : 4;  // D elements per lane that can hold real rows
+  static_assert(KQ % 4 == 0 && XCH >= 1, "a segment is a multiple of four tiles");
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int nb = blockIdx.x, m0 = blockIdx.y * MT, ks = blockIdx.z;
+  const Dims d = dims_of<G>(a.K);
+  const int kt_lo = ks * a.kt_per_split;
+  const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
+  float* red = reinterpret_cast<float*>(smem + (size_t)W * MT * KQ * 256);  // [W][MT][16]
+
+  const uint8_t* tbase = a.qp + (size_t)nb * d.KT * kTileBytes;
+  const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
+  const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
+  const uint32_t lane16 = 16u * lane;
+  const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
+  // this lane's A row of the slice (rows past MT repeat the last one)
+  const int arow = (r < MT ? r : MT - 1) * (KQ * 128) + 8 * c;
+
+  float acc[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) acc[i] = 0.0f;
+
+  for (int sg = wv; sg * KQ < nkt; sg += W) {
+    const int q0 = sg * KQ;
+    const int nq = min(KQ, nkt - q0);
+    const int kt0 = kt_lo + q0;
+
+    u4 buf[KQ];
+    uint4 xc[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
+      const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
+      xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
+    }
+    const SZ<NS> sz = load_sz<NS, true>(a, d.Gtot, srow, zrow, kt0 * GPT);
+#pragma unroll
+    for (int t = 0; t < KQ; ++t)
+      buf[t] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * kTileBytes + lane16));
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
+      const bool ok = m0 + m < a.M && kt0 * 128 + cc * 8 < a.K;
+      *reinterpret_cast<uint4*>(xw + m * (KQ * 128) + cc * 8) = ok ? xc[i] : make_uint4(0, 0, 0, 0);
+    }
+    // the slice is read back by other lanes of this wave only
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+    for (int t = 0; t < KQ; ++t) {
+      if (t >= nq) break;
+      const uint16_t* xr = xw + arow + t * 128;
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        const uint32_t z = sz.zero(t * GPT + gi);
+        const h2 zq = as_h2(z * 0x00010001u + kMagicPair);     // (1024 + z) twice
+        const h2 z64 = as_h2(z * 0x00100010u + 0x54005400u);   // (64 + z) twice: z in mantissa bits 4..7
+        f4 T;
+#pragma unroll
+        for (int jj = 0; jj < SPG; ++jj) {
+          const int j = gi * SPG + jj;
+          const uint32_t w = buf[t][j], w8 = w >> 8;
+          const h2 p0 = as_h2((w & 0x000F000Fu) | m1024) - zq;
+          const h2 p1 = as_h2((w & 0x00F000F0u) | m64) - z64;
+          const h2 p2 = as_h2((w8 & 0x000F000Fu) | m1024) - zq;
+          const h2 p3 = as_h2((w8 & 0x00F000F0u) | m64) - z64;
+          h8 bfr;
+          bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+          bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+          const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+          T = jj == 0 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                      : __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, T, 0, 0, 0);
+        }
+        const float sc = sz.scale(t * GPT + gi);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) acc[i] = fmaf(sc, T[i], acc[i]);
+      }
+    }
+    // the next segment overwrites this wave's slice: finish reading it first
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- reduce: lane (r, c) holds rows 4c + i of column r; the W waves' sums
+  // of each (row, column) meet in LDS and are added in wave order
+  if (4 * c < MT) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      if (4 * c + i < MT) red[(wv * MT + 4 * c + i) * 16 + r] = acc[i];
+  }
+  __syncthreads();
+  constexpr int NOUT = MT * 16;
+  for (int i = tid; i < NOUT; i += NT) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * NOUT + i];
+    const int rr = i & 15, m = i >> 4;
+    const int nn = nb * 16 + rr, mm = m0 + m;
+    if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
+      split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
+    else if (nn < a.N && mm < a.M)
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+  }
+  if (a.KS == 1) return;
+
+  // ---- split-K: the last workgroup of this row range adds the partial sums
+  unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
+  if (!split_arrive(ctr, a.KS)) return;
+  for (int i = tid; i < NOUT; i += NT) {
+    const int rr = i & 15, m = i >> 4;
+    const int nn = nb * 16 + rr, mm = m0 + m;
+    if (nn < a.N && mm < a.M) {
+      const float* pp = a.partial + (size_t)mm * (gridDim.x * 16) + nn;
+      const size_t plane = (size_t)gridDim.y * MT * gridDim.x * 16;
+      float v = 0.0f;
+      for (int k0 = 0; k0 < a.KS; k0 += 4) {  // four loads in flight, added in split order
+        float t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = split_load(pp + (size_t)min(k0 + j, a.KS - 1) * plane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + j < a.KS) v += t[j];
+      }
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+    }
+  }
+  if (tid == 0) split_reset(ctr);
+}
+
+// ---- One activation row (M = 1): eight weight rows per workgroup.
+//
+// Streaming a weight matrix once reads fastest in units of 16-32 KB per
+// workgroup; a 16-row block of a K = 8192 matrix is 64 KB.  With one row of
+// activations only row 0 of the matrix core's sixteen A rows carries data, so
+// a wave covers HALF the rows of two neighbouring K tiles at once: lanes
+// r = 0..7 hold rows 8h + r of tile t, lanes r = 8..15 rows 8h + r - 8 of
+// tile t + 1 (each lane still reads 16 bytes of a tile: eight rows x 16 bytes
+// = 128 contiguous bytes per tile and lane column c), and A row 0 is x over
+// tile t, A rows 1..15 are x over tile t + 1.  Then D row 0 of columns 0..7
+// and D row 1 of columns 8..15 are the two tiles' dot products for the same
+// eight weight rows; the lanes of a weight row add them.  The workgroup
+// (one half h of a 16-row block, all of K) reads half as many bytes.
+template <int W, int KQ, int G>
+__global__ __launch_bounds__(W * 64, W == 16 ? 8 : 4) void gemv_mfma_half_kernel(GemvArgs a) {
+  constexpr int GPT = 128 / G;       // groups per 128-column tile
+  constexpr int SPG = 4 / GPT;       // MFMA steps per group
+  constexpr int NS = KQ * GPT;       // groups per segment
+  constexpr int NP = KQ / 2;         // tile pairs per segment
+  constexpr int NT = W * 64;
+  static_assert(KQ == 4, "a segment is four tiles: one 16-byte x chunk per lane");
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int rr = r & 7, tsel = r >> 3;  // row within the half, which tile of the pair
+  const int hb = blockIdx.x, nb = hb >> 1, h = hb & 1, ks = blockIdx.z;
+  const Dims d = dims_of<G>(a.K);
+  const int kt_lo = ks * a.kt_per_split;
+  const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (KQ * 128);
+  float* red = reinterpret_cast<float*>(smem + (size_t)W * KQ * 256);  // [W][16]
+
+  const uint8_t* tbase = a.qp + (size_t)nb * d.KT * kTileBytes + 16u * (8 * h + rr + 16 * c);
+  const uint32_t n = (uint32_t)min(hb * 8 + rr, a.N - 1);
+  const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
+  const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
+  const int aoff = (r == 0 ? 0 : 128) + 8 * c;  // A row 0: the pair's first tile; rows 1..15: its second
+
+  float acc = 0.0f;
+  for (int sg = wv; sg * KQ < nkt; sg += W) {
+    const int q0 = sg * KQ;
+    const int nq = min(KQ, nkt - q0);
+    const int kt0 = kt_lo + q0;
+
+    // x over the segment's four tiles: one 16-byte chunk per lane; scales and
+    // zero-points of the segment's groups; this lane's two code words
+    const uint4 xc = *reinterpret_cast<const uint4*>(a.x + min(kt0 * 128 + lane * 8, a.K - 8));
+    const SZ<NS> sz = load_sz<NS, true>(a, d.Gtot, srow, zrow, kt0 * GPT);
+    u4 buf[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      buf[p] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + 2 * p + tsel, d.KT - 1) * kTileBytes));
+    *reinterpret_cast<uint4*>(xw + lane * 8) = kt0 * 128 + lane * 8 < a.K ? xc : make_uint4(0, 0, 0, 0);
+    // the slice is read back by other lanes of this wave only
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (2 * p >= nq) break;  // (a second tile past K meets zero activations)
+      const uint16_t* xr = xw + 2 * p * 128 + aoff;
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        // this lane's group: gi of local tile 2p + tsel
+        const int t = (2 * p + tsel) * GPT + gi;
+        const uint32_t z = (sz.zv[((2 * p) * GPT + gi) >> 3] >> (4 * (t & 7))) & 15u;
+        const uint32_t sw = tsel ? sz.sv[((2 * p + 1) * GPT + gi) >> 1] : sz.sv[((2 * p) * GPT + gi) >> 1];
+        const float sc = f16_bits_to_f32((uint16_t)(sw >> (16 * (t & 1))));
+        const h2 zq = as_h2(z * 0x00010001u + kMagicPair);     // (1024 + z) twice
+        const h2 z64 = as_h2(z * 0x00100010u + 0x54005400u);   // (64 + z) twice: z in mantissa bits 4..7
+        f4 T;
+#pragma unroll
+        for (int jj = 0; jj < SPG; ++jj) {
+          const int j = gi * SPG + jj;
+          const uint32_t w = buf[p][j], w8 = w >> 8;
+          const h2 p0 = as_h2((w & 0x000F000Fu) | m1024) - zq;
+          const h2 p1 = as_h2((w & 0x00F000F0u) | m64) - z64;
+          const h2 p2 = as_h2((w8 & 0x000F000Fu) | m1024) - zq;
+          const h2 p3 = as_h2((w8 & 0x00F000F0u) | m64) - z64;
+          h8 bfr;
+          bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+          bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+          const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+          T = jj == 0 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                      : __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, T, 0, 0, 0);
+        }
+        acc = fmaf(sc, tsel ? T[1] : T[0], acc);
+      }
+    }
+    // the next segment overwrites this wave's slice: finish reading it first
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- reduce: lane (r, 0) holds weight row 8h + (r & 7) over one tile of
+  // each pair; the W waves' sums and the two lanes of a row meet in LDS
+  if (c == 0) red[wv * 16 + r] = acc;
+  __syncthreads();
+  if (tid < 8) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * 16 + tid] + red[w * 16 + tid + 8];
+    const int nn = hb * 8 + tid;
+    if (a.KS > 1)  // padded plane [gridDim.x * 8]: always in bounds
+      split_store(a.partial + (size_t)ks * gridDim.x * 8 + nn, v);
+    else if (nn < a.N)
+      a.y[nn] = f32_to_f16_bits(v);
+  }
+  if (a.KS == 1) return;
+
+  // ---- split-K: the last workgroup of this half block adds the partial sums
+  unsigned* ctr = a.counters + blockIdx.x;
+  if (!split_arrive(ctr, a.KS)) return;
+  if (tid < 8) {
+    const int nn = hb * 8 + tid;
+    if (nn < a.N) {
+      const float* pp = a.partial + nn;
+      const size_t plane = (size_t)gridDim.x * 8;
+      float v = 0.0f;
+      for (int k0 = 0; k0 < a.KS; k0 += 4) {  // four loads in flight, added in split order
+        float t4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t4[j] = split_load(pp + (size_t)min(k0 + j, a.KS - 1) * plane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + j < a.KS) v += t4[j];
+      }
+      a.y[nn] = f32_to_f16_bits(v);
+    }
+  }
+  if (tid == 0) split_reset(ctr);
+}
+
 // Launch shape of the GEMV for one problem; shared by the launcher and the
 // workspace query so both agree.
 constexpr int kKQ = 4;  // K tiles per wave segment
 
 struct GemvPlan {
   int MT, W, KS, kt_per_split;
+  bool half;  // gemv_mfma_half_kernel: eight weight rows per workgroup (4-bit codes, one row of x)
   unsigned gx, gy;
   size_t lds;
 };
@@ -418,8 +716,13 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // eight-wave workgroups (two or three per CU) than with one sixteen-wave
   // workgroup per CU.
   p.W = (p.MT <= 1 && fmt != kFmtInt8) ? 16 : 8;
+  // eight-row workgroups only while they still fit the GPU in one round (two
+  // per CU): at M=1, N=1024, K=8192 they took 4.66 us against 5.60 us with
+  // 16-row workgroups, but at N=8192 (1024 workgroups, two rounds) 9.8 us
+  // against 7.9 us
+  p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
-  p.gx = (unsigned)NBLK;
+  p.gx = (unsigned)(p.half ? 2 * NBLK : NBLK);
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
   // split K across workgroups only where a workgroup would otherwise take
   // more than one pass of its waves over K, and only up to about two
@@ -430,13 +733,24 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   int64_t ks = 1;
   const int64_t wgs = (int64_t)p.gx * p.gy, pass = (int64_t)p.W * kKQ;
   const int64_t passes = (KT + pass - 1) / pass;
-  while (wgs * ks * 2 <= 512 && ks < passes) ks *= 2;
+  const int64_t target = p.half ? 1024 : 512;  // about two workgroups per CU
+  while (wgs * ks * 2 <= target && ks < passes) ks *= 2;
   if (wgs > kSplitMaxTiles) ks = 1;  // (never taken: a split grid has < 512 row ranges)
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
   p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * 64 * 4;
   return p;
+}
+
+template <int W, int G>
+hipError_t launch_kh(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  auto k = gemv_mfma_half_kernel<W, kKQ, G>;
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
+  if (e != hipSuccess) return e;
+  k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
+  return hipGetLastError();
 }
 
 template <int MT, int W, int G, int FMT>
@@ -449,12 +763,25 @@ hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MT, int W, int G>
+hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  auto k = gemv_mfma_kernel<MT, W, kKQ, G>;
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
+  if (e != hipSuccess) return e;
+  k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
   if (fmt == kFmtMxfp4) return launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
   if (fmt == kFmtInt8)
     return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
-  return group == 128 ? launch_k<MT, W, 128, kFmtInt4>(p, a, stream) : launch_k<MT, W, 32, kFmtInt4>(p, a, stream);
+  if constexpr (MT == 1 && W == 16) {
+    if (p.half) return group == 128 ? launch_kh<W, 128>(p, a, stream) : launch_kh<W, 32>(p, a, stream);
+  }
+  return group == 128 ? launch_km<MT, W, 128>(p, a, stream) : launch_km<MT, W, 32>(p, a, stream);
 }
 
 }  // namespace
@@ -465,15 +792,19 @@ int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf
     return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                     p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "MXFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
                     p.KS);
-  return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+  if (p.half)
+    return snprintf(buf, len, "gemv_mfma_half_kernel<W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+                    p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
+  return snprintf(buf, len, "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                   p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
 }
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int, int fmt) {
   const GemvPlan p = plan_gemv(M, N, K, fmt);
   if (p.KS == 1) return 0;
-  // partial-sum planes padded to whole tiles: [KS][gy * MT][gx * 16]
-  return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * 16 * sizeof(float);
+  // partial-sum planes padded to whole tiles: [KS][gy * MT][gx * 16] (gx * 8
+  // columns for eight-row workgroups)
+  return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * (p.half ? 8 : 16) * sizeof(float);
 }
 
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
