@@ -2,6 +2,7 @@
 run the HIP path through the C ABI, and compare with the oracle."""
 from __future__ import annotations
 
+import re
 import sys
 
 import numpy as np
@@ -119,3 +120,8 @@ def ref16(x_bits: np.ndarray, w_hat_f16_bits: np.ndarray) -> np.ndarray:
     """fp64 oracle product of x with fp16 weights given as bit patterns."""
     w = np.ascontiguousarray(w_hat_f16_bits, np.uint16).view(np.float16).astype(np.float32)  # exact widening
     return oracle.gemm_f64(x_bits, w)
+
+
+def split_k(plan: str) -> int:
+    """The K split count a kernel description names."""
+    return int(re.search(r"split_k=(\d+)", plan).group(1))

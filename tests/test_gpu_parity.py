@@ -9,8 +9,7 @@ import oracle
 import w4a16_bit_matmul_amd as wq
 import workloads
 from parity import (assert_quantize_matches, compare_y, compare_y_path, f16_bits, floor_for, gpu_quantize, ref16, say,
-                    to_dev_f16,
-                    to_dev_weights)
+                    split_k, to_dev_f16, to_dev_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -308,7 +307,7 @@ def test_mfma_split_k_workspace_is_reusable():
     say("MFMA split-K workspace reuse")
     cases = [(8, 256, 8192, 128), (128, 1024, 8192, 32), (70, 300, 4224, 128), (16, 48, 2048, 32), (8, 256, 8192, 128)]
     for M, N, K, g in cases:
-        assert "split_k=1" not in wq.wq_gemm_plan(M, N, K, g, wq.WQ_PATH_MFMA), (M, N, K, g)
+        assert split_k(wq.wq_gemm_plan(M, N, K, g, wq.WQ_PATH_MFMA)) > 1, (M, N, K, g)
     need = max(wq.wq_gemm_workspace_bytes(M, N, K, g) for M, N, K, g in cases)
     shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
     shared[wq.WQ_WORKSPACE_COUNTER_BYTES:] = 0xFF  # partial sums: NaN bytes, never read before written

@@ -64,3 +64,17 @@ def test_g128_quantize_fits_eight_workgroups_per_cu():
         for sym in "01":
             for name, (vgpr, scratch) in _find(meta, f"quantize_kernelILi{dt}ELi128ELb{sym}ELb0E"):
                 assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
+def test_m128_gemm_keeps_its_loop_in_registers():
+    # gemm_kernel<MB=8, G, SZV=true, FMT> (the 128-row tile every M > 64
+    # product with aligned scale rows runs): two waves per SIMD share 512
+    # registers, so each has 256; a spill inside the K loop would add a
+    # memory round trip per tile
+    meta = _kernel_metadata("wq_gemm.hip")
+    for frag in ("gemm_kernelILi8ELi128ELb1ELi4E", "gemm_kernelILi8ELi32ELb1ELi4E", "gemm_kernelILi8ELi128ELb1ELi8E",
+                 "gemm_kernelILi8ELi32ELb1ELi8E", "gemm_kernelILi8ELi32ELb1ELi2E"):
+        for name, (vgpr, scratch) in _find(meta, frag):
+            assert vgpr <= 256 and scratch == 0, (name, vgpr, scratch)
+

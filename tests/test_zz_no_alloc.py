@@ -51,11 +51,16 @@ def test_noalloc_matches_workspace_entry_point():
 
 
 def test_noalloc_rejects_products_beyond_the_scratch():
-    # 191 column blocks of 128 at M = 128 and K = 20480: the MFMA kernel splits
-    # K two ways over 128-row tiles, 382 tiles of 64 KiB of partial sums
-    M, N, K, group = 128, 191 * 128, 20480, 128
-    need = wq.wq_gemm_workspace_bytes(M, N, K, group, path=wq.WQ_PATH_AUTO)
-    assert need > wq.WQ_NOALLOC_SCRATCH_BYTES, need
+    # a grid of too few workgroups for the GPU splits K; the first of these
+    # shapes whose fp32 partial-sum planes exceed the scratch (384 x 4096 at
+    # K = 28672: three splits of 384 x 4096 sums)
+    group = 128
+    for M, N, K in [(384, 4096, 28672), (128, 12288, 28672), (128, 191 * 128, 20480)]:
+        need = wq.wq_gemm_workspace_bytes(M, N, K, group, path=wq.WQ_PATH_AUTO)
+        if need > wq.WQ_NOALLOC_SCRATCH_BYTES:
+            break
+    else:
+        pytest.fail("no shape needs more than the scratch")
     # plain device buffers of the right sizes (never read: the call returns first)
     qb, sb, zb = wq.wq_layout_bytes(N, K, group)
     qw = wq.QuantizedWeight(torch.zeros(qb, dtype=torch.uint8, device="cuda"),

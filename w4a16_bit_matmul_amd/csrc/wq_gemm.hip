@@ -33,9 +33,9 @@
 // four code words in each lane's 16 bytes, loaded three tiles ahead into a
 // four-slot register ring.  The activations of a tile are staged in LDS once
 // for the workgroup: every thread loads whole 256-byte row segments with
-// 16-byte loads (sixteen threads per row) two tiles ahead of use into
-// registers and stores them, one step before their use, into one of two LDS
-// buffers; chunk cc of row R sits in slot cc ^ (R % 16) of its row, so the
+// 16-byte loads (sixteen threads per row) three tiles ahead of use into one
+// of two register sets and stores them, one tile before their use, into one
+// of two LDS buffers; chunk cc of row R sits in slot cc ^ (R % 16) of its row, so the
 // A-operand reads (lane l = r + 16c takes chunk 4j + c of row 16i + r) spread
 // over all banks.  Scales and zero-points of eight tiles at a time are staged
 // into LDS with wide loads (a row's scales for eight tiles in one load instead
@@ -86,23 +86,20 @@ __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// A raw buffer of `bytes` bytes at `base` (32-bit data format, no swizzle).
+// Loads take a per-lane offset and a wave-uniform offset; only the per-lane
+// one takes part in the buffer's range check, so callers keep both inside
+// the buffer themselves.
+constexpr uint32_t kBufferFlags = 0x00020000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufferFlags);
+}
+
 // Forces a value into a VGPR and hides it from constant folding, so that
 // v_and_or_b32 takes the mask from an SGPR and the fp16 exponent from here.
 __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
-}
-
-// fp16(s * (q - z)) for the eight columns held by one packed word.
-__device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t magic, h2 nb, h2 sc) {
-  const h2 p0 = (as_h2((w & 0x000F000Fu) | magic) + nb) * sc;
-  const h2 p1 = (as_h2(((w >> 4) & 0x000F000Fu) | magic) + nb) * sc;
-  const h2 p2 = (as_h2(((w >> 8) & 0x000F000Fu) | magic) + nb) * sc;
-  const h2 p3 = (as_h2(((w >> 12) & 0x000F000Fu) | magic) + nb) * sc;
-  h8 out;
-  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
-  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
-  return out;
 }
 
 // fp16(E2M1(q) * 2^e) for the eight columns of an MXFP4 code word (column e in
@@ -131,19 +128,51 @@ __device__ __forceinline__ h8 dequant_words8(uint32_t lo, uint32_t hi, h2 sc) {
   return out;
 }
 
-// LDS bytes of one staged chunk for the workgroup's 128 weight rows:
-// g = 128: [tile][row] u32 (scale bits, zero-point in bits 16..19);
-// g = 32: [tile][pair][row] u32 (scales of groups 4t + 2q, 4t + 2q + 1), then
-// [tile][row] u16 (the tile's four zero-points, group 4t in bits 0..3);
-// MXFP4: [tile][row] u32 (the tile's four E8M0 scale bytes, block 4t first).
+// LDS bytes of one staged chunk of scales / zero-points (kSzChunk tiles) for
+// the workgroup's 128 weight rows:
+//   4-bit and int8 codes, g = 128: [tile][row] 8 bytes: the scale as an fp16
+//     pair (s, s), then the fp16 pair -(1024 + z) (4-bit; zero for int8);
+//   g = 32: [tile][step pair jp][row] 16 bytes: those two pairs for group
+//     4t + 2jp, then for group 4t + 2jp + 1;
+//   MXFP4: [tile][row] u32, the tile's four E8M0 scale bytes, block 4t first.
 template <int G, int FMT = kFmtInt4>
 constexpr int sz_chunk_bytes() {
-  return (G == 128 || FMT == kFmtMxfp4) ? kSzChunk * 128 * 4 : kSzChunk * 2 * 128 * 4 + kSzChunk * 128 * 2;
+  return FMT == kFmtMxfp4 ? kSzChunk * 128 * 4 : G == 128 ? kSzChunk * 128 * 8 : kSzChunk * 2 * 128 * 16;
+}
+
+// The fp16 pair -(1024 + z) (exact) as bits.
+__device__ __forceinline__ uint32_t neg_bias_pair(uint32_t z) { return (0xE400u | z) * 0x00010001u; }
+
+// fp16(s * (q - z)) for the eight columns of one packed word, given the scale
+// pair and the pairs -(1024 + z) and -(64 + z): columns 0, 1 and 4, 5 come as
+// 1024 + q (low code bits), columns 2, 3 and 6, 7 as 64 + q (code bits 4..7
+// under the exponent of 64, whose unit spacing is 2^-4).
+__device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t m1024, uint32_t m64, h2 nb, h2 nb64, h2 sc) {
+  const uint32_t w8 = w >> 8;
+  const h2 p0 = (as_h2((w & 0x000F000Fu) | m1024) + nb) * sc;
+  const h2 p1 = (as_h2((w & 0x00F000F0u) | m64) + nb64) * sc;
+  const h2 p2 = (as_h2((w8 & 0x000F000Fu) | m1024) + nb) * sc;
+  const h2 p3 = (as_h2((w8 & 0x00F000F0u) | m64) + nb64) * sc;
+  h8 out;
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+  return out;
 }
 
 // SZV: every row of s (and zpacked) is aligned for the wide staging loads.
 // FMT: kFmtInt4 (codes and zero-points), kFmtInt8 (int8 codes, no
 // zero-points) or kFmtMxfp4 (E2M1 codes, E8M0 scale bytes in a.zp, G = 32).
+//
+// Software pipeline.  Each K tile is two phases of a wave: phase A runs the
+// MFMAs of the wave's first step of the tile (step 2jp) while it reads the A
+// fragments of its second step from LDS and dequantizes that step's B
+// operands; phase B runs the second step's MFMAs while it prepares the next
+// tile's first step the same way.  So the matrix cores always have operands
+// that were formed one phase earlier, and the LDS reads and dequantization
+// overlap the MFMAs of the other phase.  One barrier per tile, between its
+// two phases: the activations of tile kt + 1 are stored in phase A (into the
+// buffer tile kt - 1 used, whose last reads were in phase A of step kt - 1,
+// before that step's barrier) and first read in phase B.
 template <int MB, int G, bool SZV, int FMT>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
@@ -156,6 +185,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   constexpr int XTILE = ROWS * 256;                            // one K tile of activations in LDS
   constexpr int XCH = ROWS * 16 >= NTH ? ROWS * 16 / NTH : 1;  // 16-byte chunks per thread per tile
   constexpr int SZB = sz_chunk_bytes<G, FMT>();
+  constexpr int SZW = FMT == kFmtMxfp4 ? 1 : 2;  // staged words per block and step
   static_assert(ROWS * 16 % NTH == 0 || NTH % (ROWS * 16) == 0, "whole chunks per thread");
   extern __shared__ __align__(16) uint8_t smem[];  // [2][XTILE] activations, [2][SZB] scales
 
@@ -166,53 +196,60 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   const int nwg0 = blockIdx.x * 8 * 16;  // first weight row of the workgroup
   const int nbw0 = blockIdx.x * 8 + cgp * NPW;
   const int mrow0 = blockIdx.y * ROWS;
-  const uint32_t magic = in_vgpr(kMagicPair);
+  const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
   const int KT = a.KT;
 
   // the codes of MFMA steps 2jp, 2jp + 1 in each of the wave's blocks: 4-bit,
   // words 2jp and 2jp + 1 of the lane's 16 bytes; 8-bit, the lane's 16 bytes
-  // of half jp (blocks past the end re-read the last one)
-  const uint8_t* tb[NPW];
-#pragma unroll
-  for (int b = 0; b < NPW; ++b)
-    tb[b] = a.qp + (size_t)min(nbw0 + b, a.NBLK - 1) * KT * TB + 16u * lane + (BITS == 4 ? 8u : 1024u) * jp;
+  // of half jp.  One buffer over the wave's blocks: the lane's offset in a
+  // tile is fixed, the tile and block offsets are wave-uniform (blocks past
+  // the end re-read the last one, tiles past the end the last one).
+  // (wave-uniform values; the explicit readfirstlane keeps the compiler from
+  // treating the buffer descriptor as per-lane)
+  const int qb0 = __builtin_amdgcn_readfirstlane(min(nbw0, a.NBLK - 1));
+  const int qbn = __builtin_amdgcn_readfirstlane(min(nbw0 + NPW - 1, a.NBLK - 1) - qb0 + 1);
+  const __amdgpu_buffer_rsrc_t qres = buffer_of(a.qp + (size_t)qb0 * KT * TB, (uint32_t)(qbn * KT * TB));
+  const uint32_t qvoff = 16u * lane + (BITS == 4 ? 8u : 1024u) * jp;
   // With few rows (MB <= 2) the kernel streams codes at HBM speed and
   // non-temporal loads measure faster; with more rows they do not.
+  constexpr int kCodeAux = MB > 2 ? 0 : 2;  // cache policy: non-temporal
   auto load_b = [&](int kt, CodeT (&d)[NPW]) {
-    kt = min(kt, KT - 1);  // tiles past the end re-load the last (unused)
+    kt = min(kt, KT - 1);
 #pragma unroll
     for (int b = 0; b < NPW; ++b) {
-      const uint8_t* p = tb[b] + (size_t)kt * TB;
-      if constexpr (MB > 2) {
-        d[b] = *reinterpret_cast<const CodeT*>(p);
-      } else if constexpr (BITS == 4) {
-        typedef uint32_t v2 __attribute__((ext_vector_type(2)));
-        const v2 t = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p));
-        d[b] = CodeT{t.x, t.y};
-      } else {
-        d[b] = __builtin_nontemporal_load(reinterpret_cast<const CodeT*>(p));
-      }
+      const uint32_t so = (uint32_t)(min(b, qbn - 1) * KT + kt) * TB;
+      if constexpr (BITS == 4)
+        d[b] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b64(qres, qvoff, so, kCodeAux));
+      else
+        d[b] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b128(qres, qvoff, so, kCodeAux));
     }
   };
 
   // activation chunk q = tid + NTH * i: row q / 16 of the tile, global chunk
   // q % 16 (with fewer chunks than threads, threads share chunks and store
-  // the same bytes).  Rows past M re-read row M - 1; in a ragged last tile,
-  // chunks past K re-read the last chunk inside K (K is a multiple of 32, so
-  // an MFMA step lies wholly inside K or is skipped).
-  const uint16_t* xrow[XCH];
+  // the same bytes); rows past M re-read row M - 1.  The loads of tile kt go
+  // through a buffer that starts at column 128 kt of the workgroup's first
+  // row and ends with its last row, so the lane's offset (its row and chunk)
+  // is fixed and range-checked: in a ragged last tile, chunks past K read
+  // the next row's first columns, or zeros past the last row (K is a
+  // multiple of 32, so an MFMA step lies wholly inside K or is skipped).
+  const int xrows = min(a.M - mrow0, ROWS);
+  const uint16_t* const xbase = a.x + (size_t)mrow0 * a.K;
+  uint32_t xvoff[XCH];
   uint32_t xlds[XCH];
   const int xcc = tid & 15;
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int row = ((tid >> 4) + (NTH / 16) * i) % ROWS;
-    xrow[i] = a.x + (size_t)min(mrow0 + row, a.M - 1) * a.K;
+    xvoff[i] = (uint32_t)min(row, xrows - 1) * a.K * 2u + 16u * xcc;
     xlds[i] = (uint32_t)(row * 256 + 16 * (xcc ^ (row & 15)));
   }
   auto load_x = [&](int kt, u4 (&v)[XCH]) {
-    const int col = min(min(kt, KT - 1) * 128 + 8 * xcc, a.K - 8);
+    kt = min(kt, KT - 1);
+    const __amdgpu_buffer_rsrc_t xres = buffer_of(xbase + kt * 128, (uint32_t)(xrows * a.K - kt * 128) * 2u);
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) v[i] = *reinterpret_cast<const u4*>(xrow[i] + col);
+    for (int i = 0; i < XCH; ++i)
+      v[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(xres, xvoff[i], 0u, 0));
   };
   auto store_x = [&](int kt, const u4 (&v)[XCH]) {
 #pragma unroll
@@ -272,6 +309,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     }
   };
   uint8_t* const szbase = smem + 2 * XTILE;
+  // scale pair and -(1024 + z) pair of one group (int8: no zero-point)
+  auto entry = [&](uint32_t s16, uint32_t z) -> uint2 {
+    return uint2{(s16 & 0xffffu) * 0x00010001u, FMT == kFmtInt4 ? neg_bias_pair(z & 15u) : 0u};
+  };
   auto sz_store = [&](int chunk, const SzStage& v) {
     uint8_t* buf = szbase + (chunk & 1) * SZB;
     if constexpr (FMT == kFmtMxfp4) {
@@ -281,17 +322,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
       const uint32_t s0 = SZV ? v.s[0] & 0xffffu : v.s[0];
       const uint32_t s1 = SZV ? v.s[0] >> 16 : v.s[1];
       // tiles 2p (low nibble) and 2p + 1 (high nibble) share a zero-point byte
-      *reinterpret_cast<uint32_t*>(buf + (2 * sp) * 512 + 4 * sn) = s0 | ((v.z & 15u) << 16);
-      *reinterpret_cast<uint32_t*>(buf + (2 * sp + 1) * 512 + 4 * sn) = s1 | ((v.z >> 4) << 16);
+      *reinterpret_cast<uint2*>(buf + ((2 * sp) * 128 + sn) * 8) = entry(s0, v.z);
+      *reinterpret_cast<uint2*>(buf + ((2 * sp + 1) * 128 + sn) * 8) = entry(s1, v.z >> 4);
     } else {
+      // the thread's eight groups: i = 4e + q for tile 2p + e; scale i in half
+      // i % 2 of s[i / 2], zero-point i in nibble i of z
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          *reinterpret_cast<uint32_t*>(buf + ((2 * sp + e) * 2 + q) * 512 + 4 * sn) = v.s[2 * e + q];
-        *reinterpret_cast<uint16_t*>(buf + kSzChunk * 1024 + (2 * sp + e) * 256 + 2 * sn) =
-            (uint16_t)(v.z >> (16 * e));
-      }
+        for (int h = 0; h < 2; ++h) {
+          const int i = 4 * e + 2 * h;
+          const uint2 ea = entry(v.s[i >> 1], v.z >> (4 * i)), eb = entry(v.s[i >> 1] >> 16, v.z >> (4 * i + 4));
+          *reinterpret_cast<u4*>(buf + (((2 * sp + e) * 2 + h) * 128 + sn) * 16) = u4{ea.x, ea.y, eb.x, eb.y};
+        }
     }
   };
 
@@ -306,12 +349,75 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   const int kt_lo = blockIdx.z * a.kt_per_split;
   const int kt_hi = min(KT, kt_lo + a.kt_per_split);
 
-  // ---- prologue: activations of the first tile (in LDS) and the second (in
-  // registers), codes of the first three tiles, scales / zero-points of the
-  // first chunk
+  // this lane's A reads: row r of block i, chunk 4j + c at slot (4j + c) ^ r;
+  // its scale / zero entries: rows (cg*NPW + b)*16 + r of the workgroup
+  const uint8_t* const arow = smem + r * 256;
+  const int szrow = cgp * NPW * 16 + r;
+
+  // staged scale / zero-point words of one step (jj) of tile kt for the
+  // wave's blocks: the scale pair and the -(1024 + z) pair (MXFP4: the tile's
+  // scale bytes)
+  struct SzRegs {
+    uint32_t w[NPW][SZW];
+  };
+  auto read_sz = [&](int kt, int jj, SzRegs& v) {
+    const uint8_t* szt = szbase + ((kt / kSzChunk) & 1) * SZB;
+    const int tt = kt % kSzChunk;
+#pragma unroll
+    for (int b = 0; b < NPW; ++b) {
+      const int row = szrow + 16 * b;
+      if constexpr (FMT == kFmtMxfp4) {
+        v.w[b][0] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * row);
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(
+            szt + (G == 128 ? (tt * 128 + row) * 8 : ((tt * 2 + jp) * 128 + row) * 16 + 8 * jj));
+        v.w[b][0] = t.x;
+        v.w[b][1] = t.y;
+      }
+    }
+  };
+  // A fragments of step jj (MFMA step 2jp + jj) of tile kt, from its LDS buffer
+  auto read_a = [&](int kt, int jj, h8 (&af)[MB]) {
+    const int j = 2 * jp + jj;
+    const uint8_t* abuf = arow + (kt & 1) * XTILE + ((4 * j + c) ^ r) * 16;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abuf + i * 16 * 256);
+  };
+  // B operands of step jj of tile kt (kt only picks the MXFP4 scale byte)
+  auto deq = [&](int kt, int jj, const CodeT (&cur)[NPW], const SzRegs& sz, h8 (&bf)[NPW]) {
+#pragma unroll
+    for (int b = 0; b < NPW; ++b) {
+      if constexpr (FMT == kFmtMxfp4) {
+        // block 4 kt + j: byte j of the tile's scale word (exponent field only)
+        const int j = 2 * jp + jj;
+        const float scale = __builtin_bit_cast(float, ((sz.w[b][0] >> (8 * j)) & 0xffu) << 23);
+        bf[b] = dequant_word_mx(jj ? cur[b].y : cur[b].x, scale);
+      } else if constexpr (FMT == kFmtInt4) {
+        const h2 nb = as_h2(sz.w[b][1]), nb64 = nb + h2{(_Float16)960.0f, (_Float16)960.0f};  // -(64 + z), exact
+        bf[b] = dequant_word(jj ? cur[b].y : cur[b].x, m1024, m64, nb, nb64, as_h2(sz.w[b][0]));
+      } else {
+        bf[b] = dequant_words8(jj ? cur[b][2] : cur[b][0], jj ? cur[b][3] : cur[b][1], as_h2(sz.w[b][0]));
+      }
+    }
+  };
+  auto mma = [&](const h8 (&af)[MB], const h8 (&bf)[NPW]) {
+#pragma unroll
+    for (int b = 0; b < NPW; ++b)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf[b], acc[i][b]);
+  };
+  // in a ragged last tile, a step that starts at or past K is skipped
+  auto step_in_k = [&](int kt, int jj) { return kt * 128 + 32 * (2 * jp + jj) < a.K; };
+
+  // ---- prologue: activations of the first tile (in LDS) and of the second
+  // and third (in registers), codes of the first three tiles, scales /
+  // zero-points of the first chunk; then the operands of the first tile's
+  // first step
   CodeT b0[NPW], b1[NPW], b2[NPW], b3[NPW];
   u4 xs0[XCH], xs1[XCH];
   SzStage szs;
+  SzRegs szc;
+  h8 af0[MB], af1[MB], bf0[NPW], bf1[NPW];
   load_x(kt_lo, xs0);
   load_x(kt_lo + 1, xs1);
   load_b(kt_lo, b0);
@@ -319,104 +425,68 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   load_b(kt_lo + 2, b2);
   sz_load(kt_lo / kSzChunk, szs);
   store_x(kt_lo, xs0);
+  load_x(kt_lo + 2, xs0);
   sz_store(kt_lo / kSzChunk, szs);
   lds_barrier();
+  read_sz(kt_lo, 0, szc);
+  read_a(kt_lo, 0, af0);
+  deq(kt_lo, 0, b0, szc, bf0);
 
-  // this lane's A reads: row r of block i, chunk 4j + c at slot (4j + c) ^ r;
-  // its scale / zero entries: rows (cg*NPW + b)*16 + r of the workgroup
-  const uint8_t* const arow = smem + r * 256;
-  const int szrow = cgp * NPW * 16 + r;
-
-  // One step (K tile kt): load the activations of tile kt + 2 and the codes
-  // of tile kt + 3, multiply tile kt, and store the activations of tile
-  // kt + 1 (loaded one step earlier) into the other LDS buffer.
-  auto step = [&](auto full_tag, int kt, u4 (&xld)[XCH], const u4 (&xst)[XCH], const CodeT (&cur)[NPW],
-                  CodeT (&nxt)[NPW]) {
+  // One tile kt.  xs: the register set holding the activations of tile
+  // kt + 1 (loaded two tiles earlier), which are stored to LDS and replaced
+  // by those of tile kt + 3.  cur: codes of tile kt; nxt: codes of tile
+  // kt + 1; ld: the ring slot that receives tile kt + 3.
+  auto tile = [&](auto full_tag, int kt, u4 (&xs)[XCH], const CodeT (&cur)[NPW], const CodeT (&nxt)[NPW],
+                  CodeT (&ld)[NPW]) {
     constexpr bool FULL = decltype(full_tag)::value;
-    load_x(kt + 2, xld);
+    // phase A: MFMAs of step 0 (operands formed earlier); prepare step 1
+    store_x(kt + 1, xs);
+    load_x(kt + 3, xs);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(kt + 3, nxt);
-    // scale / zero-point of this tile for the wave's blocks
-    const uint8_t* szt = szbase + ((kt / kSzChunk) & 1) * SZB;
-    const int tt = kt % kSzChunk;
-    uint32_t sv[NPW], zv[NPW];
-#pragma unroll
-    for (int b = 0; b < NPW; ++b) {
-      if constexpr (FMT == kFmtMxfp4) {
-        sv[b] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * (szrow + 16 * b));
-        zv[b] = 0u;
-      } else if constexpr (G == 128) {
-        sv[b] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * (szrow + 16 * b));
-        zv[b] = sv[b] >> 16;
-      } else {
-        sv[b] = *reinterpret_cast<const uint32_t*>(szt + (tt * 2 + jp) * 512 + 4 * (szrow + 16 * b));
-        zv[b] = (uint32_t)*reinterpret_cast<const uint16_t*>(szt + kSzChunk * 1024 + tt * 256 + 2 * (szrow + 16 * b)) >>
-                (8 * jp);
-      }
-    }
-    const uint8_t* abuf = arow + (kt & 1) * XTILE;
-    auto mstep = [&](int jj) {
-      const int j = 2 * jp + jj;
-      if (!FULL && kt * 128 + 32 * j >= a.K) return;  // ragged last tile
-      const int slot = ((4 * j + c) ^ r) * 16;
-      h8 af[MB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const h8*>(abuf + i * 16 * 256 + slot);
-#pragma unroll
-      for (int b = 0; b < NPW; ++b) {
-        h8 bf;
-        const uint32_t sb = G == 128 ? sv[b] & 0xffffu : (jj ? sv[b] >> 16 : sv[b] & 0xffffu);
-        const h2 sc = as_h2(sb * 0x00010001u);
-        if constexpr (FMT == kFmtMxfp4) {
-          // block 4 kt + j: byte j of the tile's scale word (exponent field only)
-          const float scale = __builtin_bit_cast(float, ((sv[b] >> (8 * j)) & 0xffu) << 23);
-          bf = dequant_word_mx(jj ? cur[b].y : cur[b].x, scale);
-        } else if constexpr (FMT == kFmtInt4) {
-          const uint32_t z = G == 128 ? zv[b] & 15u : (zv[b] >> (4 * jj)) & 15u;
-          const h2 nbias = -as_h2(z * 0x00010001u + magic);
-          bf = dequant_word(jj ? cur[b].y : cur[b].x, magic, nbias, sc);
-        } else {
-          bf = dequant_words8(jj ? cur[b][2] : cur[b][0], jj ? cur[b][3] : cur[b][1], sc);
-        }
-#pragma unroll
-        for (int i = 0; i < MB; ++i) acc[i][b] = mfma16(af[i], bf, acc[i][b]);
-      }
-    };
-    mstep(0);
-    // the other buffer was last read before the previous barrier
-    store_x(kt + 1, xst);
-    mstep(1);
+    load_b(kt + 3, ld);
+    read_sz(kt, 1, szc);
+    read_a(kt, 1, af1);
+    deq(kt, 1, cur, szc, bf1);
+    if (FULL || step_in_k(kt, 0)) mma(af0, bf0);
     lds_barrier();
+    // phase B: MFMAs of step 1; prepare step 0 of tile kt + 1
+    read_sz(kt + 1, 0, szc);
+    read_a(kt + 1, 0, af0);
+    deq(kt + 1, 0, nxt, szc, bf0);
+    if (FULL || step_in_k(kt, 1)) mma(af1, bf1);
   };
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
 
   // whole tiles in groups of eight (two turns of the code ring, four of the
   // activation registers); the next chunk's scales / zero-points are loaded
-  // at step 1 and stored at step 5
+  // at tile 1 and stored at tile 5
   const int kt_full = kt_lo + ((min(kt_hi, a.K / 128) - kt_lo) & ~(kSzChunk - 1));
   int kt = kt_lo;
   for (; kt < kt_full; kt += kSzChunk) {
     const int ch = kt / kSzChunk;
-    step(Full{}, kt, xs0, xs1, b0, b3);
+    tile(Full{}, kt, xs1, b0, b1, b3);
     sz_load(ch + 1, szs);
-    step(Full{}, kt + 1, xs1, xs0, b1, b0);
-    step(Full{}, kt + 2, xs0, xs1, b2, b1);
-    step(Full{}, kt + 3, xs1, xs0, b3, b2);
-    step(Full{}, kt + 4, xs0, xs1, b0, b3);
+    tile(Full{}, kt + 1, xs0, b1, b2, b0);
+    tile(Full{}, kt + 2, xs1, b2, b3, b1);
+    tile(Full{}, kt + 3, xs0, b3, b0, b2);
     sz_store(ch + 1, szs);
-    step(Full{}, kt + 5, xs1, xs0, b1, b0);
-    step(Full{}, kt + 6, xs0, xs1, b2, b1);
-    step(Full{}, kt + 7, xs1, xs0, b3, b2);
+    tile(Full{}, kt + 4, xs1, b0, b1, b3);
+    tile(Full{}, kt + 5, xs0, b1, b2, b0);
+    tile(Full{}, kt + 6, xs1, b2, b3, b1);
+    tile(Full{}, kt + 7, xs0, b3, b0, b2);
   }
   // the rest (fewer than eight tiles, the last one possibly ragged); their
   // chunk was staged during the previous chunk or before the loop
   for (; kt < kt_hi; kt += 4) {
-    step(Part{}, kt, xs0, xs1, b0, b3);
-    if (kt + 1 < kt_hi) step(Part{}, kt + 1, xs1, xs0, b1, b0);
-    if (kt + 2 < kt_hi) step(Part{}, kt + 2, xs0, xs1, b2, b1);
-    if (kt + 3 < kt_hi) step(Part{}, kt + 3, xs1, xs0, b3, b2);
+    tile(Part{}, kt, xs1, b0, b1, b3);
+    if (kt + 1 < kt_hi) tile(Part{}, kt + 1, xs0, b1, b2, b0);
+    if (kt + 2 < kt_hi) tile(Part{}, kt + 2, xs1, b2, b3, b1);
+    if (kt + 3 < kt_hi) tile(Part{}, kt + 3, xs0, b3, b0, b2);
   }
+
+  // every wave's last LDS reads are done before the reduction reuses LDS
+  lds_barrier();
 
   // ---- add the second step pair's sums to the first's (LDS reused), then
   // lane (r, c) of the first pair holds rows 4c..4c+3 of column r of each block
@@ -521,10 +591,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-dim3 gemm_grid(int MB, int64_t M, int64_t N) {
-  return dim3((unsigned)(((N + 15) / 16 + 7) / 8), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
-}
-
 size_t gemm_lds(int MB, int group, int fmt) {
   // two activation buffers and two staged chunks of scales / zero-points; the
   // final reduction ([4][MB*NPW*4][64] fp32) reuses the front of it
@@ -537,8 +603,8 @@ size_t gemm_lds(int MB, int group, int fmt) {
 }
 
 template <int MB, int G, bool SZV, int FMT>
-hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
-  const dim3 g2 = gemm_grid(MB, a.M, a.N), grid(g2.x, g2.y, (unsigned)a.KS), block(kWaves * 64);
+hipError_t launch_kg(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid(p.gx, p.gy, (unsigned)p.KS), block(kWaves * 64);
   const size_t lds = gemm_lds(MB, G, FMT);
   auto k = gemm_kernel<MB, G, SZV, FMT>;
   static std::atomic<uint64_t> lds_raised{0};
@@ -549,22 +615,32 @@ hipError_t launch_kg(const GemmArgs& a, hipStream_t stream) {
 }
 
 template <int MB, int FMT>
-hipError_t launch_t(int group, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_t(int group, const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   // wide staging loads of scales / zero-points when every row is aligned for
   // them: g = 128 two scales (4 bytes); g = 32 eight scales (16 bytes) and
   // eight zero-points (4 bytes); MXFP4 eight scale bytes
   const uintptr_t sp = reinterpret_cast<uintptr_t>(a.s), zp = reinterpret_cast<uintptr_t>(a.zp);
   if constexpr (FMT == kFmtMxfp4) {
-    if (a.Gtot % 8 == 0 && zp % 8 == 0) return launch_kg<MB, 32, true, FMT>(a, stream);
-    return launch_kg<MB, 32, false, FMT>(a, stream);
+    if (a.Gtot % 8 == 0 && zp % 8 == 0) return launch_kg<MB, 32, true, FMT>(p, a, stream);
+    return launch_kg<MB, 32, false, FMT>(p, a, stream);
   } else {
     if (group == 128) {
-      if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, FMT>(a, stream);
-      return launch_kg<MB, 128, false, FMT>(a, stream);
+      if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, FMT>(p, a, stream);
+      return launch_kg<MB, 128, false, FMT>(p, a, stream);
     }
     if (a.Gtot % 8 == 0 && sp % 16 == 0 && (FMT == kFmtInt8 || zp % 4 == 0))
-      return launch_kg<MB, 32, true, FMT>(a, stream);
-    return launch_kg<MB, 32, false, FMT>(a, stream);
+      return launch_kg<MB, 32, true, FMT>(p, a, stream);
+    return launch_kg<MB, 32, false, FMT>(p, a, stream);
+  }
+}
+
+template <int FMT>
+hipError_t launch_f(int group, const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  switch (p.MB) {
+    case 1: return launch_t<1, FMT>(group, p, a, stream);
+    case 2: return launch_t<2, FMT>(group, p, a, stream);
+    case 4: return launch_t<4, FMT>(group, p, a, stream);
+    default: return launch_t<8, FMT>(group, p, a, stream);
   }
 }
 
@@ -609,28 +685,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   a.Gtot = (int)(K / group);
   a.GB = (a.Gtot + 1) / 2;
   a.NBLK = (int)((N + 15) / 16);
-  if (fmt == kFmtInt8) {
-    switch (gemm_mb(M, N, K)) {
-      case 1: return launch_t<1, kFmtInt8>(group, a, stream);
-      case 2: return launch_t<2, kFmtInt8>(group, a, stream);
-      case 4: return launch_t<4, kFmtInt8>(group, a, stream);
-      default: return launch_t<8, kFmtInt8>(group, a, stream);
-    }
-  }
-  if (fmt == kFmtMxfp4) {
-    switch (gemm_mb(M, N, K)) {
-      case 1: return launch_t<1, kFmtMxfp4>(group, a, stream);
-      case 2: return launch_t<2, kFmtMxfp4>(group, a, stream);
-      case 4: return launch_t<4, kFmtMxfp4>(group, a, stream);
-      default: return launch_t<8, kFmtMxfp4>(group, a, stream);
-    }
-  }
-  switch (gemm_mb(M, N, K)) {
-    case 1: return launch_t<1, kFmtInt4>(group, a, stream);
-    case 2: return launch_t<2, kFmtInt4>(group, a, stream);
-    case 4: return launch_t<4, kFmtInt4>(group, a, stream);
-    default: return launch_t<8, kFmtInt4>(group, a, stream);
-  }
+  if (fmt == kFmtInt8) return launch_f<kFmtInt8>(group, p, a, stream);
+  if (fmt == kFmtMxfp4) return launch_f<kFmtMxfp4>(group, p, a, stream);
+  return launch_f<kFmtInt4>(group, p, a, stream);
 }
 
 }  // namespace wq
