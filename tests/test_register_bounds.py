@@ -66,15 +66,43 @@ def test_g128_quantize_fits_eight_workgroups_per_cu():
                 assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)
 
 
+def _kernel_asm(src_name):
+    src = os.path.join(_build.CSRC, src_name)
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [_build.HIPCC, *_build.COMMON, *_build.PER_FILE[src_name], "-Wno-unused-value",
+               "--cuda-device-only", "-S", src, "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            pytest.fail(res.stdout + res.stderr)
+        return open(out).read()
+
+
+def _first_loop(asm, kernel):
+    """Instructions of the kernel's first loop: from its header label to the
+    branch back to it."""
+    body = asm.split("\n" + kernel + ":", 1)[1].split("s_endpgm", 1)[0]
+    m = re.search(r"^(\.LBB\w+):[^\n]*Loop Header", body, re.M)
+    assert m, kernel
+    label = m.group(1)
+    start = m.end()
+    end = body.index("s_cbranch_scc1 " + label, start) if ("s_cbranch_scc1 " + label) in body[start:] else \
+        body.index(label, start)
+    return body[start:end]
+
+
 @pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
 def test_m128_gemm_keeps_its_loop_in_registers():
     # gemm_kernel<MB=8, G, SZV=true, FMT> (the 128-row tile every M > 64
     # product with aligned scale rows runs): two waves per SIMD share 512
     # registers, so each has 256; a spill inside the K loop would add a
-    # memory round trip per tile
+    # memory round trip (and a wait for every load in flight) per tile
+    asm = _kernel_asm("wq_gemm.hip")
     meta = _kernel_metadata("wq_gemm.hip")
     for frag in ("gemm_kernelILi8ELi128ELb1ELi4E", "gemm_kernelILi8ELi32ELb1ELi4E", "gemm_kernelILi8ELi128ELb1ELi8E",
                  "gemm_kernelILi8ELi32ELb1ELi8E", "gemm_kernelILi8ELi32ELb1ELi2E"):
         for name, (vgpr, scratch) in _find(meta, frag):
-            assert vgpr <= 256 and scratch == 0, (name, vgpr, scratch)
-
+            assert vgpr <= 256, (name, vgpr)
+            loop = _first_loop(asm, name)
+            assert loop.count("v_mfma") >= 64, name  # the K loop: eight tiles of at least eight MFMAs
+            assert "scratch_" not in loop and "s_waitcnt vmcnt(0)" not in loop, name

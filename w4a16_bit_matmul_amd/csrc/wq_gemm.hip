@@ -413,29 +413,30 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // and third (in registers), codes of the first three tiles, scales /
   // zero-points of the first chunk; then the operands of the first tile's
   // first step
-  CodeT b0[NPW], b1[NPW], b2[NPW], b3[NPW];
-  u4 xs0[XCH], xs1[XCH];
+  // the code ring: RING slots, loaded RING - 1 tiles ahead
+  constexpr int RING = 4;
+  CodeT ring[RING][NPW];
+  u4 xs[2][XCH];  // activations of even / odd tiles
   SzStage szs;
   SzRegs szc;
   h8 af0[MB], af1[MB], bf0[NPW], bf1[NPW];
-  load_x(kt_lo, xs0);
-  load_x(kt_lo + 1, xs1);
-  load_b(kt_lo, b0);
-  load_b(kt_lo + 1, b1);
-  load_b(kt_lo + 2, b2);
+  load_x(kt_lo, xs[0]);
+  load_x(kt_lo + 1, xs[1]);
+#pragma unroll
+  for (int s = 0; s < RING - 1; ++s) load_b(kt_lo + s, ring[s]);
   sz_load(kt_lo / kSzChunk, szs);
-  store_x(kt_lo, xs0);
-  load_x(kt_lo + 2, xs0);
+  store_x(kt_lo, xs[0]);
+  load_x(kt_lo + 2, xs[0]);
   sz_store(kt_lo / kSzChunk, szs);
   lds_barrier();
   read_sz(kt_lo, 0, szc);
   read_a(kt_lo, 0, af0);
-  deq(kt_lo, 0, b0, szc, bf0);
+  deq(kt_lo, 0, ring[0], szc, bf0);
 
   // One tile kt.  xs: the register set holding the activations of tile
   // kt + 1 (loaded two tiles earlier), which are stored to LDS and replaced
   // by those of tile kt + 3.  cur: codes of tile kt; nxt: codes of tile
-  // kt + 1; ld: the ring slot that receives tile kt + 3.
+  // kt + 1; ld: the ring slot that receives tile kt + RING - 1.
   auto tile = [&](auto full_tag, int kt, u4 (&xs)[XCH], const CodeT (&cur)[NPW], const CodeT (&nxt)[NPW],
                   CodeT (&ld)[NPW]) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     store_x(kt + 1, xs);
     load_x(kt + 3, xs);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(kt + 3, ld);
+    load_b(kt + RING - 1, ld);
     read_sz(kt, 1, szc);
     read_a(kt, 1, af1);
     deq(kt, 1, cur, szc, bf1);
@@ -458,31 +459,27 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
 
-  // whole tiles in groups of eight (two turns of the code ring, four of the
-  // activation registers); the next chunk's scales / zero-points are loaded
-  // at tile 1 and stored at tile 5
+  // whole tiles in groups of eight (one or two turns of the code ring, four
+  // of the activation registers); the next chunk's scales / zero-points are
+  // loaded at tile 1 and stored at tile 4
   const int kt_full = kt_lo + ((min(kt_hi, a.K / 128) - kt_lo) & ~(kSzChunk - 1));
   int kt = kt_lo;
   for (; kt < kt_full; kt += kSzChunk) {
     const int ch = kt / kSzChunk;
-    tile(Full{}, kt, xs1, b0, b1, b3);
-    sz_load(ch + 1, szs);
-    tile(Full{}, kt + 1, xs0, b1, b2, b0);
-    tile(Full{}, kt + 2, xs1, b2, b3, b1);
-    tile(Full{}, kt + 3, xs0, b3, b0, b2);
-    sz_store(ch + 1, szs);
-    tile(Full{}, kt + 4, xs1, b0, b1, b3);
-    tile(Full{}, kt + 5, xs0, b1, b2, b0);
-    tile(Full{}, kt + 6, xs1, b2, b3, b1);
-    tile(Full{}, kt + 7, xs0, b3, b0, b2);
+#pragma unroll
+    for (int u = 0; u < kSzChunk; ++u) {
+      if (u == 1) sz_load(ch + 1, szs);
+      if (u == 4) sz_store(ch + 1, szs);
+      tile(Full{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING]);
+    }
   }
   // the rest (fewer than eight tiles, the last one possibly ragged); their
   // chunk was staged during the previous chunk or before the loop
-  for (; kt < kt_hi; kt += 4) {
-    tile(Part{}, kt, xs1, b0, b1, b3);
-    if (kt + 1 < kt_hi) tile(Part{}, kt + 1, xs0, b1, b2, b0);
-    if (kt + 2 < kt_hi) tile(Part{}, kt + 2, xs1, b2, b3, b1);
-    if (kt + 3 < kt_hi) tile(Part{}, kt + 3, xs0, b3, b0, b2);
+  if (kt < kt_hi) {
+#pragma unroll
+    for (int u = 0; u < kSzChunk; ++u)
+      if (kt + u < kt_hi)
+        tile(Part{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING]);
   }
 
   // every wave's last LDS reads are done before the reduction reuses LDS
