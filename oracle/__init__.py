@@ -91,6 +91,9 @@ def _load():
         "orc_dequant_mxfp4": (I, [P, P, I64, I64, I, P]),
         "orc_pack_device_mxfp4": (I, [P, I64, I64, P]),
         "orc_gemm_rows_mxfp4_f64": (I, [I64, I64, I64, P, P, P, I64, I64, P]),
+        "orc_quantize_nvfp4": (I, [P, I, I64, I64, P, P, P]),
+        "orc_dequant_nvfp4": (I, [P, P, ctypes.c_float, I64, I64, I, P]),
+        "orc_gemm_rows_nvfp4_f64": (I, [I64, I64, I64, P, P, P, ctypes.c_float, I64, I64, P]),
         "orc_scale_activations": (I, [P, I64, I64, P, P]),
         "orc_channel_absmean": (I, [P, I64, I64, P]),
         "orc_kv_dequant": (I, [P, P, P, I64, I64, P, I64, I, P]),
@@ -370,6 +373,50 @@ def gemm_rows_mxfp4_f64(x_f16_bits, q, e8, n0: int, nrows: int) -> np.ndarray:
     y = np.empty((M, nrows), np.float64)
     _check(_load().orc_gemm_rows_mxfp4_f64(M, N, K, _ptr(x), _ptr(q), _ptr(e8), n0, nrows, _ptr(y)),
            "orc_gemm_rows_mxfp4_f64")
+    return y
+
+
+# --- NVFP4 (E2M1 elements, blocks of 16, E4M3 scale, fp32 tensor scale) -------
+
+def quantize_nvfp4(W: np.ndarray, dtype: int | None = None):
+    """NVFP4 quantization of W[N][K] (K a multiple of 16): the per-tensor fp32
+    scale S = fp32(max|W| / (6 * 448)); per block of 16 along K the E4M3 scale
+    byte nearest to the block's max|w| / (6 S), and E2M1 codes nearest to
+    w / (E4M3 * S) (ties to even, saturating; sign in bit 3).  Returns
+    (q uint8 [N][K], s8 uint8 [N][K/16], S float)."""
+    W = np.ascontiguousarray(W)
+    if dtype is None:
+        if W.dtype == np.float32:
+            dtype = F32
+        else:
+            raise ValueError("give dtype for non-float32 input")
+    N, K = W.shape
+    q = np.empty((N, K), np.uint8)
+    s8 = np.empty((N, K // 16), np.uint8)
+    S = np.zeros(1, np.float32)
+    _check(_load().orc_quantize_nvfp4(_ptr(W), dtype, N, K, _ptr(q), _ptr(s8), _ptr(S)), "orc_quantize_nvfp4")
+    return q, s8, float(S[0])
+
+
+def dequant_nvfp4(q: np.ndarray, s8: np.ndarray, tensor_scale: float, out_dtype: int = F32) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    s8 = np.ascontiguousarray(s8, np.uint8)
+    N, K = q.shape
+    out = np.empty((N, K), np.float32 if out_dtype == F32 else np.uint16)
+    _check(_load().orc_dequant_nvfp4(_ptr(q), _ptr(s8), tensor_scale, N, K, out_dtype, _ptr(out)),
+           "orc_dequant_nvfp4")
+    return out
+
+
+def gemm_rows_nvfp4_f64(x_f16_bits, q, s8, tensor_scale: float, n0: int, nrows: int) -> np.ndarray:
+    x = np.ascontiguousarray(x_f16_bits, np.uint16)
+    q = np.ascontiguousarray(q, np.uint8)
+    s8 = np.ascontiguousarray(s8, np.uint8)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, nrows), np.float64)
+    _check(_load().orc_gemm_rows_nvfp4_f64(M, N, K, _ptr(x), _ptr(q), _ptr(s8), tensor_scale, n0, nrows, _ptr(y)),
+           "orc_gemm_rows_nvfp4_f64")
     return y
 
 

@@ -29,6 +29,14 @@
  *        format of the microscaling paper that section cites: E2M1 elements
  *        (sign, 2 exponent bits with bias 1, 1 mantissa bit), blocks of 32,
  *        an E8M0 power-of-two scale.
+ *   [C]  also section "Hardware, formats and the roofline" (its key box:
+ *        NVFP4 stores 4-bit values with one FP8 E4M3 scale per 16 values and
+ *        one fp32 scale per tensor, 4.5 bits per value, 39.4 GB for 70B).
+ *        The pages leave the choice of the two scales open; read here as
+ *        S = fp32(amax / (6 * 448)) over the tensor, the block scale the E4M3
+ *        value nearest to the block's max|w| / (6 S), and every rounding to
+ *        E4M3 or E2M1 to the nearest value of the exact quotient, ties to
+ *        even, saturating at the format's largest finite value.
  *
  * Where the pages leave a step open, the readings below are used (each is also
  * listed in the design notes):
@@ -763,6 +771,140 @@ int orc_gemm_rows_mxfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * (double)wr[k];
+            y_rows[m * nrows + i] = acc;
+        }
+        free(wr);
+    }
+    free(xd);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4  ([C] "Hardware, formats and the roofline" key box: 4-bit values,    */
+/* one E4M3 scale per 16 values and a per-tensor fp32 scale, 4.5 bits per    */
+/* value; [Q] "Microscaling: NVFP4 and MXFP4")                               */
+/* ------------------------------------------------------------------------- */
+
+/* The E4M3 magnitude of code c = 0..126 (4 exponent bits with bias 7, 3
+ * mantissa bits; exponent field 0 is subnormal, m * 2^-9; 0x7F would be NaN,
+ * so 448 = code 126 is the largest finite value). */
+static double e4m3_magnitude(int c)
+{
+    int e = c >> 3, f = c & 7;
+    return e == 0 ? ldexp((double)f, -9) : ldexp(1.0 + f / 8.0, e - 7);
+}
+
+/* The code c in [0, ncodes) whose value val(c) * d is nearest to a >= 0, ties
+ * to the even code, beyond the last midpoint the last code (saturation).
+ * Values increase with c; each comparison a <> mid * d is exact in fp64 for
+ * the operands used here (a: an fp32 value; mid: a midpoint of two format
+ * values, at most five significant bits; d: at most 28 significant bits). */
+static int nearest_scaled(double a, double d, double (*val)(int), int ncodes)
+{
+    int c = 0;
+    for (int k = 0; k + 1 < ncodes; ++k) {
+        double mid = 0.5 * (val(k) + val(k + 1));
+        double rhs = mid * d;
+        if (a > rhs || (a == rhs && ((k + 1) & 1) == 0)) c = k + 1;
+        else break;
+    }
+    return c;
+}
+
+/* The per-tensor scale of a tensor whose largest |w| is amax:
+ * S = fp32(fp64(amax / (6 * 448))) (6 and 448 are the largest E2M1 and E4M3
+ * magnitudes, so the largest block scale lands on 448); S = 1 for an
+ * all-zero tensor. */
+static float nvfp4_tensor_scale(double amax)
+{
+    return amax > 0.0 ? (float)(amax / 2688.0) : 1.0f;
+}
+
+/* NVFP4 quantization of W[N][K] (K a multiple of 16): the per-tensor scale S
+ * from the largest |w| of the whole tensor; per block of 16 along K the E4M3
+ * scale byte s8 = the E4M3 value nearest to max|w| / (6 S) (ties to even,
+ * saturating at 448); the E2M1 codes (sign in bit 3) nearest to
+ * w / (E4M3(s8) * S) (ties to even, saturating at 6).  A block whose scale
+ * byte is 0 stores codes 0 (a negative value keeps its sign bit, as in MXFP4).
+ * A non-finite input is an error. */
+int orc_quantize_nvfp4(const void* W, int dtype, int64_t N, int64_t K, uint8_t* q, uint8_t* s8,
+                       float* tensor_scale)
+{
+    if (!W || !q || !s8 || !tensor_scale || N <= 0 || K <= 0 || K % 16) return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16) return ORC_EINVAL;
+    double amax = 0.0;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float v = load_w(W, dtype, i);
+        if (!isfinite(v)) return ORC_ERANGE;
+        if (fabs((double)v) > amax) amax = fabs((double)v);
+    }
+    const float S = nvfp4_tensor_scale(amax);
+    *tensor_scale = S;
+    const int64_t G = K / 16;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < G; ++j) {
+            float v[16];
+            double bmax = 0.0;
+            for (int i = 0; i < 16; ++i) {
+                v[i] = load_w(W, dtype, n * K + j * 16 + i);
+                if (fabs((double)v[i]) > bmax) bmax = fabs((double)v[i]);
+            }
+            int sc = nearest_scaled(bmax, 6.0 * (double)S, e4m3_magnitude, 127);
+            s8[n * G + j] = (uint8_t)sc;
+            double d = e4m3_magnitude(sc) * (double)S;
+            for (int i = 0; i < 16; ++i) {
+                int m = sc == 0 ? 0 : nearest_scaled(fabs((double)v[i]), d, e2m1_magnitude, 8);
+                q[n * K + j * 16 + i] = (uint8_t)(((v[i] < 0.0f) ? 8 : 0) | m);
+            }
+        }
+    }
+    return 0;
+}
+
+/* w_hat = fp32(E2M1(q) * E4M3(s8) * S): the product of the two format values
+ * is exact, and one rounding to fp32 applies the per-tensor scale; fp16 /
+ * bf16 outputs are one further rounding of that fp32 value. */
+int orc_dequant_nvfp4(const uint8_t* q, const uint8_t* s8, float tensor_scale, int64_t N, int64_t K,
+                      int out_dtype, void* out)
+{
+    if (!q || !s8 || !out || N <= 0 || K <= 0 || K % 16) return ORC_EINVAL;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EINVAL;
+    int64_t G = K / 16;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int c = q[n * K + k] & 15;
+            double mag = e2m1_magnitude(c & 7) * e4m3_magnitude(s8[n * G + k / 16] & 127);
+            float f = (float)(((c & 8) ? -mag : mag) * (double)tensor_scale);
+            if (out_dtype == ORC_F32) ((float*)out)[n * K + k] = f;
+            else if (out_dtype == ORC_F16) ((uint16_t*)out)[n * K + k] = orc_f32_to_f16(f);
+            else ((uint16_t*)out)[n * K + k] = orc_f32_to_bf16(f);
+        }
+    return 0;
+}
+
+/* Rows [n0, n0 + nrows) of y = x * What^T for NVFP4 weights, in fp64, with
+ * the exact decoded weights E2M1(q) * E4M3(s8) * S (before any rounding). */
+int orc_gemm_rows_nvfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint8_t* q,
+                            const uint8_t* s8, float tensor_scale, int64_t n0, int64_t nrows, double* y_rows)
+{
+    if (!x_f16 || !q || !s8 || !y_rows || M <= 0 || N <= 0 || K <= 0 || K % 16) return ORC_EINVAL;
+    if (n0 < 0 || nrows <= 0 || n0 + nrows > N) return ORC_EINVAL;
+    int64_t G = K / 16;
+    double* xd = x_to_f64(x_f16, M * K);
+    if (!xd) return ORC_EINVAL;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = n0 + i;
+        double* wr = (double*)malloc(sizeof(double) * (size_t)K);
+        for (int64_t k = 0; k < K; ++k) {
+            int c = q[n * K + k] & 15;
+            double mag = e2m1_magnitude(c & 7) * e4m3_magnitude(s8[n * G + k / 16] & 127) * (double)tensor_scale;
+            wr[k] = (c & 8) ? -mag : mag;
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * wr[k];
             y_rows[m * nrows + i] = acc;
         }
         free(wr);

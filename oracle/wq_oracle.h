@@ -75,6 +75,15 @@ int orc_pack_device_mxfp4(const uint8_t* q, int64_t N, int64_t K, uint8_t* out);
 int orc_gemm_rows_mxfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint8_t* q,
                             const uint8_t* e8, int64_t n0, int64_t nrows, double* y_rows);
 
+/* NVFP4: E2M1 codes (sign in bit 3), E4M3 scale bytes per block of 16 and one
+ * fp32 scale per tensor (device layout: orc_pack_device_mxfp4). */
+int orc_quantize_nvfp4(const void* W, int dtype, int64_t N, int64_t K, uint8_t* q, uint8_t* s8,
+                       float* tensor_scale);
+int orc_dequant_nvfp4(const uint8_t* q, const uint8_t* s8, float tensor_scale, int64_t N, int64_t K,
+                      int out_dtype, void* out);
+int orc_gemm_rows_nvfp4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint8_t* q,
+                            const uint8_t* s8, float tensor_scale, int64_t n0, int64_t nrows, double* y_rows);
+
 int orc_symmetric(const double* w, int64_t n, int bits, int32_t* q, double* s_out, double* w_hat);
 
 double orc_bits_per_weight(int bits, int g, int scale_bits, int zero_bits);

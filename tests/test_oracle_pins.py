@@ -757,6 +757,161 @@ def test_mxfp4_gemm_rows(M, N, K, n0, nrows):
 
 
 # --------------------------------------------------------------------------
+# NVFP4 (methods page, "Hardware, formats and the roofline" key box: 4-bit
+# values, one E4M3 scale per 16 values, a per-tensor fp32 scale, 4.5 bits)
+# --------------------------------------------------------------------------
+
+E2M1_GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+             Fraction(6)]
+
+
+def _e4m3_grid():
+    """The 127 finite non-negative E4M3 magnitudes from torch's own float8
+    decoder (codes 0..126), as exact fractions."""
+    import torch
+    v = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return [Fraction(float(x)) for x in v]
+
+
+def _nearest(a, d, grid):
+    """Index of the grid value g minimizing |a - g d| (exact), ties to the even
+    index, brute force over the whole grid."""
+    dist = [abs(a - g * d) for g in grid]
+    best = min(dist)
+    idx = [i for i, x in enumerate(dist) if x == best]
+    return idx[0] if len(idx) == 1 else [i for i in idx if i % 2 == 0][0]
+
+
+def test_nvfp4_storage_matches_printed_bits():
+    import oracle as orc
+    # the key box prints 4.5 bits per value, 70B x 4.5 / 8 = 39.4 GB, and a
+    # 3.56x reduction from fp16 (the per-tensor scale adds 32 bits per tensor)
+    assert orc.bits_per_weight(4, 16, 8, 0) == 4.5
+    assert round(orc.storage_bytes(70_000_000_000, 4, 16, 8, 0) / 1e9, 1) == 39.4
+    assert round(16 / orc.bits_per_weight(4, 16, 8, 0), 2) == 3.56
+
+
+def test_nvfp4_scale_byte_decodes_as_e4m3():
+    # code 2 (E2M1 1.0) times scale byte c times S = 1 decodes to E4M3(c):
+    # every one of the 127 finite magnitudes, against torch's float8 decoder
+    import oracle as orc
+    grid = _e4m3_grid()
+    s8 = np.arange(127, dtype=np.uint8).reshape(-1, 1)
+    q = np.full((127, 16), 2, np.uint8)
+    w = orc.dequant_nvfp4(q, s8, 1.0)
+    assert [Fraction(float(x)) for x in w[:, 0]] == grid
+    assert float(grid[126]) == 448.0 and float(grid[8]) == 2.0 ** -6 and float(grid[1]) == 2.0 ** -9
+
+
+def test_nvfp4_scales_and_codes_are_nearest_with_ties_to_even():
+    import oracle as orc
+    e4 = _e4m3_grid()
+    rng = np.random.default_rng(70)
+    S = 2.0 ** -8  # a first block with max|w| = 2688 * 2^-8 fixes S exactly
+    d6 = Fraction(6) * Fraction(S)
+    mids = [(e4[k] + e4[k + 1]) / 2 * d6 for k in range(0, 126, 5)]
+    maxes = [float(m) for m in mids] + list(rng.uniform(0, 448 * 6 * S, 40)) + [448 * 6 * S, 0.25 * 2 ** -9 * 6 * S]
+    rows = [np.full(16, 0.0, np.float32)]
+    rows[0][0] = 2688 * S
+    for m in maxes:
+        blk = (rng.uniform(-1, 1, 16) * m).astype(np.float32)
+        blk[3] = np.float32(m)
+        rows.append(blk)
+    W = np.concatenate(rows).reshape(1, -1).astype(np.float32)
+    q, s8, St = orc.quantize_nvfp4(W)
+    assert St == S
+    for j in range(W.shape[1] // 16):
+        blk = W[0, 16 * j:16 * j + 16]
+        bmax = Fraction(float(np.abs(blk).max()))
+        assert s8[0, j] == _nearest(bmax, d6, e4), j
+        sb = e4[s8[0, j]]
+        for i in range(16):
+            v = Fraction(float(blk[i]))
+            m = 0 if sb == 0 else _nearest(abs(v), sb * Fraction(S), E2M1_GRID)
+            assert q[0, 16 * j + i] & 7 == m, (j, i)
+            assert (q[0, 16 * j + i] >> 3) == (1 if blk[i] < 0 else 0)
+
+
+def test_nvfp4_tensor_scale_grid_values_and_powers_of_two():
+    import oracle as orc
+    rng = np.random.default_rng(71)
+    # the tensor scale: fp32 of max|w| / 2688, 1 for an all-zero tensor
+    W = (rng.standard_normal((5, 64)) * 0.03).astype(np.float32)
+    q, s8, S = orc.quantize_nvfp4(W)
+    assert S == float(np.float32(float(np.abs(W).max()) / 2688.0))
+    qz, sz, Sz = orc.quantize_nvfp4(np.zeros((2, 32), np.float32))
+    assert Sz == 1.0 and not sz.any() and not qz.any()
+    # scaling the tensor by 2^k scales S by 2^k and keeps every byte
+    for k in (-7, 5):
+        qk, sk, Sk = orc.quantize_nvfp4((W * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(qk, q) and np.array_equal(sk, s8) and Sk == S * 2.0 ** k
+    # weights on the grid (E2M1 times an E4M3 scale times a power-of-two S,
+    # each block holding a 6, one block with scale 448) decode exactly
+    e4 = np.array([float(x) for x in _e4m3_grid()])
+    grid = np.array([float(x) for x in E2M1_GRID])
+    Sg = 2.0 ** -12
+    sc = rng.integers(40, 127, (4, 8))
+    sc[0, 0] = 126
+    c = rng.integers(0, 8, (4, 128))
+    c[:, ::16] = 7
+    sign = np.where(rng.integers(0, 2, (4, 128)) == 1, -1.0, 1.0)
+    Wg = (sign * grid[c] * np.repeat(e4[sc], 16, axis=1) * Sg).astype(np.float32)
+    qg, sg, Sgot = orc.quantize_nvfp4(Wg)
+    assert Sgot == Sg and np.array_equal(sg, sc) and np.array_equal(qg & 7, c)
+    assert np.array_equal(orc.dequant_nvfp4(qg, sg, Sgot), Wg)
+
+
+def test_nvfp4_error_bound():
+    import oracle as orc
+    rng = np.random.default_rng(72)
+    W = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    W[:, 9] *= 30
+    q, s8, S = orc.quantize_nvfp4(W)
+    e4 = np.array([float(x) for x in _e4m3_grid()])
+    X = np.repeat(e4[s8], 16, axis=1) * S  # the step unit of each block
+    w_hat = orc.dequant_nvfp4(q, s8, S).astype(np.float64)
+    err = np.abs(w_hat - W)
+    v = np.abs(W) / np.where(X > 0, X, 1.0)
+    half_step = np.where(v < 2, 0.25, np.where(v < 4, 0.5, np.where(v <= 6, 1.0, np.inf)))
+    ulp32 = np.abs(W) * 2.0 ** -23  # the final fp32 rounding
+    inside = (v <= 6) & (X > 0)
+    assert np.all(err[inside] <= half_step[inside] * X[inside] + ulp32[inside])
+    # past 6 the code saturates; the block scale rounds to within 1/16 of the
+    # block's max / 6, so the saturated part stays below the scale's rounding
+    sat = (v > 6) & (X > 0)
+    assert np.all(err[sat] <= (v[sat] - 6) * X[sat] + ulp32[sat]) and np.all(v[sat] < 6 * (1 + 1 / 16) + 1e-9)
+
+
+@pytest.mark.parametrize("M,N,K,n0,nrows", [(3, 40, 256, 10, 17), (2, 33, 96, 0, 33), (1, 21, 160, 20, 1),
+                                            (4, 50, 64, 0, 1)])
+def test_nvfp4_gemm_rows(M, N, K, n0, nrows):
+    """The NVFP4 product rows equal the fp64 product of the exactly decoded
+    weights E2M1 * E4M3 * S, decoded here with torch's float8 grid; block
+    scales differ per row and per block, so a wrong scale-row stride or block
+    index changes the result."""
+    import oracle as orc
+    rng = np.random.default_rng(73 + M * 7 + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W *= (2.0 ** rng.integers(-6, 7, (N, K // 16))).repeat(16, axis=1).astype(np.float32)
+    x = workloads.f32_to_f16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    q, s8, S = orc.quantize_nvfp4(W)
+    assert len(np.unique(s8)) > 8
+    e4 = np.array([float(v) for v in _e4m3_grid()])
+    grid = np.array([float(v) for v in E2M1_GRID])
+    w_exact = np.where(q & 8, -1.0, 1.0) * grid[q & 7] * np.repeat(e4[s8], 16, axis=1) * S
+    xf = orc.f16_bits_to_f32(x).reshape(M, K).astype(np.float64)
+    y = np.array([[sum(xf[m, k] * w_exact[n, k] for k in range(K)) for n in range(N)] for m in range(M)])
+    assert np.allclose(orc.gemm_rows_nvfp4_f64(x, q, s8, S, n0, nrows), y[:, n0:n0 + nrows], rtol=1e-12, atol=1e-12)
+    assert np.allclose(orc.gemm_rows_nvfp4_f64(x, q, s8, S, 0, N), y, rtol=1e-12, atol=1e-12)
+    # one-hot activations select the exactly decoded weights of one input channel
+    for k in (0, 37 % K, K - 1):
+        xo = np.zeros((1, K), np.float32)
+        xo[0, k] = 1.0
+        yo = orc.gemm_rows_nvfp4_f64(workloads.f32_to_f16_bits(xo), q, s8, S, 0, N)
+        assert np.array_equal(yo[0], w_exact[:, k])
+
+
+# --------------------------------------------------------------------------
 # Number formats against independent implementations
 # --------------------------------------------------------------------------
 
