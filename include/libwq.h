@@ -372,8 +372,7 @@ int wq_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint32_t* qpacke
 int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype,
                      void* W_hat, void* stream);
 
-/* Workspace bytes for wq_gemm_mxfp4 / _ex (same rules as
- * wq_gemm_workspace_bytes at group 32).  Host-only. */
+/* Workspace bytes for wq_gemm_mxfp4 / _ex (either kernel family).  Host-only. */
 size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV
@@ -393,6 +392,61 @@ int wq_gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, con
 
 /* As wq_gemm_plan, for wq_gemm_mxfp4_ex. */
 int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, size_t buf_len);
+
+/* ---- NVFP4 weights ----------------------------------------------------------
+ * "Quantization Methods Compared: INT8, GPTQ, AWQ, FP8, FP4 and KV-Cache
+ * Quantization", section "Hardware, formats and the roofline" (its key box):
+ * 4-bit values with one FP8 E4M3 scale per 16 values plus one fp32 scale per
+ * tensor, 4.5 bits per value; "Quantization for LLM inference", section
+ * "Microscaling: NVFP4 and MXFP4".  Elements are E2M1 as in MXFP4; E4M3 has 4
+ * exponent bits (bias 7) and 3 mantissa bits, largest finite value 448.  The
+ * pages leave the two scales' choice open; read as:
+ *   S = fp32(fp64(max|W| / (6 * 448))) over the whole tensor (1 when all zero);
+ *   s8 = the E4M3 value nearest to the block's max|w| / (6 S), ties to even,
+ *   saturating at 448;
+ *   code = the E2M1 value nearest to w / (E4M3(s8) * S), ties to even,
+ *   saturating at 6, sign in bit 3; a block with s8 = 0 stores codes 0;
+ *   What = fp32(E2M1(code) * E4M3(s8) * S) (one rounding).
+ * Layouts: q_codes [N][K] uint8; s8 [N][K/16]; qpacked the MXFP4 tiles
+ * (wq_pack_mxfp4 packs codes); tensor_scale one fp32 in device memory.  K a
+ * multiple of 32 (WQ_EUNSUPPORTED otherwise).  Input weights must be finite
+ * (a non-finite weight gives unspecified codes). */
+
+/* Byte sizes of qpacked and s8 for [N][K].  Host-only. */
+int wq_layout_bytes_nvfp4(int64_t N, int64_t K, size_t* qpacked_bytes, size_t* s8_bytes);
+
+/* NVFP4 quantization of W [N][K] (WQ_F32, WQ_BF16 or WQ_F16, 16-byte aligned).
+ * tensor_scale (device, 4-byte aligned) receives S and s8 [N][K/16] the block
+ * scales (both required); q_codes (8-byte aligned) and qpacked (16-byte
+ * aligned) may each be NULL.  Four launches on `stream`: a fill and a
+ * reduction for S, then the quantizer.  Deterministic. */
+int wq_quantize_nvfp4(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* s8,
+                      float* tensor_scale, uint32_t* qpacked, void* stream);
+
+/* What = fp32(E2M1(code) * E4M3(s8) * S) into W_hat [N][K] (WQ_F32; WQ_F16 /
+ * WQ_BF16 one round-to-nearest-even of that fp32 value); W_hat 16-byte aligned. */
+int wq_dequant_nvfp4(const uint32_t* qpacked, const uint8_t* s8, const float* tensor_scale, int64_t N, int64_t K,
+                     int out_dtype, void* W_hat, void* stream);
+
+/* Workspace bytes for wq_gemm_nvfp4 / _ex (either kernel family).  Host-only. */
+size_t wq_gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y = x * What^T with NVFP4 weights decoded inside the kernel.  The tensor
+ * scale factors out of every output: y = fp16(S * sum_k x * E2M1 * E4M3), the
+ * GEMV summing exact E2M1 values times x per block in fp32 and applying the
+ * block scale in fp32, the MFMA GEMM taking the exact fp16 operands
+ * E2M1 * E4M3.  Arguments, workspace contract and errors as wq_gemm_w4a16
+ * with s8 for the scales and tensor_scale (device) for S. */
+int wq_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked, const uint8_t* s8,
+                  const float* tensor_scale, uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As wq_gemm_nvfp4, with the kernel family chosen by `path` (wq_path). */
+int wq_gemm_nvfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint8_t* s8, const float* tensor_scale, uint16_t* y_f16, void* workspace,
+                     size_t workspace_bytes, int path, void* stream);
+
+/* As wq_gemm_plan, for wq_gemm_nvfp4_ex. */
+int wq_gemm_nvfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, size_t buf_len);
 
 /* ---- INT4 KV cache in blocks of 128 -----------------------------------------
  * "Quantization for LLM inference", section "KV cache quantization": the K/V

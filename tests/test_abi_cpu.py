@@ -378,3 +378,30 @@ def test_binding_rejects_bad_activations_and_outputs():
     qm = wq.QuantizedWeightMX(torch.zeros(qb, dtype=torch.uint8), torch.zeros((N, K // 32), dtype=torch.uint8), N, K)
     with pytest.raises(ValueError):
         wq.wq_gemm_mxfp4(x, qm, y=torch.zeros((2, 32), dtype=torch.float16))
+
+
+def test_nvfp4_entry_points_checked_on_host():
+    # layout sizes: MXFP4 tiles, one scale byte per 16 values
+    qb, sb = wq.wq_layout_bytes_nvfp4(100, 1152)
+    assert (qb, sb) == (112 * 1152 // 2, 100 * 72)
+    g = "wq_gemm_nvfp4_ex"
+    # K a multiple of 32; the tensor scale and the scale bytes are required
+    assert call(g, 4, 64, 48, A, A, A, A, A, None, 0, 0, None) == wq.WQ_EUNSUPPORTED
+    assert call(g, 4, 64, 256, A, A, A, None, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(g, 4, 64, 256, A, A, None, A, A, None, 0, 0, None) == wq.WQ_EINVAL
+    assert call(g, 4, 64, 256, A, A, A, B, A, None, 0, 0, None) == wq.WQ_EALIGN
+    assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 256, None, A, None, None, None) == wq.WQ_EINVAL
+    assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 80, None, A, A, None, None) == wq.WQ_EUNSUPPORTED
+    assert call("wq_dequant_nvfp4", A, A, None, 64, 256, wq.WQ_F32, A, None) == wq.WQ_EINVAL
+    # plans: the VALU GEMV below WQ_AUTO_MFMA_MIN_M rows, the MFMA GEMM at it
+    lo = wq.WQ_AUTO_MFMA_MIN_M
+    assert wq.wq_gemm_nvfp4_plan(lo - 1, 8192, 8192).startswith("gemv_kernel<MT=4, W=8, KQ=4, G=16, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(lo, 8192, 8192).startswith("gemm_kernel<MB=1, NPW=2, G=16, NVFP4>")
+    # the workspace query covers the format's own plans
+    for M, N, K in [(1, 1024, 28672), (8, 1024, 8192), (128, 48, 28672)]:
+        need = wq.wq_gemm_nvfp4_workspace_bytes(M, N, K)
+        for path in (wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA):
+            plan = wq.wq_gemm_nvfp4_plan(M, N, K, path)
+            if split_k(plan) > 1:
+                assert need > 0, (M, N, K, plan)
+

@@ -37,6 +37,8 @@ EXPORTED = (
     "wq_quantize_groups_scaled", "wq_scale_activations", "wq_channel_absmean",
     "wq_layout_bytes_mxfp4", "wq_quantize_mxfp4", "wq_pack_mxfp4", "wq_dequant_mxfp4",
     "wq_gemm_mxfp4_workspace_bytes", "wq_gemm_mxfp4", "wq_gemm_mxfp4_ex", "wq_gemm_mxfp4_plan",
+    "wq_layout_bytes_nvfp4", "wq_quantize_nvfp4", "wq_dequant_nvfp4",
+    "wq_gemm_nvfp4_workspace_bytes", "wq_gemm_nvfp4", "wq_gemm_nvfp4_ex", "wq_gemm_nvfp4_plan",
     "wq_read_probe", "wq_mfma_probe", "wq_clock_probe",
 )
 
@@ -96,6 +98,13 @@ def lib() -> ctypes.CDLL:
         "wq_gemm_mxfp4": (I, [I64, I64, I64, P, P, P, P, P, SZ, P]),
         "wq_gemm_mxfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, SZ, I, P]),
         "wq_gemm_mxfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
+        "wq_layout_bytes_nvfp4": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "wq_quantize_nvfp4": (I, [P, I, I64, I64, P, P, P, P, P]),
+        "wq_dequant_nvfp4": (I, [P, P, P, I64, I64, I, P, P]),
+        "wq_gemm_nvfp4_workspace_bytes": (SZ, [I64, I64, I64]),
+        "wq_gemm_nvfp4": (I, [I64, I64, I64, P, P, P, P, P, P, SZ, P]),
+        "wq_gemm_nvfp4_ex": (I, [I64, I64, I64, P, P, P, P, P, P, SZ, I, P]),
+        "wq_gemm_nvfp4_plan": (I, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
         "wq_read_probe": (I, [P, SZ, SZ, I, I, I, P, P]),
         "wq_mfma_probe": (I, [I, I, I, P, P]),
         "wq_clock_probe": (I, [I, ctypes.c_uint32, P, P]),
@@ -548,6 +557,75 @@ def wq_gemm_mxfp4(x: torch.Tensor, qw: QuantizedWeightMX, *, y: torch.Tensor | N
     _check(lib().wq_gemm_mxfp4_ex(M, qw.N, qw.K, _ptr(x), _ptr(qw.qpacked), _ptr(qw.e8), _ptr(y), _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(), path,
                                   _stream(stream)), "wq_gemm_mxfp4")
+    return y
+
+
+# ---- NVFP4 weights (E2M1 codes, blocks of 16, E4M3 scales, fp32 tensor scale) --
+
+@dataclass
+class QuantizedWeightNV:
+    """Device buffers of one NVFP4-quantized [N][K] weight matrix."""
+    qpacked: torch.Tensor       # uint8, 1 KB tiles (the MXFP4 layout)
+    s8: torch.Tensor            # uint8 [N][K/16], E4M3 block scales
+    tensor_scale: torch.Tensor  # float32 [1]
+    N: int
+    K: int
+
+
+def wq_layout_bytes_nvfp4(N: int, K: int):
+    q, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wq_layout_bytes_nvfp4(N, K, ctypes.byref(q), ctypes.byref(s)), "wq_layout_bytes_nvfp4")
+    return q.value, s.value
+
+
+def alloc_quantized_nvfp4(N: int, K: int, device="cuda") -> QuantizedWeightNV:
+    qb, _ = wq_layout_bytes_nvfp4(N, K)
+    return QuantizedWeightNV(torch.empty(qb, dtype=torch.uint8, device=device),
+                             torch.empty((N, K // 16), dtype=torch.uint8, device=device),
+                             torch.empty(1, dtype=torch.float32, device=device), N, K)
+
+
+def wq_quantize_nvfp4(W: torch.Tensor, *, codes: bool = False, stream=None):
+    """NVFP4 quantization of W[N][K] (float32, bfloat16 or float16, on the GPU).
+    Returns a dict with ``qw`` (QuantizedWeightNV) and, if asked, ``q_codes``
+    (uint8 [N][K])."""
+    N, K = W.shape
+    qw = alloc_quantized_nvfp4(N, K, W.device)
+    q_codes = torch.empty((N, K), dtype=torch.uint8, device=W.device) if codes else None
+    _check(lib().wq_quantize_nvfp4(_ptr(W), _DT.get(W.dtype, -1), N, K, _ptr(q_codes), _ptr(qw.s8),
+                                   _ptr(qw.tensor_scale), _ptr(qw.qpacked), _stream(stream)), "wq_quantize_nvfp4")
+    return {"qw": qw, "q_codes": q_codes}
+
+
+def wq_dequant_nvfp4(qw: QuantizedWeightNV, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty((qw.N, qw.K), dtype=out_dtype, device=qw.qpacked.device)
+    _check(lib().wq_dequant_nvfp4(_ptr(qw.qpacked), _ptr(qw.s8), _ptr(qw.tensor_scale), qw.N, qw.K,
+                                  _DT.get(out_dtype, -1), _ptr(out), _stream(stream)), "wq_dequant_nvfp4")
+    return out
+
+
+def wq_gemm_nvfp4_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().wq_gemm_nvfp4_workspace_bytes(M, N, K))
+
+
+def wq_gemm_nvfp4_plan(M: int, N: int, K: int, path: int = WQ_PATH_AUTO) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().wq_gemm_nvfp4_plan(M, N, K, path, buf, len(buf)), "wq_gemm_nvfp4_plan")
+    return buf.value.decode()
+
+
+def wq_gemm_nvfp4(x: torch.Tensor, qw: QuantizedWeightNV, *, y: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, path: int = WQ_PATH_AUTO, stream=None) -> torch.Tensor:
+    """y[M][N] = x[M][K] * What^T with NVFP4 weights, fp16 in and out
+    (workspace as for wq_gemm_w4a16)."""
+    M = _check_x(x, qw.K, qw.qpacked)
+    y = _out_y(y, M, qw.N, x)
+    if workspace is None:
+        workspace = _default_workspace(wq_gemm_nvfp4_workspace_bytes(M, qw.N, qw.K), x.device, stream)
+    _check(lib().wq_gemm_nvfp4_ex(M, qw.N, qw.K, _ptr(x), _ptr(qw.qpacked), _ptr(qw.s8), _ptr(qw.tensor_scale),
+                                  _ptr(y), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(), path,
+                                  _stream(stream)), "wq_gemm_nvfp4")
     return y
 
 

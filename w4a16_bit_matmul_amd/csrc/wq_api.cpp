@@ -162,11 +162,12 @@ namespace {
 int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x_f16, const void* qpacked,
                const uint16_t* s_f16, const uint8_t* zpacked, const uint16_t* y_f16, const void* workspace,
                size_t workspace_bytes, int path, bool* mfma) {
-  if (!x_f16 || !qpacked || (fmt != wq::kFmtMxfp4 && !s_f16) || (fmt != wq::kFmtInt8 && !zpacked) || !y_f16)
+  const bool fp16_scales = fmt == wq::kFmtInt4 || fmt == wq::kFmtInt8;
+  if (!x_f16 || !qpacked || (fp16_scales && !s_f16) || (fmt != wq::kFmtInt8 && !zpacked) || !y_f16)
     return WQ_EINVAL;
   if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
-  int st = check_shape(N, K, group);
+  int st = check_shape(N, K, fmt == wq::kFmtNvfp4 ? 32 : group);  // NVFP4: blocks of 16, K a multiple of 32
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
   *mfma = auto_mfma(M, path);
@@ -180,9 +181,9 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
 
 hipError_t launch_one(bool mfma, int64_t M, int64_t N, int64_t K, int group, int bits, const uint16_t* x_f16,
                       const void* qpacked, const uint16_t* s_f16, const uint8_t* zpacked, uint16_t* y_f16,
-                      void* workspace, hipStream_t s) {
-  if (!mfma) return wq::launch_gemv(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
-  return wq::launch_gemm(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s);
+                      void* workspace, hipStream_t s, const float* tscale = nullptr) {
+  if (!mfma) return wq::launch_gemv(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s, tscale);
+  return wq::launch_gemm(M, N, K, group, bits, x_f16, qpacked, s_f16, zpacked, y_f16, workspace, s, tscale);
 }
 
 }  // namespace
@@ -394,7 +395,16 @@ int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int6
                                              static_cast<hipStream_t>(stream)));
 }
 
-size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) { return wq_gemm_workspace_bytes(M, N, K, 32); }
+// the larger of the two kernel families' needs, for the format's own GEMV plan
+static size_t workspace_fmt(int64_t M, int64_t N, int64_t K, int group, int fmt) {
+  if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, 32)) return 0;
+  const size_t a = wq::gemv_workspace_bytes(M, N, K, group, fmt), b = wq::gemm_workspace_bytes(M, N, K, group);
+  return a > b ? a : b;
+}
+
+size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return workspace_fmt(M, N, K, 32, wq::kFmtMxfp4);
+}
 
 int wq_gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
                      const uint8_t* e8, uint16_t* y_f16, void* workspace, size_t workspace_bytes, int path,
@@ -427,7 +437,6 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   return WQ_OK;
 }
 
-}  // extern "C"
 
 // ---- streaming-read probe (measurement aid) ----------------------------------
 
@@ -455,3 +464,77 @@ int wq_clock_probe(int workgroups, uint32_t ticks, unsigned long long* out, void
   if (!aligned(out, 8)) return WQ_EALIGN;
   return hip_status(wq::launch_clock_probe(workgroups, ticks, out, static_cast<hipStream_t>(stream)));
 }
+
+// ---- NVFP4 --------------------------------------------------------------------
+
+int wq_layout_bytes_nvfp4(int64_t N, int64_t K, size_t* qpacked_bytes, size_t* s8_bytes) {
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  const int64_t Np = (N + 15) / 16 * 16, Kp = (K + 127) / 128 * 128;
+  if (qpacked_bytes) *qpacked_bytes = (size_t)(Np * Kp / 2);
+  if (s8_bytes) *s8_bytes = (size_t)(N * (K / 16));
+  return WQ_OK;
+}
+
+int wq_quantize_nvfp4(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* s8,
+                      float* tensor_scale, uint32_t* qpacked, void* stream) {
+  if (!W || !s8 || !tensor_scale) return WQ_EINVAL;
+  if (w_dtype != WQ_F32 && w_dtype != WQ_BF16 && w_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (!aligned(W, 16) || !aligned(tensor_scale, 4) || (qpacked && !aligned(qpacked, 16)) ||
+      (q_codes && !aligned(q_codes, 8)))
+    return WQ_EALIGN;
+  return hip_status(wq::launch_quantize_nvfp4(W, w_dtype, N, K, tensor_scale, q_codes, s8,
+                                              reinterpret_cast<uint8_t*>(qpacked), static_cast<hipStream_t>(stream)));
+}
+
+int wq_dequant_nvfp4(const uint32_t* qpacked, const uint8_t* s8, const float* tensor_scale, int64_t N, int64_t K,
+                     int out_dtype, void* W_hat, void* stream) {
+  if (!qpacked || !s8 || !tensor_scale || !W_hat) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16 && out_dtype != WQ_F16) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (!aligned(qpacked, 16) || !aligned(tensor_scale, 4) || !aligned(W_hat, 16)) return WQ_EALIGN;
+  return hip_status(wq::launch_dequant_nvfp4(reinterpret_cast<const uint8_t*>(qpacked), s8, tensor_scale, N, K,
+                                             out_dtype, W_hat, static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return workspace_fmt(M, N, K, 16, wq::kFmtNvfp4);
+}
+
+int wq_gemm_nvfp4_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked,
+                     const uint8_t* s8, const float* tensor_scale, uint16_t* y_f16, void* workspace,
+                     size_t workspace_bytes, int path, void* stream) {
+  if (!tensor_scale) return WQ_EINVAL;
+  bool mfma = false;
+  const int st = check_gemm(M, N, K, 16, wq::kFmtNvfp4, x_f16, qpacked, nullptr, s8, y_f16, workspace,
+                            workspace_bytes, path, &mfma);
+  if (st) return st;
+  if (!aligned(tensor_scale, 4)) return WQ_EALIGN;
+  return hip_status(launch_one(mfma, M, N, K, 16, wq::kFmtNvfp4, x_f16, qpacked, nullptr, s8, y_f16, workspace,
+                               static_cast<hipStream_t>(stream), tensor_scale));
+}
+
+int wq_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked, const uint8_t* s8,
+                  const float* tensor_scale, uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream) {
+  return wq_gemm_nvfp4_ex(M, N, K, x_f16, qpacked, s8, tensor_scale, y_f16, workspace, workspace_bytes, WQ_PATH_AUTO,
+                          stream);
+}
+
+int wq_gemm_nvfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, size_t buf_len) {
+  if (!buf || buf_len == 0) return WQ_EINVAL;
+  buf[0] = 0;
+  if (M <= 0 || M > (int64_t(1) << 31)) return WQ_EINVAL;
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
+  const int st = check_mx_shape(N, K);
+  if (st) return st;
+  if (auto_mfma(M, path))
+    wq::describe_gemm(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);
+  else
+    wq::describe_gemv(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);
+  return WQ_OK;
+}
+
+}  // extern "C"

@@ -31,8 +31,20 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // Code formats of the product kernels: 4-bit asymmetric / symmetric INT4 (with
 // fp16 scales and 4-bit zero-points), group absmax int8 (fp16 scales), MXFP4
 // (E2M1 codes in the INT4 tile geometry, natural nibble order, one E8M0 scale
-// byte per block of 32).
-enum : int { kFmtInt4 = 4, kFmtInt8 = 8, kFmtMxfp4 = 2 };
+// byte per block of 32), NVFP4 (the same codes and layout, one E4M3 scale byte
+// per block of 16, one fp32 scale per tensor).
+enum : int { kFmtInt4 = 4, kFmtInt8 = 8, kFmtMxfp4 = 2, kFmtNvfp4 = 3 };
+
+// The E4M3 scale byte b (0..126: 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent field 0 is m * 2^-9) as fp32 and as fp16 bits (both exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? ((e + 8u) << 10) | (m << 7) : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
+}
 
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 128;

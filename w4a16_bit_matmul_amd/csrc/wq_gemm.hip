@@ -72,6 +72,7 @@ struct GemmArgs {
   uint16_t* y;
   float* partial;      // [KS][M][N] fp32 (KS > 1 only)
   unsigned* counters;  // [gridDim.y][gridDim.x] (KS > 1 only)
+  const float* tscale; // NVFP4: the per-tensor scale (device)
   int M, N, K, KT, Gtot, GB, NBLK, kt_per_split, KS;
 };
 
@@ -134,10 +135,14 @@ __device__ __forceinline__ h8 dequant_words8(uint32_t lo, uint32_t hi, h2 sc) {
 //     pair (s, s), then the fp16 pair -(1024 + z) (4-bit; zero for int8);
 //   g = 32: [tile][step pair jp][row] 16 bytes: those two pairs for group
 //     4t + 2jp, then for group 4t + 2jp + 1;
-//   MXFP4: [tile][row] u32, the tile's four E8M0 scale bytes, block 4t first.
+//   MXFP4: [tile][row] u32, the tile's four E8M0 scale bytes, block 4t first;
+//   NVFP4: [tile][row] 16 bytes, the tile's eight E4M3 block scales as fp16.
 template <int G, int FMT = kFmtInt4>
 constexpr int sz_chunk_bytes() {
-  return FMT == kFmtMxfp4 ? kSzChunk * 128 * 4 : G == 128 ? kSzChunk * 128 * 8 : kSzChunk * 2 * 128 * 16;
+  return FMT == kFmtMxfp4   ? kSzChunk * 128 * 4
+         : FMT == kFmtNvfp4 ? kSzChunk * 128 * 16
+         : G == 128         ? kSzChunk * 128 * 8
+                            : kSzChunk * 2 * 128 * 16;
 }
 
 // The fp16 pair -(1024 + z) (exact) as bits.
@@ -175,7 +180,8 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, uint32_t m1024, uint32_t 
 // before that step's barrier) and first read in phase B.
 template <int MB, int G, bool SZV, int FMT>
 __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
-  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16),
+                "code format");
   constexpr int BITS = FMT == kFmtInt8 ? 8 : 4;
   using CodeT = std::conditional_t<BITS == 4, uint2, u4>;  // one wave's two MFMA steps of a tile
   constexpr int TB = BITS == 4 ? kTileBytes : kTileBytes8;
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   constexpr int XTILE = ROWS * 256;                            // one K tile of activations in LDS
   constexpr int XCH = ROWS * 16 >= NTH ? ROWS * 16 / NTH : 1;  // 16-byte chunks per thread per tile
   constexpr int SZB = sz_chunk_bytes<G, FMT>();
-  constexpr int SZW = FMT == kFmtMxfp4 ? 1 : 2;  // staged words per block and step
+  constexpr int SZW = FMT == kFmtMxfp4 || FMT == kFmtNvfp4 ? 1 : 2;  // staged words per block and step
   static_assert(ROWS * 16 % NTH == 0 || NTH % (ROWS * 16) == 0, "whole chunks per thread");
   extern __shared__ __align__(16) uint8_t smem[];  // [2][XTILE] activations, [2][SZB] scales
 
@@ -279,6 +285,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         v.s[1] = b[1];
       }
       v.z = 0u;
+    } else if constexpr (FMT == kFmtNvfp4) {  // sixteen scale bytes: blocks 8 t0 .. 8 t0 + 15
+      if constexpr (SZV) {  // Gtot % 16 == 0
+        const u4 t = *reinterpret_cast<const u4*>(a.zp + srow + min(8 * t0, a.Gtot - 16));
+        v.s[0] = t.x; v.s[1] = t.y; v.s[2] = t.z; v.s[3] = t.w;
+      } else {
+        uint32_t b[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) b[q >> 2] |= (uint32_t)a.zp[srow + min(8 * t0 + q, a.Gtot - 1)] << (8 * (q & 3));
+        v.s[0] = b[0]; v.s[1] = b[1]; v.s[2] = b[2]; v.s[3] = b[3];
+      }
+      v.z = 0u;
     } else if constexpr (G == 128) {
       if constexpr (SZV) {  // Gtot even: one u32 holds both scales
         v.s[0] = *reinterpret_cast<const uint32_t*>(a.s + srow + min(t0, a.Gtot - 2));
@@ -318,6 +335,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     if constexpr (FMT == kFmtMxfp4) {
       *reinterpret_cast<uint32_t*>(buf + (2 * sp) * 512 + 4 * sn) = v.s[0];
       *reinterpret_cast<uint32_t*>(buf + (2 * sp + 1) * 512 + 4 * sn) = v.s[1];
+    } else if constexpr (FMT == kFmtNvfp4) {
+      // tile 2p + e: bytes of s[2e], s[2e + 1] (blocks 8 t .. 8 t + 7) as fp16
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t wd = v.s[2 * e + (k >> 1)], sh = 16 * (k & 1);
+          h[k] = e4m3_to_f16_bits((wd >> sh) & 0xffu) | (e4m3_to_f16_bits((wd >> (sh + 8)) & 0xffu) << 16);
+        }
+        *reinterpret_cast<u4*>(buf + ((2 * sp + e) * 128 + sn) * 16) = u4{h[0], h[1], h[2], h[3]};
+      }
     } else if constexpr (G == 128) {
       const uint32_t s0 = SZV ? v.s[0] & 0xffffu : v.s[0];
       const uint32_t s1 = SZV ? v.s[0] >> 16 : v.s[1];
@@ -368,6 +397,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
       const int row = szrow + 16 * b;
       if constexpr (FMT == kFmtMxfp4) {
         v.w[b][0] = *reinterpret_cast<const uint32_t*>(szt + tt * 512 + 4 * row);
+      } else if constexpr (FMT == kFmtNvfp4) {
+        // the lane's eight columns of step j lie in block 2j + c / 2 of the tile
+        const int j = 2 * jp + jj;
+        v.w[b][0] = *reinterpret_cast<const uint16_t*>(szt + (tt * 128 + row) * 16 + 2 * (2 * j + (c >> 1)));
       } else {
         const uint2 t = *reinterpret_cast<const uint2*>(
             szt + (G == 128 ? (tt * 128 + row) * 8 : ((tt * 2 + jp) * 128 + row) * 16 + 8 * jj));
@@ -392,6 +425,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         const int j = 2 * jp + jj;
         const float scale = __builtin_bit_cast(float, ((sz.w[b][0] >> (8 * j)) & 0xffu) << 23);
         bf[b] = dequant_word_mx(jj ? cur[b].y : cur[b].x, scale);
+      } else if constexpr (FMT == kFmtNvfp4) {
+        // E2M1 values (exact) times the block's E4M3 scale: exact in fp16
+        const h8 v = dequant_word_mx(jj ? cur[b].y : cur[b].x, 1.0f);
+        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sz.w[b][0]);
+        bf[b] = v * s;
       } else if constexpr (FMT == kFmtInt4) {
         const h2 nb = as_h2(sz.w[b][1]), nb64 = nb + h2{(_Float16)960.0f, (_Float16)960.0f};  // -(64 + z), exact
         bf[b] = dequant_word(jj ? cur[b].y : cur[b].x, m1024, m64, nb, nb64, as_h2(sz.w[b][0]));
@@ -484,6 +522,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 
   // every wave's last LDS reads are done before the reduction reuses LDS
   lds_barrier();
+  // NVFP4: the per-tensor scale multiplies each output (partial sums stay unscaled)
+  const float ys = FMT == kFmtNvfp4 ? *a.tscale : 1.0f;
 
   // ---- add the second step pair's sums to the first's (LDS reused), then
   // lane (r, c) of the first pair holds rows 4c..4c+3 of column r of each block
@@ -511,7 +551,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
           if (a.KS > 1)  // padded plane: every element of the tile is inside it
             split_store(a.partial + ((size_t)blockIdx.z * gridDim.y * ROWS + m) * (gridDim.x * 128) + n, v);
           else if (n < a.N && m < a.M)
-            a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v);
+            a.y[(size_t)m * a.N + n] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
         }
       }
   }
@@ -542,7 +582,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int m = mrow0 + row0 + RPP * j;
-      if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(v[j]);
+      if (n < a.N && m < a.M) a.y[(size_t)m * a.N + n] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v[j] * ys : v[j]);
     }
   }
   if (tid == 0) split_reset(ctr);
@@ -593,8 +633,10 @@ size_t gemm_lds(int MB, int group, int fmt) {
   // final reduction ([4][MB*NPW*4][64] fp32) reuses the front of it
   const size_t tiles =
       (size_t)2 * MB * 16 * 256 +
-      2 * (size_t)(fmt == kFmtMxfp4 ? sz_chunk_bytes<32, kFmtMxfp4>()
-                                    : group == 128 ? sz_chunk_bytes<128>() : sz_chunk_bytes<32>());
+      2 * (size_t)(fmt == kFmtMxfp4   ? sz_chunk_bytes<32, kFmtMxfp4>()
+                   : fmt == kFmtNvfp4 ? sz_chunk_bytes<16, kFmtNvfp4>()
+                   : group == 128     ? sz_chunk_bytes<128>()
+                                      : sz_chunk_bytes<32>());
   const size_t red = (size_t)4 * MB * kNPW * 4 * 64 * sizeof(float);
   return tiles > red ? tiles : red;
 }
@@ -620,6 +662,9 @@ hipError_t launch_t(int group, const GemmPlan& p, const GemmArgs& a, hipStream_t
   if constexpr (FMT == kFmtMxfp4) {
     if (a.Gtot % 8 == 0 && zp % 8 == 0) return launch_kg<MB, 32, true, FMT>(p, a, stream);
     return launch_kg<MB, 32, false, FMT>(p, a, stream);
+  } else if constexpr (FMT == kFmtNvfp4) {  // sixteen E4M3 scale bytes
+    if (a.Gtot % 16 == 0 && zp % 16 == 0) return launch_kg<MB, 16, true, FMT>(p, a, stream);
+    return launch_kg<MB, 16, false, FMT>(p, a, stream);
   } else {
     if (group == 128) {
       if (a.Gtot % 2 == 0 && sp % 4 == 0) return launch_kg<MB, 128, true, FMT>(p, a, stream);
@@ -653,15 +698,18 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int) {
 int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
   const GemmPlan p = plan_gemm(M, N, K);
   return snprintf(buf, len, "gemm_kernel<MB=%d, NPW=%d, G=%d%s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d", p.MB,
-                  kNPW, group, fmt == kFmtInt8 ? ", BITS=8" : fmt == kFmtMxfp4 ? ", MXFP4" : "", p.gx, p.gy, p.KS,
+                  kNPW, group,
+                  fmt == kFmtInt8 ? ", BITS=8" : fmt == kFmtMxfp4 ? ", MXFP4" : fmt == kFmtNvfp4 ? ", NVFP4" : "", p.gx,
+                  p.gy, p.KS,
                   kWaves * 64, gemm_lds(p.MB, group, fmt), p.KS);
 }
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
                        const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* tscale) {
   const GemmPlan p = plan_gemm(M, N, K);
   GemmArgs a;
+  a.tscale = tscale;
   a.KS = p.KS;
   a.kt_per_split = p.kt_per_split;
   a.partial = nullptr;
@@ -684,6 +732,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   a.NBLK = (int)((N + 15) / 16);
   if (fmt == kFmtInt8) return launch_f<kFmtInt8>(group, p, a, stream);
   if (fmt == kFmtMxfp4) return launch_f<kFmtMxfp4>(group, p, a, stream);
+  if (fmt == kFmtNvfp4) return launch_f<kFmtNvfp4>(group, p, a, stream);
   return launch_f<kFmtInt4>(group, p, a, stream);
 }
 

@@ -68,6 +68,7 @@ struct GemvArgs {
   uint16_t* y;
   float* partial;      // [KS][M][N] fp32 (KS > 1 only)
   unsigned* counters;  // [gridDim.y][gridDim.x] (KS > 1 only)
+  const float* tscale; // NVFP4: the per-tensor scale (device)
   int M, N, K, kt_per_split, KS, sz_vec;
 };
 
@@ -193,13 +194,17 @@ struct E8 {
   __device__ __forceinline__ float scale(int t) const { return e8m0_to_f32((v[t >> 2] >> (8 * (t & 3))) & 0xffu); }
 };
 
+// (scale bytes of NS = 16 blocks (MXFP4) or 32 blocks (NVFP4) per segment)
 template <int NS>
 __device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, int Gtot, uint32_t erow, int g0) {
-  static_assert(NS == 16, "segment of four tiles of four blocks");
+  static_assert(NS == 16 || NS == 32, "segment of four tiles of four or eight blocks");
   E8<NS> v;
   if (a.sz_vec) {
-    const u4 t = *reinterpret_cast<const u4*>(a.zp + erow + g0);
-    v.v[0] = t[0]; v.v[1] = t[1]; v.v[2] = t[2]; v.v[3] = t[3];
+#pragma unroll
+    for (int h = 0; h < NS / 16; ++h) {
+      const u4 t = *reinterpret_cast<const u4*>(a.zp + erow + g0 + 16 * h);
+      v.v[4 * h] = t[0]; v.v[4 * h + 1] = t[1]; v.v[4 * h + 2] = t[2]; v.v[4 * h + 3] = t[3];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < NS / 4; ++i) v.v[i] = 0;
@@ -240,10 +245,13 @@ __device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, 
 }
 
 // FMT: kFmtInt4 (codes, fp16 scales, zero-points), kFmtInt8 (2048-byte tiles,
-// fp16 scales), kFmtMxfp4 (E2M1 tiles, E8M0 scale bytes in a.zp, G = 32).
+// fp16 scales), kFmtMxfp4 (E2M1 tiles, E8M0 scale bytes in a.zp, G = 32),
+// kFmtNvfp4 (E2M1 tiles, E4M3 scale bytes in a.zp, G = 16: a block's sum of
+// exact products times its scale in fp32, the tensor scale on the output).
 template <int MT, int W, int KQ, int G, int FMT>
 __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8 : 1) void gemv_kernel(GemvArgs a) {
-  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32), "code format");
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16),
+                "code format");
   constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
   constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;     // groups per 128-column tile
@@ -301,10 +309,10 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    SZ<NS> sz;
-    E8<16> e8s;
-    if constexpr (FMT == kFmtMxfp4)
-      e8s = load_e8<16>(a, d.Gtot, srow, kt0 * GPT);
+    SZ<FMT == kFmtNvfp4 ? 4 : NS> sz;
+    E8<FMT == kFmtNvfp4 ? 32 : 16> e8s;
+    if constexpr (FMT == kFmtMxfp4 || FMT == kFmtNvfp4)
+      e8s = load_e8<FMT == kFmtNvfp4 ? 32 : 16>(a, d.Gtot, srow, kt0 * GPT);
     else
       sz = load_sz<NS, FMT == kFmtInt4>(a, d.Gtot, srow, zrow, kt0 * GPT);
 #pragma unroll
@@ -328,6 +336,16 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
         uint4 xv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 32 * j);
+        if constexpr (FMT == kFmtNvfp4) {
+          // step j: the lane's columns lie in block 2j + c / 2 of the tile,
+          // byte 2 (j % 2) + c / 2 of scale word 2t + j / 2
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t b8 = (e8s.v[2 * t + (j >> 1)] >> (16 * (j & 1) + 8 * (c >> 1))) & 0xffu;
+            acc[m] = fmaf(e4m3_to_f32(b8), dot_block_mx(buf[t][0][j], xv[j]), acc[m]);
+          }
+          continue;
+        }
 #pragma unroll
         for (int gi = 0; gi < GPT; ++gi) {
           const int j0 = gi * (4 / GPT);
@@ -348,6 +366,9 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
+
+  // NVFP4: the per-tensor scale multiplies each output (partial sums stay unscaled)
+  const float ys = FMT == kFmtNvfp4 ? *a.tscale : 1.0f;
 
   // ---- reduce: every lane's sums go to LDS as [W][MT][16 rows][4 lanes];
   // thread i = 64m + 4r + c adds the W waves' sums of lane (r, c) in wave
@@ -371,7 +392,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
       split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
     else if (nn < a.N && mm < a.M)
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
   }
   if (a.KS == 1) return;
 
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
         for (int j = 0; j < 4; ++j)
           if (k0 + j < a.KS) v += t[j];
       }
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
     }
   }
   if (tid == 0) split_reset(ctr);
@@ -776,6 +797,7 @@ hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
   if (fmt == kFmtMxfp4) return launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
+  if (fmt == kFmtNvfp4) return launch_k<MT, W, 16, kFmtNvfp4>(p, a, stream);
   if (fmt == kFmtInt8)
     return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
   if constexpr (MT == 1 && W == 16) {
@@ -788,10 +810,10 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
 
 int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
   const GemvPlan p = plan_gemv(M, N, K, fmt);
-  if (fmt == kFmtInt8 || fmt == kFmtMxfp4)
+  if (fmt == kFmtInt8 || fmt == kFmtMxfp4 || fmt == kFmtNvfp4)
     return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
-                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "MXFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
-                    p.KS);
+                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : fmt == kFmtMxfp4 ? "MXFP4" : "NVFP4", p.gx,
+                    p.gy, p.KS, p.W * 64, p.lds, p.KS);
   if (p.half)
     return snprintf(buf, len, "gemv_mfma_half_kernel<W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                     p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
@@ -809,9 +831,10 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int, int fmt) {
 
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
                        const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* tscale) {
   const GemvPlan p = plan_gemv(M, N, K, fmt);
   GemvArgs a;
+  a.tscale = tscale;
   a.x = x;
   a.qp = static_cast<const uint8_t*>(qpacked);
   a.s = s;
@@ -831,8 +854,8 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
               (fmt == kFmtInt8 || (reinterpret_cast<uintptr_t>(zpacked) & (uintptr_t)(ns / 2 > 8 ? 7 : ns / 2 - 1)) == 0))
                  ? 1
                  : 0;
-  if (fmt == kFmtMxfp4)  // 16 scale bytes per segment, one 16-byte load
-    a.sz_vec = (Gtot % 16 == 0 && KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
+  if (fmt == kFmtMxfp4 || fmt == kFmtNvfp4)  // 16 (32) scale bytes per segment, one (two) 16-byte loads
+    a.sz_vec = (Gtot % ns == 0 && KT % kKQ == 0 && p.kt_per_split % kKQ == 0 &&
                 (reinterpret_cast<uintptr_t>(zpacked) & 15) == 0)
                    ? 1
                    : 0;

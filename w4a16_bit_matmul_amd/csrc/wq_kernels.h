@@ -61,6 +61,14 @@ hipError_t launch_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint8
 hipError_t launch_dequant_mxfp4(const uint8_t* qpacked, const uint8_t* e8, int64_t N, int64_t K, int out_dtype,
                                 void* out, hipStream_t stream);
 
+// NVFP4: the per-tensor fp32 scale (device, written by the quantizer), E2M1
+// codes [N][K] (or NULL), E4M3 scale bytes [N][K/16], 1 KB tiles in the MXFP4
+// layout (or NULL).  K a multiple of 32.
+hipError_t launch_quantize_nvfp4(const void* W, int dtype, int64_t N, int64_t K, float* tensor_scale, uint8_t* q_codes,
+                                 uint8_t* s8, uint8_t* qpacked, hipStream_t stream);
+hipError_t launch_dequant_nvfp4(const uint8_t* qpacked, const uint8_t* s8, const float* tensor_scale, int64_t N,
+                                int64_t K, int out_dtype, void* out, hipStream_t stream);
+
 // INT4 KV cache in blocks of 128: token t's hd values (X [T][hd]) into cache
 // row slot[t] (slot NULL: row t; rows outside [0, S) skipped), and back.
 hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, const int32_t* slot, int64_t S,
@@ -76,16 +84,19 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int fmt)
 // problem (snprintf semantics).  fmt (wq_device.h): kFmtInt4 (tile codes +
 // zero-points), kFmtInt8 (2048-byte int8 tiles; zpacked unused) or kFmtMxfp4
 // (E2M1 tiles; zpacked holds the E8M0 scale bytes, s unused, group 32).
+// kFmtNvfp4: zpacked holds the E4M3 scale bytes, tscale the per-tensor fp32
+// scale (device), group 16.
 int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len);
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
                        const void* qpacked, const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* tscale = nullptr);
 
 // MFMA tile GEMM.  Workspace layout and size come from gemm_workspace_bytes.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 int describe_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x, const void* qpacked,
-                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream);
+                       const uint16_t* s, const uint8_t* zpacked, uint16_t* y, void* workspace, hipStream_t stream,
+                       const float* tscale = nullptr);
 
 // Streaming-read probe: count launches back to back, launch i reading the
 // window_bytes at src + (i mod (span_bytes / window_bytes)) * window_bytes once,

@@ -33,6 +33,8 @@
 // the packed tile hold (columns 32*j + 8*c + e), so each wave writes whole
 // 1024-byte tiles with one 16-byte store per lane, and a group's min/max is a
 // reduction over the four lanes r, r+16, r+32, r+48 (two xor-shuffles).
+#include <algorithm>
+
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -699,6 +701,182 @@ __global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint8_t* __res
   }
 }
 
+// ---- NVFP4 --------------------------------------------------------------------
+// E2M1 codes (the MXFP4 tile layout), one E4M3 scale byte per block of 16
+// along K, one fp32 scale per tensor.  The tensor scale comes from the largest
+// |w| of the whole tensor: a zero fill, a reduction (one atomic max of the
+// value's bits per wave: non-negative fp32 values order as their bits), then
+// one thread turns that maximum into S in place; the quantizer reads S.
+// Every choice of an E4M3 or E2M1 value is the nearest value of the exact
+// quotient, decided by exact comparisons with the midpoints between
+// neighbouring values in fp64 (both factors have few significant bits, so
+// each product is exact), ties to the even code, saturating.
+
+__global__ void nvfp4_zero_kernel(float* tensor_scale) { *tensor_scale = 0.0f; }
+
+template <int DT>
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const void* __restrict__ W, int64_t n8,
+                                                         float* __restrict__ tensor_scale) {
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float w[8];
+    load8<DT>(W, i * 8, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(w[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0)
+    atomicMax(reinterpret_cast<unsigned*>(tensor_scale), __builtin_bit_cast(unsigned, m));
+}
+
+// S = fp32(fp64(amax / (6 * 448))), 1 for an all-zero tensor.
+__global__ void nvfp4_tensor_scale_kernel(float* tensor_scale) {
+  const float amax = *tensor_scale;
+  *tensor_scale = amax > 0.0f ? (float)((double)amax / 2688.0) : 1.0f;
+}
+
+// E4M3 magnitude of code c = 0..126 (bias 7; exponent field 0 is m * 2^-9).
+__device__ __forceinline__ double e4m3_value(int c) {
+  const int e = c >> 3, f = c & 7;
+  return e == 0 ? (double)f * 0x1p-9 : (double)(8 + f) * __builtin_bit_cast(double, (uint64_t)(e - 10 + 1023) << 52);
+}
+// E2M1 magnitude of code m = 0..7.
+__device__ __forceinline__ double e2m1_value(int m) {
+  const int e = m >> 1, f = m & 1;
+  return e == 0 ? 0.5 * f : (double)(2 + f) * (double)(1 << e) * 0.25;
+}
+
+// The E4M3 code nearest to a / d (a, d >= 0; d > 0), ties to even, 126 (448)
+// past the last midpoint.
+__device__ __forceinline__ int e4m3_nearest(double a, double d) {
+  int c = 0;
+  for (int k = 0; k < 126; ++k) {
+    const double rhs = 0.5 * (e4m3_value(k) + e4m3_value(k + 1)) * d;
+    if (a > rhs || (a == rhs && ((k + 1) & 1) == 0)) c = k + 1;
+    else break;
+  }
+  return c;
+}
+// The E2M1 magnitude code nearest to a / d, ties to even, 7 (6) past 5.
+__device__ __forceinline__ uint32_t e2m1_nearest(double a, double d) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    const double rhs = 0.5 * (e2m1_value(k) + e2m1_value(k + 1)) * d;
+    if (a > rhs || (a == rhs && ((k + 1) & 1) == 0)) c = (uint32_t)(k + 1);
+    else break;
+  }
+  return c;
+}
+
+// One wavefront per (16-row block, 128-column tile), the MXFP4 decomposition:
+// lane (r, c) holds columns 32j + 8c .. +7 of row r, so the block of 16 at
+// columns 32j + 16h is shared by lanes c = 2h and 2h + 1 (lane index xor 16).
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_nvfp4_kernel(const void* __restrict__ W, int64_t N, int64_t K,
+                                                             int64_t NBLK, int64_t KT,
+                                                             const float* __restrict__ tensor_scale,
+                                                             uint8_t* __restrict__ q_codes, uint8_t* __restrict__ s8_out,
+                                                             uint8_t* __restrict__ qpacked) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;  // whole wave exits together
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  const bool row_ok = n < N;
+  const int64_t Gtot = K / 16;
+  const double S = (double)*tensor_scale;
+
+  float w[4][8];
+  bool jok[4];
+  load_lane_tile<DT>(W, n, row_ok, K, kt, c, w, jok);
+  uint32_t words[4], sb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(w[j][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    sb[j] = amax > 0.0f ? (uint32_t)e4m3_nearest((double)amax, 6.0 * S) : 0u;
+    const double d = e4m3_value((int)sb[j]) * S;
+    uint32_t word = 0;
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t mag = sb[j] == 0 ? 0u : e2m1_nearest(fabs((double)w[j][e]), d);
+      b[e] = jok[j] ? (mag | (w[j][e] < 0.0f ? 8u : 0u)) : 0u;
+      word |= b[e] << (4 * e);
+    }
+    words[j] = word;
+    if (q_codes && jok[j])
+      *reinterpret_cast<uint2*>(q_codes + n * K + kt * 128 + 32 * j + 8 * c) =
+          make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  }
+  if (qpacked)
+    *reinterpret_cast<u4*>(qpacked + tile_offset_bytes(nb, kt, KT) + 16 * lane) = u4{words[0], words[1], words[2], words[3]};
+  if (row_ok && (c & 1) == 0) {  // lanes c = 0 and 2 write the blocks 2j and 2j + 1 of each step j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t gi = kt * 8 + 2 * j + (c >> 1);
+      if (gi < Gtot) s8_out[n * Gtot + gi] = (uint8_t)sb[j];
+    }
+  }
+}
+
+// Tiles + E4M3 scale bytes + tensor scale -> What[N][K] =
+// fp32(E2M1(q) * E4M3(s8) * S): the first product is exact in fp32, the
+// multiplication by S rounds once.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_nvfp4_kernel(const uint8_t* __restrict__ qpacked,
+                                                            const uint8_t* __restrict__ s8_in,
+                                                            const float* __restrict__ tensor_scale, int64_t N, int64_t K,
+                                                            int64_t NBLK, int64_t KT, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= NBLK * KT) return;
+  const int64_t nb = item / KT, kt = item % KT;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t n = nb * 16 + r;
+  if (n >= N) return;
+  const int64_t Gtot = K / 16;
+  const float S = *tensor_scale;
+  const u4 v = *reinterpret_cast<const u4*>(qpacked + tile_offset_bytes(nb, kt, KT) + 16 * lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = kt * 128 + 32 * j + 8 * c;
+    if (k0 >= K) continue;
+    const float sc = (float)e4m3_value(s8_in[n * Gtot + k0 / 16] & 127);  // exact
+    // magnitudes first, the sign then set as a bit (a code of -0 gives -0)
+    float d[8];
+    uint32_t neg[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t cc = (v[j] >> (4 * e)) & 15u;
+      d[e] = (mx_magnitude(cc) * sc) * S;
+      neg[e] = cc >> 3;
+    }
+    if constexpr (OUT == 0) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(uint32_t, d[e]) | (neg[e] << 31);
+      uint4* o = reinterpret_cast<uint4*>(static_cast<float*>(out) + n * K + k0);
+      o[0] = make_uint4(b[0], b[1], b[2], b[3]);
+      o[1] = make_uint4(b[4], b[5], b[6], b[7]);
+    } else {
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t a = OUT == 2 ? f32_to_f16_bits(d[2 * i]) : f32_to_bf16_bits(d[2 * i]);
+        uint32_t b = OUT == 2 ? f32_to_f16_bits(d[2 * i + 1]) : f32_to_bf16_bits(d[2 * i + 1]);
+        p[i] = (a | (neg[2 * i] << 15)) | ((b | (neg[2 * i + 1] << 15)) << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + n * K + k0) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  }
+}
+
 // ---- INT4 KV cache in blocks of 128 ------------------------------------------
 // A 16-lane group owns a pair of blocks (2p, 2p + 1) of one token: lanes 0..7
 // block 2p, lanes 8..15 block 2p + 1, each lane 16 consecutive values (two
@@ -970,6 +1148,37 @@ hipError_t launch_quantize_mxfp4(const void* W, int dtype, int64_t N, int64_t K,
 hipError_t launch_pack_mxfp4(const uint8_t* q_codes, int64_t N, int64_t K, uint8_t* qpacked, hipStream_t stream) {
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   pack_mxfp4_kernel<<<dim3((unsigned)blocks_for(NBLK * KT)), dim3(256), 0, stream>>>(q_codes, N, K, NBLK, KT, qpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4(const void* W, int dtype, int64_t N, int64_t K, float* tensor_scale, uint8_t* q_codes,
+                                 uint8_t* s8, uint8_t* qpacked, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  const int64_t n8 = N * K / 8;
+  const unsigned rgrid = (unsigned)std::min<int64_t>((n8 + 255) / 256, 2048);
+  nvfp4_zero_kernel<<<1, 1, 0, stream>>>(tensor_scale);
+  if (dtype == 0) nvfp4_amax_kernel<0><<<rgrid, 256, 0, stream>>>(W, n8, tensor_scale);
+  else if (dtype == 1) nvfp4_amax_kernel<1><<<rgrid, 256, 0, stream>>>(W, n8, tensor_scale);
+  else nvfp4_amax_kernel<2><<<rgrid, 256, 0, stream>>>(W, n8, tensor_scale);
+  nvfp4_tensor_scale_kernel<<<1, 1, 0, stream>>>(tensor_scale);
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+  if (dtype == 0)
+    quantize_nvfp4_kernel<0><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, tensor_scale, q_codes, s8, qpacked);
+  else if (dtype == 1)
+    quantize_nvfp4_kernel<1><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, tensor_scale, q_codes, s8, qpacked);
+  else
+    quantize_nvfp4_kernel<2><<<grid, block, 0, stream>>>(W, N, K, NBLK, KT, tensor_scale, q_codes, s8, qpacked);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_nvfp4(const uint8_t* qpacked, const uint8_t* s8, const float* tensor_scale, int64_t N,
+                                int64_t K, int out_dtype, void* out, hipStream_t stream) {
+  const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  dim3 grid((unsigned)blocks_for(NBLK * KT)), block(256);
+  if (out_dtype == 0) dequant_nvfp4_kernel<0><<<grid, block, 0, stream>>>(qpacked, s8, tensor_scale, N, K, NBLK, KT, out);
+  else if (out_dtype == 1)
+    dequant_nvfp4_kernel<1><<<grid, block, 0, stream>>>(qpacked, s8, tensor_scale, N, K, NBLK, KT, out);
+  else dequant_nvfp4_kernel<2><<<grid, block, 0, stream>>>(qpacked, s8, tensor_scale, N, K, NBLK, KT, out);
   return hipGetLastError();
 }
 
