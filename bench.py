@@ -374,6 +374,47 @@ def bench_mxfp4(steps, warmup):
     return out
 
 
+def bench_nvfp4(steps, warmup):
+    """NVFP4 weights (E2M1, blocks of 16, E4M3 scales, fp32 tensor scale) on the
+    decode and M=128 workloads, timed like the MXFP4 leg, with the weight error
+    on the decode layer (relative Frobenius norm of W_hat - W)."""
+    import numpy as np
+    import torch
+    import w4a16_bit_matmul_amd as wq
+    import workloads
+    out = {}
+    for name in ("decode_gemv", "batched_gemm"):
+        wl = workloads.WORKLOADS[name]
+        Wd = torch.from_numpy(wl.weights().view(np.int16)).cuda().view(torch.bfloat16)
+        xd = torch.from_numpy(wl.activations().view(np.int16)).cuda().view(torch.float16)
+        qw = wq.wq_quantize_nvfp4(Wd)["qw"]
+        if name == "decode_gemv":
+            ref = Wd.float()
+            out["weight_relative_error_nvfp4_g16"] = round(float((wq.wq_dequant_nvfp4(qw) - ref).norm()) /
+                                                           float(ref.norm()), 5)
+        del Wd
+        nbytes = wl.N * wl.K // 2 + wl.N * wl.K // 16 + 4 + 2 * wl.M * wl.K + 2 * wl.M * wl.N
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        qws = [qw] + [wq.QuantizedWeightNV(qw.qpacked.clone(), qw.s8.clone(), qw.tensor_scale.clone(), qw.N, qw.K)
+                      for _ in range(copies - 1)]
+        y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
+        n = wq.wq_gemm_nvfp4_workspace_bytes(wl.M, wl.N, wl.K)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
+        nb = max(copies, 20)
+        t, proto = timed_protocol(lambda: [wq.wq_gemm_nvfp4(xd, qws[i % copies], y=y, workspace=ws)
+                                           for i in range(nb)], nb)
+        rec = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "kernel": wq.wq_gemm_nvfp4_plan(wl.M, wl.N, wl.K),
+               "us_per_launch_one_python_call_each": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
+               "gbs": round(nbytes / t / 1e9, 2), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+               "weight_copies_rotated": copies, **proto}
+        if wl.M >= 64:
+            tf = wl.flops() / t / 1e12
+            rec.update({"tflops": round(tf, 2), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)})
+        out[name] = rec
+        log(f"[bench] NVFP4 {name}: {t * 1e6:.2f} us per launch, {nbytes / t / 1e9:.1f} GB/s")
+    return out
+
+
 def bench_awq():
     """AWQ-style fold on the decode layer (8192 x 8192, g=128): salient channels
     = the 1 % with the largest mean |x| over 64 calibration rows (the library's
@@ -806,6 +847,7 @@ def main():
         line["kv_int4"] = bench_kv(args.steps, args.warmup)
         line["awq_fold"] = bench_awq()
         line["mxfp4"] = bench_mxfp4(args.steps, args.warmup)
+        line["nvfp4"] = bench_nvfp4(args.steps, args.warmup)
         line["read_ceiling"] = bench_read_ceiling(nbytes, max(200, args.steps), 2000)
         line["read_ceiling"]["gemv_frac_of_ceiling"] = round(line["read_ceiling"]["us_per_launch"] / (t_step * 1e6), 4)
     if not args.no_cpu_baseline:

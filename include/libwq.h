@@ -86,14 +86,20 @@ typedef enum {
 } wq_scheme;
 
 typedef enum {
-    WQ_PATH_AUTO = 0, /* M < WQ_AUTO_MFMA_MIN_M: GEMV kernel; otherwise MFMA GEMM kernel */
+    WQ_PATH_AUTO = 0, /* GEMV kernel for M < WQ_AUTO_MFMA_MIN_M, and for M <= WQ_AUTO_GEMV_MAX_M when
+                         N <= WQ_AUTO_GEMV_MAX_N; otherwise the MFMA GEMM kernel */
     WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; 4-bit codes take their dot products on
                          the matrix cores, int8 and MXFP4 codes on the vector units) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
 
-/* Smallest M for which WQ_PATH_AUTO runs the MFMA GEMM kernel. */
+/* WQ_PATH_AUTO: the GEMV kernel below WQ_AUTO_MFMA_MIN_M rows; up to
+ * WQ_AUTO_GEMV_MAX_M rows also when N is at most WQ_AUTO_GEMV_MAX_N (the MFMA
+ * GEMM's 128-column workgroups are then too few: at N = 1024, K = 8192,
+ * M = 8..16 the GEMV took 8.9-9.0 us against 11.6-11.8 us). */
 #define WQ_AUTO_MFMA_MIN_M 5
+#define WQ_AUTO_GEMV_MAX_M 16
+#define WQ_AUTO_GEMV_MAX_N 2048
 
 /* A product that splits K across workgroups uses a caller-provided workspace:
  * WQ_WORKSPACE_COUNTER_BYTES bytes of 32-bit counters (one per output tile),
@@ -205,8 +211,8 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path);
 
 /* y = x * What^T with What = s * (q - z) dequantized inside the kernel -- the
- * fused weight-only matmul of "Hardware, formats and the roofline".  M below
- * WQ_AUTO_MFMA_MIN_M runs the split-K GEMV kernel, larger M the MFMA tile
+ * fused weight-only matmul of "Hardware, formats and the roofline".  The
+ * WQ_PATH_AUTO rule (wq_path) picks the split-K GEMV kernel or the MFMA tile
  * GEMM kernel (which also splits K when its grid is small).
  *   x_f16     [M][K] fp16, 16-byte aligned, finite
  *   qpacked   tile-layout codes, 16-byte aligned; s_f16 [N][G]; zpacked [N][ceil(G/2)]
@@ -322,8 +328,7 @@ size_t wq_gemm_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
 
 /* y = x * What^T with What = s * q dequantized inside the kernel (the
  * weight-only product of "Hardware, formats and the roofline" with 8-bit
- * weights): M < WQ_AUTO_MFMA_MIN_M the split-K GEMV, else the MFMA tile
- * GEMM.  Arguments, workspace contract, alignment, determinism and errors as
+ * weights): the split-K GEMV or the MFMA tile GEMM by the WQ_PATH_AUTO rule.  Arguments, workspace contract, alignment, determinism and errors as
  * wq_gemm_w4a16,
  * without zero-points. */
 int wq_gemm_w8a16(int64_t M, int64_t N, int64_t K, int group,
@@ -376,7 +381,7 @@ int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int6
 size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV
- * (M < WQ_AUTO_MFMA_MIN_M) sums exact E2M1 values times x per block in fp32 and applies the block's
+ * (WQ_PATH_AUTO rule) sums exact E2M1 values times x per block in fp32 and applies the block's
  * power of two in fp32 (exact for every e8); the MFMA GEMM (larger M) takes fp16
  * operands fp16(E2M1 * 2^(e8 - 127)), exact while the block exponent lies in
  * [-23, 13] (outside, the operand rounds to fp16's range).  Arguments,

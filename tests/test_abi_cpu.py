@@ -163,6 +163,16 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert m and int(m.group(1)) == wq.WQ_AUTO_MFMA_MIN_M
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
+    for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N"):
+        m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
+        assert m and int(m.group(1)) == getattr(wq, name), name
+    # the binding's restatement of the rule agrees with the plans: small N keeps
+    # the GEMV up to WQ_AUTO_GEMV_MAX_M rows
+    for M in (1, 4, 5, 8, 16, 17, 32, 128):
+        for N in (256, 1024, 2048, 2064, 8192):
+            mfma = wq.wq_gemm_plan(M, N, 4096, 32).startswith("gemm_kernel")
+            assert mfma == wq.auto_uses_mfma(M, N), (M, N)
+    assert not wq.auto_uses_mfma(16, 1024) and wq.auto_uses_mfma(17, 1024) and wq.auto_uses_mfma(5, 8192)
     lo = wq.WQ_AUTO_MFMA_MIN_M
     assert wq.wq_gemm_plan(lo - 1, 8192, 8192, 128).startswith("gemv_mfma_kernel"), lo
     assert wq.wq_gemm_plan(lo, 8192, 8192, 128).startswith("gemm_kernel"), lo

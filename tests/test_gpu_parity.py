@@ -270,9 +270,9 @@ def test_grid_exact_weights_reduce_to_fp16_gemm(path):
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
     y_ref = oracle.gemm_f64(x, W)
-    compare_y(y, y_ref, floor_frac=floor_for(path, M))
+    compare_y(y, y_ref, floor_frac=floor_for(path, M, N))
     y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
-    compare_y(y, y_torch, floor_frac=floor_for(path, M))
+    compare_y(y, y_torch, floor_frac=floor_for(path, M, N))
 
 
 def test_split_k_workspace_is_reusable():
@@ -323,7 +323,7 @@ def test_mfma_split_k_workspace_is_reusable():
         ctr = wq.WQ_WORKSPACE_COUNTER_BYTES
         assert int(shared[:ctr].count_nonzero()) == 0 and int(fresh[:ctr].count_nonzero()) == 0
         q, s, z = oracle.quantize_groups(W, g, dtype=oracle.BF16)
-        compare_y(y_shared, oracle.gemm_f64(x, oracle.dequant(q, s, z, g)), floor_frac=floor_for(wq.WQ_PATH_MFMA, M))
+        compare_y(y_shared, oracle.gemm_f64(x, oracle.dequant(q, s, z, g)), floor_frac=floor_for(wq.WQ_PATH_MFMA, M, N))
 
 
 def test_repeated_calls_are_deterministic():

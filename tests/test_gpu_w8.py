@@ -185,9 +185,9 @@ def test_w8_grid_exact_weights_reduce_to_fp16_gemm(path):
     assert torch.equal(wh.cpu(), torch.from_numpy(W))
     y = wq.wq_gemm_w8a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    compare_y(y, oracle.gemm_f64(x, W), floor_frac=floor_for(path, M))
+    compare_y(y, oracle.gemm_f64(x, W), floor_frac=floor_for(path, M, N))
     y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
-    compare_y(y, y_torch, floor_frac=floor_for(path, M))
+    compare_y(y, y_torch, floor_frac=floor_for(path, M, N))
 
 
 @pytest.mark.parametrize("name", ["decode_gemv", "batched_gemm"])

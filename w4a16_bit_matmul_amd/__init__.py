@@ -22,7 +22,15 @@ WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_ASYM, WQ_SYM = 0, 1
-WQ_AUTO_MFMA_MIN_M = 5  # smallest M that WQ_PATH_AUTO runs on the MFMA GEMM kernel
+WQ_AUTO_MFMA_MIN_M = 5  # WQ_PATH_AUTO: the GEMV below this many rows,
+WQ_AUTO_GEMV_MAX_M = 16  # and up to this many rows when N is at most
+WQ_AUTO_GEMV_MAX_N = 2048  # this; otherwise the MFMA GEMM kernel
+
+
+def auto_uses_mfma(M: int, N: int) -> bool:
+    """Whether WQ_PATH_AUTO runs the MFMA GEMM kernel for M rows and N outputs
+    (the library's rule, restated)."""
+    return M >= WQ_AUTO_MFMA_MIN_M and not (M <= WQ_AUTO_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
 WQ_WORKSPACE_COUNTER_BYTES = 2048  # leading counter bytes of a split-K workspace (zero before first use)
 WQ_NOALLOC_SCRATCH_BYTES = WQ_WORKSPACE_COUNTER_BYTES + (16 << 20)  # per-GPU scratch of wq_gemm_w4a16_noalloc
 

@@ -13,8 +13,9 @@ static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K cou
 // Kernel family for a product: WQ_PATH_AUTO takes the MFMA tile GEMM from
 // WQ_AUTO_MFMA_MIN_M rows on (with split K it beats the GEMV from there on
 // MI355X, whose per-row VALU work grows with M), the GEMV below.
-static bool auto_mfma(int64_t M, int path) {
-  return path == WQ_PATH_MFMA || (path == WQ_PATH_AUTO && M >= WQ_AUTO_MFMA_MIN_M);
+static bool auto_mfma(int64_t M, int64_t N, int path) {
+  if (path != WQ_PATH_AUTO) return path == WQ_PATH_MFMA;
+  return M >= WQ_AUTO_MFMA_MIN_M && !(M <= WQ_AUTO_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
 }
 
 namespace {
@@ -135,7 +136,7 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
 size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path) {
   if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return 0;
-  const bool mfma = auto_mfma(M, path);
+  const bool mfma = auto_mfma(M, N, path);
   return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt4);
 }
 
@@ -146,7 +147,7 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, path);
+  const bool mfma = auto_mfma(M, N, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 4, buf, buf_len);
   else
@@ -170,7 +171,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
   int st = check_shape(N, K, fmt == wq::kFmtNvfp4 ? 32 : group);  // NVFP4: blocks of 16, K a multiple of 32
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
-  *mfma = auto_mfma(M, path);
+  *mfma = auto_mfma(M, N, path);
   const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, fmt);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
@@ -298,7 +299,7 @@ int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, cha
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, path);
+  const bool mfma = auto_mfma(M, N, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 8, buf, buf_len);
   else
@@ -429,7 +430,7 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  const bool mfma = auto_mfma(M, path);
+  const bool mfma = auto_mfma(M, N, path);
   if (mfma)
     wq::describe_gemm(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
   else
@@ -530,7 +531,7 @@ int wq_gemm_nvfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  if (auto_mfma(M, path))
+  if (auto_mfma(M, N, path))
     wq::describe_gemm(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);
   else
     wq::describe_gemv(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);

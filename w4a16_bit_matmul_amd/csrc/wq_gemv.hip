@@ -802,6 +802,10 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
     return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
   if constexpr (MT == 1 && W == 16) {
     if (p.half) return group == 128 ? launch_kh<W, 128>(p, a, stream) : launch_kh<W, 32>(p, a, stream);
+  } else {
+    // the eight-row grid (two workgroups per 16-row block) exists only for the
+    // one-row sixteen-wave kernel; any other kernel on it would read past N
+    if (p.half) return hipErrorInvalidValue;
   }
   return group == 128 ? launch_km<MT, W, 128>(p, a, stream) : launch_km<MT, W, 32>(p, a, stream);
 }
