@@ -86,20 +86,28 @@ typedef enum {
 } wq_scheme;
 
 typedef enum {
-    WQ_PATH_AUTO = 0, /* GEMV kernel for M < WQ_AUTO_MFMA_MIN_M, and for M <= WQ_AUTO_GEMV_MAX_M when
-                         N <= WQ_AUTO_GEMV_MAX_N; otherwise the MFMA GEMM kernel */
+    WQ_PATH_AUTO = 0, /* the GEMV or the MFMA GEMM kernel by the rule below */
     WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; 4-bit codes take their dot products on
                          the matrix cores, int8 and MXFP4 codes on the vector units) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
 
-/* WQ_PATH_AUTO: the GEMV kernel below WQ_AUTO_MFMA_MIN_M rows; up to
- * WQ_AUTO_GEMV_MAX_M rows also when N is at most WQ_AUTO_GEMV_MAX_N (the MFMA
- * GEMM's 128-column workgroups are then too few: at N = 1024, K = 8192,
- * M = 8..16 the GEMV took 8.9-9.0 us against 11.6-11.8 us). */
+/* WQ_PATH_AUTO.  int8, MXFP4 and NVFP4 codes (VALU GEMV): the GEMV kernel
+ * below WQ_AUTO_MFMA_MIN_M rows, and up to WQ_AUTO_GEMV_MAX_M rows when N is
+ * at most WQ_AUTO_GEMV_MAX_N (the MFMA GEMM's 128-column workgroups are then
+ * too few to fill the GPU); otherwise the MFMA GEMM.  4-bit integer codes
+ * (wq_gemm_w4a16, whose GEMV takes its dot products on the matrix cores): the
+ * GEMV up to WQ_AUTO_INT4_GEMV_MAX_M rows, and up to
+ * WQ_AUTO_INT4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N;
+ * otherwise the MFMA GEMM.  Measured with K = 8192, g = 32, one call per launch
+ * (us, GEMV / MFMA GEMM): M = 8 at N = 8192 12.2 / 16.8 and at N = 28672
+ * 35.5 / 38.5; M = 16 at N = 28672 53.4 / 38.9; M = 32 at N = 1024 8.9 /
+ * 13.3. */
 #define WQ_AUTO_MFMA_MIN_M 5
 #define WQ_AUTO_GEMV_MAX_M 16
 #define WQ_AUTO_GEMV_MAX_N 2048
+#define WQ_AUTO_INT4_GEMV_MAX_M 8
+#define WQ_AUTO_INT4_NARROW_GEMV_MAX_M 32
 
 /* A product that splits K across workgroups uses a caller-provided workspace:
  * WQ_WORKSPACE_COUNTER_BYTES bytes of 32-bit counters (one per output tile),

@@ -145,7 +145,15 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert d.startswith("gemv_mfma_half_kernel<W=16, KQ=4, G=32>") and "grid=(128,1,1)" in d, d
     d = wq.wq_gemm_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128>") and "grid=(224,1,1)" in d, d
-    assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=8")
+    # 4-bit GEMV past eight rows: a sixteen-row activation tile when that
+    # still leaves 128 workgroups before a K split, two eight-row tiles below
+    assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16")
+    assert wq.wq_gemm_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16")
+    d = wq.wq_gemm_plan(16, 1024, 8192, 32)
+    assert d.startswith("gemv_mfma_kernel<MT=8") and "grid=(64,2," in d, d
+    d = wq.wq_gemm_plan(32, 1024, 8192, 32)
+    assert d.startswith("gemv_mfma_kernel<MT=16") and "grid=(64,2," in d, d
+    assert wq.wq_gemm_w8a16_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     # a small grid splits K across workgroups in whole eight-tile chunks
     d = wq.wq_gemm_plan(128, 8192, 8192, 128)
@@ -163,19 +171,29 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert m and int(m.group(1)) == wq.WQ_AUTO_MFMA_MIN_M
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
-    for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N"):
+    for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M",
+                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M"):
         m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
         assert m and int(m.group(1)) == getattr(wq, name), name
-    # the binding's restatement of the rule agrees with the plans: small N keeps
-    # the GEMV up to WQ_AUTO_GEMV_MAX_M rows
-    for M in (1, 4, 5, 8, 16, 17, 32, 128):
-        for N in (256, 1024, 2048, 2064, 8192):
-            mfma = wq.wq_gemm_plan(M, N, 4096, 32).startswith("gemm_kernel")
-            assert mfma == wq.auto_uses_mfma(M, N), (M, N)
-    assert not wq.auto_uses_mfma(16, 1024) and wq.auto_uses_mfma(17, 1024) and wq.auto_uses_mfma(5, 8192)
+    # the binding's restatement of the rule agrees with the plans of every
+    # code format: small N keeps the GEMV for more rows
+    plans = {"int4": lambda M, N: wq.wq_gemm_plan(M, N, 4096, 32),
+             "int8": lambda M, N: wq.wq_gemm_w8a16_plan(M, N, 4096, 32),
+             "mxfp4": lambda M, N: wq.wq_gemm_mxfp4_plan(M, N, 4096),
+             "nvfp4": lambda M, N: wq.wq_gemm_nvfp4_plan(M, N, 4096)}
+    for fmt, plan in plans.items():
+        for M in (1, 4, 5, 8, 9, 16, 17, 32, 33, 128):
+            for N in (256, 1024, 2048, 2064, 8192):
+                mfma = plan(M, N).startswith("gemm_kernel")
+                assert mfma == wq.auto_uses_mfma(M, N, fmt), (fmt, M, N)
+    assert not wq.auto_uses_mfma(16, 1024, "int8") and wq.auto_uses_mfma(17, 1024, "mxfp4")
+    assert wq.auto_uses_mfma(5, 8192, "nvfp4") and not wq.auto_uses_mfma(4, 8192, "int8")
+    assert not wq.auto_uses_mfma(8, 8192) and wq.auto_uses_mfma(9, 8192)
+    assert not wq.auto_uses_mfma(32, 2048) and wq.auto_uses_mfma(33, 1024) and wq.auto_uses_mfma(9, 2064)
     lo = wq.WQ_AUTO_MFMA_MIN_M
-    assert wq.wq_gemm_plan(lo - 1, 8192, 8192, 128).startswith("gemv_mfma_kernel"), lo
-    assert wq.wq_gemm_plan(lo, 8192, 8192, 128).startswith("gemm_kernel"), lo
+    hi = wq.WQ_AUTO_INT4_GEMV_MAX_M
+    assert wq.wq_gemm_plan(hi, 8192, 8192, 128).startswith("gemv_mfma_kernel"), hi
+    assert wq.wq_gemm_plan(hi + 1, 8192, 8192, 128).startswith("gemm_kernel"), hi
     assert wq.wq_gemm_w8a16_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel")
     assert wq.wq_gemm_w8a16_plan(lo, 8192, 8192, 128).startswith("gemm_kernel")
     assert wq.wq_gemm_mxfp4_plan(lo - 1, 8192, 8192).startswith("gemv_kernel")

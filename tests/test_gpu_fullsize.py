@@ -46,7 +46,7 @@ def test_workload_full_size(name):
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws)
     torch.cuda.synchronize()
-    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
+    floor = FLOOR_MFMA if wq.auto_uses_mfma(wl.M, wl.N) else FLOOR_GEMV
     ref = oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
     nw, ew = compare_y(y, ref, floor_frac=floor)
     say(f"  all {wl.M}x{wl.N} outputs: normwise {nw:.2e} elementwise {ew:.2e}")
@@ -60,7 +60,7 @@ def test_workload_full_size(name):
 def test_mlp_up_forced_gemv_full_size():
     """The M=16 up-projection (N=28672, K=8192, g=128) on the split-K GEMV
     kernel that the workload description names (the default kernel choice runs
-    the MFMA kernel from M=5): every output against the oracle."""
+    the MFMA kernel at this shape): every output against the oracle."""
     wl = workloads.WORKLOADS["mlp_up_decode"]
     say(f"full-size forced GEMV {wl.name}: M={wl.M} N={wl.N} K={wl.K} g={wl.group}")
     q, s, z, out = _quantized(wl)

@@ -113,7 +113,7 @@ def test_matmul_mxfp4_within_tolerance(M, N, K, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant_mxfp4(q, e8))
     y = wq.wq_gemm_mxfp4(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant_mxfp4(q, e8, oracle.F16)), path, M)
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant_mxfp4(q, e8, oracle.F16)), path, M, fmt="mxfp4")
     say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
@@ -154,7 +154,7 @@ def test_mxfp4_workload_full_size(name):
     y = wq.wq_gemm_mxfp4(to_dev_f16(x), out["qw"], workspace=ws)
     torch.cuda.synchronize()
     # every output against the oracle's product over all rows of weights
-    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
+    floor = FLOOR_MFMA if wq.auto_uses_mfma(wl.M, wl.N, "mxfp4") else FLOOR_GEMV
     ref = oracle.gemm_rows_mxfp4_f64(x, q, e8, 0, wl.N)
     nw, ew = compare_y(y, ref, floor_frac=floor)
     say(f"  all {wl.M}x{wl.N} outputs: normwise {nw:.2e} elementwise {ew:.2e}")

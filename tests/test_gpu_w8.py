@@ -143,7 +143,7 @@ def test_matmul_w8_within_tolerance(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant_w8(q, s, group))
     y = wq.wq_gemm_w8a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant_w8(q, s, group, oracle.F16)), path, M)
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant_w8(q, s, group, oracle.F16)), path, M, fmt="int8")
     say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
@@ -185,9 +185,9 @@ def test_w8_grid_exact_weights_reduce_to_fp16_gemm(path):
     assert torch.equal(wh.cpu(), torch.from_numpy(W))
     y = wq.wq_gemm_w8a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    compare_y(y, oracle.gemm_f64(x, W), floor_frac=floor_for(path, M, N))
+    compare_y(y, oracle.gemm_f64(x, W), floor_frac=floor_for(path, M, N, "int8"))
     y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
-    compare_y(y, y_torch, floor_frac=floor_for(path, M, N))
+    compare_y(y, y_torch, floor_frac=floor_for(path, M, N, "int8"))
 
 
 @pytest.mark.parametrize("name", ["decode_gemv", "batched_gemm"])
@@ -208,7 +208,7 @@ def test_w8_workload_full_size(name):
     y = wq.wq_gemm_w8a16(to_dev_f16(x), out["qw"], workspace=ws)
     torch.cuda.synchronize()
     # every output against the oracle's product over all rows of weights
-    floor = FLOOR_MFMA if wl.M >= wq.WQ_AUTO_MFMA_MIN_M else FLOOR_GEMV
+    floor = FLOOR_MFMA if wq.auto_uses_mfma(wl.M, wl.N, "int8") else FLOOR_GEMV
     ref = oracle.gemm_rows_w8_f64(x, q, s, wl.group, 0, wl.N)
     nw, ew = compare_y(y, ref, floor_frac=floor)
     say(f"  all {wl.M}x{wl.N} outputs: normwise {nw:.2e} elementwise {ew:.2e}")

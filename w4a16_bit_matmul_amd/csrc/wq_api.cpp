@@ -10,11 +10,17 @@
 
 static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K counter region size");
 
-// Kernel family for a product: WQ_PATH_AUTO takes the MFMA tile GEMM from
-// WQ_AUTO_MFMA_MIN_M rows on (with split K it beats the GEMV from there on
-// MI355X, whose per-row VALU work grows with M), the GEMV below.
-static bool auto_mfma(int64_t M, int64_t N, int path) {
+// Kernel family for a product of code format fmt (wq_device.h): the
+// WQ_PATH_AUTO rule of libwq.h.  The VALU GEMV (int8, MXFP4 and NVFP4 codes)
+// does per-row work that grows with M, so the MFMA tile GEMM takes over from
+// WQ_AUTO_MFMA_MIN_M rows; the 4-bit GEMV takes its dot products on the matrix
+// cores at a cost nearly flat in M up to its 8- or 16-row activation tile and
+// keeps more rows.  Narrow outputs give the GEMM's 128-column workgroups too
+// few to fill the chip, so the GEMV keeps more rows there.
+static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
   if (path != WQ_PATH_AUTO) return path == WQ_PATH_MFMA;
+  if (fmt == wq::kFmtInt4)
+    return M > WQ_AUTO_INT4_GEMV_MAX_M && !(M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
   return M >= WQ_AUTO_MFMA_MIN_M && !(M <= WQ_AUTO_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
 }
 
@@ -136,7 +142,7 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
 size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path) {
   if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return 0;
-  const bool mfma = auto_mfma(M, N, path);
+  const bool mfma = auto_mfma(M, N, wq::kFmtInt4, path);
   return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt4);
 }
 
@@ -147,7 +153,7 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, path);
+  const bool mfma = auto_mfma(M, N, wq::kFmtInt4, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 4, buf, buf_len);
   else
@@ -171,7 +177,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
   int st = check_shape(N, K, fmt == wq::kFmtNvfp4 ? 32 : group);  // NVFP4: blocks of 16, K a multiple of 32
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
-  *mfma = auto_mfma(M, N, path);
+  *mfma = auto_mfma(M, N, fmt, path);
   const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, fmt);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
@@ -299,7 +305,7 @@ int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, cha
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, path);
+  const bool mfma = auto_mfma(M, N, wq::kFmtInt8, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 8, buf, buf_len);
   else
@@ -430,7 +436,7 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, path);
+  const bool mfma = auto_mfma(M, N, wq::kFmtMxfp4, path);
   if (mfma)
     wq::describe_gemm(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
   else
@@ -531,7 +537,7 @@ int wq_gemm_nvfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  if (auto_mfma(M, N, path))
+  if (auto_mfma(M, N, wq::kFmtNvfp4, path))
     wq::describe_gemm(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);
   else
     wq::describe_gemv(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);

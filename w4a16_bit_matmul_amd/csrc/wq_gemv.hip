@@ -730,7 +730,14 @@ struct GemvPlan {
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   GemvPlan p;
-  p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  // 4-bit codes past eight rows: a sixteen-row activation tile reads the
+  // weights once for sixteen rows (M = 16, N = 28672, K = 8192: 52.6 against
+  // 75.9 us with two eight-row tiles), unless that leaves fewer than 128
+  // workgroups before K is split (N = 1024, M = 16: 7.90 against 6.93 us;
+  // M = 32: 9.05 against 11.0 us)
+  const int64_t nblk = (N + 15) / 16;
+  p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4
+         : (M <= 8 || fmt != kFmtInt4 || nblk * ((M + 15) / 16) < 128) ? 8 : 16;
   // one row of 4-bit or MXFP4 codes: sixteen waves, two workgroups per CU at
   // 64 VGPRs.  Kernels that need more registers (two to eight rows, and int8
   // codes with twice the bytes in flight per lane) measured 4-20 % faster with
@@ -760,7 +767,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
-  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * 64 * 4;
+  // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
+  // [W][MT][16] (matrix-core kernels)
+  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * (fmt == kFmtInt4 ? 16 : 64) * 4;
   return p;
 }
 
@@ -872,7 +881,8 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   if (p.MT == 1) return p.W == 16 ? launch_t<1, 16>(p, group, fmt, a, stream) : launch_t<1, 8>(p, group, fmt, a, stream);
   if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
   if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
-  return launch_t<8, 8>(p, group, fmt, a, stream);
+  if (p.MT == 8) return launch_t<8, 8>(p, group, fmt, a, stream);
+  return group == 128 ? launch_km<16, 8, 128>(p, a, stream) : launch_km<16, 8, 32>(p, a, stream);
 }
 
 }  // namespace wq
