@@ -545,7 +545,8 @@ def bench_configs():
     by wq_gemm_w4a16_seq calls (arguments marshalled beforehand, so the host
     never gaps the GPU), weights rotated over >= 1 GB of copies (at most 128);
     effective GB/s and TFLOP/s, the inputs' SHA-256 and the clock.  The M=16
-    up-projection is also timed on the split-K GEMV kernel (forced)."""
+    up-projection, which WQ_PATH_AUTO runs on the split-K GEMV, is also timed
+    on the MFMA GEMM kernel (forced)."""
     import numpy as np
     import torch
     import w4a16_bit_matmul_amd as wq
@@ -577,12 +578,12 @@ def bench_configs():
         n = max(copies, 50)
         paths = [("auto", wq.WQ_PATH_AUTO)]
         if name == "mlp_up_decode":
-            paths.append(("forced_gemv", wq.WQ_PATH_GEMV))
+            paths.append(("forced_mfma", wq.WQ_PATH_MFMA))
         for tag, path in paths:
             if path == wq.WQ_PATH_AUTO:
                 run_seq = wq.wq_gemm_w4a16_seq_prepared([xd] * n, [qws[i % copies] for i in range(n)], [y] * n,
                                                         workspace=ws)
-            else:  # one Python call per launch: the GEMV path has no sequence entry point
+            else:  # one Python call per launch: a forced path has no sequence entry point
                 wsg = torch.zeros(max(1, wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group, path)),
                                   dtype=torch.uint8, device="cuda")
                 run_seq = lambda: [wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=wsg, path=path)

@@ -97,17 +97,22 @@ typedef enum {
  * at most WQ_AUTO_GEMV_MAX_N (the MFMA GEMM's 128-column workgroups are then
  * too few to fill the GPU); otherwise the MFMA GEMM.  4-bit integer codes
  * (wq_gemm_w4a16, whose GEMV takes its dot products on the matrix cores): the
- * GEMV up to WQ_AUTO_INT4_GEMV_MAX_M rows, and up to
- * WQ_AUTO_INT4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N;
- * otherwise the MFMA GEMM.  Measured with K = 8192, g = 32, one call per launch
- * (us, GEMV / MFMA GEMM): M = 8 at N = 8192 12.2 / 16.8 and at N = 28672
- * 35.5 / 38.5; M = 16 at N = 28672 53.4 / 38.9; M = 32 at N = 1024 8.9 /
- * 13.3. */
+ * GEMV up to WQ_AUTO_INT4_GEMV_MAX_M rows; up to WQ_AUTO_INT4_NARROW_GEMV_MAX_M
+ * rows when N is at most WQ_AUTO_GEMV_MAX_N; up to
+ * WQ_AUTO_INT4_WIDE_GEMV_MAX_M rows when N exceeds WQ_AUTO_INT4_WIDE_N (each
+ * GEMV workgroup then shares its activation slices among four 16-row
+ * blocks); otherwise the MFMA GEMM.  Measured with K = 8192, one call per
+ * launch (us, GEMV / MFMA GEMM): M = 8, g = 32: N = 8192 12.2 / 16.8, N =
+ * 28672 32.5 / 38.5; M = 16, N = 28672: g = 128 32.9 / 35.5, g = 32 37.5 /
+ * 38.8; M = 16, N = 8192, K = 28672, g = 32: 47.9 / 37.1; M = 32, N = 1024,
+ * g = 32: 8.9 / 13.3. */
 #define WQ_AUTO_MFMA_MIN_M 5
 #define WQ_AUTO_GEMV_MAX_M 16
 #define WQ_AUTO_GEMV_MAX_N 2048
 #define WQ_AUTO_INT4_GEMV_MAX_M 8
 #define WQ_AUTO_INT4_NARROW_GEMV_MAX_M 32
+#define WQ_AUTO_INT4_WIDE_GEMV_MAX_M 16
+#define WQ_AUTO_INT4_WIDE_N 16384
 
 /* A product that splits K across workgroups uses a caller-provided workspace:
  * WQ_WORKSPACE_COUNTER_BYTES bytes of 32-bit counters (one per output tile),

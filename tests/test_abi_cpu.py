@@ -148,7 +148,10 @@ def test_gemm_plan_names_the_dispatched_kernel():
     # 4-bit GEMV past eight rows: a sixteen-row activation tile when that
     # still leaves 128 workgroups before a K split, two eight-row tiles below
     assert wq.wq_gemm_plan(128, 256, 1024, 32, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16")
-    assert wq.wq_gemm_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16")
+    d = wq.wq_gemm_plan(16, 28672, 8192, 128)
+    assert d.startswith("gemv_mfma_kernel<MT=16, W=4, KQ=4, G=128, RB=4>") and "grid=(448,1,1)" in d, d
+    d = wq.wq_gemm_plan(8, 28672, 8192, 32)
+    assert d.startswith("gemv_mfma_kernel<MT=8, W=8, KQ=4, G=32, RB=2>") and "grid=(896,1,1)" in d, d
     d = wq.wq_gemm_plan(16, 1024, 8192, 32)
     assert d.startswith("gemv_mfma_kernel<MT=8") and "grid=(64,2," in d, d
     d = wq.wq_gemm_plan(32, 1024, 8192, 32)
@@ -172,7 +175,7 @@ def test_gemm_plan_names_the_dispatched_kernel():
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
     for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M",
-                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M"):
+                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N"):
         m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
         assert m and int(m.group(1)) == getattr(wq, name), name
     # the binding's restatement of the rule agrees with the plans of every
@@ -183,13 +186,14 @@ def test_gemm_plan_names_the_dispatched_kernel():
              "nvfp4": lambda M, N: wq.wq_gemm_nvfp4_plan(M, N, 4096)}
     for fmt, plan in plans.items():
         for M in (1, 4, 5, 8, 9, 16, 17, 32, 33, 128):
-            for N in (256, 1024, 2048, 2064, 8192):
+            for N in (256, 1024, 2048, 2064, 8192, 16384, 16400, 28672):
                 mfma = plan(M, N).startswith("gemm_kernel")
                 assert mfma == wq.auto_uses_mfma(M, N, fmt), (fmt, M, N)
     assert not wq.auto_uses_mfma(16, 1024, "int8") and wq.auto_uses_mfma(17, 1024, "mxfp4")
     assert wq.auto_uses_mfma(5, 8192, "nvfp4") and not wq.auto_uses_mfma(4, 8192, "int8")
     assert not wq.auto_uses_mfma(8, 8192) and wq.auto_uses_mfma(9, 8192)
     assert not wq.auto_uses_mfma(32, 2048) and wq.auto_uses_mfma(33, 1024) and wq.auto_uses_mfma(9, 2064)
+    assert not wq.auto_uses_mfma(16, 28672) and wq.auto_uses_mfma(17, 28672) and wq.auto_uses_mfma(16, 16384)
     lo = wq.WQ_AUTO_MFMA_MIN_M
     hi = wq.WQ_AUTO_INT4_GEMV_MAX_M
     assert wq.wq_gemm_plan(hi, 8192, 8192, 128).startswith("gemv_mfma_kernel"), hi

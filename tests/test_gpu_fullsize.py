@@ -57,19 +57,19 @@ def test_workload_full_size(name):
         assert torch.equal(y, y2)
 
 
-def test_mlp_up_forced_gemv_full_size():
-    """The M=16 up-projection (N=28672, K=8192, g=128) on the split-K GEMV
-    kernel that the workload description names (the default kernel choice runs
-    the MFMA kernel at this shape): every output against the oracle."""
+def test_mlp_up_forced_mfma_full_size():
+    """The M=16 up-projection (N=28672, K=8192, g=128) on the MFMA GEMM kernel
+    (the default kernel choice runs the split-K GEMV there): every output
+    against the oracle."""
     wl = workloads.WORKLOADS["mlp_up_decode"]
-    say(f"full-size forced GEMV {wl.name}: M={wl.M} N={wl.N} K={wl.K} g={wl.group}")
+    say(f"full-size forced MFMA {wl.name}: M={wl.M} N={wl.N} K={wl.K} g={wl.group}")
     q, s, z, out = _quantized(wl)
     x = wl.activations()
-    ws_bytes = wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group, path=wq.WQ_PATH_GEMV)
+    ws_bytes = wq.wq_gemm_workspace_bytes(wl.M, wl.N, wl.K, wl.group, path=wq.WQ_PATH_MFMA)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
-    say(f"  {wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group, wq.WQ_PATH_GEMV)}")
-    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws, path=wq.WQ_PATH_GEMV)
+    say(f"  {wq.wq_gemm_plan(wl.M, wl.N, wl.K, wl.group, wq.WQ_PATH_MFMA)}")
+    y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws, path=wq.WQ_PATH_MFMA)
     torch.cuda.synchronize()
     ref = oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
-    nw, ew = compare_y(y, ref, floor_frac=FLOOR_GEMV)
+    nw, ew = compare_y(y, ref, floor_frac=FLOOR_MFMA)
     say(f"  all {wl.M}x{wl.N} outputs: normwise {nw:.2e} elementwise {ew:.2e}")

@@ -183,6 +183,15 @@ MATMUL_CASES = [  # M, N, K, group
     (2, 1000, 8192, 128),
     (5, 100, 8192, 32),
     (12, 40, 8192, 32),
+    # 4-bit GEMV with several 16-row blocks per workgroup (eight or sixteen
+    # rows of x): N = 16400 has 1025 row blocks and N = 8200 513, so the last
+    # workgroup's later blocks lie past N; M = 30 takes two sixteen-row tiles;
+    # N = 8176 (511 blocks), K = 4224 runs one block per workgroup over a
+    # ragged K
+    (6, 16400, 512, 32),
+    (13, 8200, 1024, 128),
+    (30, 16400, 512, 32),
+    (12, 8176, 4224, 32),
 ]
 
 

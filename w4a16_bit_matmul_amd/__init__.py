@@ -26,7 +26,9 @@ WQ_AUTO_MFMA_MIN_M = 5  # WQ_PATH_AUTO, int8 / MXFP4 / NVFP4 codes: the GEMV bel
 WQ_AUTO_GEMV_MAX_M = 16  # and up to this many rows when N is at most
 WQ_AUTO_GEMV_MAX_N = 2048  # this; otherwise the MFMA GEMM kernel
 WQ_AUTO_INT4_GEMV_MAX_M = 8  # 4-bit integer codes: the GEMV up to this many rows,
-WQ_AUTO_INT4_NARROW_GEMV_MAX_M = 32  # and up to this many when N <= WQ_AUTO_GEMV_MAX_N
+WQ_AUTO_INT4_NARROW_GEMV_MAX_M = 32  # up to this many when N <= WQ_AUTO_GEMV_MAX_N,
+WQ_AUTO_INT4_WIDE_GEMV_MAX_M = 16  # and up to this many when N exceeds
+WQ_AUTO_INT4_WIDE_N = 16384  # this
 
 
 def auto_uses_mfma(M: int, N: int, fmt: str = "int4") -> bool:
@@ -34,7 +36,8 @@ def auto_uses_mfma(M: int, N: int, fmt: str = "int4") -> bool:
     of code format fmt ("int4", "int8", "mxfp4" or "nvfp4"): the library's
     rule, restated."""
     if fmt == "int4":
-        return M > WQ_AUTO_INT4_GEMV_MAX_M and not (M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
+        return (M > WQ_AUTO_INT4_GEMV_MAX_M and not (M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
+                and not (M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M and N > WQ_AUTO_INT4_WIDE_N))
     if fmt not in ("int8", "mxfp4", "nvfp4"):
         raise ValueError(f"unknown code format {fmt!r}")
     return M >= WQ_AUTO_MFMA_MIN_M and not (M <= WQ_AUTO_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)

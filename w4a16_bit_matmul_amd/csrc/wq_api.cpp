@@ -16,11 +16,13 @@ static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K cou
 // WQ_AUTO_MFMA_MIN_M rows; the 4-bit GEMV takes its dot products on the matrix
 // cores at a cost nearly flat in M up to its 8- or 16-row activation tile and
 // keeps more rows.  Narrow outputs give the GEMM's 128-column workgroups too
-// few to fill the chip, so the GEMV keeps more rows there.
+// few to fill the chip, so the GEMV keeps more rows there; wide outputs let
+// each GEMV workgroup share its x slices among four row blocks.
 static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
   if (path != WQ_PATH_AUTO) return path == WQ_PATH_MFMA;
   if (fmt == wq::kFmtInt4)
-    return M > WQ_AUTO_INT4_GEMV_MAX_M && !(M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
+    return M > WQ_AUTO_INT4_GEMV_MAX_M && !(M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N) &&
+           !(M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M && N > WQ_AUTO_INT4_WIDE_N);
   return M >= WQ_AUTO_MFMA_MIN_M && !(M <= WQ_AUTO_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
 }
 

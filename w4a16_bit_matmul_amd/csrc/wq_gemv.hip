@@ -54,6 +54,8 @@
 // back to zero for the next call.
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -439,8 +441,11 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
 // per group applies the scale, so the arithmetic is the VALU GEMV's with the
 // sum order of the matrix core: 9 VALU instructions per code word instead of
 // 13.  Lane (r, c) receives D rows 4c..4c+3 (activation rows) of column r.
-template <int MT, int W, int KQ, int G>
-__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfma_kernel(GemvArgs a) {
+// RB > 1: the workgroup owns RB consecutive 16-row blocks, and each wave
+// applies its segment's x slice to the codes of all of them, so x is read
+// from L2 once per RB blocks.
+template <int MT, int W, int KQ, int G, int RB = 1>
+__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) void gemv_mfma_kernel(GemvArgs a) {
   constexpr int GPT = 128 / G;       // groups per 128-column tile
   constexpr int SPG = 4 / GPT;       // MFMA steps per group
   constexpr int NS = KQ * GPT;       // groups per segment
@@ -453,31 +458,45 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfm
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, c = lane >> 4;
-  const int nb = blockIdx.x, m0 = blockIdx.y * MT, ks = blockIdx.z;
+  const int nb0 = blockIdx.x * RB, m0 = blockIdx.y * MT, ks = blockIdx.z;
+  const int nblk = (a.N + 15) >> 4;
   const Dims d = dims_of<G>(a.K);
   const int kt_lo = ks * a.kt_per_split;
   const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
   uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
-  float* red = reinterpret_cast<float*>(smem + (size_t)W * MT * KQ * 256);  // [W][MT][16]
+  // the cross-wave sums [W][RB][MT][16]: after the x slices (RB = 1), or in
+  // their place once every wave is done with its slice
+  float* red = reinterpret_cast<float*>(smem + (RB == 1 ? (size_t)W * MT * KQ * 256 : 0));
 
-  const uint8_t* tbase = a.qp + (size_t)nb * d.KT * kTileBytes;
-  const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
-  const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
+  // per row block: its tiles (blocks past the last re-read it; their outputs
+  // are never stored) and this lane's row of scales and zero-points
+  const uint8_t* tbase[RB];
+  uint32_t srow[RB], zrow[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int nb = min(nb0 + b, nblk - 1);
+    tbase[b] = a.qp + (size_t)nb * d.KT * kTileBytes;
+    const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
+    srow[b] = n * (uint32_t)d.Gtot;
+    zrow[b] = n * (uint32_t)d.GB;
+  }
   const uint32_t lane16 = 16u * lane;
   const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
   // this lane's A row of the slice (rows past MT repeat the last one)
   const int arow = (r < MT ? r : MT - 1) * (KQ * 128) + 8 * c;
 
-  float acc[NA];
+  float acc[RB][NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = 0.0f;
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int i = 0; i < NA; ++i) acc[b][i] = 0.0f;
 
   for (int sg = wv; sg * KQ < nkt; sg += W) {
     const int q0 = sg * KQ;
     const int nq = min(KQ, nkt - q0);
     const int kt0 = kt_lo + q0;
 
-    u4 buf[KQ];
+    u4 buf[RB][KQ];
     uint4 xc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -485,11 +504,15 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfm
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    const SZ<NS> sz = load_sz<NS, true>(a, d.Gtot, srow, zrow, kt0 * GPT);
+    SZ<NS> sz[RB];
 #pragma unroll
-    for (int t = 0; t < KQ; ++t)
-      buf[t] = __builtin_nontemporal_load(
-          reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * kTileBytes + lane16));
+    for (int b = 0; b < RB; ++b) sz[b] = load_sz<NS, true>(a, d.Gtot, srow[b], zrow[b], kt0 * GPT);
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int t = 0; t < KQ; ++t)
+        buf[b][t] = __builtin_nontemporal_load(
+            reinterpret_cast<const u4*>(tbase[b] + (size_t)min(kt0 + t, d.KT - 1) * kTileBytes + lane16));
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
@@ -506,28 +529,31 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfm
       const uint16_t* xr = xw + arow + t * 128;
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        const uint32_t z = sz.zero(t * GPT + gi);
-        const h2 zq = as_h2(z * 0x00010001u + kMagicPair);     // (1024 + z) twice
-        const h2 z64 = as_h2(z * 0x00100010u + 0x54005400u);   // (64 + z) twice: z in mantissa bits 4..7
-        f4 T;
 #pragma unroll
-        for (int jj = 0; jj < SPG; ++jj) {
-          const int j = gi * SPG + jj;
-          const uint32_t w = buf[t][j], w8 = w >> 8;
-          const h2 p0 = as_h2((w & 0x000F000Fu) | m1024) - zq;
-          const h2 p1 = as_h2((w & 0x00F000F0u) | m64) - z64;
-          const h2 p2 = as_h2((w8 & 0x000F000Fu) | m1024) - zq;
-          const h2 p3 = as_h2((w8 & 0x00F000F0u) | m64) - z64;
-          h8 bfr;
-          bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
-          bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
-          const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
-          T = jj == 0 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
-                      : __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, T, 0, 0, 0);
+        for (int b = 0; b < RB; ++b) {
+          const uint32_t z = sz[b].zero(t * GPT + gi);
+          const h2 zq = as_h2(z * 0x00010001u + kMagicPair);     // (1024 + z) twice
+          const h2 z64 = as_h2(z * 0x00100010u + 0x54005400u);   // (64 + z) twice: z in mantissa bits 4..7
+          f4 T;
+#pragma unroll
+          for (int jj = 0; jj < SPG; ++jj) {
+            const int j = gi * SPG + jj;
+            const uint32_t w = buf[b][t][j], w8 = w >> 8;
+            const h2 p0 = as_h2((w & 0x000F000Fu) | m1024) - zq;
+            const h2 p1 = as_h2((w & 0x00F000F0u) | m64) - z64;
+            const h2 p2 = as_h2((w8 & 0x000F000Fu) | m1024) - zq;
+            const h2 p3 = as_h2((w8 & 0x00F000F0u) | m64) - z64;
+            h8 bfr;
+            bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+            bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+            const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+            T = jj == 0 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, T, 0, 0, 0);
+          }
+          const float sc = sz[b].scale(t * GPT + gi);
+#pragma unroll
+          for (int i = 0; i < NA; ++i) acc[b][i] = fmaf(sc, T[i], acc[b][i]);
         }
-        const float sc = sz.scale(t * GPT + gi);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) acc[i] = fmaf(sc, T[i], acc[i]);
       }
     }
     // the next segment overwrites this wave's slice: finish reading it first
@@ -535,23 +561,28 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfm
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- reduce: lane (r, c) holds rows 4c + i of column r; the W waves' sums
-  // of each (row, column) meet in LDS and are added in wave order
+  // ---- reduce: lane (r, c) holds rows 4c + i of column r of each block; the
+  // W waves' sums of each (block, row, column) meet in LDS and are added in
+  // wave order
+  constexpr int NOUT = MT * 16;   // outputs per row block
+  if constexpr (RB > 1) __syncthreads();  // every wave is done with its x slice
   if (4 * c < MT) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      if (4 * c + i < MT) red[(wv * MT + 4 * c + i) * 16 + r] = acc[i];
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        if (4 * c + i < MT) red[((wv * RB + b) * MT + 4 * c + i) * 16 + r] = acc[b][i];
   }
   __syncthreads();
-  constexpr int NOUT = MT * 16;
-  for (int i = tid; i < NOUT; i += NT) {
+  for (int i = tid; i < RB * NOUT; i += NT) {
+    const int b = i / NOUT, o = i % NOUT;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) v += red[w * NOUT + i];
-    const int rr = i & 15, m = i >> 4;
-    const int nn = nb * 16 + rr, mm = m0 + m;
-    if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
-      split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
+    for (int w = 0; w < W; ++w) v += red[(w * RB + b) * NOUT + o];
+    const int rr = o & 15, m = o >> 4;
+    const int nn = (nb0 + b) * 16 + rr, mm = m0 + m;
+    if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * RB * 16]: always in bounds
+      split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * RB * 16) + nn, v);
     else if (nn < a.N && mm < a.M)
       a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
   }
@@ -560,12 +591,13 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : 1) void gemv_mfm
   // ---- split-K: the last workgroup of this row range adds the partial sums
   unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
   if (!split_arrive(ctr, a.KS)) return;
-  for (int i = tid; i < NOUT; i += NT) {
-    const int rr = i & 15, m = i >> 4;
-    const int nn = nb * 16 + rr, mm = m0 + m;
+  for (int i = tid; i < RB * NOUT; i += NT) {
+    const int b = i / NOUT, o = i % NOUT;
+    const int rr = o & 15, m = o >> 4;
+    const int nn = (nb0 + b) * 16 + rr, mm = m0 + m;
     if (nn < a.N && mm < a.M) {
-      const float* pp = a.partial + (size_t)mm * (gridDim.x * 16) + nn;
-      const size_t plane = (size_t)gridDim.y * MT * gridDim.x * 16;
+      const float* pp = a.partial + (size_t)mm * (gridDim.x * RB * 16) + nn;
+      const size_t plane = (size_t)gridDim.y * MT * gridDim.x * RB * 16;
       float v = 0.0f;
       for (int k0 = 0; k0 < a.KS; k0 += 4) {  // four loads in flight, added in split order
         float t[4];
@@ -722,7 +754,7 @@ __global__ __launch_bounds__(W * 64, W == 16 ? 8 : 4) void gemv_mfma_half_kernel
 constexpr int kKQ = 4;  // K tiles per wave segment
 
 struct GemvPlan {
-  int MT, W, KS, kt_per_split;
+  int MT, W, RB, KS, kt_per_split;
   bool half;  // gemv_mfma_half_kernel: eight weight rows per workgroup (4-bit codes, one row of x)
   unsigned gx, gy;
   size_t lds;
@@ -750,8 +782,28 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // against 7.9 us
   p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
-  p.gx = (unsigned)(p.half ? 2 * NBLK : NBLK);
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
+  // 4-bit codes, eight or sixteen rows of x: each workgroup applies its x
+  // slices to RB row blocks (x read from L2 once per RB blocks), as many as
+  // still leave the grid more than one round of workgroups (eight-row tiles
+  // run two workgroups per CU, sixteen-row tiles one) and no reason to split
+  // K.  M = 16, N = 28672, K = 8192, g = 128: 52.8 -> 33.7 us with four
+  // blocks (32.9 us in four-wave workgroups, below); M = 8, g = 32: 35.1 ->
+  // 32.5 us with two
+  p.RB = 1;
+  if (fmt == kFmtInt4 && p.MT >= 8) {
+    const int64_t round = p.MT == 8 ? 512 : 256;
+    for (int rb = 4; rb > 1; rb /= 2)
+      if ((NBLK + rb - 1) / rb * p.gy > round) {
+        p.RB = rb;
+        break;
+      }
+  }
+  // sixteen-row tiles over four row blocks: four-wave workgroups, two per CU,
+  // so that the grid runs in one round (M = 16, N = 28672, g = 32: 40.0 ->
+  // 37.5 us)
+  if (p.MT == 16 && p.RB == 4) p.W = 4;
+  p.gx = (unsigned)(p.half ? 2 * NBLK : (NBLK + p.RB - 1) / p.RB);
   // split K across workgroups only where a workgroup would otherwise take
   // more than one pass of its waves over K, and only up to about two
   // workgroups per CU: a split that leaves waves without a segment, or that
@@ -768,8 +820,13 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
   // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
-  // [W][MT][16] (matrix-core kernels)
-  p.lds = (size_t)p.W * p.MT * kKQ * 256 + (size_t)p.W * p.MT * (fmt == kFmtInt4 ? 16 : 64) * 4;
+  // [W][MT][16] (matrix-core kernels); with several row blocks the sums
+  // [W][RB][MT][16] reuse the slices' space
+  const size_t slices = (size_t)p.W * p.MT * kKQ * 256;
+  if (p.RB > 1)
+    p.lds = std::max(slices, (size_t)p.W * p.RB * p.MT * 16 * 4);
+  else
+    p.lds = slices + (size_t)p.W * p.MT * (fmt == kFmtInt4 ? 16 : 64) * 4;
   return p;
 }
 
@@ -793,9 +850,9 @@ hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int W, int G>
+template <int MT, int W, int G, int RB = 1>
 hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto k = gemv_mfma_kernel<MT, W, kKQ, G>;
+  auto k = gemv_mfma_kernel<MT, W, kKQ, G, RB>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
   if (e != hipSuccess) return e;
@@ -816,6 +873,11 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
     // one-row sixteen-wave kernel; any other kernel on it would read past N
     if (p.half) return hipErrorInvalidValue;
   }
+  if constexpr (MT == 8) {
+    if (p.RB == 4) return group == 128 ? launch_km<MT, W, 128, 4>(p, a, stream) : launch_km<MT, W, 32, 4>(p, a, stream);
+    if (p.RB == 2) return group == 128 ? launch_km<MT, W, 128, 2>(p, a, stream) : launch_km<MT, W, 32, 2>(p, a, stream);
+  }
+  if (p.RB != 1) return hipErrorInvalidValue;
   return group == 128 ? launch_km<MT, W, 128>(p, a, stream) : launch_km<MT, W, 32>(p, a, stream);
 }
 
@@ -830,6 +892,10 @@ int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf
   if (p.half)
     return snprintf(buf, len, "gemv_mfma_half_kernel<W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                     p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
+  if (p.RB > 1)
+    return snprintf(buf, len,
+                    "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d, RB=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+                    p.MT, p.W, kKQ, group, p.RB, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
   return snprintf(buf, len, "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                   p.MT, p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
 }
@@ -839,7 +905,7 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int, int fmt) {
   if (p.KS == 1) return 0;
   // partial-sum planes padded to whole tiles: [KS][gy * MT][gx * 16] (gx * 8
   // columns for eight-row workgroups)
-  return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * (p.half ? 8 : 16) * sizeof(float);
+  return kSplitCounterBytes + (size_t)p.KS * p.gy * p.MT * p.gx * (p.half ? 8 : 16 * p.RB) * sizeof(float);
 }
 
 hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16_t* x,
@@ -882,6 +948,8 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
   if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
   if (p.MT == 8) return launch_t<8, 8>(p, group, fmt, a, stream);
+  if (p.RB == 4) return group == 128 ? launch_km<16, 4, 128, 4>(p, a, stream) : launch_km<16, 4, 32, 4>(p, a, stream);
+  if (p.RB == 2) return group == 128 ? launch_km<16, 8, 128, 2>(p, a, stream) : launch_km<16, 8, 32, 2>(p, a, stream);
   return group == 128 ? launch_km<16, 8, 128>(p, a, stream) : launch_km<16, 8, 32>(p, a, stream);
 }
 
