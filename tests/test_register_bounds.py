@@ -57,6 +57,21 @@ def test_one_row_gemv_fits_two_workgroups_per_cu():
 
 
 @pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
+def test_multi_row_gemv_register_budgets():
+    # the 4-bit GEMV with eight rows of x over one or two row blocks runs two
+    # eight-wave workgroups per CU (at most 128 VGPRs: 16 waves on 4 SIMDs);
+    # with sixteen rows over four blocks two four-wave workgroups (at most 256);
+    # crossing either bound halves the workgroups per CU (a 20 % slower product)
+    meta = _kernel_metadata("wq_gemv.hip")
+    for g in (128, 32):
+        for rb in (1, 2):
+            for name, (vgpr, scratch) in _find(meta, f"gemv_mfma_kernelILi8ELi8ELi4ELi{g}ELi{rb}E"):
+                assert vgpr <= 128 and scratch == 0, (name, vgpr, scratch)
+        for name, (vgpr, scratch) in _find(meta, f"gemv_mfma_kernelILi16ELi4ELi4ELi{g}ELi4E"):
+            assert vgpr <= 256 and scratch == 0, (name, vgpr, scratch)
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
 def test_g128_quantize_fits_eight_workgroups_per_cu():
     meta = _kernel_metadata("wq_quant.hip")
     # quantize_kernel<DT, G=128, SYM, SCALED=false> for every input dtype

@@ -33,8 +33,10 @@
 // and the power-of-two scale is applied in fp32 (exact over the whole E8M0
 // range).
 //
-// Decomposition.  A workgroup owns one 16-row block, MT rows of x and a range
-// of 128-column K tiles (all of K unless the grid splits K).  Wave w walks
+// Decomposition.  A workgroup owns one 16-row block (the 4-bit kernel with
+// eight or sixteen rows of x: RB = 1, 2 or 4 consecutive blocks, which share
+// each x slice), MT rows of x and a range of 128-column K tiles (all of K
+// unless the grid splits K).  Wave w walks
 // segments of KQ consecutive K tiles (w, w + W, w + 2W, ... in segment units).
 // For each segment it first loads the segment's slice of x (one 16-byte load
 // per lane and x row), then the segment's scales and zero-points (one or two
@@ -46,7 +48,8 @@
 // a CU only if every wave holds at most 64 VGPRs (eight waves per SIMD), so the
 // one-row 4-bit and MXFP4 instances are compiled to that bound; the kernels
 // that need more registers (int8 codes, two or more rows of x) run eight-wave
-// workgroups instead, two or three per CU.  The waves' partial sums meet in
+// workgroups instead, two or three per CU (the sixteen-row 4-bit kernel over
+// four blocks: four-wave workgroups, two per CU).  The waves' partial sums meet in
 // LDS in a fixed order.  When the grid splits K, each
 // workgroup writes fp32 partial sums to the workspace and the last workgroup of
 // a row range (found with a device-scope atomic counter) adds them in split
@@ -441,17 +444,27 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
 // per group applies the scale, so the arithmetic is the VALU GEMV's with the
 // sum order of the matrix core: 9 VALU instructions per code word instead of
 // 13.  Lane (r, c) receives D rows 4c..4c+3 (activation rows) of column r.
+// Halves between the rows of a wave's x slice in the matrix-core GEMV: KQ
+// tiles, plus 16 bytes with several rows (A-fragment reads then start the
+// sixteen rows on different banks; with one row every lane reads the same one).
+constexpr __host__ __device__ int gemv_xrow(int MT, int KQ) { return KQ * 128 + (MT > 1 ? 8 : 0); }
+
 // RB > 1: the workgroup owns RB consecutive 16-row blocks, and each wave
 // applies its segment's x slice to the codes of all of them, so x is read
 // from L2 once per RB blocks.
+// (Register bounds: the one-row sixteen-wave instances run two workgroups per
+// CU at 64 VGPRs; the eight-row instances over up to two blocks two eight-wave
+// workgroups at 128; the four-wave sixteen-row instances two at 256.)
 template <int MT, int W, int KQ, int G, int RB = 1>
-__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) void gemv_mfma_kernel(GemvArgs a) {
+__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : (MT == 8 && RB <= 2) ? 4 : W == 4 ? 2 : 1) void
+gemv_mfma_kernel(GemvArgs a) {
   constexpr int GPT = 128 / G;       // groups per 128-column tile
   constexpr int SPG = 4 / GPT;       // MFMA steps per group
   constexpr int NS = KQ * GPT;       // groups per segment
   constexpr int NT = W * 64;
   constexpr int XCH = MT * KQ / 4;   // 16-byte x chunks per lane and segment
   constexpr int NA = MT < 4 ? MT : 4;  // D elements per lane that can hold real rows
+  constexpr int XROW = gemv_xrow(MT, KQ);  // halves between slice rows
   static_assert(KQ % 4 == 0 && XCH >= 1, "a segment is a multiple of four tiles");
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -463,10 +476,10 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) 
   const Dims d = dims_of<G>(a.K);
   const int kt_lo = ks * a.kt_per_split;
   const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
-  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
+  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * XROW);
   // the cross-wave sums [W][RB][MT][16]: after the x slices (RB = 1), or in
   // their place once every wave is done with its slice
-  float* red = reinterpret_cast<float*>(smem + (RB == 1 ? (size_t)W * MT * KQ * 256 : 0));
+  float* red = reinterpret_cast<float*>(smem + (RB == 1 ? (size_t)W * MT * XROW * 2 : 0));
 
   // per row block: its tiles (blocks past the last re-read it; their outputs
   // are never stored) and this lane's row of scales and zero-points
@@ -482,8 +495,10 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) 
   }
   const uint32_t lane16 = 16u * lane;
   const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
-  // this lane's A row of the slice (rows past MT repeat the last one)
-  const int arow = (r < MT ? r : MT - 1) * (KQ * 128) + 8 * c;
+  // this lane's A row of the slice (rows past MT repeat the last one); slice
+  // rows are XROW halves apart, KQ tiles plus 16 bytes, so that the sixteen
+  // rows an A-fragment read touches start on different banks
+  const uint16_t* arow = xw + (r < MT ? r : MT - 1) * XROW + 8 * c;
 
   float acc[RB][NA];
 #pragma unroll
@@ -517,7 +532,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) 
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
       const bool ok = m0 + m < a.M && kt0 * 128 + cc * 8 < a.K;
-      *reinterpret_cast<uint4*>(xw + m * (KQ * 128) + cc * 8) = ok ? xc[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(xw + m * XROW + cc * 8) = ok ? xc[i] : make_uint4(0, 0, 0, 0);
     }
     // the slice is read back by other lanes of this wave only
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : W == 4 ? 2 : 1) 
 #pragma unroll
     for (int t = 0; t < KQ; ++t) {
       if (t >= nq) break;
-      const uint16_t* xr = xw + arow + t * 128;
+      const uint16_t* xr = arow + t * 128;
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
 #pragma unroll
@@ -822,7 +837,8 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
   // [W][MT][16] (matrix-core kernels); with several row blocks the sums
   // [W][RB][MT][16] reuse the slices' space
-  const size_t slices = (size_t)p.W * p.MT * kKQ * 256;
+  const size_t slices = fmt == kFmtInt4 && !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2
+                                                   : (size_t)p.W * p.MT * kKQ * 256;
   if (p.RB > 1)
     p.lds = std::max(slices, (size_t)p.W * p.RB * p.MT * 16 * 4);
   else
