@@ -456,7 +456,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   CodeT ring[RING][NPW];
   u4 xs[2][XCH];  // activations of even / odd tiles
   SzStage szs;
-  SzRegs szc;
+  // scales / zero-points for the dequantization: with EARLY_SZ (below) two
+  // sets, step 0 of alternate tiles; otherwise one, read before each use
+  // READS_FIRST: phase A issues its LDS reads before anything else (below);
+  // EARLY_SZ: phase A also reads step 0 of the next tile's scales (one group
+  // per tile).  Both take registers that the 128-row instances of the other
+  // formats do not have to spare.
+  constexpr bool READS_FIRST = MB <= 4 || (FMT == kFmtInt4 && G == 128);
+  constexpr bool EARLY_SZ = READS_FIRST && G == 128;
+  constexpr int NSZ = EARLY_SZ ? 2 : 1;
+  SzRegs szr[NSZ];
   h8 af0[MB], af1[MB], bf0[NPW], bf1[NPW];
   load_x(kt_lo, xs[0]);
   load_x(kt_lo + 1, xs[1]);
@@ -467,31 +476,46 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   load_x(kt_lo + 2, xs[0]);
   sz_store(kt_lo / kSzChunk, szs);
   lds_barrier();
-  read_sz(kt_lo, 0, szc);
+  read_sz(kt_lo, 0, szr[0]);
   read_a(kt_lo, 0, af0);
-  deq(kt_lo, 0, ring[0], szc, bf0);
+  deq(kt_lo, 0, ring[0], szr[0], bf0);
 
   // One tile kt.  xs: the register set holding the activations of tile
   // kt + 1 (loaded two tiles earlier), which are stored to LDS and replaced
   // by those of tile kt + 3.  cur: codes of tile kt; nxt: codes of tile
   // kt + 1; ld: the ring slot that receives tile kt + RING - 1.
+  // szc: the set holding step 0 of tile kt's scales / zero-points; szn: the
+  // set that receives step 0 of tile kt + 1's (the same set without
+  // EARLY_SZ).  EARLY_SZ reads szn in phase A, which saves phase B a wait on
+  // LDS (one group per tile: step 1 reuses szc).
   auto tile = [&](auto full_tag, int kt, u4 (&xs)[XCH], const CodeT (&cur)[NPW], const CodeT (&nxt)[NPW],
-                  CodeT (&ld)[NPW]) {
+                  CodeT (&ld)[NPW], SzRegs& szc, SzRegs& szn) {
     constexpr bool FULL = decltype(full_tag)::value;
-    // phase A: MFMAs of step 0 (operands formed earlier); prepare step 1
+    // phase A: MFMAs of step 0 (operands formed earlier); prepare step 1.
+    // With READS_FIRST the phase's LDS reads go first: the barrier at the
+    // end of the phase waits for every LDS access of the wave, so reads
+    // issued late would expose their whole latency there.
+    if constexpr (READS_FIRST) {
+      if constexpr (EARLY_SZ) read_sz(kt + 1, 0, szn);  // (staged half a chunk ahead)
+      else read_sz(kt, 1, szc);
+      read_a(kt, 1, af1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     store_x(kt + 1, xs);
     load_x(kt + 3, xs);
     __builtin_amdgcn_sched_barrier(0);
     load_b(kt + RING - 1, ld);
-    read_sz(kt, 1, szc);
-    read_a(kt, 1, af1);
+    if constexpr (!READS_FIRST) {
+      read_sz(kt, 1, szc);
+      read_a(kt, 1, af1);
+    }
     deq(kt, 1, cur, szc, bf1);
     if (FULL || step_in_k(kt, 0)) mma(af0, bf0);
     lds_barrier();
     // phase B: MFMAs of step 1; prepare step 0 of tile kt + 1
-    read_sz(kt + 1, 0, szc);
+    if constexpr (!EARLY_SZ) read_sz(kt + 1, 0, szn);
     read_a(kt + 1, 0, af0);
-    deq(kt + 1, 0, nxt, szc, bf0);
+    deq(kt + 1, 0, nxt, szn, bf0);
     if (FULL || step_in_k(kt, 1)) mma(af1, bf1);
   };
   using Full = std::integral_constant<bool, true>;
@@ -508,7 +532,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
     for (int u = 0; u < kSzChunk; ++u) {
       if (u == 1) sz_load(ch + 1, szs);
       if (u == 4) sz_store(ch + 1, szs);
-      tile(Full{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING]);
+      tile(Full{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING],
+           szr[u % NSZ], szr[(u + 1) % NSZ]);
     }
   }
   // the rest (fewer than eight tiles, the last one possibly ragged); their
@@ -517,7 +542,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < kSzChunk; ++u)
       if (kt + u < kt_hi)
-        tile(Part{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING]);
+        tile(Part{}, kt + u, xs[(u + 1) % 2], ring[u % RING], ring[(u + 1) % RING], ring[(u + RING - 1) % RING],
+             szr[u % NSZ], szr[(u + 1) % NSZ]);
   }
 
   // every wave's last LDS reads are done before the reduction reuses LDS
