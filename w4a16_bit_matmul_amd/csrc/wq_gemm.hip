@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // EARLY_SZ: phase A also reads step 0 of the next tile's scales (one group
   // per tile).  Both take registers that the 128-row instances of the other
   // formats do not have to spare.
-  constexpr bool READS_FIRST = MB <= 4 || (FMT == kFmtInt4 && G == 128);
+  constexpr bool READS_FIRST =
+      MB <= 4 || (FMT == kFmtInt4 && G == 128) || ((FMT == kFmtMxfp4 || FMT == kFmtNvfp4) && SZV);
   constexpr bool EARLY_SZ = READS_FIRST && G == 128;
   constexpr int NSZ = EARLY_SZ ? 2 : 1;
   SzRegs szr[NSZ];
