@@ -831,6 +831,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   const int64_t target = p.half ? 1024 : 512;  // about two workgroups per CU
   while (wgs * ks * 2 <= target && ks < passes) ks *= 2;
   if (wgs > kSplitMaxTiles) ks = 1;  // (never taken: a split grid has < 512 row ranges)
+  if (p.RB > 1) ks = 1;  // (never taken either: row blocks are shared only past one round)
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
