@@ -460,10 +460,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
   // sets, step 0 of alternate tiles; otherwise one, read before each use
   // READS_FIRST: phase A issues its LDS reads before anything else (below);
   // EARLY_SZ: phase A also reads step 0 of the next tile's scales (one group
-  // per tile).  Both take registers that the 128-row instances of the other
-  // formats do not have to spare.
+  // per tile).  Both take registers: the 128-row int8 instances and the ones
+  // with unaligned scale rows do not have them to spare (they would spill
+  // inside the K loop); the 4-bit g = 32 instance reloads two loop-invariant
+  // values per eight tiles and still measured 2 % faster.
   constexpr bool READS_FIRST =
-      MB <= 4 || (FMT == kFmtInt4 && G == 128) || ((FMT == kFmtMxfp4 || FMT == kFmtNvfp4) && SZV);
+      MB <= 4 || (FMT == kFmtInt4 && (G == 128 || SZV)) || ((FMT == kFmtMxfp4 || FMT == kFmtNvfp4) && SZV);
   constexpr bool EARLY_SZ = READS_FIRST && G == 128;
   constexpr int NSZ = EARLY_SZ ? 2 : 1;
   SzRegs szr[NSZ];
