@@ -175,7 +175,8 @@ def test_gemm_plan_names_the_dispatched_kernel():
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
     for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M",
-                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N"):
+                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N",
+                 "WQ_AUTO_FP4_GEMV_MAX_M", "WQ_AUTO_FP4_NARROW_GEMV_MAX_M"):
         m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
         assert m and int(m.group(1)) == getattr(wq, name), name
     # the binding's restatement of the rule agrees with the plans of every
@@ -189,8 +190,12 @@ def test_gemm_plan_names_the_dispatched_kernel():
             for N in (256, 1024, 2048, 2064, 8192, 16384, 16400, 28672):
                 mfma = plan(M, N).startswith("gemm_kernel")
                 assert mfma == wq.auto_uses_mfma(M, N, fmt), (fmt, M, N)
-    assert not wq.auto_uses_mfma(16, 1024, "int8") and wq.auto_uses_mfma(17, 1024, "mxfp4")
-    assert wq.auto_uses_mfma(5, 8192, "nvfp4") and not wq.auto_uses_mfma(4, 8192, "int8")
+    assert not wq.auto_uses_mfma(16, 1024, "int8") and wq.auto_uses_mfma(17, 1024, "int8")
+    assert wq.auto_uses_mfma(5, 8192, "int8") and not wq.auto_uses_mfma(4, 8192, "int8")
+    for fmt in ("mxfp4", "nvfp4"):
+        assert not wq.auto_uses_mfma(16, 28672, fmt) and wq.auto_uses_mfma(17, 28672, fmt)
+        assert not wq.auto_uses_mfma(32, 2048, fmt) and wq.auto_uses_mfma(33, 2048, fmt)
+        assert wq.auto_uses_mfma(17, 2064, fmt)
     assert not wq.auto_uses_mfma(8, 8192) and wq.auto_uses_mfma(9, 8192)
     assert not wq.auto_uses_mfma(32, 2048) and wq.auto_uses_mfma(33, 1024) and wq.auto_uses_mfma(9, 2064)
     assert not wq.auto_uses_mfma(16, 28672) and wq.auto_uses_mfma(17, 28672) and wq.auto_uses_mfma(16, 16384)
@@ -200,8 +205,9 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert wq.wq_gemm_plan(hi + 1, 8192, 8192, 128).startswith("gemm_kernel"), hi
     assert wq.wq_gemm_w8a16_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel")
     assert wq.wq_gemm_w8a16_plan(lo, 8192, 8192, 128).startswith("gemm_kernel")
-    assert wq.wq_gemm_mxfp4_plan(lo - 1, 8192, 8192).startswith("gemv_kernel")
-    assert wq.wq_gemm_mxfp4_plan(lo, 8192, 8192).startswith("gemm_kernel")
+    fp4 = wq.WQ_AUTO_FP4_GEMV_MAX_M
+    assert wq.wq_gemm_mxfp4_plan(fp4, 8192, 8192).startswith("gemv_mfma_kernel")
+    assert wq.wq_gemm_mxfp4_plan(fp4 + 1, 8192, 8192).startswith("gemm_kernel")
     buf = ctypes.create_string_buffer(8)
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, buf, 8) == wq.WQ_OK and len(buf.value) == 7
     assert wq.lib().wq_gemm_plan(1, 8192, 8192, 128, 0, None, 8) == wq.WQ_EINVAL
@@ -357,7 +363,7 @@ def test_mxfp4_entry_points_checked_on_host():
     need = wq.wq_gemm_mxfp4_workspace_bytes(1, 1024, 28672)
     assert need > 0 and call(g, 1, 1024, 28672, A, A, A, A, None, 0, 0, None) == wq.WQ_EWORKSPACE
     d = wq.wq_gemm_mxfp4_plan(1, 8192, 8192)
-    assert d.startswith("gemv_kernel<MT=1, W=16, KQ=4, G=32, MXFP4>") and "grid=(512,1,1)" in d, d
+    assert d.startswith("gemv_mfma_kernel<MT=1, W=16, KQ=4, G=32, RB=1, MXFP4>") and "grid=(512,1,1)" in d, d
     d = wq.wq_gemm_mxfp4_plan(128, 28672, 8192)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=32, MXFP4>") and "grid=(224,1,1)" in d, d
 
@@ -425,10 +431,13 @@ def test_nvfp4_entry_points_checked_on_host():
     assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 256, None, A, None, None, None) == wq.WQ_EINVAL
     assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 80, None, A, A, None, None) == wq.WQ_EUNSUPPORTED
     assert call("wq_dequant_nvfp4", A, A, None, 64, 256, wq.WQ_F32, A, None) == wq.WQ_EINVAL
-    # plans: the VALU GEMV below WQ_AUTO_MFMA_MIN_M rows, the MFMA GEMM at it
-    lo = wq.WQ_AUTO_MFMA_MIN_M
-    assert wq.wq_gemm_nvfp4_plan(lo - 1, 8192, 8192).startswith("gemv_kernel<MT=4, W=8, KQ=4, G=16, NVFP4>")
-    assert wq.wq_gemm_nvfp4_plan(lo, 8192, 8192).startswith("gemm_kernel<MB=1, NPW=2, G=16, NVFP4>")
+    # plans: the vector-unit GEMV at one row, the matrix-core GEMV up to
+    # WQ_AUTO_FP4_GEMV_MAX_M rows, the GEMM past it
+    hi = wq.WQ_AUTO_FP4_GEMV_MAX_M
+    assert wq.wq_gemm_nvfp4_plan(1, 8192, 8192).startswith("gemv_kernel<MT=1, W=16, KQ=4, G=16, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(4, 8192, 8192).startswith("gemv_mfma_kernel<MT=4, W=8, KQ=4, G=16, RB=1, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(hi, 8192, 8192).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=16, RB=1, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(hi + 1, 8192, 8192).startswith("gemm_kernel<MB=2, NPW=2, G=16, NVFP4>")
     # the workspace query covers the format's own plans
     for M, N, K in [(1, 1024, 28672), (8, 1024, 8192), (128, 48, 28672)]:
         need = wq.wq_gemm_nvfp4_workspace_bytes(M, N, K)

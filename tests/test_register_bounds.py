@@ -3,7 +3,7 @@ gfx950 code (host-only: hipcc cross-compiles without a GPU).
 
 A 1024-thread GEMV workgroup is sixteen waves, four per SIMD; two of them share
 a CU only while every wave holds at most 64 VGPRs (eight waves per SIMD out of
-512 registers).  The one-row 4-bit and MXFP4 GEMV instances and the g = 128
+512 registers).  The one-row 4-bit, MXFP4 and NVFP4 GEMV instances and the g = 128
 quantize kernel are compiled to that bound; crossing it halves their
 workgroups per CU without any other symptom, so the bound and the absence of
 register spills are checked here."""
@@ -47,11 +47,11 @@ def _find(meta, fragment):
 def test_one_row_gemv_fits_two_workgroups_per_cu():
     meta = _kernel_metadata("wq_gemv.hip")
     # 4-bit codes: gemv_mfma_half_kernel<W=16, KQ=4, G> (the one-row launch) and
-    # gemv_mfma_kernel<MT=1, W=16, KQ=4, G>, at g = 128 and 32; MXFP4:
-    # gemv_kernel<MT=1, W=16, KQ=4, G=32, FMT>
+    # gemv_mfma_kernel<MT=1, W=16, KQ=4, G, RB=1, FMT> at g = 128 and 32, and for
+    # MXFP4 (G = 32) and NVFP4 (G = 16)
     for frag in ("gemv_mfma_half_kernelILi16ELi4ELi128E", "gemv_mfma_half_kernelILi16ELi4ELi32E",
                  "gemv_mfma_kernelILi1ELi16ELi4ELi128E", "gemv_mfma_kernelILi1ELi16ELi4ELi32E",
-                 "gemv_kernelILi1ELi16ELi4ELi32ELi2E"):
+                 "gemv_mfma_kernelILi1ELi16ELi4ELi16E"):
         for name, (vgpr, scratch) in _find(meta, frag):
             assert vgpr <= 64 and scratch == 0, (name, vgpr, scratch)
 
@@ -63,7 +63,8 @@ def test_multi_row_gemv_register_budgets():
     # with sixteen rows over four blocks two four-wave workgroups (at most 256);
     # crossing either bound halves the workgroups per CU (a 20 % slower product)
     meta = _kernel_metadata("wq_gemv.hip")
-    for g in (128, 32):
+    # (the MXFP4 instances have G = 32 too; NVFP4's G = 16)
+    for g in (128, 32, 16):
         for rb in (1, 2):
             for name, (vgpr, scratch) in _find(meta, f"gemv_mfma_kernelILi8ELi8ELi4ELi{g}ELi{rb}E"):
                 assert vgpr <= 128 and scratch == 0, (name, vgpr, scratch)

@@ -23,6 +23,8 @@ static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
   if (fmt == wq::kFmtInt4)
     return M > WQ_AUTO_INT4_GEMV_MAX_M && !(M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N) &&
            !(M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M && N > WQ_AUTO_INT4_WIDE_N);
+  if (fmt == wq::kFmtMxfp4 || fmt == wq::kFmtNvfp4)
+    return M > WQ_AUTO_FP4_GEMV_MAX_M && !(M <= WQ_AUTO_FP4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
   return M >= WQ_AUTO_MFMA_MIN_M && !(M <= WQ_AUTO_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
 }
 

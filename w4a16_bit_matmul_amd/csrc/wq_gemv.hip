@@ -1,25 +1,22 @@
-// Split-K dequantize-and-multiply GEMV for small M (gfx950, VALU path).
+// Split-K dequantize-and-multiply GEMV for small M (gfx950).
 //
-// Computes y[m][n] = sum_k x[m][k] * s[n][g(k)] * (q[n][k] - z[n][g(k)]) -- the
-// fused weight-only product of "Quantization Methods Compared: INT8, GPTQ, AWQ,
-// FP8, FP4 and KV-Cache Quantization", section "Hardware, formats and the
-// roofline" (decode reads every weight once and is bound by memory bandwidth),
-// with the decoding of "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ)
-// and GGUF", section "The minimum maths".
+// Computes y[m][n] = sum_k x[m][k] * What[n][k] -- the fused weight-only
+// product of "Quantization Methods Compared: INT8, GPTQ, AWQ, FP8, FP4 and
+// KV-Cache Quantization", section "Hardware, formats and the roofline" (decode
+// reads every weight once and is bound by memory bandwidth), with the decodings
+// of "Quantization for LLM inference: FP8, INT4 (GPTQ, AWQ) and GGUF", sections
+// "The minimum maths" (What = s (q - z) for 4-bit and s q for 8-bit integer
+// codes) and "Microscaling: NVFP4 and MXFP4" (E2M1 codes times an E8M0 or an
+// E4M3 block scale).
 //
-// Arithmetic.  A packed word (eight 4-bit codes of one row; column e in nibble
-// 4*(e%2) + e/2) splits into four fp16 pairs with one shift and four AND-ORs:
-//   word & 0x000F000F | 0x6400 6400        = (1024 + q0,    1024 + q1)
-//   word & 0x00F000F0 | 0x6400 6400        = (1024 + 16q2,  1024 + 16q3)
-//   (word>>8) & 0x000F000F | 0x6400 6400   = (1024 + q4,    1024 + q5)
-//   (word>>8) & 0x00F000F0 | 0x6400 6400   = (1024 + 16q6,  1024 + 16q7)
-// (all exact fp16 integers).  One packed fp16 subtraction of the group's
-// (1024 + z) or (1024 + 16z) pair leaves q - z or 16(q - z), still exact, and
-// v_dot2_f32_f16 multiplies those with the matching fp16 activation pairs into
-// two fp32 sums, a1 (the q - z pairs) and a16 (the 16(q - z) pairs):
-//   sum_k x (q - z) = a1 + a16 / 16,
-// after which one fp32 multiply-add applies the group's scale.  Every product
-// is exact and no sum carries a bias that would later cancel.
+// Kernels.  gemv_mfma_kernel (4-bit integer and MXFP4 codes, and NVFP4 codes
+// from two rows of x up) takes the dot products on the matrix cores: every code
+// word of a lane becomes the exact fp16 B operand of one
+// v_mfma_f32_16x16x32_f16 (the decodings are described beside it), and
+// gemv_mfma_half_kernel is its one-row form for 4-bit codes over half a 16-row
+// block.  gemv_kernel takes them on the vector units with v_dot2_f32_f16: 8-bit
+// codes, and NVFP4 codes with one row of x (there the matrix-core form's
+// per-step scale conversion measured 5-8 % slower).
 //
 // 8-bit codes (group absmax int8, decoding s * q, no zero-point): a word holds
 // four two's-complement codes; XOR-ing the sign bits and placing two bytes
@@ -27,15 +24,16 @@
 // packed fp16 subtraction of 1152 leaves q exactly, which v_dot2_f32_f16
 // multiplies with the activation pairs into one fp32 sum per group.
 //
-// MXFP4 codes (E2M1, natural nibble order, one E8M0 scale per block of 32 =
-// one code word per lane): v_cvt_scalef32_pk_f16_fp4 turns each byte into the
-// exact fp16 pair of E2M1 values, v_dot2_f32_f16 takes the block's fp32 sum,
-// and the power-of-two scale is applied in fp32 (exact over the whole E8M0
-// range).
+// NVFP4 codes on the vector units (E2M1, natural nibble order, one E4M3 scale
+// per block of 16: a lane's eight values of a step lie in one block):
+// v_cvt_scalef32_pk_f16_fp4 turns each byte into the exact fp16 pair of E2M1
+// values, v_dot2_f32_f16 takes the fp32 sum of the eight products, one fp32
+// multiply-add applies the block scale, and the tensor scale multiplies each
+// output.
 //
-// Decomposition.  A workgroup owns one 16-row block (the 4-bit kernel with
-// eight or sixteen rows of x: RB = 1, 2 or 4 consecutive blocks, which share
-// each x slice), MT rows of x and a range of 128-column K tiles (all of K
+// Decomposition.  A workgroup owns one 16-row block (the matrix-core kernel
+// with eight or sixteen rows of x: RB = 1, 2 or 4 consecutive blocks, which
+// share each x slice), MT rows of x and a range of 128-column K tiles (all of K
 // unless the grid splits K).  Wave w walks
 // segments of KQ consecutive K tiles (w, w + W, w + 2W, ... in segment units).
 // For each segment it first loads the segment's slice of x (one 16-byte load
@@ -46,9 +44,9 @@
 // workgroup barrier stands between the loads and the arithmetic, so each wave
 // starts as soon as its own data arrives.  Two 1024-thread workgroups share
 // a CU only if every wave holds at most 64 VGPRs (eight waves per SIMD), so the
-// one-row 4-bit and MXFP4 instances are compiled to that bound; the kernels
-// that need more registers (int8 codes, two or more rows of x) run eight-wave
-// workgroups instead, two or three per CU (the sixteen-row 4-bit kernel over
+// one-row 4-bit, MXFP4 and NVFP4 instances are compiled to that bound; the
+// kernels that need more registers (int8 codes, two or more rows of x) run
+// eight-wave workgroups instead, two or three per CU (sixteen-row tiles over
 // four blocks: four-wave workgroups, two per CU).  The waves' partial sums meet in
 // LDS in a fixed order.  When the grid splits K, each
 // workgroup writes fp32 partial sums to the workspace and the last workgroup of
@@ -173,25 +171,6 @@ __device__ __forceinline__ SZ<NS> load_sz(const GemvArgs& a, int Gtot, uint32_t 
   return v;
 }
 
-// sum over one group of x * (q - z) for 4-bit codes: steps j0 .. j0 + NJ - 1
-// of a tile (word j of the lane's 16 bytes), as a1 + a16 / 16.
-template <int NJ>
-__device__ __forceinline__ float dot_group4(const u4& w4, uint32_t z, uint32_t magic, int j0, const uint4 (&xv)[4]) {
-  const h2 zq = as_h2(z * 0x00010001u + magic);   // (1024 + z) twice
-  const h2 z16 = as_h2(z * 0x00100010u + magic);  // (1024 + 16z) twice
-  float a1 = 0.0f, a16 = 0.0f;
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int j = j0 + jj;
-    const uint32_t w = w4[j], w8 = w >> 8;
-    a1 = dot2(as_u32(as_h2((w & 0x000F000Fu) | magic) - zq), xv[j].x, a1);
-    a16 = dot2(as_u32(as_h2((w & 0x00F000F0u) | magic) - z16), xv[j].y, a16);
-    a1 = dot2(as_u32(as_h2((w8 & 0x000F000Fu) | magic) - zq), xv[j].z, a1);
-    a16 = dot2(as_u32(as_h2((w8 & 0x00F000F0u) | magic) - z16), xv[j].w, a16);
-  }
-  return fmaf(a16, 0.0625f, a1);
-}
-
 // E8M0 scale bytes of the NS blocks one segment covers in one row.
 template <int NS>
 struct E8 {
@@ -219,9 +198,9 @@ __device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, int Gtot, uint32_t 
   return v;
 }
 
-// sum over one block of 32 of x * E2M1(q): code word w (columns 8c .. 8c+7 of
-// the block for this lane), exact fp16 values, fp32 sum.
-__device__ __forceinline__ float dot_block_mx(uint32_t w, const uint4& xv) {
+// sum of x * E2M1(q) over one code word w (columns 8c .. 8c+7 of a step for
+// this lane): exact fp16 values, fp32 sum.
+__device__ __forceinline__ float dot_word_fp4(uint32_t w, const uint4& xv) {
   float a = 0.0f;
   a = __builtin_amdgcn_fdot2(fp4_pair<0>(w, 1.0f), as_h2(xv.x), a, false);
   a = __builtin_amdgcn_fdot2(fp4_pair<1>(w, 1.0f), as_h2(xv.y), a, false);
@@ -249,14 +228,12 @@ __device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, 
   return a;
 }
 
-// FMT: kFmtInt4 (codes, fp16 scales, zero-points), kFmtInt8 (2048-byte tiles,
-// fp16 scales), kFmtMxfp4 (E2M1 tiles, E8M0 scale bytes in a.zp, G = 32),
-// kFmtNvfp4 (E2M1 tiles, E4M3 scale bytes in a.zp, G = 16: a block's sum of
-// exact products times its scale in fp32, the tensor scale on the output).
+// FMT: kFmtInt8 (2048-byte tiles, fp16 scales) or kFmtNvfp4 (E2M1 tiles, E4M3
+// scale bytes in a.zp, G = 16: the sum of a lane's eight exact products times
+// its block's scale in fp32, the tensor scale on the output).
 template <int MT, int W, int KQ, int G, int FMT>
 __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8 : 1) void gemv_kernel(GemvArgs a) {
-  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16),
-                "code format");
+  static_assert(FMT == kFmtInt8 || (FMT == kFmtNvfp4 && G == 16), "code format");
   constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
   constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;     // groups per 128-column tile
@@ -281,7 +258,6 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
   const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
   const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
   const uint32_t lane16 = 16u * lane;
-  const uint32_t magic = in_vgpr(kMagicPair);
 
   float acc[MT];
 #pragma unroll
@@ -292,13 +268,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     const int nq = min(KQ, nkt - q0);       // tiles of the segment inside the split
     const int kt0 = kt_lo + q0;
 
-    // ---- x slice (zeros past M and K), then scales / zero-points, then codes.
-    // With 4-bit codes at g = 32 a segment's scales and zero-points take 40
-    // bytes per lane, and issuing the first code tile ahead of them measured
-    // 5 % faster (loads retire in order, so that tile still arrives before the
-    // x slice is needed); at g = 128 and for the other formats the order below
-    // measured faster.
-    constexpr bool CODE0_FIRST = FMT == kFmtInt4 && G == 32;
+    // ---- x slice (zeros past M and K), then scales, then codes
     u4 buf[KQ][HALVES];
     const auto load_tile = [&](int t) {
 #pragma unroll
@@ -306,7 +276,6 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
         buf[t][h] = __builtin_nontemporal_load(
             reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
     };
-    if constexpr (CODE0_FIRST) load_tile(0);
     uint4 xc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -315,13 +284,13 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
     SZ<FMT == kFmtNvfp4 ? 4 : NS> sz;
-    E8<FMT == kFmtNvfp4 ? 32 : 16> e8s;
-    if constexpr (FMT == kFmtMxfp4 || FMT == kFmtNvfp4)
-      e8s = load_e8<FMT == kFmtNvfp4 ? 32 : 16>(a, d.Gtot, srow, kt0 * GPT);
+    E8<32> e8s;
+    if constexpr (FMT == kFmtNvfp4)
+      e8s = load_e8<32>(a, d.Gtot, srow, kt0 * GPT);
     else
-      sz = load_sz<NS, FMT == kFmtInt4>(a, d.Gtot, srow, zrow, kt0 * GPT);
+      sz = load_sz<NS, false>(a, d.Gtot, srow, zrow, kt0 * GPT);
 #pragma unroll
-    for (int t = CODE0_FIRST ? 1 : 0; t < KQ; ++t) load_tile(t);
+    for (int t = 0; t < KQ; ++t) load_tile(t);
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
@@ -347,24 +316,13 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t b8 = (e8s.v[2 * t + (j >> 1)] >> (16 * (j & 1) + 8 * (c >> 1))) & 0xffu;
-            acc[m] = fmaf(e4m3_to_f32(b8), dot_block_mx(buf[t][0][j], xv[j]), acc[m]);
+            acc[m] = fmaf(e4m3_to_f32(b8), dot_word_fp4(buf[t][0][j], xv[j]), acc[m]);
           }
           continue;
         }
 #pragma unroll
-        for (int gi = 0; gi < GPT; ++gi) {
-          const int j0 = gi * (4 / GPT);
-          if constexpr (FMT == kFmtMxfp4) {
-            acc[m] = fmaf(e8s.scale(t * GPT + gi), dot_block_mx(buf[t][0][gi], xv[gi]), acc[m]);
-          } else {
-            float d;
-            if constexpr (FMT == kFmtInt8)
-              d = dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], j0, xv);
-            else
-              d = dot_group4<4 / GPT>(buf[t][0], sz.zero(t * GPT + gi), magic, j0, xv);
-            acc[m] = fmaf(sz.scale(t * GPT + gi), d, acc[m]);
-          }
-        }
+        for (int gi = 0; gi < GPT; ++gi)
+          acc[m] = fmaf(sz.scale(t * GPT + gi), dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], gi * (4 / GPT), xv), acc[m]);
       }
     }
     // the next segment overwrites this wave's slice: finish reading it first
@@ -455,12 +413,24 @@ constexpr __host__ __device__ int gemv_xrow(int MT, int KQ) { return KQ * 128 + 
 // (Register bounds: the one-row sixteen-wave instances run two workgroups per
 // CU at 64 VGPRs; the eight-row instances over up to two blocks two eight-wave
 // workgroups at 128; the four-wave sixteen-row instances two at 256.)
-template <int MT, int W, int KQ, int G, int RB = 1>
+// FMT: kFmtInt4 (above), kFmtMxfp4 or kFmtNvfp4.  The E2M1 codes share the
+// tile layout, so word j of a lane's 16 bytes is again the B operand of step j:
+// v_cvt_scalef32_pk_f16_fp4 at scale 1 gives its eight exact E2M1 values.
+// MXFP4 (one E8M0 scale per 32 columns = one step): the matrix core sums each
+// step, and one fp32 multiply-add applies the block's power of two (exact over
+// the whole E8M0 range).  NVFP4 (one E4M3 scale per 16 columns, so two blocks
+// per step): the lane's eight values lie in one block and are multiplied by
+// its scale as an fp16 pair (exact: E2M1 x E4M3 has at most 6 significant
+// bits inside fp16's normal range), so the matrix core sums the whole K range
+// and the per-tensor scale multiplies each output.
+template <int MT, int W, int KQ, int G, int RB = 1, int FMT = kFmtInt4>
 __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : (MT == 8 && RB <= 2) ? 4 : W == 4 ? 2 : 1) void
 gemv_mfma_kernel(GemvArgs a) {
+  static_assert(FMT == kFmtInt4 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16), "code format");
   constexpr int GPT = 128 / G;       // groups per 128-column tile
-  constexpr int SPG = 4 / GPT;       // MFMA steps per group
+  constexpr int SPG = GPT <= 4 ? 4 / GPT : 1;  // MFMA steps per group (4-bit and MXFP4 codes)
   constexpr int NS = KQ * GPT;       // groups per segment
+  constexpr int NE = FMT == kFmtNvfp4 ? 32 : 16;  // scale bytes per segment and row (MXFP4, NVFP4)
   constexpr int NT = W * 64;
   constexpr int XCH = MT * KQ / 4;   // 16-byte x chunks per lane and segment
   constexpr int NA = MT < 4 ? MT : 4;  // D elements per lane that can hold real rows
@@ -505,6 +475,9 @@ gemv_mfma_kernel(GemvArgs a) {
   for (int b = 0; b < RB; ++b)
 #pragma unroll
     for (int i = 0; i < NA; ++i) acc[b][i] = 0.0f;
+  f4 accv[RB];  // NVFP4: the matrix core's running sums
+#pragma unroll
+  for (int b = 0; b < RB; ++b) accv[b] = f4{0.f, 0.f, 0.f, 0.f};
 
   for (int sg = wv; sg * KQ < nkt; sg += W) {
     const int q0 = sg * KQ;
@@ -519,9 +492,15 @@ gemv_mfma_kernel(GemvArgs a) {
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    SZ<NS> sz[RB];
+    SZ<FMT == kFmtInt4 ? NS : 4> sz[RB];
+    E8<NE> e8s[RB];
 #pragma unroll
-    for (int b = 0; b < RB; ++b) sz[b] = load_sz<NS, true>(a, d.Gtot, srow[b], zrow[b], kt0 * GPT);
+    for (int b = 0; b < RB; ++b) {
+      if constexpr (FMT == kFmtInt4)
+        sz[b] = load_sz<NS, true>(a, d.Gtot, srow[b], zrow[b], kt0 * GPT);
+      else
+        e8s[b] = load_e8<NE>(a, d.Gtot, srow[b], kt0 * GPT);
+    }
 #pragma unroll
     for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -542,6 +521,47 @@ gemv_mfma_kernel(GemvArgs a) {
     for (int t = 0; t < KQ; ++t) {
       if (t >= nq) break;
       const uint16_t* xr = arow + t * 128;
+      if constexpr (FMT == kFmtNvfp4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            // step j: the lane's columns lie in block 2j + c / 2 of the tile,
+            // byte 2 (j % 2) + c / 2 of scale word 2t + j / 2
+            const uint32_t b8 = (e8s[b].v[2 * t + (j >> 1)] >> (16 * (j & 1) + 8 * (c >> 1))) & 0xffu;
+            const h2 s2 = as_h2(e4m3_to_f16_bits(b8) * 0x00010001u);
+            const uint32_t w = buf[b][t][j];
+            const h2 p0 = fp4_pair<0>(w, 1.0f) * s2, p1 = fp4_pair<1>(w, 1.0f) * s2;
+            const h2 p2 = fp4_pair<2>(w, 1.0f) * s2, p3 = fp4_pair<3>(w, 1.0f) * s2;
+            h8 bfr;
+            bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+            bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+            accv[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, accv[b], 0, 0, 0);
+          }
+        }
+        continue;
+      }
+      if constexpr (FMT == kFmtMxfp4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            const uint32_t w = buf[b][t][j];
+            const h2 p0 = fp4_pair<0>(w, 1.0f), p1 = fp4_pair<1>(w, 1.0f);
+            const h2 p2 = fp4_pair<2>(w, 1.0f), p3 = fp4_pair<3>(w, 1.0f);
+            h8 bfr;
+            bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+            bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+            const f4 T = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const float sc = e8s[b].scale(t * 4 + j);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) acc[b][i] = fmaf(sc, T[i], acc[b][i]);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
 #pragma unroll
@@ -576,6 +596,15 @@ gemv_mfma_kernel(GemvArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
+  if constexpr (FMT == kFmtNvfp4) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int i = 0; i < NA; ++i) acc[b][i] = accv[b][i];
+  }
+  // NVFP4: the per-tensor scale multiplies each output (partial sums stay unscaled)
+  const float ys = FMT == kFmtNvfp4 ? *a.tscale : 1.0f;
+
   // ---- reduce: lane (r, c) holds rows 4c + i of column r of each block; the
   // W waves' sums of each (block, row, column) meet in LDS and are added in
   // wave order
@@ -599,7 +628,7 @@ gemv_mfma_kernel(GemvArgs a) {
     if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * RB * 16]: always in bounds
       split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * RB * 16) + nn, v);
     else if (nn < a.N && mm < a.M)
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
   }
   if (a.KS == 1) return;
 
@@ -622,7 +651,7 @@ gemv_mfma_kernel(GemvArgs a) {
         for (int j = 0; j < 4; ++j)
           if (k0 + j < a.KS) v += t[j];
       }
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
     }
   }
   if (tid == 0) split_reset(ctr);
@@ -771,21 +800,26 @@ constexpr int kKQ = 4;  // K tiles per wave segment
 struct GemvPlan {
   int MT, W, RB, KS, kt_per_split;
   bool half;  // gemv_mfma_half_kernel: eight weight rows per workgroup (4-bit codes, one row of x)
+  bool valu;  // gemv_kernel (dot products on the vector units): 8-bit codes, NVFP4 with one row of x
   unsigned gx, gy;
   size_t lds;
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   GemvPlan p;
-  // 4-bit codes past eight rows: a sixteen-row activation tile reads the
+  // the matrix-core kernel everywhere but for 8-bit codes and one row of NVFP4
+  // codes (M = 1, N = K = 8192: 8.56 us on the vector units, 8.96 us on the
+  // matrix cores; N = 28672: 24.5 against 26.4 us)
+  p.valu = fmt == kFmtInt8 || (fmt == kFmtNvfp4 && M <= 1);
+  // matrix-core kernels past eight rows: a sixteen-row activation tile reads the
   // weights once for sixteen rows (M = 16, N = 28672, K = 8192: 52.6 against
   // 75.9 us with two eight-row tiles), unless that leaves fewer than 128
   // workgroups before K is split (N = 1024, M = 16: 7.90 against 6.93 us;
   // M = 32: 9.05 against 11.0 us)
   const int64_t nblk = (N + 15) / 16;
   p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4
-         : (M <= 8 || fmt != kFmtInt4 || nblk * ((M + 15) / 16) < 128) ? 8 : 16;
-  // one row of 4-bit or MXFP4 codes: sixteen waves, two workgroups per CU at
+         : (M <= 8 || p.valu || nblk * ((M + 15) / 16) < 128) ? 8 : 16;
+  // one row of 4-bit or FP4 codes: sixteen waves, two workgroups per CU at
   // 64 VGPRs.  Kernels that need more registers (two to eight rows, and int8
   // codes with twice the bytes in flight per lane) measured 4-20 % faster with
   // eight-wave workgroups (two or three per CU) than with one sixteen-wave
@@ -798,7 +832,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
-  // 4-bit codes, eight or sixteen rows of x: each workgroup applies its x
+  // matrix-core kernels, eight or sixteen rows of x: each workgroup applies its x
   // slices to RB row blocks (x read from L2 once per RB blocks), as many as
   // still leave the grid more than one round of workgroups (eight-row tiles
   // run two workgroups per CU, sixteen-row tiles one) and no reason to split
@@ -806,7 +840,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // blocks (32.9 us in four-wave workgroups, below); M = 8, g = 32: 35.1 ->
   // 32.5 us with two
   p.RB = 1;
-  if (fmt == kFmtInt4 && p.MT >= 8) {
+  if (!p.valu && p.MT >= 8) {
     const int64_t round = p.MT == 8 ? 512 : 256;
     for (int rb = 4; rb > 1; rb /= 2)
       if ((NBLK + rb - 1) / rb * p.gy > round) {
@@ -838,12 +872,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
   // [W][MT][16] (matrix-core kernels); with several row blocks the sums
   // [W][RB][MT][16] reuse the slices' space
-  const size_t slices = fmt == kFmtInt4 && !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2
-                                                   : (size_t)p.W * p.MT * kKQ * 256;
+  const size_t slices = !p.valu && !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2
+                                           : (size_t)p.W * p.MT * kKQ * 256;
   if (p.RB > 1)
     p.lds = std::max(slices, (size_t)p.W * p.RB * p.MT * 16 * 4);
   else
-    p.lds = slices + (size_t)p.W * p.MT * (fmt == kFmtInt4 ? 16 : 64) * 4;
+    p.lds = slices + (size_t)p.W * p.MT * (p.valu ? 64 : 16) * 4;
   return p;
 }
 
@@ -867,9 +901,9 @@ hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int W, int G, int RB = 1>
+template <int MT, int W, int G, int RB, int FMT>
 hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto k = gemv_mfma_kernel<MT, W, kKQ, G, RB>;
+  auto k = gemv_mfma_kernel<MT, W, kKQ, G, RB, FMT>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
   if (e != hipSuccess) return e;
@@ -877,12 +911,36 @@ hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// the matrix-core GEMV over p.RB row blocks (sixteen-row tiles over four
+// blocks run four-wave workgroups)
+template <int MT, int W, int G, int FMT>
+hipError_t launch_mk(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  if constexpr (MT == 8) {
+    if (p.RB == 4) return launch_km<8, W, G, 4, FMT>(p, a, stream);
+    if (p.RB == 2) return launch_km<8, W, G, 2, FMT>(p, a, stream);
+  }
+  if constexpr (MT == 16) {
+    if (p.RB == 4) return launch_km<16, 4, G, 4, FMT>(p, a, stream);
+    if (p.RB == 2) return launch_km<16, 8, G, 2, FMT>(p, a, stream);
+  }
+  if (p.RB != 1) return hipErrorInvalidValue;
+  return launch_km<MT, W, G, 1, FMT>(p, a, stream);
+}
+
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
-  if (fmt == kFmtMxfp4) return launch_k<MT, W, 32, kFmtMxfp4>(p, a, stream);
-  if (fmt == kFmtNvfp4) return launch_k<MT, W, 16, kFmtNvfp4>(p, a, stream);
-  if (fmt == kFmtInt8)
-    return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
+  if (fmt == kFmtMxfp4) return launch_mk<MT, W, 32, kFmtMxfp4>(p, a, stream);
+  if (fmt == kFmtNvfp4) {
+    if constexpr (MT == 1 && W == 16)
+      if (p.valu) return launch_k<1, 16, 16, kFmtNvfp4>(p, a, stream);
+    if (p.valu) return hipErrorInvalidValue;  // (the vector-unit NVFP4 kernel is the one-row one)
+    return launch_mk<MT, W, 16, kFmtNvfp4>(p, a, stream);
+  }
+  if (fmt == kFmtInt8) {
+    if constexpr (MT == 16) return hipErrorInvalidValue;  // (int8 tiles stop at eight rows)
+    else
+      return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
+  }
   if constexpr (MT == 1 && W == 16) {
     if (p.half) return group == 128 ? launch_kh<W, 128>(p, a, stream) : launch_kh<W, 32>(p, a, stream);
   } else {
@@ -890,22 +948,22 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
     // one-row sixteen-wave kernel; any other kernel on it would read past N
     if (p.half) return hipErrorInvalidValue;
   }
-  if constexpr (MT == 8) {
-    if (p.RB == 4) return group == 128 ? launch_km<MT, W, 128, 4>(p, a, stream) : launch_km<MT, W, 32, 4>(p, a, stream);
-    if (p.RB == 2) return group == 128 ? launch_km<MT, W, 128, 2>(p, a, stream) : launch_km<MT, W, 32, 2>(p, a, stream);
-  }
-  if (p.RB != 1) return hipErrorInvalidValue;
-  return group == 128 ? launch_km<MT, W, 128>(p, a, stream) : launch_km<MT, W, 32>(p, a, stream);
+  return group == 128 ? launch_mk<MT, W, 128, kFmtInt4>(p, a, stream) : launch_mk<MT, W, 32, kFmtInt4>(p, a, stream);
 }
 
 }  // namespace
 
 int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
   const GemvPlan p = plan_gemv(M, N, K, fmt);
-  if (fmt == kFmtInt8 || fmt == kFmtMxfp4 || fmt == kFmtNvfp4)
+  if (p.valu)
     return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
-                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : fmt == kFmtMxfp4 ? "MXFP4" : "NVFP4", p.gx,
-                    p.gy, p.KS, p.W * 64, p.lds, p.KS);
+                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "NVFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
+                    p.KS);
+  if (fmt == kFmtMxfp4 || fmt == kFmtNvfp4)
+    return snprintf(buf, len,
+                    "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d, RB=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
+                    p.MT, p.W, kKQ, group, p.RB, fmt == kFmtMxfp4 ? "MXFP4" : "NVFP4", p.gx, p.gy, p.KS, p.W * 64,
+                    p.lds, p.KS);
   if (p.half)
     return snprintf(buf, len, "gemv_mfma_half_kernel<W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
                     p.W, kKQ, group, p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
@@ -965,9 +1023,7 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
   if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
   if (p.MT == 8) return launch_t<8, 8>(p, group, fmt, a, stream);
-  if (p.RB == 4) return group == 128 ? launch_km<16, 4, 128, 4>(p, a, stream) : launch_km<16, 4, 32, 4>(p, a, stream);
-  if (p.RB == 2) return group == 128 ? launch_km<16, 8, 128, 2>(p, a, stream) : launch_km<16, 8, 32, 2>(p, a, stream);
-  return group == 128 ? launch_km<16, 8, 128>(p, a, stream) : launch_km<16, 8, 32>(p, a, stream);
+  return launch_t<16, 8>(p, group, fmt, a, stream);
 }
 
 }  // namespace wq
