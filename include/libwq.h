@@ -88,8 +88,7 @@ typedef enum {
 typedef enum {
     WQ_PATH_AUTO = 0, /* the GEMV or the MFMA GEMM kernel by the rule below */
     WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; 4-bit, MXFP4 and NVFP4 codes take
-                         their dot products on the matrix cores, int8 codes and one row of NVFP4
-                         codes on the vector units) */
+                         their dot products on the matrix cores, int8 codes on the vector units) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
 
@@ -109,8 +108,8 @@ typedef enum {
  * N = 28672: g = 128 32.9 / 35.5, g = 32 37.5 / 38.8; M = 16, N = 8192,
  * K = 28672, g = 32: 47.9 / 37.1; M = 32, N = 1024, g = 32: 8.9 / 13.3.
  * MXFP4, M = 16: N = 8192 14.6 / 15.7, N = 28672 29.7 / 34.4; NVFP4, M = 16:
- * N = 8192 16.1 / 17.5, N = 28672 38.5 / 39.2; M = 32, N = 2048: MXFP4
- * 12.0 / 12.5, NVFP4 12.4 / 14.5. */
+ * N = 8192 15.2 / 16.2, N = 28672 30.9 / 35.7; M = 32, N = 2048: MXFP4
+ * 12.0 / 12.5, NVFP4 11.8 / 13.0. */
 #define WQ_AUTO_MFMA_MIN_M 5
 #define WQ_AUTO_GEMV_MAX_M 16
 #define WQ_AUTO_GEMV_MAX_N 2048

@@ -431,10 +431,9 @@ def test_nvfp4_entry_points_checked_on_host():
     assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 256, None, A, None, None, None) == wq.WQ_EINVAL
     assert call("wq_quantize_nvfp4", A, wq.WQ_F32, 64, 80, None, A, A, None, None) == wq.WQ_EUNSUPPORTED
     assert call("wq_dequant_nvfp4", A, A, None, 64, 256, wq.WQ_F32, A, None) == wq.WQ_EINVAL
-    # plans: the vector-unit GEMV at one row, the matrix-core GEMV up to
-    # WQ_AUTO_FP4_GEMV_MAX_M rows, the GEMM past it
+    # plans: the matrix-core GEMV up to WQ_AUTO_FP4_GEMV_MAX_M rows, the GEMM past it
     hi = wq.WQ_AUTO_FP4_GEMV_MAX_M
-    assert wq.wq_gemm_nvfp4_plan(1, 8192, 8192).startswith("gemv_kernel<MT=1, W=16, KQ=4, G=16, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(1, 8192, 8192).startswith("gemv_mfma_kernel<MT=1, W=16, KQ=4, G=16, RB=1, NVFP4>")
     assert wq.wq_gemm_nvfp4_plan(4, 8192, 8192).startswith("gemv_mfma_kernel<MT=4, W=8, KQ=4, G=16, RB=1, NVFP4>")
     assert wq.wq_gemm_nvfp4_plan(hi, 8192, 8192).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=16, RB=1, NVFP4>")
     assert wq.wq_gemm_nvfp4_plan(hi + 1, 8192, 8192).startswith("gemm_kernel<MB=2, NPW=2, G=16, NVFP4>")

@@ -159,6 +159,33 @@ def test_nvfp4_one_hot_activations_select_weights_exactly(M, N, K, path):
         assert np.array_equal(got, w_hat16[:, ks].T.view(np.float16)), f"rep {rep} columns {ks[:4]}"
 
 
+@pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA])
+@pytest.mark.parametrize("M", [1, 2, 8, 16])
+def test_nvfp4_one_hot_every_scale_byte(M, path):
+    """Random codes under every E4M3 scale byte 0..126 (the subnormal scales
+    m * 2^-9 included), one-hot rows of x: each output is exactly
+    fp16(fp32(E2M1 * E4M3 * S)) of one weight, the oracle's decoding."""
+    say(f"one-hot nvfp4, every scale byte, M={M} path={path}")
+    N, K = 256, 256
+    rng = np.random.default_rng(2900 + 10 * M + path)
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    s8 = (np.arange(N * K // 16) % 127).astype(np.uint8)
+    rng.shuffle(s8)
+    s8 = s8.reshape(N, K // 16)
+    S = float(np.float32(rng.uniform(0.5, 2.0)))
+    qw = wq.QuantizedWeightNV(wq.wq_pack_mxfp4(torch.from_numpy(q).cuda()).qpacked, torch.from_numpy(s8).cuda(),
+                              torch.tensor([S], dtype=torch.float32, device="cuda"), N, K)
+    w_hat16 = oracle.dequant_nvfp4(q, s8, S, oracle.F16)
+    for rep in range(K // M):
+        ks = np.arange(M) + rep * M
+        x = np.zeros((M, K), np.float32)
+        x[np.arange(M), ks] = 1.0
+        y = wq.wq_gemm_nvfp4(to_dev_f16(workloads.f32_to_f16_bits(x)), qw, path=path)
+        torch.cuda.synchronize()
+        got = f16_bits(y).view(np.float16)
+        assert np.array_equal(got, w_hat16[:, ks].T.view(np.float16)), f"rep {rep} columns {ks[:4]}"
+
+
 @pytest.mark.parametrize("name", ["decode_gemv", "batched_gemm"])
 def test_nvfp4_workload_full_size(name):
     wl = workloads.WORKLOADS[name]

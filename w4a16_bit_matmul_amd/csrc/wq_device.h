@@ -35,15 +35,17 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // per block of 16, one fp32 scale per tensor).
 enum : int { kFmtInt4 = 4, kFmtInt8 = 8, kFmtMxfp4 = 2, kFmtNvfp4 = 3 };
 
-// The E4M3 scale byte b (0..126: 4 exponent bits with bias 7, 3 mantissa
-// bits; exponent field 0 is m * 2^-9) as fp32 and as fp16 bits (both exact).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+// E4M3 scale bytes (0..126: 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent field 0 is m * 2^-9) of one 32-bit word, converted in pairs by
+// gfx950's OCP FP8 conversions at scale 1: bytes 2 HI and 2 HI + 1 as an fp16
+// pair or an fp32 pair, low byte first.  Every E4M3 value is exact in both.
+template <bool HI>
+__device__ __forceinline__ h2 e4m3_pair_f16(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, HI);
 }
-__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e ? ((e + 8u) << 10) | (m << 7) : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
+template <bool HI>
+__device__ __forceinline__ float e4m3_lo_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, HI)[0];
 }
 
 constexpr int kTileRows = 16;

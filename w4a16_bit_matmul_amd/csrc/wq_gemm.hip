@@ -342,8 +342,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
         uint32_t h[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t wd = v.s[2 * e + (k >> 1)], sh = 16 * (k & 1);
-          h[k] = e4m3_to_f16_bits((wd >> sh) & 0xffu) | (e4m3_to_f16_bits((wd >> (sh + 8)) & 0xffu) << 16);
+          const uint32_t wd = v.s[2 * e + (k >> 1)];
+          h[k] = as_u32((k & 1) ? e4m3_pair_f16<true>(wd) : e4m3_pair_f16<false>(wd));
         }
         *reinterpret_cast<u4*>(buf + ((2 * sp + e) * 128 + sn) * 16) = u4{h[0], h[1], h[2], h[3]};
       }

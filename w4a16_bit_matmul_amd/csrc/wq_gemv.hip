@@ -9,27 +9,18 @@
 // codes) and "Microscaling: NVFP4 and MXFP4" (E2M1 codes times an E8M0 or an
 // E4M3 block scale).
 //
-// Kernels.  gemv_mfma_kernel (4-bit integer and MXFP4 codes, and NVFP4 codes
-// from two rows of x up) takes the dot products on the matrix cores: every code
-// word of a lane becomes the exact fp16 B operand of one
-// v_mfma_f32_16x16x32_f16 (the decodings are described beside it), and
-// gemv_mfma_half_kernel is its one-row form for 4-bit codes over half a 16-row
-// block.  gemv_kernel takes them on the vector units with v_dot2_f32_f16: 8-bit
-// codes, and NVFP4 codes with one row of x (there the matrix-core form's
-// per-step scale conversion measured 5-8 % slower).
+// Kernels.  gemv_mfma_kernel (4-bit integer, MXFP4 and NVFP4 codes) takes the
+// dot products on the matrix cores: every code word of a lane becomes the exact
+// fp16 B operand of one v_mfma_f32_16x16x32_f16 (the decodings are described
+// beside it), and gemv_mfma_half_kernel is its one-row form for 4-bit codes
+// over half a 16-row block.  gemv_kernel takes the dot products of 8-bit codes
+// on the vector units with v_dot2_f32_f16.
 //
 // 8-bit codes (group absmax int8, decoding s * q, no zero-point): a word holds
 // four two's-complement codes; XOR-ing the sign bits and placing two bytes
 // under the fp16 exponent of 1024 (v_perm_b32) gives (1152 + q) pairs, and one
 // packed fp16 subtraction of 1152 leaves q exactly, which v_dot2_f32_f16
 // multiplies with the activation pairs into one fp32 sum per group.
-//
-// NVFP4 codes on the vector units (E2M1, natural nibble order, one E4M3 scale
-// per block of 16: a lane's eight values of a step lie in one block):
-// v_cvt_scalef32_pk_f16_fp4 turns each byte into the exact fp16 pair of E2M1
-// values, v_dot2_f32_f16 takes the fp32 sum of the eight products, one fp32
-// multiply-add applies the block scale, and the tensor scale multiplies each
-// output.
 //
 // Decomposition.  A workgroup owns one 16-row block (the matrix-core kernel
 // with eight or sixteen rows of x: RB = 1, 2 or 4 consecutive blocks, which
@@ -198,17 +189,6 @@ __device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, int Gtot, uint32_t 
   return v;
 }
 
-// sum of x * E2M1(q) over one code word w (columns 8c .. 8c+7 of a step for
-// this lane): exact fp16 values, fp32 sum.
-__device__ __forceinline__ float dot_word_fp4(uint32_t w, const uint4& xv) {
-  float a = 0.0f;
-  a = __builtin_amdgcn_fdot2(fp4_pair<0>(w, 1.0f), as_h2(xv.x), a, false);
-  a = __builtin_amdgcn_fdot2(fp4_pair<1>(w, 1.0f), as_h2(xv.y), a, false);
-  a = __builtin_amdgcn_fdot2(fp4_pair<2>(w, 1.0f), as_h2(xv.z), a, false);
-  a = __builtin_amdgcn_fdot2(fp4_pair<3>(w, 1.0f), as_h2(xv.w), a, false);
-  return a;
-}
-
 // sum over one group of x * q for 8-bit codes: steps j0 .. j0 + NJ - 1 of a
 // tile, codes in the two halves h0 (steps 0, 1) and h1 (steps 2, 3).
 template <int NJ>
@@ -228,14 +208,11 @@ __device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, 
   return a;
 }
 
-// FMT: kFmtInt8 (2048-byte tiles, fp16 scales) or kFmtNvfp4 (E2M1 tiles, E4M3
-// scale bytes in a.zp, G = 16: the sum of a lane's eight exact products times
-// its block's scale in fp32, the tensor scale on the output).
-template <int MT, int W, int KQ, int G, int FMT>
-__global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8 : 1) void gemv_kernel(GemvArgs a) {
-  static_assert(FMT == kFmtInt8 || (FMT == kFmtNvfp4 && G == 16), "code format");
-  constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
-  constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
+// 8-bit codes: 2048-byte tiles (two 16-byte loads per lane), fp16 scales.
+template <int MT, int W, int KQ, int G>
+__global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
+  constexpr int TB = kTileBytes8;
+  constexpr int HALVES = 2;        // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;     // groups per 128-column tile
   constexpr int NS = KQ * GPT;     // groups per segment
   constexpr int NT = W * 64;
@@ -283,12 +260,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    SZ<FMT == kFmtNvfp4 ? 4 : NS> sz;
-    E8<32> e8s;
-    if constexpr (FMT == kFmtNvfp4)
-      e8s = load_e8<32>(a, d.Gtot, srow, kt0 * GPT);
-    else
-      sz = load_sz<NS, false>(a, d.Gtot, srow, zrow, kt0 * GPT);
+    const SZ<NS> sz = load_sz<NS, false>(a, d.Gtot, srow, zrow, kt0 * GPT);
 #pragma unroll
     for (int t = 0; t < KQ; ++t) load_tile(t);
 #pragma unroll
@@ -310,28 +282,15 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
         uint4 xv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 32 * j);
-        if constexpr (FMT == kFmtNvfp4) {
-          // step j: the lane's columns lie in block 2j + c / 2 of the tile,
-          // byte 2 (j % 2) + c / 2 of scale word 2t + j / 2
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t b8 = (e8s.v[2 * t + (j >> 1)] >> (16 * (j & 1) + 8 * (c >> 1))) & 0xffu;
-            acc[m] = fmaf(e4m3_to_f32(b8), dot_word_fp4(buf[t][0][j], xv[j]), acc[m]);
-          }
-          continue;
-        }
 #pragma unroll
         for (int gi = 0; gi < GPT; ++gi)
-          acc[m] = fmaf(sz.scale(t * GPT + gi), dot_group8<4 / GPT>(buf[t][0], buf[t][HALVES - 1], gi * (4 / GPT), xv), acc[m]);
+          acc[m] = fmaf(sz.scale(t * GPT + gi), dot_group8<4 / GPT>(buf[t][0], buf[t][1], gi * (4 / GPT), xv), acc[m]);
       }
     }
     // the next segment overwrites this wave's slice: finish reading it first
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
-
-  // NVFP4: the per-tensor scale multiplies each output (partial sums stay unscaled)
-  const float ys = FMT == kFmtNvfp4 ? *a.tscale : 1.0f;
 
   // ---- reduce: every lane's sums go to LDS as [W][MT][16 rows][4 lanes];
   // thread i = 64m + 4r + c adds the W waves' sums of lane (r, c) in wave
@@ -355,7 +314,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
     if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
       split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
     else if (nn < a.N && mm < a.M)
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
   }
   if (a.KS == 1) return;
 
@@ -377,7 +336,7 @@ __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1 && FMT != kFmtInt8) ? 8
         for (int j = 0; j < 4; ++j)
           if (k0 + j < a.KS) v += t[j];
       }
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(FMT == kFmtNvfp4 ? v * ys : v);
+      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
     }
   }
   if (tid == 0) split_reset(ctr);
@@ -420,9 +379,10 @@ constexpr __host__ __device__ int gemv_xrow(int MT, int KQ) { return KQ * 128 + 
 // step, and one fp32 multiply-add applies the block's power of two (exact over
 // the whole E8M0 range).  NVFP4 (one E4M3 scale per 16 columns, so two blocks
 // per step): the lane's eight values lie in one block and are multiplied by
-// its scale as an fp16 pair (exact: E2M1 x E4M3 has at most 6 significant
-// bits inside fp16's normal range), so the matrix core sums the whole K range
-// and the per-tensor scale multiplies each output.
+// its scale as an fp16 pair (the FP8 conversion gives the E4M3 value exactly;
+// the product is exact too: E2M1 x E4M3 has at most 6 significant bits inside
+// fp16's normal range), so the matrix core sums the whole K range and the
+// per-tensor scale multiplies each output.
 template <int MT, int W, int KQ, int G, int RB = 1, int FMT = kFmtInt4>
 __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : (MT == 8 && RB <= 2) ? 4 : W == 4 ? 2 : 1) void
 gemv_mfma_kernel(GemvArgs a) {
@@ -529,8 +489,9 @@ gemv_mfma_kernel(GemvArgs a) {
           for (int b = 0; b < RB; ++b) {
             // step j: the lane's columns lie in block 2j + c / 2 of the tile,
             // byte 2 (j % 2) + c / 2 of scale word 2t + j / 2
-            const uint32_t b8 = (e8s[b].v[2 * t + (j >> 1)] >> (16 * (j & 1) + 8 * (c >> 1))) & 0xffu;
-            const h2 s2 = as_h2(e4m3_to_f16_bits(b8) * 0x00010001u);
+            const uint32_t sw = e8s[b].v[2 * t + (j >> 1)] >> (8 * (c >> 1));
+            const h2 sp = (j & 1) ? e4m3_pair_f16<true>(sw) : e4m3_pair_f16<false>(sw);
+            const h2 s2 = h2{sp[0], sp[0]};
             const uint32_t w = buf[b][t][j];
             const h2 p0 = fp4_pair<0>(w, 1.0f) * s2, p1 = fp4_pair<1>(w, 1.0f) * s2;
             const h2 p2 = fp4_pair<2>(w, 1.0f) * s2, p3 = fp4_pair<3>(w, 1.0f) * s2;
@@ -800,17 +761,15 @@ constexpr int kKQ = 4;  // K tiles per wave segment
 struct GemvPlan {
   int MT, W, RB, KS, kt_per_split;
   bool half;  // gemv_mfma_half_kernel: eight weight rows per workgroup (4-bit codes, one row of x)
-  bool valu;  // gemv_kernel (dot products on the vector units): 8-bit codes, NVFP4 with one row of x
+  bool valu;  // gemv_kernel (dot products on the vector units): 8-bit codes
   unsigned gx, gy;
   size_t lds;
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   GemvPlan p;
-  // the matrix-core kernel everywhere but for 8-bit codes and one row of NVFP4
-  // codes (M = 1, N = K = 8192: 8.56 us on the vector units, 8.96 us on the
-  // matrix cores; N = 28672: 24.5 against 26.4 us)
-  p.valu = fmt == kFmtInt8 || (fmt == kFmtNvfp4 && M <= 1);
+  // the matrix-core kernel for every format but 8-bit codes
+  p.valu = fmt == kFmtInt8;
   // matrix-core kernels past eight rows: a sixteen-row activation tile reads the
   // weights once for sixteen rows (M = 16, N = 28672, K = 8192: 52.6 against
   // 75.9 us with two eight-row tiles), unless that leaves fewer than 128
@@ -891,9 +850,9 @@ hipError_t launch_kh(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int W, int G, int FMT>
+template <int MT, int W, int G>
 hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto k = gemv_kernel<MT, W, kKQ, G, FMT>;
+  auto k = gemv_kernel<MT, W, kKQ, G>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
   if (e != hipSuccess) return e;
@@ -930,16 +889,11 @@ hipError_t launch_mk(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
   if (fmt == kFmtMxfp4) return launch_mk<MT, W, 32, kFmtMxfp4>(p, a, stream);
-  if (fmt == kFmtNvfp4) {
-    if constexpr (MT == 1 && W == 16)
-      if (p.valu) return launch_k<1, 16, 16, kFmtNvfp4>(p, a, stream);
-    if (p.valu) return hipErrorInvalidValue;  // (the vector-unit NVFP4 kernel is the one-row one)
-    return launch_mk<MT, W, 16, kFmtNvfp4>(p, a, stream);
-  }
+  if (fmt == kFmtNvfp4) return launch_mk<MT, W, 16, kFmtNvfp4>(p, a, stream);
   if (fmt == kFmtInt8) {
     if constexpr (MT == 16) return hipErrorInvalidValue;  // (int8 tiles stop at eight rows)
     else
-      return group == 128 ? launch_k<MT, W, 128, kFmtInt8>(p, a, stream) : launch_k<MT, W, 32, kFmtInt8>(p, a, stream);
+      return group == 128 ? launch_k<MT, W, 128>(p, a, stream) : launch_k<MT, W, 32>(p, a, stream);
   }
   if constexpr (MT == 1 && W == 16) {
     if (p.half) return group == 128 ? launch_kh<W, 128>(p, a, stream) : launch_kh<W, 32>(p, a, stream);
@@ -957,8 +911,7 @@ int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf
   const GemvPlan p = plan_gemv(M, N, K, fmt);
   if (p.valu)
     return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
-                    p.MT, p.W, kKQ, group, fmt == kFmtInt8 ? "BITS=8" : "NVFP4", p.gx, p.gy, p.KS, p.W * 64, p.lds,
-                    p.KS);
+                    p.MT, p.W, kKQ, group, "BITS=8", p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
   if (fmt == kFmtMxfp4 || fmt == kFmtNvfp4)
     return snprintf(buf, len,
                     "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d, RB=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
