@@ -87,36 +87,38 @@ typedef enum {
 
 typedef enum {
     WQ_PATH_AUTO = 0, /* the GEMV or the MFMA GEMM kernel by the rule below */
-    WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; 4-bit, MXFP4 and NVFP4 codes take
-                         their dot products on the matrix cores, int8 codes on the vector units) */
+    WQ_PATH_GEMV = 1, /* force the split-K GEMV kernel (any M; dot products on the matrix cores) */
     WQ_PATH_MFMA = 2  /* force the MFMA tile GEMM kernel (any M) */
 } wq_path;
 
-/* WQ_PATH_AUTO.  The GEMV kernel for few rows of x, the MFMA GEMM otherwise.
- * 4-bit integer codes (wq_gemm_w4a16): the GEMV up to WQ_AUTO_INT4_GEMV_MAX_M
- * rows; up to WQ_AUTO_INT4_NARROW_GEMV_MAX_M rows when N is at most
- * WQ_AUTO_GEMV_MAX_N (the MFMA GEMM's 128-column workgroups are then too few
- * to fill the GPU); up to WQ_AUTO_INT4_WIDE_GEMV_MAX_M rows when N exceeds
- * WQ_AUTO_INT4_WIDE_N (each GEMV workgroup then shares its activation slices
- * among four 16-row blocks).  MXFP4 and NVFP4 codes: the GEMV up to
- * WQ_AUTO_FP4_GEMV_MAX_M rows, and up to WQ_AUTO_FP4_NARROW_GEMV_MAX_M rows
- * when N is at most WQ_AUTO_GEMV_MAX_N.  int8 codes (whose GEMV takes its dot
- * products on the vector units): the GEMV below WQ_AUTO_MFMA_MIN_M rows, and
- * up to WQ_AUTO_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N.
- * Measured with K = 8192, one call per launch (us, GEMV / MFMA GEMM): 4-bit
- * codes, M = 8, g = 32: N = 8192 12.2 / 16.8, N = 28672 32.5 / 38.5; M = 16,
- * N = 28672: g = 128 32.9 / 35.5, g = 32 37.5 / 38.8; M = 16, N = 8192,
- * K = 28672, g = 32: 47.9 / 37.1; M = 32, N = 1024, g = 32: 8.9 / 13.3.
- * MXFP4, M = 16: N = 8192 14.6 / 15.7, N = 28672 29.7 / 34.4; NVFP4, M = 16:
- * N = 8192 15.2 / 16.2, N = 28672 30.9 / 35.7; M = 32, N = 2048: MXFP4
- * 12.0 / 12.5, NVFP4 11.8 / 13.0. */
-#define WQ_AUTO_MFMA_MIN_M 5
-#define WQ_AUTO_GEMV_MAX_M 16
+/* WQ_PATH_AUTO.  The GEMV kernel for few rows of x, the MFMA GEMM otherwise
+ * (every GEMV takes its dot products on the matrix cores, so its time grows
+ * slowly with M up to its 16-row activation tile).  4-bit integer codes
+ * (wq_gemm_w4a16): the GEMV up to WQ_AUTO_INT4_GEMV_MAX_M rows; up to
+ * WQ_AUTO_INT4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N
+ * (the MFMA GEMM's 128-column workgroups are then too few to fill the GPU);
+ * up to WQ_AUTO_INT4_WIDE_GEMV_MAX_M rows when N exceeds WQ_AUTO_INT4_WIDE_N
+ * (each GEMV workgroup then shares its activation slices among four 16-row
+ * blocks).  int8 codes: up to WQ_AUTO_INT8_GEMV_MAX_M rows, and up to
+ * WQ_AUTO_INT8_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N.
+ * MXFP4 and NVFP4 codes: up to WQ_AUTO_FP4_GEMV_MAX_M rows, and up to
+ * WQ_AUTO_FP4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N.
+ * Measured with K = 8192 (us, GEMV / MFMA GEMM; 4-bit codes one call per
+ * launch, the others back-to-back calls): 4-bit codes, M = 8, g = 32:
+ * N = 8192 12.2 / 16.8, N = 28672 32.5 / 38.5; M = 16, N = 28672: g = 128
+ * 32.9 / 35.5, g = 32 37.5 / 38.8; M = 16, N = 8192, K = 28672, g = 32:
+ * 47.9 / 37.1; M = 32, N = 1024, g = 32: 8.9 / 13.3.  int8, g = 128: M = 8,
+ * N = 8192 14.5 / 19.3, N = 28672 41.4 / 40.5; M = 16, N = 8192 18.8 / 18.1;
+ * M = 32, N = 2048 12.3 / 13.3.  MXFP4, M = 16: N = 8192 14.6 / 15.7,
+ * N = 28672 29.7 / 34.4; NVFP4, M = 16: N = 8192 15.2 / 16.2, N = 28672
+ * 30.9 / 35.7; M = 32, N = 2048: MXFP4 12.0 / 12.5, NVFP4 11.8 / 13.0. */
 #define WQ_AUTO_GEMV_MAX_N 2048
 #define WQ_AUTO_INT4_GEMV_MAX_M 8
 #define WQ_AUTO_INT4_NARROW_GEMV_MAX_M 32
 #define WQ_AUTO_INT4_WIDE_GEMV_MAX_M 16
 #define WQ_AUTO_INT4_WIDE_N 16384
+#define WQ_AUTO_INT8_GEMV_MAX_M 8
+#define WQ_AUTO_INT8_NARROW_GEMV_MAX_M 32
 #define WQ_AUTO_FP4_GEMV_MAX_M 16
 #define WQ_AUTO_FP4_NARROW_GEMV_MAX_M 32
 

@@ -156,7 +156,7 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert d.startswith("gemv_mfma_kernel<MT=8") and "grid=(64,2," in d, d
     d = wq.wq_gemm_plan(32, 1024, 8192, 32)
     assert d.startswith("gemv_mfma_kernel<MT=16") and "grid=(64,2," in d, d
-    assert wq.wq_gemm_w8a16_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_kernel<MT=8")
+    assert wq.wq_gemm_w8a16_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=128, RB=1, BITS=8>")
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     # a small grid splits K across workgroups in whole eight-tile chunks
     d = wq.wq_gemm_plan(128, 8192, 8192, 128)
@@ -168,15 +168,12 @@ def test_gemm_plan_names_the_dispatched_kernel():
     # one pass of the waves covers K = 8192 at one row: no split, which would
     # only leave waves idle and add the hand-off
     assert split_k(wq.wq_gemm_plan(1, 1024, 8192, 32)) == 1
-    # AUTO switches from the GEMV to the MFMA GEMM at WQ_AUTO_MFMA_MIN_M rows,
-    # the same value in the header and the binding
-    m = re.search(r"#define WQ_AUTO_MFMA_MIN_M (\d+)", open(HEADER).read())
-    assert m and int(m.group(1)) == wq.WQ_AUTO_MFMA_MIN_M
+    # the AUTO rule's bounds: the same values in the header and the binding
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
-    for name in ("WQ_AUTO_GEMV_MAX_M", "WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M",
-                 "WQ_AUTO_INT4_NARROW_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N",
-                 "WQ_AUTO_FP4_GEMV_MAX_M", "WQ_AUTO_FP4_NARROW_GEMV_MAX_M"):
+    for name in ("WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M", "WQ_AUTO_INT4_NARROW_GEMV_MAX_M",
+                 "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N", "WQ_AUTO_INT8_GEMV_MAX_M",
+                 "WQ_AUTO_INT8_NARROW_GEMV_MAX_M", "WQ_AUTO_FP4_GEMV_MAX_M", "WQ_AUTO_FP4_NARROW_GEMV_MAX_M"):
         m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
         assert m and int(m.group(1)) == getattr(wq, name), name
     # the binding's restatement of the rule agrees with the plans of every
@@ -190,8 +187,9 @@ def test_gemm_plan_names_the_dispatched_kernel():
             for N in (256, 1024, 2048, 2064, 8192, 16384, 16400, 28672):
                 mfma = plan(M, N).startswith("gemm_kernel")
                 assert mfma == wq.auto_uses_mfma(M, N, fmt), (fmt, M, N)
-    assert not wq.auto_uses_mfma(16, 1024, "int8") and wq.auto_uses_mfma(17, 1024, "int8")
-    assert wq.auto_uses_mfma(5, 8192, "int8") and not wq.auto_uses_mfma(4, 8192, "int8")
+    assert not wq.auto_uses_mfma(32, 1024, "int8") and wq.auto_uses_mfma(33, 1024, "int8")
+    assert wq.auto_uses_mfma(9, 8192, "int8") and not wq.auto_uses_mfma(8, 28672, "int8")
+    assert wq.auto_uses_mfma(16, 28672, "int8") and wq.auto_uses_mfma(9, 2064, "int8")
     for fmt in ("mxfp4", "nvfp4"):
         assert not wq.auto_uses_mfma(16, 28672, fmt) and wq.auto_uses_mfma(17, 28672, fmt)
         assert not wq.auto_uses_mfma(32, 2048, fmt) and wq.auto_uses_mfma(33, 2048, fmt)
@@ -199,12 +197,12 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert not wq.auto_uses_mfma(8, 8192) and wq.auto_uses_mfma(9, 8192)
     assert not wq.auto_uses_mfma(32, 2048) and wq.auto_uses_mfma(33, 1024) and wq.auto_uses_mfma(9, 2064)
     assert not wq.auto_uses_mfma(16, 28672) and wq.auto_uses_mfma(17, 28672) and wq.auto_uses_mfma(16, 16384)
-    lo = wq.WQ_AUTO_MFMA_MIN_M
     hi = wq.WQ_AUTO_INT4_GEMV_MAX_M
     assert wq.wq_gemm_plan(hi, 8192, 8192, 128).startswith("gemv_mfma_kernel"), hi
     assert wq.wq_gemm_plan(hi + 1, 8192, 8192, 128).startswith("gemm_kernel"), hi
-    assert wq.wq_gemm_w8a16_plan(lo - 1, 8192, 8192, 128).startswith("gemv_kernel")
-    assert wq.wq_gemm_w8a16_plan(lo, 8192, 8192, 128).startswith("gemm_kernel")
+    i8 = wq.WQ_AUTO_INT8_GEMV_MAX_M
+    assert wq.wq_gemm_w8a16_plan(i8, 8192, 8192, 128).startswith("gemv_mfma_kernel")
+    assert wq.wq_gemm_w8a16_plan(i8 + 1, 8192, 8192, 128).startswith("gemm_kernel")
     fp4 = wq.WQ_AUTO_FP4_GEMV_MAX_M
     assert wq.wq_gemm_mxfp4_plan(fp4, 8192, 8192).startswith("gemv_mfma_kernel")
     assert wq.wq_gemm_mxfp4_plan(fp4 + 1, 8192, 8192).startswith("gemm_kernel")
@@ -287,7 +285,7 @@ def test_w8_entry_points_checked_on_host():
 
 def test_w8_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_w8a16_plan(1, 8192, 8192, 128)
-    assert d.startswith("gemv_kernel<MT=1, W=8, KQ=4, G=128, BITS=8>") and "grid=(512,1,1)" in d, d
+    assert d.startswith("gemv_mfma_kernel<MT=1, W=8, KQ=4, G=128, RB=1, BITS=8>") and "grid=(512,1,1)" in d, d
     d = wq.wq_gemm_w8a16_plan(128, 28672, 8192, 128)
     assert d.startswith("gemm_kernel<MB=8, NPW=2, G=128, BITS=8>") and "grid=(224,1,1)" in d, d
     assert wq.wq_gemm_w8a16_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32, BITS=8>")

@@ -128,7 +128,11 @@ def test_dequant_w8_all_codes_and_scales():
 MATMUL_CASES = [(1, 256, 1024, 128), (1, 1000, 1152, 128), (3, 37, 96, 32), (8, 272, 640, 128),
                 (17, 100, 256, 32), (63, 48, 256, 32), (64, 272, 640, 128), (128, 512, 2048, 128),
                 (130, 100, 256, 128), (40, 100, 96, 32), (96, 50, 4224, 128), (129, 300, 1056, 32),
-                (1, 48, 8192, 128), (5, 100, 8192, 32)]
+                (1, 48, 8192, 128), (5, 100, 8192, 32),
+                # forced GEMV: sixteen-row tiles (one and two of them, ragged N),
+                # two rows, and a split K at g = 32
+                (16, 2064, 512, 32), (30, 8176, 4224, 128), (12, 8176, 1024, 32), (2, 1000, 1152, 32),
+                (1, 48, 28672, 32)]
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA, wq.WQ_PATH_AUTO])

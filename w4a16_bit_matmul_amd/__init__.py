@@ -22,13 +22,13 @@ WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_ASYM, WQ_SYM = 0, 1
-WQ_AUTO_MFMA_MIN_M = 5  # WQ_PATH_AUTO, int8 codes: the GEMV below this many rows,
-WQ_AUTO_GEMV_MAX_M = 16  # and up to this many rows when N is at most
-WQ_AUTO_GEMV_MAX_N = 2048  # this; otherwise the MFMA GEMM kernel
+WQ_AUTO_GEMV_MAX_N = 2048  # WQ_PATH_AUTO: the narrow-output bound below
 WQ_AUTO_INT4_GEMV_MAX_M = 8  # 4-bit integer codes: the GEMV up to this many rows,
 WQ_AUTO_INT4_NARROW_GEMV_MAX_M = 32  # up to this many when N <= WQ_AUTO_GEMV_MAX_N,
 WQ_AUTO_INT4_WIDE_GEMV_MAX_M = 16  # and up to this many when N exceeds
 WQ_AUTO_INT4_WIDE_N = 16384  # this
+WQ_AUTO_INT8_GEMV_MAX_M = 8  # int8 codes: the GEMV up to this many rows,
+WQ_AUTO_INT8_NARROW_GEMV_MAX_M = 32  # and up to this many when N <= WQ_AUTO_GEMV_MAX_N
 WQ_AUTO_FP4_GEMV_MAX_M = 16  # MXFP4 / NVFP4 codes: the GEMV up to this many rows,
 WQ_AUTO_FP4_NARROW_GEMV_MAX_M = 32  # and up to this many when N <= WQ_AUTO_GEMV_MAX_N
 
@@ -44,7 +44,7 @@ def auto_uses_mfma(M: int, N: int, fmt: str = "int4") -> bool:
         return M > WQ_AUTO_FP4_GEMV_MAX_M and not (M <= WQ_AUTO_FP4_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
     if fmt != "int8":
         raise ValueError(f"unknown code format {fmt!r}")
-    return M >= WQ_AUTO_MFMA_MIN_M and not (M <= WQ_AUTO_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
+    return M > WQ_AUTO_INT8_GEMV_MAX_M and not (M <= WQ_AUTO_INT8_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
 WQ_WORKSPACE_COUNTER_BYTES = 2048  # leading counter bytes of a split-K workspace (zero before first use)
 WQ_NOALLOC_SCRATCH_BYTES = WQ_WORKSPACE_COUNTER_BYTES + (16 << 20)  # per-GPU scratch of wq_gemm_w4a16_noalloc
 

@@ -11,13 +11,13 @@
 static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K counter region size");
 
 // Kernel family for a product of code format fmt (wq_device.h): the
-// WQ_PATH_AUTO rule of libwq.h.  The VALU GEMV (int8, MXFP4 and NVFP4 codes)
-// does per-row work that grows with M, so the MFMA tile GEMM takes over from
-// WQ_AUTO_MFMA_MIN_M rows; the 4-bit GEMV takes its dot products on the matrix
-// cores at a cost nearly flat in M up to its 8- or 16-row activation tile and
-// keeps more rows.  Narrow outputs give the GEMM's 128-column workgroups too
-// few to fill the chip, so the GEMV keeps more rows there; wide outputs let
-// each GEMV workgroup share its x slices among four row blocks.
+// WQ_PATH_AUTO rule of libwq.h.  The GEMV takes its dot products on the matrix
+// cores at a cost nearly flat in M up to its 8- or 16-row activation tile, and
+// hands over to the MFMA tile GEMM where re-reading the weights per activation
+// tile costs more than the GEMM's staging.  Narrow outputs give the GEMM's
+// 128-column workgroups too few to fill the chip, so the GEMV keeps more rows
+// there; wide outputs let each 4-bit or FP4 GEMV workgroup share its x slices
+// among four row blocks.
 static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
   if (path != WQ_PATH_AUTO) return path == WQ_PATH_MFMA;
   if (fmt == wq::kFmtInt4)
@@ -25,7 +25,7 @@ static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
            !(M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M && N > WQ_AUTO_INT4_WIDE_N);
   if (fmt == wq::kFmtMxfp4 || fmt == wq::kFmtNvfp4)
     return M > WQ_AUTO_FP4_GEMV_MAX_M && !(M <= WQ_AUTO_FP4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
-  return M >= WQ_AUTO_MFMA_MIN_M && !(M <= WQ_AUTO_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
+  return M > WQ_AUTO_INT8_GEMV_MAX_M && !(M <= WQ_AUTO_INT8_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
 }
 
 namespace {

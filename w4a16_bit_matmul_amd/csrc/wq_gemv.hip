@@ -9,18 +9,17 @@
 // codes) and "Microscaling: NVFP4 and MXFP4" (E2M1 codes times an E8M0 or an
 // E4M3 block scale).
 //
-// Kernels.  gemv_mfma_kernel (4-bit integer, MXFP4 and NVFP4 codes) takes the
-// dot products on the matrix cores: every code word of a lane becomes the exact
-// fp16 B operand of one v_mfma_f32_16x16x32_f16 (the decodings are described
-// beside it), and gemv_mfma_half_kernel is its one-row form for 4-bit codes
-// over half a 16-row block.  gemv_kernel takes the dot products of 8-bit codes
-// on the vector units with v_dot2_f32_f16.
+// Kernels.  gemv_mfma_kernel (4-bit and 8-bit integer, MXFP4 and NVFP4 codes)
+// takes the dot products on the matrix cores: every code word of a lane
+// becomes the exact fp16 B operand of one v_mfma_f32_16x16x32_f16 (the
+// decodings are described beside it), and gemv_mfma_half_kernel is its one-row
+// form for 4-bit codes over half a 16-row block.
 //
 // 8-bit codes (group absmax int8, decoding s * q, no zero-point): a word holds
 // four two's-complement codes; XOR-ing the sign bits and placing two bytes
 // under the fp16 exponent of 1024 (v_perm_b32) gives (1152 + q) pairs, and one
-// packed fp16 subtraction of 1152 leaves q exactly, which v_dot2_f32_f16
-// multiplies with the activation pairs into one fp32 sum per group.
+// packed fp16 subtraction of 1152 leaves q exactly: the matrix core sums x * q
+// over a group in fp32, and one multiply-add applies the group's scale.
 //
 // Decomposition.  A workgroup owns one 16-row block (the matrix-core kernel
 // with eight or sixteen rows of x: RB = 1, 2 or 4 consecutive blocks, which
@@ -36,7 +35,7 @@
 // starts as soon as its own data arrives.  Two 1024-thread workgroups share
 // a CU only if every wave holds at most 64 VGPRs (eight waves per SIMD), so the
 // one-row 4-bit, MXFP4 and NVFP4 instances are compiled to that bound; the
-// kernels that need more registers (int8 codes, two or more rows of x) run
+// instances that need more registers (8-bit codes, two or more rows of x) run
 // eight-wave workgroups instead, two or three per CU (sixteen-row tiles over
 // four blocks: four-wave workgroups, two per CU).  The waves' partial sums meet in
 // LDS in a fixed order.  When the grid splits K, each
@@ -77,17 +76,6 @@ template <int G>
 __device__ __forceinline__ Dims dims_of(int K) {
   const int gtot = K / G;
   return Dims{(K + 127) >> 7, gtot, (gtot + 1) >> 1};
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
-}
-
-// The value that lane perm(lane) of this lane's quad holds (DPP quad_perm control
-// CTRL; every lane of the quad must be active).
-template <int CTRL>
-__device__ __forceinline__ float quad_xchg(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
 // Forces a value into a VGPR and hides it from constant folding, so that
@@ -189,164 +177,10 @@ __device__ __forceinline__ E8<NS> load_e8(const GemvArgs& a, int Gtot, uint32_t 
   return v;
 }
 
-// sum over one group of x * q for 8-bit codes: steps j0 .. j0 + NJ - 1 of a
-// tile, codes in the two halves h0 (steps 0, 1) and h1 (steps 2, 3).
-template <int NJ>
-__device__ __forceinline__ float dot_group8(const u4& h0, const u4& h1, int j0, const uint4 (&xv)[4]) {
-  const h2 bias = as_h2(0x64806480u);  // (1152, 1152)
-  float a = 0.0f;
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int j = j0 + jj;
-    const u4& h = j < 2 ? h0 : h1;
-    const uint32_t lo = h[2 * (j & 1)] ^ 0x80808080u, hi = h[2 * (j & 1) + 1] ^ 0x80808080u;
-    a = dot2(as_u32(as_h2(byte_pair(lo, 0x04010400u)) - bias), xv[j].x, a);
-    a = dot2(as_u32(as_h2(byte_pair(lo, 0x04030402u)) - bias), xv[j].y, a);
-    a = dot2(as_u32(as_h2(byte_pair(hi, 0x04010400u)) - bias), xv[j].z, a);
-    a = dot2(as_u32(as_h2(byte_pair(hi, 0x04030402u)) - bias), xv[j].w, a);
-  }
-  return a;
-}
-
-// 8-bit codes: 2048-byte tiles (two 16-byte loads per lane), fp16 scales.
-template <int MT, int W, int KQ, int G>
-__global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
-  constexpr int TB = kTileBytes8;
-  constexpr int HALVES = 2;        // 16-byte loads per lane and tile
-  constexpr int GPT = 128 / G;     // groups per 128-column tile
-  constexpr int NS = KQ * GPT;     // groups per segment
-  constexpr int NT = W * 64;
-  constexpr int XCH = MT * KQ / 4; // 16-byte x chunks per lane and segment (64 lanes x 16 B = 4 tiles of one row)
-  static_assert(KQ % 4 == 0, "a segment is a multiple of four tiles");
-  extern __shared__ __align__(16) uint8_t smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15, c = lane >> 4;
-  const int nb = blockIdx.x, m0 = blockIdx.y * MT, ks = blockIdx.z;
-  const Dims d = dims_of<G>(a.K);
-  const int kt_lo = ks * a.kt_per_split;
-  const int nkt = min(d.KT, kt_lo + a.kt_per_split) - kt_lo;
-  // this wave's x slice: [MT][KQ * 128] halves
-  uint16_t* xw = reinterpret_cast<uint16_t*>(smem) + wv * (MT * KQ * 128);
-  float* red = reinterpret_cast<float*>(smem + (size_t)NT / 64 * MT * KQ * 256);  // [W][MT][64]
-
-  const uint8_t* tbase = a.qp + (size_t)nb * d.KT * TB;
-  const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
-  const uint32_t srow = n * (uint32_t)d.Gtot, zrow = n * (uint32_t)d.GB;
-  const uint32_t lane16 = 16u * lane;
-
-  float acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-
-  for (int sg = wv; sg * KQ < nkt; sg += W) {
-    const int q0 = sg * KQ;                 // first local tile of the segment
-    const int nq = min(KQ, nkt - q0);       // tiles of the segment inside the split
-    const int kt0 = kt_lo + q0;
-
-    // ---- x slice (zeros past M and K), then scales, then codes
-    u4 buf[KQ][HALVES];
-    const auto load_tile = [&](int t) {
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h)
-        buf[t][h] = __builtin_nontemporal_load(
-            reinterpret_cast<const u4*>(tbase + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
-    };
-    uint4 xc[XCH];
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
-      const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
-      xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
-    }
-    const SZ<NS> sz = load_sz<NS, false>(a, d.Gtot, srow, zrow, kt0 * GPT);
-#pragma unroll
-    for (int t = 0; t < KQ; ++t) load_tile(t);
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
-      const bool ok = m0 + m < a.M && kt0 * 128 + cc * 8 < a.K;
-      *reinterpret_cast<uint4*>(xw + m * (KQ * 128) + cc * 8) = ok ? xc[i] : make_uint4(0, 0, 0, 0);
-    }
-    // the slice is read back by other lanes of this wave only
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-
-#pragma unroll
-    for (int t = 0; t < KQ; ++t) {
-      if (t >= nq) break;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint16_t* xr = xw + m * (KQ * 128) + t * 128 + 8 * c;
-        uint4 xv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xr + 32 * j);
-#pragma unroll
-        for (int gi = 0; gi < GPT; ++gi)
-          acc[m] = fmaf(sz.scale(t * GPT + gi), dot_group8<4 / GPT>(buf[t][0], buf[t][1], gi * (4 / GPT), xv), acc[m]);
-      }
-    }
-    // the next segment overwrites this wave's slice: finish reading it first
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // ---- reduce: every lane's sums go to LDS as [W][MT][16 rows][4 lanes];
-  // thread i = 64m + 4r + c adds the W waves' sums of lane (r, c) in wave
-  // order (all reads in flight together), and the four lanes of row r, which
-  // are one quad of threads, meet by two DPP quad exchanges: no cross-row
-  // shuffle through LDS and no dependent LDS reads on the workgroup's tail.
-#pragma unroll
-  for (int m = 0; m < MT; ++m) red[(wv * MT + m) * 64 + 4 * r + c] = acc[m];
-  __syncthreads();
-  constexpr int NOUT = MT * 16;
-  constexpr int NQ = MT * 64;  // a multiple of 64: every wave runs the loop with all lanes
-  for (int i = tid; i < NQ; i += NT) {
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) v += red[w * NQ + i];
-    v += quad_xchg<0xb1>(v);  // lane c ^ 1
-    v += quad_xchg<0x4e>(v);  // lane c ^ 2
-    if ((i & 3) != 0) continue;
-    const int rr = (i >> 2) & 15, m = i >> 6;
-    const int nn = nb * 16 + rr, mm = m0 + m;
-    if (a.KS > 1)  // padded plane [gridDim.y * MT][gridDim.x * 16]: always in bounds
-      split_store(a.partial + ((size_t)ks * gridDim.y * MT + mm) * (gridDim.x * 16) + nn, v);
-    else if (nn < a.N && mm < a.M)
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
-  }
-  if (a.KS == 1) return;
-
-  // ---- split-K: the last workgroup of this row range adds the partial sums
-  unsigned* ctr = a.counters + blockIdx.y * gridDim.x + blockIdx.x;
-  if (!split_arrive(ctr, a.KS)) return;
-  for (int i = tid; i < NOUT; i += NT) {
-    const int rr = i & 15, m = i >> 4;
-    const int nn = nb * 16 + rr, mm = m0 + m;
-    if (nn < a.N && mm < a.M) {
-      const float* pp = a.partial + (size_t)mm * (gridDim.x * 16) + nn;
-      const size_t plane = (size_t)gridDim.y * MT * gridDim.x * 16;
-      float v = 0.0f;
-      for (int k0 = 0; k0 < a.KS; k0 += 4) {  // four loads in flight, added in split order
-        float t[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = split_load(pp + (size_t)min(k0 + j, a.KS - 1) * plane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (k0 + j < a.KS) v += t[j];
-      }
-      a.y[(size_t)mm * a.N + nn] = f32_to_f16_bits(v);
-    }
-  }
-  if (tid == 0) split_reset(ctr);
-}
-
-// ---- GEMV with the dot products on the matrix cores (4-bit codes, M <= 16).
+// ---- GEMV with the dot products on the matrix cores (M <= 16 rows of x per tile).
 //
-// The same decomposition, loads and LDS slices as gemv_kernel, but each code
-// word j of a tile becomes one v_mfma_f32_16x16x32_f16 B operand instead of
-// four v_dot2_f32_f16 operands: lane l = r + 16c supplies B column r (weight
+// Each code word j of a tile (the decomposition above) becomes one
+// v_mfma_f32_16x16x32_f16 B operand: lane l = r + 16c supplies B column r (weight
 // row nb*16 + r) with k-slots 8c..8c+7 of step j, which is exactly word j of
 // its 16 bytes, and A row r (activation row m0 + r, clamped to the block's
 // last row; the D rows it produces past MT are never read) with the same
@@ -358,9 +192,9 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
 // 2^6 has unit spacing 2^-4, so code bits 4..7 land on whole numbers), minus
 // the group's (1024 + z) or (64 + z) pair; the matrix core accumulates the
 // exact products x * (q - z) in fp32 over a group, and one fp32 multiply-add
-// per group applies the scale, so the arithmetic is the VALU GEMV's with the
-// sum order of the matrix core: 9 VALU instructions per code word instead of
-// 13.  Lane (r, c) receives D rows 4c..4c+3 (activation rows) of column r.
+// per group applies the scale: 9 VALU instructions per code word, against 13
+// for the same exact arithmetic on the vector units with v_dot2_f32_f16.  Lane
+// (r, c) receives D rows 4c..4c+3 (activation rows) of column r.
 // Halves between the rows of a wave's x slice in the matrix-core GEMV: KQ
 // tiles, plus 16 bytes with several rows (A-fragment reads then start the
 // sixteen rows on different banks; with one row every lane reads the same one).
@@ -386,9 +220,12 @@ constexpr __host__ __device__ int gemv_xrow(int MT, int KQ) { return KQ * 128 + 
 template <int MT, int W, int KQ, int G, int RB = 1, int FMT = kFmtInt4>
 __global__ __launch_bounds__(W * 64, (W == 16 && MT == 1) ? 8 : (MT == 8 && RB <= 2) ? 4 : W == 4 ? 2 : 1) void
 gemv_mfma_kernel(GemvArgs a) {
-  static_assert(FMT == kFmtInt4 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16), "code format");
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt8 || (FMT == kFmtMxfp4 && G == 32) || (FMT == kFmtNvfp4 && G == 16),
+                "code format");
+  constexpr int TB = FMT == kFmtInt8 ? kTileBytes8 : kTileBytes;
+  constexpr int HALVES = FMT == kFmtInt8 ? 2 : 1;  // 16-byte loads per lane and tile
   constexpr int GPT = 128 / G;       // groups per 128-column tile
-  constexpr int SPG = GPT <= 4 ? 4 / GPT : 1;  // MFMA steps per group (4-bit and MXFP4 codes)
+  constexpr int SPG = GPT <= 4 ? 4 / GPT : 1;  // MFMA steps per group (integer and MXFP4 codes)
   constexpr int NS = KQ * GPT;       // groups per segment
   constexpr int NE = FMT == kFmtNvfp4 ? 32 : 16;  // scale bytes per segment and row (MXFP4, NVFP4)
   constexpr int NT = W * 64;
@@ -418,13 +255,14 @@ gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int nb = min(nb0 + b, nblk - 1);
-    tbase[b] = a.qp + (size_t)nb * d.KT * kTileBytes;
+    tbase[b] = a.qp + (size_t)nb * d.KT * TB;
     const uint32_t n = (uint32_t)min(nb * 16 + r, a.N - 1);
     srow[b] = n * (uint32_t)d.Gtot;
     zrow[b] = n * (uint32_t)d.GB;
   }
   const uint32_t lane16 = 16u * lane;
   const uint32_t m1024 = in_vgpr(kMagicPair), m64 = in_vgpr(0x54005400u);
+  const h2 b1152 = as_h2(in_vgpr(0x64806480u));  // (1152, 1152): 8-bit codes
   // this lane's A row of the slice (rows past MT repeat the last one); slice
   // rows are XROW halves apart, KQ tiles plus 16 bytes, so that the sixteen
   // rows an A-fragment read touches start on different banks
@@ -444,7 +282,7 @@ gemv_mfma_kernel(GemvArgs a) {
     const int nq = min(KQ, nkt - q0);
     const int kt0 = kt_lo + q0;
 
-    u4 buf[RB][KQ];
+    u4 buf[RB][KQ][HALVES];
     uint4 xc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -452,12 +290,12 @@ gemv_mfma_kernel(GemvArgs a) {
       const int row = min(m0 + m, a.M - 1), col = min(kt0 * 128 + cc * 8, a.K - 8);
       xc[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)row * a.K + col);
     }
-    SZ<FMT == kFmtInt4 ? NS : 4> sz[RB];
+    SZ<(FMT == kFmtInt4 || FMT == kFmtInt8) ? NS : 4> sz[RB];
     E8<NE> e8s[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      if constexpr (FMT == kFmtInt4)
-        sz[b] = load_sz<NS, true>(a, d.Gtot, srow[b], zrow[b], kt0 * GPT);
+      if constexpr (FMT == kFmtInt4 || FMT == kFmtInt8)
+        sz[b] = load_sz<NS, FMT == kFmtInt4>(a, d.Gtot, srow[b], zrow[b], kt0 * GPT);
       else
         e8s[b] = load_e8<NE>(a, d.Gtot, srow[b], kt0 * GPT);
     }
@@ -465,8 +303,10 @@ gemv_mfma_kernel(GemvArgs a) {
     for (int b = 0; b < RB; ++b)
 #pragma unroll
       for (int t = 0; t < KQ; ++t)
-        buf[b][t] = __builtin_nontemporal_load(
-            reinterpret_cast<const u4*>(tbase[b] + (size_t)min(kt0 + t, d.KT - 1) * kTileBytes + lane16));
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h)
+          buf[b][t][h] = __builtin_nontemporal_load(
+              reinterpret_cast<const u4*>(tbase[b] + (size_t)min(kt0 + t, d.KT - 1) * TB + 1024u * h + lane16));
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int ci = i * 64 + lane, m = ci / (KQ * 16), cc = ci % (KQ * 16);
@@ -492,7 +332,7 @@ gemv_mfma_kernel(GemvArgs a) {
             const uint32_t sw = e8s[b].v[2 * t + (j >> 1)] >> (8 * (c >> 1));
             const h2 sp = (j & 1) ? e4m3_pair_f16<true>(sw) : e4m3_pair_f16<false>(sw);
             const h2 s2 = h2{sp[0], sp[0]};
-            const uint32_t w = buf[b][t][j];
+            const uint32_t w = buf[b][t][0][j];
             const h2 p0 = fp4_pair<0>(w, 1.0f) * s2, p1 = fp4_pair<1>(w, 1.0f) * s2;
             const h2 p2 = fp4_pair<2>(w, 1.0f) * s2, p3 = fp4_pair<3>(w, 1.0f) * s2;
             h8 bfr;
@@ -509,7 +349,7 @@ gemv_mfma_kernel(GemvArgs a) {
           const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
 #pragma unroll
           for (int b = 0; b < RB; ++b) {
-            const uint32_t w = buf[b][t][j];
+            const uint32_t w = buf[b][t][0][j];
             const h2 p0 = fp4_pair<0>(w, 1.0f), p1 = fp4_pair<1>(w, 1.0f);
             const h2 p2 = fp4_pair<2>(w, 1.0f), p3 = fp4_pair<3>(w, 1.0f);
             h8 bfr;
@@ -517,6 +357,35 @@ gemv_mfma_kernel(GemvArgs a) {
             bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
             const f4 T = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             const float sc = e8s[b].scale(t * 4 + j);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) acc[b][i] = fmaf(sc, T[i], acc[b][i]);
+          }
+        }
+        continue;
+      }
+      if constexpr (FMT == kFmtInt8) {
+        // step j: the lane's eight codes are words 2 (j % 2) and 2 (j % 2) + 1
+        // of half j / 2 of the tile, (1152 + q) pairs minus 1152 in fp16
+#pragma unroll
+        for (int gi = 0; gi < GPT; ++gi) {
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            f4 T;
+#pragma unroll
+            for (int jj = 0; jj < SPG; ++jj) {
+              const int j = gi * SPG + jj;
+              const u4& hv = buf[b][t][j >> 1];
+              const uint32_t lo = hv[2 * (j & 1)] ^ 0x80808080u, hi = hv[2 * (j & 1) + 1] ^ 0x80808080u;
+              const h2 p0 = as_h2(byte_pair(lo, 0x04010400u)) - b1152, p1 = as_h2(byte_pair(lo, 0x04030402u)) - b1152;
+              const h2 p2 = as_h2(byte_pair(hi, 0x04010400u)) - b1152, p3 = as_h2(byte_pair(hi, 0x04030402u)) - b1152;
+              h8 bfr;
+              bfr[0] = p0[0]; bfr[1] = p0[1]; bfr[2] = p1[0]; bfr[3] = p1[1];
+              bfr[4] = p2[0]; bfr[5] = p2[1]; bfr[6] = p3[0]; bfr[7] = p3[1];
+              const h8 afr = *reinterpret_cast<const h8*>(xr + 32 * j);
+              T = jj == 0 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, T, 0, 0, 0);
+            }
+            const float sc = sz[b].scale(t * GPT + gi);
 #pragma unroll
             for (int i = 0; i < NA; ++i) acc[b][i] = fmaf(sc, T[i], acc[b][i]);
           }
@@ -534,7 +403,7 @@ gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
           for (int jj = 0; jj < SPG; ++jj) {
             const int j = gi * SPG + jj;
-            const uint32_t w = buf[b][t][j], w8 = w >> 8;
+            const uint32_t w = buf[b][t][0][j], w8 = w >> 8;
             const h2 p0 = as_h2((w & 0x000F000Fu) | m1024) - zq;
             const h2 p1 = as_h2((w & 0x00F000F0u) | m64) - z64;
             const h2 p2 = as_h2((w8 & 0x000F000Fu) | m1024) - zq;
@@ -761,25 +630,22 @@ constexpr int kKQ = 4;  // K tiles per wave segment
 struct GemvPlan {
   int MT, W, RB, KS, kt_per_split;
   bool half;  // gemv_mfma_half_kernel: eight weight rows per workgroup (4-bit codes, one row of x)
-  bool valu;  // gemv_kernel (dot products on the vector units): 8-bit codes
   unsigned gx, gy;
   size_t lds;
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   GemvPlan p;
-  // the matrix-core kernel for every format but 8-bit codes
-  p.valu = fmt == kFmtInt8;
-  // matrix-core kernels past eight rows: a sixteen-row activation tile reads the
+  // past eight rows a sixteen-row activation tile reads the
   // weights once for sixteen rows (M = 16, N = 28672, K = 8192: 52.6 against
   // 75.9 us with two eight-row tiles), unless that leaves fewer than 128
   // workgroups before K is split (N = 1024, M = 16: 7.90 against 6.93 us;
   // M = 32: 9.05 against 11.0 us)
   const int64_t nblk = (N + 15) / 16;
   p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4
-         : (M <= 8 || p.valu || nblk * ((M + 15) / 16) < 128) ? 8 : 16;
+         : (M <= 8 || nblk * ((M + 15) / 16) < 128) ? 8 : 16;
   // one row of 4-bit or FP4 codes: sixteen waves, two workgroups per CU at
-  // 64 VGPRs.  Kernels that need more registers (two to eight rows, and int8
+  // 64 VGPRs.  Instances that need more registers (two to eight rows, and int8
   // codes with twice the bytes in flight per lane) measured 4-20 % faster with
   // eight-wave workgroups (two or three per CU) than with one sixteen-wave
   // workgroup per CU.
@@ -791,7 +657,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
-  // matrix-core kernels, eight or sixteen rows of x: each workgroup applies its x
+  // eight or sixteen rows of x: each workgroup applies its x
   // slices to RB row blocks (x read from L2 once per RB blocks), as many as
   // still leave the grid more than one round of workgroups (eight-row tiles
   // run two workgroups per CU, sixteen-row tiles one) and no reason to split
@@ -799,7 +665,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // blocks (32.9 us in four-wave workgroups, below); M = 8, g = 32: 35.1 ->
   // 32.5 us with two
   p.RB = 1;
-  if (!p.valu && p.MT >= 8) {
+  if (fmt != kFmtInt8 && p.MT >= 8) {  // (8-bit codes: twice the code registers per block)
     const int64_t round = p.MT == 8 ? 512 : 256;
     for (int rb = 4; rb > 1; rb /= 2)
       if ((NBLK + rb - 1) / rb * p.gy > round) {
@@ -831,28 +697,17 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
   // [W][MT][16] (matrix-core kernels); with several row blocks the sums
   // [W][RB][MT][16] reuse the slices' space
-  const size_t slices = !p.valu && !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2
-                                           : (size_t)p.W * p.MT * kKQ * 256;
+  const size_t slices = !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2 : (size_t)p.W * p.MT * kKQ * 256;
   if (p.RB > 1)
     p.lds = std::max(slices, (size_t)p.W * p.RB * p.MT * 16 * 4);
   else
-    p.lds = slices + (size_t)p.W * p.MT * (p.valu ? 64 : 16) * 4;
+    p.lds = slices + (size_t)p.W * p.MT * 16 * 4;
   return p;
 }
 
 template <int W, int G>
 hipError_t launch_kh(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   auto k = gemv_mfma_half_kernel<W, kKQ, G>;
-  static std::atomic<uint64_t> lds_raised{0};
-  const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
-  if (e != hipSuccess) return e;
-  k<<<dim3(p.gx, p.gy, p.KS), dim3(W * 64), p.lds, stream>>>(a);
-  return hipGetLastError();
-}
-
-template <int MT, int W, int G>
-hipError_t launch_k(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto k = gemv_kernel<MT, W, kKQ, G>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
   if (e != hipSuccess) return e;
@@ -874,27 +729,29 @@ hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 // blocks run four-wave workgroups)
 template <int MT, int W, int G, int FMT>
 hipError_t launch_mk(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  if constexpr (MT == 8) {
-    if (p.RB == 4) return launch_km<8, W, G, 4, FMT>(p, a, stream);
-    if (p.RB == 2) return launch_km<8, W, G, 2, FMT>(p, a, stream);
+  if constexpr (FMT == kFmtInt8) {  // one row block per workgroup, eight waves
+    if (p.RB != 1 || W != 8) return hipErrorInvalidValue;
+    return launch_km<MT, 8, G, 1, FMT>(p, a, stream);
+  } else {
+    if constexpr (MT == 8) {
+      if (p.RB == 4) return launch_km<8, W, G, 4, FMT>(p, a, stream);
+      if (p.RB == 2) return launch_km<8, W, G, 2, FMT>(p, a, stream);
+    }
+    if constexpr (MT == 16) {
+      if (p.RB == 4) return launch_km<16, 4, G, 4, FMT>(p, a, stream);
+      if (p.RB == 2) return launch_km<16, 8, G, 2, FMT>(p, a, stream);
+    }
+    if (p.RB != 1) return hipErrorInvalidValue;
+    return launch_km<MT, W, G, 1, FMT>(p, a, stream);
   }
-  if constexpr (MT == 16) {
-    if (p.RB == 4) return launch_km<16, 4, G, 4, FMT>(p, a, stream);
-    if (p.RB == 2) return launch_km<16, 8, G, 2, FMT>(p, a, stream);
-  }
-  if (p.RB != 1) return hipErrorInvalidValue;
-  return launch_km<MT, W, G, 1, FMT>(p, a, stream);
 }
 
 template <int MT, int W>
 hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream_t stream) {
   if (fmt == kFmtMxfp4) return launch_mk<MT, W, 32, kFmtMxfp4>(p, a, stream);
   if (fmt == kFmtNvfp4) return launch_mk<MT, W, 16, kFmtNvfp4>(p, a, stream);
-  if (fmt == kFmtInt8) {
-    if constexpr (MT == 16) return hipErrorInvalidValue;  // (int8 tiles stop at eight rows)
-    else
-      return group == 128 ? launch_k<MT, W, 128>(p, a, stream) : launch_k<MT, W, 32>(p, a, stream);
-  }
+  if (fmt == kFmtInt8)
+    return group == 128 ? launch_mk<MT, W, 128, kFmtInt8>(p, a, stream) : launch_mk<MT, W, 32, kFmtInt8>(p, a, stream);
   if constexpr (MT == 1 && W == 16) {
     if (p.half) return group == 128 ? launch_kh<W, 128>(p, a, stream) : launch_kh<W, 32>(p, a, stream);
   } else {
@@ -909,13 +766,11 @@ hipError_t launch_t(const GemvPlan& p, int group, int fmt, GemvArgs a, hipStream
 
 int describe_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, char* buf, size_t len) {
   const GemvPlan p = plan_gemv(M, N, K, fmt);
-  if (p.valu)
-    return snprintf(buf, len, "gemv_kernel<MT=%d, W=%d, KQ=%d, G=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
-                    p.MT, p.W, kKQ, group, "BITS=8", p.gx, p.gy, p.KS, p.W * 64, p.lds, p.KS);
-  if (fmt == kFmtMxfp4 || fmt == kFmtNvfp4)
+  if (fmt == kFmtMxfp4 || fmt == kFmtNvfp4 || fmt == kFmtInt8)
     return snprintf(buf, len,
                     "gemv_mfma_kernel<MT=%d, W=%d, KQ=%d, G=%d, RB=%d, %s> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
-                    p.MT, p.W, kKQ, group, p.RB, fmt == kFmtMxfp4 ? "MXFP4" : "NVFP4", p.gx, p.gy, p.KS, p.W * 64,
+                    p.MT, p.W, kKQ, group, p.RB, fmt == kFmtMxfp4 ? "MXFP4" : fmt == kFmtNvfp4 ? "NVFP4" : "BITS=8",
+                    p.gx, p.gy, p.KS, p.W * 64,
                     p.lds, p.KS);
   if (p.half)
     return snprintf(buf, len, "gemv_mfma_half_kernel<W=%d, KQ=%d, G=%d> grid=(%u,%u,%d) block=%d lds=%zu split_k=%d",
