@@ -73,6 +73,17 @@ def test_multi_row_gemv_register_budgets():
 
 
 @pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
+def test_no_gemv_instance_spills():
+    # every compiled GEMV instance (all code formats, tile heights and row
+    # blocks the plans can launch) keeps its values in registers
+    meta = _kernel_metadata("wq_gemv.hip")
+    gemv = [(n, v) for n, v in meta.items() if "gemv_mfma" in n]
+    assert len(gemv) >= 30, len(gemv)
+    for name, (vgpr, scratch) in gemv:
+        assert scratch == 0 and vgpr <= 256, (name, vgpr, scratch)
+
+
+@pytest.mark.skipif(not os.path.exists(_build.HIPCC), reason="hipcc is not installed")
 def test_g128_quantize_fits_eight_workgroups_per_cu():
     meta = _kernel_metadata("wq_quant.hip")
     # quantize_kernel<DT, G=128, SYM, SCALED=false> for every input dtype
