@@ -481,7 +481,7 @@ def bench_sweep(steps):
         y = torch.empty((wl.M, wl.N), dtype=torch.float16, device="cuda")
         ws = _workspace(wl)
         rec = {"workload": name, "M": wl.M, "N": wl.N, "K": wl.K, "group": wl.group,
-               "auto": "mfma" if wq.auto_uses_mfma(wl.M, wl.N) else "gemv"}
+               "auto": "mfma" if wq.auto_uses_mfma(wl.M, wl.N, "int4", wl.K, wl.group) else "gemv"}
         for path, tag in ((wq.WQ_PATH_GEMV, "gemv"), (wq.WQ_PATH_MFMA, "mfma")):
             n_steps = max(20, steps // 4)
             t = _time_calls(lambda i: wq.wq_gemm_w4a16(xd, qws[i % copies], y=y, workspace=ws, path=path), n_steps,

@@ -93,34 +93,30 @@ typedef enum {
 
 /* WQ_PATH_AUTO.  The GEMV kernel for few rows of x, the MFMA GEMM otherwise
  * (every GEMV takes its dot products on the matrix cores, so its time grows
- * slowly with M up to its 16-row activation tile).  4-bit integer codes
- * (wq_gemm_w4a16): the GEMV up to WQ_AUTO_INT4_GEMV_MAX_M rows; up to
- * WQ_AUTO_INT4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N
- * (the MFMA GEMM's 128-column workgroups are then too few to fill the GPU);
- * up to WQ_AUTO_INT4_WIDE_GEMV_MAX_M rows when N exceeds WQ_AUTO_INT4_WIDE_N
- * (each GEMV workgroup then shares its activation slices among four 16-row
- * blocks).  int8 codes: up to WQ_AUTO_INT8_GEMV_MAX_M rows, and up to
- * WQ_AUTO_INT8_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N.
- * MXFP4 and NVFP4 codes: up to WQ_AUTO_FP4_GEMV_MAX_M rows, and up to
- * WQ_AUTO_FP4_NARROW_GEMV_MAX_M rows when N is at most WQ_AUTO_GEMV_MAX_N.
- * Measured with K = 8192 (us, GEMV / MFMA GEMM; 4-bit codes one call per
- * launch, the others back-to-back calls): 4-bit codes, M = 8, g = 32:
- * N = 8192 12.2 / 16.8, N = 28672 32.5 / 38.5; M = 16, N = 28672: g = 128
- * 32.9 / 35.5, g = 32 37.5 / 38.8; M = 16, N = 8192, K = 28672, g = 32:
- * 47.9 / 37.1; M = 32, N = 1024, g = 32: 8.9 / 13.3.  int8, g = 128: M = 8,
- * N = 8192 14.5 / 19.3, N = 28672 41.4 / 40.5; M = 16, N = 8192 18.8 / 18.1;
- * M = 32, N = 2048 12.3 / 13.3.  MXFP4, M = 16: N = 8192 14.6 / 15.7,
- * N = 28672 29.7 / 34.4; NVFP4, M = 16: N = 8192 15.2 / 16.2, N = 28672
- * 30.9 / 35.7; M = 32, N = 2048: MXFP4 12.0 / 12.5, NVFP4 11.8 / 13.0. */
+ * slowly with M up to its 16-row activation tile).  Every format keeps the
+ * GEMV up to WQ_AUTO_NARROW_GEMV_MAX_M rows when N is at most
+ * WQ_AUTO_GEMV_MAX_N (the MFMA GEMM's 128-column workgroups are then too few
+ * to fill the GPU).  Otherwise the GEMV runs up to WQ_AUTO_INT4_GEMV_MAX_M
+ * rows of 4-bit integer codes (up to WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M rows
+ * at group 32 with K above WQ_AUTO_INT4_G32_LONG_K), up to
+ * WQ_AUTO_FP4_GEMV_MAX_M rows of MXFP4 or NVFP4 codes and up to
+ * WQ_AUTO_INT8_GEMV_MAX_M rows of int8 codes.  Measured (back-to-back calls,
+ * us, GEMV / MFMA GEMM, N = 8192): 4-bit codes, K = 8192: M = 8, g = 32
+ * 11.3 / 16.1; M = 16, g = 32 13.1 / 16.6, g = 128 12.5 / 15.7; M = 24, g = 32
+ * 23.8 / 18.1; K = 16384, M = 16: g = 128 20.9 / 24.1, g = 32 22.8 / 25.5;
+ * K = 28672, M = 16: g = 128 33.5 / 33.5, g = 32 38.0 / 35.8, M = 8, g = 32
+ * 31.1 / 34.3; N = 28672, K = 8192, M = 16, g = 128: 32.8 / 34.6.  MXFP4,
+ * M = 16: K = 8192 11.3 / 15.7, K = 28672 31.4 / 33.1; NVFP4, M = 16: K = 8192
+ * 12.3 / 16.2, K = 28672 32.8 / 33.5.  int8, g = 128, K = 8192: M = 8 14.5 /
+ * 19.3, M = 16 18.8 / 18.1.  M = 32, N = 2048: 4-bit 8.9 / 13.3 (N = 1024),
+ * MXFP4 12.0 / 12.5, NVFP4 11.8 / 13.0, int8 12.3 / 13.3. */
 #define WQ_AUTO_GEMV_MAX_N 2048
-#define WQ_AUTO_INT4_GEMV_MAX_M 8
-#define WQ_AUTO_INT4_NARROW_GEMV_MAX_M 32
-#define WQ_AUTO_INT4_WIDE_GEMV_MAX_M 16
-#define WQ_AUTO_INT4_WIDE_N 16384
-#define WQ_AUTO_INT8_GEMV_MAX_M 8
-#define WQ_AUTO_INT8_NARROW_GEMV_MAX_M 32
+#define WQ_AUTO_NARROW_GEMV_MAX_M 32
+#define WQ_AUTO_INT4_GEMV_MAX_M 16
+#define WQ_AUTO_INT4_G32_LONG_K 16384
+#define WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M 8
 #define WQ_AUTO_FP4_GEMV_MAX_M 16
-#define WQ_AUTO_FP4_NARROW_GEMV_MAX_M 32
+#define WQ_AUTO_INT8_GEMV_MAX_M 8
 
 /* A product that splits K across workgroups uses a caller-provided workspace:
  * WQ_WORKSPACE_COUNTER_BYTES bytes of 32-bit counters (one per output tile),

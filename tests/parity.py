@@ -78,8 +78,8 @@ FLOOR_GEMV = 1e-3
 FLOOR_MFMA = 5e-2
 
 
-def floor_for(path, M, N, fmt="int4"):
-    return FLOOR_MFMA if uses_mfma(path, M, N, fmt) else FLOOR_GEMV
+def floor_for(path, M, N, fmt="int4", K=None, group=None):
+    return FLOOR_MFMA if uses_mfma(path, M, N, fmt, K, group) else FLOOR_GEMV
 
 
 def compare_y(y_gpu: torch.Tensor, y_ref: np.ndarray, tol: float = TOL, floor_frac: float = FLOOR_MFMA):
@@ -99,20 +99,20 @@ def compare_y(y_gpu: torch.Tensor, y_ref: np.ndarray, tol: float = TOL, floor_fr
     return normwise, elementwise
 
 
-def uses_mfma(path, M, N, fmt="int4") -> bool:
-    return path == wq.WQ_PATH_MFMA or (path == wq.WQ_PATH_AUTO and wq.auto_uses_mfma(M, N, fmt))
+def uses_mfma(path, M, N, fmt="int4", K=None, group=None) -> bool:
+    return path == wq.WQ_PATH_MFMA or (path == wq.WQ_PATH_AUTO and wq.auto_uses_mfma(M, N, fmt, K, group))
 
 
 def compare_y_path(y_gpu: torch.Tensor, y_ref: np.ndarray, y_ref16: np.ndarray | None, path, M, tol: float = TOL,
-                   fmt: str = "int4"):
+                   fmt: str = "int4", K=None, group=None):
     """The gate against the exact-What oracle product (normwise, and
     elementwise with the path's floor); on the MFMA path, also the elementwise
     check at FLOOR_GEMV against y_ref16, the oracle product of fp16(What).
     Returns (normwise, elementwise, elementwise vs y_ref16 or None)."""
     N = y_ref.shape[1]
-    nw, ew = compare_y(y_gpu, y_ref, tol=tol, floor_frac=floor_for(path, M, N, fmt))
+    nw, ew = compare_y(y_gpu, y_ref, tol=tol, floor_frac=floor_for(path, M, N, fmt, K, group))
     ew16 = None
-    if uses_mfma(path, M, N, fmt) and y_ref16 is not None:
+    if uses_mfma(path, M, N, fmt, K, group) and y_ref16 is not None:
         _, ew16 = compare_y(y_gpu, y_ref16, tol=tol, floor_frac=FLOOR_GEMV)
     return nw, ew, ew16
 

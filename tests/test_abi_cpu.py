@@ -171,22 +171,27 @@ def test_gemm_plan_names_the_dispatched_kernel():
     # the AUTO rule's bounds: the same values in the header and the binding
     m = re.search(r"#define WQ_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == wq.WQ_WORKSPACE_COUNTER_BYTES
-    for name in ("WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_INT4_GEMV_MAX_M", "WQ_AUTO_INT4_NARROW_GEMV_MAX_M",
-                 "WQ_AUTO_INT4_WIDE_GEMV_MAX_M", "WQ_AUTO_INT4_WIDE_N", "WQ_AUTO_INT8_GEMV_MAX_M",
-                 "WQ_AUTO_INT8_NARROW_GEMV_MAX_M", "WQ_AUTO_FP4_GEMV_MAX_M", "WQ_AUTO_FP4_NARROW_GEMV_MAX_M"):
+    for name in ("WQ_AUTO_GEMV_MAX_N", "WQ_AUTO_NARROW_GEMV_MAX_M", "WQ_AUTO_INT4_GEMV_MAX_M",
+                 "WQ_AUTO_INT4_G32_LONG_K", "WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M", "WQ_AUTO_FP4_GEMV_MAX_M",
+                 "WQ_AUTO_INT8_GEMV_MAX_M"):
         m = re.search(r"#define %s (\d+)" % name, open(HEADER).read())
         assert m and int(m.group(1)) == getattr(wq, name), name
     # the binding's restatement of the rule agrees with the plans of every
-    # code format: small N keeps the GEMV for more rows
-    plans = {"int4": lambda M, N: wq.wq_gemm_plan(M, N, 4096, 32),
-             "int8": lambda M, N: wq.wq_gemm_w8a16_plan(M, N, 4096, 32),
-             "mxfp4": lambda M, N: wq.wq_gemm_mxfp4_plan(M, N, 4096),
-             "nvfp4": lambda M, N: wq.wq_gemm_nvfp4_plan(M, N, 4096)}
-    for fmt, plan in plans.items():
-        for M in (1, 4, 5, 8, 9, 16, 17, 32, 33, 128):
-            for N in (256, 1024, 2048, 2064, 8192, 16384, 16400, 28672):
-                mfma = plan(M, N).startswith("gemm_kernel")
-                assert mfma == wq.auto_uses_mfma(M, N, fmt), (fmt, M, N)
+    # code format, group and K: small N keeps the GEMV for more rows, long K
+    # at group 32 fewer
+    for K in (4096, 16384, 16512, 28672):
+        plans = {("int4", 32): lambda M, N: wq.wq_gemm_plan(M, N, K, 32),
+                 ("int4", 128): lambda M, N: wq.wq_gemm_plan(M, N, K, 128),
+                 ("int8", 32): lambda M, N: wq.wq_gemm_w8a16_plan(M, N, K, 32),
+                 ("mxfp4", 32): lambda M, N: wq.wq_gemm_mxfp4_plan(M, N, K),
+                 ("nvfp4", 16): lambda M, N: wq.wq_gemm_nvfp4_plan(M, N, K)}
+        for (fmt, group), plan in plans.items():
+            for M in (1, 4, 5, 8, 9, 16, 17, 32, 33, 128):
+                for N in (256, 1024, 2048, 2064, 8192, 16384, 16400, 28672):
+                    mfma = plan(M, N).startswith("gemm_kernel")
+                    assert mfma == wq.auto_uses_mfma(M, N, fmt, K, group), (fmt, group, K, M, N)
+    with pytest.raises(ValueError):
+        wq.auto_uses_mfma(16, 8192)  # the 4-bit rule needs K and the group
     assert not wq.auto_uses_mfma(32, 1024, "int8") and wq.auto_uses_mfma(33, 1024, "int8")
     assert wq.auto_uses_mfma(9, 8192, "int8") and not wq.auto_uses_mfma(8, 28672, "int8")
     assert wq.auto_uses_mfma(16, 28672, "int8") and wq.auto_uses_mfma(9, 2064, "int8")
@@ -194,9 +199,11 @@ def test_gemm_plan_names_the_dispatched_kernel():
         assert not wq.auto_uses_mfma(16, 28672, fmt) and wq.auto_uses_mfma(17, 28672, fmt)
         assert not wq.auto_uses_mfma(32, 2048, fmt) and wq.auto_uses_mfma(33, 2048, fmt)
         assert wq.auto_uses_mfma(17, 2064, fmt)
-    assert not wq.auto_uses_mfma(8, 8192) and wq.auto_uses_mfma(9, 8192)
-    assert not wq.auto_uses_mfma(32, 2048) and wq.auto_uses_mfma(33, 1024) and wq.auto_uses_mfma(9, 2064)
-    assert not wq.auto_uses_mfma(16, 28672) and wq.auto_uses_mfma(17, 28672) and wq.auto_uses_mfma(16, 16384)
+    for g in (32, 128):
+        assert not wq.auto_uses_mfma(16, 8192, "int4", 8192, g) and wq.auto_uses_mfma(17, 8192, "int4", 8192, g)
+        assert not wq.auto_uses_mfma(32, 2048, "int4", 28672, g) and wq.auto_uses_mfma(33, 1024, "int4", 8192, g)
+    assert not wq.auto_uses_mfma(16, 8192, "int4", 28672, 128) and wq.auto_uses_mfma(9, 8192, "int4", 28672, 32)
+    assert not wq.auto_uses_mfma(8, 8192, "int4", 28672, 32) and not wq.auto_uses_mfma(16, 8192, "int4", 16384, 32)
     hi = wq.WQ_AUTO_INT4_GEMV_MAX_M
     assert wq.wq_gemm_plan(hi, 8192, 8192, 128).startswith("gemv_mfma_kernel"), hi
     assert wq.wq_gemm_plan(hi + 1, 8192, 8192, 128).startswith("gemm_kernel"), hi
@@ -433,7 +440,7 @@ def test_nvfp4_entry_points_checked_on_host():
     hi = wq.WQ_AUTO_FP4_GEMV_MAX_M
     assert wq.wq_gemm_nvfp4_plan(1, 8192, 8192).startswith("gemv_mfma_kernel<MT=1, W=16, KQ=4, G=16, RB=1, NVFP4>")
     assert wq.wq_gemm_nvfp4_plan(4, 8192, 8192).startswith("gemv_mfma_kernel<MT=4, W=8, KQ=4, G=16, RB=1, NVFP4>")
-    assert wq.wq_gemm_nvfp4_plan(hi, 8192, 8192).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=16, RB=1, NVFP4>")
+    assert wq.wq_gemm_nvfp4_plan(hi, 8192, 8192).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=16, RB=2, NVFP4>")
     assert wq.wq_gemm_nvfp4_plan(hi + 1, 8192, 8192).startswith("gemm_kernel<MB=2, NPW=2, G=16, NVFP4>")
     # the workspace query covers the format's own plans
     for M, N, K in [(1, 1024, 28672), (8, 1024, 8192), (128, 48, 28672)]:

@@ -76,7 +76,7 @@ def test_awq_product_matches_oracle(path):
     torch.cuda.synchronize()
     q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16, alpha=alpha)
     y_ref = oracle.gemm_f64(oracle.scale_activations(x, alpha), oracle.dequant(q, s, z, group))
-    compare_y(y, y_ref, floor_frac=floor_for(path, M, N))
+    compare_y(y, y_ref, floor_frac=floor_for(path, M, N, K=K, group=group))
 
 
 def test_awq_fold_reduces_error_on_decode_distribution():

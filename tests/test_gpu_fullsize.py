@@ -46,7 +46,7 @@ def test_workload_full_size(name):
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], workspace=ws)
     torch.cuda.synchronize()
-    floor = FLOOR_MFMA if wq.auto_uses_mfma(wl.M, wl.N) else FLOOR_GEMV
+    floor = FLOOR_MFMA if wq.auto_uses_mfma(wl.M, wl.N, "int4", wl.K, wl.group) else FLOOR_GEMV
     ref = oracle.gemm_rows_f64(x, q, s, z, wl.group, 0, wl.N)
     nw, ew = compare_y(y, ref, floor_frac=floor)
     say(f"  all {wl.M}x{wl.N} outputs: normwise {nw:.2e} elementwise {ew:.2e}")

@@ -119,7 +119,9 @@ MATMUL_CASES = [(1, 256, 1024), (1, 1000, 1152), (3, 37, 96), (8, 272, 640), (17
                 (1, 48, 28672), (5, 100, 8192),
                 # forced GEMV: eight- and sixteen-row tiles over one, two and four
                 # row blocks (N past 16384: 1025 blocks, the last one ragged), two rows
-                (6, 16400, 512), (16, 16400, 512), (30, 16400, 512), (12, 8176, 4224), (2, 1000, 1152)]
+                (6, 16400, 512), (16, 16400, 512), (30, 16400, 512), (12, 8176, 4224), (2, 1000, 1152),
+                # eight-row tiles over two blocks, sixteen-wave workgroups (511 blocks)
+                (8, 8176, 640)]
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA, wq.WQ_PATH_AUTO])

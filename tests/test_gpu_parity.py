@@ -186,12 +186,18 @@ MATMUL_CASES = [  # M, N, K, group
     # 4-bit GEMV with several 16-row blocks per workgroup (eight or sixteen
     # rows of x): N = 16400 has 1025 row blocks and N = 8200 513, so the last
     # workgroup's later blocks lie past N; M = 30 takes two sixteen-row tiles;
-    # N = 8176 (511 blocks), K = 4224 runs one block per workgroup over a
-    # ragged K
+    # N = 8176 (511 blocks), K = 4224: two blocks per workgroup over a ragged
+    # K; N = 2064 (129 blocks): one
     (6, 16400, 512, 32),
     (13, 8200, 1024, 128),
     (30, 16400, 512, 32),
     (12, 8176, 4224, 32),
+    (16, 2064, 4224, 32),
+    # eight-row tiles over two blocks: N = 8176 (511 blocks, the last
+    # workgroup's second block past N) in sixteen-wave workgroups, and
+    # N = 12000 (750 blocks, 375 workgroups) in eight-wave ones
+    (8, 8176, 640, 32),
+    (6, 12000, 512, 128),
 ]
 
 
@@ -211,7 +217,8 @@ def test_matmul_within_tolerance(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M,
+                                  K=K, group=group)
     say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
@@ -232,7 +239,8 @@ def test_matmul_offset_activations(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M,
+                                  K=K, group=group)
     say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 
@@ -279,9 +287,9 @@ def test_grid_exact_weights_reduce_to_fp16_gemm(path):
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
     y_ref = oracle.gemm_f64(x, W)
-    compare_y(y, y_ref, floor_frac=floor_for(path, M, N))
+    compare_y(y, y_ref, floor_frac=floor_for(path, M, N, K=K, group=group))
     y_torch = (to_dev_f16(x).float() @ torch.from_numpy(W).cuda().t()).cpu().numpy().astype(np.float64)
-    compare_y(y, y_torch, floor_frac=floor_for(path, M, N))
+    compare_y(y, y_torch, floor_frac=floor_for(path, M, N, K=K, group=group))
 
 
 def test_split_k_workspace_is_reusable():
@@ -421,7 +429,8 @@ def test_matmul_symmetric_within_tolerance(M, N, K, group, path):
     y_ref = oracle.gemm_f64(x, oracle.dequant(q, s, z, group))
     y = wq.wq_gemm_w4a16(to_dev_f16(x), out["qw"], path=path)
     torch.cuda.synchronize()
-    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M)
+    nw, ew, ew16 = compare_y_path(y, y_ref, ref16(x, oracle.dequant(q, s, z, group, oracle.F16)), path, M,
+                                  K=K, group=group)
     say(f"  normwise {nw:.2e} elementwise {ew:.2e} elementwise vs fp16(What) {ew16}")
 
 

@@ -41,7 +41,7 @@ def test_noalloc_matches_workspace_entry_point():
         # and within tolerance of the oracle (every output)
         q, s, z = oracle.quantize_groups(W, group, dtype=oracle.BF16)
         nw, ew = compare_y(y, oracle.gemm_rows_f64(x, q, s, z, group, 0, N),
-                           floor_frac=floor_for(wq.WQ_PATH_AUTO, M, N))
+                           floor_frac=floor_for(wq.WQ_PATH_AUTO, M, N, K=K, group=group))
         say(f"  identical to the workspace entry point; normwise {nw:.2e} elementwise {ew:.2e}")
         # the same call again: the scratch's counters were left zero
         y2 = torch.full_like(y_ref, float("nan"))

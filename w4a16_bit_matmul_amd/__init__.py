@@ -22,29 +22,33 @@ WQ_OK, WQ_EINVAL, WQ_EUNSUPPORTED, WQ_EALIGN, WQ_EWORKSPACE, WQ_EHIP = 0, -1, -2
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_ASYM, WQ_SYM = 0, 1
-WQ_AUTO_GEMV_MAX_N = 2048  # WQ_PATH_AUTO: the narrow-output bound below
-WQ_AUTO_INT4_GEMV_MAX_M = 8  # 4-bit integer codes: the GEMV up to this many rows,
-WQ_AUTO_INT4_NARROW_GEMV_MAX_M = 32  # up to this many when N <= WQ_AUTO_GEMV_MAX_N,
-WQ_AUTO_INT4_WIDE_GEMV_MAX_M = 16  # and up to this many when N exceeds
-WQ_AUTO_INT4_WIDE_N = 16384  # this
-WQ_AUTO_INT8_GEMV_MAX_M = 8  # int8 codes: the GEMV up to this many rows,
-WQ_AUTO_INT8_NARROW_GEMV_MAX_M = 32  # and up to this many when N <= WQ_AUTO_GEMV_MAX_N
-WQ_AUTO_FP4_GEMV_MAX_M = 16  # MXFP4 / NVFP4 codes: the GEMV up to this many rows,
-WQ_AUTO_FP4_NARROW_GEMV_MAX_M = 32  # and up to this many when N <= WQ_AUTO_GEMV_MAX_N
+WQ_AUTO_GEMV_MAX_N = 2048  # WQ_PATH_AUTO: every format keeps the GEMV up to
+WQ_AUTO_NARROW_GEMV_MAX_M = 32  # this many rows when N <= WQ_AUTO_GEMV_MAX_N; otherwise up to
+WQ_AUTO_INT4_GEMV_MAX_M = 16  # this many rows of 4-bit integer codes (at group 32 with
+WQ_AUTO_INT4_G32_LONG_K = 16384  # K above this only up to
+WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M = 8  # this many),
+WQ_AUTO_FP4_GEMV_MAX_M = 16  # this many rows of MXFP4 / NVFP4 codes
+WQ_AUTO_INT8_GEMV_MAX_M = 8  # and this many rows of int8 codes
 
 
-def auto_uses_mfma(M: int, N: int, fmt: str = "int4") -> bool:
-    """Whether WQ_PATH_AUTO runs the MFMA GEMM kernel for M rows and N outputs
-    of code format fmt ("int4", "int8", "mxfp4" or "nvfp4"): the library's
-    rule, restated."""
-    if fmt == "int4":
-        return (M > WQ_AUTO_INT4_GEMV_MAX_M and not (M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
-                and not (M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M and N > WQ_AUTO_INT4_WIDE_N))
-    if fmt in ("mxfp4", "nvfp4"):
-        return M > WQ_AUTO_FP4_GEMV_MAX_M and not (M <= WQ_AUTO_FP4_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
-    if fmt != "int8":
+def auto_uses_mfma(M: int, N: int, fmt: str = "int4", K: int | None = None, group: int | None = None) -> bool:
+    """Whether WQ_PATH_AUTO runs the MFMA GEMM kernel for M rows, N outputs and
+    K inputs of code format fmt ("int4", "int8", "mxfp4" or "nvfp4"): the
+    library's rule, restated.  4-bit integer codes need K and group."""
+    if fmt not in ("int4", "int8", "mxfp4", "nvfp4"):
         raise ValueError(f"unknown code format {fmt!r}")
-    return M > WQ_AUTO_INT8_GEMV_MAX_M and not (M <= WQ_AUTO_INT8_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N)
+    if M <= WQ_AUTO_NARROW_GEMV_MAX_M and N <= WQ_AUTO_GEMV_MAX_N:
+        return False
+    if fmt == "int4":
+        if K is None or group is None:
+            raise ValueError("the 4-bit rule depends on K and group")
+        long_k = group == 32 and K > WQ_AUTO_INT4_G32_LONG_K
+        return M > (WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M if long_k else WQ_AUTO_INT4_GEMV_MAX_M)
+    if fmt in ("mxfp4", "nvfp4"):
+        return M > WQ_AUTO_FP4_GEMV_MAX_M
+    return M > WQ_AUTO_INT8_GEMV_MAX_M
+
+
 WQ_WORKSPACE_COUNTER_BYTES = 2048  # leading counter bytes of a split-K workspace (zero before first use)
 WQ_NOALLOC_SCRATCH_BYTES = WQ_WORKSPACE_COUNTER_BYTES + (16 << 20)  # per-GPU scratch of wq_gemm_w4a16_noalloc
 

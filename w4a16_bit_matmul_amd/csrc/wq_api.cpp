@@ -16,16 +16,15 @@ static_assert(wq::kSplitCounterBytes == WQ_WORKSPACE_COUNTER_BYTES, "split-K cou
 // hands over to the MFMA tile GEMM where re-reading the weights per activation
 // tile costs more than the GEMM's staging.  Narrow outputs give the GEMM's
 // 128-column workgroups too few to fill the chip, so the GEMV keeps more rows
-// there; wide outputs let each 4-bit or FP4 GEMV workgroup share its x slices
-// among four row blocks.
-static bool auto_mfma(int64_t M, int64_t N, int fmt, int path) {
+// there.
+static bool auto_mfma(int64_t M, int64_t N, int64_t K, int group, int fmt, int path) {
   if (path != WQ_PATH_AUTO) return path == WQ_PATH_MFMA;
+  if (M <= WQ_AUTO_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N) return false;
   if (fmt == wq::kFmtInt4)
-    return M > WQ_AUTO_INT4_GEMV_MAX_M && !(M <= WQ_AUTO_INT4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N) &&
-           !(M <= WQ_AUTO_INT4_WIDE_GEMV_MAX_M && N > WQ_AUTO_INT4_WIDE_N);
-  if (fmt == wq::kFmtMxfp4 || fmt == wq::kFmtNvfp4)
-    return M > WQ_AUTO_FP4_GEMV_MAX_M && !(M <= WQ_AUTO_FP4_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
-  return M > WQ_AUTO_INT8_GEMV_MAX_M && !(M <= WQ_AUTO_INT8_NARROW_GEMV_MAX_M && N <= WQ_AUTO_GEMV_MAX_N);
+    return M > (group == 32 && K > WQ_AUTO_INT4_G32_LONG_K ? WQ_AUTO_INT4_G32_LONG_K_GEMV_MAX_M
+                                                           : WQ_AUTO_INT4_GEMV_MAX_M);
+  if (fmt == wq::kFmtMxfp4 || fmt == wq::kFmtNvfp4) return M > WQ_AUTO_FP4_GEMV_MAX_M;
+  return M > WQ_AUTO_INT8_GEMV_MAX_M;
 }
 
 namespace {
@@ -146,7 +145,7 @@ size_t wq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
 size_t wq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, int group, int path) {
   if (M <= 0 || M > (int64_t(1) << 31) || check_shape(N, K, group)) return 0;
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return 0;
-  const bool mfma = auto_mfma(M, N, wq::kFmtInt4, path);
+  const bool mfma = auto_mfma(M, N, K, group, wq::kFmtInt4, path);
   return mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, wq::kFmtInt4);
 }
 
@@ -157,7 +156,7 @@ int wq_gemm_plan(int64_t M, int64_t N, int64_t K, int group, int path, char* buf
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, wq::kFmtInt4, path);
+  const bool mfma = auto_mfma(M, N, K, group, wq::kFmtInt4, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 4, buf, buf_len);
   else
@@ -181,7 +180,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int group, int fmt, const uint16
   int st = check_shape(N, K, fmt == wq::kFmtNvfp4 ? 32 : group);  // NVFP4: blocks of 16, K a multiple of 32
   if (st) return st;
   if (!aligned(x_f16, 16) || !aligned(qpacked, 16) || !aligned(s_f16, 2) || !aligned(y_f16, 2)) return WQ_EALIGN;
-  *mfma = auto_mfma(M, N, fmt, path);
+  *mfma = auto_mfma(M, N, K, group, fmt, path);
   const size_t need = *mfma ? wq::gemm_workspace_bytes(M, N, K, group) : wq::gemv_workspace_bytes(M, N, K, group, fmt);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQ_EWORKSPACE;
@@ -309,7 +308,7 @@ int wq_gemm_w8a16_plan(int64_t M, int64_t N, int64_t K, int group, int path, cha
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   int st = check_shape(N, K, group);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, wq::kFmtInt8, path);
+  const bool mfma = auto_mfma(M, N, K, group, wq::kFmtInt8, path);
   if (mfma)
     wq::describe_gemm(M, N, K, group, 8, buf, buf_len);
   else
@@ -440,7 +439,7 @@ int wq_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  const bool mfma = auto_mfma(M, N, wq::kFmtMxfp4, path);
+  const bool mfma = auto_mfma(M, N, K, 32, wq::kFmtMxfp4, path);
   if (mfma)
     wq::describe_gemm(M, N, K, 32, wq::kFmtMxfp4, buf, buf_len);
   else
@@ -541,7 +540,7 @@ int wq_gemm_nvfp4_plan(int64_t M, int64_t N, int64_t K, int path, char* buf, siz
   if (path != WQ_PATH_AUTO && path != WQ_PATH_GEMV && path != WQ_PATH_MFMA) return WQ_EINVAL;
   const int st = check_mx_shape(N, K);
   if (st) return st;
-  if (auto_mfma(M, N, wq::kFmtNvfp4, path))
+  if (auto_mfma(M, N, K, 16, wq::kFmtNvfp4, path))
     wq::describe_gemm(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);
   else
     wq::describe_gemv(M, N, K, 16, wq::kFmtNvfp4, buf, buf_len);

@@ -663,7 +663,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // run two workgroups per CU, sixteen-row tiles one) and no reason to split
   // K.  M = 16, N = 28672, K = 8192, g = 128: 52.8 -> 33.7 us with four
   // blocks (32.9 us in four-wave workgroups, below); M = 8, g = 32: 35.1 ->
-  // 32.5 us with two
+  // 32.5 us with two.  Both tile heights also take two blocks where that
+  // still leaves one workgroup per CU (eight-row tiles: sixteen waves, below):
+  // re-reading x from L2 costs more than the second round saves (M = 8,
+  // N = 8192, g = 32: K = 8192 12.13 -> 11.18 us, K = 28672 36.7 -> 30.7 us;
+  // M = 16, N = K = 8192, MXFP4 14.7 -> 11.3 us).
   p.RB = 1;
   if (fmt != kFmtInt8 && p.MT >= 8) {  // (8-bit codes: twice the code registers per block)
     const int64_t round = p.MT == 8 ? 512 : 256;
@@ -672,11 +676,14 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
         p.RB = rb;
         break;
       }
+    if (p.RB == 1 && (NBLK + 1) / 2 * p.gy >= 256) p.RB = 2;
   }
   // sixteen-row tiles over four row blocks: four-wave workgroups, two per CU,
   // so that the grid runs in one round (M = 16, N = 28672, g = 32: 40.0 ->
-  // 37.5 us)
+  // 37.5 us); eight-row tiles over two blocks in a grid of at most 256
+  // workgroups: sixteen waves, one workgroup per CU
   if (p.MT == 16 && p.RB == 4) p.W = 4;
+  if (p.MT == 8 && p.RB == 2 && (NBLK + 1) / 2 * p.gy <= 256) p.W = 16;
   p.gx = (unsigned)(p.half ? 2 * NBLK : (NBLK + p.RB - 1) / p.RB);
   // split K across workgroups only where a workgroup would otherwise take
   // more than one pass of its waves over K, and only up to about two
@@ -726,12 +733,16 @@ hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 }
 
 // the matrix-core GEMV over p.RB row blocks (sixteen-row tiles over four
-// blocks run four-wave workgroups)
+// blocks run four-wave workgroups; sixteen-wave eight-row workgroups exist
+// only over two blocks)
 template <int MT, int W, int G, int FMT>
 hipError_t launch_mk(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   if constexpr (FMT == kFmtInt8) {  // one row block per workgroup, eight waves
     if (p.RB != 1 || W != 8) return hipErrorInvalidValue;
     return launch_km<MT, 8, G, 1, FMT>(p, a, stream);
+  } else if constexpr (MT == 8 && W == 16) {
+    if (p.RB != 2) return hipErrorInvalidValue;
+    return launch_km<8, 16, G, 2, FMT>(p, a, stream);
   } else {
     if constexpr (MT == 8) {
       if (p.RB == 4) return launch_km<8, W, G, 4, FMT>(p, a, stream);
@@ -830,7 +841,7 @@ hipError_t launch_gemv(int64_t M, int64_t N, int64_t K, int group, int fmt, cons
   if (p.MT == 1) return p.W == 16 ? launch_t<1, 16>(p, group, fmt, a, stream) : launch_t<1, 8>(p, group, fmt, a, stream);
   if (p.MT == 2) return launch_t<2, 8>(p, group, fmt, a, stream);
   if (p.MT == 4) return launch_t<4, 8>(p, group, fmt, a, stream);
-  if (p.MT == 8) return launch_t<8, 8>(p, group, fmt, a, stream);
+  if (p.MT == 8) return p.W == 16 ? launch_t<8, 16>(p, group, fmt, a, stream) : launch_t<8, 8>(p, group, fmt, a, stream);
   return launch_t<16, 8>(p, group, fmt, a, stream);
 }
 
