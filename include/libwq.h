@@ -398,8 +398,9 @@ int wq_dequant_mxfp4(const uint32_t* qpacked, const uint8_t* e8, int64_t N, int6
 size_t wq_gemm_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* y = x * What^T with MXFP4 weights decoded inside the kernel: the GEMV
- * (WQ_PATH_AUTO rule) sums exact E2M1 values times x per block in fp32 and applies the block's
- * power of two in fp32 (exact for every e8); the MFMA GEMM (larger M) takes fp16
+ * (WQ_PATH_AUTO rule) has the matrix cores sum exact E2M1 values times x per
+ * block in fp32 and applies the block's power of two in fp32 (exact for every
+ * e8); the MFMA GEMM (larger M) takes fp16
  * operands fp16(E2M1 * 2^(e8 - 127)), exact while the block exponent lies in
  * [-23, 13] (outside, the operand rounds to fp16's range).  Arguments,
  * workspace contract and errors as wq_gemm_w4a16 with e8 for the scales and no
@@ -455,10 +456,9 @@ size_t wq_gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* y = x * What^T with NVFP4 weights decoded inside the kernel.  The tensor
  * scale factors out of every output: y = fp16(S * sum_k x * E2M1 * E4M3), the
- * GEMV summing exact E2M1 values times x per block in fp32 and applying the
- * block scale in fp32, the MFMA GEMM taking the exact fp16 operands
- * E2M1 * E4M3.  Arguments, workspace contract and errors as wq_gemm_w4a16
- * with s8 for the scales and tensor_scale (device) for S. */
+ * GEMV and the MFMA GEMM both giving the matrix cores the exact fp16 operands
+ * E2M1 * E4M3 (fp32 sums).  Arguments, workspace contract and errors as
+ * wq_gemm_w4a16 with s8 for the scales and tensor_scale (device) for S. */
 int wq_gemm_nvfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x_f16, const uint32_t* qpacked, const uint8_t* s8,
                   const float* tensor_scale, uint16_t* y_f16, void* workspace, size_t workspace_bytes, void* stream);
 
