@@ -193,6 +193,8 @@ MATMUL_CASES = [  # M, N, K, group
     (30, 16400, 512, 32),
     (12, 8176, 4224, 32),
     (16, 2064, 4224, 32),
+    # group 32 with K past 16384: AUTO hands M > 8 to the GEMM
+    (12, 2064, 16512, 32),
     # eight-row tiles over two blocks: N = 8176 (511 blocks, the last
     # workgroup's second block past N) in sixteen-wave workgroups, and
     # N = 12000 (750 blocks, 375 workgroups) in eight-wave ones
