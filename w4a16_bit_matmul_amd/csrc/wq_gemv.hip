@@ -205,8 +205,11 @@ constexpr __host__ __device__ int gemv_xrow(int MT, int KQ) { return KQ * 128 + 
 // from L2 once per RB blocks.
 // (Register bounds: the one-row sixteen-wave instances run two workgroups per
 // CU at 64 VGPRs; the eight-row instances over up to two blocks two eight-wave
-// workgroups at 128; the four-wave sixteen-row instances two at 256.)
-// FMT: kFmtInt4 (above), kFmtMxfp4 or kFmtNvfp4.  The E2M1 codes share the
+// workgroups, or one sixteen-wave workgroup, at 128; the four-wave
+// sixteen-row instances two at 256.)
+// FMT: kFmtInt4 (above), kFmtInt8 (2048-byte tiles, 32 bytes per lane: step
+// j's eight codes are words 2 (j % 2) and 2 (j % 2) + 1 of half j / 2, decoded
+// to exact fp16 q), kFmtMxfp4 or kFmtNvfp4.  The E2M1 codes share the
 // tile layout, so word j of a lane's 16 bytes is again the B operand of step j:
 // v_cvt_scalef32_pk_f16_fp4 at scale 1 gives its eight exact E2M1 values.
 // MXFP4 (one E8M0 scale per 32 columns = one step): the matrix core sums each
@@ -506,7 +509,6 @@ __global__ __launch_bounds__(W * 64, W == 16 ? 8 : 4) void gemv_mfma_half_kernel
   constexpr int SPG = 4 / GPT;       // MFMA steps per group
   constexpr int NS = KQ * GPT;       // groups per segment
   constexpr int NP = KQ / 2;         // tile pairs per segment
-  constexpr int NT = W * 64;
   static_assert(KQ == 4, "a segment is four tiles: one 16-byte x chunk per lane");
   extern __shared__ __align__(16) uint8_t smem[];
 

@@ -76,7 +76,7 @@ hipError_t launch_kv_quantize(const void* X, int dtype, int64_t T, int64_t hd, c
 hipError_t launch_kv_dequant(const uint8_t* codes, const uint16_t* s, const uint8_t* zp, int64_t T, int64_t hd,
                              const int32_t* slot, int64_t S, int out_dtype, void* out, hipStream_t stream);
 
-// VALU split-K GEMV for small M.  It needs a workspace (a counter region that
+// Split-K GEMV for small M (dot products on the matrix cores).  It needs a workspace (a counter region that
 // is zero on entry and left zero, then fp32 partial sums) only when it splits K
 // across workgroups; gemv_workspace_bytes gives the size (0 otherwise).
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group, int fmt);
