@@ -103,7 +103,7 @@ def test_workspace_query_and_check():
     # across workgroups to fill the GPU (few row or column blocks); the
     # query covers both families (the M=128, N=28672 GEMM splits nothing)
     assert wq.wq_gemm_workspace_bytes(128, 28672, 8192, 128) == 0
-    for M, N, K, g in [(1, 1024, 28672, 32), (8, 1024, 8192, 128), (1, 48, 28672, 128), (16, 64, 8192, 32)]:
+    for M, N, K, g in [(1, 1024, 28672, 32), (8, 1024, 8192, 128), (1, 48, 28672, 128), (16, 64, 28672, 32)]:
         for path in (wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA):
             need = wq.wq_gemm_workspace_bytes(M, N, K, g, path)
             assert 0 < need <= wq.wq_gemm_workspace_bytes(M, N, K, g), (M, N, K, g, path)
@@ -152,10 +152,26 @@ def test_gemm_plan_names_the_dispatched_kernel():
     assert d.startswith("gemv_mfma_kernel<MT=16, W=4, KQ=4, G=128, RB=4>") and "grid=(448,1,1)" in d, d
     d = wq.wq_gemm_plan(8, 28672, 8192, 32)
     assert d.startswith("gemv_mfma_kernel<MT=8, W=8, KQ=4, G=32, RB=2>") and "grid=(896,1,1)" in d, d
-    d = wq.wq_gemm_plan(16, 1024, 8192, 32)
-    assert d.startswith("gemv_mfma_kernel<MT=8") and "grid=(64,2," in d, d
-    d = wq.wq_gemm_plan(32, 1024, 8192, 32)
-    assert d.startswith("gemv_mfma_kernel<MT=16") and "grid=(64,2," in d, d
+    # narrow outputs (N <= 2048) with 9..32 rows: eight-row tiles in
+    # sixteen-wave workgroups over all of K, where that is one pass of the
+    # waves or fills 256 workgroups; otherwise the split plans above
+    for M, N, K in ((16, 1024, 8192), (32, 1024, 8192), (9, 300, 1024), (16, 2048, 8192), (32, 2048, 8192),
+                    (32, 1024, 14336), (24, 512, 4096)):
+        for g in (32, 128):
+            d = wq.wq_gemm_plan(M, N, K, g, wq.WQ_PATH_GEMV)
+            assert d.startswith(f"gemv_mfma_kernel<MT=8, W=16, KQ=4, G={g}>") and split_k(d) == 1, d
+            assert f"grid=({(N + 15) // 16},{(M + 7) // 8},1) block=1024" in d, d
+        assert wq.wq_gemm_mxfp4_plan(M, N, K, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=8, W=16, KQ=4, G=32, RB=1, MXFP4>")
+        assert wq.wq_gemm_nvfp4_plan(M, N, K, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=8, W=16, KQ=4, G=16, RB=1, NVFP4>")
+        # 8-bit codes keep eight-wave workgroups
+        assert "W=8" in wq.wq_gemm_w8a16_plan(M, N, K, 32, wq.WQ_PATH_GEMV)
+    d = wq.wq_gemm_plan(16, 1024, 14336, 32)  # two passes over K, 128 workgroups: split
+    assert d.startswith("gemv_mfma_kernel<MT=8, W=8,") and split_k(d) == 4, d
+    d = wq.wq_gemm_plan(8, 1024, 8192, 32)
+    assert d.startswith("gemv_mfma_kernel<MT=8, W=8,") and split_k(d) == 2, d
+    d = wq.wq_gemm_plan(33, 1024, 8192, 32, wq.WQ_PATH_GEMV)
+    assert d.startswith("gemv_mfma_kernel<MT=16") and "grid=(64,3," in d, d
+    assert wq.wq_gemm_plan(16, 2064, 8192, 32).startswith("gemv_mfma_kernel<MT=16")
     assert wq.wq_gemm_w8a16_plan(16, 28672, 8192, 128, wq.WQ_PATH_GEMV).startswith("gemv_mfma_kernel<MT=16, W=8, KQ=4, G=128, RB=1, BITS=8>")
     assert wq.wq_gemm_plan(1, 256, 1024, 32, wq.WQ_PATH_MFMA).startswith("gemm_kernel<MB=1, NPW=2, G=32>")
     # a small grid splits K across workgroups in whole eight-tile chunks

@@ -103,7 +103,10 @@ MATMUL_CASES = [(1, 256, 1024), (1, 1000, 1152), (3, 37, 96), (8, 272, 640), (17
                 # row blocks (N past 16384: 1025 blocks, the last one ragged), two rows
                 (6, 16400, 512), (16, 16400, 512), (30, 16400, 512), (12, 8176, 4224), (2, 1000, 1152),
                 # eight-row tiles over two blocks, sixteen-wave workgroups (511 blocks)
-                (8, 8176, 640)]
+                (8, 8176, 640),
+                # narrow outputs, 9..32 rows: eight-row tiles in sixteen-wave
+                # workgroups over all of K (one pass, ragged N and K; two passes)
+                (24, 1000, 8192), (12, 520, 4224), (32, 1040, 14336)]
 
 
 @pytest.mark.parametrize("path", [wq.WQ_PATH_GEMV, wq.WQ_PATH_MFMA, wq.WQ_PATH_AUTO])

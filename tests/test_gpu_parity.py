@@ -200,6 +200,13 @@ MATMUL_CASES = [  # M, N, K, group
     # N = 12000 (750 blocks, 375 workgroups) in eight-wave ones
     (8, 8176, 640, 32),
     (6, 12000, 512, 128),
+    # narrow outputs with 9..32 rows: eight-row tiles in sixteen-wave
+    # workgroups over all of K (no split): one pass with the last row block
+    # ragged (N = 1000) and a ragged K (33 tiles), and two passes of the waves
+    # over K = 14336 in 260 workgroups
+    (24, 1000, 8192, 32),
+    (12, 520, 4224, 32),
+    (32, 1040, 14336, 128),
 ]
 
 

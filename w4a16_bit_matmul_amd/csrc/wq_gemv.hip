@@ -37,7 +37,9 @@
 // one-row 4-bit, MXFP4 and NVFP4 instances are compiled to that bound; the
 // instances that need more registers (8-bit codes, two or more rows of x) run
 // eight-wave workgroups instead, two or three per CU (sixteen-row tiles over
-// four blocks: four-wave workgroups, two per CU).  The waves' partial sums meet in
+// four blocks: four-wave workgroups, two per CU; eight-row tiles over two
+// blocks, or over one block of a narrow output: sixteen waves, one workgroup
+// per CU, at most 128 VGPRs).  The waves' partial sums meet in
 // LDS in a fixed order.  When the grid splits K, each
 // workgroup writes fp32 partial sums to the workspace and the last workgroup of
 // a row range (found with a device-scope atomic counter) adds them in split
@@ -658,6 +660,19 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // against 7.9 us
   p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
+  // narrow outputs (N <= 2048) with 9..32 rows of x: eight-row tiles in
+  // sixteen-wave workgroups, each covering all of K, where that takes one pass
+  // of the waves or still fills the GPU (256 workgroups).  The row tiles of a
+  // column block re-read its codes, but from the same XCD's L2 (the grid's x
+  // extent is a multiple of eight); what is saved is the split-K hand-off and
+  // half of each wave's x slice.  N = 1024, K = 8192, g = 32: M = 16 6.87 ->
+  // 6.67 us, M = 32 7.80 -> 6.59 us; N = 2048, M = 16 7.98 -> 6.82 us;
+  // N = 1024, K = 14336, M = 32 12.84 -> 9.46 us (M = 16 there, 128
+  // workgroups over two passes: 8.48 -> 9.64 us, so not taken); MXFP4 and
+  // NVFP4 gain as much.  8-bit codes keep eight-wave workgroups (registers).
+  const bool narrow = fmt != kFmtInt8 && M > 8 && M <= 32 && N <= 2048 &&
+                      (KT <= 16 * kKQ || NBLK * ((M + 7) / 8) >= 256);
+  if (narrow) p.MT = 8;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
   // eight or sixteen rows of x: each workgroup applies its x
   // slices to RB row blocks (x read from L2 once per RB blocks), as many as
@@ -671,7 +686,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // N = 8192, g = 32: K = 8192 12.13 -> 11.18 us, K = 28672 36.7 -> 30.7 us;
   // M = 16, N = K = 8192, MXFP4 14.7 -> 11.3 us).
   p.RB = 1;
-  if (fmt != kFmtInt8 && p.MT >= 8) {  // (8-bit codes: twice the code registers per block)
+  if (!narrow && fmt != kFmtInt8 && p.MT >= 8) {  // (8-bit codes: twice the code registers per block)
     const int64_t round = p.MT == 8 ? 512 : 256;
     for (int rb = 4; rb > 1; rb /= 2)
       if ((NBLK + rb - 1) / rb * p.gy > round) {
@@ -686,6 +701,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // workgroups: sixteen waves, one workgroup per CU
   if (p.MT == 16 && p.RB == 4) p.W = 4;
   if (p.MT == 8 && p.RB == 2 && (NBLK + 1) / 2 * p.gy <= 256) p.W = 16;
+  if (narrow) p.W = 16;
   p.gx = (unsigned)(p.half ? 2 * NBLK : (NBLK + p.RB - 1) / p.RB);
   // split K across workgroups only where a workgroup would otherwise take
   // more than one pass of its waves over K, and only up to about two
@@ -700,6 +716,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   while (wgs * ks * 2 <= target && ks < passes) ks *= 2;
   if (wgs > kSplitMaxTiles) ks = 1;  // (never taken: a split grid has < 512 row ranges)
   if (p.RB > 1) ks = 1;  // (never taken either: row blocks are shared only past one round)
+  if (narrow) ks = 1;     // (K = 14336, M = 32: 9.46 us whole, 14.26 us split two ways)
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
@@ -736,13 +753,14 @@ hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 
 // the matrix-core GEMV over p.RB row blocks (sixteen-row tiles over four
 // blocks run four-wave workgroups; sixteen-wave eight-row workgroups exist
-// only over two blocks)
+// over one block, for narrow outputs, and over two)
 template <int MT, int W, int G, int FMT>
 hipError_t launch_mk(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   if constexpr (FMT == kFmtInt8) {  // one row block per workgroup, eight waves
     if (p.RB != 1 || W != 8) return hipErrorInvalidValue;
     return launch_km<MT, 8, G, 1, FMT>(p, a, stream);
   } else if constexpr (MT == 8 && W == 16) {
+    if (p.RB == 1) return launch_km<8, 16, G, 1, FMT>(p, a, stream);
     if (p.RB != 2) return hipErrorInvalidValue;
     return launch_km<8, 16, G, 2, FMT>(p, a, stream);
   } else {
