@@ -108,8 +108,8 @@ typedef enum {
  * 31.1 / 34.3; N = 28672, K = 8192, M = 16, g = 128: 32.8 / 34.6.  MXFP4,
  * M = 16: K = 8192 11.3 / 15.7, K = 28672 31.4 / 33.1; NVFP4, M = 16: K = 8192
  * 12.3 / 16.2, K = 28672 32.8 / 33.5.  int8, g = 128, K = 8192: M = 8 14.5 /
- * 19.3, M = 16 18.8 / 18.1.  M = 32, N = 2048: 4-bit 8.9 / 13.3 (N = 1024),
- * MXFP4 12.0 / 12.5, NVFP4 11.8 / 13.0, int8 12.3 / 13.3. */
+ * 19.3, M = 16 18.8 / 18.1.  M = 32, N = 2048: MXFP4 10.5 / 12.5, NVFP4
+ * 10.4 / 13.0, int8 12.3 / 13.3; 4-bit at N = 1024 6.6 / 13.3. */
 #define WQ_AUTO_GEMV_MAX_N 2048
 #define WQ_AUTO_NARROW_GEMV_MAX_M 32
 #define WQ_AUTO_INT4_GEMV_MAX_M 16
