@@ -153,10 +153,11 @@ def test_gemm_plan_names_the_dispatched_kernel():
     d = wq.wq_gemm_plan(8, 28672, 8192, 32)
     assert d.startswith("gemv_mfma_kernel<MT=8, W=8, KQ=4, G=32, RB=2>") and "grid=(896,1,1)" in d, d
     # narrow outputs (N <= 2048) with 9..32 rows: eight-row tiles in
-    # sixteen-wave workgroups over all of K, where that is one pass of the
-    # waves or fills 256 workgroups; otherwise the split plans above
-    for M, N, K in ((16, 1024, 8192), (32, 1024, 8192), (9, 300, 1024), (16, 2048, 8192), (32, 2048, 8192),
-                    (32, 1024, 14336), (24, 512, 4096)):
+    # sixteen-wave workgroups over all of K where that fills the GPU (at least
+    # 64 workgroups and eight K segments, sixteen past 256 workgroups, one pass
+    # over K unless the grid has 256); otherwise the plans above
+    for M, N, K in ((16, 1024, 8192), (32, 1024, 8192), (16, 2048, 8192), (32, 2048, 8192), (32, 1024, 14336),
+                    (24, 512, 4096), (16, 512, 8192), (12, 520, 4224), (32, 1024, 4096)):
         for g in (32, 128):
             d = wq.wq_gemm_plan(M, N, K, g, wq.WQ_PATH_GEMV)
             assert d.startswith(f"gemv_mfma_kernel<MT=8, W=16, KQ=4, G={g}>") and split_k(d) == 1, d
@@ -167,6 +168,11 @@ def test_gemm_plan_names_the_dispatched_kernel():
         assert "W=8" in wq.wq_gemm_w8a16_plan(M, N, K, 32, wq.WQ_PATH_GEMV)
     d = wq.wq_gemm_plan(16, 1024, 14336, 32)  # two passes over K, 128 workgroups: split
     assert d.startswith("gemv_mfma_kernel<MT=8, W=8,") and split_k(d) == 4, d
+    # too few K segments (K = 2048: four; K = 4096 past 256 workgroups) or
+    # workgroups (N = 64, 160): the plans above
+    for M, N, K in ((32, 2048, 2048), (16, 1024, 2048), (32, 2048, 4096), (16, 64, 8192), (24, 160, 8192), (9, 300, 1024)):
+        d = wq.wq_gemm_plan(M, N, K, 128, wq.WQ_PATH_GEMV)
+        assert "W=16" not in d, (M, N, K, d)
     d = wq.wq_gemm_plan(8, 1024, 8192, 32)
     assert d.startswith("gemv_mfma_kernel<MT=8, W=8,") and split_k(d) == 2, d
     d = wq.wq_gemm_plan(33, 1024, 8192, 32, wq.WQ_PATH_GEMV)

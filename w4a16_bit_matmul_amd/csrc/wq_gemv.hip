@@ -661,17 +661,22 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   p.half = p.MT == 1 && fmt == kFmtInt4 && (N + 15) / 16 * 2 <= 512;
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   // narrow outputs (N <= 2048) with 9..32 rows of x: eight-row tiles in
-  // sixteen-wave workgroups, each covering all of K, where that takes one pass
-  // of the waves or still fills the GPU (256 workgroups).  The row tiles of a
+  // sixteen-wave workgroups, each covering all of K.  The row tiles of a
   // column block re-read its codes, but from the same XCD's L2 (the grid's x
   // extent is a multiple of eight); what is saved is the split-K hand-off and
   // half of each wave's x slice.  N = 1024, K = 8192, g = 32: M = 16 6.87 ->
   // 6.67 us, M = 32 7.80 -> 6.59 us; N = 2048, M = 16 7.98 -> 6.82 us;
-  // N = 1024, K = 14336, M = 32 12.84 -> 9.46 us (M = 16 there, 128
-  // workgroups over two passes: 8.48 -> 9.64 us, so not taken); MXFP4 and
-  // NVFP4 gain as much.  8-bit codes keep eight-wave workgroups (registers).
-  const bool narrow = fmt != kFmtInt8 && M > 8 && M <= 32 && N <= 2048 &&
-                      (KT <= 16 * kKQ || NBLK * ((M + 7) / 8) >= 256);
+  // N = 1024, K = 14336, M = 32 12.84 -> 9.46 us; MXFP4 and NVFP4 gain as
+  // much.  Taken only where it fills the GPU: at least 64 workgroups (N = 64,
+  // M = 16: 6.05 -> 6.33 us), at least eight K segments for the sixteen waves
+  // (K = 2048, N = 2048, M = 32: 4.03 -> 5.68 us, the 141 KB of LDS holding
+  // one workgroup per CU), sixteen past one round of 256 workgroups, and one
+  // pass over K unless the grid fills one round (N = 1024, K = 14336, M = 16,
+  // 128 workgroups over two passes: 8.48 -> 9.64 us).  8-bit codes keep
+  // eight-wave workgroups (registers).
+  const int64_t nwg8 = NBLK * ((M + 7) / 8), segs = (KT + kKQ - 1) / kKQ;
+  const bool narrow = fmt != kFmtInt8 && M > 8 && M <= 32 && N <= 2048 && nwg8 >= 64 && segs >= 8 &&
+                      (segs >= 16 || nwg8 <= 256) && (KT <= 16 * kKQ || nwg8 >= 256);
   if (narrow) p.MT = 8;
   p.gy = (unsigned)((M + p.MT - 1) / p.MT);
   // eight or sixteen rows of x: each workgroup applies its x
