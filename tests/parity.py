@@ -62,9 +62,10 @@ def assert_quantize_matches(W_host: np.ndarray, w_dtype: str, group: int, out=No
     return q, s, z, out
 
 
-# Elementwise floors.  The VALU GEMV multiplies exact codes in fp32, so its
-# elementwise error against the exact-What product is checked down to 1e-3 of
-# max|y|.  The MFMA path multiplies fp16(What): one rounding per weight, a
+# Elementwise floors.  The GEMV multiplies x by the exact code differences
+# q - z (small integers, exact in fp16) on the matrix cores, sums the exact
+# products in fp32 and applies each group's scale once, so its elementwise
+# error against the exact-What product is checked down to 1e-3 of max|y|.  The MFMA path multiplies fp16(What): one rounding per weight, a
 # relative error uniform in +-2^-11 (rms 2^-11/sqrt(3) = 2.8e-4).  Over K terms
 # the output error then has about 2.8e-4 times the spread of y itself, so an
 # output near zero can carry an error of ~3e-4 of max|y|; against the

@@ -725,8 +725,8 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   // split boundaries on whole segments
   p.kt_per_split = (int)(((KT + ks - 1) / ks + kKQ - 1) / kKQ * kKQ);
   p.KS = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
-  // x slices, then the cross-wave sums: [W][MT][64] fp32 (VALU kernels) or
-  // [W][MT][16] (matrix-core kernels); with several row blocks the sums
+  // x slices (the eight-row kernel: [W][KQ * 128] halves), then the
+  // cross-wave sums [W][MT][16] fp32; with several row blocks the sums
   // [W][RB][MT][16] reuse the slices' space
   const size_t slices = !p.half ? (size_t)p.W * p.MT * gemv_xrow(p.MT, kKQ) * 2 : (size_t)p.W * p.MT * kKQ * 256;
   if (p.RB > 1)
