@@ -662,9 +662,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
   const int64_t NBLK = (N + 15) / 16, KT = (K + 127) / 128;
   // narrow outputs (N <= 2048) with 9..32 rows of x: eight-row tiles in
   // sixteen-wave workgroups, each covering all of K.  The row tiles of a
-  // column block re-read its codes, but from the same XCD's L2 (the grid's x
-  // extent is a multiple of eight); what is saved is the split-K hand-off and
-  // half of each wave's x slice.  N = 1024, K = 8192, g = 32: M = 16 6.87 ->
+  // column block re-read its codes from L2 (from the same XCD's when the
+  // grid's x extent is a multiple of eight: workgroups go round the eight
+  // XCDs in order); what is saved is the split-K hand-off and half of each
+  // wave's x slice.  N = 1024, K = 8192, g = 32: M = 16 6.87 ->
   // 6.67 us, M = 32 7.80 -> 6.59 us; N = 2048, M = 16 7.98 -> 6.82 us;
   // N = 1024, K = 14336, M = 32 12.84 -> 9.46 us; MXFP4 and NVFP4 gain as
   // much.  Taken only where it fills the GPU: at least 64 workgroups (N = 64,
