@@ -739,6 +739,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int fmt) {
 
 template <int W, int G>
 hipError_t launch_kh(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  if (!p.half || p.MT != 1 || p.W != W || p.RB != 1) return hipErrorInvalidValue;
   auto k = gemv_mfma_half_kernel<W, kKQ, G>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
@@ -749,6 +750,9 @@ hipError_t launch_kh(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
 
 template <int MT, int W, int G, int RB, int FMT>
 hipError_t launch_km(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  // the plan sized the grid and the LDS for its own (MT, W, RB): launch only
+  // the instance it describes
+  if (p.half || p.MT != MT || p.W != W || p.RB != RB) return hipErrorInvalidValue;
   auto k = gemv_mfma_kernel<MT, W, kKQ, G, RB, FMT>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit((const void*)k, p.lds, lds_raised);
